@@ -1,0 +1,236 @@
+"""Python binding of the MI355X QSA library (libqsa.so, C ABI in include/qsa.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Tensors supply device pointers; the current torch stream supplies the
+HIP stream.  Each function has the name of the C entry point it calls and
+raises QSAError on a non-OK status.  If libqsa.so has not been built this
+module raises at first use -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqsa.so")
+
+QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE = range(6)
+
+STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPPORTED", 4: "QSA_ERR_ALIGN",
+          5: "QSA_ERR_CAPACITY", 6: "QSA_ERR_WORKSPACE", 7: "QSA_ERR_HIP"}
+
+# The C entry points (kept in step with include/qsa.h).
+EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
+           "qsa_append", "qsa_index", "qsa_select", "qsa_attend", "qsa_forward", "qsa_decode",
+           "qsa_status_string", "qsa_last_hip_error"]
+
+
+class QSAError(RuntimeError):
+    def __init__(self, status: int, where: str, hip: int = 0):
+        self.status = status
+        msg = "%s failed: %s" % (where, STATUS.get(status, status))
+        if status == 7:
+            msg += " (hip error %d)" % hip
+        super().__init__(msg)
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_dim", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
+                ("idx_rope_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("budget_blocks", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("max_ctx", ctypes.c_int64), ("rope_theta", ctypes.c_double),
+                ("yarn_factor", ctypes.c_double), ("yarn_orig_ctx", ctypes.c_int64)]
+
+
+_lib_handle = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqsa.so; raise if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libqsa.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    L.qsa_default_params.argtypes = [ctypes.POINTER(Params)]
+    L.qsa_default_params.restype = None
+    L.qsa_create.argtypes = [ctypes.POINTER(Params), ctypes.c_int, ctypes.POINTER(vp)]
+    L.qsa_create.restype = ctypes.c_int
+    L.qsa_destroy.argtypes = [vp]
+    L.qsa_destroy.restype = None
+    L.qsa_get_params.argtypes = [vp, ctypes.POINTER(Params)]
+    L.qsa_get_params.restype = ctypes.c_int
+    L.qsa_workspace_size.argtypes = [vp, ctypes.c_int, i32, i64, i64]
+    L.qsa_workspace_size.restype = sz
+    L.qsa_append.argtypes = [vp, vp, i32, i64, i64] + [vp] * 7
+    L.qsa_append.restype = ctypes.c_int
+    L.qsa_index.argtypes = [vp, vp, i32, i64, i64] + [vp] * 6 + [sz]
+    L.qsa_index.restype = ctypes.c_int
+    L.qsa_select.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, sz]
+    L.qsa_select.restype = ctypes.c_int
+    L.qsa_attend.argtypes = [vp, vp, i32, i64, i64] + [vp] * 8 + [sz]
+    L.qsa_attend.restype = ctypes.c_int
+    L.qsa_forward.argtypes = [vp, vp, i32, i64, i64] + [vp] * 12 + [sz]
+    L.qsa_forward.restype = ctypes.c_int
+    L.qsa_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 12 + [sz]
+    L.qsa_decode.restype = ctypes.c_int
+    L.qsa_status_string.argtypes = [ctypes.c_int]
+    L.qsa_status_string.restype = ctypes.c_char_p
+    L.qsa_last_hip_error.argtypes = []
+    L.qsa_last_hip_error.restype = ctypes.c_int
+    _lib_handle = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise QSAError(status, where, lib().qsa_last_hip_error())
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t.data_ptr()
+
+
+def _bf(t, name):
+    return _ptr(t, torch.bfloat16, name)
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def default_params(**overrides) -> Params:
+    p = Params()
+    lib().qsa_default_params(ctypes.byref(p))
+    for k, v in overrides.items():
+        setattr(p, k, v)
+    return p
+
+
+class Handle:
+    """Owns a qsa_handle (the layer parameters and device rotary tables)."""
+
+    def __init__(self, params: Optional[Params] = None, device: int = 0, **overrides):
+        if params is None:
+            params = default_params(**overrides)
+        self.params = params
+        self.device = device
+        h = ctypes.c_void_p()
+        _check(lib().qsa_create(ctypes.byref(params), device, ctypes.byref(h)), "qsa_create")
+        self._h = h
+
+    @property
+    def ptr(self):
+        return self._h
+
+    @property
+    def budget(self) -> int:
+        return self.params.budget_blocks
+
+    @property
+    def max_ctx(self) -> int:
+        return self.params.max_ctx
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().qsa_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def qsa_create(params: Optional[Params] = None, device: int = 0, **overrides) -> Handle:
+    return Handle(params, device, **overrides)
+
+
+def qsa_destroy(h: Handle):
+    h.close()
+
+
+def qsa_workspace_size(h: Handle, op: int, batch: int, length: int, q_offset: int) -> int:
+    return int(lib().qsa_workspace_size(h.ptr, op, batch, length, q_offset))
+
+
+def workspace(h: Handle, op: int, batch: int, length: int, q_offset: int, device="cuda") -> torch.Tensor:
+    n = qsa_workspace_size(h, op, batch, length, q_offset)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def alloc_caches(h: Handle, batch: int, device="cuda"):
+    """Caller-owned caches in the library's layouts (see include/qsa.h)."""
+    nb = h.max_ctx // 4
+    bf = torch.bfloat16
+    return {
+        "k_cache": torch.empty((batch, 2, nb, 8, 4, 32), dtype=bf, device=device),
+        "v_cache": torch.empty((batch, 2, nb, 256, 4), dtype=bf, device=device),
+        "kbar_cache": torch.empty((batch, nb, 128), dtype=bf, device=device),
+        "kpend": torch.zeros((batch, 4, 128), dtype=bf, device=device),
+    }
+
+
+def qsa_append(h, B, L, q_offset, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend, stream=None):
+    _check(lib().qsa_append(h.ptr, _stream(stream), B, L, q_offset, _bf(k, "k"), _bf(v, "v"), _bf(k_idx, "k_idx"),
+                            _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
+                            _bf(kpend, "kpend")), "qsa_append")
+
+
+def qsa_index(h, B, L, q_offset, q_idx, k_idx, kbar_cache, kpend, scores, ws, stream=None):
+    _check(lib().qsa_index(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
+                           _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"), _ptr(scores, torch.float32, "scores"),
+                           _ptr(ws, None, "ws"), ws.numel() * ws.element_size()), "qsa_index")
+
+
+def qsa_select(h, B, L, q_offset, scores, block_idx, ws=None, stream=None):
+    _check(lib().qsa_select(h.ptr, _stream(stream), B, L, q_offset, _ptr(scores, torch.float32, "scores"),
+                            _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
+                            0 if ws is None else ws.numel() * ws.element_size()), "qsa_select")
+
+
+def qsa_attend(h, B, L, q_offset, q, k, v, k_cache, v_cache, block_idx, out, ws=None, stream=None):
+    _check(lib().qsa_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
+                            _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _ptr(block_idx, torch.int32, "block_idx"),
+                            _bf(out, "out"), _ptr(ws, None, "ws"),
+                            0 if ws is None else ws.numel() * ws.element_size()), "qsa_attend")
+
+
+def qsa_forward(h, B, L, q_offset, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, block_idx, ws,
+                stream=None):
+    _check(lib().qsa_forward(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
+                             _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"), _bf(k_cache, "k_cache"),
+                             _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"),
+                             _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
+                             ws.numel() * ws.element_size()), "qsa_forward")
+
+
+def qsa_decode(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out,
+               block_idx, ws, stream=None):
+    _check(lib().qsa_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"), ctx_bound,
+                            _bf(q, "q"), _bf(k, "k"), _bf(v, "v"), _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
+                            _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
+                            _bf(kpend, "kpend"), _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"),
+                            _ptr(ws, None, "ws"), ws.numel() * ws.element_size()), "qsa_decode")
+
+
+def qsa_status_string(status: int) -> str:
+    return lib().qsa_status_string(status).decode()
+
+
+def qsa_last_hip_error() -> int:
+    return int(lib().qsa_last_hip_error())

@@ -1,0 +1,314 @@
+// Sparse core attention over the selected micro-blocks (PyTorchKR post
+// "Qwen3.8-Flash-Next, 1/9의 학습 비용으로 …", section "QSA: 인덱서 자체의 비용을
+// 줄이는 희소 어텐션": GQA over the top blocks; the tail tokens of the last
+// incomplete block are always included; spec table: 24 query heads, 2 KV
+// heads, head dim 256, RoPE on 64 dims).
+//
+// One wave computes one (query, KV head) pair: the 12 query heads of the group
+// share every gathered K~/V micro-block.  The token list of query p is the
+// selected blocks (ascending) followed by its own block 4*floor(p/4) .. p; it is
+// walked in chunks of 8 blocks (32 tokens).
+//
+// Matrix-core layout (v_mfma_f32_16x16x32_bf16, 16x16 output, lane l holds
+// column l%16 and rows 4*(l/16) .. +3):
+//   S^T  = K~ . Q~^T   A = 16 tokens x 32 dims of K~ (straight 16-byte loads
+//                      from the blocked cache), B = Q~^T (head l%16), so each
+//                      lane ends with 4 tokens of one head;
+//   O^T += V^T . P^T   B = P^T comes straight from the S^T registers (the
+//                      contraction index is permuted to match), A = V^T from
+//                      the blocked V cache ([dim][4 tokens] per block, 8-byte
+//                      loads), and every O^T accumulator of a lane belongs to
+//                      the same head as its softmax state -- no shuffles.
+// Softmax is online in fp32 (base-2 exponentials, max over the 4 lane groups
+// by two xor-shuffles); P is rounded to bf16 for the PV product.
+#include "qsa_common.h"
+
+namespace qsa {
+
+constexpr int kChunkBlocks = 8;                  // 32 tokens per step
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct RowState {
+    float m;        // running max of the raw logits of head l%16 (same in the 4 lane groups)
+    float l;        // this lane's partial softmax denominator
+    f32x4 o[16];    // O^T: dims 16n + 4*(l/16) + j of head l%16
+};
+
+// Q~^T fragments of one (query, KV group): lane (h = l%16, g = l/16) holds, for
+// k-step s, dims 32s + 8g .. +7 of head 12*grp + h, rotated at `pos` (heads
+// 12..15 of the 16-wide tile are zero).
+__device__ __forceinline__ void load_q_frags(const bf16_t *qrow /*[24][256] of this token*/, int grp, int64_t pos,
+                                             const Tables &tab, bf16x8 (&qf)[8])
+{
+    const int lane = threadIdx.x & 63;
+    const int h = lane & 15, g = lane >> 4;
+    if (h >= kGroup) {
+        for (int s = 0; s < 8; ++s) qf[s] = bf16x8{};
+        return;
+    }
+    const bf16_t *src = qrow + (grp * kGroup + h) * kHeadDim + 8 * g;
+    u32x4 x[8];
+    for (int s = 0; s < 8; ++s) x[s] = *reinterpret_cast<const u32x4 *>(src + 32 * s);
+    // rotary pairs (j, j + 32), j = 8g + e: k-step 0 holds x_j, k-step 1 holds x_{j+32}
+    const float *cs = tab.cos + pos * kPairs + 8 * g;
+    const float *sn = tab.sin + pos * kPairs + 8 * g;
+    uint32_t w0[4], w1[4];
+    for (int i = 0; i < 4; ++i) {
+        float r0[2], r1[2];
+        for (int e = 0; e < 2; ++e) {
+            float a = __uint_as_float(e ? (x[0][i] & 0xFFFF0000u) : (x[0][i] << 16));
+            float b = __uint_as_float(e ? (x[1][i] & 0xFFFF0000u) : (x[1][i] << 16));
+            rotate_pair(a, b, cs[2 * i + e], sn[2 * i + e]);
+            r0[e] = a;
+            r1[e] = b;
+        }
+        w0[i] = pack_bf16x2(r0[0], r0[1]);
+        w1[i] = pack_bf16x2(r1[0], r1[1]);
+    }
+    x[0] = u32x4{w0[0], w0[1], w0[2], w0[3]};
+    x[1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
+    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, x[s]);
+}
+
+// Block id and valid-token mask (bit t = token t valid) of list entry li.
+__device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o, int li, int own_last,
+                                           int64_t &blk, uint32_t &tmask)
+{
+    if (li < n_sel) {
+        const int64_t id = sel[li];
+        const bool ok = id >= 0 && id < o;
+        blk = ok ? id : 0;
+        tmask = ok ? 0xFu : 0u;
+    } else if (li == n_sel) {
+        blk = o;
+        tmask = (1u << (own_last + 1)) - 1u;
+    } else {
+        blk = 0;
+        tmask = 0u;
+    }
+}
+
+// Walk chunks [c_lo, c_hi) of one (query, group) token list.
+__device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
+                                              const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
+                                              int n_sel, int64_t o, int own_last, int c_lo, int c_hi, float c2,
+                                              RowState &st)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;           // K-load token row / V-load dim
+    const int g = lane >> 4;
+    for (int c = c_lo; c < c_hi; ++c) {
+        const int lb = kChunkBlocks * c;
+        // ---- gather K~ (A operand of S^T): tile t, token row r -> list entry lb + 4t + r/4
+        int64_t kblk[2];
+        uint32_t kmask[2];
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
+        bf16x8 kf[2][8];
+        for (int t = 0; t < 2; ++t) {
+            const bf16_t *src = kc + kblk[t] * kBlockElems + (r & 3) * 32 + 8 * g;
+            for (int s = 0; s < 8; ++s) kf[t][s] = *reinterpret_cast<const bf16x8 *>(src + s * 128);
+        }
+        // ---- gather V (A operand of O^T): list entries lb + g and lb + 4 + g, dim 16n + r
+        int64_t vblk[2];
+        uint32_t vmask[2];
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
+        u32x2 vraw[16][2];
+        for (int t = 0; t < 2; ++t) {
+            const bf16_t *src = vc + vblk[t] * kBlockElems + r * kBlock;
+            for (int n = 0; n < 16; ++n) vraw[n][t] = *reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock);
+        }
+        // ---- S^T = K~ . Q~^T
+        f32x4 sc[2];
+        for (int t = 0; t < 2; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], qf[s], acc, 0, 0, 0);
+            sc[t] = acc;
+        }
+        // lane holds tokens j = 0..3 of list entry lb + 4t + g for head r
+        float cmax = -INFINITY;
+        for (int t = 0; t < 2; ++t) {
+            for (int j = 0; j < 4; ++j) {
+                if (!((vmask[t] >> j) & 1u)) sc[t][j] = -INFINITY;
+                cmax = fmaxf(cmax, sc[t][j]);
+            }
+        }
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+        const float m_new = fmaxf(st.m, cmax);
+        const float alpha = exp2f((st.m - m_new) * c2);
+        st.m = m_new;
+        uint32_t pw[4];
+        float psum = 0.f;
+        for (int t = 0; t < 2; ++t) {
+            float p[4];
+            for (int j = 0; j < 4; ++j) {
+                p[j] = exp2f((sc[t][j] - m_new) * c2);
+            }
+            pw[2 * t] = pack_bf16x2(p[0], p[1]);
+            pw[2 * t + 1] = pack_bf16x2(p[2], p[3]);
+            for (int j = 0; j < 4; ++j) psum += bf16_to_f32(f32_to_bf16(p[j]));
+        }
+        st.l = st.l * alpha + psum;
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        // ---- O^T += V^T . P^T  (zero the V of masked tokens: their cache slots may hold anything)
+        for (int n = 0; n < 16; ++n) {
+            u32x2 lo = vraw[n][0], hi = vraw[n][1];
+            const uint32_t m0 = vmask[0], m1 = vmask[1];
+            lo[0] &= ((m0 & 1u) ? 0xFFFFu : 0u) | ((m0 & 2u) ? 0xFFFF0000u : 0u);
+            lo[1] &= ((m0 & 4u) ? 0xFFFFu : 0u) | ((m0 & 8u) ? 0xFFFF0000u : 0u);
+            hi[0] &= ((m1 & 1u) ? 0xFFFFu : 0u) | ((m1 & 2u) ? 0xFFFF0000u : 0u);
+            hi[1] &= ((m1 & 4u) ? 0xFFFFu : 0u) | ((m1 & 8u) ? 0xFFFF0000u : 0u);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            f32x4 acc = st.o[n];
+            for (int j = 0; j < 4; ++j) acc[j] *= alpha;
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc, 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void init_state(RowState &st) {
+    st.m = -INFINITY;
+    st.l = 0.f;
+    for (int n = 0; n < 16; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Prefill: 4 waves per workgroup = 2 queries x 2 KV groups.
+__global__ __launch_bounds__(256) void attend_prefill_kernel(
+    Tables tab, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out)
+{
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.y;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 2 + (wave >> 1);
+    const int grp = wave & 1;
+    if (i >= L) return;
+    const int64_t pos = q_offset + i;
+    const int64_t o = pos / kBlock;
+    const int own_last = static_cast<int>(pos - o * kBlock);
+    const int n_sel = static_cast<int>(o < budget ? o : budget);
+    const int nchunks = (n_sel + 1 + kChunkBlocks - 1) / kChunkBlocks;
+
+    bf16x8 qf[8];
+    load_q_frags(q + (b * L + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
+    const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const int32_t *sel = block_idx + (b * L + i) * budget;
+
+    RowState st;
+    init_state(st);
+    attend_chunks(qf, kc, vc, sel, n_sel, o, own_last, 0, nchunks, c2, st);
+
+    float lt = st.l + __shfl_xor(st.l, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int h = lane & 15, g = lane >> 4;
+    if (h < kGroup) {
+        bf16_t *dst = out + ((b * L + i) * kQHeads + grp * kGroup + h) * kHeadDim + 4 * g;
+        for (int n = 0; n < 16; ++n) {
+            u32x2 w = u32x2{pack_bf16x2(st.o[n][0] * inv, st.o[n][1] * inv),
+                            pack_bf16x2(st.o[n][2] * inv, st.o[n][3] * inv)};
+            *reinterpret_cast<u32x2 *>(dst + 16 * n) = w;
+        }
+    }
+}
+
+// Decode, split over the token list: one wave per (split, group, sequence)
+// writes its unnormalised partial (m, l, O) for the 12 heads.
+__global__ __launch_bounds__(64) void attend_decode_split_kernel(
+    Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t nblk_cap, int budget, int nsplit,
+    float c2,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_idx, float *__restrict__ part_o, float *__restrict__ part_ml)
+{
+    const int lane = threadIdx.x & 63;
+    const int split = blockIdx.x;
+    const int grp = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t pos = decode_pos(cache_len, b, ctx_bound);
+    const int64_t o = pos / kBlock;
+    const int own_last = static_cast<int>(pos - o * kBlock);
+    const int n_sel = static_cast<int>(o < budget ? o : budget);
+    const int nchunks = (n_sel + 1 + kChunkBlocks - 1) / kChunkBlocks;
+    const int per = (nchunks + nsplit - 1) / nsplit;
+    const int c_lo = split * per;
+    const int c_hi = (c_lo + per < nchunks) ? c_lo + per : nchunks;
+
+    RowState st;
+    init_state(st);
+    if (c_lo < c_hi) {
+        bf16x8 qf[8];
+        load_q_frags(q + b * kQHeads * kHeadDim, grp, pos, tab, qf);
+        const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
+        const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
+        attend_chunks(qf, kc, vc, block_idx + b * budget, n_sel, o, own_last, c_lo, c_hi, c2, st);
+    }
+    float lt = st.l + __shfl_xor(st.l, 16);
+    lt += __shfl_xor(lt, 32);
+    const int h = lane & 15, g = lane >> 4;
+    if (h < kGroup) {
+        const int64_t slot = ((b * kKVHeads + grp) * nsplit + split) * kGroup + h;
+        float *dst = part_o + slot * kHeadDim + 4 * g;
+        for (int n = 0; n < 16; ++n) *reinterpret_cast<f32x4 *>(dst + 16 * n) = st.o[n];
+        if (g == 0) {
+            part_ml[slot * 2] = st.m;
+            part_ml[slot * 2 + 1] = lt;
+        }
+    }
+}
+
+// Merge the splits of one (sequence, head): 256 threads = one per dim.
+__global__ __launch_bounds__(256) void attend_decode_merge_kernel(int nsplit, float c2,
+                                                                  const float *__restrict__ part_o,
+                                                                  const float *__restrict__ part_ml,
+                                                                  bf16_t *__restrict__ out)
+{
+    const int d = threadIdx.x;
+    const int head = blockIdx.x;                    // 0..23
+    const int64_t b = blockIdx.y;
+    const int grp = head / kGroup, h = head % kGroup;
+    const int64_t slot0 = ((b * kKVHeads + grp) * nsplit) * kGroup + h;
+    float m = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[(slot0 + s * kGroup) * 2]);
+    float l = 0.f, acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+        const int64_t slot = slot0 + s * kGroup;
+        const float ms = part_ml[slot * 2];
+        if (ms == -INFINITY) continue;
+        const float w = exp2f((ms - m) * c2);
+        l += part_ml[slot * 2 + 1] * w;
+        acc += part_o[slot * kHeadDim + d] * w;
+    }
+    out[(b * kQHeads + head) * kHeadDim + d] = f32_to_bf16(acc / l);
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
+                                 int64_t nblk_cap, int budget, float sigma, const bf16_t *q, const bf16_t *k_cache,
+                                 const bf16_t *v_cache, const int32_t *block_idx, bf16_t *out)
+{
+    if (L <= 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>((L + 1) / 2), static_cast<unsigned>(B));
+    hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, L, q_offset, nblk_cap, budget,
+                       sigma * kLog2e, q, k_cache, v_cache, block_idx, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_decode(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
+                                int64_t ctx_bound, int64_t nblk_cap, int budget, int nsplit, float sigma, const bf16_t *q,
+                                const bf16_t *k_cache, const bf16_t *v_cache, const int32_t *block_idx,
+                                float *part_o, float *part_ml, bf16_t *out)
+{
+    if (B <= 0) return hipSuccess;
+    const float c2 = sigma * kLog2e;
+    hipLaunchKernelGGL(attend_decode_split_kernel, dim3(nsplit, kKVHeads, B), dim3(64), 0, st, tab, cache_len,
+                       ctx_bound, nblk_cap, budget, nsplit, c2, q, k_cache, v_cache, block_idx, part_o, part_ml);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(attend_decode_merge_kernel, dim3(kQHeads, B), dim3(256), 0, st, nsplit, c2, part_o, part_ml,
+                       out);
+    return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,410 @@
+// Host side of the QSA C ABI: argument checks, workspace sizing and launch
+// order.  Every check runs before the first launch, so a failing call leaves
+// all buffers untouched.  The library never allocates device memory inside a
+// call; the only device memory it owns is the handle's rotary tables.
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "qsa.h"
+#include "qsa_common.h"
+
+namespace qsa {
+void host_inv_freq(double theta, double yarn_factor, int64_t yarn_orig_ctx, double *out);
+void host_rope_tables(const double *inv_freq, int64_t n_pos, float *cos_out, float *sin_out);
+
+hipError_t launch_kv_pool(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, const bf16_t *,
+                          const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *, const bf16_t *, bool, bool);
+hipError_t launch_kpend_store(hipStream_t, int32_t, int64_t, int64_t, const bf16_t *, bf16_t *);
+hipError_t launch_qidx_rotate(const Tables &, hipStream_t, int32_t, int64_t, int64_t, const int32_t *,
+                              const bf16_t *, bf16_t *);
+hipError_t launch_indexer_scores(hipStream_t, int32_t, int64_t, int64_t, int64_t, int64_t, const bf16_t *, int64_t,
+                                 const bf16_t *, float *, int64_t, bool);
+hipError_t launch_select(hipStream_t, int32_t, int64_t, int64_t, const int32_t *, int64_t, const float *, int64_t,
+                         int32_t *, int64_t, int);
+hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
+                                 const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
+hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int, int, float,
+                                const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
+                                bf16_t *);
+hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const bf16_t *,
+                                const bf16_t *, const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *,
+                                bf16_t *, bf16_t *);
+hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int64_t, const bf16_t *,
+                              const bf16_t *, float *);
+}  // namespace qsa
+
+using namespace qsa;
+
+struct qsa_handle {
+    qsa_params p;
+    int device;
+    float *d_cos;
+    float *d_sin;
+    float sigma;        // softmax scale of the core logits
+};
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+// Score-matrix slice of one qsa_forward sub-chunk: at most this many bytes.
+constexpr size_t kForwardScoreBytes = size_t(2) << 30;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+qsa_status hip_fail(hipError_t e) {
+    g_last_hip = static_cast<int>(e);
+    return QSA_ERR_HIP;
+}
+
+// Make the handle's device current for the duration of a call.
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+Tables tables(const qsa_handle *h) { return Tables{h->d_cos, h->d_sin}; }
+int64_t nblk_cap(const qsa_handle *h) { return h->p.max_ctx / kBlock; }
+
+// Rows of one qsa_forward score sub-chunk.
+int64_t forward_rows(int32_t B, int64_t L, int64_t ncol) {
+    const size_t per_row = static_cast<size_t>(B) * static_cast<size_t>(ncol) * 4u;
+    int64_t rows = static_cast<int64_t>(kForwardScoreBytes / (per_row ? per_row : 1));
+    rows = (rows / 64) * 64;
+    if (rows < 64) rows = 64;
+    return rows < L ? rows : L;
+}
+
+int decode_splits(int32_t B) {
+    int s = (1024 + 2 * B - 1) / (2 * B);
+    return s < 1 ? 1 : (s > 32 ? 32 : s);
+}
+
+struct FwdLayout { size_t qrot, bidx, scores, total; int64_t rows, ncol; };
+FwdLayout forward_layout(const qsa_handle *h, int32_t B, int64_t L, int64_t q_offset) {
+    FwdLayout f{};
+    f.ncol = (q_offset + L + kBlock - 1) / kBlock;
+    f.rows = forward_rows(B, L, f.ncol);
+    f.qrot = 0;
+    f.bidx = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
+    f.scores = f.bidx + align_up(static_cast<size_t>(B) * L * h->p.budget_blocks * 4);
+    f.total = f.scores + align_up(static_cast<size_t>(B) * f.rows * f.ncol * 4);
+    return f;
+}
+
+struct DecLayout { size_t qrot, scores, bidx, part_o, part_ml, total; int64_t ncol; int nsplit; };
+DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
+    DecLayout d{};
+    d.ncol = ctx_bound / kBlock;
+    if (d.ncol < 1) d.ncol = 1;
+    d.nsplit = decode_splits(B);
+    d.qrot = 0;
+    d.scores = align_up(static_cast<size_t>(B) * kIdxHeads * kIdxDim * 2);
+    d.bidx = d.scores + align_up(static_cast<size_t>(B) * d.ncol * 4);
+    d.part_o = d.bidx + align_up(static_cast<size_t>(B) * h->p.budget_blocks * 4);
+    const size_t slots = static_cast<size_t>(B) * kKVHeads * d.nsplit * kGroup;
+    d.part_ml = d.part_o + align_up(slots * kHeadDim * 4);
+    d.total = d.part_ml + align_up(slots * 2 * 4);
+    return d;
+}
+
+qsa_status check_chunk(const qsa_handle *h, int32_t B, int64_t L, int64_t q_offset, bool aligned_offset) {
+    if (!h) return QSA_ERR_NULL;
+    if (B < 1 || L < 0 || q_offset < 0) return QSA_ERR_SHAPE;
+    if (aligned_offset && (q_offset % kBlock) != 0) return QSA_ERR_ALIGN;
+    if (q_offset + L > h->p.max_ctx) return QSA_ERR_CAPACITY;
+    return QSA_OK;
+}
+
+qsa_status check_ptrs(std::initializer_list<const void *> ptrs) {
+    for (const void *p : ptrs)
+        if (!p) return QSA_ERR_NULL;
+    for (const void *p : ptrs)
+        if (!aligned16(p)) return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void qsa_default_params(qsa_params *p) {
+    if (!p) return;
+    memset(p, 0, sizeof(*p));
+    p->n_q_heads = kQHeads;
+    p->n_kv_heads = kKVHeads;
+    p->head_dim = kHeadDim;
+    p->rope_dim = kRopeDim;
+    p->n_idx_heads = kIdxHeads;
+    p->idx_dim = kIdxDim;
+    p->idx_rope_dim = 64;
+    p->block = kBlock;
+    p->budget_blocks = kMaxBudget;
+    p->max_ctx = 262144;
+    p->rope_theta = 1e7;
+    p->yarn_factor = 1.0;
+    p->yarn_orig_ctx = 262144;
+}
+
+qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
+    if (!params || !out) return QSA_ERR_NULL;
+    *out = nullptr;
+    const qsa_params &p = *params;
+    if (p.n_q_heads != kQHeads || p.n_kv_heads != kKVHeads || p.head_dim != kHeadDim || p.rope_dim != kRopeDim ||
+        p.n_idx_heads != kIdxHeads || p.idx_dim != kIdxDim || p.idx_rope_dim != 64 || p.block != kBlock ||
+        p.reserved0 != 0)
+        return QSA_ERR_UNSUPPORTED;
+    if (p.budget_blocks < 1 || p.budget_blocks > kMaxBudget) return QSA_ERR_SHAPE;
+    if (p.max_ctx < kBlock || p.max_ctx % kBlock != 0 || p.max_ctx > (int64_t(1) << 30)) return QSA_ERR_SHAPE;
+    if (!(p.rope_theta > 1.0) || !isfinite(p.rope_theta)) return QSA_ERR_SHAPE;
+    if (!(p.yarn_factor >= 1.0) || !isfinite(p.yarn_factor)) return QSA_ERR_SHAPE;
+    if (p.yarn_factor > 1.0 && p.yarn_orig_ctx < 1) return QSA_ERR_SHAPE;
+
+    double inv[kPairs];
+    host_inv_freq(p.rope_theta, p.yarn_factor, p.yarn_orig_ctx, inv);
+    const size_t n = static_cast<size_t>(p.max_ctx) * kPairs;
+    std::vector<float> hc(n), hs(n);
+    host_rope_tables(inv, p.max_ctx, hc.data(), hs.data());
+
+    DeviceGuard guard(device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    qsa_handle *h = static_cast<qsa_handle *>(calloc(1, sizeof(qsa_handle)));
+    if (!h) return QSA_ERR_SHAPE;
+    h->p = p;
+    h->device = device;
+    double sigma = 1.0 / sqrt(static_cast<double>(kHeadDim));
+    if (p.yarn_factor > 1.0) {
+        const double m = 0.1 * log(p.yarn_factor) + 1.0;
+        sigma *= m * m;
+    }
+    h->sigma = static_cast<float>(sigma);
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&h->d_cos), n * sizeof(float));
+    if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->d_sin), n * sizeof(float));
+    if (e == hipSuccess) e = hipMemcpy(h->d_cos, hc.data(), n * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipMemcpy(h->d_sin, hs.data(), n * sizeof(float), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+        if (h->d_cos) (void)hipFree(h->d_cos);
+        if (h->d_sin) (void)hipFree(h->d_sin);
+        free(h);
+        return hip_fail(e);
+    }
+    *out = h;
+    return QSA_OK;
+}
+
+void qsa_destroy(qsa_handle *h) {
+    if (!h) return;
+    DeviceGuard guard(h->device);
+    if (h->d_cos) (void)hipFree(h->d_cos);
+    if (h->d_sin) (void)hipFree(h->d_sin);
+    free(h);
+}
+
+qsa_status qsa_get_params(const qsa_handle *h, qsa_params *out) {
+    if (!h || !out) return QSA_ERR_NULL;
+    *out = h->p;
+    return QSA_OK;
+}
+
+size_t qsa_workspace_size(const qsa_handle *h, int op, int32_t batch, int64_t len, int64_t q_offset) {
+    if (!h || batch < 1 || len < 0 || q_offset < 0) return 0;
+    switch (op) {
+    case QSA_OP_APPEND:
+    case QSA_OP_SELECT:
+    case QSA_OP_ATTEND:
+        return 0;
+    case QSA_OP_INDEX:
+        return align_up(static_cast<size_t>(batch) * len * kIdxHeads * kIdxDim * 2);
+    case QSA_OP_FORWARD:
+        return forward_layout(h, batch, len, q_offset).total;
+    case QSA_OP_DECODE:
+        return decode_layout(h, batch, q_offset).total;
+    default:
+        return 0;
+    }
+}
+
+qsa_status qsa_append(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                      const uint16_t *k, const uint16_t *v, const uint16_t *k_idx, uint16_t *k_cache,
+                      uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend) {
+    qsa_status s = check_chunk(h, B, L, q_offset, false);
+    if (s != QSA_OK) return s;
+    if ((s = check_ptrs({k, v, k_idx, k_cache, v_cache, kbar_cache, kpend})) != QSA_OK) return s;
+    if (L == 0) return QSA_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nblk_cap(h), k, v, k_idx, k_cache, v_cache,
+                                  kbar_cache, kpend, true, true);
+    if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_index(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                     const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *kbar_cache, uint16_t *kpend,
+                     float *scores, void *ws, size_t ws_bytes) {
+    qsa_status s = check_chunk(h, B, L, q_offset, true);
+    if (s != QSA_OK) return s;
+    if ((s = check_ptrs({q_idx, k_idx, kbar_cache, kpend, scores})) != QSA_OK) return s;
+    if (L == 0) return QSA_OK;
+    if ((s = check_ptrs({ws})) != QSA_OK) return s;
+    if (ws_bytes < qsa_workspace_size(h, QSA_OP_INDEX, B, L, q_offset)) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bf16_t *qrot = static_cast<bf16_t *>(ws);
+    const int64_t ncol = (q_offset + L + kBlock - 1) / kBlock;
+    hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nblk_cap(h), nullptr, nullptr, k_idx, nullptr,
+                                  nullptr, kbar_cache, kpend, false, true);
+    if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
+    if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
+    if (e == hipSuccess)
+        e = launch_indexer_scores(st, B, L, q_offset, ncol, nblk_cap(h), qrot, L * kIdxHeads * kIdxDim, kbar_cache,
+                                  scores, L * ncol, true);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                      const float *scores, int32_t *block_idx, void *ws, size_t ws_bytes) {
+    (void)ws;
+    (void)ws_bytes;
+    qsa_status s = check_chunk(h, B, L, q_offset, true);
+    if (s != QSA_OK) return s;
+    if ((s = check_ptrs({scores, block_idx})) != QSA_OK) return s;
+    if (L == 0) return QSA_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    const int64_t ncol = (q_offset + L + kBlock - 1) / kBlock;
+    const int budget = h->p.budget_blocks;
+    hipError_t e = launch_select(static_cast<hipStream_t>(stream), B, L, q_offset, nullptr, ncol, scores, L * ncol,
+                                 block_idx, L * budget, budget);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset, const uint16_t *q,
+                      const uint16_t *k, const uint16_t *v, uint16_t *k_cache, uint16_t *v_cache,
+                      const int32_t *block_idx, uint16_t *out, void *ws, size_t ws_bytes) {
+    (void)ws;
+    (void)ws_bytes;
+    qsa_status s = check_chunk(h, B, L, q_offset, true);
+    if (s != QSA_OK) return s;
+    if ((s = check_ptrs({q, k, v, k_cache, v_cache, block_idx, out})) != QSA_OK) return s;
+    if (L == 0) return QSA_OK;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nblk_cap(h), k, v, nullptr, k_cache, v_cache,
+                                  nullptr, nullptr, true, false);
+    if (e == hipSuccess)
+        e = launch_attend_prefill(tables(h), st, B, L, q_offset, nblk_cap(h), h->p.budget_blocks, h->sigma, q,
+                                  k_cache, v_cache, block_idx, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset, const uint16_t *q,
+                       const uint16_t *k, const uint16_t *v, const uint16_t *q_idx, const uint16_t *k_idx,
+                       uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend, uint16_t *out,
+                       int32_t *block_idx, void *ws, size_t ws_bytes) {
+    qsa_status s = check_chunk(h, B, L, q_offset, true);
+    if (s != QSA_OK) return s;
+    if ((s = check_ptrs({q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out})) != QSA_OK) return s;
+    if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
+    if (L == 0) return QSA_OK;
+    if ((s = check_ptrs({ws})) != QSA_OK) return s;
+    const FwdLayout f = forward_layout(h, B, L, q_offset);
+    if (ws_bytes < f.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
+    int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + f.bidx);
+    float *scores = reinterpret_cast<float *>(w + f.scores);
+    const int budget = h->p.budget_blocks;
+    const int64_t nbc = nblk_cap(h);
+
+    hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nbc, k, v, k_idx, k_cache, v_cache, kbar_cache,
+                                  kpend, true, true);
+    if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
+    if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
+    for (int64_t r0 = 0; r0 < L && e == hipSuccess; r0 += f.rows) {
+        const int64_t nr = (r0 + f.rows < L) ? f.rows : L - r0;
+        const int64_t pos0 = q_offset + r0;
+        e = launch_indexer_scores(st, B, nr, pos0, f.ncol, nbc, qrot + r0 * kIdxHeads * kIdxDim,
+                                  L * kIdxHeads * kIdxDim, kbar_cache, scores, f.rows * f.ncol, false);
+        if (e == hipSuccess)
+            e = launch_select(st, B, nr, pos0, nullptr, f.ncol, scores, f.rows * f.ncol, bidx + r0 * budget,
+                              L * budget, budget);
+    }
+    if (e == hipSuccess)
+        e = launch_attend_prefill(tables(h), st, B, L, q_offset, nbc, budget, h->sigma, q, k_cache, v_cache, bidx,
+                                  out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *q_idx,
+                      const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache,
+                      uint16_t *kpend, uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes) {
+    if (!h) return QSA_ERR_NULL;
+    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
+    qsa_status s = check_ptrs({cache_len, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, ws});
+    if (s != QSA_OK) return s;
+    if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
+    const DecLayout d = decode_layout(h, B, ctx_bound);
+    if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
+    float *scores = reinterpret_cast<float *>(w + d.scores);
+    int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + d.bidx);
+    float *part_o = reinterpret_cast<float *>(w + d.part_o);
+    float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
+    const int budget = h->p.budget_blocks;
+    const int64_t nbc = nblk_cap(h);
+
+    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, q_idx, k_cache, v_cache,
+                                        kbar_cache, kpend, qrot);
+    if (e == hipSuccess) e = launch_decode_scan(st, B, cache_len, ctx_bound, nbc, d.ncol, qrot, kbar_cache, scores);
+    if (e == hipSuccess)
+        e = launch_select(st, B, 1, ctx_bound, cache_len, d.ncol, scores, d.ncol, bidx, budget, budget);
+    if (e == hipSuccess)
+        e = launch_attend_decode(tables(h), st, B, cache_len, ctx_bound, nbc, budget, d.nsplit, h->sigma, q, k_cache, v_cache,
+                                 bidx, part_o, part_ml, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+const char *qsa_status_string(qsa_status s) {
+    switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_NULL: return "a required pointer is NULL";
+    case QSA_ERR_SHAPE: return "a size or count is out of range";
+    case QSA_ERR_UNSUPPORTED: return "head counts or dims other than the built ones";
+    case QSA_ERR_ALIGN: return "pointer not 16-byte aligned or q_offset not a multiple of 4";
+    case QSA_ERR_CAPACITY: return "positions beyond the cache capacity max_ctx";
+    case QSA_ERR_WORKSPACE: return "workspace smaller than qsa_workspace_size()";
+    case QSA_ERR_HIP: return "HIP runtime error (see qsa_last_hip_error)";
+    default: return "unknown status";
+    }
+}
+
+int qsa_last_hip_error(void) { return g_last_hip; }
+
+}  // extern "C"

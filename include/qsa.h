@@ -1,0 +1,225 @@
+/*
+ * qsa.h -- C ABI of the MI355X (gfx950) Qwen Sparse Attention layer library.
+ *
+ * One QSA layer has three stages:
+ *   1. an MQA indexer (4 query heads, 1 shared key head, dim 128) scores the
+ *      mean-pooled 4-token micro-blocks of the causal past,
+ *   2. each query keeps its top `budget` blocks (512 blocks = 2048 tokens),
+ *   3. GQA attention (24 query heads, 2 KV heads, dim 256, RoPE on the first 64
+ *      dims) runs over the selected blocks plus the query's own block.
+ *
+ * Sources (web pages on the Qwen3.8-Flash-Next release):
+ *   [PKR] discuss.pytorch.kr, "Qwen3.8-Flash-Next, 1/9의 학습 비용으로
+ *         Qwen3.7-Plus(397B-A17B) 수준에 도달한 125B-A6B 모델":
+ *         spec table (rows Qwen Sparse Attention, QSA 인덱서, QSA 예산);
+ *         section "QSA: 인덱서 자체의 비용을 줄이는 희소 어텐션" (pooling,
+ *         compression before RoPE, score I_ib, block-causal rule, budget,
+ *         always-included tail); section "100만 토큰까지 늘리기" (rope_parameters).
+ *   [LMF] llmfeed.kr, "Qwen 팀, 새 구조를 적용한 Qwen3.8-Flash-Next 공개 가중치로
+ *         출시", section "규모와 구조" (QSA bullet: shapes and budget).
+ *   [YaRN] Peng et al. 2023, NTK-by-parts frequency ramp and temperature.
+ *
+ * Conventions for every entry point below
+ *   - Pointers named q, k, v, q_idx, k_idx, *_cache, kpend, scores, block_idx,
+ *     out, ws are DEVICE pointers to caller-owned memory; the library never
+ *     allocates or frees them.  Every device pointer must be 16-byte aligned.
+ *   - bf16 means IEEE bfloat16 stored as uint16_t.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and is asynchronous: the call returns before the GPU finishes.  Nothing
+ *     synchronises the host.
+ *   - All arguments are checked on the host before anything is enqueued.  A
+ *     status other than QSA_OK means no kernel was launched and no buffer was
+ *     touched, except QSA_ERR_HIP, which reports a failed launch (the HIP code
+ *     is then available from qsa_last_hip_error()).  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Inputs must be finite; non-finite values are not detected.
+ *   - Calls that share a cache must be ordered (same stream or explicit
+ *     events); the handle itself is immutable and may be shared by threads.
+ *
+ * Token-major input layouts (per call, positions q_offset .. q_offset+L-1):
+ *   q      bf16 [B][L][24][256]     query heads
+ *   k, v   bf16 [B][L][2][256]      key / value heads
+ *   q_idx  bf16 [B][L][4][128]      indexer query heads
+ *   k_idx  bf16 [B][L][128]         indexer key (one shared head)
+ *   out    bf16 [B][L][24][256]     attention output (RNE from fp32)
+ *
+ * Caches (capacity max_ctx tokens per sequence; max_ctx is a multiple of 4):
+ *   k_cache    bf16 [B][2][max_ctx/4][8][4][32]  rotated keys; micro-block
+ *              `blk` of head g is 2 KiB at [b][g][blk]; inside it element
+ *              (token 4*blk+t, dim d) sits at [d/32][t][d%32].
+ *   v_cache    bf16 [B][2][max_ctx/4][256][4]    values; inside block `blk`
+ *              element (token 4*blk+t, dim d) sits at [d][t].
+ *   kbar_cache bf16 [B][max_ctx/4][128]          pooled, rotated indexer key
+ *              of every complete block.
+ *   kpend      bf16 [B][4][128]                  raw indexer keys of the
+ *              current incomplete block (slot = position % 4).
+ *
+ * Scores (qsa_index output) are fp32 [B][L][ncol], ncol = ceil((q_offset+L)/4):
+ *   entry (p, blk) = I_p,blk for blk < floor(p/4) (the candidates), else -1.
+ * Selections are int32 [B][L][budget]: the selected candidate blocks of each
+ *   query in ascending order, padded with -1.  The query's own block
+ *   floor(p/4) is never listed; it is always attended over 4*floor(p/4)..p.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_NULL = 1,         /* a required pointer is NULL */
+    QSA_ERR_SHAPE = 2,        /* a size or count is out of range */
+    QSA_ERR_UNSUPPORTED = 3,  /* head counts/dims other than the built ones */
+    QSA_ERR_ALIGN = 4,        /* pointer not 16-byte aligned, or q_offset % 4 != 0 */
+    QSA_ERR_CAPACITY = 5,     /* positions would reach beyond max_ctx */
+    QSA_ERR_WORKSPACE = 6,    /* ws_bytes smaller than qsa_workspace_size() */
+    QSA_ERR_HIP = 7           /* a HIP runtime call failed */
+} qsa_status;
+
+/* Layer parameters, fixed at handle creation.  The library is built for the
+ * shapes of [PKR] spec table / [LMF] "규모와 구조": 24 query heads, 2 KV heads,
+ * head dim 256, rotary dim 64; indexer 4 heads x 128 with rotary dim 64; micro-
+ * block 4.  Other values return QSA_ERR_UNSUPPORTED.  budget_blocks is 1..512
+ * ([PKR] spec table row QSA 예산).  The rotary frequencies are
+ * rope_theta^(-2j/64), j = 0..31 ([PKR] "100만 토큰까지 늘리기": theta 1e7,
+ * partial factor 0.25); yarn_factor > 1 applies the [YaRN] NTK-by-parts ramp
+ * (alpha 1, beta 32) over yarn_orig_ctx and multiplies the attention logits by
+ * (0.1 ln(yarn_factor) + 1)^2. */
+typedef struct qsa_params {
+    int32_t n_q_heads;      /* 24 */
+    int32_t n_kv_heads;     /* 2 */
+    int32_t head_dim;       /* 256 */
+    int32_t rope_dim;       /* 64 */
+    int32_t n_idx_heads;    /* 4 */
+    int32_t idx_dim;        /* 128 */
+    int32_t idx_rope_dim;   /* 64 */
+    int32_t block;          /* 4 */
+    int32_t budget_blocks;  /* 1..512 */
+    int32_t reserved0;      /* must be 0 */
+    int64_t max_ctx;        /* cache capacity in tokens, multiple of 4, >= 4 */
+    double  rope_theta;     /* 1e7 */
+    double  yarn_factor;    /* 1.0 = off, else > 1 */
+    int64_t yarn_orig_ctx;  /* 262144 */
+} qsa_params;
+
+typedef struct qsa_handle qsa_handle;
+
+/* Operation codes for qsa_workspace_size. */
+enum { QSA_OP_APPEND = 0, QSA_OP_INDEX = 1, QSA_OP_SELECT = 2, QSA_OP_ATTEND = 3,
+       QSA_OP_FORWARD = 4, QSA_OP_DECODE = 5 };
+
+/* Fill *p with the layer's published shapes, budget 512, max_ctx 262144,
+ * theta 1e7, no YaRN (factor 1), yarn_orig_ctx 262144.  Host only. */
+void qsa_default_params(qsa_params *p);
+
+/* Validate *params, build the fp32 cos/sin tables of positions 0..max_ctx-1 on
+ * the host (fp64 libm cos/sin of position * frequency, rounded once to fp32)
+ * and upload them to `device`.  The handle owns that device memory (2 x
+ * max_ctx x 32 x 4 bytes) until qsa_destroy.  Returns QSA_ERR_NULL,
+ * QSA_ERR_UNSUPPORTED, QSA_ERR_SHAPE or QSA_ERR_HIP on failure (*out = NULL). */
+qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out);
+
+/* Release the handle and its tables.  NULL is a no-op.  Not stream-ordered:
+ * the caller must make sure no enqueued call still uses the handle. */
+void qsa_destroy(qsa_handle *h);
+
+/* Copy the handle's parameters to *out.  Host only. */
+qsa_status qsa_get_params(const qsa_handle *h, qsa_params *out);
+
+/* Workspace bytes `op` needs for `batch` sequences and `len` new tokens at
+ * `q_offset` (for QSA_OP_DECODE: len = 1 and q_offset = ctx_bound, the host
+ * upper bound of cache_len).  0 for invalid arguments.  Host only. */
+size_t qsa_workspace_size(const qsa_handle *h, int op, int32_t batch, int64_t len, int64_t q_offset);
+
+/* Cache fill (the keys' half of the prologue): for positions
+ * t = q_offset .. q_offset+L-1 of each sequence, rotate k at t into k_cache,
+ * copy v into v_cache, and push raw k_idx into the micro-block pool: every
+ * block that becomes complete gets k̄ = bf16(rotate(mean of its 4 raw keys,
+ * 4*blk)) in kbar_cache ([PKR] "QSA: ..." -- mean pooling, compression before
+ * the positional encoding, block-start position); raw keys of a trailing
+ * incomplete block are left in kpend.  Blocks that were incomplete before the
+ * call take their earlier tokens from kpend.  Rotations are fp32 with every
+ * product and sum rounded separately, then bf16 RNE.
+ * Requires q_offset + L <= max_ctx; q_offset need not be a multiple of 4.
+ * ws may be NULL (needs none). */
+qsa_status qsa_append(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                      const uint16_t *k, const uint16_t *v, const uint16_t *k_idx,
+                      uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend);
+
+/* Indexer ([PKR] "QSA: ...", equation I_ib = sum_h ReLU(<q_i^h, k̄_b>)):
+ * appends the chunk's indexer keys (as qsa_append does for k_idx only), rotates
+ * q_idx at its positions, and writes the score matrix `scores` (layout above)
+ * for queries q_offset .. q_offset+L-1 against every complete block before the
+ * query's own block (block-causal: only fully observed blocks are scored).
+ * Scores accumulate in fp32 from bf16 operands (MFMA).  q_offset % 4 == 0.
+ * ws: qsa_workspace_size(QSA_OP_INDEX) bytes. */
+qsa_status qsa_index(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                     const uint16_t *q_idx, const uint16_t *k_idx,
+                     uint16_t *kbar_cache, uint16_t *kpend, float *scores,
+                     void *ws, size_t ws_bytes);
+
+/* Selection ([PKR] "QSA: ...": K = 2048 tokens, r = 4, up to 512 blocks per
+ * query): for each query p, the min(budget, floor(p/4)) candidates with the
+ * largest scores, ties broken toward the larger block index, written ascending
+ * and padded with -1 into block_idx [B][L][budget].  Reads `scores` as written
+ * by qsa_index for the same (B, L, q_offset).  q_offset % 4 == 0.
+ * ws: qsa_workspace_size(QSA_OP_SELECT) bytes (may be 0). */
+qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                      const float *scores, int32_t *block_idx, void *ws, size_t ws_bytes);
+
+/* Sparse core attention ([PKR] "QSA: ...", sparse core attention over the
+ * selected blocks; the tail of the last incomplete block is always included):
+ * writes the chunk's rotated keys and values into the caches (as qsa_append
+ * does for k and v), then for each query p and head h (KV head h / 12) computes
+ * softmax(sigma * q~_h . K~^T) V over the tokens of the blocks in
+ * block_idx[p] plus tokens 4*floor(p/4) .. p, with sigma = 1/16 (times the YaRN
+ * temperature).  Scores and softmax in fp32, P rounded to bf16 for the PV
+ * product, output bf16.  q_offset % 4 == 0.
+ * ws: qsa_workspace_size(QSA_OP_ATTEND) bytes (may be 0). */
+qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      uint16_t *k_cache, uint16_t *v_cache,
+                      const int32_t *block_idx, uint16_t *out, void *ws, size_t ws_bytes);
+
+/* Prefill (or one prefill chunk): qsa_append + indexer + selection + sparse
+ * attention for queries q_offset .. q_offset+L-1, without handing the score
+ * matrix to the caller.  block_idx may be NULL; when given it receives the
+ * selection ([B][L][budget]).  Earlier chunks must already be in the caches.
+ * q_offset % 4 == 0.  ws: qsa_workspace_size(QSA_OP_FORWARD) bytes. */
+qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                       const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                       const uint16_t *q_idx, const uint16_t *k_idx,
+                       uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
+                       uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes);
+
+/* Decode one new token per sequence.  cache_len is a DEVICE int32 [B]: sequence
+ * b holds positions 0..cache_len[b]-1 in its caches and the new token sits at
+ * p = cache_len[b].  The call appends the new token (k, v, k_idx of shape
+ * [B][1][...]), scores its query against every complete block before its own,
+ * selects the top budget blocks and attends (same rules as qsa_forward).
+ * ctx_bound is a host-side bound: cache_len[b] <= ctx_bound < max_ctx for all b
+ * (grids are sized by it).  cache_len is not modified; the caller advances it.
+ * ws: qsa_workspace_size(QSA_OP_DECODE, B, 1, ctx_bound) bytes. */
+qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                      int64_t ctx_bound,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                      const uint16_t *q_idx, const uint16_t *k_idx,
+                      uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
+                      uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes);
+
+/* Static string for a status code. */
+const char *qsa_status_string(qsa_status s);
+
+/* HIP error code of the last QSA_ERR_HIP returned on this thread (0 if none). */
+int qsa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

@@ -266,3 +266,32 @@ def decode_inputs(w: Workload, device="cpu", ctx: Optional[int] = None, batch: O
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Raw bf16 bit patterns of a tensor as a host uint16 array (no arithmetic)."""
     return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def score_rows(seed: int, B: int, L: int, q_offset: int, tie_mode: str = "mixed") -> np.ndarray:
+    """Seeded fp32 score matrices [B][L][ceil((q_offset+L)/4)] for testing selection alone.
+
+    Candidate entries (block < floor(p/4)) are >= +0; the rest hold -1.
+    tie_mode: 'float'  -- continuous values (no ties);
+              'coarse' -- multiples of 0.25 in [0, 8] (many exact ties);
+              'zeros'  -- mostly +0 with a few positive values (ties at zero);
+              'mixed'  -- rows cycle through the three.
+    """
+    rng = np.random.default_rng(_seed(seed, 7, B, L, q_offset))
+    ncol = (q_offset + L + BLOCK - 1) // BLOCK
+    out = np.full((B, L, ncol), -1.0, dtype=np.float32)
+    modes = ["float", "coarse", "zeros"]
+    for b in range(B):
+        for i in range(L):
+            o = (q_offset + i) // BLOCK
+            if o == 0:
+                continue
+            mode = modes[(b * L + i) % 3] if tie_mode == "mixed" else tie_mode
+            if mode == "float":
+                v = np.abs(rng.standard_normal(o)).astype(np.float32) * 10
+            elif mode == "coarse":
+                v = rng.integers(0, 33, o).astype(np.float32) * 0.25
+            else:
+                v = np.where(rng.random(o) < 0.05, rng.random(o) * 5, 0.0).astype(np.float32)
+            out[b, i, :o] = v
+    return out

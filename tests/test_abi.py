@@ -1,0 +1,65 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/qsa.h declares, and rejects bad arguments on the host before any HIP
+call (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_qsa_amd as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(Q.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = Q.lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_default_params_are_the_layer_shapes():
+    p = Q.default_params()
+    assert (p.n_q_heads, p.n_kv_heads, p.head_dim, p.rope_dim) == (24, 2, 256, 64)
+    assert (p.n_idx_heads, p.idx_dim, p.idx_rope_dim, p.block) == (4, 128, 64, 4)
+    assert p.budget_blocks == 512 and p.rope_theta == 1e7 and p.yarn_orig_ctx == 262144
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_q_heads", 32, 3), ("head_dim", 128, 3), ("block", 8, 3), ("reserved0", 1, 3),
+    ("budget_blocks", 0, 2), ("budget_blocks", 513, 2), ("max_ctx", 6, 2), ("max_ctx", 0, 2),
+    ("yarn_factor", 0.5, 2), ("rope_theta", 0.0, 2)])
+def test_create_rejects_bad_params_on_host(field, value, status):
+    p = Q.default_params(**{field: value})
+    h = ctypes.c_void_p(123)
+    assert Q.lib().qsa_create(ctypes.byref(p), 0, ctypes.byref(h)) == status
+    assert h.value is None
+
+
+def test_null_handle_and_status_strings():
+    lib = Q.lib()
+    assert lib.qsa_create(None, 0, None) == 1
+    assert lib.qsa_workspace_size(None, 4, 1, 10, 0) == 0
+    assert lib.qsa_append(None, None, 1, 4, 0, *([None] * 7)) == 1
+    assert lib.qsa_forward(None, None, 1, 4, 0, *([None] * 12), 0) == 1
+    assert lib.qsa_decode(None, None, 1, None, 0, *([None] * 12), 0) == 1
+    for s in range(8):
+        assert Q.qsa_status_string(s)
+    assert Q.qsa_last_hip_error() == 0
+    lib.qsa_destroy(None)
+
+
+def test_no_cpu_fallback_in_binding():
+    src = open(os.path.join(ROOT, "block_sparse_long_qsa_amd", "__init__.py")).read()
+    assert "oracle" not in src and "import synth" not in src

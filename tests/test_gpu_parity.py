@@ -1,0 +1,301 @@
+"""Parity of the HIP library against the CPU oracle, element by element, on
+seeded synthetic inputs small enough for the oracle to finish in seconds but
+spanning several tiles of every kernel and a ragged tail.  All calls go
+through the C ABI (ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_qsa_amd as Q
+import oracle as O
+import synth
+from helpers import (bits, check_out, check_scores, check_selection, f32, kcache_tokens, oracle_layer,
+                     vcache_tokens)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _to(x):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+
+
+def _prefill(w, L=None, B=None):
+    x = synth.prefill_inputs(w, "cpu", seq_len=L, batch=B)
+    return x, _to(x)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    Q.lib()          # fails loudly if libqsa.so is missing
+    yield
+    torch.cuda.synchronize()
+
+
+def _forward(h, xd, B, L, q_offset=0, caches=None, chunks=None):
+    c = caches if caches is not None else Q.alloc_caches(h, B)
+    out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bidx = torch.empty((B, L, h.budget), dtype=torch.int32, device=DEV)
+    spans = chunks or [(0, L)]
+    for s0, s1 in spans:
+        n = s1 - s0
+        ws = Q.workspace(h, Q.QSA_OP_FORWARD, B, n, q_offset + s0)
+        sl = lambda t: t[:, s0:s1].contiguous()
+        o = torch.empty((B, n, 24, 256), dtype=torch.bfloat16, device=DEV)
+        bi = torch.empty((B, n, h.budget), dtype=torch.int32, device=DEV)
+        Q.qsa_forward(h, B, n, q_offset + s0, sl(xd["q"]), sl(xd["k"]), sl(xd["v"]), sl(xd["q_idx"]),
+                      sl(xd["k_idx"]), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], o, bi, ws)
+        out[:, s0:s1] = o
+        bidx[:, s0:s1] = bi
+    torch.cuda.synchronize()
+    return out, bidx, c
+
+
+# ---------------------------------------------------------------- prologue
+@pytest.mark.parametrize("yarn", [1.0, 4.0])
+def test_append_caches_bit_exact(yarn):
+    """Rotated K~, transposed V, pooled k̄ and pending raw keys, appended in
+    three calls at unaligned offsets, equal the oracle's bf16 values bit for bit."""
+    B, L = 2, 203
+    w = synth.Workload("t", "prefill", B, L, 64, 4, "random", 21)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=256, budget_blocks=64, yarn_factor=yarn)
+    c = Q.alloc_caches(h, B)
+    for s0, s1 in [(0, 33), (33, 34), (34, 203)]:
+        sl = lambda t: t[:, s0:s1].contiguous()
+        Q.qsa_append(h, B, s1 - s0, s0, sl(xd["k"]), sl(xd["v"]), sl(xd["k_idx"]), c["k_cache"], c["v_cache"],
+                     c["kbar_cache"], c["kpend"])
+    torch.cuda.synchronize()
+    p = O.Params(yarn_factor=yarn)
+    kt = kcache_tokens(c["k_cache"])
+    vt = vcache_tokens(c["v_cache"])
+    pos = np.arange(L)
+    for b in range(B):
+        ref_k = O.f32_to_bf16_bits(O.core_rotate(bits(x["k"][b]), pos, p))          # [L][2][256]
+        got_k = bits(kt[b, :, :L].permute(1, 0, 2))
+        assert np.array_equal(got_k, ref_k)
+        assert np.array_equal(bits(vt[b, :, :L].permute(1, 0, 2)), bits(x["v"][b]))
+        ref_kbar = O.f32_to_bf16_bits(O.indexer_keys(bits(x["k_idx"][b]), p))      # [50][128]
+        assert np.array_equal(bits(c["kbar_cache"][b, :L // 4]), ref_kbar)
+        assert np.array_equal(bits(c["kpend"][b, :L % 4]), bits(x["k_idx"][b, (L // 4) * 4:]))
+
+
+# ---------------------------------------------------------------- indexer
+@pytest.mark.parametrize("B,L,q_offset", [(1, 2500, 0), (2, 333, 0), (1, 640, 1024)])
+def test_index_scores(B, L, q_offset):
+    """qsa_index scores vs the oracle's fp64 scores; -1 on every non-candidate."""
+    w = synth.Workload("t", "prefill", B, q_offset + L, 64, 6, "random", 22)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=4096, budget_blocks=64)
+    c = Q.alloc_caches(h, B)
+    if q_offset:
+        Q.qsa_append(h, B, q_offset, 0, xd["k"][:, :q_offset].contiguous(), xd["v"][:, :q_offset].contiguous(),
+                     xd["k_idx"][:, :q_offset].contiguous(), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    ncol = (q_offset + L + 3) // 4
+    scores = torch.empty((B, L, ncol), dtype=torch.float32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_INDEX, B, L, q_offset)
+    sl = lambda t: t[:, q_offset:q_offset + L].contiguous()
+    Q.qsa_index(h, B, L, q_offset, sl(xd["q_idx"]), sl(xd["k_idx"]), c["kbar_cache"], c["kpend"], scores, ws)
+    torch.cuda.synchronize()
+    s = f32(scores)
+    p = O.Params()
+    for b in range(B):
+        kbar = O.indexer_keys(bits(x["k_idx"][b]), p)
+        qt = O.indexer_queries(bits(x["q_idx"][b, q_offset:]), np.arange(q_offset, q_offset + L), p)
+        for i in range(L):
+            o = (q_offset + i) // 4
+            check_scores(s[b, i, :o], O.block_scores(qt[i], kbar[:o]), "b%d row %d" % (b, i))
+            assert np.all(s[b, i, o:] == -1.0)
+
+
+# ---------------------------------------------------------------- select
+@pytest.mark.parametrize("mode", ["float", "coarse", "zeros", "mixed"])
+@pytest.mark.parametrize("budget", [1, 7, 64, 512])
+def test_select_bit_exact(mode, budget):
+    """qsa_select on seeded score rows (with many exact ties) equals the oracle's
+    (score desc, block desc) top-k exactly."""
+    B, L, q_offset = 2, 300, 2400
+    s = synth.score_rows(31 + budget, B, L, q_offset, mode)
+    h = Q.Handle(max_ctx=4096, budget_blocks=budget)
+    bidx = torch.empty((B, L, budget), dtype=torch.int32, device=DEV)
+    Q.qsa_select(h, B, L, q_offset, torch.from_numpy(s).to(DEV), bidx)
+    torch.cuda.synchronize()
+    got = bidx.cpu().numpy()
+    for b in range(B):
+        for i in range(L):
+            o = (q_offset + i) // 4
+            ref = O.select_blocks(s[b, i, :o].astype(np.float64), budget)
+            assert np.array_equal(got[b, i], ref), (mode, budget, b, i)
+
+
+def test_select_small_rows():
+    """Rows with fewer candidates than the budget (including none) take them all."""
+    B, L = 1, 40
+    s = synth.score_rows(5, B, L, 0, "coarse")
+    h = Q.Handle(max_ctx=64, budget_blocks=8)
+    bidx = torch.empty((B, L, 8), dtype=torch.int32, device=DEV)
+    Q.qsa_select(h, B, L, 0, torch.from_numpy(s).to(DEV), bidx)
+    torch.cuda.synchronize()
+    got = bidx.cpu().numpy()
+    for i in range(L):
+        assert np.array_equal(got[0, i], O.select_blocks(s[0, i, :i // 4].astype(np.float64), 8))
+
+
+# ---------------------------------------------------------------- attention
+def test_attend_with_oracle_selection():
+    """qsa_attend over the oracle's own selection vs the oracle's output rows."""
+    B, L, budget = 1, 700, 16
+    w = synth.Workload("t", "prefill", B, L, budget, 4, "random", 23)
+    x, xd = _prefill(w)
+    p = O.Params(budget=budget)
+    rows = np.arange(L)
+    ref, sel, _ = O.prefill_rows(*(bits(x[n][0]) for n in ("q", "k", "v", "q_idx", "k_idx")), rows, p)
+    h = Q.Handle(max_ctx=1024, budget_blocks=budget)
+    c = Q.alloc_caches(h, B)
+    out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    Q.qsa_attend(h, B, L, 0, xd["q"], xd["k"], xd["v"], c["k_cache"], c["v_cache"],
+                 torch.from_numpy(sel[None]).to(DEV), out)
+    torch.cuda.synchronize()
+    check_out(f32(out[0]), ref, "attend")
+
+
+# ---------------------------------------------------------------- forward
+def _check_forward(x, out, bidx, p, rows, seqs=(0,), q_offset=0):
+    n_swapped = 0
+    for b in seqs:
+        lay = oracle_layer(x, b, p)
+        for i in rows:
+            pos = q_offset + int(i)
+            ref, sel, sc = lay.row(pos, bits(x["q"][b, i]), bits(x["q_idx"][b, i]))
+            n_swapped += check_selection(bidx[b, i], sel, sc, p.budget, pos // 4, "b%d row %d" % (b, i))
+            check_out(out[b, i], ref, "b%d row %d" % (b, i))
+    return n_swapped
+
+
+def test_forward_prefill_1k_all_rows():
+    """The small prefill workload (L=1024, budget 64, 8 needles): every row."""
+    w = synth.WORKLOADS["prefill_1k"]
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=1024, budget_blocks=w.budget)
+    out, bidx, _ = _forward(h, xd, 1, w.seq_len)
+    _check_forward(x, f32(out), bidx.cpu().numpy(), O.Params(budget=w.budget), range(w.seq_len))
+    # planted needles are selected by their probes
+    plan = x["needles"][0]
+    bi = bidx.cpu().numpy()[0]
+    for n, blk in enumerate(plan.blocks):
+        for pr in plan.probes[n]:
+            assert blk in bi[pr]
+
+
+def test_forward_ragged_batch2():
+    B, L, budget = 2, 1027, 40
+    w = synth.Workload("t", "prefill", B, L, budget, 5, "random", 24)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    out, bidx, c = _forward(h, xd, B, L)
+    rows = list(range(0, 12)) + list(range(150, 170)) + list(range(L - 40, L))
+    _check_forward(x, f32(out), bidx.cpu().numpy(), O.Params(budget=budget), rows, seqs=(0, 1))
+    # the trailing incomplete block's raw keys are pending
+    assert np.array_equal(bits(c["kpend"][:, :L % 4]), bits(x["k_idx"][:, (L // 4) * 4:]))
+
+
+def test_forward_chunked_equals_one_shot():
+    """Chunked prefill (chunk starts multiple of 4) is bit-identical to one shot."""
+    B, L, budget = 1, 2048, 64
+    w = synth.Workload("t", "prefill", B, L, budget, 8, "even", 25)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    o1, b1, _ = _forward(h, xd, B, L)
+    o2, b2, _ = _forward(h, xd, B, L, chunks=[(0, 512), (512, 1300), (1300, 2048)])
+    assert torch.equal(b1, b2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    _check_forward(x, f32(o2), b2.cpu().numpy(), O.Params(budget=budget), [511, 512, 513, 1299, 1300, 2047])
+
+
+def test_forward_deterministic():
+    B, L, budget = 1, 1500, 100
+    w = synth.Workload("t", "prefill", B, L, budget, 4, "random", 26)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=1536, budget_blocks=budget)
+    o1, b1, _ = _forward(h, xd, B, L)
+    o2, b2, _ = _forward(h, xd, B, L)
+    assert torch.equal(b1, b2) and torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_forward_yarn_small():
+    B, L, budget = 1, 900, 32
+    w = synth.Workload("t", "prefill", B, L, budget, 4, "random", 27, yarn_factor=4.0)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=1024, budget_blocks=budget, yarn_factor=4.0)
+    out, bidx, _ = _forward(h, xd, B, L)
+    _check_forward(x, f32(out), bidx.cpu().numpy(), O.Params(budget=budget, yarn_factor=4.0),
+                   list(range(0, 8)) + list(range(800, 900)))
+
+
+# ---------------------------------------------------------------- decode
+def _decode_setup(w, ctx_per_seq, h):
+    """Caches filled by qsa_append to each sequence's own length, then one decode step."""
+    B = len(ctx_per_seq)
+    x = synth.decode_inputs(w, "cpu", ctx=max(ctx_per_seq), batch=B)
+    xd = _to(x)
+    c = Q.alloc_caches(h, B)
+    for b, n in enumerate(ctx_per_seq):
+        sl = lambda t: t[b:b + 1, :n].contiguous()
+        cs = {k: v[b:b + 1] for k, v in c.items()}
+        Q.qsa_append(h, 1, n, 0, sl(xd["k"]), sl(xd["v"]), sl(xd["k_idx"]), cs["k_cache"], cs["v_cache"],
+                     cs["kbar_cache"], cs["kpend"])
+    # the new token of sequence b sits at position n_b: take its k/v/k_idx from that row
+    new = {n: torch.stack([xd[n][b, ctx_per_seq[b]] for b in range(B)])[:, None].contiguous()
+           for n in ("k", "v", "k_idx")}
+    cache_len = torch.tensor(ctx_per_seq, dtype=torch.int32, device=DEV)
+    out = torch.empty((B, 1, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bidx = torch.empty((B, 1, h.budget), dtype=torch.int32, device=DEV)
+    bound = max(ctx_per_seq)
+    ws = Q.workspace(h, Q.QSA_OP_DECODE, B, 1, bound)
+    Q.qsa_decode(h, B, cache_len, bound, xd["q"], new["k"], new["v"], xd["q_idx"], new["k_idx"], c["k_cache"],
+                 c["v_cache"], c["kbar_cache"], c["kpend"], out, bidx, ws)
+    torch.cuda.synchronize()
+    return x, out, bidx, c
+
+
+def test_decode_small_ragged_lengths():
+    budget = 48
+    lens = [1500, 3, 0, 1201, 1202, 1203, 700, 257]
+    w = synth.Workload("t", "decode", len(lens), max(lens), budget, 6, "random", 28)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    x, out, bidx, c = _decode_setup(w, lens, h)
+    p = O.Params(budget=budget)
+    o = f32(out)
+    bi = bidx.cpu().numpy()
+    for b, n in enumerate(lens):
+        lay = oracle_layer(x, b, p, n_keys=n + 1)
+        ref, sel, sc = lay.row(n, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
+        check_selection(bi[b, 0], sel, sc, budget, n // 4, "seq %d" % b)
+        check_out(o[b, 0], ref, "seq %d" % b)
+        # the appended token and, for completed blocks, its pooled key are in the caches
+        if n % 4 == 3:
+            ref_kbar = O.f32_to_bf16_bits(O.indexer_keys(bits(x["k_idx"][b, :n + 1]), p))
+            assert np.array_equal(bits(c["kbar_cache"][b, n // 4]), ref_kbar[n // 4])
+
+
+def test_decode_matches_prefill_row():
+    """Decode at p and prefill row p (same n+1 tokens, same query) both meet the
+    oracle's row p, and agree with each other."""
+    budget, n = 64, 1403
+    w = synth.Workload("t", "decode", 1, n, budget, 6, "random", 29)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    x, out_d, bidx_d, _ = _decode_setup(w, [n], h)
+    xp = {k: x[k][:, :n + 1].clone() for k in ("k", "v", "k_idx")}
+    xp["q"] = torch.zeros((1, n + 1, 24, 256), dtype=torch.bfloat16)
+    xp["q_idx"] = torch.zeros((1, n + 1, 4, 128), dtype=torch.bfloat16)
+    xp["q"][:, n] = x["q"][:, 0]
+    xp["q_idx"][:, n] = x["q_idx"][:, 0]
+    out_p, bidx_p, _ = _forward(h, _to(xp), 1, n + 1)
+    p = O.Params(budget=budget)
+    ref, sel, sc = oracle_layer(x, 0, p, n_keys=n + 1).row(n, bits(x["q"][0, 0]), bits(x["q_idx"][0, 0]))
+    for name, o, bi in (("decode", out_d[0, 0], bidx_d[0, 0]), ("prefill", out_p[0, n], bidx_p[0, n])):
+        check_selection(bi.cpu().numpy(), sel, sc, budget, n // 4, name)
+        check_out(f32(o), ref, name)
+    check_out(f32(out_d[0, 0]), f32(out_p[0, n]).astype(np.float64), "decode vs prefill")
