@@ -17,14 +17,14 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqsa.so")
 
-QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE = range(6)
+QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE, QSA_OP_INDEX_SELECT = range(7)
 
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPPORTED", 4: "QSA_ERR_ALIGN",
           5: "QSA_ERR_CAPACITY", 6: "QSA_ERR_WORKSPACE", 7: "QSA_ERR_HIP"}
 
 # The C entry points (kept in step with include/qsa.h).
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
-           "qsa_append", "qsa_index", "qsa_select", "qsa_attend", "qsa_forward", "qsa_decode",
+           "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
            "qsa_status_string", "qsa_last_hip_error"]
 
 
@@ -69,11 +69,13 @@ def lib() -> ctypes.CDLL:
     L.qsa_workspace_size.restype = sz
     L.qsa_append.argtypes = [vp, vp, i32, i64, i64] + [vp] * 7
     L.qsa_append.restype = ctypes.c_int
-    L.qsa_index.argtypes = [vp, vp, i32, i64, i64] + [vp] * 6 + [sz]
+    L.qsa_index.argtypes = [vp, vp, i32, i64, i64] + [vp] * 4 + [sz]
     L.qsa_index.restype = ctypes.c_int
-    L.qsa_select.argtypes = [vp, vp, i32, i64, i64, vp, vp, vp, sz]
+    L.qsa_select.argtypes = [vp, vp, i32, i64, i64, vp, vp]
     L.qsa_select.restype = ctypes.c_int
-    L.qsa_attend.argtypes = [vp, vp, i32, i64, i64] + [vp] * 8 + [sz]
+    L.qsa_index_select.argtypes = [vp, vp, i32, i64, i64] + [vp] * 4 + [sz]
+    L.qsa_index_select.restype = ctypes.c_int
+    L.qsa_attend.argtypes = [vp, vp, i32, i64, i64] + [vp] * 5
     L.qsa_attend.restype = ctypes.c_int
     L.qsa_forward.argtypes = [vp, vp, i32, i64, i64] + [vp] * 12 + [sz]
     L.qsa_forward.restype = ctypes.c_int
@@ -104,6 +106,10 @@ def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
 
 def _bf(t, name):
     return _ptr(t, torch.bfloat16, name)
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream=None):
@@ -191,23 +197,26 @@ def qsa_append(h, B, L, q_offset, k, v, k_idx, k_cache, v_cache, kbar_cache, kpe
                             _bf(kpend, "kpend")), "qsa_append")
 
 
-def qsa_index(h, B, L, q_offset, q_idx, k_idx, kbar_cache, kpend, scores, ws, stream=None):
-    _check(lib().qsa_index(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
-                           _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"), _ptr(scores, torch.float32, "scores"),
-                           _ptr(ws, None, "ws"), ws.numel() * ws.element_size()), "qsa_index")
+def qsa_index(h, B, L, q_offset, q_idx, kbar_cache, scores, ws, stream=None):
+    _check(lib().qsa_index(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"), _bf(kbar_cache, "kbar_cache"),
+                           _ptr(scores, torch.float32, "scores"), _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_index")
 
 
-def qsa_select(h, B, L, q_offset, scores, block_idx, ws=None, stream=None):
+def qsa_select(h, B, L, q_offset, scores, block_idx, stream=None):
     _check(lib().qsa_select(h.ptr, _stream(stream), B, L, q_offset, _ptr(scores, torch.float32, "scores"),
-                            _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
-                            0 if ws is None else ws.numel() * ws.element_size()), "qsa_select")
+                            _ptr(block_idx, torch.int32, "block_idx")), "qsa_select")
 
 
-def qsa_attend(h, B, L, q_offset, q, k, v, k_cache, v_cache, block_idx, out, ws=None, stream=None):
-    _check(lib().qsa_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
-                            _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _ptr(block_idx, torch.int32, "block_idx"),
-                            _bf(out, "out"), _ptr(ws, None, "ws"),
-                            0 if ws is None else ws.numel() * ws.element_size()), "qsa_attend")
+def qsa_index_select(h, B, L, q_offset, q_idx, kbar_cache, block_idx, ws, stream=None):
+    _check(lib().qsa_index_select(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"),
+                                  _bf(kbar_cache, "kbar_cache"), _ptr(block_idx, torch.int32, "block_idx"),
+                                  _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_index_select")
+
+
+def qsa_attend(h, B, L, q_offset, q, k_cache, v_cache, block_idx, out, stream=None):
+    _check(lib().qsa_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q"), _bf(k_cache, "k_cache"),
+                            _bf(v_cache, "v_cache"), _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out")),
+           "qsa_attend")
 
 
 def qsa_forward(h, B, L, q_offset, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, block_idx, ws,
@@ -216,7 +225,7 @@ def qsa_forward(h, B, L, q_offset, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar
                              _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"), _bf(k_cache, "k_cache"),
                              _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"),
                              _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
-                             ws.numel() * ws.element_size()), "qsa_forward")
+                             _nbytes(ws)), "qsa_forward")
 
 
 def qsa_decode(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out,
@@ -225,7 +234,7 @@ def qsa_decode(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cac
                             _bf(q, "q"), _bf(k, "k"), _bf(v, "v"), _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
                             _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
                             _bf(kpend, "kpend"), _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"),
-                            _ptr(ws, None, "ws"), ws.numel() * ws.element_size()), "qsa_decode")
+                            _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_decode")
 
 
 def qsa_status_string(status: int) -> str:

@@ -94,14 +94,15 @@ int decode_splits(int32_t B) {
     return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
-struct FwdLayout { size_t qrot, bidx, scores, total; int64_t rows, ncol; };
-FwdLayout forward_layout(const qsa_handle *h, int32_t B, int64_t L, int64_t q_offset) {
-    FwdLayout f{};
+// Workspace of the fused index + select stage: rotated indexer queries, then
+// the score slice of one query sub-chunk (never the whole causal matrix).
+struct IdxSelLayout { size_t qrot, scores, total; int64_t rows, ncol; };
+IdxSelLayout index_select_layout(int32_t B, int64_t L, int64_t q_offset) {
+    IdxSelLayout f{};
     f.ncol = (q_offset + L + kBlock - 1) / kBlock;
     f.rows = forward_rows(B, L, f.ncol);
     f.qrot = 0;
-    f.bidx = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
-    f.scores = f.bidx + align_up(static_cast<size_t>(B) * L * h->p.budget_blocks * 4);
+    f.scores = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
     f.total = f.scores + align_up(static_cast<size_t>(B) * f.rows * f.ncol * 4);
     return f;
 }
@@ -120,6 +121,25 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     d.part_ml = d.part_o + align_up(slots * kHeadDim * 4);
     d.total = d.part_ml + align_up(slots * 2 * 4);
     return d;
+}
+
+hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
+                            const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *bidx, char *w,
+                            const IdxSelLayout &f) {
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
+    float *scores = reinterpret_cast<float *>(w + f.scores);
+    const int budget = h->p.budget_blocks;
+    hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
+    for (int64_t r0 = 0; r0 < L && e == hipSuccess; r0 += f.rows) {
+        const int64_t nr = (r0 + f.rows < L) ? f.rows : L - r0;
+        const int64_t pos0 = q_offset + r0;
+        e = launch_indexer_scores(st, B, nr, pos0, f.ncol, nblk_cap(h), qrot + r0 * kIdxHeads * kIdxDim,
+                                  L * kIdxHeads * kIdxDim, kbar_cache, scores, f.rows * f.ncol, false);
+        if (e == hipSuccess)
+            e = launch_select(st, B, nr, pos0, nullptr, f.ncol, scores, f.rows * f.ncol, bidx + r0 * budget,
+                              L * budget, budget);
+    }
+    return e;
 }
 
 qsa_status check_chunk(const qsa_handle *h, int32_t B, int64_t L, int64_t q_offset, bool aligned_offset) {
@@ -229,8 +249,11 @@ size_t qsa_workspace_size(const qsa_handle *h, int op, int32_t batch, int64_t le
         return 0;
     case QSA_OP_INDEX:
         return align_up(static_cast<size_t>(batch) * len * kIdxHeads * kIdxDim * 2);
+    case QSA_OP_INDEX_SELECT:
+        return index_select_layout(batch, len, q_offset).total;
     case QSA_OP_FORWARD:
-        return forward_layout(h, batch, len, q_offset).total;
+        return index_select_layout(batch, len, q_offset).total +
+               align_up(static_cast<size_t>(batch) * len * h->p.budget_blocks * 4);
     case QSA_OP_DECODE:
         return decode_layout(h, batch, q_offset).total;
     default:
@@ -242,9 +265,8 @@ qsa_status qsa_append(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
                       const uint16_t *k, const uint16_t *v, const uint16_t *k_idx, uint16_t *k_cache,
                       uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend) {
     qsa_status s = check_chunk(h, B, L, q_offset, false);
-    if (s != QSA_OK) return s;
+    if (s != QSA_OK || L == 0) return s;
     if ((s = check_ptrs({k, v, k_idx, k_cache, v_cache, kbar_cache, kpend})) != QSA_OK) return s;
-    if (L == 0) return QSA_OK;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -255,23 +277,17 @@ qsa_status qsa_append(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
 }
 
 qsa_status qsa_index(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
-                     const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *kbar_cache, uint16_t *kpend,
-                     float *scores, void *ws, size_t ws_bytes) {
+                     const uint16_t *q_idx, const uint16_t *kbar_cache, float *scores, void *ws, size_t ws_bytes) {
     qsa_status s = check_chunk(h, B, L, q_offset, true);
-    if (s != QSA_OK) return s;
-    if ((s = check_ptrs({q_idx, k_idx, kbar_cache, kpend, scores})) != QSA_OK) return s;
-    if (L == 0) return QSA_OK;
-    if ((s = check_ptrs({ws})) != QSA_OK) return s;
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q_idx, kbar_cache, scores, ws})) != QSA_OK) return s;
     if (ws_bytes < qsa_workspace_size(h, QSA_OP_INDEX, B, L, q_offset)) return QSA_ERR_WORKSPACE;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
     bf16_t *qrot = static_cast<bf16_t *>(ws);
     const int64_t ncol = (q_offset + L + kBlock - 1) / kBlock;
-    hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nblk_cap(h), nullptr, nullptr, k_idx, nullptr,
-                                  nullptr, kbar_cache, kpend, false, true);
-    if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
-    if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
+    hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
     if (e == hipSuccess)
         e = launch_indexer_scores(st, B, L, q_offset, ncol, nblk_cap(h), qrot, L * kIdxHeads * kIdxDim, kbar_cache,
                                   scores, L * ncol, true);
@@ -279,13 +295,10 @@ qsa_status qsa_index(const qsa_handle *h, void *stream, int32_t B, int64_t L, in
 }
 
 qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
-                      const float *scores, int32_t *block_idx, void *ws, size_t ws_bytes) {
-    (void)ws;
-    (void)ws_bytes;
+                      const float *scores, int32_t *block_idx) {
     qsa_status s = check_chunk(h, B, L, q_offset, true);
-    if (s != QSA_OK) return s;
+    if (s != QSA_OK || L == 0) return s;
     if ((s = check_ptrs({scores, block_idx})) != QSA_OK) return s;
-    if (L == 0) return QSA_OK;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     const int64_t ncol = (q_offset + L + kBlock - 1) / kBlock;
@@ -296,22 +309,30 @@ qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
 }
 
 qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset, const uint16_t *q,
-                      const uint16_t *k, const uint16_t *v, uint16_t *k_cache, uint16_t *v_cache,
-                      const int32_t *block_idx, uint16_t *out, void *ws, size_t ws_bytes) {
-    (void)ws;
-    (void)ws_bytes;
+                      const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *block_idx, uint16_t *out) {
     qsa_status s = check_chunk(h, B, L, q_offset, true);
-    if (s != QSA_OK) return s;
-    if ((s = check_ptrs({q, k, v, k_cache, v_cache, block_idx, out})) != QSA_OK) return s;
-    if (L == 0) return QSA_OK;
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q, k_cache, v_cache, block_idx, out})) != QSA_OK) return s;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nblk_cap(h), k, v, nullptr, k_cache, v_cache,
-                                  nullptr, nullptr, true, false);
-    if (e == hipSuccess)
-        e = launch_attend_prefill(tables(h), st, B, L, q_offset, nblk_cap(h), h->p.budget_blocks, h->sigma, q,
+    hipError_t e = launch_attend_prefill(tables(h), st, B, L, q_offset, nblk_cap(h), h->p.budget_blocks, h->sigma, q,
                                   k_cache, v_cache, block_idx, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_index_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                            const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *block_idx, void *ws,
+                            size_t ws_bytes) {
+    qsa_status s = check_chunk(h, B, L, q_offset, true);
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q_idx, kbar_cache, block_idx, ws})) != QSA_OK) return s;
+    const IdxSelLayout f = index_select_layout(B, L, q_offset);
+    if (ws_bytes < f.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipError_t e = run_index_select(h, static_cast<hipStream_t>(stream), B, L, q_offset, q_idx, kbar_cache, block_idx,
+                                    static_cast<char *>(ws), f);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 
@@ -320,39 +341,27 @@ qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, 
                        uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend, uint16_t *out,
                        int32_t *block_idx, void *ws, size_t ws_bytes) {
     qsa_status s = check_chunk(h, B, L, q_offset, true);
-    if (s != QSA_OK) return s;
-    if ((s = check_ptrs({q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out})) != QSA_OK) return s;
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, ws})) != QSA_OK) return s;
     if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
-    if (L == 0) return QSA_OK;
-    if ((s = check_ptrs({ws})) != QSA_OK) return s;
-    const FwdLayout f = forward_layout(h, B, L, q_offset);
-    if (ws_bytes < f.total) return QSA_ERR_WORKSPACE;
+    const IdxSelLayout f = index_select_layout(B, L, q_offset);
+    const size_t bidx_off = f.total;
+    const size_t total = bidx_off + align_up(static_cast<size_t>(B) * L * h->p.budget_blocks * 4);
+    if (ws_bytes < total) return QSA_ERR_WORKSPACE;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(ws);
-    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
-    int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + f.bidx);
-    float *scores = reinterpret_cast<float *>(w + f.scores);
-    const int budget = h->p.budget_blocks;
+    int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + bidx_off);
     const int64_t nbc = nblk_cap(h);
 
     hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nbc, k, v, k_idx, k_cache, v_cache, kbar_cache,
                                   kpend, true, true);
     if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
-    if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
-    for (int64_t r0 = 0; r0 < L && e == hipSuccess; r0 += f.rows) {
-        const int64_t nr = (r0 + f.rows < L) ? f.rows : L - r0;
-        const int64_t pos0 = q_offset + r0;
-        e = launch_indexer_scores(st, B, nr, pos0, f.ncol, nbc, qrot + r0 * kIdxHeads * kIdxDim,
-                                  L * kIdxHeads * kIdxDim, kbar_cache, scores, f.rows * f.ncol, false);
-        if (e == hipSuccess)
-            e = launch_select(st, B, nr, pos0, nullptr, f.ncol, scores, f.rows * f.ncol, bidx + r0 * budget,
-                              L * budget, budget);
-    }
+    if (e == hipSuccess) e = run_index_select(h, st, B, L, q_offset, q_idx, kbar_cache, bidx, w, f);
     if (e == hipSuccess)
-        e = launch_attend_prefill(tables(h), st, B, L, q_offset, nbc, budget, h->sigma, q, k_cache, v_cache, bidx,
-                                  out);
+        e = launch_attend_prefill(tables(h), st, B, L, q_offset, nbc, h->p.budget_blocks, h->sigma, q, k_cache,
+                                  v_cache, bidx, out);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

@@ -32,6 +32,8 @@
  *     touched, except QSA_ERR_HIP, which reports a failed launch (the HIP code
  *     is then available from qsa_last_hip_error()).  Faults inside kernels
  *     surface at the caller's next synchronisation.
+ *   - A call with L = 0 is a no-op that returns QSA_OK after the shape checks
+ *     (its pointers may then be NULL).
  *   - Inputs must be finite; non-finite values are not detected.
  *   - Calls that share a cache must be ordered (same stream or explicit
  *     events); the handle itself is immutable and may be shared by threads.
@@ -111,7 +113,7 @@ typedef struct qsa_handle qsa_handle;
 
 /* Operation codes for qsa_workspace_size. */
 enum { QSA_OP_APPEND = 0, QSA_OP_INDEX = 1, QSA_OP_SELECT = 2, QSA_OP_ATTEND = 3,
-       QSA_OP_FORWARD = 4, QSA_OP_DECODE = 5 };
+       QSA_OP_FORWARD = 4, QSA_OP_DECODE = 5, QSA_OP_INDEX_SELECT = 6 };
 
 /* Fill *p with the layer's published shapes, budget 512, max_ctx 262144,
  * theta 1e7, no YaRN (factor 1), yarn_orig_ctx 262144.  Host only. */
@@ -152,45 +154,51 @@ qsa_status qsa_append(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
                       uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend);
 
 /* Indexer ([PKR] "QSA: ...", equation I_ib = sum_h ReLU(<q_i^h, k̄_b>)):
- * appends the chunk's indexer keys (as qsa_append does for k_idx only), rotates
- * q_idx at its positions, and writes the score matrix `scores` (layout above)
- * for queries q_offset .. q_offset+L-1 against every complete block before the
- * query's own block (block-causal: only fully observed blocks are scored).
- * Scores accumulate in fp32 from bf16 operands (MFMA).  q_offset % 4 == 0.
- * ws: qsa_workspace_size(QSA_OP_INDEX) bytes. */
+ * rotates q_idx at positions q_offset .. q_offset+L-1 and writes the score
+ * matrix `scores` (layout above) of those queries against every complete block
+ * before each query's own block (block-causal: only fully observed blocks are
+ * scored; non-candidates get -1).  kbar_cache must already hold those blocks
+ * (qsa_append).  Scores accumulate in fp32 from bf16 operands (matrix cores).
+ * q_offset % 4 == 0.  ws: qsa_workspace_size(QSA_OP_INDEX) bytes. */
 qsa_status qsa_index(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
-                     const uint16_t *q_idx, const uint16_t *k_idx,
-                     uint16_t *kbar_cache, uint16_t *kpend, float *scores,
+                     const uint16_t *q_idx, const uint16_t *kbar_cache, float *scores,
                      void *ws, size_t ws_bytes);
 
 /* Selection ([PKR] "QSA: ...": K = 2048 tokens, r = 4, up to 512 blocks per
  * query): for each query p, the min(budget, floor(p/4)) candidates with the
  * largest scores, ties broken toward the larger block index, written ascending
  * and padded with -1 into block_idx [B][L][budget].  Reads `scores` as written
- * by qsa_index for the same (B, L, q_offset).  q_offset % 4 == 0.
- * ws: qsa_workspace_size(QSA_OP_SELECT) bytes (may be 0). */
+ * by qsa_index for the same (B, L, q_offset).  q_offset % 4 == 0.  Needs no
+ * workspace. */
 qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
-                      const float *scores, int32_t *block_idx, void *ws, size_t ws_bytes);
+                      const float *scores, int32_t *block_idx);
+
+/* qsa_index followed by qsa_select without handing the score matrix to the
+ * caller: scores live only in the workspace, one bounded slice of query rows
+ * at a time (at most 2 GiB), so any context length fits.  Same results as the
+ * two calls.  ws: qsa_workspace_size(QSA_OP_INDEX_SELECT) bytes. */
+qsa_status qsa_index_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                            const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *block_idx,
+                            void *ws, size_t ws_bytes);
 
 /* Sparse core attention ([PKR] "QSA: ...", sparse core attention over the
  * selected blocks; the tail of the last incomplete block is always included):
- * writes the chunk's rotated keys and values into the caches (as qsa_append
- * does for k and v), then for each query p and head h (KV head h / 12) computes
- * softmax(sigma * q~_h . K~^T) V over the tokens of the blocks in
- * block_idx[p] plus tokens 4*floor(p/4) .. p, with sigma = 1/16 (times the YaRN
- * temperature).  Scores and softmax in fp32, P rounded to bf16 for the PV
- * product, output bf16.  q_offset % 4 == 0.
- * ws: qsa_workspace_size(QSA_OP_ATTEND) bytes (may be 0). */
+ * for each query p = q_offset + i and head h (KV head h / 12) computes
+ * softmax(sigma * q~_h . K~^T) V over the tokens of the blocks in block_idx[p]
+ * plus tokens 4*floor(p/4) .. p, read from the caches, with q~ = q rotated at p
+ * and sigma = 1/16 (times the YaRN temperature).  The caches must already hold
+ * positions 0..p (qsa_append).  Entries of block_idx outside [0, floor(p/4))
+ * are skipped.  Logits and softmax in fp32, P rounded to bf16 for the PV
+ * product, output bf16.  q_offset % 4 == 0.  Needs no workspace. */
 qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
-                      const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                      uint16_t *k_cache, uint16_t *v_cache,
-                      const int32_t *block_idx, uint16_t *out, void *ws, size_t ws_bytes);
+                      const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                      const int32_t *block_idx, uint16_t *out);
 
-/* Prefill (or one prefill chunk): qsa_append + indexer + selection + sparse
- * attention for queries q_offset .. q_offset+L-1, without handing the score
- * matrix to the caller.  block_idx may be NULL; when given it receives the
- * selection ([B][L][budget]).  Earlier chunks must already be in the caches.
- * q_offset % 4 == 0.  ws: qsa_workspace_size(QSA_OP_FORWARD) bytes. */
+/* Prefill (or one prefill chunk): qsa_append, qsa_index_select and qsa_attend
+ * for positions q_offset .. q_offset+L-1.  block_idx may be NULL; when given
+ * it receives the selection ([B][L][budget]).  Earlier chunks must already be
+ * in the caches.  q_offset % 4 == 0.
+ * ws: qsa_workspace_size(QSA_OP_FORWARD) bytes. */
 qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
                        const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const uint16_t *q_idx, const uint16_t *k_idx,

@@ -53,6 +53,8 @@ def test_null_handle_and_status_strings():
     assert lib.qsa_workspace_size(None, 4, 1, 10, 0) == 0
     assert lib.qsa_append(None, None, 1, 4, 0, *([None] * 7)) == 1
     assert lib.qsa_forward(None, None, 1, 4, 0, *([None] * 12), 0) == 1
+    assert lib.qsa_index_select(None, None, 1, 4, 0, None, None, None, None, 0) == 1
+    assert lib.qsa_attend(None, None, 1, 4, 0, None, None, None, None, None) == 1
     assert lib.qsa_decode(None, None, 1, None, 0, *([None] * 12), 0) == 1
     for s in range(8):
         assert Q.qsa_status_string(s)

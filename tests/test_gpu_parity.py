@@ -90,14 +90,19 @@ def test_index_scores(B, L, q_offset):
     x, xd = _prefill(w)
     h = Q.Handle(max_ctx=4096, budget_blocks=64)
     c = Q.alloc_caches(h, B)
-    if q_offset:
-        Q.qsa_append(h, B, q_offset, 0, xd["k"][:, :q_offset].contiguous(), xd["v"][:, :q_offset].contiguous(),
-                     xd["k_idx"][:, :q_offset].contiguous(), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    Q.qsa_append(h, B, q_offset + L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"],
+                 c["kpend"])
     ncol = (q_offset + L + 3) // 4
     scores = torch.empty((B, L, ncol), dtype=torch.float32, device=DEV)
     ws = Q.workspace(h, Q.QSA_OP_INDEX, B, L, q_offset)
     sl = lambda t: t[:, q_offset:q_offset + L].contiguous()
-    Q.qsa_index(h, B, L, q_offset, sl(xd["q_idx"]), sl(xd["k_idx"]), c["kbar_cache"], c["kpend"], scores, ws)
+    Q.qsa_index(h, B, L, q_offset, sl(xd["q_idx"]), c["kbar_cache"], scores, ws)
+    # the fused index + select stage selects what select(scores) selects
+    bidx_a = torch.empty((B, L, h.budget), dtype=torch.int32, device=DEV)
+    bidx_b = torch.empty_like(bidx_a)
+    Q.qsa_select(h, B, L, q_offset, scores, bidx_a)
+    ws2 = Q.workspace(h, Q.QSA_OP_INDEX_SELECT, B, L, q_offset)
+    Q.qsa_index_select(h, B, L, q_offset, sl(xd["q_idx"]), c["kbar_cache"], bidx_b, ws2)
     torch.cuda.synchronize()
     s = f32(scores)
     p = O.Params()
@@ -108,6 +113,7 @@ def test_index_scores(B, L, q_offset):
             o = (q_offset + i) // 4
             check_scores(s[b, i, :o], O.block_scores(qt[i], kbar[:o]), "b%d row %d" % (b, i))
             assert np.all(s[b, i, o:] == -1.0)
+    assert torch.equal(bidx_a, bidx_b)
 
 
 # ---------------------------------------------------------------- select
@@ -154,9 +160,9 @@ def test_attend_with_oracle_selection():
     ref, sel, _ = O.prefill_rows(*(bits(x[n][0]) for n in ("q", "k", "v", "q_idx", "k_idx")), rows, p)
     h = Q.Handle(max_ctx=1024, budget_blocks=budget)
     c = Q.alloc_caches(h, B)
+    Q.qsa_append(h, B, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
     out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
-    Q.qsa_attend(h, B, L, 0, xd["q"], xd["k"], xd["v"], c["k_cache"], c["v_cache"],
-                 torch.from_numpy(sel[None]).to(DEV), out)
+    Q.qsa_attend(h, B, L, 0, xd["q"], c["k_cache"], c["v_cache"], torch.from_numpy(sel[None]).to(DEV), out)
     torch.cuda.synchronize()
     check_out(f32(out[0]), ref, "attend")
 
@@ -242,6 +248,8 @@ def _decode_setup(w, ctx_per_seq, h):
     xd = _to(x)
     c = Q.alloc_caches(h, B)
     for b, n in enumerate(ctx_per_seq):
+        if n == 0:
+            continue
         sl = lambda t: t[b:b + 1, :n].contiguous()
         cs = {k: v[b:b + 1] for k, v in c.items()}
         Q.qsa_append(h, 1, n, 0, sl(xd["k"]), sl(xd["v"]), sl(xd["k_idx"]), cs["k_cache"], cs["v_cache"],
