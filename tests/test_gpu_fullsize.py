@@ -1,0 +1,173 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times, on sampled rows the oracle computes one by one, plus properties checked
+on every row (needles, selection invariants).
+
+Large inputs are drawn on the GPU by the seeded generator (a GPU and a CPU
+generator give different streams); the oracle reads host copies of those
+inputs -- never anything the library wrote.
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_qsa_amd as Q
+import oracle as O
+import synth
+from helpers import bits, check_out, check_selection
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    assert torch.cuda.is_available()
+    Q.lib()
+    yield
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _prefill_run(w, x, chunk=None):
+    """Prefill of one sequence: chunks via qsa_forward, or the bench's stage calls."""
+    L = w.seq_len
+    h = Q.Handle(max_ctx=L, budget_blocks=w.budget, yarn_factor=w.yarn_factor)
+    c = Q.alloc_caches(h, 1)
+    bidx = torch.empty((1, L, w.budget), dtype=torch.int32, device=DEV)
+    out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    if chunk is None:
+        ws = Q.workspace(h, Q.QSA_OP_INDEX_SELECT, 1, L, 0)
+        Q.qsa_append(h, 1, L, 0, x["k"], x["v"], x["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+        Q.qsa_index_select(h, 1, L, 0, x["q_idx"], c["kbar_cache"], bidx, ws)
+        Q.qsa_attend(h, 1, L, 0, x["q"], c["k_cache"], c["v_cache"], bidx, out)
+    else:
+        for s0 in range(0, L, chunk):
+            n = min(chunk, L - s0)
+            ws = Q.workspace(h, Q.QSA_OP_FORWARD, 1, n, s0)
+            sl = lambda t: t[:, s0:s0 + n]
+            Q.qsa_forward(h, 1, n, s0, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["q_idx"]), sl(x["k_idx"]),
+                          c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sl(out), sl(bidx), ws)
+            del ws
+            torch.cuda.synchronize()
+            _say("  chunk at %d done" % s0)
+    torch.cuda.synchronize()
+    return out, bidx
+
+
+def _check_needles_prefill(plan, bidx):
+    rows = np.concatenate(plan.probes)
+    owners = np.concatenate([[b] * len(p) for b, p in zip(plan.blocks, plan.probes)])
+    got = bidx[0, torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    miss = [(int(r), int(b)) for r, b, g in zip(rows, owners, got) if b not in g]
+    assert not miss, "needle blocks not selected by their probes: %s" % miss[:5]
+    return len(rows)
+
+
+def _check_rows(x, out, bidx, p, rows):
+    lay = O.LayerOracle(bits(x["k"][0]), bits(x["v"][0]), bits(x["k_idx"][0]), p)
+    o = out[0, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    bi = bidx[0, torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    worst = 0.0
+    for j, r in enumerate(rows):
+        ref, sel, sc = lay.row(int(r), bits(x["q"][0, r]), bits(x["q_idx"][0, r]))
+        check_selection(bi[j], sel, sc, p.budget, int(r) // 4, "row %d" % r)
+        err, _ = check_out(o[j], ref, "row %d" % r)
+        worst = max(worst, err)
+    return worst
+
+
+def _sample_rows(L, stride, tail, extra=()):
+    rows = set(range(stride - 1, L, stride)) | set(range(L - tail, L)) | set(int(e) for e in extra if 0 <= e < L)
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def test_prefill_32k_sampled():
+    w = synth.WORKLOADS["prefill_32k"]
+    x = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in synth.prefill_inputs(w, "cpu").items()}
+    out, bidx = _prefill_run(w, x)
+    n = _check_needles_prefill(x["needles"][0], bidx)
+    plan = x["needles"][0]
+    rows = _sample_rows(w.seq_len, 512, 16, [p[0] for p in plan.probes[::8]] + [2044, 2047, 2048, 2051, 2052])
+    worst = _check_rows(x, out, bidx, O.Params(budget=w.budget), rows)
+    _say("prefill 32k: %d rows vs oracle (max abs err %.4g), %d needle probes" % (len(rows), worst, n))
+
+
+def test_prefill_256k_sampled_bench_config():
+    w = synth.WORKLOADS["prefill_256k"]
+    x = synth.prefill_inputs(w, DEV)
+    out, bidx = _prefill_run(w, x)
+    n = _check_needles_prefill(x["needles"][0], bidx)
+    plan = x["needles"][0]
+    # every 4096th row, the recency-scaled tail, and one probe of every 16th needle
+    rows = _sample_rows(w.seq_len, 4096, 24, [p[0] for p in plan.probes[::16]] + [262144 - 257, 262144 - 256])
+    worst = _check_rows(x, out, bidx, O.Params(budget=w.budget), rows)
+    _say("prefill 256k: %d rows vs oracle (max abs err %.4g), %d needle probes" % (len(rows), worst, n))
+
+
+def _decode_run(w):
+    B, ctx = w.batch, w.seq_len
+    x = synth.decode_inputs(w, DEV)
+    h = Q.Handle(max_ctx=ctx + 4, budget_blocks=w.budget, yarn_factor=w.yarn_factor)
+    c = Q.alloc_caches(h, B)
+    for b in range(B):
+        cs = {k: v[b:b + 1] for k, v in c.items()}
+        Q.qsa_append(h, 1, ctx, 0, x["k"][b:b + 1, :ctx], x["v"][b:b + 1, :ctx], x["k_idx"][b:b + 1, :ctx],
+                     cs["k_cache"], cs["v_cache"], cs["kbar_cache"], cs["kpend"])
+    new = {n: x[n][:, ctx:ctx + 1].contiguous() for n in ("k", "v", "k_idx")}
+    cache_len = torch.full((B,), ctx, dtype=torch.int32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_DECODE, B, 1, ctx)
+    out = torch.empty((B, 1, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bidx = torch.empty((B, 1, w.budget), dtype=torch.int32, device=DEV)
+    Q.qsa_decode(h, B, cache_len, ctx, x["q"], new["k"], new["v"], x["q_idx"], new["k_idx"], c["k_cache"],
+                 c["v_cache"], c["kbar_cache"], c["kpend"], out, bidx, ws)
+    torch.cuda.synchronize()
+    return x, out, bidx
+
+
+def _check_decode(w, x, out, bidx, seqs):
+    p = O.Params(budget=w.budget, yarn_factor=w.yarn_factor)
+    bi = bidx.cpu().numpy()
+    for b in range(w.batch):                      # needles of every sequence
+        for blk in x["needles"][b].blocks:
+            assert blk in bi[b, 0], "sequence %d misses needle block %d" % (b, blk)
+    worst = 0.0
+    for b in seqs:
+        lay = O.LayerOracle(bits(x["k"][b]), bits(x["v"][b]), bits(x["k_idx"][b]), p)
+        ref, sel, sc = lay.row(w.seq_len, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
+        check_selection(bi[b, 0], sel, sc, w.budget, w.seq_len // 4, "seq %d" % b)
+        err, _ = check_out(out[b, 0].float().cpu().numpy(), ref, "seq %d" % b)
+        worst = max(worst, err)
+        del lay
+    return worst
+
+
+def test_decode_128k_sampled_bench_config():
+    w = synth.WORKLOADS["decode_128k"]
+    x, out, bidx = _decode_run(w)
+    worst = _check_decode(w, x, out, bidx, seqs=(0, 17, 63))
+    _say("decode 128k: 3 sequences vs oracle (max abs err %.4g), needles of 64 sequences" % worst)
+
+
+def test_decode_1m_yarn_sampled():
+    w = synth.WORKLOADS["decode_1m"]
+    x, out, bidx = _decode_run(w)
+    worst = _check_decode(w, x, out, bidx, seqs=(0, 7))
+    _say("decode 1M yarn: 2 sequences vs oracle (max abs err %.4g), needles of 8 sequences" % worst)
+
+
+def test_prefill_1m_yarn_chunked_sampled():
+    w = synth.WORKLOADS["prefill_1m"]
+    x = synth.prefill_inputs(w, DEV)
+    out, bidx = _prefill_run(w, x, chunk=w.chunk)
+    n = _check_needles_prefill(x["needles"][0], bidx)
+    bounds = [c + d for c in range(w.chunk, w.seq_len, w.chunk) for d in (-1, 0, 1)]
+    rows = _sample_rows(w.seq_len, 65536, 4, bounds[::2])
+    worst = _check_rows(x, out, bidx, O.Params(budget=w.budget, yarn_factor=w.yarn_factor), rows)
+    _say("prefill 1M chunked yarn: %d rows vs oracle (max abs err %.4g), %d needle probes" % (len(rows), worst, n))
