@@ -166,12 +166,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     torch.cuda.init()
+    if args.calib_copy:
+        src = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wp = synth.WORKLOADS["prefill_256k"]
     wd = synth.WORKLOADS["decode_128k"]
     sp = setup_prefill(wp)
