@@ -41,7 +41,7 @@ class Params(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("rope_dim", ctypes.c_int32), ("n_idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32),
                 ("idx_rope_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("budget_blocks", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32), ("max_ctx", ctypes.c_int64), ("rope_theta", ctypes.c_double),
+                ("topk_cap", ctypes.c_int32), ("max_ctx", ctypes.c_int64), ("rope_theta", ctypes.c_double),
                 ("yarn_factor", ctypes.c_double), ("yarn_orig_ctx", ctypes.c_int64)]
 
 

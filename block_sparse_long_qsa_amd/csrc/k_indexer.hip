@@ -142,4 +142,199 @@ hipError_t launch_indexer_scores(hipStream_t st, int32_t B, int64_t L, int64_t q
     return hipGetLastError();
 }
 
+
+
+// ----------------------------------------------------------------------------
+// Fused indexer + streaming candidate filter (the index + select stage without
+// a score matrix).
+//
+// A workgroup owns 64 consecutive queries and walks every candidate column
+// 0 .. floor(p_last/4) in k̄ tiles of 64, computing the same MFMA scores as
+// indexer_scores_kernel.  Each query keeps
+//   * a running threshold tau (fp32), below which a block can no longer be in
+//     its top `budget`: tau is the lower edge of the highest bin of a 128-bin
+//     log histogram (8 bins per octave over [2^-8, 2^8)) of the scores kept so
+//     far whose suffix count reaches `budget` -- at least `budget` kept scores
+//     are >= tau, so the budget-th largest score is >= tau;
+//   * the list of (score, block) pairs with score >= tau, appended in ascending
+//     block order (ballot + prefix count per 32-column tile).
+// Queries are owned by one wave each, so the histograms, counters and
+// thresholds need no workgroup barrier.  The exact top-`budget` is then taken
+// from the short list by select_compact_kernel.  A list that would outgrow
+// `cap` keeps counting without storing; its row is recomputed exactly there.
+// Workgroups are issued latest-queries-first (longest rows first).
+constexpr int kTopkBins = 128;
+constexpr int kTopkBinBase = 951;      // bin 1 = [2^-8, 2^-8 * 1.125); 952 = (127 - 8) * 8
+constexpr uint32_t kTauRefresh = 32;    // appends between threshold refreshes
+
+__device__ __forceinline__ int topk_bin(float s) {
+    const int b = static_cast<int>(__float_as_uint(s) >> 20) - kTopkBinBase;
+    return b < 0 ? 0 : (b >= kTopkBins ? kTopkBins - 1 : b);
+}
+__device__ __forceinline__ float topk_bin_edge(int b) {
+    return b <= 0 ? 0.0f : __uint_as_float(static_cast<uint32_t>(b + kTopkBinBase) << 20);
+}
+
+__global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
+    int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, int cap,
+    const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar,
+    float *__restrict__ cand_score, int32_t *__restrict__ cand_idx, int32_t *__restrict__ cand_count)
+{
+    __shared__ __attribute__((aligned(16))) bf16_t lds[2][kIdxSubCols * kLdsRow];
+    __shared__ uint32_t hist[kIdxQueriesPerWG][kTopkBins];
+    __shared__ uint32_t cnt[kIdxQueriesPerWG];
+    __shared__ uint32_t since[kIdxQueriesPerWG];
+    __shared__ float tau_s[kIdxQueriesPerWG];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int half = lane >> 5;
+    const int64_t b = blockIdx.y;
+    const int64_t tile = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
+    const int64_t q0 = tile * kIdxQueriesPerWG;
+    const int64_t q_last = (q0 + kIdxQueriesPerWG - 1 < L) ? q0 + kIdxQueriesPerWG - 1 : L - 1;
+    const int64_t o_hi = (q_offset + q_last) / kBlock;
+    if (o_hi <= budget) return;                 // every row of the tile keeps all its candidates
+
+    for (int x = tid; x < kIdxQueriesPerWG * kTopkBins; x += 256) (&hist[0][0])[x] = 0;
+    if (tid < kIdxQueriesPerWG) {
+        cnt[tid] = 0;
+        since[tid] = 0;
+        tau_s[tid] = 0.0f;
+    }
+
+    bf16x8 afrag[2][8];
+    for (int a = 0; a < 2; ++a) {
+        const int r = 64 * wave + 32 * a + (lane & 31);
+        const int64_t q = q0 + (r >> 2);
+        const int h = r & 3;
+        for (int s = 0; s < 8; ++s) {
+            if (q < L) {
+                const bf16_t *src = qrot + b * qrot_bstride + (q * kIdxHeads + h) * kIdxDim + 16 * s + 8 * (lane >> 5);
+                afrag[a][s] = *reinterpret_cast<const bf16x8 *>(src);
+            } else {
+                afrag[a][s] = bf16x8{};
+            }
+        }
+    }
+    // per lane: the 8 queries it scores, their candidate limits and thresholds
+    int32_t qo[2][4];
+    float tau[2][4];
+    for (int a = 0; a < 2; ++a)
+        for (int i = 0; i < 4; ++i) {
+            const int64_t q = q0 + 16 * wave + 8 * a + 2 * i + half;
+            qo[a][i] = (q < L) ? static_cast<int32_t>((q_offset + q) / kBlock) : 0;
+            tau[a][i] = 0.0f;
+        }
+
+    const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
+    auto stage = [&](int buf, int64_t cs) {
+        for (int it = 0; it < 4; ++it) {
+            const int chunk = it * 256 + tid;
+            const int row = chunk >> 4, c = chunk & 15;
+            const int64_t blk = cs + row;
+            u32x4 val = u32x4{0, 0, 0, 0};
+            if (blk < nblk_cap) val = *reinterpret_cast<const u32x4 *>(kb + blk * kIdxDim + 8 * c);
+            *reinterpret_cast<u32x4 *>(&lds[buf][row * kLdsRow + 8 * c]) = val;
+        }
+    };
+
+    int buf = 0;
+    stage(0, 0);
+    __syncthreads();
+    for (int64_t cs = 0; cs < o_hi; cs += kIdxSubCols) {
+        if (cs + kIdxSubCols < o_hi) stage(buf ^ 1, cs + kIdxSubCols);
+
+        f32x16 acc[2][2];
+        for (int ct = 0; ct < 2; ++ct) {
+            bf16x8 bfrag[8];
+            const bf16_t *brow = &lds[buf][(32 * ct + (lane & 31)) * kLdsRow + 8 * (lane >> 5)];
+            for (int s = 0; s < 8; ++s) bfrag[s] = *reinterpret_cast<const bf16x8 *>(brow + 16 * s);
+            for (int a = 0; a < 2; ++a) {
+                f32x16 c = {};
+                for (int s = 0; s < 8; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag[a][s], bfrag[s], c, 0, 0, 0);
+                acc[a][ct] = c;
+            }
+        }
+        bool any = false;
+        for (int a = 0; a < 2; ++a) {
+            for (int i = 0; i < 4; ++i) {
+                const int ql = 16 * wave + 8 * a + 2 * i + half;     // local query of this lane
+                for (int ct = 0; ct < 2; ++ct) {
+                    const int32_t col = static_cast<int32_t>(cs) + 32 * ct + (lane & 31);
+                    const f32x16 &c = acc[a][ct];
+                    const float s = relu_sum4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+                    const bool keep = col < qo[a][i] && s >= tau[a][i];
+                    const uint64_t m = __ballot(keep);
+                    if (m == 0) continue;                            // wave-uniform
+                    any = true;
+                    const uint32_t mh = half ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
+                    const uint32_t below = mh & ((1u << (lane & 31)) - 1u);
+                    const uint32_t base = cnt[ql];
+                    if (keep) {
+                        const uint32_t pos = base + static_cast<uint32_t>(__popc(below));
+                        const int64_t row = b * L + q0 + ql;
+                        if (pos < static_cast<uint32_t>(cap)) {
+                            cand_score[row * cap + pos] = s;
+                            cand_idx[row * cap + pos] = col;
+                        }
+                        atomicAdd(&hist[ql][topk_bin(s)], 1u);
+                    }
+                    if ((lane & 31) == 0 && mh != 0) {
+                        cnt[ql] = base + static_cast<uint32_t>(__popc(mh));
+                        since[ql] += static_cast<uint32_t>(__popc(mh));
+                    }
+                }
+            }
+        }
+        if (any) {
+            // refresh the thresholds of this wave's queries that kept enough new scores
+            bool changed = false;
+            for (int j = 0; j < 16; ++j) {
+                const int ql = 16 * wave + j;
+                if (since[ql] < kTauRefresh) continue;              // wave-uniform (LDS broadcast)
+                const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
+                const uint32_t part = h0 + h1;
+                uint32_t incl = part;                                // kept scores in bins >= 2*lane
+                for (int off = 1; off < 64; off <<= 1) {
+                    const uint32_t other = __shfl_down(incl, off);
+                    if (lane + off < 64) incl += other;
+                }
+                const uint32_t c1 = incl - h0;                       // bins >= 2*lane + 1
+                const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
+                                 : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
+                const uint64_t vm = __ballot(cand >= 0);
+                if (lane == 0) since[ql] = 0;
+                if (vm != 0) {
+                    const int hi = 63 - __clzll(vm);
+                    const int bin = __shfl(cand, hi);
+                    const float t = topk_bin_edge(bin);
+                    if (lane == 0 && t > tau_s[ql]) tau_s[ql] = t;
+                    changed = true;
+                }
+            }
+            if (changed) {
+                for (int a = 0; a < 2; ++a)
+                    for (int i = 0; i < 4; ++i) tau[a][i] = tau_s[16 * wave + 8 * a + 2 * i + half];
+            }
+        }
+        __syncthreads();
+        buf ^= 1;
+    }
+    __syncthreads();
+    if (tid < kIdxQueriesPerWG && q0 + tid < L) cand_count[b * L + q0 + tid] = static_cast<int32_t>(cnt[tid]);
+}
+
+hipError_t launch_indexer_topk(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget,
+                               int cap, const bf16_t *qrot, int64_t qrot_bstride, const bf16_t *kbar,
+                               float *cand_score, int32_t *cand_idx, int32_t *cand_count)
+{
+    if (L <= 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>((L + kIdxQueriesPerWG - 1) / kIdxQueriesPerWG), static_cast<unsigned>(B));
+    hipLaunchKernelGGL(indexer_topk_kernel, grid, dim3(256), 0, st, L, q_offset, nblk_cap, budget, cap, qrot,
+                       qrot_bstride, kbar, cand_score, cand_idx, cand_count);
+    return hipGetLastError();
+}
+
 }  // namespace qsa

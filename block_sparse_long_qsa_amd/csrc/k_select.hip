@@ -1,14 +1,20 @@
-// Per-query top-K block selection over a materialised score row (PyTorchKR post
-// "Qwen3.8-Flash-Next, 1/9의 학습 비용으로 …", section "QSA: 인덱서 자체의 비용을
-// 줄이는 희소 어텐션": token budget K = 2048 with r = 4, i.e. at most 512 blocks
-// per query).
+// Per-query top-K block selection (PyTorchKR post "Qwen3.8-Flash-Next, 1/9의 학습
+// 비용으로 …", section "QSA: 인덱서 자체의 비용을 줄이는 희소 어텐션": token budget
+// K = 2048 with r = 4, i.e. at most 512 blocks per query).
 //
 // Order: score descending, then block index descending (ties go to the more
 // recent block).  Scores are >= +0, so their IEEE bit patterns order like the
 // values and the K-th largest score is found by an exact MSB-first radix
 // select on the 31 value bits (11 + 11 + 9 bits) with LDS histograms.  The
 // selected blocks are then emitted in ascending block order by one more pass
-// with workgroup-wide prefix counts built from wave ballots.
+// with workgroup-wide prefix counts built from wave ballots.  The same routine
+// serves three sources of a row's (score, block) sequence, always in ascending
+// block order:
+//   * a materialised score row (qsa_select, decode),
+//   * the compact candidate list a query kept while streaming its scores
+//     (the fused index + select path; loaded into LDS first),
+//   * scores recomputed on the fly for a query whose candidate list
+//     overflowed (exact fallback).
 //
 // One workgroup of 256 threads per query row.
 #include "qsa_common.h"
@@ -17,43 +23,25 @@ namespace qsa {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxBins = 2048;
-
-__device__ __forceinline__ uint32_t ballot_count(uint64_t m) { return static_cast<uint32_t>(__popcll(m)); }
+constexpr int kMaxCandCap = 8192;      // largest candidate list the compact path stages in LDS
 
 __device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
-    // number of set bits of m below this lane
     const int lane = threadIdx.x & 63;
     const uint64_t below = (lane == 0) ? 0ull : (m & ((~0ull) >> (64 - lane)));
     return static_cast<uint32_t>(__popcll(below));
 }
 
-// Row (b, i), i < L, is the query at position q_offset + i (or cache_len[b]
-// clamped to [0, q_offset] when cache_len is given: decode passes its bound); its scores start at scores + b*sc_bstride + i*ncol
-// and its selection at block_idx + b*bi_bstride + i*budget.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
-    int64_t L, int64_t q_offset, const int32_t *__restrict__ cache_len, int64_t ncol,
-    const float *__restrict__ scores, int64_t sc_bstride, int32_t *__restrict__ block_idx, int64_t bi_bstride,
-    int budget)
+// Exact top-`budget` of n > budget keys.  key(j) gives the score bits of
+// element j (j ascending = block ascending), id(j) its block.  Writes `budget`
+// block ids in ascending order to out.  `hist` is LDS of kSelMaxBins words.
+template <typename KeyFn, typename IdFn>
+__device__ void radix_topk(int64_t n, int budget, KeyFn key, IdFn id, int32_t *__restrict__ out, uint32_t *hist)
 {
-    __shared__ uint32_t hist[kSelMaxBins];
     __shared__ uint32_t s_digit, s_above;
     __shared__ uint32_t s_eq[2][4], s_take[2][4];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t row = blockIdx.x;
-    const int64_t b = row / L;
-    const int64_t i = row - b * L;
-    const int64_t pos = cache_len ? decode_pos(cache_len, b, q_offset) : q_offset + i;
-    const int64_t o = pos / kBlock;
-    const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * sc_bstride + i * ncol);
-    int32_t *out = block_idx + b * bi_bstride + i * budget;
-
-    if (o <= budget) {
-        for (int j = tid; j < budget; j += kSelThreads) out[j] = (j < o) ? j : -1;
-        return;
-    }
 
     uint32_t prefix = 0, mask = 0, k_rem = static_cast<uint32_t>(budget), n_eq = 0;
     const int shifts[3] = {20, 9, 0};
@@ -64,9 +52,18 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const uint32_t dmask = static_cast<uint32_t>(nb - 1);
         for (int x = tid; x < nb; x += kSelThreads) hist[x] = 0;
         __syncthreads();
-        for (int64_t j = tid; j < o; j += kSelThreads) {
-            const uint32_t key = srow[j];
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1u);
+        int64_t j = tid;
+        for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {        // 4 independent loads in flight
+            const uint32_t k0 = key(j), k1 = key(j + kSelThreads), k2 = key(j + 2 * kSelThreads),
+                           k3 = key(j + 3 * kSelThreads);
+            if ((k0 & mask) == prefix) atomicAdd(&hist[(k0 >> shift) & dmask], 1u);
+            if ((k1 & mask) == prefix) atomicAdd(&hist[(k1 >> shift) & dmask], 1u);
+            if ((k2 & mask) == prefix) atomicAdd(&hist[(k2 >> shift) & dmask], 1u);
+            if ((k3 & mask) == prefix) atomicAdd(&hist[(k3 >> shift) & dmask], 1u);
+        }
+        for (; j < n; j += kSelThreads) {
+            const uint32_t k0 = key(j);
+            if ((k0 & mask) == prefix) atomicAdd(&hist[(k0 >> shift) & dmask], 1u);
         }
         __syncthreads();
         if (wave == 0) {
@@ -74,8 +71,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             const int lo = lane * per;
             uint32_t part = 0;
             for (int d = 0; d < per; ++d) part += hist[lo + d];
-            // inclusive suffix sum over lanes: incl = sum of parts of lanes >= lane
-            uint32_t incl = part;
+            uint32_t incl = part;                 // sum of parts of lanes >= lane
             for (int off = 1; off < 64; off <<= 1) {
                 const uint32_t other = __shfl_down(incl, off);
                 if (lane + off < 64) incl += other;
@@ -102,21 +98,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         n_eq = hist[digit];
         __syncthreads();
     }
-    // prefix is now the K-th largest score T; n_eq elements equal T and the
-    // k_rem of them with the largest block indices are taken.
+    // prefix is the K-th largest score T; n_eq elements equal T and the k_rem
+    // of them with the largest block ids (the last ones) are taken.
     const uint32_t T = prefix;
-    const uint32_t eq_skip = n_eq - k_rem;     // ties with the smallest indices are dropped
+    const uint32_t eq_skip = n_eq - k_rem;
 
     uint32_t eq_run = 0, take_run = 0;
     int par = 0;
-    for (int64_t base = 0; base < o; base += kSelThreads) {
+    for (int64_t base = 0; base < n; base += kSelThreads) {
         const int64_t j = base + tid;
-        const bool valid = j < o;
-        const uint32_t key = valid ? srow[j] : 0u;
-        const bool gt = valid && key > T;
-        const bool eq = valid && key == T;
+        const bool valid = j < n;
+        const uint32_t k = valid ? key(j) : 0u;
+        const bool gt = valid && k > T;
+        const bool eq = valid && k == T;
         const uint64_t em = __ballot(eq);
-        if (lane == 0) s_eq[par][wave] = ballot_count(em);
+        if (lane == 0) s_eq[par][wave] = static_cast<uint32_t>(__popcll(em));
         __syncthreads();
         uint32_t eq_before = eq_run + lane_rank(em);
         uint32_t eq_tile = 0;
@@ -127,7 +123,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         }
         const bool take = gt || (eq && eq_before >= eq_skip);
         const uint64_t tm = __ballot(take);
-        if (lane == 0) s_take[par][wave] = ballot_count(tm);
+        if (lane == 0) s_take[par][wave] = static_cast<uint32_t>(__popcll(tm));
         __syncthreads();
         uint32_t posn = take_run + lane_rank(tm);
         uint32_t take_tile = 0;
@@ -136,11 +132,95 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
             if (w < wave) posn += cnt;
             take_tile += cnt;
         }
-        if (take && posn < static_cast<uint32_t>(budget)) out[posn] = static_cast<int32_t>(j);
+        if (take && posn < static_cast<uint32_t>(budget)) out[posn] = static_cast<int32_t>(id(j));
         eq_run += eq_tile;
         take_run += take_tile;
         par ^= 1;
+        if (take_run >= static_cast<uint32_t>(budget)) break;     // uniform: every thread saw the same counts
     }
+}
+
+// Score of block j for the query whose rotated indexer heads are qs (fp32 [4][128]
+// in LDS): sum_h ReLU(<q~_h, k̄_j>), fp32 FMA accumulation (overflow fallback).
+__device__ __noinline__ uint32_t recompute_score(const float *qs, const bf16_t *__restrict__ kb, int64_t j)
+{
+    float d[kIdxHeads] = {0.f, 0.f, 0.f, 0.f};
+    const u32x4 *kr = reinterpret_cast<const u32x4 *>(kb + j * kIdxDim);
+#pragma unroll 1
+    for (int cch = 0; cch < 16; ++cch) {
+        const u32x4 w = kr[cch];
+        for (int e = 0; e < 8; ++e) {
+            const float kv = __uint_as_float(e & 1 ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+            for (int h = 0; h < kIdxHeads; ++h) d[h] = __builtin_fmaf(qs[h * kIdxDim + 8 * cch + e], kv, d[h]);
+        }
+    }
+    const float s = fmaxf(d[0], 0.f) + fmaxf(d[1], 0.f) + fmaxf(d[2], 0.f) + fmaxf(d[3], 0.f);
+    return __float_as_uint(s) & 0x7FFFFFFFu;
+}
+
+__device__ __forceinline__ bool take_all(int64_t o, int budget, int32_t *out) {
+    if (o > budget) return false;
+    for (int j = threadIdx.x; j < budget; j += kSelThreads) out[j] = (j < o) ? j : -1;
+    return true;
+}
+
+// Row (b, i), i < L, is the query at position q_offset + i (or cache_len[b]
+// clamped to [0, q_offset] when cache_len is given: decode passes its bound); its
+// scores start at scores + b*sc_bstride + i*ncol and its selection at
+// block_idx + b*bi_bstride + i*budget.
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    int64_t L, int64_t q_offset, const int32_t *__restrict__ cache_len, int64_t ncol,
+    const float *__restrict__ scores, int64_t sc_bstride, int32_t *__restrict__ block_idx, int64_t bi_bstride,
+    int budget)
+{
+    __shared__ uint32_t hist[kSelMaxBins];
+    const int64_t row = blockIdx.x;
+    const int64_t b = row / L;
+    const int64_t i = row - b * L;
+    const int64_t pos = cache_len ? decode_pos(cache_len, b, q_offset) : q_offset + i;
+    const int64_t o = pos / kBlock;
+    const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * sc_bstride + i * ncol);
+    int32_t *out = block_idx + b * bi_bstride + i * budget;
+    if (take_all(o, budget, out)) return;
+    radix_topk(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
+}
+
+// Selection from the candidate lists of the fused index + select kernel.
+// Row (b, i) kept cand_count[row] (score, block) pairs in ascending block order
+// at cand_score/cand_idx + row*cap (row = b*L + i); a count above `cap` means
+// the list overflowed and the row's scores are recomputed here from q~ and k̄.
+__global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
+    int64_t L, int64_t q_offset, int budget, int cap,
+    const float *__restrict__ cand_score, const int32_t *__restrict__ cand_idx,
+    const int32_t *__restrict__ cand_count, int32_t *__restrict__ block_idx, int64_t bi_bstride,
+    const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar, int64_t nblk_cap)
+{
+    __shared__ uint32_t hist[kSelMaxBins];
+    __shared__ uint32_t keys[kMaxCandCap];
+    __shared__ float qs[kIdxHeads * kIdxDim];
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int64_t b = row / L;
+    const int64_t i = row - b * L;
+    const int64_t o = (q_offset + i) / kBlock;
+    int32_t *out = block_idx + b * bi_bstride + i * budget;
+    if (take_all(o, budget, out)) return;
+    const int64_t c = cand_count[row];
+    if (c <= cap) {
+        const uint32_t *src = reinterpret_cast<const uint32_t *>(cand_score + row * cap);
+        for (int64_t j = tid; j < c; j += kSelThreads) keys[j] = src[j];
+        __syncthreads();
+        const int32_t *ids = cand_idx + row * cap;
+        radix_topk(c, budget, [&](int64_t j) { return keys[j]; }, [&](int64_t j) { return ids[j]; }, out, hist);
+        return;
+    }
+    // Overflow: recompute I[p][j] = sum_h ReLU(<q~_h, k̄_j>) for every candidate.
+    const bf16_t *qr = qrot + b * qrot_bstride + i * kIdxHeads * kIdxDim;
+    for (int x = tid; x < kIdxHeads * kIdxDim; x += kSelThreads) qs[x] = bf16_to_f32(qr[x]);
+    __syncthreads();
+    const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
+    auto score = [&](int64_t j) -> uint32_t { return recompute_score(qs, kb, j); };
+    radix_topk(o, budget, score, [](int64_t j) { return j; }, out, hist);
 }
 
 hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, const int32_t *cache_len,
@@ -151,6 +231,20 @@ hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
     if (rows == 0) return hipSuccess;
     hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0, st, L, q_offset,
                        cache_len, ncol, scores, sc_bstride, block_idx, bi_bstride, budget);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_compact(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int budget, int cap,
+                                 const float *cand_score, const int32_t *cand_idx, const int32_t *cand_count,
+                                 int32_t *block_idx, int64_t bi_bstride, const bf16_t *qrot, int64_t qrot_bstride,
+                                 const bf16_t *kbar, int64_t nblk_cap)
+{
+    const int64_t rows = static_cast<int64_t>(B) * L;
+    if (rows == 0) return hipSuccess;
+    if (cap > kMaxCandCap) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(select_compact_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0, st, L,
+                       q_offset, budget, cap, cand_score, cand_idx, cand_count, block_idx, bi_bstride, qrot,
+                       qrot_bstride, kbar, nblk_cap);
     return hipGetLastError();
 }
 

@@ -24,6 +24,11 @@ hipError_t launch_indexer_scores(hipStream_t, int32_t, int64_t, int64_t, int64_t
                                  const bf16_t *, float *, int64_t, bool);
 hipError_t launch_select(hipStream_t, int32_t, int64_t, int64_t, const int32_t *, int64_t, const float *, int64_t,
                          int32_t *, int64_t, int);
+hipError_t launch_indexer_topk(hipStream_t, int32_t, int64_t, int64_t, int64_t, int, int, const bf16_t *, int64_t,
+                               const bf16_t *, float *, int32_t *, int32_t *);
+hipError_t launch_select_compact(hipStream_t, int32_t, int64_t, int64_t, int, int, const float *, const int32_t *,
+                                 const int32_t *, int32_t *, int64_t, const bf16_t *, int64_t, const bf16_t *,
+                                 int64_t);
 hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
                                  const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
 hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int, int, float,
@@ -40,6 +45,7 @@ using namespace qsa;
 
 struct qsa_handle {
     qsa_params p;
+    int cap;            // candidate list length per query of the fused index + select stage
     int device;
     float *d_cos;
     float *d_sin;
@@ -50,8 +56,9 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-// Score-matrix slice of one qsa_forward sub-chunk: at most this many bytes.
-constexpr size_t kForwardScoreBytes = size_t(2) << 30;
+// Candidate lists of one fused index + select launch: at most this many bytes.
+constexpr size_t kCandBytes = size_t(4) << 30;
+constexpr int kDefaultCap = 8192;
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
@@ -80,10 +87,10 @@ struct DeviceGuard {
 Tables tables(const qsa_handle *h) { return Tables{h->d_cos, h->d_sin}; }
 int64_t nblk_cap(const qsa_handle *h) { return h->p.max_ctx / kBlock; }
 
-// Rows of one qsa_forward score sub-chunk.
-int64_t forward_rows(int32_t B, int64_t L, int64_t ncol) {
-    const size_t per_row = static_cast<size_t>(B) * static_cast<size_t>(ncol) * 4u;
-    int64_t rows = static_cast<int64_t>(kForwardScoreBytes / (per_row ? per_row : 1));
+// Query rows of one fused index + select launch.
+int64_t cand_rows(int32_t B, int64_t L, int cap) {
+    const size_t per_row = static_cast<size_t>(B) * static_cast<size_t>(cap) * 8u;
+    int64_t rows = static_cast<int64_t>(kCandBytes / per_row);
     rows = (rows / 64) * 64;
     if (rows < 64) rows = 64;
     return rows < L ? rows : L;
@@ -95,15 +102,17 @@ int decode_splits(int32_t B) {
 }
 
 // Workspace of the fused index + select stage: rotated indexer queries, then
-// the score slice of one query sub-chunk (never the whole causal matrix).
-struct IdxSelLayout { size_t qrot, scores, total; int64_t rows, ncol; };
-IdxSelLayout index_select_layout(int32_t B, int64_t L, int64_t q_offset) {
+// the candidate lists (score, block) and counts of one launch of query rows.
+struct IdxSelLayout { size_t qrot, cscore, cidx, ccount, total; int64_t rows; };
+IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     IdxSelLayout f{};
-    f.ncol = (q_offset + L + kBlock - 1) / kBlock;
-    f.rows = forward_rows(B, L, f.ncol);
+    f.rows = cand_rows(B, L, cap);
+    const size_t n = static_cast<size_t>(B) * f.rows;
     f.qrot = 0;
-    f.scores = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
-    f.total = f.scores + align_up(static_cast<size_t>(B) * f.rows * f.ncol * 4);
+    f.cscore = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
+    f.cidx = f.cscore + align_up(n * cap * 4);
+    f.ccount = f.cidx + align_up(n * cap * 4);
+    f.total = f.ccount + align_up(n * 4);
     return f;
 }
 
@@ -127,17 +136,21 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
                             const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *bidx, char *w,
                             const IdxSelLayout &f) {
     bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
-    float *scores = reinterpret_cast<float *>(w + f.scores);
+    float *cscore = reinterpret_cast<float *>(w + f.cscore);
+    int32_t *cidx = reinterpret_cast<int32_t *>(w + f.cidx);
+    int32_t *ccount = reinterpret_cast<int32_t *>(w + f.ccount);
     const int budget = h->p.budget_blocks;
+    const int64_t qstride = L * kIdxHeads * kIdxDim;
     hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
     for (int64_t r0 = 0; r0 < L && e == hipSuccess; r0 += f.rows) {
         const int64_t nr = (r0 + f.rows < L) ? f.rows : L - r0;
         const int64_t pos0 = q_offset + r0;
-        e = launch_indexer_scores(st, B, nr, pos0, f.ncol, nblk_cap(h), qrot + r0 * kIdxHeads * kIdxDim,
-                                  L * kIdxHeads * kIdxDim, kbar_cache, scores, f.rows * f.ncol, false);
+        const bf16_t *qr = qrot + r0 * kIdxHeads * kIdxDim;
+        e = launch_indexer_topk(st, B, nr, pos0, nblk_cap(h), budget, h->cap, qr, qstride, kbar_cache, cscore, cidx,
+                                ccount);
         if (e == hipSuccess)
-            e = launch_select(st, B, nr, pos0, nullptr, f.ncol, scores, f.rows * f.ncol, bidx + r0 * budget,
-                              L * budget, budget);
+            e = launch_select_compact(st, B, nr, pos0, budget, h->cap, cscore, cidx, ccount, bidx + r0 * budget,
+                                      L * budget, qr, qstride, kbar_cache, nblk_cap(h));
     }
     return e;
 }
@@ -185,9 +198,9 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
     *out = nullptr;
     const qsa_params &p = *params;
     if (p.n_q_heads != kQHeads || p.n_kv_heads != kKVHeads || p.head_dim != kHeadDim || p.rope_dim != kRopeDim ||
-        p.n_idx_heads != kIdxHeads || p.idx_dim != kIdxDim || p.idx_rope_dim != 64 || p.block != kBlock ||
-        p.reserved0 != 0)
+        p.n_idx_heads != kIdxHeads || p.idx_dim != kIdxDim || p.idx_rope_dim != 64 || p.block != kBlock)
         return QSA_ERR_UNSUPPORTED;
+    if (p.topk_cap != 0 && (p.topk_cap < 64 || p.topk_cap > kDefaultCap)) return QSA_ERR_SHAPE;
     if (p.budget_blocks < 1 || p.budget_blocks > kMaxBudget) return QSA_ERR_SHAPE;
     if (p.max_ctx < kBlock || p.max_ctx % kBlock != 0 || p.max_ctx > (int64_t(1) << 30)) return QSA_ERR_SHAPE;
     if (!(p.rope_theta > 1.0) || !isfinite(p.rope_theta)) return QSA_ERR_SHAPE;
@@ -205,6 +218,7 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
     qsa_handle *h = static_cast<qsa_handle *>(calloc(1, sizeof(qsa_handle)));
     if (!h) return QSA_ERR_SHAPE;
     h->p = p;
+    h->cap = p.topk_cap ? p.topk_cap : kDefaultCap;
     h->device = device;
     double sigma = 1.0 / sqrt(static_cast<double>(kHeadDim));
     if (p.yarn_factor > 1.0) {
@@ -250,9 +264,9 @@ size_t qsa_workspace_size(const qsa_handle *h, int op, int32_t batch, int64_t le
     case QSA_OP_INDEX:
         return align_up(static_cast<size_t>(batch) * len * kIdxHeads * kIdxDim * 2);
     case QSA_OP_INDEX_SELECT:
-        return index_select_layout(batch, len, q_offset).total;
+        return index_select_layout(batch, len, h->cap).total;
     case QSA_OP_FORWARD:
-        return index_select_layout(batch, len, q_offset).total +
+        return index_select_layout(batch, len, h->cap).total +
                align_up(static_cast<size_t>(batch) * len * h->p.budget_blocks * 4);
     case QSA_OP_DECODE:
         return decode_layout(h, batch, q_offset).total;
@@ -327,7 +341,7 @@ qsa_status qsa_index_select(const qsa_handle *h, void *stream, int32_t B, int64_
     qsa_status s = check_chunk(h, B, L, q_offset, true);
     if (s != QSA_OK || L == 0) return s;
     if ((s = check_ptrs({q_idx, kbar_cache, block_idx, ws})) != QSA_OK) return s;
-    const IdxSelLayout f = index_select_layout(B, L, q_offset);
+    const IdxSelLayout f = index_select_layout(B, L, h->cap);
     if (ws_bytes < f.total) return QSA_ERR_WORKSPACE;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
@@ -344,7 +358,7 @@ qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, 
     if (s != QSA_OK || L == 0) return s;
     if ((s = check_ptrs({q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, ws})) != QSA_OK) return s;
     if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
-    const IdxSelLayout f = index_select_layout(B, L, q_offset);
+    const IdxSelLayout f = index_select_layout(B, L, h->cap);
     const size_t bidx_off = f.total;
     const size_t total = bidx_off + align_up(static_cast<size_t>(B) * L * h->p.budget_blocks * 4);
     if (ws_bytes < total) return QSA_ERR_WORKSPACE;

@@ -102,7 +102,9 @@ typedef struct qsa_params {
     int32_t idx_rope_dim;   /* 64 */
     int32_t block;          /* 4 */
     int32_t budget_blocks;  /* 1..512 */
-    int32_t reserved0;      /* must be 0 */
+    int32_t topk_cap;       /* candidate list per query of the fused index + select
+                               stage: 0 = 8192, else 64..8192 (smaller lists save
+                               workspace; a list that overflows is recomputed exactly) */
     int64_t max_ctx;        /* cache capacity in tokens, multiple of 4, >= 4 */
     double  rope_theta;     /* 1e7 */
     double  yarn_factor;    /* 1.0 = off, else > 1 */
@@ -173,10 +175,14 @@ qsa_status qsa_index(const qsa_handle *h, void *stream, int32_t B, int64_t L, in
 qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
                       const float *scores, int32_t *block_idx);
 
-/* qsa_index followed by qsa_select without handing the score matrix to the
- * caller: scores live only in the workspace, one bounded slice of query rows
- * at a time (at most 2 GiB), so any context length fits.  Same results as the
- * two calls.  ws: qsa_workspace_size(QSA_OP_INDEX_SELECT) bytes. */
+/* qsa_index followed by qsa_select without materialising the score matrix:
+ * one fused kernel computes the same scores tile by tile and keeps, per query,
+ * only the (score, block) pairs at or above a running threshold that provably
+ * lies at or below the query's budget-th largest score; the exact selection is
+ * then taken from that short list.  A list longer than topk_cap is recomputed
+ * exactly for its row.  Same results as qsa_index + qsa_select.  The
+ * workspace holds the rotated queries and the lists of at most 4 GiB of query
+ * rows at a time.  ws: qsa_workspace_size(QSA_OP_INDEX_SELECT) bytes. */
 qsa_status qsa_index_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
                             const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *block_idx,
                             void *ws, size_t ws_bytes);

@@ -37,7 +37,7 @@ def test_default_params_are_the_layer_shapes():
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("n_q_heads", 32, 3), ("head_dim", 128, 3), ("block", 8, 3), ("reserved0", 1, 3),
+    ("n_q_heads", 32, 3), ("head_dim", 128, 3), ("block", 8, 3), ("topk_cap", 1, 2), ("topk_cap", 9000, 2),
     ("budget_blocks", 0, 2), ("budget_blocks", 513, 2), ("max_ctx", 6, 2), ("max_ctx", 0, 2),
     ("yarn_factor", 0.5, 2), ("rope_theta", 0.0, 2)])
 def test_create_rejects_bad_params_on_host(field, value, status):

@@ -116,6 +116,48 @@ def test_index_scores(B, L, q_offset):
     assert torch.equal(bidx_a, bidx_b)
 
 
+# ---------------------------------------------------------------- fused index + select
+def _index_paths(h, x, xd, B, L):
+    c = Q.alloc_caches(h, B)
+    Q.qsa_append(h, B, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    ncol = (L + 3) // 4
+    scores = torch.empty((B, L, ncol), dtype=torch.float32, device=DEV)
+    Q.qsa_index(h, B, L, 0, xd["q_idx"], c["kbar_cache"], scores, Q.workspace(h, Q.QSA_OP_INDEX, B, L, 0))
+    a = torch.empty((B, L, h.budget), dtype=torch.int32, device=DEV)
+    Q.qsa_select(h, B, L, 0, scores, a)
+    f = torch.empty_like(a)
+    Q.qsa_index_select(h, B, L, 0, xd["q_idx"], c["kbar_cache"], f, Q.workspace(h, Q.QSA_OP_INDEX_SELECT, B, L, 0))
+    torch.cuda.synchronize()
+    return a, f
+
+
+@pytest.mark.parametrize("budget", [17, 64, 512])
+def test_index_select_fused_equals_score_matrix_path(budget):
+    """The fused streaming kernel selects exactly what select(score matrix) selects."""
+    B, L = 2, 6000
+    w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 40 + budget)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=6144, budget_blocks=budget)
+    a, f = _index_paths(h, x, xd, B, L)
+    assert torch.equal(a, f)
+
+
+def test_index_select_overflow_fallback():
+    """With a candidate list far shorter than needed every long row overflows and
+    is recomputed exactly: the result still meets the oracle."""
+    B, L, budget = 1, 5000, 64
+    w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 41)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=5120, budget_blocks=budget, topk_cap=64)
+    a, f = _index_paths(h, x, xd, B, L)
+    p = O.Params(budget=budget)
+    lay = oracle_layer(x, 0, p)
+    fb = f.cpu().numpy()
+    for i in list(range(250, 270)) + list(range(4990, 5000)) + [1234, 3000]:
+        _, sel, sc = lay.row(i, bits(x["q"][0, i]), bits(x["q_idx"][0, i]))
+        check_selection(fb[0, i], sel, sc, budget, i // 4, "row %d" % i)
+
+
 # ---------------------------------------------------------------- select
 @pytest.mark.parametrize("mode", ["float", "coarse", "zeros", "mixed"])
 @pytest.mark.parametrize("budget", [1, 7, 64, 512])
