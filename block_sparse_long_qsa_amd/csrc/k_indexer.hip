@@ -178,7 +178,8 @@ __device__ __forceinline__ float topk_bin_edge(int b) {
 __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, int cap,
     const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar,
-    float *__restrict__ cand_score, int32_t *__restrict__ cand_idx, int32_t *__restrict__ cand_count)
+    float *__restrict__ cand_score, int32_t *__restrict__ cand_idx, int32_t *__restrict__ cand_count,
+    int32_t *__restrict__ cand_meta)
 {
     __shared__ __attribute__((aligned(16))) bf16_t lds[2][kIdxSubCols * kLdsRow];
     __shared__ uint32_t hist[kIdxQueriesPerWG][kTopkBins];
@@ -229,23 +230,32 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         }
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
-    auto stage = [&](int buf, int64_t cs) {
+    // k̄ tiles: the next tile is loaded into registers before the current
+    // tile's MFMAs and written to LDS after them, so the load latency overlaps
+    // the matrix work.
+    u32x4 pre[4];
+    auto fetch = [&](int64_t cs) {
         for (int it = 0; it < 4; ++it) {
             const int chunk = it * 256 + tid;
-            const int row = chunk >> 4, c = chunk & 15;
-            const int64_t blk = cs + row;
-            u32x4 val = u32x4{0, 0, 0, 0};
-            if (blk < nblk_cap) val = *reinterpret_cast<const u32x4 *>(kb + blk * kIdxDim + 8 * c);
-            *reinterpret_cast<u32x4 *>(&lds[buf][row * kLdsRow + 8 * c]) = val;
+            const int64_t blk = cs + (chunk >> 4);
+            pre[it] = (blk < nblk_cap) ? *reinterpret_cast<const u32x4 *>(kb + blk * kIdxDim + 8 * (chunk & 15))
+                                       : u32x4{0, 0, 0, 0};
+        }
+    };
+    auto put = [&](int buf) {
+        for (int it = 0; it < 4; ++it) {
+            const int chunk = it * 256 + tid;
+            *reinterpret_cast<u32x4 *>(&lds[buf][(chunk >> 4) * kLdsRow + 8 * (chunk & 15)]) = pre[it];
         }
     };
 
     int buf = 0;
-    stage(0, 0);
+    fetch(0);
+    put(0);
     __syncthreads();
     for (int64_t cs = 0; cs < o_hi; cs += kIdxSubCols) {
-        if (cs + kIdxSubCols < o_hi) stage(buf ^ 1, cs + kIdxSubCols);
-
+        const bool more = cs + kIdxSubCols < o_hi;
+        if (more) fetch(cs + kIdxSubCols);
         f32x16 acc[2][2];
         for (int ct = 0; ct < 2; ++ct) {
             bf16x8 bfrag[8];
@@ -319,21 +329,46 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                     for (int i = 0; i < 4; ++i) tau[a][i] = tau_s[16 * wave + 8 * a + 2 * i + half];
             }
         }
+        if (more) put(buf ^ 1);
         __syncthreads();
         buf ^= 1;
     }
-    __syncthreads();
-    if (tid < kIdxQueriesPerWG && q0 + tid < L) cand_count[b * L + q0 + tid] = static_cast<int32_t>(cnt[tid]);
+    // final boundary bin of each query: the highest bin whose suffix count
+    // reaches the budget, and the number of kept scores above it
+    for (int j = 0; j < 16; ++j) {
+        const int ql = 16 * wave + j;
+        const int64_t q = q0 + ql;
+        if (q >= L) break;
+        const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
+        uint32_t incl = h0 + h1;
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t other = __shfl_down(incl, off);
+            if (lane + off < 64) incl += other;
+        }
+        const uint32_t c1 = incl - h0;
+        const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
+                         : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
+        const uint32_t above = (cand == 2 * lane + 1) ? c1 - h1 : incl - h0;    // bins > cand
+        const uint64_t vm = __ballot(cand >= 0);
+        const int hi = vm ? 63 - __clzll(vm) : 0;
+        const int bin = vm ? __shfl(cand, hi) : -1;
+        const uint32_t ab = __shfl(above, hi);
+        if (lane == 0) {
+            cand_count[b * L + q] = static_cast<int32_t>(cnt[ql]);
+            cand_meta[2 * (b * L + q)] = bin;
+            cand_meta[2 * (b * L + q) + 1] = static_cast<int32_t>(vm ? ab : 0);
+        }
+    }
 }
 
 hipError_t launch_indexer_topk(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget,
                                int cap, const bf16_t *qrot, int64_t qrot_bstride, const bf16_t *kbar,
-                               float *cand_score, int32_t *cand_idx, int32_t *cand_count)
+                               float *cand_score, int32_t *cand_idx, int32_t *cand_count, int32_t *cand_meta)
 {
     if (L <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((L + kIdxQueriesPerWG - 1) / kIdxQueriesPerWG), static_cast<unsigned>(B));
     hipLaunchKernelGGL(indexer_topk_kernel, grid, dim3(256), 0, st, L, q_offset, nblk_cap, budget, cap, qrot,
-                       qrot_bstride, kbar, cand_score, cand_idx, cand_count);
+                       qrot_bstride, kbar, cand_score, cand_idx, cand_count, cand_meta);
     return hipGetLastError();
 }
 

@@ -185,18 +185,53 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     radix_topk(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
 }
 
+// Workgroup-wide exclusive prefix sum of one value per thread (256 threads).
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wsum /* LDS [4] */, uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) before += wsum[w];
+        total += wsum[w];
+    }
+    __syncthreads();
+    return before + incl - v;
+}
+
+__device__ __forceinline__ int score_bin(uint32_t bits) {
+    const int b = static_cast<int>(bits >> 20) - 951;      // same bins as the fused indexer kernel
+    return b < 0 ? 0 : (b > 127 ? 127 : b);
+}
+
 // Selection from the candidate lists of the fused index + select kernel.
 // Row (b, i) kept cand_count[row] (score, block) pairs in ascending block order
-// at cand_score/cand_idx + row*cap (row = b*L + i); a count above `cap` means
-// the list overflowed and the row's scores are recomputed here from q~ and k̄.
+// at cand_score/cand_idx + row*cap (row = b*L + i).  cand_meta[row] = (bin,
+// above): every kept score in a higher 128-bin log bin than `bin` is selected
+// (`above` of them), none below is, and the remaining budget - above come from
+// the scores inside `bin`, ranked exactly.  A count above `cap` means the list
+// overflowed: the row's scores are recomputed here from q~ and k̄.
+constexpr int kBoundaryMax = 2048;
 __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
     int64_t L, int64_t q_offset, int budget, int cap,
     const float *__restrict__ cand_score, const int32_t *__restrict__ cand_idx,
-    const int32_t *__restrict__ cand_count, int32_t *__restrict__ block_idx, int64_t bi_bstride,
+    const int32_t *__restrict__ cand_count, const int32_t *__restrict__ cand_meta,
+    int32_t *__restrict__ block_idx, int64_t bi_bstride,
     const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar, int64_t nblk_cap)
 {
     __shared__ uint32_t hist[kSelMaxBins];
     __shared__ uint32_t keys[kMaxCandCap];
+    __shared__ uint32_t bl[kBoundaryMax];               // list positions of the boundary-bin scores
+    __shared__ int32_t selpos[kMaxBudget];              // boundary positions selected
+    __shared__ uint32_t selbits[kMaxCandCap / 32];
+    __shared__ uint32_t wsum[4];
     __shared__ float qs[kIdxHeads * kIdxDim];
     const int tid = threadIdx.x;
     const int64_t row = blockIdx.x;
@@ -208,10 +243,63 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
     const int64_t c = cand_count[row];
     if (c <= cap) {
         const uint32_t *src = reinterpret_cast<const uint32_t *>(cand_score + row * cap);
-        for (int64_t j = tid; j < c; j += kSelThreads) keys[j] = src[j];
-        __syncthreads();
         const int32_t *ids = cand_idx + row * cap;
-        radix_topk(c, budget, [&](int64_t j) { return keys[j]; }, [&](int64_t j) { return ids[j]; }, out, hist);
+        const int bstar = cand_meta[2 * row];
+        const uint32_t k_rem = static_cast<uint32_t>(budget - cand_meta[2 * row + 1]);
+        for (int64_t j = tid; j < c; j += kSelThreads) keys[j] = src[j];
+        for (int x = tid; x < kMaxCandCap / 32; x += kSelThreads) selbits[x] = 0;
+        __syncthreads();
+        // contiguous segment of the list per thread
+        const int seg = static_cast<int>((c + kSelThreads - 1) / kSelThreads);
+        const int j0 = tid * seg;
+        const int j1 = (j0 + seg < c) ? j0 + seg : static_cast<int>(c);
+        uint32_t nb = 0;
+        for (int j = j0; j < j1; ++j) nb += score_bin(keys[j]) == bstar;
+        uint32_t n_b;
+        uint32_t at = block_exclusive_scan(nb, wsum, n_b);
+        if (n_b > kBoundaryMax || bstar < 0 || n_b < k_rem) {   // crowded bin (or no bin): radix over the list
+            radix_topk(c, budget, [&](int64_t j) { return keys[j]; }, [&](int64_t j) { return ids[j]; }, out, hist);
+            return;
+        }
+        for (int j = j0; j < j1; ++j)
+            if (score_bin(keys[j]) == bstar) bl[at++] = static_cast<uint32_t>(j);
+        __syncthreads();
+        if (n_b == k_rem) {
+            for (uint32_t t = tid; t < n_b; t += kSelThreads) atomicOr(&selbits[bl[t] >> 5], 1u << (bl[t] & 31));
+        } else if (n_b <= kSelThreads) {
+            // rank inside the bin: order (score desc, position desc)
+            if (static_cast<uint32_t>(tid) < n_b) {
+                const uint32_t px = bl[tid], kx = keys[px];
+                uint32_t r = 0;
+                for (uint32_t u = 0; u < n_b; ++u) {
+                    const uint32_t py = bl[u], ky = keys[py];
+                    r += (ky > kx) || (ky == kx && py > px);
+                }
+                if (r < k_rem) atomicOr(&selbits[px >> 5], 1u << (px & 31));
+            }
+        } else {
+            radix_topk(n_b, static_cast<int>(k_rem), [&](int64_t t) { return keys[bl[t]]; },
+                       [&](int64_t t) { return static_cast<int64_t>(bl[t]); }, selpos, hist);
+            __syncthreads();
+            for (uint32_t t = tid; t < k_rem; t += kSelThreads)
+                atomicOr(&selbits[selpos[t] >> 5], 1u << (selpos[t] & 31));
+        }
+        __syncthreads();
+        // ordered emission
+        uint32_t ns = 0;
+        for (int j = j0; j < j1; ++j) {
+            const int bj = score_bin(keys[j]);
+            ns += bj > bstar || (bj == bstar && ((selbits[j >> 5] >> (j & 31)) & 1u));
+        }
+        uint32_t tot;
+        uint32_t w = block_exclusive_scan(ns, wsum, tot);
+        for (int j = j0; j < j1; ++j) {
+            const int bj = score_bin(keys[j]);
+            if (bj > bstar || (bj == bstar && ((selbits[j >> 5] >> (j & 31)) & 1u))) {
+                if (w < static_cast<uint32_t>(budget)) out[w] = ids[j];
+                ++w;
+            }
+        }
         return;
     }
     // Overflow: recompute I[p][j] = sum_h ReLU(<q~_h, k̄_j>) for every candidate.
@@ -236,14 +324,14 @@ hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
 
 hipError_t launch_select_compact(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int budget, int cap,
                                  const float *cand_score, const int32_t *cand_idx, const int32_t *cand_count,
-                                 int32_t *block_idx, int64_t bi_bstride, const bf16_t *qrot, int64_t qrot_bstride,
+                                 const int32_t *cand_meta, int32_t *block_idx, int64_t bi_bstride, const bf16_t *qrot, int64_t qrot_bstride,
                                  const bf16_t *kbar, int64_t nblk_cap)
 {
     const int64_t rows = static_cast<int64_t>(B) * L;
     if (rows == 0) return hipSuccess;
     if (cap > kMaxCandCap) return hipErrorInvalidValue;
     hipLaunchKernelGGL(select_compact_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0, st, L,
-                       q_offset, budget, cap, cand_score, cand_idx, cand_count, block_idx, bi_bstride, qrot,
+                       q_offset, budget, cap, cand_score, cand_idx, cand_count, cand_meta, block_idx, bi_bstride, qrot,
                        qrot_bstride, kbar, nblk_cap);
     return hipGetLastError();
 }

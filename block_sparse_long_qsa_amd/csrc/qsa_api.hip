@@ -25,10 +25,10 @@ hipError_t launch_indexer_scores(hipStream_t, int32_t, int64_t, int64_t, int64_t
 hipError_t launch_select(hipStream_t, int32_t, int64_t, int64_t, const int32_t *, int64_t, const float *, int64_t,
                          int32_t *, int64_t, int);
 hipError_t launch_indexer_topk(hipStream_t, int32_t, int64_t, int64_t, int64_t, int, int, const bf16_t *, int64_t,
-                               const bf16_t *, float *, int32_t *, int32_t *);
+                               const bf16_t *, float *, int32_t *, int32_t *, int32_t *);
 hipError_t launch_select_compact(hipStream_t, int32_t, int64_t, int64_t, int, int, const float *, const int32_t *,
-                                 const int32_t *, int32_t *, int64_t, const bf16_t *, int64_t, const bf16_t *,
-                                 int64_t);
+                                 const int32_t *, const int32_t *, int32_t *, int64_t, const bf16_t *, int64_t,
+                                 const bf16_t *, int64_t);
 hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
                                  const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
 hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int, int, float,
@@ -103,7 +103,7 @@ int decode_splits(int32_t B) {
 
 // Workspace of the fused index + select stage: rotated indexer queries, then
 // the candidate lists (score, block) and counts of one launch of query rows.
-struct IdxSelLayout { size_t qrot, cscore, cidx, ccount, total; int64_t rows; };
+struct IdxSelLayout { size_t qrot, cscore, cidx, ccount, cmeta, total; int64_t rows; };
 IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     IdxSelLayout f{};
     f.rows = cand_rows(B, L, cap);
@@ -112,7 +112,8 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     f.cscore = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
     f.cidx = f.cscore + align_up(n * cap * 4);
     f.ccount = f.cidx + align_up(n * cap * 4);
-    f.total = f.ccount + align_up(n * 4);
+    f.cmeta = f.ccount + align_up(n * 4);
+    f.total = f.cmeta + align_up(n * 8);
     return f;
 }
 
@@ -139,6 +140,7 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
     float *cscore = reinterpret_cast<float *>(w + f.cscore);
     int32_t *cidx = reinterpret_cast<int32_t *>(w + f.cidx);
     int32_t *ccount = reinterpret_cast<int32_t *>(w + f.ccount);
+    int32_t *cmeta = reinterpret_cast<int32_t *>(w + f.cmeta);
     const int budget = h->p.budget_blocks;
     const int64_t qstride = L * kIdxHeads * kIdxDim;
     hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
@@ -147,9 +149,9 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
         const int64_t pos0 = q_offset + r0;
         const bf16_t *qr = qrot + r0 * kIdxHeads * kIdxDim;
         e = launch_indexer_topk(st, B, nr, pos0, nblk_cap(h), budget, h->cap, qr, qstride, kbar_cache, cscore, cidx,
-                                ccount);
+                                ccount, cmeta);
         if (e == hipSuccess)
-            e = launch_select_compact(st, B, nr, pos0, budget, h->cap, cscore, cidx, ccount, bidx + r0 * budget,
+            e = launch_select_compact(st, B, nr, pos0, budget, h->cap, cscore, cidx, ccount, cmeta, bidx + r0 * budget,
                                       L * budget, qr, qstride, kbar_cache, nblk_cap(h));
     }
     return e;
