@@ -15,6 +15,8 @@
 // are staged through LDS (double buffered) and shared by the 4 waves.
 // Workgroups whose column range lies wholly past the causal limit of their
 // queries exit at once (causal tile skipping).
+#include <type_traits>
+
 #include "qsa_common.h"
 
 namespace qsa {
@@ -23,6 +25,13 @@ constexpr int kIdxQueriesPerWG = 64;
 constexpr int kIdxColsPerWG = 512;
 constexpr int kIdxSubCols = 64;
 constexpr int kLdsRow = kIdxDim + 8;   // padded row (elements) against bank conflicts
+
+// ReLU as a clamp to [0, FLT_MAX] (v_med3_f32): one instruction, no NaN
+// canonicalisation (inputs are finite).  May return -0 for -0.
+__device__ __forceinline__ float relu_fast(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 3.402823466e38f); }
+__device__ __forceinline__ float relu_sum4_fast(float a, float b, float c, float d) {
+    return (relu_fast(a) + relu_fast(b)) + (relu_fast(c) + relu_fast(d));
+}
 
 __device__ __forceinline__ float relu_sum4(float a, float b, float c, float d) {
     float s = fmaxf(a, 0.0f) + fmaxf(b, 0.0f) + fmaxf(c, 0.0f) + fmaxf(d, 0.0f);
@@ -222,6 +231,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     // per lane: the 8 queries it scores, their candidate limits and thresholds
     int32_t qo[2][4];
     float tau[2][4];
+    const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
     for (int a = 0; a < 2; ++a)
         for (int i = 0; i < 4; ++i) {
             const int64_t q = q0 + 16 * wave + 8 * a + 2 * i + half;
@@ -249,6 +259,28 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         }
     };
 
+    // Append this lane's score if its bit is set in m (lanes 0..31 and 32..63
+    // carry two different queries); positions follow lane order, i.e. block order.
+    auto append = [&](uint64_t m, float s, int32_t col, int ql) {
+        const uint32_t mh = half ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
+        const uint32_t bit = 1u << (lane & 31);
+        const uint32_t base = cnt[ql];
+        if (mh & bit) {
+            const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
+            const uint32_t pos = base + static_cast<uint32_t>(__popc(mh & (bit - 1u)));
+            const int64_t row = b * L + q0 + ql;
+            if (pos < static_cast<uint32_t>(cap)) {
+                cand_score[row * cap + pos] = sc;
+                cand_idx[row * cap + pos] = col;
+            }
+            atomicAdd(&hist[ql][topk_bin(sc)], 1u);
+        }
+        if ((lane & 31) == 0 && mh != 0) {
+            cnt[ql] = base + static_cast<uint32_t>(__popc(mh));
+            since[ql] += static_cast<uint32_t>(__popc(mh));
+        }
+    };
+
     int buf = 0;
     fetch(0);
     put(0);
@@ -268,36 +300,33 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             }
         }
         bool any = false;
-        for (int a = 0; a < 2; ++a) {
-            for (int i = 0; i < 4; ++i) {
-                const int ql = 16 * wave + 8 * a + 2 * i + half;     // local query of this lane
-                for (int ct = 0; ct < 2; ++ct) {
-                    const int32_t col = static_cast<int32_t>(cs) + 32 * ct + (lane & 31);
-                    const f32x16 &c = acc[a][ct];
-                    const float s = relu_sum4(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
-                    const bool keep = col < qo[a][i] && s >= tau[a][i];
-                    const uint64_t m = __ballot(keep);
-                    if (m == 0) continue;                            // wave-uniform
-                    any = true;
-                    const uint32_t mh = half ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
-                    const uint32_t below = mh & ((1u << (lane & 31)) - 1u);
-                    const uint32_t base = cnt[ql];
-                    if (keep) {
-                        const uint32_t pos = base + static_cast<uint32_t>(__popc(below));
-                        const int64_t row = b * L + q0 + ql;
-                        if (pos < static_cast<uint32_t>(cap)) {
-                            cand_score[row * cap + pos] = s;
-                            cand_idx[row * cap + pos] = col;
-                        }
-                        atomicAdd(&hist[ql][topk_bin(s)], 1u);
-                    }
-                    if ((lane & 31) == 0 && mh != 0) {
-                        cnt[ql] = base + static_cast<uint32_t>(__popc(mh));
-                        since[ql] += static_cast<uint32_t>(__popc(mh));
+        // Columns of this tile lie below every query's causal limit except on
+        // the last one or two tiles of the row range (queries of a tile span 16
+        // blocks), so the causal mask is applied there only.
+        auto epilogue = [&](auto masked) {
+            for (int a = 0; a < 2; ++a) {
+                for (int i = 0; i < 4; ++i) {
+                    const int ql = 16 * wave + 8 * a + 2 * i + half;     // local query of this lane
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const int32_t col = static_cast<int32_t>(cs) + 32 * ct + (lane & 31);
+                        const f32x16 &c = acc[a][ct];
+                        const float s = relu_sum4_fast(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
+                        uint64_t m;
+                        if constexpr (decltype(masked)::value)
+                            m = __builtin_amdgcn_ballot_w64(s >= tau[a][i] && col < qo[a][i]);
+                        else
+                            m = __builtin_amdgcn_ballot_w64(s >= tau[a][i]);
+                        if (m == 0) continue;                            // wave-uniform
+                        any = true;
+                        append(m, s, col, ql);
                     }
                 }
             }
-        }
+        };
+        if (cs + kIdxSubCols <= o_min)
+            epilogue(std::integral_constant<bool, false>{});
+        else
+            epilogue(std::integral_constant<bool, true>{});
         if (any) {
             // refresh the thresholds of this wave's queries that kept enough new scores
             bool changed = false;
