@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     if (tid < kIdxQueriesPerWG) {
         cnt[tid] = 0;
         since[tid] = 0;
-        tau_s[tid] = 0.0f;
+        tau_s[tid] = (q0 + tid < L) ? 0.0f : INFINITY;     // padding queries of a ragged tile keep nothing
     }
 
     bf16x8 afrag[2][8];
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         for (int i = 0; i < 4; ++i) {
             const int64_t q = q0 + 16 * wave + 8 * a + 2 * i + half;
             qo[a][i] = (q < L) ? static_cast<int32_t>((q_offset + q) / kBlock) : 0;
-            tau[a][i] = 0.0f;
+            tau[a][i] = (q < L) ? 0.0f : INFINITY;
         }
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         const uint32_t mh = half ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
         const uint32_t bit = 1u << (lane & 31);
         const uint32_t base = cnt[ql];
-        if (mh & bit) {
+        if ((mh & bit) && q0 + ql < L) {
             const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
             const uint32_t pos = base + static_cast<uint32_t>(__popc(mh & (bit - 1u)));
             const int64_t row = b * L + q0 + ql;
