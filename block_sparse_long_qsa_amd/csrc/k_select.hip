@@ -158,6 +158,34 @@ __device__ __noinline__ uint32_t recompute_score(const float *qs, const bf16_t *
     return __float_as_uint(s) & 0x7FFFFFFFu;
 }
 
+// Copy n 32-bit words from global memory into LDS: 16-byte loads when the
+// source is 16-byte aligned, several per thread issued before any store.
+__device__ __forceinline__ void stage_words(const uint32_t *__restrict__ src, int64_t n, uint32_t *dst)
+{
+    const int tid = threadIdx.x;
+    if ((reinterpret_cast<uintptr_t>(src) & 15u) == 0) {
+        const int64_t n4 = n >> 2;
+        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
+        int64_t j = tid;
+        for (; j + 3 * kSelThreads < n4; j += 4 * kSelThreads) {
+            const u32x4 a = s4[j], b = s4[j + kSelThreads], c = s4[j + 2 * kSelThreads], d = s4[j + 3 * kSelThreads];
+            reinterpret_cast<u32x4 *>(dst)[j] = a;
+            reinterpret_cast<u32x4 *>(dst)[j + kSelThreads] = b;
+            reinterpret_cast<u32x4 *>(dst)[j + 2 * kSelThreads] = c;
+            reinterpret_cast<u32x4 *>(dst)[j + 3 * kSelThreads] = d;
+        }
+        for (; j < n4; j += kSelThreads) reinterpret_cast<u32x4 *>(dst)[j] = s4[j];
+        for (int64_t t = (n4 << 2) + tid; t < n; t += kSelThreads) dst[t] = src[t];
+    } else {
+        int64_t j = tid;
+        for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {
+            const uint32_t a = src[j], b = src[j + kSelThreads], c = src[j + 2 * kSelThreads], d = src[j + 3 * kSelThreads];
+            dst[j] = a; dst[j + kSelThreads] = b; dst[j + 2 * kSelThreads] = c; dst[j + 3 * kSelThreads] = d;
+        }
+        for (; j < n; j += kSelThreads) dst[j] = src[j];
+    }
+}
+
 __device__ __forceinline__ bool take_all(int64_t o, int budget, int32_t *out) {
     if (o > budget) return false;
     for (int j = threadIdx.x; j < budget; j += kSelThreads) out[j] = (j < o) ? j : -1;
@@ -168,12 +196,15 @@ __device__ __forceinline__ bool take_all(int64_t o, int budget, int32_t *out) {
 // clamped to [0, q_offset] when cache_len is given: decode passes its bound); its
 // scores start at scores + b*sc_bstride + i*ncol and its selection at
 // block_idx + b*bi_bstride + i*budget.
+// Rows of up to `lds_words` scores are first staged in (dynamic) LDS so the
+// radix passes read on-chip memory; longer rows are read from global memory.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int64_t L, int64_t q_offset, const int32_t *__restrict__ cache_len, int64_t ncol,
     const float *__restrict__ scores, int64_t sc_bstride, int32_t *__restrict__ block_idx, int64_t bi_bstride,
-    int budget)
+    int budget, int64_t lds_words)
 {
     __shared__ uint32_t hist[kSelMaxBins];
+    extern __shared__ uint32_t rowbuf[];
     const int64_t row = blockIdx.x;
     const int64_t b = row / L;
     const int64_t i = row - b * L;
@@ -182,7 +213,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * sc_bstride + i * ncol);
     int32_t *out = block_idx + b * bi_bstride + i * budget;
     if (take_all(o, budget, out)) return;
-    radix_topk(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
+    if (o <= lds_words) {
+        stage_words(srow, o, rowbuf);
+        __syncthreads();
+        radix_topk(o, budget, [&](int64_t j) { return rowbuf[j]; }, [](int64_t j) { return j; }, out, hist);
+    } else {
+        radix_topk(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
+    }
 }
 
 // Workgroup-wide exclusive prefix sum of one value per thread (256 threads).
@@ -246,7 +283,7 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
         const int32_t *ids = cand_idx + row * cap;
         const int bstar = cand_meta[2 * row];
         const uint32_t k_rem = static_cast<uint32_t>(budget - cand_meta[2 * row + 1]);
-        for (int64_t j = tid; j < c; j += kSelThreads) keys[j] = src[j];
+        stage_words(src, c, keys);
         for (int x = tid; x < kMaxCandCap / 32; x += kSelThreads) selbits[x] = 0;
         __syncthreads();
         // contiguous segment of the list per thread
@@ -317,8 +354,18 @@ hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
 {
     const int64_t rows = static_cast<int64_t>(B) * L;
     if (rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0, st, L, q_offset,
-                       cache_len, ncol, scores, sc_bstride, block_idx, bi_bstride, budget);
+    // stage rows in LDS when one row fits beside the histogram (up to 36,864 scores)
+    const int64_t lds_words = (ncol <= 36864) ? ncol : 0;
+    const size_t dyn = static_cast<size_t>(lds_words) * 4;
+    static thread_local int lds_limit_set = 0;      // per thread: attribute calls are not stream-ordered
+    if (dyn > 64 * 1024 && !lds_limit_set) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(select_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 36864 * 4);
+        if (e != hipSuccess) return e;
+        lds_limit_set = 1;
+    }
+    hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), dyn, st, L, q_offset,
+                       cache_len, ncol, scores, sc_bstride, block_idx, bi_bstride, budget, lds_words);
     return hipGetLastError();
 }
 
