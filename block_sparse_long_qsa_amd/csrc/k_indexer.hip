@@ -192,14 +192,12 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
 {
     __shared__ __attribute__((aligned(16))) bf16_t lds[2][kIdxSubCols * kLdsRow];
     __shared__ uint32_t hist[kIdxQueriesPerWG][kTopkBins];
-    __shared__ uint32_t cnt[kIdxQueriesPerWG];
-    __shared__ uint32_t since[kIdxQueriesPerWG];
-    __shared__ float tau_s[kIdxQueriesPerWG];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int half = lane >> 5;
+    const uint32_t bit = 1u << (lane & 31);
     const int64_t b = blockIdx.y;
     const int64_t tile = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
     const int64_t q0 = tile * kIdxQueriesPerWG;
@@ -208,11 +206,6 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     if (o_hi <= budget) return;                 // every row of the tile keeps all its candidates
 
     for (int x = tid; x < kIdxQueriesPerWG * kTopkBins; x += 256) (&hist[0][0])[x] = 0;
-    if (tid < kIdxQueriesPerWG) {
-        cnt[tid] = 0;
-        since[tid] = 0;
-        tau_s[tid] = (q0 + tid < L) ? 0.0f : INFINITY;     // padding queries of a ragged tile keep nothing
-    }
 
     bf16x8 afrag[2][8];
     for (int a = 0; a < 2; ++a) {
@@ -228,21 +221,26 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             }
         }
     }
-    // per lane: the 8 queries it scores, their candidate limits and thresholds
+    // The wave scores queries 16*wave + j, j = 8a + 2i + p (p = lane half).
+    // Their kept counts, appends since the last threshold refresh and
+    // thresholds live in lane j of st_cnt / st_since / st_tau; tau_v is each
+    // lane's copy of its own query's threshold.  Padding queries of a ragged
+    // tile get an infinite threshold and keep nothing.
+    uint32_t st_cnt = 0, st_since = 0;
+    float st_tau = (lane < 16 && q0 + 16 * wave + lane < L) ? 0.0f : INFINITY;
+    float tau_v[2][4];
     int32_t qo[2][4];
-    float tau[2][4];
-    const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
     for (int a = 0; a < 2; ++a)
         for (int i = 0; i < 4; ++i) {
             const int64_t q = q0 + 16 * wave + 8 * a + 2 * i + half;
             qo[a][i] = (q < L) ? static_cast<int32_t>((q_offset + q) / kBlock) : 0;
-            tau[a][i] = (q < L) ? 0.0f : INFINITY;
+            tau_v[a][i] = (q < L) ? 0.0f : INFINITY;
         }
+    const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
     // k̄ tiles: the next tile is loaded into registers before the current
-    // tile's MFMAs and written to LDS after them, so the load latency overlaps
-    // the matrix work.
+    // tile's MFMAs and written to LDS after them.
     u32x4 pre[4];
     auto fetch = [&](int64_t cs) {
         for (int it = 0; it < 4; ++it) {
@@ -259,28 +257,6 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         }
     };
 
-    // Append this lane's score if its bit is set in m (lanes 0..31 and 32..63
-    // carry two different queries); positions follow lane order, i.e. block order.
-    auto append = [&](uint64_t m, float s, int32_t col, int ql) {
-        const uint32_t mh = half ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
-        const uint32_t bit = 1u << (lane & 31);
-        const uint32_t base = cnt[ql];
-        if ((mh & bit) && q0 + ql < L) {
-            const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
-            const uint32_t pos = base + static_cast<uint32_t>(__popc(mh & (bit - 1u)));
-            const int64_t row = b * L + q0 + ql;
-            if (pos < static_cast<uint32_t>(cap)) {
-                cand_score[row * cap + pos] = sc;
-                cand_idx[row * cap + pos] = col;
-            }
-            atomicAdd(&hist[ql][topk_bin(sc)], 1u);
-        }
-        if ((lane & 31) == 0 && mh != 0) {
-            cnt[ql] = base + static_cast<uint32_t>(__popc(mh));
-            since[ql] += static_cast<uint32_t>(__popc(mh));
-        }
-    };
-
     int buf = 0;
     fetch(0);
     put(0);
@@ -288,6 +264,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     for (int64_t cs = 0; cs < o_hi; cs += kIdxSubCols) {
         const bool more = cs + kIdxSubCols < o_hi;
         if (more) fetch(cs + kIdxSubCols);
+
         f32x16 acc[2][2];
         for (int ct = 0; ct < 2; ++ct) {
             bf16x8 bfrag[8];
@@ -306,19 +283,37 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         auto epilogue = [&](auto masked) {
             for (int a = 0; a < 2; ++a) {
                 for (int i = 0; i < 4; ++i) {
-                    const int ql = 16 * wave + 8 * a + 2 * i + half;     // local query of this lane
                     for (int ct = 0; ct < 2; ++ct) {
                         const int32_t col = static_cast<int32_t>(cs) + 32 * ct + (lane & 31);
                         const f32x16 &c = acc[a][ct];
                         const float s = relu_sum4_fast(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
                         uint64_t m;
                         if constexpr (decltype(masked)::value)
-                            m = __builtin_amdgcn_ballot_w64(s >= tau[a][i] && col < qo[a][i]);
+                            m = __builtin_amdgcn_ballot_w64(s >= tau_v[a][i] && col < qo[a][i]);
                         else
-                            m = __builtin_amdgcn_ballot_w64(s >= tau[a][i]);
+                            m = __builtin_amdgcn_ballot_w64(s >= tau_v[a][i]);
                         if (m == 0) continue;                            // wave-uniform
                         any = true;
-                        append(m, s, col, ql);
+                        const int j0 = 8 * a + 2 * i;                    // queries j0 (lanes 0..31), j0 + 1
+                        const uint32_t m0 = static_cast<uint32_t>(m), m1 = static_cast<uint32_t>(m >> 32);
+                        const uint32_t mh = half ? m1 : m0;
+                        if (mh & bit) {
+                            const int ql = 16 * wave + j0 + half;
+                            const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
+                            const uint32_t b0 = __builtin_amdgcn_readlane(st_cnt, j0);
+                            const uint32_t b1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1);
+                            const uint32_t pos = (half ? b1 : b0) + static_cast<uint32_t>(__popc(mh & (bit - 1u)));
+                            const int64_t row = b * L + q0 + ql;
+                            if (pos < static_cast<uint32_t>(cap)) {
+                                cand_score[row * cap + pos] = sc;
+                                cand_idx[row * cap + pos] = col;
+                            }
+                            atomicAdd(&hist[ql][topk_bin(sc)], 1u);
+                        }
+                        const uint32_t add = (lane == j0) ? static_cast<uint32_t>(__popc(m0))
+                                             : (lane == j0 + 1 ? static_cast<uint32_t>(__popc(m1)) : 0u);
+                        st_cnt += add;
+                        st_since += add;
                     }
                 }
             }
@@ -328,34 +323,33 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         else
             epilogue(std::integral_constant<bool, true>{});
         if (any) {
-            // refresh the thresholds of this wave's queries that kept enough new scores
-            bool changed = false;
-            for (int j = 0; j < 16; ++j) {
-                const int ql = 16 * wave + j;
-                if (since[ql] < kTauRefresh) continue;              // wave-uniform (LDS broadcast)
-                const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
-                const uint32_t part = h0 + h1;
-                uint32_t incl = part;                                // kept scores in bins >= 2*lane
-                for (int off = 1; off < 64; off <<= 1) {
-                    const uint32_t other = __shfl_down(incl, off);
-                    if (lane + off < 64) incl += other;
+            // refresh the thresholds of queries that kept enough new scores: the
+            // highest bin whose suffix count reaches the budget gives tau
+            uint64_t todo = __builtin_amdgcn_ballot_w64(lane < 16 && st_since >= kTauRefresh);
+            if (todo) {
+                while (todo) {
+                    const int j = __builtin_ctzll(todo);
+                    todo &= todo - 1;
+                    const int ql = 16 * wave + j;
+                    const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
+                    uint32_t incl = h0 + h1;                           // kept scores in bins >= 2*lane
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const uint32_t other = __shfl_down(incl, off);
+                        if (lane + off < 64) incl += other;
+                    }
+                    const uint32_t c1 = incl - h0;                     // bins >= 2*lane + 1
+                    const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
+                                     : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
+                    const uint64_t vm = __builtin_amdgcn_ballot_w64(cand >= 0);
+                    if (vm != 0) {
+                        const int hi = 63 - __clzll(vm);
+                        const float t = topk_bin_edge(__shfl(cand, hi));
+                        if (lane == j && t > st_tau) st_tau = t;
+                    }
+                    if (lane == j) st_since = 0;
                 }
-                const uint32_t c1 = incl - h0;                       // bins >= 2*lane + 1
-                const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
-                                 : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
-                const uint64_t vm = __ballot(cand >= 0);
-                if (lane == 0) since[ql] = 0;
-                if (vm != 0) {
-                    const int hi = 63 - __clzll(vm);
-                    const int bin = __shfl(cand, hi);
-                    const float t = topk_bin_edge(bin);
-                    if (lane == 0 && t > tau_s[ql]) tau_s[ql] = t;
-                    changed = true;
-                }
-            }
-            if (changed) {
                 for (int a = 0; a < 2; ++a)
-                    for (int i = 0; i < 4; ++i) tau[a][i] = tau_s[16 * wave + 8 * a + 2 * i + half];
+                    for (int i = 0; i < 4; ++i) tau_v[a][i] = __shfl(st_tau, 8 * a + 2 * i + half);
             }
         }
         if (more) put(buf ^ 1);
@@ -378,12 +372,13 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
                          : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
         const uint32_t above = (cand == 2 * lane + 1) ? c1 - h1 : incl - h0;    // bins > cand
-        const uint64_t vm = __ballot(cand >= 0);
+        const uint64_t vm = __builtin_amdgcn_ballot_w64(cand >= 0);
         const int hi = vm ? 63 - __clzll(vm) : 0;
         const int bin = vm ? __shfl(cand, hi) : -1;
         const uint32_t ab = __shfl(above, hi);
+        const uint32_t n = __shfl(st_cnt, j);
         if (lane == 0) {
-            cand_count[b * L + q] = static_cast<int32_t>(cnt[ql]);
+            cand_count[b * L + q] = static_cast<int32_t>(n);
             cand_meta[2 * (b * L + q)] = bin;
             cand_meta[2 * (b * L + q) + 1] = static_cast<int32_t>(vm ? ab : 0);
         }
