@@ -237,6 +237,10 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             tau_v[a][i] = (q < L) ? 0.0f : INFINITY;
         }
     const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
+    // candidate lists of this workgroup's 64 queries (rows b*L + q0 .. +63); the
+    // padding queries of a ragged tile never append (infinite threshold)
+    float *__restrict__ wg_score = cand_score + (b * L + q0) * cap;
+    int32_t *__restrict__ wg_idx = cand_idx + (b * L + q0) * cap;
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
     // k̄ tiles: the next tile is loaded into registers before the current
@@ -287,31 +291,33 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                         const int32_t col = static_cast<int32_t>(cs) + 32 * ct + (lane & 31);
                         const f32x16 &c = acc[a][ct];
                         const float s = relu_sum4_fast(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
-                        uint64_t m;
+                        bool keep;
                         if constexpr (decltype(masked)::value)
-                            m = __builtin_amdgcn_ballot_w64(s >= tau_v[a][i] && col < qo[a][i]);
+                            keep = s >= tau_v[a][i] && col < qo[a][i];
                         else
-                            m = __builtin_amdgcn_ballot_w64(s >= tau_v[a][i]);
+                            keep = s >= tau_v[a][i];
+                        const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
                         if (m == 0) continue;                            // wave-uniform
                         any = true;
                         const int j0 = 8 * a + 2 * i;                    // queries j0 (lanes 0..31), j0 + 1
                         const uint32_t m0 = static_cast<uint32_t>(m), m1 = static_cast<uint32_t>(m >> 32);
-                        const uint32_t mh = half ? m1 : m0;
-                        if (mh & bit) {
-                            const int ql = 16 * wave + j0 + half;
-                            const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
+                        const uint32_t n0 = static_cast<uint32_t>(__popc(m0)), n1 = static_cast<uint32_t>(__popc(m1));
+                        if (keep) {
+                            // position = kept count of the lane's query + kept lanes below it in its half
                             const uint32_t b0 = __builtin_amdgcn_readlane(st_cnt, j0);
-                            const uint32_t b1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1);
-                            const uint32_t pos = (half ? b1 : b0) + static_cast<uint32_t>(__popc(mh & (bit - 1u)));
-                            const int64_t row = b * L + q0 + ql;
+                            const uint32_t b1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1) - n0;
+                            const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(m0, 0u));
+                            const uint32_t pos = (half ? b1 : b0) + below;
+                            const uint32_t ql = static_cast<uint32_t>(16 * wave + j0 + half);
+                            const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
                             if (pos < static_cast<uint32_t>(cap)) {
-                                cand_score[row * cap + pos] = sc;
-                                cand_idx[row * cap + pos] = col;
+                                const uint32_t off = ql * static_cast<uint32_t>(cap) + pos;
+                                wg_score[off] = sc;
+                                wg_idx[off] = col;
                             }
                             atomicAdd(&hist[ql][topk_bin(sc)], 1u);
                         }
-                        const uint32_t add = (lane == j0) ? static_cast<uint32_t>(__popc(m0))
-                                             : (lane == j0 + 1 ? static_cast<uint32_t>(__popc(m1)) : 0u);
+                        const uint32_t add = (lane == j0) ? n0 : (lane == j0 + 1 ? n1 : 0u);
                         st_cnt += add;
                         st_since += add;
                     }

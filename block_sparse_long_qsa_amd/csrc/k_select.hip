@@ -34,11 +34,12 @@ __device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
 // Exact top-`budget` of n > budget keys.  key(j) gives the score bits of
 // element j (j ascending = block ascending), id(j) its block.  Writes `budget`
 // block ids in ascending order to out.  `hist` is LDS of kSelMaxBins words.
-template <typename KeyFn, typename IdFn>
+template <int NT = kSelThreads, typename KeyFn, typename IdFn>
 __device__ void radix_topk(int64_t n, int budget, KeyFn key, IdFn id, int32_t *__restrict__ out, uint32_t *hist)
 {
+    constexpr int NW = NT / 64;
     __shared__ uint32_t s_digit, s_above;
-    __shared__ uint32_t s_eq[2][4], s_take[2][4];
+    __shared__ uint32_t s_eq[2][NW], s_take[2][NW];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -50,18 +51,18 @@ __device__ void radix_topk(int64_t n, int budget, KeyFn key, IdFn id, int32_t *_
         const int shift = shifts[r];
         const int nb = 1 << nbits[r];
         const uint32_t dmask = static_cast<uint32_t>(nb - 1);
-        for (int x = tid; x < nb; x += kSelThreads) hist[x] = 0;
+        for (int x = tid; x < nb; x += NT) hist[x] = 0;
         __syncthreads();
         int64_t j = tid;
-        for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {        // 4 independent loads in flight
-            const uint32_t k0 = key(j), k1 = key(j + kSelThreads), k2 = key(j + 2 * kSelThreads),
-                           k3 = key(j + 3 * kSelThreads);
+        for (; j + 3 * NT < n; j += 4 * NT) {        // 4 independent loads in flight
+            const uint32_t k0 = key(j), k1 = key(j + NT), k2 = key(j + 2 * NT),
+                           k3 = key(j + 3 * NT);
             if ((k0 & mask) == prefix) atomicAdd(&hist[(k0 >> shift) & dmask], 1u);
             if ((k1 & mask) == prefix) atomicAdd(&hist[(k1 >> shift) & dmask], 1u);
             if ((k2 & mask) == prefix) atomicAdd(&hist[(k2 >> shift) & dmask], 1u);
             if ((k3 & mask) == prefix) atomicAdd(&hist[(k3 >> shift) & dmask], 1u);
         }
-        for (; j < n; j += kSelThreads) {
+        for (; j < n; j += NT) {
             const uint32_t k0 = key(j);
             if ((k0 & mask) == prefix) atomicAdd(&hist[(k0 >> shift) & dmask], 1u);
         }
@@ -105,7 +106,7 @@ __device__ void radix_topk(int64_t n, int budget, KeyFn key, IdFn id, int32_t *_
 
     uint32_t eq_run = 0, take_run = 0;
     int par = 0;
-    for (int64_t base = 0; base < n; base += kSelThreads) {
+    for (int64_t base = 0; base < n; base += NT) {
         const int64_t j = base + tid;
         const bool valid = j < n;
         const uint32_t k = valid ? key(j) : 0u;
@@ -116,7 +117,7 @@ __device__ void radix_topk(int64_t n, int budget, KeyFn key, IdFn id, int32_t *_
         __syncthreads();
         uint32_t eq_before = eq_run + lane_rank(em);
         uint32_t eq_tile = 0;
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const uint32_t cnt = s_eq[par][w];
             if (w < wave) eq_before += cnt;
             eq_tile += cnt;
@@ -127,7 +128,7 @@ __device__ void radix_topk(int64_t n, int budget, KeyFn key, IdFn id, int32_t *_
         __syncthreads();
         uint32_t posn = take_run + lane_rank(tm);
         uint32_t take_tile = 0;
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const uint32_t cnt = s_take[par][w];
             if (w < wave) posn += cnt;
             take_tile += cnt;
@@ -160,6 +161,7 @@ __device__ __noinline__ uint32_t recompute_score(const float *qs, const bf16_t *
 
 // Copy n 32-bit words from global memory into LDS: 16-byte loads when the
 // source is 16-byte aligned, several per thread issued before any store.
+template <int NT = kSelThreads>
 __device__ __forceinline__ void stage_words(const uint32_t *__restrict__ src, int64_t n, uint32_t *dst)
 {
     const int tid = threadIdx.x;
@@ -167,28 +169,28 @@ __device__ __forceinline__ void stage_words(const uint32_t *__restrict__ src, in
         const int64_t n4 = n >> 2;
         const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
         int64_t j = tid;
-        for (; j + 3 * kSelThreads < n4; j += 4 * kSelThreads) {
-            const u32x4 a = s4[j], b = s4[j + kSelThreads], c = s4[j + 2 * kSelThreads], d = s4[j + 3 * kSelThreads];
+        for (; j + 3 * NT < n4; j += 4 * NT) {
+            const u32x4 a = s4[j], b = s4[j + NT], c = s4[j + 2 * NT], d = s4[j + 3 * NT];
             reinterpret_cast<u32x4 *>(dst)[j] = a;
-            reinterpret_cast<u32x4 *>(dst)[j + kSelThreads] = b;
-            reinterpret_cast<u32x4 *>(dst)[j + 2 * kSelThreads] = c;
-            reinterpret_cast<u32x4 *>(dst)[j + 3 * kSelThreads] = d;
+            reinterpret_cast<u32x4 *>(dst)[j + NT] = b;
+            reinterpret_cast<u32x4 *>(dst)[j + 2 * NT] = c;
+            reinterpret_cast<u32x4 *>(dst)[j + 3 * NT] = d;
         }
-        for (; j < n4; j += kSelThreads) reinterpret_cast<u32x4 *>(dst)[j] = s4[j];
-        for (int64_t t = (n4 << 2) + tid; t < n; t += kSelThreads) dst[t] = src[t];
+        for (; j < n4; j += NT) reinterpret_cast<u32x4 *>(dst)[j] = s4[j];
+        for (int64_t t = (n4 << 2) + tid; t < n; t += NT) dst[t] = src[t];
     } else {
         int64_t j = tid;
-        for (; j + 3 * kSelThreads < n; j += 4 * kSelThreads) {
-            const uint32_t a = src[j], b = src[j + kSelThreads], c = src[j + 2 * kSelThreads], d = src[j + 3 * kSelThreads];
-            dst[j] = a; dst[j + kSelThreads] = b; dst[j + 2 * kSelThreads] = c; dst[j + 3 * kSelThreads] = d;
+        for (; j + 3 * NT < n; j += 4 * NT) {
+            const uint32_t a = src[j], b = src[j + NT], c = src[j + 2 * NT], d = src[j + 3 * NT];
+            dst[j] = a; dst[j + NT] = b; dst[j + 2 * NT] = c; dst[j + 3 * NT] = d;
         }
-        for (; j < n; j += kSelThreads) dst[j] = src[j];
+        for (; j < n; j += NT) dst[j] = src[j];
     }
 }
 
 __device__ __forceinline__ bool take_all(int64_t o, int budget, int32_t *out) {
     if (o > budget) return false;
-    for (int j = threadIdx.x; j < budget; j += kSelThreads) out[j] = (j < o) ? j : -1;
+    for (int j = threadIdx.x; j < budget; j += blockDim.x) out[j] = (j < o) ? j : -1;
     return true;
 }
 
@@ -198,7 +200,8 @@ __device__ __forceinline__ bool take_all(int64_t o, int budget, int32_t *out) {
 // block_idx + b*bi_bstride + i*budget.
 // Rows of up to `lds_words` scores are first staged in (dynamic) LDS so the
 // radix passes read on-chip memory; longer rows are read from global memory.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+template <int NT>
+__global__ __launch_bounds__(NT) void select_kernel(
     int64_t L, int64_t q_offset, const int32_t *__restrict__ cache_len, int64_t ncol,
     const float *__restrict__ scores, int64_t sc_bstride, int32_t *__restrict__ block_idx, int64_t bi_bstride,
     int budget, int64_t lds_words)
@@ -214,11 +217,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int32_t *out = block_idx + b * bi_bstride + i * budget;
     if (take_all(o, budget, out)) return;
     if (o <= lds_words) {
-        stage_words(srow, o, rowbuf);
+        stage_words<NT>(srow, o, rowbuf);
         __syncthreads();
-        radix_topk(o, budget, [&](int64_t j) { return rowbuf[j]; }, [](int64_t j) { return j; }, out, hist);
+        radix_topk<NT>(o, budget, [&](int64_t j) { return rowbuf[j]; }, [](int64_t j) { return j; }, out, hist);
     } else {
-        radix_topk(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
+        radix_topk<NT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
     }
 }
 
@@ -357,15 +360,24 @@ hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
     // stage rows in LDS when one row fits beside the histogram (up to 36,864 scores)
     const int64_t lds_words = (ncol <= 36864) ? ncol : 0;
     const size_t dyn = static_cast<size_t>(lds_words) * 4;
+    // few long rows (decode): 1024 threads per row; many rows: 256
+    const bool wide = rows < 1024;
     static thread_local int lds_limit_set = 0;      // per thread: attribute calls are not stream-ordered
     if (dyn > 64 * 1024 && !lds_limit_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(select_kernel),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(select_kernel<256>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, 36864 * 4);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute(reinterpret_cast<const void *>(select_kernel<1024>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 36864 * 4);
         if (e != hipSuccess) return e;
         lds_limit_set = 1;
     }
-    hipLaunchKernelGGL(select_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), dyn, st, L, q_offset,
-                       cache_len, ncol, scores, sc_bstride, block_idx, bi_bstride, budget, lds_words);
+    if (wide)
+        hipLaunchKernelGGL(select_kernel<1024>, dim3(static_cast<unsigned>(rows)), dim3(1024), dyn, st, L, q_offset,
+                           cache_len, ncol, scores, sc_bstride, block_idx, bi_bstride, budget, lds_words);
+    else
+        hipLaunchKernelGGL(select_kernel<256>, dim3(static_cast<unsigned>(rows)), dim3(256), dyn, st, L, q_offset,
+                           cache_len, ncol, scores, sc_bstride, block_idx, bi_bstride, budget, lds_words);
     return hipGetLastError();
 }
 
