@@ -25,7 +25,7 @@
 
 namespace qsa {
 
-constexpr int kChunkBlocks = 4;                  // 16 tokens per step
+constexpr int kChunkBlocks = 8;                  // 32 tokens per step
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct RowState {
@@ -88,15 +88,7 @@ __device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_
     }
 }
 
-// Walk steps [c_lo, c_hi) of one (query, group) token list; step c covers list
-// entries 4c .. 4c+3 (16 tokens).
-//   S^T (16 tokens x 16 heads) = K~ . Q~^T : v_mfma_f32_16x16x32_bf16, A = K~ rows
-//       (token r = lane%16 of the step, dims 32s + 8*(lane/16) .. +7),
-//   lane (h = lane%16, g = lane/16) ends with the 4 tokens of list entry 4c+g
-//   for head h, which is exactly the B operand (P^T, k = 4g..4g+3) of
-//   O^T (16 dims x 16 heads) += V^T . P^T : v_mfma_f32_16x16x16bf16_1k, A = the
-//   8-byte [dim][4 tokens] slice of block 4c+g's V for dim 16n + lane%16.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
+// Walk chunks [c_lo, c_hi) of one (query, group) token list.
 __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
                                               const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
                                               int n_sel, int64_t o, int own_last, int c_lo, int c_hi, float c2,
@@ -106,53 +98,70 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
     const int r = lane & 15;           // K-load token row / V-load dim
     const int g = lane >> 4;
     for (int c = c_lo; c < c_hi; ++c) {
-        const int lb = 4 * c;
-        int64_t kblk, vblk;
-        uint32_t kmask, vmask;
-        list_entry(sel, n_sel, o, lb + (r >> 2), own_last, kblk, kmask);
-        list_entry(sel, n_sel, o, lb + g, own_last, vblk, vmask);
-        bf16x8 kf[8];
-        {
-            const bf16_t *src = kc + kblk * kBlockElems + (r & 3) * 32 + 8 * g;
-            for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8 *>(src + s * 128);
+        const int lb = kChunkBlocks * c;
+        // ---- gather K~ (A operand of S^T): tile t, token row r -> list entry lb + 4t + r/4
+        int64_t kblk[2];
+        uint32_t kmask[2];
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
+        bf16x8 kf[2][8];
+        for (int t = 0; t < 2; ++t) {
+            const bf16_t *src = kc + kblk[t] * kBlockElems + (r & 3) * 32 + 8 * g;
+            for (int s = 0; s < 8; ++s) kf[t][s] = *reinterpret_cast<const bf16x8 *>(src + s * 128);
         }
-        u32x2 vraw[16];
-        {
-            const bf16_t *src = vc + vblk * kBlockElems + r * kBlock;
-            for (int n = 0; n < 16; ++n) vraw[n] = *reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock);
+        // ---- gather V (A operand of O^T): list entries lb + g and lb + 4 + g, dim 16n + r
+        int64_t vblk[2];
+        uint32_t vmask[2];
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
+        u32x2 vraw[16][2];
+        for (int t = 0; t < 2; ++t) {
+            const bf16_t *src = vc + vblk[t] * kBlockElems + r * kBlock;
+            for (int n = 0; n < 16; ++n) vraw[n][t] = *reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock);
         }
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < 8; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
+        // ---- S^T = K~ . Q~^T
+        f32x4 sc[2];
+        for (int t = 0; t < 2; ++t) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], qf[s], acc, 0, 0, 0);
+            sc[t] = acc;
+        }
+        // lane holds tokens j = 0..3 of list entry lb + 4t + g for head r
         float cmax = -INFINITY;
-        for (int j = 0; j < 4; ++j) {
-            if (!((vmask >> j) & 1u)) sc[j] = -INFINITY;
-            cmax = fmaxf(cmax, sc[j]);
+        for (int t = 0; t < 2; ++t) {
+            for (int j = 0; j < 4; ++j) {
+                if (!((vmask[t] >> j) & 1u)) sc[t][j] = -INFINITY;
+                cmax = fmaxf(cmax, sc[t][j]);
+            }
         }
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
         const float m_new = fmaxf(st.m, cmax);
-        const bool grew = m_new > st.m;
         const float alpha = exp2f((st.m - m_new) * c2);
         st.m = m_new;
-        float p[4];
+        uint32_t pw[4];
         float psum = 0.f;
-        for (int j = 0; j < 4; ++j) {
-            p[j] = bf16_to_f32(f32_to_bf16(exp2f((sc[j] - m_new) * c2)));
-            psum += p[j];
+        for (int t = 0; t < 2; ++t) {
+            float p[4];
+            for (int j = 0; j < 4; ++j) {
+                p[j] = exp2f((sc[t][j] - m_new) * c2);
+            }
+            pw[2 * t] = pack_bf16x2(p[0], p[1]);
+            pw[2 * t + 1] = pack_bf16x2(p[2], p[3]);
+            for (int j = 0; j < 4; ++j) psum += bf16_to_f32(f32_to_bf16(p[j]));
         }
         st.l = st.l * alpha + psum;
-        const s16x4 pf = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-        // rescale O only when some head's running max grew (alpha = 1 elsewhere)
-        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-            for (int n = 0; n < 16; ++n)
-                for (int j = 0; j < 4; ++j) st.o[n][j] *= alpha;
-        }
-        // zero the V of masked tokens: their cache slots may hold anything
-        const uint32_t vm0 = ((vmask & 1u) ? 0xFFFFu : 0u) | ((vmask & 2u) ? 0xFFFF0000u : 0u);
-        const uint32_t vm1 = ((vmask & 4u) ? 0xFFFFu : 0u) | ((vmask & 8u) ? 0xFFFF0000u : 0u);
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+        // ---- O^T += V^T . P^T  (zero the V of masked tokens: their cache slots may hold anything)
         for (int n = 0; n < 16; ++n) {
-            const s16x4 vf = __builtin_bit_cast(s16x4, u32x2{vraw[n][0] & vm0, vraw[n][1] & vm1});
-            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, st.o[n], 0, 0, 0);
+            u32x2 lo = vraw[n][0], hi = vraw[n][1];
+            const uint32_t m0 = vmask[0], m1 = vmask[1];
+            lo[0] &= ((m0 & 1u) ? 0xFFFFu : 0u) | ((m0 & 2u) ? 0xFFFF0000u : 0u);
+            lo[1] &= ((m0 & 4u) ? 0xFFFFu : 0u) | ((m0 & 8u) ? 0xFFFF0000u : 0u);
+            hi[0] &= ((m1 & 1u) ? 0xFFFFu : 0u) | ((m1 & 2u) ? 0xFFFF0000u : 0u);
+            hi[1] &= ((m1 & 4u) ? 0xFFFFu : 0u) | ((m1 & 8u) ? 0xFFFF0000u : 0u);
+            const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            f32x4 acc = st.o[n];
+            for (int j = 0; j < 4; ++j) acc[j] *= alpha;
+            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc, 0, 0, 0);
         }
     }
 }
