@@ -7,6 +7,8 @@
 
 namespace qsa {
 
+constexpr int kDecodeBins = 2048;      // histogram of score bits 30..20 per sequence
+
 // One wave per sequence.  p = cache_len[b]:
 //   lanes: head g = lane/32, chunk c = lane%32 -> rotate k at p into K~ slot p%4
 //          and copy v into V slot p%4;
@@ -18,10 +20,11 @@ __global__ __launch_bounds__(64) void decode_append_kernel(
     const bf16_t *__restrict__ k, const bf16_t *__restrict__ v, const bf16_t *__restrict__ k_idx,
     const bf16_t *__restrict__ q_idx,
     bf16_t *__restrict__ k_cache, bf16_t *__restrict__ v_cache, bf16_t *__restrict__ kbar,
-    bf16_t *__restrict__ kpend, bf16_t *__restrict__ qrot)
+    bf16_t *__restrict__ kpend, bf16_t *__restrict__ qrot, uint32_t *__restrict__ dhist)
 {
     const int lane = threadIdx.x;
     const int64_t b = blockIdx.x;
+    for (int x = lane; x < kDecodeBins; x += 64) dhist[b * kDecodeBins + x] = 0;   // filled by the scan
     const int64_t p = decode_pos(cache_len, b, ctx_bound);
     const int64_t blk = p / kBlock;
     const int t = static_cast<int>(p - blk * kBlock);
@@ -136,18 +139,24 @@ __global__ __launch_bounds__(64) void decode_append_kernel(
 constexpr int kScanBlocksPerWave = 256;
 constexpr int kScanBlocksPerWG = 4 * kScanBlocksPerWave;
 
+// Each workgroup also histograms the top 11 value bits of its scores and adds
+// the histogram to the sequence's (zeroed by decode_append_kernel).
 __global__ __launch_bounds__(256) void decode_scan_kernel(const int32_t *__restrict__ cache_len, int64_t ctx_bound,
                                                           int64_t nblk_cap,
                                                           int64_t ncol, const bf16_t *__restrict__ qrot,
                                                           const bf16_t *__restrict__ kbar,
-                                                          float *__restrict__ scores)
+                                                          float *__restrict__ scores, uint32_t *__restrict__ dhist)
 {
+    __shared__ uint32_t lh[kDecodeBins];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
     const int64_t o = decode_pos(cache_len, b, ctx_bound) / kBlock;
+    if (static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG >= o) return;     // whole workgroup idle
+    for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
+    __syncthreads();
     const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG + wave * kScanBlocksPerWave;
-    if (w0 >= o) return;
+    if (w0 < o) {
     const int r = lane & 15, g = lane >> 4;
     bf16x8 af[4];
     for (int s = 0; s < 4; ++s) {
@@ -173,31 +182,38 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const int32_t *__restr
             const int64_t blk = c0 + 16 * u + r;
             if (g == 0 && blk < o) {
                 float sc = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) + fmaxf(acc[3], 0.f);
-                srow[blk] = __uint_as_float(__float_as_uint(sc) & 0x7FFFFFFFu);
+                const uint32_t bits = __float_as_uint(sc) & 0x7FFFFFFFu;
+                srow[blk] = __uint_as_float(bits);
+                atomicAdd(&lh[bits >> 20], 1u);
             }
         }
     }
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < kDecodeBins; x += 256)
+        if (lh[x]) atomicAdd(&dhist[b * kDecodeBins + x], lh[x]);
 }
 
 hipError_t launch_decode_append(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
                                 int64_t ctx_bound, int64_t nblk_cap, const bf16_t *k, const bf16_t *v, const bf16_t *k_idx,
                                 const bf16_t *q_idx, bf16_t *k_cache, bf16_t *v_cache, bf16_t *kbar,
-                                bf16_t *kpend, bf16_t *qrot)
+                                bf16_t *kpend, bf16_t *qrot, uint32_t *dhist)
 {
     hipLaunchKernelGGL(decode_append_kernel, dim3(B), dim3(64), 0, st, tab, cache_len, ctx_bound, nblk_cap, k, v,
                        k_idx, q_idx,
-                       k_cache, v_cache, kbar, kpend, qrot);
+                       k_cache, v_cache, kbar, kpend, qrot, dhist);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_scan(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
-                              int64_t nblk_cap, int64_t ncol, const bf16_t *qrot, const bf16_t *kbar, float *scores)
+                              int64_t nblk_cap, int64_t ncol, const bf16_t *qrot, const bf16_t *kbar, float *scores,
+                              uint32_t *dhist)
 {
     const int64_t o_max = ctx_bound / kBlock;
     if (o_max <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((o_max + kScanBlocksPerWG - 1) / kScanBlocksPerWG), static_cast<unsigned>(B));
     hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, cache_len, ctx_bound, nblk_cap, ncol, qrot, kbar,
-                       scores);
+                       scores, dhist);
     return hipGetLastError();
 }
 

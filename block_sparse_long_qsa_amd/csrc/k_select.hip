@@ -351,6 +351,137 @@ __global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
     radix_topk(o, budget, score, [](int64_t j) { return j; }, out, hist);
 }
 
+// Block-wide exclusive prefix sum for NT threads.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t *wsum /* LDS [NT/64] */, uint32_t &total)
+{
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+    for (int w = 0; w < NW; ++w) {
+        if (w < wave) before += wsum[w];
+        total += wsum[w];
+    }
+    __syncthreads();
+    return before + incl - v;
+}
+
+// Decode selection from a score row whose histogram of bits 30..20 (2048
+// digits) the scan kernel already built: the boundary digit d* and the count
+// above it come from the histogram; one ordered pass gathers the scores of
+// digit d* (in block order), an exact select among them picks the remaining
+// ones, and a second ordered pass emits the selection ascending.  Rows whose
+// boundary digit holds more than kEqMax scores use the plain radix select.
+constexpr int kHistNT = 1024;
+constexpr int kEqMax = 8192;
+__global__ __launch_bounds__(kHistNT) void select_hist_kernel(
+    const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
+    const uint32_t *__restrict__ dhist, int32_t *__restrict__ block_idx, int budget)
+{
+    __shared__ uint32_t hist[kSelMaxBins];
+    __shared__ uint32_t eqk[kEqMax];
+    __shared__ uint32_t selbits[kEqMax / 32];
+    __shared__ int32_t selpos[kMaxBudget];
+    __shared__ uint32_t wsum[kHistNT / 64];
+    __shared__ uint32_t s_digit, s_above;
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
+    int32_t *out = block_idx + b * budget;
+    if (take_all(o, budget, out)) return;
+    const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * ncol);
+    // boundary digit from the histogram: 2 digits per thread, suffix sums
+    {
+        const uint32_t h0 = dhist[b * kSelMaxBins + 2 * tid], h1 = dhist[b * kSelMaxBins + 2 * tid + 1];
+        hist[2 * tid] = h0;
+        hist[2 * tid + 1] = h1;
+        // inclusive suffix sum over threads of h0 + h1: total - exclusive prefix
+        uint32_t tot;
+        const uint32_t before = block_scan_nt<kHistNT>(h0 + h1, wsum, tot);
+        const uint32_t incl = tot - before;             // digits >= 2*tid
+        const uint32_t c1 = incl - h0;                  // digits >= 2*tid + 1
+        const uint32_t K = static_cast<uint32_t>(budget);
+        if (c1 >= K && c1 - h1 < K) { s_digit = 2 * tid + 1; s_above = c1 - h1; }
+        else if (incl >= K && c1 < K) { s_digit = 2 * tid; s_above = c1; }
+        __syncthreads();
+    }
+    const uint32_t dstar = s_digit;
+    const uint32_t k_rem = static_cast<uint32_t>(budget) - s_above;
+    const uint32_t n_eq = hist[dstar];
+    if (n_eq > kEqMax) {
+        radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
+        return;
+    }
+    const int64_t seg = (o + kHistNT - 1) / kHistNT;
+    const int64_t j0 = tid * seg;
+    const int64_t j1 = (j0 + seg < o) ? j0 + seg : o;
+    // pass A: gather digit-d* scores in block order
+    uint32_t ne = 0;
+    for (int64_t j = j0; j < j1; ++j) ne += (srow[j] >> 20) == dstar;
+    uint32_t tot_eq;
+    const uint32_t eq_base = block_scan_nt<kHistNT>(ne, wsum, tot_eq);
+    {
+        uint32_t at = eq_base;
+        for (int64_t j = j0; j < j1; ++j) {
+            const uint32_t k = srow[j];
+            if ((k >> 20) == dstar) eqk[at++] = k;
+        }
+    }
+    for (int x = tid; x < kEqMax / 32; x += kHistNT) selbits[x] = 0;
+    __syncthreads();
+    if (n_eq == k_rem) {
+        for (uint32_t t = tid; t < n_eq; t += kHistNT) atomicOr(&selbits[t >> 5], 1u << (t & 31));
+    } else {
+        radix_topk<kHistNT>(n_eq, static_cast<int>(k_rem), [&](int64_t t) { return eqk[t]; },
+                            [](int64_t t) { return t; }, selpos, hist);
+        __syncthreads();
+        for (uint32_t t = tid; t < k_rem; t += kHistNT) atomicOr(&selbits[selpos[t] >> 5], 1u << (selpos[t] & 31));
+    }
+    __syncthreads();
+    // pass B: ordered emission
+    auto taken = [&](uint32_t k, uint32_t &eqi) -> bool {
+        const uint32_t d = k >> 20;
+        if (d > dstar) return true;
+        if (d < dstar) return false;
+        const bool t = (selbits[eqi >> 5] >> (eqi & 31)) & 1u;
+        ++eqi;
+        return t;
+    };
+    uint32_t ns = 0;
+    {
+        uint32_t eqi = eq_base;
+        for (int64_t j = j0; j < j1; ++j) ns += taken(srow[j], eqi);
+    }
+    uint32_t tot;
+    uint32_t w = block_scan_nt<kHistNT>(ns, wsum, tot);
+    {
+        uint32_t eqi = eq_base;
+        for (int64_t j = j0; j < j1; ++j) {
+            if (taken(srow[j], eqi)) {
+                if (w < static_cast<uint32_t>(budget)) out[w] = static_cast<int32_t>(j);
+                ++w;
+            }
+        }
+    }
+}
+
+hipError_t launch_select_hist(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int64_t ncol,
+                              const float *scores, const uint32_t *dhist, int32_t *block_idx, int budget)
+{
+    if (B <= 0) return hipSuccess;
+    hipLaunchKernelGGL(select_hist_kernel, dim3(B), dim3(kHistNT), 0, st, cache_len, pos_bound, ncol, scores, dhist,
+                       block_idx, budget);
+    return hipGetLastError();
+}
+
 hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, const int32_t *cache_len,
                          int64_t ncol, const float *scores, int64_t sc_bstride, int32_t *block_idx,
                          int64_t bi_bstride, int budget)

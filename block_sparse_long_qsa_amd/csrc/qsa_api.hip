@@ -36,9 +36,11 @@ hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int3
                                 bf16_t *);
 hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const bf16_t *,
                                 const bf16_t *, const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *,
-                                bf16_t *, bf16_t *);
+                                bf16_t *, bf16_t *, uint32_t *);
 hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int64_t, const bf16_t *,
-                              const bf16_t *, float *);
+                              const bf16_t *, float *, uint32_t *);
+hipError_t launch_select_hist(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const float *,
+                              const uint32_t *, int32_t *, int);
 }  // namespace qsa
 
 using namespace qsa;
@@ -117,7 +119,7 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     return f;
 }
 
-struct DecLayout { size_t qrot, scores, bidx, part_o, part_ml, total; int64_t ncol; int nsplit; };
+struct DecLayout { size_t qrot, scores, bidx, part_o, part_ml, hist, total; int64_t ncol; int nsplit; };
 DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     DecLayout d{};
     d.ncol = ctx_bound / kBlock;
@@ -129,7 +131,8 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     d.part_o = d.bidx + align_up(static_cast<size_t>(B) * h->p.budget_blocks * 4);
     const size_t slots = static_cast<size_t>(B) * kKVHeads * d.nsplit * kGroup;
     d.part_ml = d.part_o + align_up(slots * kHeadDim * 4);
-    d.total = d.part_ml + align_up(slots * 2 * 4);
+    d.hist = d.part_ml + align_up(slots * 2 * 4);
+    d.total = d.hist + align_up(static_cast<size_t>(B) * 2048 * 4);
     return d;
 }
 
@@ -402,14 +405,15 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
     int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + d.bidx);
     float *part_o = reinterpret_cast<float *>(w + d.part_o);
     float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
+    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
     const int budget = h->p.budget_blocks;
     const int64_t nbc = nblk_cap(h);
 
     hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, q_idx, k_cache, v_cache,
-                                        kbar_cache, kpend, qrot);
-    if (e == hipSuccess) e = launch_decode_scan(st, B, cache_len, ctx_bound, nbc, d.ncol, qrot, kbar_cache, scores);
+                                        kbar_cache, kpend, qrot, dhist);
     if (e == hipSuccess)
-        e = launch_select(st, B, 1, ctx_bound, cache_len, d.ncol, scores, d.ncol, bidx, budget, budget);
+        e = launch_decode_scan(st, B, cache_len, ctx_bound, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
+    if (e == hipSuccess) e = launch_select_hist(st, B, cache_len, ctx_bound, d.ncol, scores, dhist, bidx, budget);
     if (e == hipSuccess)
         e = launch_attend_decode(tables(h), st, B, cache_len, ctx_bound, nbc, budget, d.nsplit, h->sigma, q, k_cache, v_cache,
                                  bidx, part_o, part_ml, out);
