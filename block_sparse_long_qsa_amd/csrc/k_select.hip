@@ -420,19 +420,29 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
         radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
         return;
     }
-    const int64_t seg = (o + kHistNT - 1) / kHistNT;
-    const int64_t j0 = tid * seg;
-    const int64_t j1 = (j0 + seg < o) ? j0 + seg : o;
+    // each wave owns a contiguous range of the row, read 64 scores per step
+    constexpr int NW = kHistNT / 64;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t per = ((o + NW - 1) / NW + 63) & ~int64_t(63);
+    const int64_t r0 = wave * per;
+    const int64_t r1 = (r0 + per < o) ? r0 + per : o;
     // pass A: gather digit-d* scores in block order
     uint32_t ne = 0;
-    for (int64_t j = j0; j < j1; ++j) ne += (srow[j] >> 20) == dstar;
+    for (int64_t j = r0 + lane; j < r1; j += 64) ne += (srow[j] >> 20) == dstar;
+    for (int off = 32; off > 0; off >>= 1) ne += __shfl_xor(ne, off);
     uint32_t tot_eq;
-    const uint32_t eq_base = block_scan_nt<kHistNT>(ne, wsum, tot_eq);
+    const uint32_t eq_wbase = block_scan_nt<kHistNT>(lane == 0 ? ne : 0u, wsum, tot_eq);
+    const uint32_t eq_base = __shfl(eq_wbase, 0);      // wave's first position in eqk
     {
-        uint32_t at = eq_base;
-        for (int64_t j = j0; j < j1; ++j) {
-            const uint32_t k = srow[j];
-            if ((k >> 20) == dstar) eqk[at++] = k;
+        uint32_t run = eq_base;
+        for (int64_t jb = r0; jb < r1; jb += 64) {
+            const int64_t j = jb + lane;
+            const uint32_t k = (j < r1) ? srow[j] : 0u;
+            const bool e = j < r1 && (k >> 20) == dstar;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(e);
+            if (e) eqk[run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))] = k;
+            run += static_cast<uint32_t>(__popcll(m));
         }
     }
     for (int x = tid; x < kEqMax / 32; x += kHistNT) selbits[x] = 0;
@@ -446,29 +456,41 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
         for (uint32_t t = tid; t < k_rem; t += kHistNT) atomicOr(&selbits[selpos[t] >> 5], 1u << (selpos[t] & 31));
     }
     __syncthreads();
-    // pass B: ordered emission
-    auto taken = [&](uint32_t k, uint32_t &eqi) -> bool {
+    // pass B: ordered emission (taken = digit above d*, or a selected digit-d* score)
+    auto step = [&](int64_t jb, uint32_t &eqrun, uint64_t &tm) {
+        const int64_t j = jb + lane;
+        const uint32_t k = (j < r1) ? srow[j] : 0u;
         const uint32_t d = k >> 20;
-        if (d > dstar) return true;
-        if (d < dstar) return false;
-        const bool t = (selbits[eqi >> 5] >> (eqi & 31)) & 1u;
-        ++eqi;
+        const bool e = j < r1 && d == dstar;
+        const uint64_t em = __builtin_amdgcn_ballot_w64(e);
+        const uint32_t ei = eqrun + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(em >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(em), 0u));
+        eqrun += static_cast<uint32_t>(__popcll(em));
+        const bool t = j < r1 && (d > dstar || (e && ((selbits[ei >> 5] >> (ei & 31)) & 1u)));
+        tm = __builtin_amdgcn_ballot_w64(t);
         return t;
     };
     uint32_t ns = 0;
     {
-        uint32_t eqi = eq_base;
-        for (int64_t j = j0; j < j1; ++j) ns += taken(srow[j], eqi);
+        uint32_t eqrun = eq_base;
+        for (int64_t jb = r0; jb < r1; jb += 64) {
+            uint64_t tm;
+            step(jb, eqrun, tm);
+            ns += static_cast<uint32_t>(__popcll(tm));
+        }
     }
     uint32_t tot;
-    uint32_t w = block_scan_nt<kHistNT>(ns, wsum, tot);
+    const uint32_t wbase = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ns : 0u, wsum, tot), 0);
     {
-        uint32_t eqi = eq_base;
-        for (int64_t j = j0; j < j1; ++j) {
-            if (taken(srow[j], eqi)) {
-                if (w < static_cast<uint32_t>(budget)) out[w] = static_cast<int32_t>(j);
-                ++w;
+        uint32_t eqrun = eq_base, run = wbase;
+        for (int64_t jb = r0; jb < r1; jb += 64) {
+            uint64_t tm;
+            if (step(jb, eqrun, tm)) {
+                const uint32_t p = run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tm), 0u));
+                if (p < static_cast<uint32_t>(budget)) out[p] = static_cast<int32_t>(jb + lane);
             }
+            run += static_cast<uint32_t>(__popcll(tm));
         }
     }
 }
