@@ -165,6 +165,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="decode step only (profiling)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (counter calibration)")
@@ -183,13 +184,14 @@ def main():
         del src, dst
     wp = synth.WORKLOADS["prefill_256k"]
     wd = synth.WORKLOADS["decode_128k"]
-    sp = setup_prefill(wp)
+    sp = None if args.no_prefill else setup_prefill(wp)
     sd = None if args.no_decode else setup_decode(wd)
     torch.cuda.synchronize()
     print("setup done", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
-        prefill_stages(sp, _events(4))
+        if sp:
+            prefill_stages(sp, _events(4))
         if sd:
             decode_step(sd)
     torch.cuda.synchronize()
@@ -200,7 +202,8 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        prefill_stages(sp, ev_p[i])
+        if sp:
+            prefill_stages(sp, ev_p[i])
         if sd:
             ev_d[i][0].record()
             decode_step(sd)
@@ -208,6 +211,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    if sp is None:
+        t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_d]))
+        print(json.dumps({"decode_only": True, "ms": t_dec, "tok_s": wd.batch / (t_dec * 1e-3),
+                          "hbm_frac": decode_bytes(wd.batch, wd.seq_len, wd.budget) / (t_dec * 1e-3) / 1e9 /
+                          HBM_PEAK_GBS}))
+        return
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev_p])   # ms
     t_append, t_isel, t_attn = st.mean(axis=0)
     t_prefill = float(st.sum(axis=1).mean())

@@ -426,23 +426,37 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     const int64_t per = ((o + NW - 1) / NW + 63) & ~int64_t(63);
     const int64_t r0 = wave * per;
     const int64_t r1 = (r0 + per < o) ? r0 + per : o;
-    // pass A: gather digit-d* scores in block order
+    // Passes walk the wave's range in groups of 8 x 64 scores: the 8 loads of a
+    // group are issued together, then the 8 steps are processed in order.
+    constexpr int U = 8;
+    auto load8 = [&](int64_t jb, uint32_t (&v)[U]) {
+        for (int u = 0; u < U; ++u) {
+            const int64_t j = jb + 64 * u + lane;
+            v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: digit 4095, never counted
+        }
+    };
+    // pass A: count, then gather digit-d* scores in block order
     uint32_t ne = 0;
-    for (int64_t j = r0 + lane; j < r1; j += 64) ne += (srow[j] >> 20) == dstar;
+    for (int64_t jb = r0; jb < r1; jb += 64 * U) {
+        uint32_t v[U];
+        load8(jb, v);
+        for (int u = 0; u < U; ++u) ne += (v[u] >> 20) == dstar;
+    }
     for (int off = 32; off > 0; off >>= 1) ne += __shfl_xor(ne, off);
     uint32_t tot_eq;
-    const uint32_t eq_wbase = block_scan_nt<kHistNT>(lane == 0 ? ne : 0u, wsum, tot_eq);
-    const uint32_t eq_base = __shfl(eq_wbase, 0);      // wave's first position in eqk
+    const uint32_t eq_base = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ne : 0u, wsum, tot_eq), 0);
     {
         uint32_t run = eq_base;
-        for (int64_t jb = r0; jb < r1; jb += 64) {
-            const int64_t j = jb + lane;
-            const uint32_t k = (j < r1) ? srow[j] : 0u;
-            const bool e = j < r1 && (k >> 20) == dstar;
-            const uint64_t m = __builtin_amdgcn_ballot_w64(e);
-            if (e) eqk[run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))] = k;
-            run += static_cast<uint32_t>(__popcll(m));
+        for (int64_t jb = r0; jb < r1; jb += 64 * U) {
+            uint32_t v[U];
+            load8(jb, v);
+            for (int u = 0; u < U; ++u) {
+                const bool e = (v[u] >> 20) == dstar;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(e);
+                if (e) eqk[run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))] = v[u];
+                run += static_cast<uint32_t>(__popcll(m));
+            }
         }
     }
     for (int x = tid; x < kEqMax / 32; x += kHistNT) selbits[x] = 0;
@@ -457,40 +471,41 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     }
     __syncthreads();
     // pass B: ordered emission (taken = digit above d*, or a selected digit-d* score)
-    auto step = [&](int64_t jb, uint32_t &eqrun, uint64_t &tm) {
-        const int64_t j = jb + lane;
-        const uint32_t k = (j < r1) ? srow[j] : 0u;
+    auto taken = [&](uint32_t k, uint32_t &eqrun) -> uint64_t {
         const uint32_t d = k >> 20;
-        const bool e = j < r1 && d == dstar;
+        const bool e = d == dstar;
         const uint64_t em = __builtin_amdgcn_ballot_w64(e);
         const uint32_t ei = eqrun + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(em >> 32),
                                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(em), 0u));
         eqrun += static_cast<uint32_t>(__popcll(em));
-        const bool t = j < r1 && (d > dstar || (e && ((selbits[ei >> 5] >> (ei & 31)) & 1u)));
-        tm = __builtin_amdgcn_ballot_w64(t);
-        return t;
+        const bool t = (d > dstar && d < 4095u) || (e && ((selbits[ei >> 5] >> (ei & 31)) & 1u));
+        return __builtin_amdgcn_ballot_w64(t);
     };
     uint32_t ns = 0;
     {
         uint32_t eqrun = eq_base;
-        for (int64_t jb = r0; jb < r1; jb += 64) {
-            uint64_t tm;
-            step(jb, eqrun, tm);
-            ns += static_cast<uint32_t>(__popcll(tm));
+        for (int64_t jb = r0; jb < r1; jb += 64 * U) {
+            uint32_t v[U];
+            load8(jb, v);
+            for (int u = 0; u < U; ++u) ns += static_cast<uint32_t>(__popcll(taken(v[u], eqrun)));
         }
     }
     uint32_t tot;
     const uint32_t wbase = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ns : 0u, wsum, tot), 0);
     {
         uint32_t eqrun = eq_base, run = wbase;
-        for (int64_t jb = r0; jb < r1; jb += 64) {
-            uint64_t tm;
-            if (step(jb, eqrun, tm)) {
-                const uint32_t p = run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),
-                                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tm), 0u));
-                if (p < static_cast<uint32_t>(budget)) out[p] = static_cast<int32_t>(jb + lane);
+        for (int64_t jb = r0; jb < r1; jb += 64 * U) {
+            uint32_t v[U];
+            load8(jb, v);
+            for (int u = 0; u < U; ++u) {
+                const uint64_t tm = taken(v[u], eqrun);
+                if ((tm >> lane) & 1u) {
+                    const uint32_t p = run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),
+                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tm), 0u));
+                    if (p < static_cast<uint32_t>(budget)) out[p] = static_cast<int32_t>(jb + 64 * u + lane);
+                }
+                run += static_cast<uint32_t>(__popcll(tm));
             }
-            run += static_cast<uint32_t>(__popcll(tm));
         }
     }
 }
