@@ -166,75 +166,6 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
     }
 }
 
-// Walk steps [c_lo, c_hi) of one (query, group) token list; step c covers list
-// entries 4c .. 4c+3 (16 tokens).
-//   S^T (16 tokens x 16 heads) = K~ . Q~^T : v_mfma_f32_16x16x32_bf16, A = K~ rows
-//       (token r = lane%16 of the step, dims 32s + 8*(lane/16) .. +7),
-//   lane (h = lane%16, g = lane/16) ends with the 4 tokens of list entry 4c+g
-//   for head h, which is exactly the B operand (P^T, k = 4g..4g+3) of
-//   O^T (16 dims x 16 heads) += V^T . P^T : v_mfma_f32_16x16x16bf16_1k, A = the
-//   8-byte [dim][4 tokens] slice of block 4c+g's V for dim 16n + lane%16.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ void attend_steps16(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
-                                              const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
-                                              int n_sel, int64_t o, int own_last, int c_lo, int c_hi, float c2,
-                                              RowState &st)
-{
-    const int lane = threadIdx.x & 63;
-    const int r = lane & 15;           // K-load token row / V-load dim
-    const int g = lane >> 4;
-    for (int c = c_lo; c < c_hi; ++c) {
-        const int lb = 4 * c;
-        int64_t kblk, vblk;
-        uint32_t kmask, vmask;
-        list_entry(sel, n_sel, o, lb + (r >> 2), own_last, kblk, kmask);
-        list_entry(sel, n_sel, o, lb + g, own_last, vblk, vmask);
-        bf16x8 kf[8];
-        {
-            const bf16_t *src = kc + kblk * kBlockElems + (r & 3) * 32 + 8 * g;
-            for (int s = 0; s < 8; ++s) kf[s] = *reinterpret_cast<const bf16x8 *>(src + s * 128);
-        }
-        u32x2 vraw[16];
-        {
-            const bf16_t *src = vc + vblk * kBlockElems + r * kBlock;
-            for (int n = 0; n < 16; ++n) vraw[n] = *reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock);
-        }
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-        for (int s = 0; s < 8; ++s) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], sc, 0, 0, 0);
-        float cmax = -INFINITY;
-        for (int j = 0; j < 4; ++j) {
-            if (!((vmask >> j) & 1u)) sc[j] = -INFINITY;
-            cmax = fmaxf(cmax, sc[j]);
-        }
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-        cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
-        const float m_new = fmaxf(st.m, cmax);
-        const bool grew = m_new > st.m;
-        const float alpha = exp2f((st.m - m_new) * c2);
-        st.m = m_new;
-        float p[4];
-        float psum = 0.f;
-        for (int j = 0; j < 4; ++j) {
-            p[j] = bf16_to_f32(f32_to_bf16(exp2f((sc[j] - m_new) * c2)));
-            psum += p[j];
-        }
-        st.l = st.l * alpha + psum;
-        const s16x4 pf = __builtin_bit_cast(s16x4, u32x2{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])});
-        // rescale O only when some head's running max grew (alpha = 1 elsewhere)
-        if (__builtin_amdgcn_ballot_w64(grew) != 0) {
-            for (int n = 0; n < 16; ++n)
-                for (int j = 0; j < 4; ++j) st.o[n][j] *= alpha;
-        }
-        // zero the V of masked tokens: their cache slots may hold anything
-        const uint32_t vm0 = ((vmask & 1u) ? 0xFFFFu : 0u) | ((vmask & 2u) ? 0xFFFF0000u : 0u);
-        const uint32_t vm1 = ((vmask & 4u) ? 0xFFFFu : 0u) | ((vmask & 8u) ? 0xFFFF0000u : 0u);
-        for (int n = 0; n < 16; ++n) {
-            const s16x4 vf = __builtin_bit_cast(s16x4, u32x2{vraw[n][0] & vm0, vraw[n][1] & vm1});
-            st.o[n] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, st.o[n], 0, 0, 0);
-        }
-    }
-}
-
 __device__ __forceinline__ void init_state(RowState &st) {
     st.m = -INFINITY;
     st.l = 0.f;
@@ -285,7 +216,6 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 
 // Decode, split over the token list: one wave per (split, group, sequence)
 // writes its unnormalised partial (m, l, O) for the 12 heads.
-// (16-token steps: fewer registers, two waves per SIMD, so twice the splits fit.)
 __global__ __launch_bounds__(64) void attend_decode_split_kernel(
     Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t nblk_cap, int budget, int nsplit,
     float c2,
@@ -300,7 +230,7 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
     const int64_t o = pos / kBlock;
     const int own_last = static_cast<int>(pos - o * kBlock);
     const int n_sel = static_cast<int>(o < budget ? o : budget);
-    const int nchunks = (n_sel + 1 + 3) / 4;              // 16-token steps
+    const int nchunks = (n_sel + 1 + kChunkBlocks - 1) / kChunkBlocks;
     const int per = (nchunks + nsplit - 1) / nsplit;
     const int c_lo = split * per;
     const int c_hi = (c_lo + per < nchunks) ? c_lo + per : nchunks;
@@ -312,7 +242,7 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
         load_q_frags(q + b * kQHeads * kHeadDim, grp, pos, tab, qf);
         const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
         const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-        attend_steps16(qf, kc, vc, block_idx + b * budget, n_sel, o, own_last, c_lo, c_hi, c2, st);
+        attend_chunks(qf, kc, vc, block_idx + b * budget, n_sel, o, own_last, c_lo, c_hi, c2, st);
     }
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);

@@ -426,31 +426,35 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     const int64_t per = ((o + NW - 1) / NW + 63) & ~int64_t(63);
     const int64_t r0 = wave * per;
     const int64_t r1 = (r0 + per < o) ? r0 + per : o;
-    // Passes walk the wave's range in groups of 8 x 64 scores: the 8 loads of a
-    // group are issued together, then the 8 steps are processed in order.
-    constexpr int U = 8;
-    auto load8 = [&](int64_t jb, uint32_t (&v)[U]) {
-        for (int u = 0; u < U; ++u) {
+    // The wave's range is processed in register chunks of RC x 64 scores: a
+    // chunk is loaded once (RC loads per lane in flight) and every pass over it
+    // reads registers.  Rows up to 16 waves x RC x 64 = 32,768 scores take one
+    // chunk per wave.
+    constexpr int RC = 32;
+    uint32_t v[RC];
+    auto load_chunk = [&](int64_t jb) {
+        for (int u = 0; u < RC; ++u) {
             const int64_t j = jb + 64 * u + lane;
             v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: digit 4095, never counted
         }
     };
+    const int64_t chunk = 64 * RC;
+    const bool one_chunk = r1 - r0 <= chunk;
+    if (one_chunk) load_chunk(r0);
     // pass A: count, then gather digit-d* scores in block order
     uint32_t ne = 0;
-    for (int64_t jb = r0; jb < r1; jb += 64 * U) {
-        uint32_t v[U];
-        load8(jb, v);
-        for (int u = 0; u < U; ++u) ne += (v[u] >> 20) == dstar;
+    for (int64_t jb = r0; jb < r1; jb += chunk) {
+        if (!one_chunk) load_chunk(jb);
+        for (int u = 0; u < RC; ++u) ne += (v[u] >> 20) == dstar;
     }
     for (int off = 32; off > 0; off >>= 1) ne += __shfl_xor(ne, off);
     uint32_t tot_eq;
     const uint32_t eq_base = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ne : 0u, wsum, tot_eq), 0);
     {
         uint32_t run = eq_base;
-        for (int64_t jb = r0; jb < r1; jb += 64 * U) {
-            uint32_t v[U];
-            load8(jb, v);
-            for (int u = 0; u < U; ++u) {
+        for (int64_t jb = r0; jb < r1; jb += chunk) {
+            if (!one_chunk) load_chunk(jb);
+            for (int u = 0; u < RC; ++u) {
                 const bool e = (v[u] >> 20) == dstar;
                 const uint64_t m = __builtin_amdgcn_ballot_w64(e);
                 if (e) eqk[run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
@@ -484,20 +488,18 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     uint32_t ns = 0;
     {
         uint32_t eqrun = eq_base;
-        for (int64_t jb = r0; jb < r1; jb += 64 * U) {
-            uint32_t v[U];
-            load8(jb, v);
-            for (int u = 0; u < U; ++u) ns += static_cast<uint32_t>(__popcll(taken(v[u], eqrun)));
+        for (int64_t jb = r0; jb < r1; jb += chunk) {
+            if (!one_chunk) load_chunk(jb);
+            for (int u = 0; u < RC; ++u) ns += static_cast<uint32_t>(__popcll(taken(v[u], eqrun)));
         }
     }
     uint32_t tot;
     const uint32_t wbase = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ns : 0u, wsum, tot), 0);
     {
         uint32_t eqrun = eq_base, run = wbase;
-        for (int64_t jb = r0; jb < r1; jb += 64 * U) {
-            uint32_t v[U];
-            load8(jb, v);
-            for (int u = 0; u < U; ++u) {
+        for (int64_t jb = r0; jb < r1; jb += chunk) {
+            if (!one_chunk) load_chunk(jb);
+            for (int u = 0; u < RC; ++u) {
                 const uint64_t tm = taken(v[u], eqrun);
                 if ((tm >> lane) & 1u) {
                     const uint32_t p = run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),

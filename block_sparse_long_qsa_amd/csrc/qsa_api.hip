@@ -98,10 +98,10 @@ int64_t cand_rows(int32_t B, int64_t L, int cap) {
     return rows < L ? rows : L;
 }
 
-// Splits of the decode attention: about two waves per SIMD (2,048 waves).
+// Splits of the decode attention: about one wave per SIMD (1,024 waves).
 int decode_splits(int32_t B) {
-    int s = (2048 + 2 * B - 1) / (2 * B);
-    return s < 1 ? 1 : (s > 64 ? 64 : s);
+    int s = (1024 + 2 * B - 1) / (2 * B);
+    return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
 // Workspace of the fused index + select stage: rotated indexer queries, then
