@@ -467,6 +467,17 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     __syncthreads();
     if (n_eq == k_rem) {
         for (uint32_t t = tid; t < n_eq; t += kHistNT) atomicOr(&selbits[t >> 5], 1u << (t & 31));
+    } else if (n_eq <= static_cast<uint32_t>(kHistNT)) {
+        // rank inside the digit under (score desc, position desc); position order is block order
+        if (static_cast<uint32_t>(tid) < n_eq) {
+            const uint32_t kx = eqk[tid];
+            uint32_t r = 0;
+            for (uint32_t u = 0; u < n_eq; ++u) {
+                const uint32_t ky = eqk[u];
+                r += (ky > kx) || (ky == kx && u > static_cast<uint32_t>(tid));
+            }
+            if (r < k_rem) atomicOr(&selbits[tid >> 5], 1u << (tid & 31));
+        }
     } else {
         radix_topk<kHistNT>(n_eq, static_cast<int>(k_rem), [&](int64_t t) { return eqk[t]; },
                             [](int64_t t) { return t; }, selpos, hist);
