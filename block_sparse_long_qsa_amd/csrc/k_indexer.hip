@@ -168,9 +168,13 @@ hipError_t launch_indexer_scores(hipStream_t st, int32_t B, int64_t L, int64_t q
 //   * the list of (score, block) pairs with score >= tau, appended in ascending
 //     block order (ballot + prefix count per 32-column tile).
 // Queries are owned by one wave each, so the histograms, counters and
-// thresholds need no workgroup barrier.  The exact top-`budget` is then taken
-// from the short list by select_compact_kernel.  A list that would outgrow
-// `cap` keeps counting without storing; its row is recomputed exactly there.
+// thresholds need no workgroup barrier.  After the last tile each wave takes
+// its queries' exact top-`budget` from their lists: every kept score in a bin
+// above the boundary bin (the highest bin whose suffix count reaches `budget`)
+// is selected, and the rest come from the boundary bin, ranked in LDS; the
+// selection is written in ascending block order.  A list that outgrew `cap`
+// (it keeps counting without storing) or a boundary bin too crowded to rank
+// here sends its row to select_fixup_kernel, which recomputes it exactly.
 // Workgroups are issued latest-queries-first (longest rows first).
 constexpr int kTopkBins = 128;
 constexpr int kTopkBinBase = 951;      // bin 1 = [2^-8, 2^-8 * 1.125); 952 = (127 - 8) * 8
@@ -184,11 +188,101 @@ __device__ __forceinline__ float topk_bin_edge(int b) {
     return b <= 0 ? 0.0f : __uint_as_float(static_cast<uint32_t>(b + kTopkBinBase) << 20);
 }
 
+constexpr int kTopkBMax = 1536;        // boundary-bin entries a wave ranks in LDS
+constexpr int kTopkRankMax = 512;      // clamped end bins: ranked by counting up to this many
+constexpr int kU = 32;                 // list entries per lane in flight in the final pass
+
+// Order this wave's LDS accesses: a write by one lane is seen by a later read of
+// another lane.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of set lanes of m below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Bitonic sort of 64*R 32-bit keys held by one wave, descending.  Element
+// r*64 + lane sits in k[r] of that lane: strides of 64 and more compare
+// registers of one lane, smaller strides exchange between lanes.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint32_t (&k)[R], int lane) {
+#pragma unroll
+    for (int size = 2; size <= 64 * R; size <<= 1) {
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            if (stride >= 64) {
+                const int rs = stride >> 6;
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if ((r & rs) == 0) {
+                        const bool desc = ((r * 64) & size) == 0;
+                        const uint32_t x = k[r], y = k[r + rs];
+                        const uint32_t hi = x > y ? x : y, lo = x > y ? y : x;
+                        k[r] = desc ? hi : lo;
+                        k[r + rs] = desc ? lo : hi;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    const uint32_t y = __shfl_xor(k[r], stride);
+                    const bool desc = ((r * 64 + lane) & size) == 0;
+                    const bool lower = (lane & stride) == 0;
+                    const uint32_t hi = k[r] > y ? k[r] : y, lo = k[r] > y ? y : k[r];
+                    k[r] = (lower == desc) ? hi : lo;
+                }
+            }
+        }
+    }
+}
+
+// The k_rem largest of nb packed boundary keys (nb <= 64*R): their block ids go
+// to dst[0 .. k_rem), in rank order.  Padding keys are 0: a real key is 0 only
+// for ordinal 0 with equal low score bits, the smallest real key, which ties
+// the padding at the end of the order where no rank below k_rem < nb reaches.
+template <int R>
+__device__ __forceinline__ void boundary_take(const uint32_t *bkey, const int32_t *bid, uint32_t nb, uint32_t k_rem, int32_t *dst,
+                              int lane) {
+    uint32_t k[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t i = r * 64 + lane;
+        k[r] = (i < nb) ? bkey[i] : 0u;
+    }
+    wave_sort_desc<R>(k, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint32_t i = r * 64 + lane;
+        if (i < k_rem) dst[i] = bid[k[r] & 0x7FFu];
+    }
+}
+
+// Write the n (<= 64*R) selected block ids of sel[] to out[] ascending.
+template <int R>
+__device__ __forceinline__ void emit_sorted(const int32_t *sel, int n, int32_t *__restrict__ out, int lane) {
+    uint32_t k[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * 64 + lane;
+        k[r] = (i < n) ? static_cast<uint32_t>(sel[i]) + 1u : 0u;     // ids + 1 sort ahead of the padding
+    }
+    wave_sort_desc<R>(k, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * 64 + lane;
+        if (i < n) out[n - 1 - i] = static_cast<int32_t>(k[r] - 1u);
+    }
+}
+
 __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, int cap,
     const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar,
-    float *__restrict__ cand_score, int32_t *__restrict__ cand_idx, int32_t *__restrict__ cand_count,
-    int32_t *__restrict__ cand_meta)
+    uint2 *__restrict__ cand, int32_t *__restrict__ bidx, int64_t bi_bstride, int32_t *__restrict__ ovf)
 {
     __shared__ __attribute__((aligned(16))) bf16_t lds[2][kIdxSubCols * kLdsRow];
     __shared__ uint32_t hist[kIdxQueriesPerWG][kTopkBins];
@@ -203,7 +297,14 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     const int64_t q0 = tile * kIdxQueriesPerWG;
     const int64_t q_last = (q0 + kIdxQueriesPerWG - 1 < L) ? q0 + kIdxQueriesPerWG - 1 : L - 1;
     const int64_t o_hi = (q_offset + q_last) / kBlock;
-    if (o_hi <= budget) return;                 // every row of the tile keeps all its candidates
+    if (o_hi <= budget) {                       // every row of the tile keeps all its candidates
+        for (int64_t q = q0 + wave; q <= q_last; q += 4) {
+            const int64_t o = (q_offset + q) / kBlock;
+            int32_t *out = bidx + b * bi_bstride + q * budget;
+            for (int t = lane; t < budget; t += 64) out[t] = (t < o) ? t : -1;
+        }
+        return;
+    }
 
     for (int x = tid; x < kIdxQueriesPerWG * kTopkBins; x += 256) (&hist[0][0])[x] = 0;
 
@@ -239,8 +340,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
     // candidate lists of this workgroup's 64 queries (rows b*L + q0 .. +63); the
     // padding queries of a ragged tile never append (infinite threshold)
-    float *__restrict__ wg_score = cand_score + (b * L + q0) * cap;
-    int32_t *__restrict__ wg_idx = cand_idx + (b * L + q0) * cap;
+    uint2 *__restrict__ wg_cand = cand + (b * L + q0) * cap;
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
     // k̄ tiles: the next tile is loaded into registers before the current
@@ -312,8 +412,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                             const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
                             if (pos < static_cast<uint32_t>(cap)) {
                                 const uint32_t off = ql * static_cast<uint32_t>(cap) + pos;
-                                wg_score[off] = sc;
-                                wg_idx[off] = col;
+                                wg_cand[off] = make_uint2(__float_as_uint(sc), static_cast<uint32_t>(col));
                             }
                             atomicAdd(&hist[ql][topk_bin(sc)], 1u);
                         }
@@ -362,12 +461,15 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         __syncthreads();
         buf ^= 1;
     }
-    // final boundary bin of each query: the highest bin whose suffix count
-    // reaches the budget, and the number of kept scores above it
+    // ---- final selection of each query, by the wave that owns it.
+    __syncthreads();
+    // Boundary bin of each of the wave's queries: the highest bin whose suffix
+    // count of kept scores reaches the budget; `above` kept scores lie in
+    // higher bins and are all selected.  Lane j keeps query 16*wave + j's.
+    int my_bstar = -1;
+    uint32_t my_above = 0;
     for (int j = 0; j < 16; ++j) {
         const int ql = 16 * wave + j;
-        const int64_t q = q0 + ql;
-        if (q >= L) break;
         const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
         uint32_t incl = h0 + h1;
         for (int off = 1; off < 64; off <<= 1) {
@@ -375,30 +477,143 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             if (lane + off < 64) incl += other;
         }
         const uint32_t c1 = incl - h0;
-        const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
-                         : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
-        const uint32_t above = (cand == 2 * lane + 1) ? c1 - h1 : incl - h0;    // bins > cand
-        const uint64_t vm = __builtin_amdgcn_ballot_w64(cand >= 0);
+        const int candb = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
+                          : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
+        const uint32_t ab = (candb == 2 * lane + 1) ? c1 - h1 : c1;
+        const uint64_t vm = __builtin_amdgcn_ballot_w64(candb >= 0);
         const int hi = vm ? 63 - __clzll(vm) : 0;
-        const int bin = vm ? __shfl(cand, hi) : -1;
-        const uint32_t ab = __shfl(above, hi);
-        const uint32_t n = __shfl(st_cnt, j);
-        if (lane == 0) {
-            cand_count[b * L + q] = static_cast<int32_t>(n);
-            cand_meta[2 * (b * L + q)] = bin;
-            cand_meta[2 * (b * L + q) + 1] = static_cast<int32_t>(vm ? ab : 0);
+        const int bs = __shfl(candb, hi);
+        const uint32_t av = __shfl(ab, hi);
+        if (lane == j) {
+            my_bstar = vm ? bs : -1;
+            my_above = av;
         }
+    }
+    wave_sync();
+    // The k̄ tiles and this wave's histogram rows are now per-wave scratch:
+    // boundary keys and the unordered selection in the first, the boundary
+    // entries' block ids in the second.
+    uint32_t *bkey = reinterpret_cast<uint32_t *>(&lds[0][0]) + wave * (kTopkBMax + kMaxBudget);
+    int32_t *sel = reinterpret_cast<int32_t *>(bkey + kTopkBMax);
+    int32_t *bid = reinterpret_cast<int32_t *>(&hist[16 * wave][0]);
+    for (int j = 0; j < 16; ++j) {
+        const int ql = 16 * wave + j;
+        const int64_t q = q0 + ql;
+        if (q >= L) break;
+        const int64_t o = (q_offset + q) / kBlock;
+        int32_t *out = bidx + b * bi_bstride + q * budget;
+        if (o <= budget) {
+            for (int t = lane; t < budget; t += 64) out[t] = (t < o) ? t : -1;
+            continue;
+        }
+        const uint32_t c = __builtin_amdgcn_readlane(st_cnt, j);
+        const int bstar = __builtin_amdgcn_readlane(my_bstar, j);
+        const uint32_t above = __builtin_amdgcn_readlane(my_above, j);
+        const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
+        // Inside an interior bin the high score bits are fixed, so (low 20
+        // score bits, boundary ordinal) packs (score desc, block desc) into one
+        // 32-bit key.  The two clamped end bins keep full score bits.
+        const bool clamped = bstar == 0 || bstar == kTopkBins - 1;
+        bool fail = c > static_cast<uint32_t>(cap) || bstar < 0;
+        uint32_t nb = 0, ng = 0;
+        if (!fail) {
+            // one pass over the list, kU entries per lane in flight: the
+            // higher-bin blocks go to sel[], the boundary-bin ones to bkey/bid
+            const uint2 *lst = wg_cand + ql * cap;
+            for (uint32_t p0 = 0; p0 < c; p0 += 64 * kU) {
+                uint2 e[kU];
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const uint32_t p = p0 + 64 * u + lane;
+                    e[u] = (p < c) ? lst[p] : make_uint2(0xFFFFFFFFu, 0u);
+                }
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    const bool valid = e[u].x != 0xFFFFFFFFu;
+                    const int bn = topk_bin(__uint_as_float(e[u].x));
+                    const bool g = valid && bn > bstar;
+                    const bool eq = valid && bn == bstar;
+                    const uint64_t gm = __builtin_amdgcn_ballot_w64(g);
+                    const uint64_t em = __builtin_amdgcn_ballot_w64(eq);
+                    if (g) {
+                        const uint32_t t = ng + lanes_below(gm);
+                        if (t < static_cast<uint32_t>(kMaxBudget)) sel[t] = static_cast<int32_t>(e[u].y);
+                    }
+                    if (eq) {
+                        const uint32_t t = nb + lanes_below(em);
+                        if (t < static_cast<uint32_t>(kTopkBMax)) {
+                            bkey[t] = clamped ? e[u].x : ((e[u].x & 0xFFFFFu) << 11) | t;
+                            bid[t] = static_cast<int32_t>(e[u].y);
+                        }
+                    }
+                    ng += static_cast<uint32_t>(__popcll(gm));
+                    nb += static_cast<uint32_t>(__popcll(em));
+                }
+            }
+            fail = ng != above || nb < k_rem || nb > static_cast<uint32_t>(kTopkBMax) ||
+                   (clamped && nb != k_rem && nb > static_cast<uint32_t>(kTopkRankMax));
+        }
+        if (fail) {                                   // exact recompute by select_fixup_kernel
+            if (lane == 0) {
+                const int slot = atomicAdd(&ovf[0], 1);
+                ovf[1 + slot] = static_cast<int32_t>(b * L + q);
+            }
+            continue;
+        }
+        wave_sync();
+        // the k_rem best boundary entries join sel[above ..)
+        if (nb == k_rem) {
+            for (uint32_t t = lane; t < nb; t += 64) sel[above + t] = bid[t];
+        } else if (clamped) {
+            // rank = entries ahead in (score desc, ordinal desc); ranks are unique
+            for (uint32_t t = lane; t < nb; t += 64) {
+                const uint32_t kx = bkey[t];
+                uint32_t r = 0;
+                for (uint32_t u = 0; u < nb; ++u) {
+                    const uint32_t ky = bkey[u];
+                    r += (ky > kx) || (ky == kx && u > t);
+                }
+                if (r < k_rem) sel[above + r] = bid[t];
+            }
+        } else {
+            const uint32_t n64 = (nb + 63) >> 6;
+            if (n64 <= 1)       boundary_take<1>(bkey, bid, nb, k_rem, sel + above, lane);
+            else if (n64 <= 2)  boundary_take<2>(bkey, bid, nb, k_rem, sel + above, lane);
+            else if (n64 <= 4)  boundary_take<4>(bkey, bid, nb, k_rem, sel + above, lane);
+            else if (n64 <= 8)  boundary_take<8>(bkey, bid, nb, k_rem, sel + above, lane);
+            else if (n64 <= 16) boundary_take<16>(bkey, bid, nb, k_rem, sel + above, lane);
+            else                boundary_take<32>(bkey, bid, nb, k_rem, sel + above, lane);
+        }
+        wave_sync();
+        // ascending block order
+        if (budget <= 64)       emit_sorted<1>(sel, budget, out, lane);
+        else if (budget <= 128) emit_sorted<2>(sel, budget, out, lane);
+        else if (budget <= 256) emit_sorted<4>(sel, budget, out, lane);
+        else                    emit_sorted<8>(sel, budget, out, lane);
+        wave_sync();
     }
 }
 
 hipError_t launch_indexer_topk(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget,
                                int cap, const bf16_t *qrot, int64_t qrot_bstride, const bf16_t *kbar,
-                               float *cand_score, int32_t *cand_idx, int32_t *cand_count, int32_t *cand_meta)
+                               uint2 *cand, int32_t *bidx, int64_t bi_bstride, int32_t *ovf)
 {
     if (L <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((L + kIdxQueriesPerWG - 1) / kIdxQueriesPerWG), static_cast<unsigned>(B));
     hipLaunchKernelGGL(indexer_topk_kernel, grid, dim3(256), 0, st, L, q_offset, nblk_cap, budget, cap, qrot,
-                       qrot_bstride, kbar, cand_score, cand_idx, cand_count, cand_meta);
+                       qrot_bstride, kbar, cand, bidx, bi_bstride, ovf);
+    return hipGetLastError();
+}
+
+// Clear n words (counters that a later kernel accumulates into).
+__global__ void zero_words_kernel(int32_t *p, int64_t n) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0;
+}
+
+hipError_t launch_zero_words(hipStream_t st, int32_t *p, int64_t n) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_words_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st, p, n);
     return hipGetLastError();
 }
 

@@ -23,7 +23,6 @@ namespace qsa {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelMaxBins = 2048;
-constexpr int kMaxCandCap = 8192;      // largest candidate list the compact path stages in LDS
 
 __device__ __forceinline__ uint32_t lane_rank(uint64_t m) {
     const int lane = threadIdx.x & 63;
@@ -251,104 +250,35 @@ __device__ __forceinline__ int score_bin(uint32_t bits) {
     return b < 0 ? 0 : (b > 127 ? 127 : b);
 }
 
-// Selection from the candidate lists of the fused index + select kernel.
-// Row (b, i) kept cand_count[row] (score, block) pairs in ascending block order
-// at cand_score/cand_idx + row*cap (row = b*L + i).  cand_meta[row] = (bin,
-// above): every kept score in a higher 128-bin log bin than `bin` is selected
-// (`above` of them), none below is, and the remaining budget - above come from
-// the scores inside `bin`, ranked exactly.  A count above `cap` means the list
-// overflowed: the row's scores are recomputed here from q~ and k̄.
-constexpr int kBoundaryMax = 2048;
-__global__ __launch_bounds__(kSelThreads) void select_compact_kernel(
-    int64_t L, int64_t q_offset, int budget, int cap,
-    const float *__restrict__ cand_score, const int32_t *__restrict__ cand_idx,
-    const int32_t *__restrict__ cand_count, const int32_t *__restrict__ cand_meta,
+// Rows the fused index + select kernel could not finish (a candidate list
+// longer than its capacity, or a boundary bin too crowded for its in-LDS
+// ranking) are listed in ovf[1 .. ovf[0]] as b*L + i.  Their scores
+// I[p][j] = sum_h ReLU(<q~_h, k̄_j>) are recomputed from q~ and k̄ and the
+// selection is taken exactly.  Workgroups stride over the list, so the launch
+// needs no host-side count.
+__global__ __launch_bounds__(kSelThreads) void select_fixup_kernel(
+    int64_t L, int64_t q_offset, int budget, const int32_t *__restrict__ ovf,
     int32_t *__restrict__ block_idx, int64_t bi_bstride,
     const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar, int64_t nblk_cap)
 {
     __shared__ uint32_t hist[kSelMaxBins];
-    __shared__ uint32_t keys[kMaxCandCap];
-    __shared__ uint32_t bl[kBoundaryMax];               // list positions of the boundary-bin scores
-    __shared__ int32_t selpos[kMaxBudget];              // boundary positions selected
-    __shared__ uint32_t selbits[kMaxCandCap / 32];
-    __shared__ uint32_t wsum[4];
     __shared__ float qs[kIdxHeads * kIdxDim];
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
-    const int64_t b = row / L;
-    const int64_t i = row - b * L;
-    const int64_t o = (q_offset + i) / kBlock;
-    int32_t *out = block_idx + b * bi_bstride + i * budget;
-    if (take_all(o, budget, out)) return;
-    const int64_t c = cand_count[row];
-    if (c <= cap) {
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(cand_score + row * cap);
-        const int32_t *ids = cand_idx + row * cap;
-        const int bstar = cand_meta[2 * row];
-        const uint32_t k_rem = static_cast<uint32_t>(budget - cand_meta[2 * row + 1]);
-        stage_words(src, c, keys);
-        for (int x = tid; x < kMaxCandCap / 32; x += kSelThreads) selbits[x] = 0;
+    const int n = ovf[0];
+    for (int k = blockIdx.x; k < n; k += gridDim.x) {
+        const int64_t row = ovf[1 + k];
+        const int64_t b = row / L;
+        const int64_t i = row - b * L;
+        const int64_t o = (q_offset + i) / kBlock;
+        int32_t *out = block_idx + b * bi_bstride + i * budget;
+        const bf16_t *qr = qrot + b * qrot_bstride + i * kIdxHeads * kIdxDim;
+        for (int x = tid; x < kIdxHeads * kIdxDim; x += kSelThreads) qs[x] = bf16_to_f32(qr[x]);
         __syncthreads();
-        // contiguous segment of the list per thread
-        const int seg = static_cast<int>((c + kSelThreads - 1) / kSelThreads);
-        const int j0 = tid * seg;
-        const int j1 = (j0 + seg < c) ? j0 + seg : static_cast<int>(c);
-        uint32_t nb = 0;
-        for (int j = j0; j < j1; ++j) nb += score_bin(keys[j]) == bstar;
-        uint32_t n_b;
-        uint32_t at = block_exclusive_scan(nb, wsum, n_b);
-        if (n_b > kBoundaryMax || bstar < 0 || n_b < k_rem) {   // crowded bin (or no bin): radix over the list
-            radix_topk(c, budget, [&](int64_t j) { return keys[j]; }, [&](int64_t j) { return ids[j]; }, out, hist);
-            return;
-        }
-        for (int j = j0; j < j1; ++j)
-            if (score_bin(keys[j]) == bstar) bl[at++] = static_cast<uint32_t>(j);
+        const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
+        auto score = [&](int64_t j) -> uint32_t { return recompute_score(qs, kb, j); };
+        radix_topk(o, budget, score, [](int64_t j) { return j; }, out, hist);
         __syncthreads();
-        if (n_b == k_rem) {
-            for (uint32_t t = tid; t < n_b; t += kSelThreads) atomicOr(&selbits[bl[t] >> 5], 1u << (bl[t] & 31));
-        } else if (n_b <= kSelThreads) {
-            // rank inside the bin: order (score desc, position desc)
-            if (static_cast<uint32_t>(tid) < n_b) {
-                const uint32_t px = bl[tid], kx = keys[px];
-                uint32_t r = 0;
-                for (uint32_t u = 0; u < n_b; ++u) {
-                    const uint32_t py = bl[u], ky = keys[py];
-                    r += (ky > kx) || (ky == kx && py > px);
-                }
-                if (r < k_rem) atomicOr(&selbits[px >> 5], 1u << (px & 31));
-            }
-        } else {
-            radix_topk(n_b, static_cast<int>(k_rem), [&](int64_t t) { return keys[bl[t]]; },
-                       [&](int64_t t) { return static_cast<int64_t>(bl[t]); }, selpos, hist);
-            __syncthreads();
-            for (uint32_t t = tid; t < k_rem; t += kSelThreads)
-                atomicOr(&selbits[selpos[t] >> 5], 1u << (selpos[t] & 31));
-        }
-        __syncthreads();
-        // ordered emission
-        uint32_t ns = 0;
-        for (int j = j0; j < j1; ++j) {
-            const int bj = score_bin(keys[j]);
-            ns += bj > bstar || (bj == bstar && ((selbits[j >> 5] >> (j & 31)) & 1u));
-        }
-        uint32_t tot;
-        uint32_t w = block_exclusive_scan(ns, wsum, tot);
-        for (int j = j0; j < j1; ++j) {
-            const int bj = score_bin(keys[j]);
-            if (bj > bstar || (bj == bstar && ((selbits[j >> 5] >> (j & 31)) & 1u))) {
-                if (w < static_cast<uint32_t>(budget)) out[w] = ids[j];
-                ++w;
-            }
-        }
-        return;
     }
-    // Overflow: recompute I[p][j] = sum_h ReLU(<q~_h, k̄_j>) for every candidate.
-    const bf16_t *qr = qrot + b * qrot_bstride + i * kIdxHeads * kIdxDim;
-    for (int x = tid; x < kIdxHeads * kIdxDim; x += kSelThreads) qs[x] = bf16_to_f32(qr[x]);
-    __syncthreads();
-    const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
-    auto score = [&](int64_t j) -> uint32_t { return recompute_score(qs, kb, j); };
-    radix_topk(o, budget, score, [](int64_t j) { return j; }, out, hist);
 }
 
 // Block-wide exclusive prefix sum for NT threads.
@@ -562,17 +492,15 @@ hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
     return hipGetLastError();
 }
 
-hipError_t launch_select_compact(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int budget, int cap,
-                                 const float *cand_score, const int32_t *cand_idx, const int32_t *cand_count,
-                                 const int32_t *cand_meta, int32_t *block_idx, int64_t bi_bstride, const bf16_t *qrot, int64_t qrot_bstride,
-                                 const bf16_t *kbar, int64_t nblk_cap)
+hipError_t launch_select_fixup(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int budget,
+                               const int32_t *ovf, int32_t *block_idx, int64_t bi_bstride, const bf16_t *qrot,
+                               int64_t qrot_bstride, const bf16_t *kbar, int64_t nblk_cap)
 {
     const int64_t rows = static_cast<int64_t>(B) * L;
     if (rows == 0) return hipSuccess;
-    if (cap > kMaxCandCap) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(select_compact_kernel, dim3(static_cast<unsigned>(rows)), dim3(kSelThreads), 0, st, L,
-                       q_offset, budget, cap, cand_score, cand_idx, cand_count, cand_meta, block_idx, bi_bstride, qrot,
-                       qrot_bstride, kbar, nblk_cap);
+    const unsigned grid = static_cast<unsigned>(rows < 512 ? rows : 512);
+    hipLaunchKernelGGL(select_fixup_kernel, dim3(grid), dim3(kSelThreads), 0, st, L, q_offset, budget, ovf, block_idx,
+                       bi_bstride, qrot, qrot_bstride, kbar, nblk_cap);
     return hipGetLastError();
 }
 

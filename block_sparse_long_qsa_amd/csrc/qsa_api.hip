@@ -25,10 +25,10 @@ hipError_t launch_indexer_scores(hipStream_t, int32_t, int64_t, int64_t, int64_t
 hipError_t launch_select(hipStream_t, int32_t, int64_t, int64_t, const int32_t *, int64_t, const float *, int64_t,
                          int32_t *, int64_t, int);
 hipError_t launch_indexer_topk(hipStream_t, int32_t, int64_t, int64_t, int64_t, int, int, const bf16_t *, int64_t,
-                               const bf16_t *, float *, int32_t *, int32_t *, int32_t *);
-hipError_t launch_select_compact(hipStream_t, int32_t, int64_t, int64_t, int, int, const float *, const int32_t *,
-                                 const int32_t *, const int32_t *, int32_t *, int64_t, const bf16_t *, int64_t,
-                                 const bf16_t *, int64_t);
+                               const bf16_t *, uint2 *, int32_t *, int64_t, int32_t *);
+hipError_t launch_zero_words(hipStream_t, int32_t *, int64_t);
+hipError_t launch_select_fixup(hipStream_t, int32_t, int64_t, int64_t, int, const int32_t *, int32_t *, int64_t,
+                               const bf16_t *, int64_t, const bf16_t *, int64_t);
 hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
                                  const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
 hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int, int, float,
@@ -104,19 +104,18 @@ int decode_splits(int32_t B) {
     return s < 1 ? 1 : (s > 32 ? 32 : s);
 }
 
-// Workspace of the fused index + select stage: rotated indexer queries, then
-// the candidate lists (score, block) and counts of one launch of query rows.
-struct IdxSelLayout { size_t qrot, cscore, cidx, ccount, cmeta, total; int64_t rows; };
+// Workspace of the fused index + select stage: rotated indexer queries, the
+// candidate lists (score, block) of one launch of query rows, and the list of
+// rows left to the exact fixup (a count, then b*rows + i per row).
+struct IdxSelLayout { size_t qrot, cand, ovf, total; int64_t rows; };
 IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     IdxSelLayout f{};
     f.rows = cand_rows(B, L, cap);
     const size_t n = static_cast<size_t>(B) * f.rows;
     f.qrot = 0;
-    f.cscore = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
-    f.cidx = f.cscore + align_up(n * cap * 4);
-    f.ccount = f.cidx + align_up(n * cap * 4);
-    f.cmeta = f.ccount + align_up(n * 4);
-    f.total = f.cmeta + align_up(n * 8);
+    f.cand = align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2);
+    f.ovf = f.cand + align_up(n * cap * 8);
+    f.total = f.ovf + align_up((n + 1) * 4);
     return f;
 }
 
@@ -141,10 +140,8 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
                             const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *bidx, char *w,
                             const IdxSelLayout &f) {
     bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
-    float *cscore = reinterpret_cast<float *>(w + f.cscore);
-    int32_t *cidx = reinterpret_cast<int32_t *>(w + f.cidx);
-    int32_t *ccount = reinterpret_cast<int32_t *>(w + f.ccount);
-    int32_t *cmeta = reinterpret_cast<int32_t *>(w + f.cmeta);
+    uint2 *cand = reinterpret_cast<uint2 *>(w + f.cand);
+    int32_t *ovf = reinterpret_cast<int32_t *>(w + f.ovf);
     const int budget = h->p.budget_blocks;
     const int64_t qstride = L * kIdxHeads * kIdxDim;
     hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
@@ -152,11 +149,13 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
         const int64_t nr = (r0 + f.rows < L) ? f.rows : L - r0;
         const int64_t pos0 = q_offset + r0;
         const bf16_t *qr = qrot + r0 * kIdxHeads * kIdxDim;
-        e = launch_indexer_topk(st, B, nr, pos0, nblk_cap(h), budget, h->cap, qr, qstride, kbar_cache, cscore, cidx,
-                                ccount, cmeta);
+        e = launch_zero_words(st, ovf, 1);
         if (e == hipSuccess)
-            e = launch_select_compact(st, B, nr, pos0, budget, h->cap, cscore, cidx, ccount, cmeta, bidx + r0 * budget,
-                                      L * budget, qr, qstride, kbar_cache, nblk_cap(h));
+            e = launch_indexer_topk(st, B, nr, pos0, nblk_cap(h), budget, h->cap, qr, qstride, kbar_cache, cand,
+                                    bidx + r0 * budget, L * budget, ovf);
+        if (e == hipSuccess)
+            e = launch_select_fixup(st, B, nr, pos0, budget, ovf, bidx + r0 * budget, L * budget, qr, qstride,
+                                    kbar_cache, nblk_cap(h));
     }
     return e;
 }
