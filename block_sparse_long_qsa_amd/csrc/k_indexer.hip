@@ -192,55 +192,6 @@ constexpr int kTopkBMax = 1536;        // boundary-bin entries a wave ranks in L
 constexpr int kTopkRankMax = 512;      // clamped end bins: ranked by counting up to this many
 constexpr int kU = 32;                 // list entries per lane in flight in the final pass
 
-// Order this wave's LDS accesses: a write by one lane is seen by a later read of
-// another lane.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Number of set lanes of m below this lane.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-}
-
-// Bitonic sort of 64*R 32-bit keys held by one wave, descending.  Element
-// r*64 + lane sits in k[r] of that lane: strides of 64 and more compare
-// registers of one lane, smaller strides exchange between lanes.
-template <int R>
-__device__ __forceinline__ void wave_sort_desc(uint32_t (&k)[R], int lane) {
-#pragma unroll
-    for (int size = 2; size <= 64 * R; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            if (stride >= 64) {
-                const int rs = stride >> 6;
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    if ((r & rs) == 0) {
-                        const bool desc = ((r * 64) & size) == 0;
-                        const uint32_t x = k[r], y = k[r + rs];
-                        const uint32_t hi = x > y ? x : y, lo = x > y ? y : x;
-                        k[r] = desc ? hi : lo;
-                        k[r + rs] = desc ? lo : hi;
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int r = 0; r < R; ++r) {
-                    const uint32_t y = __shfl_xor(k[r], stride);
-                    const bool desc = ((r * 64 + lane) & size) == 0;
-                    const bool lower = (lane & stride) == 0;
-                    const uint32_t hi = k[r] > y ? k[r] : y, lo = k[r] > y ? y : k[r];
-                    k[r] = (lower == desc) ? hi : lo;
-                }
-            }
-        }
-    }
-}
-
 // The k_rem largest of nb packed boundary keys (nb <= 64*R): their block ids go
 // to dst[0 .. k_rem), in rank order.  Padding keys are 0: a real key is 0 only
 // for ordinal 0 with equal low score bits, the smallest real key, which ties
@@ -257,25 +208,8 @@ __device__ __forceinline__ void boundary_take(const uint32_t *bkey, const int32_
     wave_sort_desc<R>(k, lane);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        const uint32_t i = r * 64 + lane;
+        const uint32_t i = lane * R + r;
         if (i < k_rem) dst[i] = bid[k[r] & 0x7FFu];
-    }
-}
-
-// Write the n (<= 64*R) selected block ids of sel[] to out[] ascending.
-template <int R>
-__device__ __forceinline__ void emit_sorted(const int32_t *sel, int n, int32_t *__restrict__ out, int lane) {
-    uint32_t k[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * 64 + lane;
-        k[r] = (i < n) ? static_cast<uint32_t>(sel[i]) + 1u : 0u;     // ids + 1 sort ahead of the padding
-    }
-    wave_sort_desc<R>(k, lane);
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int i = r * 64 + lane;
-        if (i < n) out[n - 1 - i] = static_cast<int32_t>(k[r] - 1u);
     }
 }
 

@@ -305,35 +305,60 @@ __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t *wsum /* 
 }
 
 // Decode selection from a score row whose histogram of bits 30..20 (2048
-// digits) the scan kernel already built: the boundary digit d* and the count
-// above it come from the histogram; one ordered pass gathers the scores of
-// digit d* (in block order), an exact select among them picks the remaining
-// ones, and a second ordered pass emits the selection ascending.  Rows whose
-// boundary digit holds more than kEqMax scores use the plain radix select.
+// digits) the scan kernel already built.  The boundary digit d* and the count
+// above it come from the histogram.  The row is held in registers (loaded
+// while the histogram is read); each wave owns a contiguous range of it.  A
+// counting pass and a scan of the per-wave counts give every wave its offsets,
+// so one ordered pass stores the blocks of digits above d* and the digit-d*
+// scores in block order.  Inside digit d* the high 12 score bits are equal, so
+// (low 20 bits, ordinal) is one 32-bit key ordering (score desc, block desc):
+// the remaining budget is the digit-d* scores of rank below it.  Both lists
+// are ascending; a merge writes the selection.  Rows whose boundary digit holds more
+// than kEqMax scores use the plain radix select.
 constexpr int kHistNT = 1024;
-constexpr int kEqMax = 8192;
+constexpr int kEqMax = kHistNT;
+
 __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
     const uint32_t *__restrict__ dhist, int32_t *__restrict__ block_idx, int budget)
 {
+    constexpr int NW = kHistNT / 64;
     __shared__ uint32_t hist[kSelMaxBins];
-    __shared__ uint32_t eqk[kEqMax];
-    __shared__ uint32_t selbits[kEqMax / 32];
-    __shared__ int32_t selpos[kMaxBudget];
-    __shared__ uint32_t wsum[kHistNT / 64];
+    __shared__ __attribute__((aligned(16))) uint32_t eqk[kEqMax];
+    __shared__ int32_t eqb[kEqMax];
+    __shared__ int32_t sel[kMaxBudget];
+    __shared__ int32_t selq[kMaxBudget];
+    __shared__ uint32_t wsum[NW];
+    __shared__ uint32_t wcnt[2][NW];
     __shared__ uint32_t s_digit, s_above;
     const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
     int32_t *out = block_idx + b * budget;
     if (take_all(o, budget, out)) return;
     const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * ncol);
+    // register chunks of RC x 64 scores (rows up to 16 x 2048 scores: one chunk)
+    constexpr int RC = 32;
+    const int64_t per = ((o + NW - 1) / NW + 63) & ~int64_t(63);
+    const int64_t r0 = wave * per;
+    const int64_t r1 = (r0 + per < o) ? r0 + per : o;
+    uint32_t v[RC];
+    auto load_chunk = [&](int64_t jb) {
+#pragma unroll
+        for (int u = 0; u < RC; ++u) {
+            const int64_t j = jb + 64 * u + lane;
+            v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: digit 4095, never taken
+        }
+    };
+    const int64_t chunk = 64 * RC;
+    const bool one_chunk = r1 - r0 <= chunk;
+    if (one_chunk) load_chunk(r0);
     // boundary digit from the histogram: 2 digits per thread, suffix sums
     {
         const uint32_t h0 = dhist[b * kSelMaxBins + 2 * tid], h1 = dhist[b * kSelMaxBins + 2 * tid + 1];
         hist[2 * tid] = h0;
         hist[2 * tid + 1] = h1;
-        // inclusive suffix sum over threads of h0 + h1: total - exclusive prefix
         uint32_t tot;
         const uint32_t before = block_scan_nt<kHistNT>(h0 + h1, wsum, tot);
         const uint32_t incl = tot - before;             // digits >= 2*tid
@@ -344,112 +369,100 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
         __syncthreads();
     }
     const uint32_t dstar = s_digit;
-    const uint32_t k_rem = static_cast<uint32_t>(budget) - s_above;
+    const uint32_t above = s_above;
+    const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
     const uint32_t n_eq = hist[dstar];
-    if (n_eq > kEqMax) {
+    if (n_eq > static_cast<uint32_t>(kEqMax)) {
         radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
         return;
     }
-    // each wave owns a contiguous range of the row, read 64 scores per step
-    constexpr int NW = kHistNT / 64;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int64_t per = ((o + NW - 1) / NW + 63) & ~int64_t(63);
-    const int64_t r0 = wave * per;
-    const int64_t r1 = (r0 + per < o) ? r0 + per : o;
-    // The wave's range is processed in register chunks of RC x 64 scores: a
-    // chunk is loaded once (RC loads per lane in flight) and every pass over it
-    // reads registers.  Rows up to 16 waves x RC x 64 = 32,768 scores take one
-    // chunk per wave.
-    constexpr int RC = 32;
-    uint32_t v[RC];
-    auto load_chunk = [&](int64_t jb) {
-        for (int u = 0; u < RC; ++u) {
-            const int64_t j = jb + 64 * u + lane;
-            v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: digit 4095, never counted
-        }
-    };
-    const int64_t chunk = 64 * RC;
-    const bool one_chunk = r1 - r0 <= chunk;
-    if (one_chunk) load_chunk(r0);
-    // pass A: count, then gather digit-d* scores in block order
-    uint32_t ne = 0;
+    // counting pass, then the wave's offsets among all waves
+    uint32_t ng = 0, ne = 0;
     for (int64_t jb = r0; jb < r1; jb += chunk) {
         if (!one_chunk) load_chunk(jb);
-        for (int u = 0; u < RC; ++u) ne += (v[u] >> 20) == dstar;
-    }
-    for (int off = 32; off > 0; off >>= 1) ne += __shfl_xor(ne, off);
-    uint32_t tot_eq;
-    const uint32_t eq_base = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ne : 0u, wsum, tot_eq), 0);
-    {
-        uint32_t run = eq_base;
-        for (int64_t jb = r0; jb < r1; jb += chunk) {
-            if (!one_chunk) load_chunk(jb);
-            for (int u = 0; u < RC; ++u) {
-                const bool e = (v[u] >> 20) == dstar;
-                const uint64_t m = __builtin_amdgcn_ballot_w64(e);
-                if (e) eqk[run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))] = v[u];
-                run += static_cast<uint32_t>(__popcll(m));
-            }
+#pragma unroll
+        for (int u = 0; u < RC; ++u) {
+            const uint32_t d = v[u] >> 20;
+            ng += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(d > dstar && d < 4095u)));
+            ne += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(d == dstar)));
         }
     }
-    for (int x = tid; x < kEqMax / 32; x += kHistNT) selbits[x] = 0;
-    __syncthreads();
-    if (n_eq == k_rem) {
-        for (uint32_t t = tid; t < n_eq; t += kHistNT) atomicOr(&selbits[t >> 5], 1u << (t & 31));
-    } else if (n_eq <= static_cast<uint32_t>(kHistNT)) {
-        // rank inside the digit under (score desc, position desc); position order is block order
-        if (static_cast<uint32_t>(tid) < n_eq) {
-            const uint32_t kx = eqk[tid];
-            uint32_t r = 0;
-            for (uint32_t u = 0; u < n_eq; ++u) {
-                const uint32_t ky = eqk[u];
-                r += (ky > kx) || (ky == kx && u > static_cast<uint32_t>(tid));
-            }
-            if (r < k_rem) atomicOr(&selbits[tid >> 5], 1u << (tid & 31));
-        }
-    } else {
-        radix_topk<kHistNT>(n_eq, static_cast<int>(k_rem), [&](int64_t t) { return eqk[t]; },
-                            [](int64_t t) { return t; }, selpos, hist);
-        __syncthreads();
-        for (uint32_t t = tid; t < k_rem; t += kHistNT) atomicOr(&selbits[selpos[t] >> 5], 1u << (selpos[t] & 31));
+    if (lane == 0) {
+        wcnt[0][wave] = ng;
+        wcnt[1][wave] = ne;
     }
     __syncthreads();
-    // pass B: ordered emission (taken = digit above d*, or a selected digit-d* score)
-    auto taken = [&](uint32_t k, uint32_t &eqrun) -> uint64_t {
-        const uint32_t d = k >> 20;
-        const bool e = d == dstar;
-        const uint64_t em = __builtin_amdgcn_ballot_w64(e);
-        const uint32_t ei = eqrun + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(em >> 32),
-                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(em), 0u));
-        eqrun += static_cast<uint32_t>(__popcll(em));
-        const bool t = (d > dstar && d < 4095u) || (e && ((selbits[ei >> 5] >> (ei & 31)) & 1u));
-        return __builtin_amdgcn_ballot_w64(t);
-    };
-    uint32_t ns = 0;
-    {
-        uint32_t eqrun = eq_base;
-        for (int64_t jb = r0; jb < r1; jb += chunk) {
-            if (!one_chunk) load_chunk(jb);
-            for (int u = 0; u < RC; ++u) ns += static_cast<uint32_t>(__popcll(taken(v[u], eqrun)));
-        }
+    uint32_t gpos = 0, epos = 0;
+    for (int w = 0; w < wave; ++w) {
+        gpos += wcnt[0][w];
+        epos += wcnt[1][w];
     }
-    uint32_t tot;
-    const uint32_t wbase = __shfl(block_scan_nt<kHistNT>(lane == 0 ? ns : 0u, wsum, tot), 0);
-    {
-        uint32_t eqrun = eq_base, run = wbase;
-        for (int64_t jb = r0; jb < r1; jb += chunk) {
-            if (!one_chunk) load_chunk(jb);
-            for (int u = 0; u < RC; ++u) {
-                const uint64_t tm = taken(v[u], eqrun);
-                if ((tm >> lane) & 1u) {
-                    const uint32_t p = run + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(tm >> 32),
-                                                                       __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tm), 0u));
-                    if (p < static_cast<uint32_t>(budget)) out[p] = static_cast<int32_t>(jb + 64 * u + lane);
+    // ordered pass
+    for (int64_t jb = r0; jb < r1; jb += chunk) {
+        if (!one_chunk) load_chunk(jb);
+#pragma unroll
+        for (int u = 0; u < RC; ++u) {
+            const uint32_t d = v[u] >> 20;
+            const bool g = d > dstar && d < 4095u;
+            const bool e = d == dstar;
+            const uint64_t gm = __builtin_amdgcn_ballot_w64(g);
+            const uint64_t em = __builtin_amdgcn_ballot_w64(e);
+            const int32_t blk = static_cast<int32_t>(jb + 64 * u + lane);
+            if (g) {
+                const uint32_t t = gpos + lanes_below(gm);
+                if (t < static_cast<uint32_t>(kMaxBudget)) sel[t] = blk;
+            }
+            if (e) {
+                const uint32_t t = epos + lanes_below(em);
+                if (t < static_cast<uint32_t>(kEqMax)) {
+                    eqk[t] = ((v[u] & 0xFFFFFu) << 10) | t;
+                    eqb[t] = blk;
                 }
-                run += static_cast<uint32_t>(__popcll(tm));
             }
+            gpos += static_cast<uint32_t>(__popcll(gm));
+            epos += static_cast<uint32_t>(__popcll(em));
         }
+    }
+    __syncthreads();
+    // digit-d* scores taken: rank < k_rem by key (keys are distinct); their
+    // block ids are compacted in block order into selq[0 .. k_rem)
+    for (uint32_t u = n_eq + tid; u < ((n_eq + 31) & ~31u); u += kHistNT) eqk[u] = 0u;   // pad: ranks nothing
+    __syncthreads();
+    bool take = false;
+    if (static_cast<uint32_t>(tid) < n_eq) {
+        if (n_eq == k_rem) {
+            take = true;
+        } else {
+            const uint32_t kx = eqk[tid];
+            const u32x4 *e4 = reinterpret_cast<const u32x4 *>(eqk);
+            const uint32_t nq = ((n_eq + 31) & ~31u) >> 2;
+            uint32_t r = 0;
+            for (uint32_t u = 0; u < nq; u += 8) {
+                u32x4 y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] = e4[u + i];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) r += (y[i][0] > kx) + (y[i][1] > kx) + (y[i][2] > kx) + (y[i][3] > kx);
+            }
+            take = r < k_rem;
+        }
+    }
+    uint32_t ntake;
+    const uint32_t qpos = block_scan_nt<kHistNT>(take ? 1u : 0u, wsum, ntake);
+    if (take) selq[qpos] = eqb[tid];
+    __syncthreads();
+    // merge the two ascending lists sel[0 .. above) and selq[0 .. k_rem)
+    const int budget_i = budget;
+    if (tid < budget_i) {
+        const bool from_gt = static_cast<uint32_t>(tid) < above;
+        const int32_t x = from_gt ? sel[tid] : selq[tid - above];
+        const int32_t *other = from_gt ? selq : sel;
+        uint32_t lo = 0, hi = from_gt ? k_rem : above;        // count of other < x
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (other[mid] < x) lo = mid + 1; else hi = mid;
+        }
+        out[(from_gt ? tid : tid - above) + lo] = x;
     }
 }
 

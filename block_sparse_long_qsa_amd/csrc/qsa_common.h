@@ -79,4 +79,103 @@ __device__ __forceinline__ int kblock_off(int t, int d) { return ((d >> 5) * kBl
 // element (token t in block, dim d) of a V block: [d][t]
 __device__ __forceinline__ int vblock_off(int t, int d) { return d * kBlock + t; }
 
+
+// ---- wave-level helpers (64-lane wavefronts)
+
+// Order this wave's LDS accesses: a write by one lane is seen by a later read of
+// another lane.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of set lanes of m below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+}
+
+// Value of lane (lane ^ X) of this wave.  X < 16 moves data inside the
+// VALU with DPP: quad permutations for 1 and 2; 4 = half-row mirror then quad
+// reversal; 8 = row mirror then half-row mirror.  Larger X use ds_bpermute.
+template <int X>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    const int x = static_cast<int>(v);
+    if constexpr (X == 1) {
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xF, 0xF, false));   // [1,0,3,2]
+    } else if constexpr (X == 2) {
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xF, 0xF, false));   // [2,3,0,1]
+    } else if constexpr (X == 4) {
+        const int t = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, false);                 // half mirror
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, false));  // [3,2,1,0]
+    } else if constexpr (X == 8) {
+        const int t = __builtin_amdgcn_update_dpp(0, x, 0x140, 0xF, 0xF, false);                 // row mirror
+        return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, t, 0x141, 0xF, 0xF, false)); // half mirror
+    } else {
+        return static_cast<uint32_t>(__shfl_xor(x, X));
+    }
+}
+
+// One bitonic merge step of (SIZE, STRIDE) and the smaller strides after it,
+// over 64*R keys held lane-major: element lane*R + r sits in k[r] of that
+// lane.  Strides below R compare registers of one lane; larger ones compare
+// register r of lanes lane and lane ^ (STRIDE/R).
+template <int R, int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_steps(uint32_t (&k)[R], int lane) {
+    if constexpr (STRIDE < R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if ((r & STRIDE) == 0) {
+                const bool desc = ((lane * R + r) & SIZE) == 0;
+                const uint32_t x = k[r], y = k[r | STRIDE];
+                const uint32_t hi = x > y ? x : y, lo = x > y ? y : x;
+                k[r] = desc ? hi : lo;
+                k[r | STRIDE] = desc ? lo : hi;
+            }
+        }
+    } else {
+        constexpr int X = STRIDE / R;
+        const bool desc = ((lane * R) & SIZE) == 0;
+        const bool lower = (lane & X) == 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint32_t y = lane_xor<X>(k[r]);
+            const uint32_t hi = k[r] > y ? k[r] : y, lo = k[r] > y ? y : k[r];
+            k[r] = (lower == desc) ? hi : lo;
+        }
+    }
+    if constexpr (STRIDE > 1) bitonic_steps<R, SIZE, STRIDE / 2>(k, lane);
+}
+
+template <int R, int SIZE>
+__device__ __forceinline__ void bitonic_stages(uint32_t (&k)[R], int lane) {
+    bitonic_steps<R, SIZE, SIZE / 2>(k, lane);
+    if constexpr (SIZE < 64 * R) bitonic_stages<R, SIZE * 2>(k, lane);
+}
+
+// Bitonic sort of 64*R 32-bit keys held by one wave, descending: afterwards
+// element lane*R + r (k[r] of lane `lane`) is the (lane*R + r)-th largest.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint32_t (&k)[R], int lane) {
+    bitonic_stages<R, 2>(k, lane);
+}
+
+// Write the n (<= 64*R) selected block ids of sel[] to out[] ascending.
+template <int R>
+__device__ __forceinline__ void emit_sorted(const int32_t *sel, int n, int32_t *__restrict__ out, int lane) {
+    uint32_t k[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = r * 64 + lane;
+        k[r] = (i < n) ? static_cast<uint32_t>(sel[i]) + 1u : 0u;     // ids + 1 sort ahead of the padding
+    }
+    wave_sort_desc<R>(k, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = lane * R + r;
+        if (i < n) out[n - 1 - i] = static_cast<int32_t>(k[r] - 1u);
+    }
+}
+
 }  // namespace qsa

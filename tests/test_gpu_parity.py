@@ -142,6 +142,33 @@ def test_index_select_fused_equals_score_matrix_path(budget):
     assert torch.equal(a, f)
 
 
+@pytest.mark.parametrize("kind", ["zero_blocks", "large_scores"])
+def test_index_select_fused_end_bins(kind):
+    """Boundaries in the two clamped end bins of the fused kernel's histogram:
+    half the pooled keys zero (many exact 0 scores, ties broken by block), or
+    keys scaled by 16 (budget-th score above the histogram's top edge)."""
+    B, L, budget = 1, 6000, 512
+    w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 43)
+    x = synth.prefill_inputs(w, "cpu")
+    if kind == "zero_blocks":
+        g = np.random.default_rng(44)
+        dead = np.nonzero(g.random(L // 4) < 0.5)[0]
+        tok = (dead[:, None] * 4 + np.arange(4)[None, :]).reshape(-1)
+        x["k_idx"][:, torch.from_numpy(tok)] = 0
+    else:
+        x["k_idx"] = x["k_idx"] * 16
+    xd = _to(x)
+    h = Q.Handle(max_ctx=6144, budget_blocks=budget)
+    a, f = _index_paths(h, x, xd, B, L)
+    assert torch.equal(a, f)
+    p = O.Params(budget=budget)
+    lay = oracle_layer(x, 0, p)
+    fb = f.cpu().numpy()
+    for i in [2051, 2400, 3000, 4095, 4099, 5999]:
+        _, sel, sc = lay.row(i, bits(x["q"][0, i]), bits(x["q_idx"][0, i]))
+        check_selection(fb[0, i], sel, sc, budget, i // 4, "row %d" % i)
+
+
 def test_index_select_overflow_fallback():
     """With a candidate list far shorter than needed every long row overflows and
     is recomputed exactly: the result still meets the oracle."""
