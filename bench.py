@@ -34,6 +34,27 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 
+# HBM-side bytes of one attend_prefill_kernel launch on the 262,144-token
+# workload, read by rocprofv3 --pmc (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB;
+# the factors are what the counters read for a plain 1 GiB copy).  The counter
+# summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
+# is reported only while the kernel's sources hash to the digests it was taken with.
+ATTEND_TRAFFIC_BYTES = (442737369.3 * 2.000 + 3145753.2 * 1.000) * 1024
+ATTEND_TRAFFIC_SOURCES = {
+    "k_attend.hip": "881a1afe68714d3570a006713f8b4efa341e3f69123ef3be938f9f2cf7c56de8",
+    "qsa_common.h": "174608b1e7eeed848fb54879a70fe06889ff333acfb43e741c5fe5247ffc1673",
+}
+
+
+def attend_traffic_bytes():
+    """Counter-measured bytes per launch, or None if the kernel changed since."""
+    import hashlib
+    for name, digest in ATTEND_TRAFFIC_SOURCES.items():
+        with open(os.path.join(ROOT, "block_sparse_long_qsa_amd", "csrc", name), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return ATTEND_TRAFFIC_BYTES
+
 
 def _events(n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
@@ -225,6 +246,7 @@ def main():
     L = wp.seq_len
     attn_bytes, sum_T = attention_bytes(L, wp.budget)
     attn_gbs = attn_bytes / (t_attn * 1e-3) / 1e9
+    tr_bytes = attend_traffic_bytes()
     idx_tfs = indexer_flops(L) / (t_isel * 1e-3) / 1e12
     res = {
         "metric": "QSA prefill tok/s @256K + decode tok/s @128K ctx; % of MFMA/HBM peak",
@@ -254,7 +276,9 @@ def main():
         "roofline": {
             "kernel": "attend_prefill_kernel (qsa_attend)",
             "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": attn_gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": attn_gbs / HBM_PEAK_GBS,
+            "traffic": None if tr_bytes is None else tr_bytes / (t_attn * 1e-3) / 1e9,
+            "traffic_bytes_per_launch": tr_bytes,
             "algorithmic_bytes": attn_bytes, "gathered_tokens": sum_T, "avg_ms": float(t_attn),
         },
     }
