@@ -178,7 +178,6 @@ hipError_t launch_indexer_scores(hipStream_t st, int32_t B, int64_t L, int64_t q
 // Workgroups are issued latest-queries-first (longest rows first).
 constexpr int kTopkBins = 128;
 constexpr int kTopkBinBase = 951;      // bin 1 = [2^-8, 2^-8 * 1.125); 952 = (127 - 8) * 8
-constexpr uint32_t kTauRefresh = 32;    // appends between threshold refreshes
 
 __device__ __forceinline__ int topk_bin(float s) {
     const int b = static_cast<int>(__float_as_uint(s) >> 20) - kTopkBinBase;
@@ -257,12 +256,14 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         }
     }
     // The wave scores queries 16*wave + j, j = 8a + 2i + p (p = lane half).
-    // Their kept counts, appends since the last threshold refresh and
-    // thresholds live in lane j of st_cnt / st_since / st_tau; tau_v is each
-    // lane's copy of its own query's threshold.  Padding queries of a ragged
-    // tile get an infinite threshold and keep nothing.
-    uint32_t st_cnt = 0, st_since = 0;
-    float st_tau = (lane < 16 && q0 + 16 * wave + lane < L) ? 0.0f : INFINITY;
+    // Lane j of st_cnt / st_bt / st_ca holds query j's kept count, its
+    // threshold bin bt (tau = lower edge of bin bt) and the number of kept
+    // scores in bins above bt; tau_v is each lane's copy of its own query's
+    // threshold.  Padding queries of a ragged tile get an infinite threshold
+    // and keep nothing.
+    uint32_t st_cnt = 0, st_ca = 0;
+    int st_bt = 0;
+    const bool st_live = lane < 16 && q0 + 16 * wave + lane < L;
     float tau_v[2][4];
     int32_t qo[2][4];
     for (int a = 0; a < 2; ++a)
@@ -336,23 +337,34 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                         const int j0 = 8 * a + 2 * i;                    // queries j0 (lanes 0..31), j0 + 1
                         const uint32_t m0 = static_cast<uint32_t>(m), m1 = static_cast<uint32_t>(m >> 32);
                         const uint32_t n0 = static_cast<uint32_t>(__popc(m0)), n1 = static_cast<uint32_t>(__popc(m1));
+                        const uint32_t c0 = __builtin_amdgcn_readlane(st_cnt, j0);
+                        const uint32_t c1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1);
+                        // kept scores above the threshold bin: bits >= lower edge of bin bt + 1
+                        // (none above the top bin, whose edge is 2^8)
+                        const uint32_t tb = __float_as_uint(tau_v[a][i]);
+                        const uint32_t tn = (tb == 0u) ? (static_cast<uint32_t>(kTopkBinBase + 1) << 20)
+                                            : (tb >= (static_cast<uint32_t>(kTopkBinBase + kTopkBins - 1) << 20)
+                                                   ? 0x7F800000u : tb + (1u << 20));
+                        const uint32_t sb = __float_as_uint(s) & 0x7FFFFFFFu;      // -0 -> +0
+                        const uint64_t am = __builtin_amdgcn_ballot_w64(keep && sb >= tn);
                         if (keep) {
                             // position = kept count of the lane's query + kept lanes below it in its half
-                            const uint32_t b0 = __builtin_amdgcn_readlane(st_cnt, j0);
-                            const uint32_t b1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1) - n0;
                             const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(m0, 0u));
-                            const uint32_t pos = (half ? b1 : b0) + below;
+                            const uint32_t pos = (half ? c1 - n0 : c0) + below;
                             const uint32_t ql = static_cast<uint32_t>(16 * wave + j0 + half);
-                            const float sc = __uint_as_float(__float_as_uint(s) & 0x7FFFFFFFu);   // -0 -> +0
                             if (pos < static_cast<uint32_t>(cap)) {
                                 const uint32_t off = ql * static_cast<uint32_t>(cap) + pos;
-                                wg_cand[off] = make_uint2(__float_as_uint(sc), static_cast<uint32_t>(col));
+                                wg_cand[off] = make_uint2(sb, static_cast<uint32_t>(col));
                             }
-                            atomicAdd(&hist[ql][topk_bin(sc)], 1u);
+                            atomicAdd(&hist[ql][topk_bin(__uint_as_float(sb))], 1u);
                         }
-                        const uint32_t add = (lane == j0) ? n0 : (lane == j0 + 1 ? n1 : 0u);
-                        st_cnt += add;
-                        st_since += add;
+                        const bool l0 = lane == j0, l1 = lane == j0 + 1;
+                        st_cnt += l0 ? n0 : (l1 ? n1 : 0u);
+                        if (am) {
+                            const uint32_t a0 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(am)));
+                            const uint32_t a1 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(am >> 32)));
+                            st_ca += l0 ? a0 : (l1 ? a1 : 0u);
+                        }
                     }
                 }
             }
@@ -361,35 +373,23 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             epilogue(std::integral_constant<bool, false>{});
         else
             epilogue(std::integral_constant<bool, true>{});
-        if (any) {
-            // refresh the thresholds of queries that kept enough new scores: the
-            // highest bin whose suffix count reaches the budget gives tau
-            uint64_t todo = __builtin_amdgcn_ballot_w64(lane < 16 && st_since >= kTauRefresh);
-            if (todo) {
-                while (todo) {
-                    const int j = __builtin_ctzll(todo);
-                    todo &= todo - 1;
-                    const int ql = 16 * wave + j;
-                    const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
-                    uint32_t incl = h0 + h1;                           // kept scores in bins >= 2*lane
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const uint32_t other = __shfl_down(incl, off);
-                        if (lane + off < 64) incl += other;
-                    }
-                    const uint32_t c1 = incl - h0;                     // bins >= 2*lane + 1
-                    const int cand = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
-                                     : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
-                    const uint64_t vm = __builtin_amdgcn_ballot_w64(cand >= 0);
-                    if (vm != 0) {
-                        const int hi = 63 - __clzll(vm);
-                        const float t = topk_bin_edge(__shfl(cand, hi));
-                        if (lane == j && t > st_tau) st_tau = t;
-                    }
-                    if (lane == j) st_since = 0;
+        if (any && __builtin_amdgcn_ballot_w64(st_ca >= static_cast<uint32_t>(budget))) {
+            // raise thresholds: while the kept scores above bin bt reach the
+            // budget, bin bt + 1's lower edge is a valid threshold
+            if (lane < 16) {
+                while (st_ca >= static_cast<uint32_t>(budget) && st_bt < kTopkBins - 1) {
+                    ++st_bt;
+                    st_ca -= hist[16 * wave + lane][st_bt];
                 }
-                for (int a = 0; a < 2; ++a)
-                    for (int i = 0; i < 4; ++i) tau_v[a][i] = __shfl(st_tau, 8 * a + 2 * i + half);
             }
+            const float st_tau = st_live ? topk_bin_edge(st_bt) : INFINITY;
+            for (int a = 0; a < 2; ++a)
+                for (int i = 0; i < 4; ++i) {
+                    const int j0 = 8 * a + 2 * i;
+                    const float ta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st_tau), j0));
+                    const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st_tau), j0 + 1));
+                    tau_v[a][i] = half ? tb : ta;
+                }
         }
         if (more) put(buf ^ 1);
         __syncthreads();
@@ -397,32 +397,9 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     }
     // ---- final selection of each query, by the wave that owns it.
     __syncthreads();
-    // Boundary bin of each of the wave's queries: the highest bin whose suffix
-    // count of kept scores reaches the budget; `above` kept scores lie in
-    // higher bins and are all selected.  Lane j keeps query 16*wave + j's.
-    int my_bstar = -1;
-    uint32_t my_above = 0;
-    for (int j = 0; j < 16; ++j) {
-        const int ql = 16 * wave + j;
-        const uint32_t h0 = hist[ql][2 * lane], h1 = hist[ql][2 * lane + 1];
-        uint32_t incl = h0 + h1;
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t other = __shfl_down(incl, off);
-            if (lane + off < 64) incl += other;
-        }
-        const uint32_t c1 = incl - h0;
-        const int candb = (c1 >= static_cast<uint32_t>(budget)) ? 2 * lane + 1
-                          : (incl >= static_cast<uint32_t>(budget) ? 2 * lane : -1);
-        const uint32_t ab = (candb == 2 * lane + 1) ? c1 - h1 : c1;
-        const uint64_t vm = __builtin_amdgcn_ballot_w64(candb >= 0);
-        const int hi = vm ? 63 - __clzll(vm) : 0;
-        const int bs = __shfl(candb, hi);
-        const uint32_t av = __shfl(ab, hi);
-        if (lane == j) {
-            my_bstar = vm ? bs : -1;
-            my_above = av;
-        }
-    }
+    // Boundary bin of each query: its final threshold bin bt (the highest bin
+    // whose suffix count of kept scores reaches the budget), with st_ca kept
+    // scores above it, all selected.
     wave_sync();
     // The k̄ tiles and this wave's histogram rows are now per-wave scratch:
     // boundary keys and the unordered selection in the first, the boundary
@@ -441,8 +418,8 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             continue;
         }
         const uint32_t c = __builtin_amdgcn_readlane(st_cnt, j);
-        const int bstar = __builtin_amdgcn_readlane(my_bstar, j);
-        const uint32_t above = __builtin_amdgcn_readlane(my_above, j);
+        const int bstar = __builtin_amdgcn_readlane(st_bt, j);
+        const uint32_t above = __builtin_amdgcn_readlane(st_ca, j);
         const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
         // Inside an interior bin the high score bits are fixed, so (low 20
         // score bits, boundary ordinal) packs (score desc, block desc) into one
