@@ -138,6 +138,39 @@ def decode_bytes(B, ctx, budget):
     return B * per
 
 
+def measured_ceilings():
+    """Rates this GPU reaches with plain library operations, beside the
+    datasheet peaks: a 4 GiB device-to-device copy (bytes read + written per
+    second) and a 8192^3 bf16 GEMM (torch.matmul)."""
+    src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * src.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = a @ b
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tfs = 20 * 2 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_GBs": copy_gbs, "gemm_bf16_TFs": gemm_tfs,
+            "how": "4 GiB device copy (read + write bytes) and 8192^3 bf16 torch.matmul"}
+
+
 def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
     """Time the oracle on an evenly spaced sample of the prefill's rows."""
     import oracle as O
@@ -188,6 +221,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="decode step only (profiling)")
     ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-ceilings", action="store_true", help="skip the measured copy / GEMM ceilings")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -288,6 +322,13 @@ def main():
         res["decode"] = {"ms": t_dec, "tok_s": wd.batch / (t_dec * 1e-3),
                          "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                       "frac": dgbs / HBM_PEAK_GBS, "algorithmic_bytes": db}}
+    if not args.no_ceilings:
+        ceil = measured_ceilings()
+        res["measured_ceilings"] = ceil
+        res["roofline"]["frac_of_measured_copy"] = attn_gbs / ceil["copy_GBs"]
+        res["prefill"]["index_select_frac_of_measured_gemm"] = idx_tfs / ceil["gemm_bf16_TFs"]
+        if sd:
+            res["decode"]["roofline"]["frac_of_measured_copy"] = res["decode"]["roofline"]["achieved"] / ceil["copy_GBs"]
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         res["cpu_baseline"] = cpu_baseline(sp, wp, n_rows=args.cpu_rows)

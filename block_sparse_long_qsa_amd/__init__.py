@@ -25,7 +25,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPP
 # The C entry points (kept in step with include/qsa.h).
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
            "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
-           "qsa_status_string", "qsa_last_hip_error"]
+           "qsa_decode_reuse", "qsa_status_string", "qsa_last_hip_error"]
 
 
 class QSAError(RuntimeError):
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_forward.restype = ctypes.c_int
     L.qsa_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 12 + [sz]
     L.qsa_decode.restype = ctypes.c_int
+    L.qsa_decode_reuse.argtypes = [vp, vp, i32, vp, vp, i64] + [vp] * 11 + [sz]
+    L.qsa_decode_reuse.restype = ctypes.c_int
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     L.qsa_last_hip_error.argtypes = []
@@ -235,6 +237,16 @@ def qsa_decode(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cac
                             _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
                             _bf(kpend, "kpend"), _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"),
                             _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_decode")
+
+
+def qsa_decode_reuse(h, B, cache_len, sel_pos, ctx_bound, q, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend,
+                     block_idx, out, ws, stream=None):
+    _check(lib().qsa_decode_reuse(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"),
+                                  _ptr(sel_pos, torch.int32, "sel_pos"), ctx_bound, _bf(q, "q"), _bf(k, "k"),
+                                  _bf(v, "v"), _bf(k_idx, "k_idx"), _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"),
+                                  _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"),
+                                  _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out"), _ptr(ws, None, "ws"),
+                                  _nbytes(ws)), "qsa_decode_reuse")
 
 
 def qsa_status_string(status: int) -> str:

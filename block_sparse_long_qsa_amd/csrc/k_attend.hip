@@ -71,28 +71,38 @@ __device__ __forceinline__ void load_q_frags(const bf16_t *qrow /*[24][256] of t
 }
 
 // Block id and valid-token mask (bit t = token t valid) of list entry li.
-__device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o, int li, int own_last,
-                                           int64_t &blk, uint32_t &tmask)
+// The list is the n_sel selected blocks (only ids in [0, o0) count), then the
+// tail blocks o0 .. o, whole except the query's own block o, whose tokens run
+// to own_last.  A selection made at the query itself has o0 = o (the tail is
+// the own block alone); one reused from an earlier position has o0 = its own
+// block there.
+__device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o0, int64_t o, int li,
+                                           int own_last, int64_t &blk, uint32_t &tmask)
 {
     if (li < n_sel) {
         const int64_t id = sel[li];
-        const bool ok = id >= 0 && id < o;
+        const bool ok = id >= 0 && id < o0;
         blk = ok ? id : 0;
         tmask = ok ? 0xFu : 0u;
-    } else if (li == n_sel) {
-        blk = o;
-        tmask = (1u << (own_last + 1)) - 1u;
+    } else if (li - n_sel <= o - o0) {
+        blk = o0 + (li - n_sel);
+        tmask = (blk == o) ? (1u << (own_last + 1)) - 1u : 0xFu;
     } else {
         blk = 0;
         tmask = 0u;
     }
 }
 
+// Chunks of a token list of n_sel selected blocks and tail blocks o0 .. o.
+__device__ __forceinline__ int list_chunks(int n_sel, int64_t o0, int64_t o) {
+    return static_cast<int>((n_sel + (o - o0) + 1 + kChunkBlocks - 1) / kChunkBlocks);
+}
+
 // Walk chunks [c_lo, c_hi) of one (query, group) token list.
 __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
                                               const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
-                                              int n_sel, int64_t o, int own_last, int c_lo, int c_hi, float c2,
-                                              RowState &st)
+                                              int n_sel, int64_t o0, int64_t o, int own_last, int c_lo, int c_hi,
+                                              float c2, RowState &st)
 {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;           // K-load token row / V-load dim
@@ -102,7 +112,7 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         // ---- gather K~ (A operand of S^T): tile t, token row r -> list entry lb + 4t + r/4
         int64_t kblk[2];
         uint32_t kmask[2];
-        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
         bf16x8 kf[2][8];
         for (int t = 0; t < 2; ++t) {
             const bf16_t *src = kc + kblk[t] * kBlockElems + (r & 3) * 32 + 8 * g;
@@ -111,7 +121,7 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         // ---- gather V (A operand of O^T): list entries lb + g and lb + 4 + g, dim 16n + r
         int64_t vblk[2];
         uint32_t vmask[2];
-        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o0, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
         u32x2 vraw[16][2];
         for (int t = 0; t < 2; ++t) {
             const bf16_t *src = vc + vblk[t] * kBlockElems + r * kBlock;
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     const int64_t o = pos / kBlock;
     const int own_last = static_cast<int>(pos - o * kBlock);
     const int n_sel = static_cast<int>(o < budget ? o : budget);
-    const int nchunks = (n_sel + 1 + kChunkBlocks - 1) / kChunkBlocks;
+    const int nchunks = list_chunks(n_sel, o, o);
 
     bf16x8 qf[8];
     load_q_frags(q + (b * L + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
@@ -198,7 +208,7 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 
     RowState st;
     init_state(st);
-    attend_chunks(qf, kc, vc, sel, n_sel, o, own_last, 0, nchunks, c2, st);
+    attend_chunks(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
 
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
@@ -215,10 +225,13 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 }
 
 // Decode, split over the token list: one wave per (split, group, sequence)
-// writes its unnormalised partial (m, l, O) for the 12 heads.
+// writes its unnormalised partial (m, l, O) for the 12 heads.  With sel_pos
+// (a reused selection) the list is block_idx as selected at position
+// p0 = sel_pos[b] (clamped to [0, p]) followed by every block from p0's own
+// block up to the query's.
 __global__ __launch_bounds__(64) void attend_decode_split_kernel(
-    Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t nblk_cap, int budget, int nsplit,
-    float c2,
+    Tables tab, const int32_t *__restrict__ cache_len, const int32_t *__restrict__ sel_pos, int64_t ctx_bound,
+    int64_t nblk_cap, int budget, int nsplit, float c2,
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
     const int32_t *__restrict__ block_idx, float *__restrict__ part_o, float *__restrict__ part_ml)
 {
@@ -229,8 +242,9 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
     const int64_t pos = decode_pos(cache_len, b, ctx_bound);
     const int64_t o = pos / kBlock;
     const int own_last = static_cast<int>(pos - o * kBlock);
-    const int n_sel = static_cast<int>(o < budget ? o : budget);
-    const int nchunks = (n_sel + 1 + kChunkBlocks - 1) / kChunkBlocks;
+    const int64_t o0 = sel_pos ? decode_pos(sel_pos, b, pos) / kBlock : o;
+    const int n_sel = static_cast<int>(o0 < budget ? o0 : budget);
+    const int nchunks = list_chunks(n_sel, o0, o);
     const int per = (nchunks + nsplit - 1) / nsplit;
     const int c_lo = split * per;
     const int c_hi = (c_lo + per < nchunks) ? c_lo + per : nchunks;
@@ -242,7 +256,7 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
         load_q_frags(q + b * kQHeads * kHeadDim, grp, pos, tab, qf);
         const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
         const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-        attend_chunks(qf, kc, vc, block_idx + b * budget, n_sel, o, own_last, c_lo, c_hi, c2, st);
+        attend_chunks(qf, kc, vc, block_idx + b * budget, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
     }
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
@@ -296,14 +310,15 @@ hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, i
 }
 
 hipError_t launch_attend_decode(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
-                                int64_t ctx_bound, int64_t nblk_cap, int budget, int nsplit, float sigma, const bf16_t *q,
-                                const bf16_t *k_cache, const bf16_t *v_cache, const int32_t *block_idx,
+                                const int32_t *sel_pos, int64_t ctx_bound, int64_t nblk_cap, int budget, int nsplit,
+                                float sigma, const bf16_t *q, const bf16_t *k_cache, const bf16_t *v_cache,
+                                const int32_t *block_idx,
                                 float *part_o, float *part_ml, bf16_t *out)
 {
     if (B <= 0) return hipSuccess;
     const float c2 = sigma * kLog2e;
     hipLaunchKernelGGL(attend_decode_split_kernel, dim3(nsplit, kKVHeads, B), dim3(64), 0, st, tab, cache_len,
-                       ctx_bound, nblk_cap, budget, nsplit, c2, q, k_cache, v_cache, block_idx, part_o, part_ml);
+                       sel_pos, ctx_bound, nblk_cap, budget, nsplit, c2, q, k_cache, v_cache, block_idx, part_o, part_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attend_decode_merge_kernel, dim3(kQHeads, B), dim3(256), 0, st, nsplit, c2, part_o, part_ml,

@@ -14,7 +14,8 @@ constexpr int kDecodeBins = 2048;      // histogram of score bits 30..20 per seq
 //          and copy v into V slot p%4;
 //   lanes 0..15: raw k_idx into kpend[p%4]; when p%4 == 3 pool the completed
 //          block (kpend slots 0..2 + this token) into kbar;
-//   lanes: head lane/16, chunk lane%16 -> rotated q_idx at p into qrot.
+//   lanes: head lane/16, chunk lane%16 -> rotated q_idx at p into qrot (when
+//          q_idx is given).
 __global__ __launch_bounds__(64) void decode_append_kernel(
     Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t nblk_cap,
     const bf16_t *__restrict__ k, const bf16_t *__restrict__ v, const bf16_t *__restrict__ k_idx,
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(64) void decode_append_kernel(
                       pack_bf16x2(r[6], r[7])};
         }
     }
-    {   // rotated indexer query
+    if (q_idx) {   // rotated indexer query (not needed when a selection is reused)
         const int h = lane >> 4, c = lane & 15;
         const bf16_t *src = q_idx + (b * kIdxHeads + h) * kIdxDim;
         u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);

@@ -31,7 +31,8 @@ hipError_t launch_select_fixup(hipStream_t, int32_t, int64_t, int64_t, int, cons
                                const bf16_t *, int64_t, const bf16_t *, int64_t);
 hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
                                  const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
-hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int, int, float,
+hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, const int32_t *, int64_t, int64_t,
+                                int, int, float,
                                 const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
                                 bf16_t *);
 hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const bf16_t *,
@@ -415,8 +416,37 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
         e = launch_decode_scan(st, B, cache_len, ctx_bound, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
     if (e == hipSuccess) e = launch_select_hist(st, B, cache_len, ctx_bound, d.ncol, scores, dhist, bidx, budget);
     if (e == hipSuccess)
-        e = launch_attend_decode(tables(h), st, B, cache_len, ctx_bound, nbc, budget, d.nsplit, h->sigma, q, k_cache, v_cache,
-                                 bidx, part_o, part_ml, out);
+        e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, budget, d.nsplit, h->sigma, q,
+                                 k_cache, v_cache, bidx, part_o, part_ml, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                            const int32_t *sel_pos, int64_t ctx_bound, const uint16_t *q, const uint16_t *k,
+                            const uint16_t *v, const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache,
+                            uint16_t *kbar_cache, uint16_t *kpend, const int32_t *block_idx, uint16_t *out, void *ws,
+                            size_t ws_bytes) {
+    if (!h) return QSA_ERR_NULL;
+    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
+    qsa_status s = check_ptrs({cache_len, sel_pos, q, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend, block_idx, out,
+                               ws});
+    if (s != QSA_OK) return s;
+    const DecLayout d = decode_layout(h, B, ctx_bound);
+    if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    float *part_o = reinterpret_cast<float *>(w + d.part_o);
+    float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
+    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
+    const int64_t nbc = nblk_cap(h);
+    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, nullptr, k_cache,
+                                        v_cache, kbar_cache, kpend, nullptr, dhist);
+    if (e == hipSuccess)
+        e = launch_attend_decode(tables(h), st, B, cache_len, sel_pos, ctx_bound, nbc, h->p.budget_blocks, d.nsplit,
+                                 h->sigma, q, k_cache, v_cache, block_idx, part_o, part_ml, out);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

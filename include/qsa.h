@@ -226,6 +226,23 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
                       uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
                       uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes);
 
+/* Decode one new token per sequence reusing a block selection made at an
+ * earlier position instead of scoring and selecting again ([PKR] section on the
+ * MTP module for speculative decoding: the top-k block indices are reused
+ * between speculative steps).  Sequence b's new token sits at p = cache_len[b]
+ * (appended as in qsa_decode, including its indexer key); block_idx [B][budget]
+ * is the selection qsa_decode returned for position p0 = sel_pos[b] (DEVICE
+ * int32 [B], clamped to [0, p]).  The token attends over the selected blocks
+ * below p0's own block plus every token from the start of p0's own block up to
+ * p; with p0 = p this is exactly qsa_decode's attention.  No indexer query is
+ * read.  ctx_bound as for qsa_decode.
+ * ws: qsa_workspace_size(QSA_OP_DECODE, B, 1, ctx_bound) bytes. */
+qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                            const int32_t *sel_pos, int64_t ctx_bound,
+                            const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *k_idx,
+                            uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
+                            const int32_t *block_idx, uint16_t *out, void *ws, size_t ws_bytes);
+
 /* Static string for a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -257,6 +257,21 @@ def token_set(sel: np.ndarray, pos: int, p: Params) -> np.ndarray:
     return np.concatenate([blk, own])
 
 
+def token_set_reused(sel: np.ndarray, sel_pos: int, pos: int, p: Params) -> np.ndarray:
+    """Tokens attended by query `pos` that reuses the selection made for an
+    earlier query at `sel_pos` <= pos ([PKR] section on the MTP module: top-k
+    indices reused across speculative decoding steps).  Reading: the reused
+    blocks (those before sel_pos's own block) keep their meaning, and the query
+    attends every token from the start of sel_pos's own block up to itself --
+    the own-block rule widened to cover the blocks completed since the
+    selection.  With sel_pos = pos this is token_set."""
+    o0 = own_block(sel_pos, p)
+    sel = sel[(sel >= 0) & (sel < o0)].astype(np.int64)
+    blk = (sel[:, None] * p.block + np.arange(p.block)[None, :]).reshape(-1)
+    tail = np.arange(o0 * p.block, pos + 1, dtype=np.int64)
+    return np.concatenate([blk, tail])
+
+
 def attend(qt: np.ndarray, kt: np.ndarray, v: np.ndarray, sigma: float, p: Params) -> np.ndarray:
     """Softmax attention of each query head over the given tokens, fp64.
 
@@ -308,6 +323,16 @@ class LayerOracle:
         qt = core_rotate(q_bits[None], np.array([pos]), p)[0]
         out = attend(qt, kt, self.v[toks], self.sigma, p)
         return out, sel, scores
+
+    def row_reused(self, pos: int, q_bits: np.ndarray, sel: np.ndarray, sel_pos: int):
+        """Output fp64 [24][256] of query `pos` attending with the selection
+        `sel` that was made for position sel_pos (token_set_reused)."""
+        p = self.p
+        assert 0 <= sel_pos <= pos < self.n_keys
+        toks = token_set_reused(np.asarray(sel), sel_pos, pos, p)
+        kt = core_rotate(self.k_bits[toks], toks, p)
+        qt = core_rotate(q_bits[None], np.array([pos]), p)[0]
+        return attend(qt, kt, self.v[toks], self.sigma, p)
 
 
 def prefill_rows(q_bits, k_bits, v_bits, q_idx_bits, k_idx_bits, rows, p: Params, q_offset: int = 0):

@@ -23,6 +23,24 @@ def test_header_declares_the_binding_names():
     assert _declared() == sorted(Q.EXPORTS)
 
 
+def _param_counts():
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for name, params in re.findall(r"\b(qsa_[a-z_]+)\s*\(([^;{]*?)\)\s*;", src):
+        params = params.strip()
+        out[name] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_argument_counts_match_header():
+    lib = Q.lib()
+    counts = _param_counts()
+    assert counts, "no declarations parsed"
+    for name, n in counts.items():
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None and len(argtypes) == n, (name, n, argtypes)
+
+
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     for name in _declared():
@@ -56,6 +74,7 @@ def test_null_handle_and_status_strings():
     assert lib.qsa_index_select(None, None, 1, 4, 0, None, None, None, None, 0) == 1
     assert lib.qsa_attend(None, None, 1, 4, 0, None, None, None, None, None) == 1
     assert lib.qsa_decode(None, None, 1, None, 0, *([None] * 12), 0) == 1
+    assert lib.qsa_decode_reuse(None, None, 1, None, None, 0, *([None] * 11), 0) == 1
     for s in range(8):
         assert Q.qsa_status_string(s)
     assert Q.qsa_last_hip_error() == 0

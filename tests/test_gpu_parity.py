@@ -376,3 +376,62 @@ def test_decode_matches_prefill_row():
         check_selection(bi.cpu().numpy(), sel, sc, budget, n // 4, name)
         check_out(f32(o), ref, name)
     check_out(f32(out_d[0, 0]), f32(out_p[0, n]).astype(np.float64), "decode vs prefill")
+
+
+def test_decode_reuse_speculative_steps():
+    """A full decode step at p0, then draft steps p0+1 .. p0+4 (crossing a block
+    boundary) that reuse its selection: reuse at p0 itself reproduces the full
+    step bit for bit, and every draft step meets the oracle's reused-selection
+    row; the appended tokens keep the caches exact."""
+    budget, p0s = 48, [1202, 999]
+    B, L = len(p0s), max(p0s) + 6
+    w = synth.Workload("t", "prefill", B, L, budget, 6, "random", 30)
+    x = synth.prefill_inputs(w, "cpu")
+    xd = _to(x)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    c = Q.alloc_caches(h, B)
+    for b, n in enumerate(p0s):
+        sl = lambda t: t[b:b + 1, :n].contiguous()
+        cs = {k: v[b:b + 1] for k, v in c.items()}
+        Q.qsa_append(h, 1, n, 0, sl(xd["k"]), sl(xd["v"]), sl(xd["k_idx"]), cs["k_cache"], cs["v_cache"],
+                     cs["kbar_cache"], cs["kpend"])
+
+    def tok(name, pos):
+        return torch.stack([xd[name][b, pos[b]] for b in range(B)])[:, None].contiguous()
+
+    bound = max(p0s) + 4
+    ws = Q.workspace(h, Q.QSA_OP_DECODE, B, 1, bound)
+    sel_pos = torch.tensor(p0s, dtype=torch.int32, device=DEV)
+    out0 = torch.empty((B, 1, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bidx0 = torch.empty((B, 1, budget), dtype=torch.int32, device=DEV)
+    Q.qsa_decode(h, B, sel_pos, bound, tok("q", p0s), tok("k", p0s), tok("v", p0s), tok("q_idx", p0s),
+                 tok("k_idx", p0s), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], out0, bidx0, ws)
+    sel_gpu = bidx0.view(B, budget).contiguous()
+    out_r = torch.empty_like(out0)
+    Q.qsa_decode_reuse(h, B, sel_pos, sel_pos, bound, tok("q", p0s), tok("k", p0s), tok("v", p0s),
+                       tok("k_idx", p0s), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel_gpu, out_r, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out_r, out0)
+    p = O.Params(budget=budget)
+    lays = [oracle_layer(x, b, p) for b in range(B)]
+    sels = []
+    for b, n in enumerate(p0s):
+        _, sel, sc = lays[b].row(n, bits(x["q"][b, n]), bits(x["q_idx"][b, n]))
+        got = sel_gpu[b].cpu().numpy()
+        assert sorted(got[got >= 0].tolist()) == sorted(sel[sel >= 0].tolist()), "seq %d selection" % b
+        sels.append(sel)
+    for i in range(1, 5):
+        pos = [n + i for n in p0s]
+        cache_len = torch.tensor(pos, dtype=torch.int32, device=DEV)
+        out = torch.empty_like(out0)
+        Q.qsa_decode_reuse(h, B, cache_len, sel_pos, bound, tok("q", pos), tok("k", pos), tok("v", pos),
+                           tok("k_idx", pos), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel_gpu, out,
+                           ws)
+        torch.cuda.synchronize()
+        o = f32(out)
+        for b in range(B):
+            ref = lays[b].row_reused(pos[b], bits(x["q"][b, pos[b]]), sels[b], p0s[b])
+            check_out(o[b, 0], ref, "seq %d step %d" % (b, i))
+            if pos[b] % 4 == 3:
+                ref_kbar = O.f32_to_bf16_bits(O.indexer_keys(bits(x["k_idx"][b, :pos[b] + 1]), p))
+                assert np.array_equal(bits(c["kbar_cache"][b, pos[b] // 4]), ref_kbar[pos[b] // 4])

@@ -242,6 +242,20 @@ def test_token_set_own_block_tail():
     assert O.token_set(np.array([1, 3]), 17, p).tolist() == [4, 5, 6, 7, 12, 13, 14, 15, 16, 17]
 
 
+def test_token_set_reused_widens_the_own_block_tail():
+    p = O.Params()
+    sel = np.array([1, 3, 5, -1])
+    # reuse at the selecting position itself is the plain rule (candidates of
+    # position 21..23 are blocks 0..4)
+    for pos in (21, 22, 23):
+        assert O.token_set_reused(sel, pos, pos, p).tolist() == O.token_set(sel[sel < 5], pos, p).tolist()
+    # selection made at 21 (own block 5): block 5 is no longer a selected block
+    # but part of the tail, which now runs from token 20 to the query
+    assert O.token_set_reused(sel, 21, 26, p).tolist() == [4, 5, 6, 7, 12, 13, 14, 15] + list(range(20, 27))
+    # blocks at or after the selecting position's own block are never read from the list
+    assert O.token_set_reused(np.array([6, 7]), 21, 30, p).tolist() == list(range(20, 31))
+
+
 # ---------------------------------------------------------------- attention
 def _small(L, budget, seed=0, needles=0):
     w = synth.Workload("t", "prefill", 1, L, budget, needles, "random", seed)
@@ -275,6 +289,36 @@ def test_dense_equivalence_when_budget_covers_everything():
                                  _bits(x["q_idx"][0]), _bits(x["k_idx"][0]), rows, p)
     ref = _sdpa_rows(x, p, lambda n: np.tril(np.ones((n, n), dtype=bool)))
     np.testing.assert_allclose(out, ref, atol=1e-12, rtol=1e-10)
+
+
+def test_reused_selection_dense_and_masked_equivalence():
+    """A query reusing an earlier query's selection equals SDPA over exactly
+    the reused blocks and the widened tail; with a budget covering every block
+    before the selecting position it is dense causal attention."""
+    L = 120
+    w, x = _small(L, budget=40, seed=8)
+    for budget in (40, 3):
+        p = O.Params(budget=budget)
+        lay = O.LayerOracle(_bits(x["k"][0]), _bits(x["v"][0]), _bits(x["k_idx"][0]), p)
+        pairs = [(101, 101), (101, 103), (101, 107), (99, 116), (3, 9)]
+        sels = {sp: lay.row(sp, _bits(x["q"][0, sp]), _bits(x["q_idx"][0, sp]))[1] for sp, _ in pairs}
+
+        def mask_fn(n):
+            m = np.zeros((n, n), dtype=bool)
+            for sp, pos in pairs:
+                for b in sels[sp]:
+                    if 0 <= b < sp // 4:
+                        m[pos, 4 * b:4 * b + 4] = True
+                m[pos, 4 * (sp // 4):pos + 1] = True
+            return m
+
+        ref = _sdpa_rows(x, p, mask_fn)
+        for sp, pos in pairs:
+            out = lay.row_reused(pos, _bits(x["q"][0, pos]), sels[sp], sp)
+            np.testing.assert_allclose(out, ref[pos], atol=1e-12, rtol=1e-10)
+            if budget >= sp // 4:
+                dense = _sdpa_rows(x, p, lambda n: np.tril(np.ones((n, n), dtype=bool)))
+                np.testing.assert_allclose(out, dense[pos], atol=1e-12, rtol=1e-10)
 
 
 def test_masked_equivalence_small_budget():
