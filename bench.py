@@ -39,9 +39,9 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # the factors are what the counters read for a plain 1 GiB copy).  The counter
 # summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
 # is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (442737369.3 * 2.000 + 3145753.2 * 1.000) * 1024
+ATTEND_TRAFFIC_BYTES = (444488476.4 * 2.000 + 3145762.5 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "881a1afe68714d3570a006713f8b4efa341e3f69123ef3be938f9f2cf7c56de8",
+    "k_attend.hip": "428d63382b9514cc275c24cde801cf01b6cf7f11e6d3cb54ae5b85ac071c561a",
     "qsa_common.h": "174608b1e7eeed848fb54879a70fe06889ff333acfb43e741c5fe5247ffc1673",
 }
 
