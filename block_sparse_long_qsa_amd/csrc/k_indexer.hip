@@ -322,49 +322,67 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         auto epilogue = [&](auto masked) {
             for (int a = 0; a < 2; ++a) {
                 for (int i = 0; i < 4; ++i) {
+                    // lanes 0..31 score query j0, lanes 32..63 query j0 + 1, at
+                    // columns cs + 32*ct + lane%32 of the two column tiles
+                    const int j0 = 8 * a + 2 * i;
+                    uint32_t sb[2];
+                    bool keep[2];
+                    uint64_t m[2];
                     for (int ct = 0; ct < 2; ++ct) {
                         const int32_t col = static_cast<int32_t>(cs) + 32 * ct + (lane & 31);
                         const f32x16 &c = acc[a][ct];
                         const float s = relu_sum4_fast(c[4 * i], c[4 * i + 1], c[4 * i + 2], c[4 * i + 3]);
-                        bool keep;
                         if constexpr (decltype(masked)::value)
-                            keep = s >= tau_v[a][i] && col < qo[a][i];
+                            keep[ct] = s >= tau_v[a][i] && col < qo[a][i];
                         else
-                            keep = s >= tau_v[a][i];
-                        const uint64_t m = __builtin_amdgcn_ballot_w64(keep);
-                        if (m == 0) continue;                            // wave-uniform
-                        any = true;
-                        const int j0 = 8 * a + 2 * i;                    // queries j0 (lanes 0..31), j0 + 1
-                        const uint32_t m0 = static_cast<uint32_t>(m), m1 = static_cast<uint32_t>(m >> 32);
-                        const uint32_t n0 = static_cast<uint32_t>(__popc(m0)), n1 = static_cast<uint32_t>(__popc(m1));
-                        const uint32_t c0 = __builtin_amdgcn_readlane(st_cnt, j0);
-                        const uint32_t c1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1);
-                        // kept scores above the threshold bin: bits >= lower edge of bin bt + 1
-                        // (none above the top bin, whose edge is 2^8)
-                        const uint32_t tb = __float_as_uint(tau_v[a][i]);
-                        const uint32_t tn = (tb == 0u) ? (static_cast<uint32_t>(kTopkBinBase + 1) << 20)
-                                            : (tb >= (static_cast<uint32_t>(kTopkBinBase + kTopkBins - 1) << 20)
-                                                   ? 0x7F800000u : tb + (1u << 20));
-                        const uint32_t sb = __float_as_uint(s) & 0x7FFFFFFFu;      // -0 -> +0
-                        const uint64_t am = __builtin_amdgcn_ballot_w64(keep && sb >= tn);
-                        if (keep) {
-                            // position = kept count of the lane's query + kept lanes below it in its half
-                            const uint32_t below = __builtin_amdgcn_mbcnt_hi(m1, __builtin_amdgcn_mbcnt_lo(m0, 0u));
-                            const uint32_t pos = (half ? c1 - n0 : c0) + below;
-                            const uint32_t ql = static_cast<uint32_t>(16 * wave + j0 + half);
+                            keep[ct] = s >= tau_v[a][i];
+                        sb[ct] = __float_as_uint(s) & 0x7FFFFFFFu;           // -0 -> +0
+                        m[ct] = __builtin_amdgcn_ballot_w64(keep[ct]);
+                    }
+                    if ((m[0] | m[1]) == 0) continue;                        // wave-uniform
+                    any = true;
+                    const uint32_t c0 = __builtin_amdgcn_readlane(st_cnt, j0);
+                    const uint32_t c1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1);
+                    // kept scores above the threshold bin: bits >= lower edge of bin bt + 1
+                    // (none above the top bin, whose edge is 2^8)
+                    const uint32_t tb = __float_as_uint(tau_v[a][i]);
+                    const uint32_t tn = (tb == 0u) ? (static_cast<uint32_t>(kTopkBinBase + 1) << 20)
+                                        : (tb >= (static_cast<uint32_t>(kTopkBinBase + kTopkBins - 1) << 20)
+                                               ? 0x7F800000u : tb + (1u << 20));
+                    const uint32_t nl0 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[0])));
+                    const uint32_t nh0 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[0] >> 32)));
+                    const uint32_t nl1 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[1])));
+                    const uint32_t nh1 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[1] >> 32)));
+                    const uint32_t ql = static_cast<uint32_t>(16 * wave + j0 + half);
+                    // list positions: the query's kept count, then its column tile 0
+                    // entries, then tile 1 (block order); mbcnt counts the whole wave,
+                    // so upper-half lanes drop the lower half's count
+                    const uint32_t base0 = half ? c1 - nl0 : c0;
+                    const uint32_t base1 = half ? c1 + nh0 - nl1 : c0 + nl0;
+                    uint64_t am = 0, am1 = 0;
+                    for (int ct = 0; ct < 2; ++ct) {
+                        const uint64_t a_m = __builtin_amdgcn_ballot_w64(keep[ct] && sb[ct] >= tn);
+                        if (ct == 0) am = a_m; else am1 = a_m;
+                        if (keep[ct]) {
+                            const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m[ct] >> 32),
+                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m[ct]), 0u));
+                            const uint32_t pos = (ct == 0 ? base0 : base1) + below;
                             if (pos < static_cast<uint32_t>(cap)) {
                                 const uint32_t off = ql * static_cast<uint32_t>(cap) + pos;
-                                wg_cand[off] = make_uint2(sb, static_cast<uint32_t>(col));
+                                const uint32_t col = static_cast<uint32_t>(cs) + 32 * ct + (lane & 31);
+                                wg_cand[off] = make_uint2(sb[ct], col);
                             }
-                            atomicAdd(&hist[ql][topk_bin(__uint_as_float(sb))], 1u);
+                            atomicAdd(&hist[ql][topk_bin(__uint_as_float(sb[ct]))], 1u);
                         }
-                        const bool l0 = lane == j0, l1 = lane == j0 + 1;
-                        st_cnt += l0 ? n0 : (l1 ? n1 : 0u);
-                        if (am) {
-                            const uint32_t a0 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(am)));
-                            const uint32_t a1 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(am >> 32)));
-                            st_ca += l0 ? a0 : (l1 ? a1 : 0u);
-                        }
+                    }
+                    const bool l0 = lane == j0, l1 = lane == j0 + 1;
+                    st_cnt += l0 ? nl0 + nl1 : (l1 ? nh0 + nh1 : 0u);
+                    if (am | am1) {
+                        const uint32_t al = static_cast<uint32_t>(__popc(static_cast<uint32_t>(am)) +
+                                                                  __popc(static_cast<uint32_t>(am1)));
+                        const uint32_t ah = static_cast<uint32_t>(__popc(static_cast<uint32_t>(am >> 32)) +
+                                                                  __popc(static_cast<uint32_t>(am1 >> 32)));
+                        st_ca += l0 ? al : (l1 ? ah : 0u);
                     }
                 }
             }
