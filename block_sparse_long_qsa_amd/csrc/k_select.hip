@@ -348,15 +348,16 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
 #pragma unroll
         for (int u = 0; u < RC; ++u) {
             const int64_t j = jb + 64 * u + lane;
-            v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: digit 4095, never taken
+            v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: -1 as int32, below every threshold
         }
     };
     const int64_t chunk = 64 * RC;
     const bool one_chunk = r1 - r0 <= chunk;
+    // boundary digit from the histogram: 2 digits per thread, suffix sums (the
+    // histogram is loaded first so the scan overlaps the row's loads)
+    const uint32_t h0 = dhist[b * kSelMaxBins + 2 * tid], h1 = dhist[b * kSelMaxBins + 2 * tid + 1];
     if (one_chunk) load_chunk(r0);
-    // boundary digit from the histogram: 2 digits per thread, suffix sums
     {
-        const uint32_t h0 = dhist[b * kSelMaxBins + 2 * tid], h1 = dhist[b * kSelMaxBins + 2 * tid + 1];
         hist[2 * tid] = h0;
         hist[2 * tid + 1] = h1;
         uint32_t tot;
@@ -376,20 +377,23 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
         radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
         return;
     }
+    // Digit d* as signed bounds on the score bits (scores are >= +0, so their
+    // bits order like the values): above d* <=> bits >= T1, at or above <=> bits >= T0.
+    const int32_t T0 = static_cast<int32_t>(dstar << 20);
+    const int32_t T1 = dstar >= 2047u ? INT32_MAX : static_cast<int32_t>((dstar + 1) << 20);
     // counting pass, then the wave's offsets among all waves
-    uint32_t ng = 0, ne = 0;
+    uint32_t ng = 0, nge = 0;
     for (int64_t jb = r0; jb < r1; jb += chunk) {
         if (!one_chunk) load_chunk(jb);
 #pragma unroll
         for (int u = 0; u < RC; ++u) {
-            const uint32_t d = v[u] >> 20;
-            ng += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(d > dstar && d < 4095u)));
-            ne += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(d == dstar)));
+            ng += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u]) >= T1)));
+            nge += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u]) >= T0)));
         }
     }
     if (lane == 0) {
         wcnt[0][wave] = ng;
-        wcnt[1][wave] = ne;
+        wcnt[1][wave] = nge - ng;
     }
     __syncthreads();
     uint32_t gpos = 0, epos = 0;
@@ -402,17 +406,17 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
         if (!one_chunk) load_chunk(jb);
 #pragma unroll
         for (int u = 0; u < RC; ++u) {
-            const uint32_t d = v[u] >> 20;
-            const bool g = d > dstar && d < 4095u;
-            const bool e = d == dstar;
+            const bool ge = static_cast<int32_t>(v[u]) >= T0;
+            const uint64_t gem = __builtin_amdgcn_ballot_w64(ge);
+            if (gem == 0) continue;                                  // wave-uniform
+            const bool g = static_cast<int32_t>(v[u]) >= T1;
             const uint64_t gm = __builtin_amdgcn_ballot_w64(g);
-            const uint64_t em = __builtin_amdgcn_ballot_w64(e);
+            const uint64_t em = gem & ~gm;
             const int32_t blk = static_cast<int32_t>(jb + 64 * u + lane);
             if (g) {
                 const uint32_t t = gpos + lanes_below(gm);
                 if (t < static_cast<uint32_t>(kMaxBudget)) sel[t] = blk;
-            }
-            if (e) {
+            } else if (ge) {
                 const uint32_t t = epos + lanes_below(em);
                 if (t < static_cast<uint32_t>(kEqMax)) {
                     eqk[t] = ((v[u] & 0xFFFFFu) << 10) | t;
@@ -425,31 +429,33 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     }
     __syncthreads();
     // digit-d* scores taken: rank < k_rem by key (keys are distinct); their
-    // block ids are compacted in block order into selq[0 .. k_rem)
-    for (uint32_t u = n_eq + tid; u < ((n_eq + 31) & ~31u); u += kHistNT) eqk[u] = 0u;   // pad: ranks nothing
+    // block ids are compacted in block order into selq[0 .. k_rem).  S = 4, 2
+    // or 1 adjacent threads share a key, each counting the keys ahead of it in
+    // one slice of the list (padded to 128 with zeros, which rank nothing).
+    const uint32_t npad = (n_eq + 127) & ~127u;
+    for (uint32_t u = n_eq + tid; u < npad; u += kHistNT) eqk[u] = 0u;
     __syncthreads();
-    bool take = false;
-    if (static_cast<uint32_t>(tid) < n_eq) {
-        if (n_eq == k_rem) {
-            take = true;
-        } else {
-            const uint32_t kx = eqk[tid];
-            const u32x4 *e4 = reinterpret_cast<const u32x4 *>(eqk);
-            const uint32_t nq = ((n_eq + 31) & ~31u) >> 2;
-            uint32_t r = 0;
-            for (uint32_t u = 0; u < nq; u += 8) {
-                u32x4 y[8];
+    const int S = n_eq <= 256 ? 4 : (n_eq <= 512 ? 2 : 1);
+    const uint32_t key_t = static_cast<uint32_t>(tid) / S, slice = static_cast<uint32_t>(tid) % S;
+    uint32_t r = 0;
+    if (n_eq != k_rem && key_t < n_eq) {
+        const uint32_t kx = eqk[key_t];
+        const uint32_t per = npad / S;                     // a multiple of 32
+        const u32x4 *e4 = reinterpret_cast<const u32x4 *>(eqk + slice * per);
+        for (uint32_t u = 0; u < per / 4; u += 8) {
+            u32x4 y[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) y[i] = e4[u + i];
+            for (int i = 0; i < 8; ++i) y[i] = e4[u + i];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) r += (y[i][0] > kx) + (y[i][1] > kx) + (y[i][2] > kx) + (y[i][3] > kx);
-            }
-            take = r < k_rem;
+            for (int i = 0; i < 8; ++i) r += (y[i][0] > kx) + (y[i][1] > kx) + (y[i][2] > kx) + (y[i][3] > kx);
         }
     }
+    if (S >= 2) r += __shfl_xor(r, 1);
+    if (S >= 4) r += __shfl_xor(r, 2);
+    const bool take = slice == 0 && key_t < n_eq && (n_eq == k_rem || r < k_rem);
     uint32_t ntake;
     const uint32_t qpos = block_scan_nt<kHistNT>(take ? 1u : 0u, wsum, ntake);
-    if (take) selq[qpos] = eqb[tid];
+    if (take) selq[qpos] = eqb[key_t];
     __syncthreads();
     // merge the two ascending lists sel[0 .. above) and selq[0 .. k_rem)
     const int budget_i = budget;
