@@ -212,6 +212,62 @@ def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
     }
 
 
+def run_c5(steps):
+    """The 1M-token configuration (YaRN factor 4): a chunked prefill of
+    1,048,576 tokens in 65,536-token qsa_forward calls, and decode steps of
+    8 sequences with 1,048,576 cached tokens each.  One JSON line."""
+    wp, wd = synth.WORKLOADS["prefill_1m"], synth.WORKLOADS["decode_1m"]
+    L, C = wp.seq_len, wp.chunk
+    x = synth.prefill_inputs(wp, "cuda")
+    h = Q.Handle(max_ctx=L, budget_blocks=wp.budget, yarn_factor=wp.yarn_factor)
+    c = Q.alloc_caches(h, 1)
+    ws = Q.workspace(h, Q.QSA_OP_FORWARD, 1, C, L - C)
+    out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device="cuda")
+    bidx = torch.empty((1, L, wp.budget), dtype=torch.int32, device="cuda")
+
+    def prefill():
+        for s0 in range(0, L, C):
+            sl = lambda t: t[:, s0:s0 + C]
+            Q.qsa_forward(h, 1, C, s0, sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["q_idx"]), sl(x["k_idx"]),
+                          c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sl(out), sl(bidx), ws)
+
+    prefill()
+    torch.cuda.synchronize()
+    ev = _events(2)
+    ev[0].record()
+    for _ in range(steps):
+        prefill()
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_pre = ev[0].elapsed_time(ev[1]) / steps
+    del x, c, ws, out, bidx, h
+    torch.cuda.empty_cache()
+    sd = setup_decode(wd)
+    for _ in range(3):
+        decode_step(sd)
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(10 * steps):
+        decode_step(sd)
+    ev[1].record()
+    torch.cuda.synchronize()
+    t_dec = ev[0].elapsed_time(ev[1]) / (10 * steps)
+    ab, _ = attention_bytes(L, wp.budget)
+    db = decode_bytes(wd.batch, wd.seq_len, wd.budget)
+    res = {
+        "c5": {
+            "prefill": {"workload": wp.name, "ms": t_pre, "tok_s": L / (t_pre * 1e-3),
+                        "indexer_tflop": indexer_flops(L) / 1e12, "attention_gathered_TB": ab / 1e12},
+            "decode": {"workload": wd.name, "ms": t_dec, "tok_s": wd.batch / (t_dec * 1e-3),
+                       "roofline": {"bound": "hbm", "achieved": db / (t_dec * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                    "unit": "GB/s", "frac": db / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "algorithmic_bytes": db}},
+            "steps": steps, "dtype": "bf16", "data": "synthetic",
+        }
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +278,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="decode step only (profiling)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured copy / GEMM ceilings")
+    ap.add_argument("--c5", action="store_true",
+                    help="measure the 1M-token configuration instead (chunked prefill, B=8 decode)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -230,6 +288,9 @@ def main():
         sys.exit(2)
 
     torch.cuda.init()
+    if args.c5:
+        run_c5(max(1, min(args.steps, 3)))
+        return
     if args.calib_copy:
         src = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -278,21 +278,40 @@ __global__ __launch_bounds__(256) void attend_decode_merge_kernel(int nsplit, fl
                                                                   const float *__restrict__ part_ml,
                                                                   bf16_t *__restrict__ out)
 {
+    constexpr int kMaxSplits = 32;
+    __shared__ float ws_w[kMaxSplits], ws_l[kMaxSplits];
     const int d = threadIdx.x;
     const int head = blockIdx.x;                    // 0..23
     const int64_t b = blockIdx.y;
     const int grp = head / kGroup, h = head % kGroup;
     const int64_t slot0 = ((b * kKVHeads + grp) * nsplit) * kGroup + h;
-    float m = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_ml[(slot0 + s * kGroup) * 2]);
+    // split weights 2^{(m_s - m) c2}, one lane per split (0 for an empty split)
+    if (d < 64) {
+        const bool on = d < nsplit;
+        const float ms = on ? part_ml[(slot0 + d * kGroup) * 2] : -INFINITY;
+        const float ls = on ? part_ml[(slot0 + d * kGroup) * 2 + 1] : 0.f;
+        float m = ms;
+        for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+        if (d < kMaxSplits) {
+            ws_w[d] = (on && ms != -INFINITY) ? exp2f((ms - m) * c2) : 0.f;
+            ws_l[d] = (on && ms != -INFINITY) ? ls : -1.f;       // -1 marks a skipped split
+        }
+    }
+    __syncthreads();
+    // sums in split order; the partial rows are loaded eight splits at a time
     float l = 0.f, acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-        const int64_t slot = slot0 + s * kGroup;
-        const float ms = part_ml[slot * 2];
-        if (ms == -INFINITY) continue;
-        const float w = exp2f((ms - m) * c2);
-        l += part_ml[slot * 2 + 1] * w;
-        acc += part_o[slot * kHeadDim + d] * w;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+        float po[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            po[i] = (s0 + i < nsplit) ? part_o[(slot0 + (s0 + i) * kGroup) * kHeadDim + d] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (s0 + i >= nsplit || ws_l[s0 + i] < 0.f) continue;
+            const float w = ws_w[s0 + i];
+            l += ws_l[s0 + i] * w;
+            acc += po[i] * w;
+        }
     }
     out[(b * kQHeads + head) * kHeadDim + d] = f32_to_bf16(acc / l);
 }

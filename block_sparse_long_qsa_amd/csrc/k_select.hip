@@ -318,6 +318,61 @@ __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t *wsum /* 
 constexpr int kHistNT = 1024;
 constexpr int kEqMax = kHistNT;
 
+// Tail of a decode selection, for the kHistNT threads of a workgroup: the
+// digit-d* scores (packed keys eqk: low 20 score bits << 10 | ordinal, block
+// ids eqb; n_eq of them, in block order) yield the k_rem of rank below k_rem,
+// compacted in block order into selq; sel holds the `above` blocks of higher
+// digits, ascending; the two lists are merged into out ascending.
+__device__ void finish_digit_select(uint32_t *eqk, const int32_t *eqb, const int32_t *sel, int32_t *selq,
+                                    uint32_t *wsum, uint32_t n_eq, uint32_t k_rem, uint32_t above, int budget,
+                                    int32_t *__restrict__ out)
+{
+    const int tid = threadIdx.x;
+    // digit-d* scores taken: rank < k_rem by key (keys are distinct); their
+    // block ids are compacted in block order into selq[0 .. k_rem).  S = 4, 2
+    // or 1 adjacent threads share a key, each counting the keys ahead of it in
+    // one slice of the list (padded to 128 with zeros, which rank nothing).
+    const uint32_t npad = (n_eq + 127) & ~127u;
+    for (uint32_t u = n_eq + tid; u < npad; u += kHistNT) eqk[u] = 0u;
+    __syncthreads();
+    const int S = n_eq <= 256 ? 4 : (n_eq <= 512 ? 2 : 1);
+    const uint32_t key_t = static_cast<uint32_t>(tid) / S, slice = static_cast<uint32_t>(tid) % S;
+    uint32_t r = 0;
+    if (n_eq != k_rem && key_t < n_eq) {
+        const uint32_t kx = eqk[key_t];
+        const uint32_t per = npad / S;                     // a multiple of 32
+        const u32x4 *e4 = reinterpret_cast<const u32x4 *>(eqk + slice * per);
+        for (uint32_t u = 0; u < per / 4; u += 8) {
+            u32x4 y[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) y[i] = e4[u + i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r += (y[i][0] > kx) + (y[i][1] > kx) + (y[i][2] > kx) + (y[i][3] > kx);
+        }
+    }
+    if (S >= 2) r += __shfl_xor(r, 1);
+    if (S >= 4) r += __shfl_xor(r, 2);
+    const bool take = slice == 0 && key_t < n_eq && (n_eq == k_rem || r < k_rem);
+    uint32_t ntake;
+    const uint32_t qpos = block_scan_nt<kHistNT>(take ? 1u : 0u, wsum, ntake);
+    if (take) selq[qpos] = eqb[key_t];
+    __syncthreads();
+    // merge the two ascending lists sel[0 .. above) and selq[0 .. k_rem)
+    const int budget_i = budget;
+    if (tid < budget_i) {
+        const bool from_gt = static_cast<uint32_t>(tid) < above;
+        const int32_t x = from_gt ? sel[tid] : selq[tid - above];
+        const int32_t *other = from_gt ? selq : sel;
+        uint32_t lo = 0, hi = from_gt ? k_rem : above;        // count of other < x
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (other[mid] < x) lo = mid + 1; else hi = mid;
+        }
+        out[(from_gt ? tid : tid - above) + lo] = x;
+    }
+}
+
+
 __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
     const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
     const uint32_t *__restrict__ dhist, int32_t *__restrict__ block_idx, int budget)
@@ -428,48 +483,214 @@ __global__ __launch_bounds__(kHistNT) void select_hist_kernel(
         }
     }
     __syncthreads();
-    // digit-d* scores taken: rank < k_rem by key (keys are distinct); their
-    // block ids are compacted in block order into selq[0 .. k_rem).  S = 4, 2
-    // or 1 adjacent threads share a key, each counting the keys ahead of it in
-    // one slice of the list (padded to 128 with zeros, which rank nothing).
-    const uint32_t npad = (n_eq + 127) & ~127u;
-    for (uint32_t u = n_eq + tid; u < npad; u += kHistNT) eqk[u] = 0u;
-    __syncthreads();
-    const int S = n_eq <= 256 ? 4 : (n_eq <= 512 ? 2 : 1);
-    const uint32_t key_t = static_cast<uint32_t>(tid) / S, slice = static_cast<uint32_t>(tid) % S;
-    uint32_t r = 0;
-    if (n_eq != k_rem && key_t < n_eq) {
-        const uint32_t kx = eqk[key_t];
-        const uint32_t per = npad / S;                     // a multiple of 32
-        const u32x4 *e4 = reinterpret_cast<const u32x4 *>(eqk + slice * per);
-        for (uint32_t u = 0; u < per / 4; u += 8) {
-            u32x4 y[8];
+    finish_digit_select(eqk, eqb, sel, selq, wsum, n_eq, k_rem, above, budget, out);
+}
+
+// Two-stage decode selection: the same selection as select_hist_kernel with
+// the row's passes spread over many workgroups (long rows, small batches).
+// Stage 1 (select_chunk_kernel): a 256-thread workgroup per kSelChunk scores
+// of a row finds the boundary digit d* from the row's histogram, and stores
+// its chunk's blocks of digits above d* and its digit-d* (score bits, block)
+// pairs, each in block order, with their counts.  Stage 2
+// (select_gather_kernel): one workgroup per row concatenates the chunks'
+// lists in chunk order (so in block order) and finishes as select_hist_kernel.
+constexpr int kSelChunk = 4096;
+constexpr int kSelChunkMax = kHistNT;       // chunk prefixes are scanned by one workgroup
+
+// Boundary digit of a 2048-bin histogram for NT threads: s_out[0] = d* (the
+// highest digit whose suffix count reaches K), s_out[1] = scores above d*.
+template <int NT>
+__device__ void boundary_digit(const uint32_t *__restrict__ dh, uint32_t K, uint32_t *wsum, uint32_t *s_out)
+{
+    constexpr int PER = kSelMaxBins / NT;
+    const int tid = threadIdx.x;
+    uint32_t h[PER];
+    uint32_t sum = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] = e4[u + i];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) r += (y[i][0] > kx) + (y[i][1] > kx) + (y[i][2] > kx) + (y[i][3] > kx);
+    for (int i = 0; i < PER; ++i) {
+        h[i] = dh[tid * PER + i];
+        sum += h[i];
+    }
+    uint32_t tot;
+    const uint32_t before = block_scan_nt<NT>(sum, wsum, tot);
+    uint32_t acc = tot - before - sum;                  // scores in digits above this thread's bins
+    if (acc < K && acc + sum >= K) {
+        for (int i = PER - 1; i >= 0; --i) {
+            if (acc + h[i] >= K) {
+                s_out[0] = static_cast<uint32_t>(tid * PER + i);
+                s_out[1] = acc;
+                break;
+            }
+            acc += h[i];
         }
     }
-    if (S >= 2) r += __shfl_xor(r, 1);
-    if (S >= 4) r += __shfl_xor(r, 2);
-    const bool take = slice == 0 && key_t < n_eq && (n_eq == k_rem || r < k_rem);
-    uint32_t ntake;
-    const uint32_t qpos = block_scan_nt<kHistNT>(take ? 1u : 0u, wsum, ntake);
-    if (take) selq[qpos] = eqb[key_t];
     __syncthreads();
-    // merge the two ascending lists sel[0 .. above) and selq[0 .. k_rem)
-    const int budget_i = budget;
-    if (tid < budget_i) {
-        const bool from_gt = static_cast<uint32_t>(tid) < above;
-        const int32_t x = from_gt ? sel[tid] : selq[tid - above];
-        const int32_t *other = from_gt ? selq : sel;
-        uint32_t lo = 0, hi = from_gt ? k_rem : above;        // count of other < x
-        while (lo < hi) {
-            const uint32_t mid = (lo + hi) >> 1;
-            if (other[mid] < x) lo = mid + 1; else hi = mid;
-        }
-        out[(from_gt ? tid : tid - above) + lo] = x;
+}
+
+__global__ __launch_bounds__(256) void select_chunk_kernel(
+    const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
+    const uint32_t *__restrict__ dhist, int budget, int nchunk, int32_t *__restrict__ cnt,
+    int32_t *__restrict__ gtb, uint32_t *__restrict__ eqs, int32_t *__restrict__ eqi)
+{
+    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t wcnt[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t b = blockIdx.y;
+    const int ch = blockIdx.x;
+    const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
+    const int64_t c0 = static_cast<int64_t>(ch) * kSelChunk;
+    if (o <= budget || c0 >= o) return;                     // whole workgroup
+    const int64_t c1 = (c0 + kSelChunk < o) ? c0 + kSelChunk : o;
+    const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * ncol);
+    // wave w holds scores c0 + 1024w .. +1023, 16 per lane
+    uint32_t v[16];
+    const int64_t wb = c0 + 1024 * wave;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const int64_t j = wb + 64 * u + lane;
+        v[u] = (j < c1) ? srow[j] : 0xFFFFFFFFu;          // sentinel: -1 as int32, below every threshold
     }
+    const uint32_t *dh = dhist + b * kSelMaxBins;
+    boundary_digit<256>(dh, static_cast<uint32_t>(budget), wsum, s_dig);
+    const uint32_t dstar = s_dig[0];
+    const bool store_eq = dh[dstar] <= static_cast<uint32_t>(kEqMax);
+    const int32_t T0 = static_cast<int32_t>(dstar << 20);
+    const int32_t T1 = dstar >= 2047u ? INT32_MAX : static_cast<int32_t>((dstar + 1) << 20);
+    uint32_t ng = 0, nge = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        ng += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u]) >= T1)));
+        nge += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u]) >= T0)));
+    }
+    if (lane == 0) {
+        wcnt[0][wave] = ng;
+        wcnt[1][wave] = nge - ng;
+    }
+    __syncthreads();
+    uint32_t gpos = 0, epos = 0, gtot = 0, etot = 0;
+    for (int w = 0; w < 4; ++w) {
+        if (w < wave) {
+            gpos += wcnt[0][w];
+            epos += wcnt[1][w];
+        }
+        gtot += wcnt[0][w];
+        etot += wcnt[1][w];
+    }
+    const int64_t slot = b * nchunk + ch;
+    int32_t *g_out = gtb + slot * kMaxBudget;
+    uint32_t *e_bits = eqs + slot * kEqMax;
+    int32_t *e_ids = eqi + slot * kEqMax;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+        const bool ge = static_cast<int32_t>(v[u]) >= T0;
+        const uint64_t gem = __builtin_amdgcn_ballot_w64(ge);
+        if (gem == 0) continue;                                  // wave-uniform
+        const bool g = static_cast<int32_t>(v[u]) >= T1;
+        const uint64_t gm = __builtin_amdgcn_ballot_w64(g);
+        const uint64_t em = gem & ~gm;
+        const int32_t blk = static_cast<int32_t>(wb + 64 * u + lane);
+        if (g) {
+            const uint32_t t = gpos + lanes_below(gm);
+            if (t < static_cast<uint32_t>(kMaxBudget)) g_out[t] = blk;
+        } else if (ge && store_eq) {
+            const uint32_t t = epos + lanes_below(em);
+            if (t < static_cast<uint32_t>(kEqMax)) {
+                e_bits[t] = v[u];
+                e_ids[t] = blk;
+            }
+        }
+        gpos += static_cast<uint32_t>(__popcll(gm));
+        epos += static_cast<uint32_t>(__popcll(em));
+    }
+    if (tid == 0) {
+        cnt[slot * 2] = static_cast<int32_t>(gtot);
+        cnt[slot * 2 + 1] = static_cast<int32_t>(etot);
+    }
+}
+
+// Largest c in [0, n) with pre[c] <= t (pre ascending, pre[0] = 0).
+__device__ __forceinline__ int chunk_of(const uint32_t *pre, int n, uint32_t t) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kHistNT) void select_gather_kernel(
+    const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
+    const uint32_t *__restrict__ dhist, int nchunk, const int32_t *__restrict__ cnt, const int32_t *__restrict__ gtb,
+    const uint32_t *__restrict__ eqs, const int32_t *__restrict__ eqi, int32_t *__restrict__ block_idx, int budget)
+{
+    constexpr int NW = kHistNT / 64;
+    __shared__ uint32_t hist[kSelMaxBins];
+    __shared__ __attribute__((aligned(16))) uint32_t eqk[kEqMax];
+    __shared__ int32_t eqb[kEqMax];
+    __shared__ int32_t sel[kMaxBudget];
+    __shared__ int32_t selq[kMaxBudget];
+    __shared__ uint32_t wsum[NW];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t gpre[kSelChunkMax], epre[kSelChunkMax];
+    const int tid = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
+    int32_t *out = block_idx + b * budget;
+    if (take_all(o, budget, out)) return;
+    const uint32_t *dh = dhist + b * kSelMaxBins;
+    boundary_digit<kHistNT>(dh, static_cast<uint32_t>(budget), wsum, s_dig);
+    const uint32_t dstar = s_dig[0];
+    const uint32_t above = s_dig[1];
+    const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
+    const uint32_t n_eq = dh[dstar];
+    if (n_eq > static_cast<uint32_t>(kEqMax)) {
+        const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * ncol);
+        radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
+        return;
+    }
+    const int nch = static_cast<int>((o + kSelChunk - 1) / kSelChunk);
+    const int64_t slot0 = b * nchunk;
+    const uint32_t cg = tid < nch ? static_cast<uint32_t>(cnt[(slot0 + tid) * 2]) : 0u;
+    const uint32_t ce = tid < nch ? static_cast<uint32_t>(cnt[(slot0 + tid) * 2 + 1]) : 0u;
+    uint32_t tg, te;
+    const uint32_t pg = block_scan_nt<kHistNT>(cg, wsum, tg);
+    const uint32_t pe = block_scan_nt<kHistNT>(ce, wsum, te);
+    if (tid < nch) {
+        gpre[tid] = pg;
+        epre[tid] = pe;
+    }
+    __syncthreads();
+    // concatenate the chunks' lists in chunk (= block) order
+    if (static_cast<uint32_t>(tid) < above) {
+        const int c = chunk_of(gpre, nch, static_cast<uint32_t>(tid));
+        sel[tid] = gtb[(slot0 + c) * kMaxBudget + (tid - gpre[c])];
+    }
+    if (static_cast<uint32_t>(tid) < n_eq) {
+        const int c = chunk_of(epre, nch, static_cast<uint32_t>(tid));
+        const int64_t e = (slot0 + c) * kEqMax + (tid - epre[c]);
+        eqk[tid] = ((eqs[e] & 0xFFFFFu) << 10) | static_cast<uint32_t>(tid);
+        eqb[tid] = eqi[e];
+    }
+    __syncthreads();
+    finish_digit_select(eqk, eqb, sel, selq, wsum, n_eq, k_rem, above, budget, out);
+}
+
+hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound,
+                                   int64_t ncol, const float *scores, const uint32_t *dhist, int32_t *cnt,
+                                   int32_t *gtb, uint32_t *eqs, int32_t *eqi, int32_t *block_idx, int budget)
+{
+    if (B <= 0) return hipSuccess;
+    const int64_t nchunk = (ncol + kSelChunk - 1) / kSelChunk;
+    if (nchunk > kSelChunkMax) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(select_chunk_kernel, dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(B)), dim3(256),
+                       0, st, cache_len, pos_bound, ncol, scores, dhist, budget, static_cast<int>(nchunk), cnt, gtb,
+                       eqs, eqi);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_gather_kernel, dim3(static_cast<unsigned>(B)), dim3(kHistNT), 0, st, cache_len, pos_bound,
+                       ncol, scores, dhist, static_cast<int>(nchunk), cnt, gtb, eqs, eqi, block_idx, budget);
+    return hipGetLastError();
 }
 
 hipError_t launch_select_hist(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int64_t ncol,

@@ -42,6 +42,8 @@ hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, in
                               const bf16_t *, float *, uint32_t *);
 hipError_t launch_select_hist(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const float *,
                               const uint32_t *, int32_t *, int);
+hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const float *,
+                                   const uint32_t *, int32_t *, int32_t *, uint32_t *, int32_t *, int32_t *, int);
 }  // namespace qsa
 
 using namespace qsa;
@@ -120,7 +122,11 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     return f;
 }
 
-struct DecLayout { size_t qrot, scores, bidx, part_o, part_ml, hist, total; int64_t ncol; int nsplit; };
+struct DecLayout {
+    size_t qrot, scores, bidx, part_o, part_ml, hist, s2cnt, s2gt, s2eqs, s2eqi, total;
+    int64_t ncol, nchunk;
+    int nsplit;
+};
 DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     DecLayout d{};
     d.ncol = ctx_bound / kBlock;
@@ -133,7 +139,15 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     const size_t slots = static_cast<size_t>(B) * kKVHeads * d.nsplit * kGroup;
     d.part_ml = d.part_o + align_up(slots * kHeadDim * 4);
     d.hist = d.part_ml + align_up(slots * 2 * 4);
-    d.total = d.hist + align_up(static_cast<size_t>(B) * 2048 * 4);
+    // two-stage selection: per 4,096-score chunk a count pair and the chunk's
+    // lists (at most budget blocks above the boundary digit, 1,024 at it)
+    d.nchunk = (d.ncol + 4095) / 4096;
+    const size_t nck = static_cast<size_t>(B) * d.nchunk;
+    d.s2cnt = d.hist + align_up(static_cast<size_t>(B) * 2048 * 4);
+    d.s2gt = d.s2cnt + align_up(nck * 2 * 4);
+    d.s2eqs = d.s2gt + align_up(nck * kMaxBudget * 4);
+    d.s2eqi = d.s2eqs + align_up(nck * 1024 * 4);
+    d.total = d.s2eqi + align_up(nck * 1024 * 4);
     return d;
 }
 
@@ -414,7 +428,11 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
                                         kbar_cache, kpend, qrot, dhist);
     if (e == hipSuccess)
         e = launch_decode_scan(st, B, cache_len, ctx_bound, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
-    if (e == hipSuccess) e = launch_select_hist(st, B, cache_len, ctx_bound, d.ncol, scores, dhist, bidx, budget);
+    if (e == hipSuccess)
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, d.ncol, scores, dhist,
+                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
+                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
+                                    bidx, budget);
     if (e == hipSuccess)
         e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, budget, d.nsplit, h->sigma, q,
                                  k_cache, v_cache, bidx, part_o, part_ml, out);
