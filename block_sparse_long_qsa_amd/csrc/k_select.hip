@@ -305,16 +305,11 @@ __device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t *wsum /* 
 }
 
 // Decode selection from a score row whose histogram of bits 30..20 (2048
-// digits) the scan kernel already built.  The boundary digit d* and the count
-// above it come from the histogram.  The row is held in registers (loaded
-// while the histogram is read); each wave owns a contiguous range of it.  A
-// counting pass and a scan of the per-wave counts give every wave its offsets,
-// so one ordered pass stores the blocks of digits above d* and the digit-d*
-// scores in block order.  Inside digit d* the high 12 score bits are equal, so
-// (low 20 bits, ordinal) is one 32-bit key ordering (score desc, block desc):
-// the remaining budget is the digit-d* scores of rank below it.  Both lists
-// are ascending; a merge writes the selection.  Rows whose boundary digit holds more
-// than kEqMax scores use the plain radix select.
+// digits) the scan kernel already built: the boundary digit d* and the count
+// above it come from the histogram.  Inside digit d* the high 12 score bits
+// are equal, so (low 20 bits, ordinal) is one 32-bit key ordering (score
+// desc, block desc).  Rows whose boundary digit holds more than kEqMax scores
+// use the plain radix select.
 constexpr int kHistNT = 1024;
 constexpr int kEqMax = kHistNT;
 
@@ -372,128 +367,14 @@ __device__ void finish_digit_select(uint32_t *eqk, const int32_t *eqb, const int
     }
 }
 
-
-__global__ __launch_bounds__(kHistNT) void select_hist_kernel(
-    const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
-    const uint32_t *__restrict__ dhist, int32_t *__restrict__ block_idx, int budget)
-{
-    constexpr int NW = kHistNT / 64;
-    __shared__ uint32_t hist[kSelMaxBins];
-    __shared__ __attribute__((aligned(16))) uint32_t eqk[kEqMax];
-    __shared__ int32_t eqb[kEqMax];
-    __shared__ int32_t sel[kMaxBudget];
-    __shared__ int32_t selq[kMaxBudget];
-    __shared__ uint32_t wsum[NW];
-    __shared__ uint32_t wcnt[2][NW];
-    __shared__ uint32_t s_digit, s_above;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int64_t b = blockIdx.x;
-    const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
-    int32_t *out = block_idx + b * budget;
-    if (take_all(o, budget, out)) return;
-    const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * ncol);
-    // register chunks of RC x 64 scores (rows up to 16 x 2048 scores: one chunk)
-    constexpr int RC = 32;
-    const int64_t per = ((o + NW - 1) / NW + 63) & ~int64_t(63);
-    const int64_t r0 = wave * per;
-    const int64_t r1 = (r0 + per < o) ? r0 + per : o;
-    uint32_t v[RC];
-    auto load_chunk = [&](int64_t jb) {
-#pragma unroll
-        for (int u = 0; u < RC; ++u) {
-            const int64_t j = jb + 64 * u + lane;
-            v[u] = (j < r1) ? srow[j] : 0xFFFFFFFFu;     // sentinel: -1 as int32, below every threshold
-        }
-    };
-    const int64_t chunk = 64 * RC;
-    const bool one_chunk = r1 - r0 <= chunk;
-    // boundary digit from the histogram: 2 digits per thread, suffix sums (the
-    // histogram is loaded first so the scan overlaps the row's loads)
-    const uint32_t h0 = dhist[b * kSelMaxBins + 2 * tid], h1 = dhist[b * kSelMaxBins + 2 * tid + 1];
-    if (one_chunk) load_chunk(r0);
-    {
-        hist[2 * tid] = h0;
-        hist[2 * tid + 1] = h1;
-        uint32_t tot;
-        const uint32_t before = block_scan_nt<kHistNT>(h0 + h1, wsum, tot);
-        const uint32_t incl = tot - before;             // digits >= 2*tid
-        const uint32_t c1 = incl - h0;                  // digits >= 2*tid + 1
-        const uint32_t K = static_cast<uint32_t>(budget);
-        if (c1 >= K && c1 - h1 < K) { s_digit = 2 * tid + 1; s_above = c1 - h1; }
-        else if (incl >= K && c1 < K) { s_digit = 2 * tid; s_above = c1; }
-        __syncthreads();
-    }
-    const uint32_t dstar = s_digit;
-    const uint32_t above = s_above;
-    const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
-    const uint32_t n_eq = hist[dstar];
-    if (n_eq > static_cast<uint32_t>(kEqMax)) {
-        radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
-        return;
-    }
-    // Digit d* as signed bounds on the score bits (scores are >= +0, so their
-    // bits order like the values): above d* <=> bits >= T1, at or above <=> bits >= T0.
-    const int32_t T0 = static_cast<int32_t>(dstar << 20);
-    const int32_t T1 = dstar >= 2047u ? INT32_MAX : static_cast<int32_t>((dstar + 1) << 20);
-    // counting pass, then the wave's offsets among all waves
-    uint32_t ng = 0, nge = 0;
-    for (int64_t jb = r0; jb < r1; jb += chunk) {
-        if (!one_chunk) load_chunk(jb);
-#pragma unroll
-        for (int u = 0; u < RC; ++u) {
-            ng += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u]) >= T1)));
-            nge += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u]) >= T0)));
-        }
-    }
-    if (lane == 0) {
-        wcnt[0][wave] = ng;
-        wcnt[1][wave] = nge - ng;
-    }
-    __syncthreads();
-    uint32_t gpos = 0, epos = 0;
-    for (int w = 0; w < wave; ++w) {
-        gpos += wcnt[0][w];
-        epos += wcnt[1][w];
-    }
-    // ordered pass
-    for (int64_t jb = r0; jb < r1; jb += chunk) {
-        if (!one_chunk) load_chunk(jb);
-#pragma unroll
-        for (int u = 0; u < RC; ++u) {
-            const bool ge = static_cast<int32_t>(v[u]) >= T0;
-            const uint64_t gem = __builtin_amdgcn_ballot_w64(ge);
-            if (gem == 0) continue;                                  // wave-uniform
-            const bool g = static_cast<int32_t>(v[u]) >= T1;
-            const uint64_t gm = __builtin_amdgcn_ballot_w64(g);
-            const uint64_t em = gem & ~gm;
-            const int32_t blk = static_cast<int32_t>(jb + 64 * u + lane);
-            if (g) {
-                const uint32_t t = gpos + lanes_below(gm);
-                if (t < static_cast<uint32_t>(kMaxBudget)) sel[t] = blk;
-            } else if (ge) {
-                const uint32_t t = epos + lanes_below(em);
-                if (t < static_cast<uint32_t>(kEqMax)) {
-                    eqk[t] = ((v[u] & 0xFFFFFu) << 10) | t;
-                    eqb[t] = blk;
-                }
-            }
-            gpos += static_cast<uint32_t>(__popcll(gm));
-            epos += static_cast<uint32_t>(__popcll(em));
-        }
-    }
-    __syncthreads();
-    finish_digit_select(eqk, eqb, sel, selq, wsum, n_eq, k_rem, above, budget, out);
-}
-
-// Two-stage decode selection: the same selection as select_hist_kernel with
-// the row's passes spread over many workgroups (long rows, small batches).
+// Two-stage decode selection, the row's passes spread over many workgroups.
 // Stage 1 (select_chunk_kernel): a 256-thread workgroup per kSelChunk scores
 // of a row finds the boundary digit d* from the row's histogram, and stores
 // its chunk's blocks of digits above d* and its digit-d* (score bits, block)
 // pairs, each in block order, with their counts.  Stage 2
 // (select_gather_kernel): one workgroup per row concatenates the chunks'
-// lists in chunk order (so in block order) and finishes as select_hist_kernel.
+// lists in chunk order (so in block order), ranks the boundary digit's
+// scores and merges the two ascending lists.
 constexpr int kSelChunk = 4096;
 constexpr int kSelChunkMax = kHistNT;       // chunk prefixes are scanned by one workgroup
 
@@ -530,7 +411,7 @@ __device__ void boundary_digit(const uint32_t *__restrict__ dh, uint32_t K, uint
 __global__ __launch_bounds__(256) void select_chunk_kernel(
     const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
     const uint32_t *__restrict__ dhist, int budget, int nchunk, int32_t *__restrict__ cnt,
-    int32_t *__restrict__ gtb, uint32_t *__restrict__ eqs, int32_t *__restrict__ eqi)
+    int32_t *__restrict__ gtb, uint32_t *__restrict__ eqs, int32_t *__restrict__ eqi, uint32_t *__restrict__ rowinfo)
 {
     __shared__ uint32_t wsum[4];
     __shared__ uint32_t s_dig[2];
@@ -554,7 +435,13 @@ __global__ __launch_bounds__(256) void select_chunk_kernel(
     const uint32_t *dh = dhist + b * kSelMaxBins;
     boundary_digit<256>(dh, static_cast<uint32_t>(budget), wsum, s_dig);
     const uint32_t dstar = s_dig[0];
-    const bool store_eq = dh[dstar] <= static_cast<uint32_t>(kEqMax);
+    const uint32_t n_eq = dh[dstar];
+    const bool store_eq = n_eq <= static_cast<uint32_t>(kEqMax);
+    if (ch == 0 && tid == 0) {                              // the row's boundary for stage two
+        rowinfo[b * 3] = dstar;
+        rowinfo[b * 3 + 1] = s_dig[1];
+        rowinfo[b * 3 + 2] = n_eq;
+    }
     const int32_t T0 = static_cast<int32_t>(dstar << 20);
     const int32_t T1 = dstar >= 2047u ? INT32_MAX : static_cast<int32_t>((dstar + 1) << 20);
     uint32_t ng = 0, nge = 0;
@@ -621,7 +508,7 @@ __device__ __forceinline__ int chunk_of(const uint32_t *pre, int n, uint32_t t) 
 
 __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
     const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
-    const uint32_t *__restrict__ dhist, int nchunk, const int32_t *__restrict__ cnt, const int32_t *__restrict__ gtb,
+    const uint32_t *__restrict__ rowinfo, int nchunk, const int32_t *__restrict__ cnt, const int32_t *__restrict__ gtb,
     const uint32_t *__restrict__ eqs, const int32_t *__restrict__ eqi, int32_t *__restrict__ block_idx, int budget)
 {
     constexpr int NW = kHistNT / 64;
@@ -631,19 +518,15 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
     __shared__ int32_t sel[kMaxBudget];
     __shared__ int32_t selq[kMaxBudget];
     __shared__ uint32_t wsum[NW];
-    __shared__ uint32_t s_dig[2];
     __shared__ uint32_t gpre[kSelChunkMax], epre[kSelChunkMax];
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
     int32_t *out = block_idx + b * budget;
     if (take_all(o, budget, out)) return;
-    const uint32_t *dh = dhist + b * kSelMaxBins;
-    boundary_digit<kHistNT>(dh, static_cast<uint32_t>(budget), wsum, s_dig);
-    const uint32_t dstar = s_dig[0];
-    const uint32_t above = s_dig[1];
+    const uint32_t above = rowinfo[b * 3 + 1];
     const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
-    const uint32_t n_eq = dh[dstar];
+    const uint32_t n_eq = rowinfo[b * 3 + 2];
     if (n_eq > static_cast<uint32_t>(kEqMax)) {
         const uint32_t *srow = reinterpret_cast<const uint32_t *>(scores + b * ncol);
         radix_topk<kHistNT>(o, budget, [&](int64_t j) { return srow[j]; }, [](int64_t j) { return j; }, out, hist);
@@ -678,27 +561,19 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
 
 hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound,
                                    int64_t ncol, const float *scores, const uint32_t *dhist, int32_t *cnt,
-                                   int32_t *gtb, uint32_t *eqs, int32_t *eqi, int32_t *block_idx, int budget)
+                                   int32_t *gtb, uint32_t *eqs, int32_t *eqi, uint32_t *rowinfo, int32_t *block_idx,
+                                   int budget)
 {
     if (B <= 0) return hipSuccess;
     const int64_t nchunk = (ncol + kSelChunk - 1) / kSelChunk;
     if (nchunk > kSelChunkMax) return hipErrorInvalidValue;
     hipLaunchKernelGGL(select_chunk_kernel, dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(B)), dim3(256),
                        0, st, cache_len, pos_bound, ncol, scores, dhist, budget, static_cast<int>(nchunk), cnt, gtb,
-                       eqs, eqi);
+                       eqs, eqi, rowinfo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(select_gather_kernel, dim3(static_cast<unsigned>(B)), dim3(kHistNT), 0, st, cache_len, pos_bound,
-                       ncol, scores, dhist, static_cast<int>(nchunk), cnt, gtb, eqs, eqi, block_idx, budget);
-    return hipGetLastError();
-}
-
-hipError_t launch_select_hist(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int64_t ncol,
-                              const float *scores, const uint32_t *dhist, int32_t *block_idx, int budget)
-{
-    if (B <= 0) return hipSuccess;
-    hipLaunchKernelGGL(select_hist_kernel, dim3(B), dim3(kHistNT), 0, st, cache_len, pos_bound, ncol, scores, dhist,
-                       block_idx, budget);
+                       ncol, scores, rowinfo, static_cast<int>(nchunk), cnt, gtb, eqs, eqi, block_idx, budget);
     return hipGetLastError();
 }
 

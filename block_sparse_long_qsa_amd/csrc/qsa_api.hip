@@ -40,10 +40,9 @@ hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int3
                                 bf16_t *, bf16_t *, uint32_t *);
 hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int64_t, const bf16_t *,
                               const bf16_t *, float *, uint32_t *);
-hipError_t launch_select_hist(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const float *,
-                              const uint32_t *, int32_t *, int);
 hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const float *,
-                                   const uint32_t *, int32_t *, int32_t *, uint32_t *, int32_t *, int32_t *, int);
+                                   const uint32_t *, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *, int32_t *,
+                                   int);
 }  // namespace qsa
 
 using namespace qsa;
@@ -123,7 +122,7 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
 }
 
 struct DecLayout {
-    size_t qrot, scores, bidx, part_o, part_ml, hist, s2cnt, s2gt, s2eqs, s2eqi, total;
+    size_t qrot, scores, bidx, part_o, part_ml, hist, s2cnt, s2gt, s2eqs, s2eqi, s2row, total;
     int64_t ncol, nchunk;
     int nsplit;
 };
@@ -147,7 +146,8 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     d.s2gt = d.s2cnt + align_up(nck * 2 * 4);
     d.s2eqs = d.s2gt + align_up(nck * kMaxBudget * 4);
     d.s2eqi = d.s2eqs + align_up(nck * 1024 * 4);
-    d.total = d.s2eqi + align_up(nck * 1024 * 4);
+    d.s2row = d.s2eqi + align_up(nck * 1024 * 4);
+    d.total = d.s2row + align_up(static_cast<size_t>(B) * 3 * 4);
     return d;
 }
 
@@ -432,7 +432,7 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
         e = launch_select_two_stage(st, B, cache_len, ctx_bound, d.ncol, scores, dhist,
                                     reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
                                     reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
-                                    bidx, budget);
+                                    reinterpret_cast<uint32_t *>(w + d.s2row), bidx, budget);
     if (e == hipSuccess)
         e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, budget, d.nsplit, h->sigma, q,
                                  k_cache, v_cache, bidx, part_o, part_ml, out);
