@@ -183,6 +183,18 @@ __device__ __forceinline__ int topk_bin(float s) {
     const int b = static_cast<int>(__float_as_uint(s) >> 20) - kTopkBinBase;
     return b < 0 ? 0 : (b >= kTopkBins ? kTopkBins - 1 : b);
 }
+// The same bin for the bits of a score >= +0 (sign bit clear).
+__device__ __forceinline__ int topk_bin_bits(uint32_t bits) {
+    const int b = static_cast<int>(bits >> 20) - kTopkBinBase;
+    return max(0, min(kTopkBins - 1, b));
+}
+// Bits of the lower edge of the bin above threshold t (a bin edge or +inf):
+// kept scores with bits >= it lie above t's bin; none lies above the top bin.
+__device__ __forceinline__ uint32_t next_bin_bits(float t) {
+    const uint32_t tb = __float_as_uint(t);
+    if (tb == 0u) return static_cast<uint32_t>(kTopkBinBase + 1) << 20;
+    return tb >= (static_cast<uint32_t>(kTopkBinBase + kTopkBins - 1) << 20) ? 0x7F800000u : tb + (1u << 20);
+}
 __device__ __forceinline__ float topk_bin_edge(int b) {
     return b <= 0 ? 0.0f : __uint_as_float(static_cast<uint32_t>(b + kTopkBinBase) << 20);
 }
@@ -265,12 +277,14 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     int st_bt = 0;
     const bool st_live = lane < 16 && q0 + 16 * wave + lane < L;
     float tau_v[2][4];
+    uint32_t tn_v[2][4];       // bits of the lower edge of the bin above tau (kept scores at or above it raise st_ca)
     int32_t qo[2][4];
     for (int a = 0; a < 2; ++a)
         for (int i = 0; i < 4; ++i) {
             const int64_t q = q0 + 16 * wave + 8 * a + 2 * i + half;
             qo[a][i] = (q < L) ? static_cast<int32_t>((q_offset + q) / kBlock) : 0;
             tau_v[a][i] = (q < L) ? 0.0f : INFINITY;
+            tn_v[a][i] = next_bin_bits(tau_v[a][i]);
         }
     const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
     // candidate lists of this workgroup's 64 queries (rows b*L + q0 .. +63); the
@@ -343,12 +357,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                     any = true;
                     const uint32_t c0 = __builtin_amdgcn_readlane(st_cnt, j0);
                     const uint32_t c1 = __builtin_amdgcn_readlane(st_cnt, j0 + 1);
-                    // kept scores above the threshold bin: bits >= lower edge of bin bt + 1
-                    // (none above the top bin, whose edge is 2^8)
-                    const uint32_t tb = __float_as_uint(tau_v[a][i]);
-                    const uint32_t tn = (tb == 0u) ? (static_cast<uint32_t>(kTopkBinBase + 1) << 20)
-                                        : (tb >= (static_cast<uint32_t>(kTopkBinBase + kTopkBins - 1) << 20)
-                                               ? 0x7F800000u : tb + (1u << 20));
+                    const uint32_t tn = tn_v[a][i];
                     const uint32_t nl0 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[0])));
                     const uint32_t nh0 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[0] >> 32)));
                     const uint32_t nl1 = static_cast<uint32_t>(__popc(static_cast<uint32_t>(m[1])));
@@ -367,12 +376,12 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                             const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m[ct] >> 32),
                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m[ct]), 0u));
                             const uint32_t pos = (ct == 0 ? base0 : base1) + below;
-                            if (pos < static_cast<uint32_t>(cap)) {
-                                const uint32_t off = ql * static_cast<uint32_t>(cap) + pos;
-                                const uint32_t col = static_cast<uint32_t>(cs) + 32 * ct + (lane & 31);
-                                wg_cand[off] = make_uint2(sb[ct], col);
-                            }
-                            atomicAdd(&hist[ql][topk_bin(__uint_as_float(sb[ct]))], 1u);
+                            // a list past its capacity stays in bounds (its row is
+                            // recomputed exactly: see the final selection)
+                            const uint32_t slot = pos < static_cast<uint32_t>(cap) ? pos : cap - 1;
+                            const uint32_t col = static_cast<uint32_t>(cs) + 32 * ct + (lane & 31);
+                            wg_cand[ql * static_cast<uint32_t>(cap) + slot] = make_uint2(sb[ct], col);
+                            atomicAdd(&hist[ql][topk_bin_bits(sb[ct])], 1u);
                         }
                     }
                     const bool l0 = lane == j0, l1 = lane == j0 + 1;
@@ -407,6 +416,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                     const float ta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st_tau), j0));
                     const float tb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(st_tau), j0 + 1));
                     tau_v[a][i] = half ? tb : ta;
+                    tn_v[a][i] = next_bin_bits(tau_v[a][i]);
                 }
         }
         if (more) put(buf ^ 1);
