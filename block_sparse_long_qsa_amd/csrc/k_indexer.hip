@@ -290,6 +290,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     // candidate lists of this workgroup's 64 queries (rows b*L + q0 .. +63); the
     // padding queries of a ragged tile never append (infinite threshold)
     uint2 *__restrict__ wg_cand = cand + (b * L + q0) * cap;
+    char *__restrict__ wg_cand_bytes = reinterpret_cast<char *>(wg_cand);   // 32-bit byte offsets below 4 MiB
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
     // k̄ tiles: the next tile is loaded into registers before the current
@@ -378,9 +379,10 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                             const uint32_t pos = (ct == 0 ? base0 : base1) + below;
                             // a list past its capacity stays in bounds (its row is
                             // recomputed exactly: see the final selection)
-                            const uint32_t slot = pos < static_cast<uint32_t>(cap) ? pos : cap - 1;
+                            const uint32_t slot = min(pos, static_cast<uint32_t>(cap) - 1u);
                             const uint32_t col = static_cast<uint32_t>(cs) + 32 * ct + (lane & 31);
-                            wg_cand[ql * static_cast<uint32_t>(cap) + slot] = make_uint2(sb[ct], col);
+                            *reinterpret_cast<uint2 *>(wg_cand_bytes + (ql * static_cast<uint32_t>(cap) + slot) * 8u) =
+                                make_uint2(sb[ct], col);
                             atomicAdd(&hist[ql][topk_bin_bits(sb[ct])], 1u);
                         }
                     }
