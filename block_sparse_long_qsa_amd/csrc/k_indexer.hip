@@ -371,7 +371,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                     const uint32_t base1 = half ? c1 + nh0 - nl1 : c0 + nl0;
                     uint64_t am = 0, am1 = 0;
                     for (int ct = 0; ct < 2; ++ct) {
-                        const uint64_t a_m = __builtin_amdgcn_ballot_w64(keep[ct] && sb[ct] >= tn);
+                        const uint64_t a_m = __builtin_amdgcn_ballot_w64(sb[ct] >= tn) & m[ct];
                         if (ct == 0) am = a_m; else am1 = a_m;
                         if (keep[ct]) {
                             const uint32_t below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m[ct] >> 32),
