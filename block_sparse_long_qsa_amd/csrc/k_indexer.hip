@@ -183,11 +183,6 @@ __device__ __forceinline__ int topk_bin(float s) {
     const int b = static_cast<int>(__float_as_uint(s) >> 20) - kTopkBinBase;
     return b < 0 ? 0 : (b >= kTopkBins ? kTopkBins - 1 : b);
 }
-// The same bin for the bits of a score >= +0 (sign bit clear).
-__device__ __forceinline__ int topk_bin_bits(uint32_t bits) {
-    const int b = static_cast<int>(bits >> 20) - kTopkBinBase;
-    return max(0, min(kTopkBins - 1, b));
-}
 // Bits of the lower edge of the bin above threshold t (a bin edge or +inf):
 // kept scores with bits >= it lie above t's bin; none lies above the top bin.
 __device__ __forceinline__ uint32_t next_bin_bits(float t) {
@@ -291,6 +286,8 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     // padding queries of a ragged tile never append (infinite threshold)
     uint2 *__restrict__ wg_cand = cand + (b * L + q0) * cap;
     char *__restrict__ wg_cand_bytes = reinterpret_cast<char *>(wg_cand);   // 32-bit byte offsets below 4 MiB
+    // hist indexed by the unclamped bin field: hist_rebased[ql * 128 + (bits >> 20)], bits >> 20 >= base
+    uint32_t *hist_rebased = &hist[0][0] - kTopkBinBase;
 
     const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
     // k̄ tiles: the next tile is loaded into registers before the current
@@ -383,7 +380,10 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
                             const uint32_t col = static_cast<uint32_t>(cs) + 32 * ct + (lane & 31);
                             *reinterpret_cast<uint2 *>(wg_cand_bytes + (ql * static_cast<uint32_t>(cap) + slot) * 8u) =
                                 make_uint2(sb[ct], col);
-                            atomicAdd(&hist[ql][topk_bin_bits(sb[ct])], 1u);
+                            // bin = clamp(bits >> 20, base, base + 127) - base, folded into the row address
+                            const uint32_t e = min(max(sb[ct] >> 20, static_cast<uint32_t>(kTopkBinBase)),
+                                                   static_cast<uint32_t>(kTopkBinBase + kTopkBins - 1));
+                            atomicAdd(hist_rebased + ql * kTopkBins + e, 1u);
                         }
                     }
                     const bool l0 = lane == j0, l1 = lane == j0 + 1;
