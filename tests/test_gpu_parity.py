@@ -435,3 +435,38 @@ def test_decode_reuse_speculative_steps():
             if pos[b] % 4 == 3:
                 ref_kbar = O.f32_to_bf16_bits(O.indexer_keys(bits(x["k_idx"][b, :pos[b] + 1]), p))
                 assert np.array_equal(bits(c["kbar_cache"][b, pos[b] // 4]), ref_kbar[pos[b] // 4])
+
+
+def test_decode_reuse_selection_position_bounds():
+    """sel_pos is clamped to [0, p]: past p it is the plain decode step (bit for
+    bit); below 0 it is 0, so the query attends every token 0..p (its reused
+    list names no block before block 0).  Bad sizes are rejected on the host."""
+    budget, n, B = 32, 777, 1
+    w = synth.Workload("t", "decode", B, n, budget, 4, "random", 31)
+    h = Q.Handle(max_ctx=1024, budget_blocks=budget)
+    x, out0, bidx0, c = _decode_setup(w, [n], h)
+    xd = _to(x)
+    new = {k: xd[k][:, n:n + 1].contiguous() for k in ("k", "v", "k_idx")}
+    cache_len = torch.tensor([n], dtype=torch.int32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_DECODE, B, 1, n)
+    sel = bidx0.view(B, budget).contiguous()
+    outs = {}
+    for name, sp in (("past", n + 50), ("neg", -7)):
+        o = torch.empty_like(out0)
+        Q.qsa_decode_reuse(h, B, cache_len, torch.tensor([sp], dtype=torch.int32, device=DEV), n, xd["q"], new["k"],
+                           new["v"], new["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel, o, ws)
+        outs[name] = o
+    torch.cuda.synchronize()
+    assert torch.equal(outs["past"], out0)
+    p = O.Params(budget=budget)
+    lay = oracle_layer(x, 0, p, n_keys=n + 1)
+    ref = lay.row_reused(n, bits(x["q"][0, 0]), np.full(budget, -1), 0)
+    check_out(f32(outs["neg"][0, 0]), ref, "sel_pos < 0")
+    with pytest.raises(Q.QSAError) as e:
+        Q.qsa_decode_reuse(h, B, cache_len, cache_len, n, xd["q"], new["k"], new["v"], new["k_idx"], c["k_cache"],
+                           c["v_cache"], c["kbar_cache"], c["kpend"], sel, outs["neg"], ws[:16])
+    assert e.value.status == 6
+    with pytest.raises(Q.QSAError) as e:
+        Q.qsa_decode_reuse(h, B, cache_len, cache_len, 1024, xd["q"], new["k"], new["v"], new["k_idx"],
+                           c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel, outs["neg"], ws)
+    assert e.value.status == 5
