@@ -212,11 +212,10 @@ def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
     }
 
 
-def run_c5(steps):
-    """The 1M-token configuration (YaRN factor 4): a chunked prefill of
-    1,048,576 tokens in 65,536-token qsa_forward calls, and decode steps of
-    8 sequences with 1,048,576 cached tokens each.  One JSON line."""
-    wp, wd = synth.WORKLOADS["prefill_1m"], synth.WORKLOADS["decode_1m"]
+def qsa_prefill_1m_ms(steps):
+    """QSA chunked prefill of 1,048,576 tokens (YaRN 4) in 65,536-token
+    qsa_forward calls: one warm-up pass, then the mean of `steps` passes (ms)."""
+    wp = synth.WORKLOADS["prefill_1m"]
     L, C = wp.seq_len, wp.chunk
     x = synth.prefill_inputs(wp, "cuda")
     h = Q.Handle(max_ctx=L, budget_blocks=wp.budget, yarn_factor=wp.yarn_factor)
@@ -239,9 +238,20 @@ def run_c5(steps):
         prefill()
     ev[1].record()
     torch.cuda.synchronize()
-    t_pre = ev[0].elapsed_time(ev[1]) / steps
+    t = ev[0].elapsed_time(ev[1]) / steps
     del x, c, ws, out, bidx, h
     torch.cuda.empty_cache()
+    return t
+
+
+def run_c5(steps):
+    """The 1M-token configuration (YaRN factor 4): a chunked prefill of
+    1,048,576 tokens in 65,536-token qsa_forward calls, and decode steps of
+    8 sequences with 1,048,576 cached tokens each.  One JSON line."""
+    wp, wd = synth.WORKLOADS["prefill_1m"], synth.WORKLOADS["decode_1m"]
+    L = wp.seq_len
+    t_pre = qsa_prefill_1m_ms(steps)
+    ev = _events(2)
     sd = setup_decode(wd)
     for _ in range(3):
         decode_step(sd)
@@ -268,6 +278,86 @@ def run_c5(steps):
     print(json.dumps(res), flush=True)
 
 
+def dense_prefill_ms(L, reps=1):
+    """Dense causal GQA attention over L tokens (24 query heads, 2 KV heads, head
+    dim 256, bf16) with PyTorch's flash / memory-efficient SDPA kernels: the
+    dense baseline of the pages' speed-up figures.  Timing only (random
+    operands of the layer's shapes)."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    q = torch.randn(1, 24, L, 256, device="cuda", generator=g).to(torch.bfloat16)
+    k = torch.randn(1, 2, L, 256, device="cuda", generator=g).to(torch.bfloat16)
+    v = torch.randn(1, 2, L, 256, device="cuda", generator=g).to(torch.bfloat16)
+    f = torch.nn.functional.scaled_dot_product_attention
+    with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+        o = f(q, k, v, is_causal=True, scale=1.0 / 16, enable_gqa=True)
+        torch.cuda.synchronize()
+        ev = _events(2)
+        ev[0].record()
+        for _ in range(reps):
+            o = f(q, k, v, is_causal=True, scale=1.0 / 16, enable_gqa=True)
+        ev[1].record()
+        torch.cuda.synchronize()
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def run_ratios(steps):
+    """QSA against dense attention on this GPU, as in the pages' module
+    speed-ups (prefill and decode at 1M tokens): QSA prefill (append + fused
+    index/select + sparse attention) against dense causal SDPA at 262,144 and
+    1,048,576 tokens, and QSA decode of 8 x 1,048,576 against the same split-K
+    decode kernel over every cached token (qsa_decode_reuse with a selection
+    made at position 0: no selected block, the tail is the whole context)."""
+    res = {}
+    wp = synth.WORKLOADS["prefill_256k"]
+    sp = setup_prefill(wp)
+    for _ in range(2):
+        prefill_stages(sp, _events(4))
+    ev = [_events(4) for _ in range(steps)]
+    for e in ev:
+        prefill_stages(sp, e)
+    torch.cuda.synchronize()
+    t_qsa = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    del sp
+    torch.cuda.empty_cache()
+    t_dense = dense_prefill_ms(wp.seq_len, reps=2)
+    res["prefill_262144"] = {"qsa_ms": t_qsa, "dense_sdpa_ms": t_dense, "speedup": t_dense / t_qsa}
+    t_qsa_1m = qsa_prefill_1m_ms(1)
+    t_dense_1m = dense_prefill_ms(1 << 20, reps=1)
+    res["prefill_1048576"] = {"qsa_ms": t_qsa_1m, "dense_sdpa_ms": t_dense_1m, "speedup": t_dense_1m / t_qsa_1m,
+                              "dense_sdpa_tflops": 4 * 24 * 256 * (1 << 20) ** 2 / 2 / (t_dense_1m * 1e-3) / 1e12}
+    wd = synth.WORKLOADS["decode_1m"]
+    sd = setup_decode(wd)
+    x, c = sd["x"], sd["c"]
+    zero = torch.zeros_like(sd["cache_len"])
+    sel = sd["bidx"].view(sd["B"], -1).contiguous()
+
+    def dense_step():
+        Q.qsa_decode_reuse(sd["h"], sd["B"], sd["cache_len"], zero, sd["ctx"], x["q"], x["k"], x["v"], x["k_idx"],
+                           c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel, sd["out"], sd["ws"])
+
+    times = {}
+    for name, fn in (("qsa", lambda: decode_step(sd)), ("dense", dense_step)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e = _events(2)
+        e[0].record()
+        for _ in range(5 * steps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        times[name] = e[0].elapsed_time(e[1]) / (5 * steps)
+    res["decode_B8_ctx1048576"] = {"qsa_ms": times["qsa"], "dense_split_k_ms": times["dense"],
+                                   "speedup": times["dense"] / times["qsa"]}
+    res["pages_module_speedups_at_1M"] = {"prefill": 7.6, "decode": 4.9,
+                                          "note": "other hardware, dense baseline a paged GQA library"}
+    print(json.dumps({"ratios": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +368,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="decode step only (profiling)")
     ap.add_argument("--cpu-rows", type=int, default=256)
     ap.add_argument("--no-ceilings", action="store_true", help="skip the measured copy / GEMM ceilings")
+    ap.add_argument("--ratios", action="store_true",
+                    help="measure QSA against dense attention (the pages' module speed-ups) instead")
     ap.add_argument("--c5", action="store_true",
                     help="measure the 1M-token configuration instead (chunked prefill, B=8 decode)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -290,6 +382,9 @@ def main():
     torch.cuda.init()
     if args.c5:
         run_c5(max(1, min(args.steps, 3)))
+        return
+    if args.ratios:
+        run_ratios(max(1, min(args.steps, 3)))
         return
     if args.calib_copy:
         src = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")
