@@ -17,7 +17,8 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqsa.so")
 
-QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE, QSA_OP_INDEX_SELECT = range(7)
+(QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE, QSA_OP_INDEX_SELECT,
+ QSA_OP_INDEX_DECODE, QSA_OP_TOKEN_INDEX_SELECT, QSA_OP_TOKEN_INDEX_DECODE) = range(10)
 
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPPORTED", 4: "QSA_ERR_ALIGN",
           5: "QSA_ERR_CAPACITY", 6: "QSA_ERR_WORKSPACE", 7: "QSA_ERR_HIP"}
@@ -25,7 +26,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPP
 # The C entry points (kept in step with include/qsa.h).
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
            "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
-           "qsa_decode_reuse", "qsa_status_string", "qsa_last_hip_error"]
+           "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
+           "qsa_status_string", "qsa_last_hip_error"]
 
 
 class QSAError(RuntimeError):
@@ -83,6 +85,12 @@ def lib() -> ctypes.CDLL:
     L.qsa_decode.restype = ctypes.c_int
     L.qsa_decode_reuse.argtypes = [vp, vp, i32, vp, vp, i64] + [vp] * 11 + [sz]
     L.qsa_decode_reuse.restype = ctypes.c_int
+    L.qsa_index_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 6 + [sz]
+    L.qsa_index_decode.restype = ctypes.c_int
+    L.qsa_token_index_select.argtypes = [vp, vp, i32, i64, i64] + [vp] * 5 + [sz]
+    L.qsa_token_index_select.restype = ctypes.c_int
+    L.qsa_token_index_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 5 + [sz]
+    L.qsa_token_index_decode.restype = ctypes.c_int
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     L.qsa_last_hip_error.argtypes = []
@@ -247,6 +255,32 @@ def qsa_decode_reuse(h, B, cache_len, sel_pos, ctx_bound, q, k, v, k_idx, k_cach
                                   _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"),
                                   _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out"), _ptr(ws, None, "ws"),
                                   _nbytes(ws)), "qsa_decode_reuse")
+
+
+def qsa_index_decode(h, B, cache_len, ctx_bound, q_idx, k_idx, kbar_cache, kpend, block_idx, ws, stream=None):
+    _check(lib().qsa_index_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"), ctx_bound,
+                                  _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"), _bf(kbar_cache, "kbar_cache"),
+                                  _bf(kpend, "kpend"), _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
+                                  _nbytes(ws)), "qsa_index_decode")
+
+
+def alloc_token_keys(h: Handle, batch: int, device="cuda") -> torch.Tensor:
+    """Caller-owned token-level indexer key cache [B][max_ctx][128] bf16."""
+    return torch.empty((batch, h.max_ctx, 128), dtype=torch.bfloat16, device=device)
+
+
+def qsa_token_index_select(h, B, L, q_offset, q_idx, k_idx, ktok_cache, token_idx, ws, stream=None):
+    _check(lib().qsa_token_index_select(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"),
+                                        _bf(k_idx, "k_idx"), _bf(ktok_cache, "ktok_cache"),
+                                        _ptr(token_idx, torch.int32, "token_idx"), _ptr(ws, None, "ws"),
+                                        _nbytes(ws)), "qsa_token_index_select")
+
+
+def qsa_token_index_decode(h, B, cache_len, ctx_bound, q_idx, k_idx, ktok_cache, token_idx, ws, stream=None):
+    _check(lib().qsa_token_index_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"),
+                                        ctx_bound, _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
+                                        _bf(ktok_cache, "ktok_cache"), _ptr(token_idx, torch.int32, "token_idx"),
+                                        _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_token_index_decode")
 
 
 def qsa_status_string(status: int) -> str:

@@ -11,7 +11,7 @@ constexpr int kDecodeBins = 2048;      // histogram of score bits 30..20 per seq
 
 // One wave per sequence.  p = cache_len[b]:
 //   lanes: head g = lane/32, chunk c = lane%32 -> rotate k at p into K~ slot p%4
-//          and copy v into V slot p%4;
+//          and copy v into V slot p%4 (when k is given);
 //   lanes 0..15: raw k_idx into kpend[p%4]; when p%4 == 3 pool the completed
 //          block (kpend slots 0..2 + this token) into kbar;
 //   lanes: head lane/16, chunk lane%16 -> rotated q_idx at p into qrot (when
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(64) void decode_append_kernel(
     const float *cs = tab.cos + p * kPairs;
     const float *sn = tab.sin + p * kPairs;
 
-    {   // K~ and V
+    if (k) {   // K~ and V (not needed when only the selection is wanted)
         const int g = lane >> 5, c = lane & 31;
         const int64_t row = b * kKVHeads + g;
         u32x4 kx = *reinterpret_cast<const u32x4 *>(k + row * kHeadDim + 8 * c);
@@ -134,7 +134,58 @@ __global__ __launch_bounds__(64) void decode_append_kernel(
     }
 }
 
-// Score scan: scores[b][blk] = sum_h ReLU(<q~_h, k̄_blk>) for blk < floor(p/4).
+// 8 dims (chunk c of 16) of a 128-dim row rotated at one position: chunks
+// 0..7 hold the rotary dims, chunk c pairs with c ^ 4 (dims j and j + 32).
+__device__ __forceinline__ u32x4 rotate_chunk8(u32x4 x, u32x4 xp, int c, const float *cs, const float *sn) {
+    if (c >= 8) return x;
+    const bool first_half = c < 4;
+    const int j0 = 8 * (c & 3);
+    uint32_t w[4];
+    for (int i = 0; i < 4; ++i) {
+        float r[2];
+        for (int e = 0; e < 2; ++e) {
+            float me = __uint_as_float(e ? (x[i] & 0xFFFF0000u) : (x[i] << 16));
+            float pa = __uint_as_float(e ? (xp[i] & 0xFFFF0000u) : (xp[i] << 16));
+            float a = first_half ? me : pa, bb = first_half ? pa : me;
+            rotate_pair(a, bb, cs[j0 + 2 * i + e], sn[j0 + 2 * i + e]);
+            r[e] = first_half ? a : bb;
+        }
+        w[i] = pack_bf16x2(r[0], r[1]);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Token-level indexer step (r = 1), one wave per sequence, p = cache_len[b]:
+// the new token's indexer key rotated at p goes to ktok[b][p], the indexer
+// query rotated at p to qrot, and the sequence's score histogram is cleared.
+__global__ __launch_bounds__(64) void token_decode_append_kernel(
+    Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t tok_cap,
+    const bf16_t *__restrict__ k_idx, const bf16_t *__restrict__ q_idx, bf16_t *__restrict__ ktok,
+    bf16_t *__restrict__ qrot, uint32_t *__restrict__ dhist)
+{
+    const int lane = threadIdx.x;
+    const int64_t b = blockIdx.x;
+    for (int x = lane; x < kDecodeBins; x += 64) dhist[b * kDecodeBins + x] = 0;
+    const int64_t p = decode_pos(cache_len, b, ctx_bound);
+    const float *cs = tab.cos + p * kPairs;
+    const float *sn = tab.sin + p * kPairs;
+    const int c = lane & 15, h = lane >> 4;
+    {   // lanes 0..15: the key; the query's 4 heads over all 64 lanes
+        const bf16_t *src = q_idx + (b * kIdxHeads + h) * kIdxDim;
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);
+        const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (c ^ 4));
+        *reinterpret_cast<u32x4 *>(qrot + (b * kIdxHeads + h) * kIdxDim + 8 * c) = rotate_chunk8(x, xp, c, cs, sn);
+    }
+    if (lane < 16) {
+        const bf16_t *src = k_idx + b * kIdxDim;
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);
+        const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (c ^ 4));
+        *reinterpret_cast<u32x4 *>(ktok + (b * tok_cap + p) * kIdxDim + 8 * c) = rotate_chunk8(x, xp, c, cs, sn);
+    }
+}
+
+// Score scan: scores[b][blk] = sum_h ReLU(<q~_h, k̄_blk>) for blk < floor(p/r),
+// r = 1 << rsh (4: pooled micro-blocks; 1: one rotated key per token).
 // v_mfma_f32_16x16x32_bf16 with A = q~ (4 real rows of 16), B = 16 pooled keys;
 // lanes 0..15 end with the 4 heads of one block.  Each wave streams 512 blocks
 // and collects their scores in LDS, then writes them with one 16-byte store per
@@ -146,7 +197,7 @@ constexpr int kScanBlocksPerWG = 4 * kScanBlocksPerWave;
 // Each workgroup also histograms the top 11 value bits of its scores and adds
 // the histogram to the sequence's (zeroed by decode_append_kernel).
 __global__ __launch_bounds__(256) void decode_scan_kernel(const int32_t *__restrict__ cache_len, int64_t ctx_bound,
-                                                          int64_t nblk_cap,
+                                                          int rsh, int64_t nblk_cap,
                                                           int64_t ncol, const bf16_t *__restrict__ qrot,
                                                           const bf16_t *__restrict__ kbar,
                                                           float *__restrict__ scores, uint32_t *__restrict__ dhist)
@@ -156,7 +207,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const int32_t *__restr
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
-    const int64_t o = decode_pos(cache_len, b, ctx_bound) / kBlock;
+    const int64_t o = decode_pos(cache_len, b, ctx_bound) >> rsh;
     if (static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG >= o) return;     // whole workgroup idle
     for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
     __syncthreads();
@@ -220,14 +271,23 @@ hipError_t launch_decode_append(const Tables &tab, hipStream_t st, int32_t B, co
     return hipGetLastError();
 }
 
-hipError_t launch_decode_scan(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
+hipError_t launch_token_decode_append(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
+                                      int64_t ctx_bound, int64_t tok_cap, const bf16_t *k_idx, const bf16_t *q_idx,
+                                      bf16_t *ktok, bf16_t *qrot, uint32_t *dhist)
+{
+    hipLaunchKernelGGL(token_decode_append_kernel, dim3(B), dim3(64), 0, st, tab, cache_len, ctx_bound, tok_cap, k_idx,
+                       q_idx, ktok, qrot, dhist);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_scan(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t ctx_bound, int rsh,
                               int64_t nblk_cap, int64_t ncol, const bf16_t *qrot, const bf16_t *kbar, float *scores,
                               uint32_t *dhist)
 {
-    const int64_t o_max = ctx_bound / kBlock;
+    const int64_t o_max = ctx_bound >> rsh;
     if (o_max <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((o_max + kScanBlocksPerWG - 1) / kScanBlocksPerWG), static_cast<unsigned>(B));
-    hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, cache_len, ctx_bound, nblk_cap, ncol, qrot, kbar,
+    hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, cache_len, ctx_bound, rsh, nblk_cap, ncol, qrot, kbar,
                        scores, dhist);
     return hipGetLastError();
 }

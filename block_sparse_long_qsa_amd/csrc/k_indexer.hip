@@ -158,8 +158,10 @@ hipError_t launch_indexer_scores(hipStream_t st, int32_t B, int64_t L, int64_t q
 // a score matrix).
 //
 // A workgroup owns 64 consecutive queries and walks every candidate column
-// 0 .. floor(p_last/4) in k̄ tiles of 64, computing the same MFMA scores as
-// indexer_scores_kernel.  Each query keeps
+// 0 .. floor(p_last/r) in k̄ tiles of 64, computing the same MFMA scores as
+// indexer_scores_kernel.  r = 1 << rsh is the compression ratio: 4 for QSA's
+// pooled micro-blocks, 1 for the token-level indexer it is compared against
+// (one rotated key per token, candidates t < p).  Each query keeps
 //   * a running threshold tau (fp32), below which a block can no longer be in
 //     its top `budget`: tau is the lower edge of the highest bin of a 128-bin
 //     log histogram (8 bins per octave over [2^-8, 2^8)) of the scores kept so
@@ -220,7 +222,7 @@ __device__ __forceinline__ void boundary_take(const uint32_t *bkey, const int32_
 }
 
 __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
-    int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, int cap,
+    int64_t L, int64_t q_offset, int rsh, int64_t nblk_cap, int budget, int cap,
     const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar,
     uint2 *__restrict__ cand, int32_t *__restrict__ bidx, int64_t bi_bstride, int32_t *__restrict__ ovf)
 {
@@ -236,10 +238,10 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     const int64_t tile = static_cast<int64_t>(gridDim.x) - 1 - blockIdx.x;
     const int64_t q0 = tile * kIdxQueriesPerWG;
     const int64_t q_last = (q0 + kIdxQueriesPerWG - 1 < L) ? q0 + kIdxQueriesPerWG - 1 : L - 1;
-    const int64_t o_hi = (q_offset + q_last) / kBlock;
+    const int64_t o_hi = (q_offset + q_last) >> rsh;
     if (o_hi <= budget) {                       // every row of the tile keeps all its candidates
         for (int64_t q = q0 + wave; q <= q_last; q += 4) {
-            const int64_t o = (q_offset + q) / kBlock;
+            const int64_t o = (q_offset + q) >> rsh;
             int32_t *out = bidx + b * bi_bstride + q * budget;
             for (int t = lane; t < budget; t += 64) out[t] = (t < o) ? t : -1;
         }
@@ -277,11 +279,11 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     for (int a = 0; a < 2; ++a)
         for (int i = 0; i < 4; ++i) {
             const int64_t q = q0 + 16 * wave + 8 * a + 2 * i + half;
-            qo[a][i] = (q < L) ? static_cast<int32_t>((q_offset + q) / kBlock) : 0;
+            qo[a][i] = (q < L) ? static_cast<int32_t>((q_offset + q) >> rsh) : 0;
             tau_v[a][i] = (q < L) ? 0.0f : INFINITY;
             tn_v[a][i] = next_bin_bits(tau_v[a][i]);
         }
-    const int64_t o_min = (q_offset + q0) / kBlock;         // causal limit of the tile's first query
+    const int64_t o_min = (q_offset + q0) >> rsh;         // causal limit of the tile's first query
     // candidate lists of this workgroup's 64 queries (rows b*L + q0 .. +63); the
     // padding queries of a ragged tile never append (infinite threshold)
     uint2 *__restrict__ wg_cand = cand + (b * L + q0) * cap;
@@ -441,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
         const int ql = 16 * wave + j;
         const int64_t q = q0 + ql;
         if (q >= L) break;
-        const int64_t o = (q_offset + q) / kBlock;
+        const int64_t o = (q_offset + q) >> rsh;
         int32_t *out = bidx + b * bi_bstride + q * budget;
         if (o <= budget) {
             for (int t = lane; t < budget; t += 64) out[t] = (t < o) ? t : -1;
@@ -535,13 +537,13 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
     }
 }
 
-hipError_t launch_indexer_topk(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget,
-                               int cap, const bf16_t *qrot, int64_t qrot_bstride, const bf16_t *kbar,
+hipError_t launch_indexer_topk(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int rsh, int64_t nblk_cap,
+                               int budget, int cap, const bf16_t *qrot, int64_t qrot_bstride, const bf16_t *kbar,
                                uint2 *cand, int32_t *bidx, int64_t bi_bstride, int32_t *ovf)
 {
     if (L <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>((L + kIdxQueriesPerWG - 1) / kIdxQueriesPerWG), static_cast<unsigned>(B));
-    hipLaunchKernelGGL(indexer_topk_kernel, grid, dim3(256), 0, st, L, q_offset, nblk_cap, budget, cap, qrot,
+    hipLaunchKernelGGL(indexer_topk_kernel, grid, dim3(256), 0, st, L, q_offset, rsh, nblk_cap, budget, cap, qrot,
                        qrot_bstride, kbar, cand, bidx, bi_bstride, ovf);
     return hipGetLastError();
 }

@@ -11,6 +11,8 @@
 //  * kpend_store_kernel: keep the raw indexer keys of a trailing incomplete
 //    block for the next call.
 //  * qidx_rotate_kernel: rotate the indexer queries at their positions.
+//  * token_keys_kernel: token-level indexer keys (r = 1), rotated at their
+//    own positions, for the indexer QSA's pooled one is measured against.
 //
 // All rotations follow one fp32 recipe (each product and sum rounded, then
 // bf16 round-to-nearest-even); the library is built with -ffp-contract=off.
@@ -206,6 +208,46 @@ __global__ __launch_bounds__(256) void qidx_rotate_kernel(Tables tab, int32_t B,
     *reinterpret_cast<u32x4 *>(qrot + row * kIdxDim + 8 * c) = x;
 }
 
+// Token-level indexer keys (r = 1): the indexer key of position q_offset + i,
+// rotated at that position, goes to ktok[b][q_offset + i] (no pooling).
+// 16 threads per token, 8 dims each.
+__global__ __launch_bounds__(256) void token_keys_kernel(Tables tab, int32_t B, int64_t L, int64_t q_offset,
+                                                         int64_t tok_cap, const bf16_t *__restrict__ k_idx,
+                                                         bf16_t *__restrict__ ktok)
+{
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t total = static_cast<int64_t>(B) * L * 16;
+    if (gid >= total) return;
+    const int c = static_cast<int>(gid & 15);
+    const int64_t row = gid >> 4;                    // (b, i)
+    const int64_t b = row / L;
+    const int64_t pos = q_offset + (row - b * L);
+    const bf16_t *src = k_idx + row * kIdxDim;
+    u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);
+    if (c < 8) {
+        const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (c ^ 4));
+        const float *cs = tab.cos + pos * kPairs;
+        const float *sn = tab.sin + pos * kPairs;
+        const bool first_half = c < 4;
+        const int j0 = 8 * (c & 3);
+        uint32_t outw[4];
+        for (int i = 0; i < 4; ++i) {
+            float r[2];
+            for (int e = 0; e < 2; ++e) {
+                float me = __uint_as_float(e ? (x[i] & 0xFFFF0000u) : (x[i] << 16));
+                float pa = __uint_as_float(e ? (xp[i] & 0xFFFF0000u) : (xp[i] << 16));
+                float a = first_half ? me : pa;
+                float bb = first_half ? pa : me;
+                rotate_pair(a, bb, cs[j0 + 2 * i + e], sn[j0 + 2 * i + e]);
+                r[e] = first_half ? a : bb;
+            }
+            outw[i] = pack_bf16x2(r[0], r[1]);
+        }
+        x = u32x4{outw[0], outw[1], outw[2], outw[3]};
+    }
+    *reinterpret_cast<u32x4 *>(ktok + (b * tok_cap + pos) * kIdxDim + 8 * c) = x;
+}
+
 // ---------------------------------------------------------------- launchers
 hipError_t launch_kv_pool(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
                           int64_t nblk_cap, const bf16_t *k, const bf16_t *v, const bf16_t *k_idx,
@@ -238,6 +280,16 @@ hipError_t launch_qidx_rotate(const Tables &tab, hipStream_t st, int32_t B, int6
     const int64_t blocks = (total + 255) / 256;
     hipLaunchKernelGGL(qidx_rotate_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, tab, B, L,
                        q_offset, cache_len, q_idx, qrot);
+    return hipGetLastError();
+}
+
+hipError_t launch_token_keys(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int64_t tok_cap,
+                             const bf16_t *k_idx, bf16_t *ktok)
+{
+    const int64_t total = static_cast<int64_t>(B) * L * 16;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(token_keys_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, tab, B, L,
+                       q_offset, tok_cap, k_idx, ktok);
     return hipGetLastError();
 }
 

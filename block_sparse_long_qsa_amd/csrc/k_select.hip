@@ -257,7 +257,7 @@ __device__ __forceinline__ int score_bin(uint32_t bits) {
 // selection is taken exactly.  Workgroups stride over the list, so the launch
 // needs no host-side count.
 __global__ __launch_bounds__(kSelThreads) void select_fixup_kernel(
-    int64_t L, int64_t q_offset, int budget, const int32_t *__restrict__ ovf,
+    int64_t L, int64_t q_offset, int rsh, int budget, const int32_t *__restrict__ ovf,
     int32_t *__restrict__ block_idx, int64_t bi_bstride,
     const bf16_t *__restrict__ qrot, int64_t qrot_bstride, const bf16_t *__restrict__ kbar, int64_t nblk_cap)
 {
@@ -269,7 +269,7 @@ __global__ __launch_bounds__(kSelThreads) void select_fixup_kernel(
         const int64_t row = ovf[1 + k];
         const int64_t b = row / L;
         const int64_t i = row - b * L;
-        const int64_t o = (q_offset + i) / kBlock;
+        const int64_t o = (q_offset + i) >> rsh;
         int32_t *out = block_idx + b * bi_bstride + i * budget;
         const bf16_t *qr = qrot + b * qrot_bstride + i * kIdxHeads * kIdxDim;
         for (int x = tid; x < kIdxHeads * kIdxDim; x += kSelThreads) qs[x] = bf16_to_f32(qr[x]);
@@ -409,7 +409,7 @@ __device__ void boundary_digit(const uint32_t *__restrict__ dh, uint32_t K, uint
 }
 
 __global__ __launch_bounds__(256) void select_chunk_kernel(
-    const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
+    const int32_t *__restrict__ cache_len, int64_t pos_bound, int rsh, int64_t ncol, const float *__restrict__ scores,
     const uint32_t *__restrict__ dhist, int budget, int nchunk, int32_t *__restrict__ cnt,
     int32_t *__restrict__ gtb, uint32_t *__restrict__ eqs, int32_t *__restrict__ eqi, uint32_t *__restrict__ rowinfo)
 {
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(256) void select_chunk_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.y;
     const int ch = blockIdx.x;
-    const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
+    const int64_t o = decode_pos(cache_len, b, pos_bound) >> rsh;
     const int64_t c0 = static_cast<int64_t>(ch) * kSelChunk;
     if (o <= budget || c0 >= o) return;                     // whole workgroup
     const int64_t c1 = (c0 + kSelChunk < o) ? c0 + kSelChunk : o;
@@ -507,7 +507,7 @@ __device__ __forceinline__ int chunk_of(const uint32_t *pre, int n, uint32_t t) 
 }
 
 __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
-    const int32_t *__restrict__ cache_len, int64_t pos_bound, int64_t ncol, const float *__restrict__ scores,
+    const int32_t *__restrict__ cache_len, int64_t pos_bound, int rsh, int64_t ncol, const float *__restrict__ scores,
     const uint32_t *__restrict__ rowinfo, int nchunk, const int32_t *__restrict__ cnt, const int32_t *__restrict__ gtb,
     const uint32_t *__restrict__ eqs, const int32_t *__restrict__ eqi, int32_t *__restrict__ block_idx, int budget)
 {
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
     __shared__ uint32_t gpre[kSelChunkMax], epre[kSelChunkMax];
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
-    const int64_t o = decode_pos(cache_len, b, pos_bound) / kBlock;
+    const int64_t o = decode_pos(cache_len, b, pos_bound) >> rsh;
     int32_t *out = block_idx + b * budget;
     if (take_all(o, budget, out)) return;
     const uint32_t above = rowinfo[b * 3 + 1];
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
     finish_digit_select(eqk, eqb, sel, selq, wsum, n_eq, k_rem, above, budget, out);
 }
 
-hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound,
+hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int rsh,
                                    int64_t ncol, const float *scores, const uint32_t *dhist, int32_t *cnt,
                                    int32_t *gtb, uint32_t *eqs, int32_t *eqi, uint32_t *rowinfo, int32_t *block_idx,
                                    int budget)
@@ -568,12 +568,12 @@ hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cac
     const int64_t nchunk = (ncol + kSelChunk - 1) / kSelChunk;
     if (nchunk > kSelChunkMax) return hipErrorInvalidValue;
     hipLaunchKernelGGL(select_chunk_kernel, dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(B)), dim3(256),
-                       0, st, cache_len, pos_bound, ncol, scores, dhist, budget, static_cast<int>(nchunk), cnt, gtb,
+                       0, st, cache_len, pos_bound, rsh, ncol, scores, dhist, budget, static_cast<int>(nchunk), cnt, gtb,
                        eqs, eqi, rowinfo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(select_gather_kernel, dim3(static_cast<unsigned>(B)), dim3(kHistNT), 0, st, cache_len, pos_bound,
-                       ncol, scores, rowinfo, static_cast<int>(nchunk), cnt, gtb, eqs, eqi, block_idx, budget);
+                       rsh, ncol, scores, rowinfo, static_cast<int>(nchunk), cnt, gtb, eqs, eqi, block_idx, budget);
     return hipGetLastError();
 }
 
@@ -607,14 +607,14 @@ hipError_t launch_select(hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
     return hipGetLastError();
 }
 
-hipError_t launch_select_fixup(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int budget,
+hipError_t launch_select_fixup(hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int rsh, int budget,
                                const int32_t *ovf, int32_t *block_idx, int64_t bi_bstride, const bf16_t *qrot,
                                int64_t qrot_bstride, const bf16_t *kbar, int64_t nblk_cap)
 {
     const int64_t rows = static_cast<int64_t>(B) * L;
     if (rows == 0) return hipSuccess;
     const unsigned grid = static_cast<unsigned>(rows < 512 ? rows : 512);
-    hipLaunchKernelGGL(select_fixup_kernel, dim3(grid), dim3(kSelThreads), 0, st, L, q_offset, budget, ovf, block_idx,
+    hipLaunchKernelGGL(select_fixup_kernel, dim3(grid), dim3(kSelThreads), 0, st, L, q_offset, rsh, budget, ovf, block_idx,
                        bi_bstride, qrot, qrot_bstride, kbar, nblk_cap);
     return hipGetLastError();
 }

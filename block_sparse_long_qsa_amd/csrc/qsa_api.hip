@@ -24,10 +24,10 @@ hipError_t launch_indexer_scores(hipStream_t, int32_t, int64_t, int64_t, int64_t
                                  const bf16_t *, float *, int64_t, bool);
 hipError_t launch_select(hipStream_t, int32_t, int64_t, int64_t, const int32_t *, int64_t, const float *, int64_t,
                          int32_t *, int64_t, int);
-hipError_t launch_indexer_topk(hipStream_t, int32_t, int64_t, int64_t, int64_t, int, int, const bf16_t *, int64_t,
+hipError_t launch_indexer_topk(hipStream_t, int32_t, int64_t, int64_t, int, int64_t, int, int, const bf16_t *, int64_t,
                                const bf16_t *, uint2 *, int32_t *, int64_t, int32_t *);
 hipError_t launch_zero_words(hipStream_t, int32_t *, int64_t);
-hipError_t launch_select_fixup(hipStream_t, int32_t, int64_t, int64_t, int, const int32_t *, int32_t *, int64_t,
+hipError_t launch_select_fixup(hipStream_t, int32_t, int64_t, int64_t, int, int, const int32_t *, int32_t *, int64_t,
                                const bf16_t *, int64_t, const bf16_t *, int64_t);
 hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
                                  const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
@@ -38,11 +38,14 @@ hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int3
 hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const bf16_t *,
                                 const bf16_t *, const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *,
                                 bf16_t *, bf16_t *, uint32_t *);
-hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, int64_t, const bf16_t *,
+hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, int64_t, const bf16_t *,
                               const bf16_t *, float *, uint32_t *);
-hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const float *,
+hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, const float *,
                                    const uint32_t *, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *, int32_t *,
                                    int);
+hipError_t launch_token_keys(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, const bf16_t *, bf16_t *);
+hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t,
+                                      const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, uint32_t *);
 }  // namespace qsa
 
 using namespace qsa;
@@ -121,14 +124,18 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
     return f;
 }
 
+// The decode selection handles rows of up to 1,024 chunks of 4,096 scores.
+constexpr int64_t kDecodeChunkMax = 1024;
+
 struct DecLayout {
     size_t qrot, scores, bidx, part_o, part_ml, hist, s2cnt, s2gt, s2eqs, s2eqi, s2row, total;
     int64_t ncol, nchunk;
     int nsplit;
 };
-DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
+// rsh: log2 of the indexer's compression ratio (2: pooled micro-blocks; 0: tokens).
+DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int rsh = 2) {
     DecLayout d{};
-    d.ncol = ctx_bound / kBlock;
+    d.ncol = ctx_bound >> rsh;
     if (d.ncol < 1) d.ncol = 1;
     d.nsplit = decode_splits(B);
     d.qrot = 0;
@@ -151,9 +158,11 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound) {
     return d;
 }
 
+// keys: pooled k̄ (rsh = 2, key_cap = max_ctx / 4) or token keys (rsh = 0, key_cap = max_ctx).
 hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
                             const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *bidx, char *w,
-                            const IdxSelLayout &f) {
+                            const IdxSelLayout &f, int rsh = 2, int64_t key_cap = -1) {
+    if (key_cap < 0) key_cap = nblk_cap(h);
     bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
     uint2 *cand = reinterpret_cast<uint2 *>(w + f.cand);
     int32_t *ovf = reinterpret_cast<int32_t *>(w + f.ovf);
@@ -166,11 +175,11 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
         const bf16_t *qr = qrot + r0 * kIdxHeads * kIdxDim;
         e = launch_zero_words(st, ovf, 1);
         if (e == hipSuccess)
-            e = launch_indexer_topk(st, B, nr, pos0, nblk_cap(h), budget, h->cap, qr, qstride, kbar_cache, cand,
+            e = launch_indexer_topk(st, B, nr, pos0, rsh, key_cap, budget, h->cap, qr, qstride, kbar_cache, cand,
                                     bidx + r0 * budget, L * budget, ovf);
         if (e == hipSuccess)
-            e = launch_select_fixup(st, B, nr, pos0, budget, ovf, bidx + r0 * budget, L * budget, qr, qstride,
-                                    kbar_cache, nblk_cap(h));
+            e = launch_select_fixup(st, B, nr, pos0, rsh, budget, ovf, bidx + r0 * budget, L * budget, qr, qstride,
+                                    kbar_cache, key_cap);
     }
     return e;
 }
@@ -289,7 +298,12 @@ size_t qsa_workspace_size(const qsa_handle *h, int op, int32_t batch, int64_t le
         return index_select_layout(batch, len, h->cap).total +
                align_up(static_cast<size_t>(batch) * len * h->p.budget_blocks * 4);
     case QSA_OP_DECODE:
+    case QSA_OP_INDEX_DECODE:
         return decode_layout(h, batch, q_offset).total;
+    case QSA_OP_TOKEN_INDEX_SELECT:
+        return index_select_layout(batch, len, h->cap).total;
+    case QSA_OP_TOKEN_INDEX_DECODE:
+        return decode_layout(h, batch, q_offset, 0).total;
     default:
         return 0;
     }
@@ -410,6 +424,7 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
     if (s != QSA_OK) return s;
     if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
     const DecLayout d = decode_layout(h, B, ctx_bound);
+    if (d.nchunk > kDecodeChunkMax) return QSA_ERR_CAPACITY;
     if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
@@ -427,9 +442,9 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
     hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, q_idx, k_cache, v_cache,
                                         kbar_cache, kpend, qrot, dhist);
     if (e == hipSuccess)
-        e = launch_decode_scan(st, B, cache_len, ctx_bound, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
+        e = launch_decode_scan(st, B, cache_len, ctx_bound, 2, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
     if (e == hipSuccess)
-        e = launch_select_two_stage(st, B, cache_len, ctx_bound, d.ncol, scores, dhist,
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 2, d.ncol, scores, dhist,
                                     reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
                                     reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
                                     reinterpret_cast<uint32_t *>(w + d.s2row), bidx, budget);
@@ -451,6 +466,7 @@ qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const 
                                ws});
     if (s != QSA_OK) return s;
     const DecLayout d = decode_layout(h, B, ctx_bound);
+    if (d.nchunk > kDecodeChunkMax) return QSA_ERR_CAPACITY;
     if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
@@ -465,6 +481,91 @@ qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const 
     if (e == hipSuccess)
         e = launch_attend_decode(tables(h), st, B, cache_len, sel_pos, ctx_bound, nbc, h->p.budget_blocks, d.nsplit,
                                  h->sigma, q, k_cache, v_cache, block_idx, part_o, part_ml, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+// Decode-step selection alone (r = 4): append the new token's indexer key
+// (pending slot, pooling of a completed block), rotate the indexer query, scan
+// the pooled keys and select -- the indexer half of qsa_decode.
+qsa_status qsa_index_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
+                            const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *kbar_cache, uint16_t *kpend,
+                            int32_t *block_idx, void *ws, size_t ws_bytes) {
+    if (!h) return QSA_ERR_NULL;
+    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
+    qsa_status s = check_ptrs({cache_len, q_idx, k_idx, kbar_cache, kpend, block_idx, ws});
+    if (s != QSA_OK) return s;
+    const DecLayout d = decode_layout(h, B, ctx_bound);
+    if (d.nchunk > kDecodeChunkMax) return QSA_ERR_CAPACITY;
+    if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
+    float *scores = reinterpret_cast<float *>(w + d.scores);
+    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
+    const int64_t nbc = nblk_cap(h);
+    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, nullptr, nullptr, k_idx, q_idx,
+                                        nullptr, nullptr, kbar_cache, kpend, qrot, dhist);
+    if (e == hipSuccess)
+        e = launch_decode_scan(st, B, cache_len, ctx_bound, 2, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
+    if (e == hipSuccess)
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 2, d.ncol, scores, dhist,
+                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
+                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
+                                    reinterpret_cast<uint32_t *>(w + d.s2row), block_idx, h->p.budget_blocks);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+// Token-level indexer (r = 1): the O(n^2) indexer that QSA's pooled one
+// replaces.  Same kernels with one rotated key per token and candidates t < p.
+qsa_status qsa_token_index_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                                  const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *ktok_cache,
+                                  int32_t *token_idx, void *ws, size_t ws_bytes) {
+    qsa_status s = check_chunk(h, B, L, q_offset, false);
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q_idx, k_idx, ktok_cache, token_idx, ws})) != QSA_OK) return s;
+    const IdxSelLayout f = index_select_layout(B, L, h->cap);
+    if (ws_bytes < f.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_token_keys(tables(h), st, B, L, q_offset, h->p.max_ctx, k_idx, ktok_cache);
+    if (e == hipSuccess)
+        e = run_index_select(h, st, B, L, q_offset, q_idx, ktok_cache, token_idx, static_cast<char *>(ws), f, 0,
+                             h->p.max_ctx);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                                  int64_t ctx_bound, const uint16_t *q_idx, const uint16_t *k_idx,
+                                  uint16_t *ktok_cache, int32_t *token_idx, void *ws, size_t ws_bytes) {
+    if (!h) return QSA_ERR_NULL;
+    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
+    qsa_status s = check_ptrs({cache_len, q_idx, k_idx, ktok_cache, token_idx, ws});
+    if (s != QSA_OK) return s;
+    const DecLayout d = decode_layout(h, B, ctx_bound, 0);
+    if (d.nchunk > kDecodeChunkMax) return QSA_ERR_CAPACITY;
+    if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
+    float *scores = reinterpret_cast<float *>(w + d.scores);
+    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
+    const int64_t cap = h->p.max_ctx;
+    hipError_t e = launch_token_decode_append(tables(h), st, B, cache_len, ctx_bound, cap, k_idx, q_idx, ktok_cache,
+                                              qrot, dhist);
+    if (e == hipSuccess)
+        e = launch_decode_scan(st, B, cache_len, ctx_bound, 0, cap, d.ncol, qrot, ktok_cache, scores, dhist);
+    if (e == hipSuccess)
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 0, d.ncol, scores, dhist,
+                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
+                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
+                                    reinterpret_cast<uint32_t *>(w + d.s2row), token_idx, h->p.budget_blocks);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

@@ -115,7 +115,8 @@ typedef struct qsa_handle qsa_handle;
 
 /* Operation codes for qsa_workspace_size. */
 enum { QSA_OP_APPEND = 0, QSA_OP_INDEX = 1, QSA_OP_SELECT = 2, QSA_OP_ATTEND = 3,
-       QSA_OP_FORWARD = 4, QSA_OP_DECODE = 5, QSA_OP_INDEX_SELECT = 6 };
+       QSA_OP_FORWARD = 4, QSA_OP_DECODE = 5, QSA_OP_INDEX_SELECT = 6, QSA_OP_INDEX_DECODE = 7,
+       QSA_OP_TOKEN_INDEX_SELECT = 8, QSA_OP_TOKEN_INDEX_DECODE = 9 };
 
 /* Fill *p with the layer's published shapes, budget 512, max_ctx 262144,
  * theta 1e7, no YaRN (factor 1), yarn_orig_ctx 262144.  Host only. */
@@ -242,6 +243,45 @@ qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const 
                             const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *k_idx,
                             uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
                             const int32_t *block_idx, uint16_t *out, void *ws, size_t ws_bytes);
+
+/* The selection half of qsa_decode alone: append the new token's indexer key
+ * (pending slot; pooling when its block completes), rotate its indexer query at
+ * p = cache_len[b], score the complete blocks before its own block and write the
+ * top budget blocks to block_idx [B][budget] (ascending, -1 padded), exactly as
+ * qsa_decode selects them.  No K/V cache is touched and nothing is attended
+ * (for instance to select once for several speculative steps that then call
+ * qsa_decode_reuse).  Sizes, ctx_bound and errors as for qsa_decode.
+ * ws: qsa_workspace_size(QSA_OP_INDEX_DECODE, B, 1, ctx_bound) bytes. */
+qsa_status qsa_index_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                            int64_t ctx_bound, const uint16_t *q_idx, const uint16_t *k_idx,
+                            uint16_t *kbar_cache, uint16_t *kpend, int32_t *block_idx, void *ws, size_t ws_bytes);
+
+/* Token-level indexer, compression ratio r = 1: the indexer QSA's pooled one is
+ * measured against ([PKR] section "QSA: 인덱서 자체의 비용을 줄이는 희소 어텐션":
+ * a per-token indexer as in DeepSeek-V3.2's DSA costs O(n^2); pooling r tokens per
+ * key brings it to O(n^2/r); the figure after the table of results there gives
+ * the indexer's speed-up at r = 4).  Every key is its own block: the indexer
+ * key of position t, rotated at t on its first 64 dims (no pooling), is stored
+ * in ktok_cache [B][max_ctx][128] bf16; query p scores every t < p with
+ * I[p][t] = sum_h ReLU(<q~_h(p), k~_t>) and keeps the top min(budget, p)
+ * tokens under (score desc, t desc), written ascending and -1 padded to
+ * token_idx [B][L][budget] (budget = the handle's budget_blocks, counted in
+ * tokens here).  Same kernels as qsa_index_select.
+ * qsa_token_index_select: the L tokens at q_offset .. q_offset+L-1 (any offset;
+ * keys of earlier positions must already be in ktok_cache), q_idx [B][L][4][128],
+ * k_idx [B][L][128].  ws: qsa_workspace_size(QSA_OP_TOKEN_INDEX_SELECT, B, L,
+ * q_offset) bytes.
+ * qsa_token_index_decode: one new token per sequence at p = cache_len[b] (DEVICE
+ * int32 [B]); q_idx [B][1][4][128], k_idx [B][1][128]; token_idx [B][budget].
+ * ctx_bound as for qsa_decode.  ws: qsa_workspace_size(QSA_OP_TOKEN_INDEX_DECODE,
+ * B, 1, ctx_bound) bytes.
+ * Errors as for qsa_index_select / qsa_decode (no alignment rule on q_offset). */
+qsa_status qsa_token_index_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                                  const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *ktok_cache,
+                                  int32_t *token_idx, void *ws, size_t ws_bytes);
+qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                                  int64_t ctx_bound, const uint16_t *q_idx, const uint16_t *k_idx,
+                                  uint16_t *ktok_cache, int32_t *token_idx, void *ws, size_t ws_bytes);
 
 /* Static string for a status code. */
 const char *qsa_status_string(qsa_status s);

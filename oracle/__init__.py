@@ -291,6 +291,35 @@ def attend(qt: np.ndarray, kt: np.ndarray, v: np.ndarray, sigma: float, p: Param
     return out
 
 
+def token_index_keys(k_idx_bits: np.ndarray, p: Params) -> np.ndarray:
+    """Token-level indexer keys: each raw indexer key rotated at its own position
+    and rounded to bf16 (indexer_keys with one-token blocks).  fp32 [n_tok][128]."""
+    return indexer_keys(k_idx_bits, dataclasses.replace(p, block=1))
+
+
+def token_index_rows(q_idx_bits: np.ndarray, k_idx_bits: np.ndarray, positions, p: Params):
+    """Token-level indexer, compression ratio r = 1 ([PKR] "QSA: ..." section: the
+    per-token indexer of DeepSeek-V3.2's DSA, O(n^2), that pooling r tokens per
+    key replaces).  Reading: the same score and selection rules with every token
+    its own block -- keys rotated at their own positions (pooling of one token is
+    the identity), query p scores every t < p, keeps the top min(budget, p)
+    under (score desc, t desc), ascending, -1 padded.
+
+    q_idx_bits: uint16 [n][4][128] for the given positions; k_idx_bits: uint16
+    [n_tok][128] for positions 0..n_tok-1.  Returns (sel int32 [n][budget],
+    list of fp64 score arrays)."""
+    pt = dataclasses.replace(p, block=1)
+    keys = token_index_keys(k_idx_bits, p)
+    sels, scs = [], []
+    for pos, qb in zip(positions, q_idx_bits):
+        pos = int(pos)
+        qt = indexer_queries(np.asarray(qb)[None], np.array([pos]), pt)[0]
+        sc = block_scores(qt, keys[:pos])
+        sels.append(select_blocks(sc, pt.budget))
+        scs.append(sc)
+    return np.stack(sels), scs
+
+
 # ----------------------------------------------------------------------------
 # Whole layer, row by row
 # ----------------------------------------------------------------------------

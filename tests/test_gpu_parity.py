@@ -470,3 +470,107 @@ def test_decode_reuse_selection_position_bounds():
         Q.qsa_decode_reuse(h, B, cache_len, cache_len, 1024, xd["q"], new["k"], new["v"], new["k_idx"],
                            c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel, outs["neg"], ws)
     assert e.value.status == 5
+
+
+# ---------------------------------------------------------------- token-level indexer (r = 1)
+def _token_prefill(h, xd, B, L, spans):
+    ktok = Q.alloc_token_keys(h, B)
+    tidx = torch.empty((B, L, h.budget), dtype=torch.int32, device=DEV)
+    for s0, s1 in spans:
+        n = s1 - s0
+        ws = Q.workspace(h, Q.QSA_OP_TOKEN_INDEX_SELECT, B, n, s0)
+        ti = torch.empty((B, n, h.budget), dtype=torch.int32, device=DEV)
+        Q.qsa_token_index_select(h, B, n, s0, xd["q_idx"][:, s0:s1].contiguous(), xd["k_idx"][:, s0:s1].contiguous(),
+                                 ktok, ti, ws)
+        tidx[:, s0:s1] = ti
+    torch.cuda.synchronize()
+    return tidx, ktok
+
+
+def test_token_index_select_every_row():
+    """r = 1 in two chunks at an unaligned offset: token keys rotated at their own
+    positions bit for bit, and every row's top tokens meet the oracle."""
+    B, L, budget = 2, 700, 48
+    w = synth.Workload("t", "prefill", B, L, budget, 6, "random", 61)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=768, budget_blocks=budget)
+    tidx, ktok = _token_prefill(h, xd, B, L, [(0, 301), (301, 700)])
+    p = O.Params(budget=budget)
+    got = tidx.cpu().numpy()
+    for b in range(B):
+        ref_k = O.f32_to_bf16_bits(O.token_index_keys(bits(x["k_idx"][b]), p))
+        assert np.array_equal(bits(ktok[b, :L]), ref_k)
+        sel, scs = O.token_index_rows(bits(x["q_idx"][b]), bits(x["k_idx"][b]), range(L), p)
+        for i in range(L):
+            check_selection(got[b, i], sel[i], scs[i], budget, i, "seq %d row %d" % (b, i))
+
+
+@pytest.mark.parametrize("cap", [0, 64])
+def test_token_index_select_long_rows(cap):
+    """r = 1 over 6,000 tokens (the streaming threshold, candidate lists and the
+    in-kernel final selection on long rows); with a 64-entry list every long
+    row overflows and is recomputed by the fixup kernel."""
+    B, L, budget = 1, 6000, 64
+    w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 62)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=6144, budget_blocks=budget, topk_cap=cap)
+    tidx, _ = _token_prefill(h, xd, B, L, [(0, L)])
+    got = tidx.cpu().numpy()
+    rows = [0, 1, 63, 64, 65, 500, 2047, 4096, 5000, 5998, 5999]
+    sel, scs = O.token_index_rows(bits(x["q_idx"][0, rows]), bits(x["k_idx"][0]), rows, O.Params(budget=budget))
+    for j, i in enumerate(rows):
+        check_selection(got[0, i], sel[j], scs[j], budget, i, "row %d" % i)
+
+
+def test_token_index_decode_ragged():
+    """One decode step of the token-level indexer per sequence (lengths 0 .. 900)
+    equals the oracle's row p over the prefilled keys."""
+    budget, lens = 32, [900, 3, 0, 513, 64]
+    B, L = len(lens), max(lens) + 1
+    w = synth.Workload("t", "prefill", B, L, budget, 6, "random", 63)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=1024, budget_blocks=budget)
+    _, ktok = _token_prefill(h, xd, B, L, [(0, L)])
+    new_q = torch.stack([xd["q_idx"][b, n] for b, n in enumerate(lens)])[:, None].contiguous()
+    new_k = torch.stack([xd["k_idx"][b, n] for b, n in enumerate(lens)])[:, None].contiguous()
+    cache_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    bound = max(lens)
+    ws = Q.workspace(h, Q.QSA_OP_TOKEN_INDEX_DECODE, B, 1, bound)
+    tidx = torch.empty((B, budget), dtype=torch.int32, device=DEV)
+    Q.qsa_token_index_decode(h, B, cache_len, bound, new_q, new_k, ktok, tidx, ws)
+    torch.cuda.synchronize()
+    got = tidx.cpu().numpy()
+    p = O.Params(budget=budget)
+    for b, n in enumerate(lens):
+        sel, scs = O.token_index_rows(bits(x["q_idx"][b, n:n + 1]), bits(x["k_idx"][b, :n + 1]), [n], p)
+        check_selection(got[b], sel[0], scs[0], budget, n, "seq %d" % b)
+
+
+def test_index_decode_equals_decode_selection():
+    """qsa_index_decode selects what qsa_decode selects (and the oracle), and
+    appends the new token's indexer key the same way."""
+    budget = 48
+    lens = [1500, 3, 0, 1203, 700]
+    w = synth.Workload("t", "decode", len(lens), max(lens), budget, 6, "random", 64)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    x, _, bidx, c = _decode_setup(w, lens, h)
+    B = len(lens)
+    xd = _to(x)
+    c2 = Q.alloc_caches(h, B)
+    for b, n in enumerate(lens):
+        if n:
+            sl = lambda t: t[b:b + 1, :n].contiguous()
+            cs = {k: v[b:b + 1] for k, v in c2.items()}
+            Q.qsa_append(h, 1, n, 0, sl(xd["k"]), sl(xd["v"]), sl(xd["k_idx"]), cs["k_cache"], cs["v_cache"],
+                         cs["kbar_cache"], cs["kpend"])
+    new_k = torch.stack([xd["k_idx"][b, n] for b, n in enumerate(lens)])[:, None].contiguous()
+    cache_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_INDEX_DECODE, B, 1, max(lens))
+    sel = torch.empty((B, budget), dtype=torch.int32, device=DEV)
+    Q.qsa_index_decode(h, B, cache_len, max(lens), xd["q_idx"], new_k, c2["kbar_cache"], c2["kpend"], sel, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, bidx[:, 0])
+    for b, n in enumerate(lens):
+        nb = (n + 1) // 4
+        assert torch.equal(c2["kbar_cache"][b, :nb], c["kbar_cache"][b, :nb])
+        assert torch.equal(c2["kpend"][b, :(n % 4) + 1], c["kpend"][b, :(n % 4) + 1])

@@ -199,6 +199,36 @@ def test_pooled_score_equals_mean_of_token_logits():
         kraw[4:8].astype(np.float64), 4, w).T).mean(axis=1).sum()) > 1e-3
 
 
+def test_token_level_indexer_brute_force():
+    """r = 1: every key rotated at its own position (fp64 complex arithmetic on
+    the bf16 inputs), logits against the query rotated at p, ReLU, sum over
+    heads, candidates t < p only; the selection is the brute-force top-k of
+    those scores up to near-ties (bf16 rounding of the rotated operands)."""
+    rng = np.random.default_rng(11)
+    p = O.Params(budget=5)
+    w = O.inv_freq(p)
+    n_tok = 40
+    kb = O.f32_to_bf16_bits(rng.standard_normal((n_tok, 128)).astype(np.float32))
+    qb = O.f32_to_bf16_bits(rng.standard_normal((n_tok, 4, 128)).astype(np.float32))
+    pos = [0, 1, 4, 5, 17, 39]
+    sel, scs = O.token_index_rows(qb[pos], kb, pos, p)
+    kf = O.bf16_bits_to_f32(kb).astype(np.float64)
+    for i, pq in enumerate(pos):
+        assert scs[i].shape == (pq,)
+        qt = _rot_complex(O.bf16_bits_to_f32(qb[pq]).astype(np.float64), pq, w)
+        ref = np.zeros(pq)
+        for t in range(pq):
+            kt = _rot_complex(kf[t:t + 1], t, w)[0]
+            ref[t] = sum(max(0.0, float(qt[h] @ kt)) for h in range(4))
+        np.testing.assert_allclose(scs[i], ref, rtol=2e-2, atol=0.1)
+        n = min(p.budget, pq)
+        assert np.all(sel[i, n:] == -1) and np.all(np.diff(sel[i, :n]) > 0)
+        order = sorted(range(pq), key=lambda t: (-ref[t], -t))[:n]
+        kth = sorted(ref, reverse=True)[n - 1] if n else 0.0
+        for t in set(order) ^ set(sel[i, :n].tolist()):
+            assert abs(ref[t] - kth) < 0.5, (pq, t)
+
+
 def test_pooling_is_token_order_fp32_mean():
     x = np.array([[1.0], [2.0 ** -24], [2.0 ** -24], [-1.0]], dtype=np.float32)
     # ((1 + 2^-24) + 2^-24) - 1 in fp32: each 2^-24 is lost against 1 (ties to even)
