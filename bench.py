@@ -304,13 +304,102 @@ def dense_prefill_ms(L, reps=1):
     return ev[0].elapsed_time(ev[1]) / reps
 
 
+def indexer_ratio_prefill(w, steps):
+    """The indexer alone at compression ratio 4 against ratio 1 on prefill
+    workload w (in w.chunk-token calls when it is chunked): qsa_index_select over
+    the pooled keys (built beforehand by qsa_append) against
+    qsa_token_index_select over every token's key (its per-call key rotation
+    included), both selecting the budget's 512 entries per query.  ms per pass."""
+    L = w.seq_len
+    C = w.chunk or L
+    x = synth.prefill_inputs(w, "cuda")
+    h = Q.Handle(max_ctx=L, budget_blocks=w.budget, yarn_factor=w.yarn_factor)
+    c = Q.alloc_caches(h, 1)
+    for s0 in range(0, L, C):
+        sl = lambda t: t[:, s0:s0 + C]
+        Q.qsa_append(h, 1, C, s0, sl(x["k"]), sl(x["v"]), sl(x["k_idx"]), c["k_cache"], c["v_cache"],
+                     c["kbar_cache"], c["kpend"])
+    for n in ("q", "k", "v"):
+        del x[n]
+    torch.cuda.empty_cache()
+    ktok = Q.alloc_token_keys(h, 1)
+    sel = torch.empty((1, C, w.budget), dtype=torch.int32, device="cuda")
+    ws4 = Q.workspace(h, Q.QSA_OP_INDEX_SELECT, 1, C, L - C)
+    ws1 = Q.workspace(h, Q.QSA_OP_TOKEN_INDEX_SELECT, 1, C, L - C)
+
+    def r4():
+        for s0 in range(0, L, C):
+            Q.qsa_index_select(h, 1, C, s0, x["q_idx"][:, s0:s0 + C], c["kbar_cache"], sel, ws4)
+
+    def r1():
+        for s0 in range(0, L, C):
+            Q.qsa_token_index_select(h, 1, C, s0, x["q_idx"][:, s0:s0 + C], x["k_idx"][:, s0:s0 + C], ktok, sel,
+                                     ws1)
+
+    t = {}
+    for name, fn in (("r4", r4), ("r1", r1)):
+        fn()
+        torch.cuda.synchronize()
+        e = _events(2)
+        e[0].record()
+        for _ in range(steps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        t[name] = e[0].elapsed_time(e[1]) / steps
+    del x, c, ktok, sel, ws4, ws1, h
+    torch.cuda.empty_cache()
+    return t
+
+
+def indexer_ratio_decode(wd, steps):
+    """One decode step's indexer alone at ratio 4 (qsa_index_decode over the pooled
+    cache) against ratio 1 (qsa_token_index_decode over a token-key cache of
+    random bf16 keys: timing only) for wd.batch sequences of wd.seq_len tokens."""
+    sd = setup_decode(wd)
+    h, B, ctx, x, c = sd["h"], sd["B"], sd["ctx"], sd["x"], sd["c"]
+    for n in ("k_cache", "v_cache"):
+        del c[n]
+    torch.cuda.empty_cache()
+    ktok = Q.alloc_token_keys(h, B)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    for b in range(B):
+        ktok[b].copy_(torch.randn(ktok.shape[1:], device="cuda", generator=g).to(torch.bfloat16))
+    sel = torch.empty((B, wd.budget), dtype=torch.int32, device="cuda")
+    ws4 = Q.workspace(h, Q.QSA_OP_INDEX_DECODE, B, 1, ctx)
+    ws1 = Q.workspace(h, Q.QSA_OP_TOKEN_INDEX_DECODE, B, 1, ctx)
+    fns = {"r4": lambda: Q.qsa_index_decode(h, B, sd["cache_len"], ctx, x["q_idx"], x["k_idx"], c["kbar_cache"],
+                                            c["kpend"], sel, ws4),
+           "r1": lambda: Q.qsa_token_index_decode(h, B, sd["cache_len"], ctx, x["q_idx"], x["k_idx"], ktok, sel,
+                                                  ws1)}
+    t = {}
+    for name, fn in fns.items():
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e = _events(2)
+        e[0].record()
+        for _ in range(10 * steps):
+            fn()
+        e[1].record()
+        torch.cuda.synchronize()
+        t[name] = e[0].elapsed_time(e[1]) / (10 * steps)
+    del sd, ktok, sel, ws4, ws1
+    torch.cuda.empty_cache()
+    return t
+
+
 def run_ratios(steps):
     """QSA against dense attention on this GPU, as in the pages' module
     speed-ups (prefill and decode at 1M tokens): QSA prefill (append + fused
     index/select + sparse attention) against dense causal SDPA at 262,144 and
     1,048,576 tokens, and QSA decode of 8 x 1,048,576 against the same split-K
     decode kernel over every cached token (qsa_decode_reuse with a selection
-    made at position 0: no selected block, the tail is the whole context)."""
+    made at position 0: no selected block, the tail is the whole context).
+    Then the indexer alone at compression ratio 4 against ratio 1 (the pages'
+    indexer speed-ups), at 262,144 and 1,048,576 prefill tokens and for the
+    8 x 1,048,576 decode step."""
     res = {}
     wp = synth.WORKLOADS["prefill_256k"]
     sp = setup_prefill(wp)
@@ -325,6 +414,7 @@ def run_ratios(steps):
     torch.cuda.empty_cache()
     t_dense = dense_prefill_ms(wp.seq_len, reps=2)
     res["prefill_262144"] = {"qsa_ms": t_qsa, "dense_sdpa_ms": t_dense, "speedup": t_dense / t_qsa}
+    wp_1m = synth.WORKLOADS["prefill_1m"]
     t_qsa_1m = qsa_prefill_1m_ms(1)
     t_dense_1m = dense_prefill_ms(1 << 20, reps=1)
     res["prefill_1048576"] = {"qsa_ms": t_qsa_1m, "dense_sdpa_ms": t_dense_1m, "speedup": t_dense_1m / t_qsa_1m,
@@ -355,6 +445,16 @@ def run_ratios(steps):
                                    "speedup": times["dense"] / times["qsa"]}
     res["pages_module_speedups_at_1M"] = {"prefill": 7.6, "decode": 4.9,
                                           "note": "other hardware, dense baseline a paged GQA library"}
+    del sd, x, c, sel
+    torch.cuda.empty_cache()
+    idx = {}
+    for key, w in (("prefill_262144", synth.WORKLOADS["prefill_256k"]), ("prefill_1048576", wp_1m)):
+        t = indexer_ratio_prefill(w, steps)
+        idx[key] = {"r4_ms": t["r4"], "r1_ms": t["r1"], "speedup": t["r1"] / t["r4"]}
+    t = indexer_ratio_decode(wd, steps)
+    idx["decode_B8_ctx1048576"] = {"r4_ms": t["r4"], "r1_ms": t["r1"], "speedup": t["r1"] / t["r4"]}
+    idx["pages_indexer_speedups_r4"] = {"prefill": 3.8, "decode": 4.4, "note": "other hardware"}
+    res["indexer_r4_vs_r1"] = idx
     print(json.dumps({"ratios": res}), flush=True)
 
 
