@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqsa.so")
 
 (QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE, QSA_OP_INDEX_SELECT,
- QSA_OP_INDEX_DECODE, QSA_OP_TOKEN_INDEX_SELECT, QSA_OP_TOKEN_INDEX_DECODE) = range(10)
+ QSA_OP_INDEX_DECODE, QSA_OP_TOKEN_INDEX_SELECT, QSA_OP_TOKEN_INDEX_DECODE, QSA_OP_TRAIN_FORWARD,
+ QSA_OP_TRAIN_BACKWARD) = range(12)
 
 STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPPORTED", 4: "QSA_ERR_ALIGN",
           5: "QSA_ERR_CAPACITY", 6: "QSA_ERR_WORKSPACE", 7: "QSA_ERR_HIP"}
@@ -27,7 +28,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPP
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
            "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
            "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
-           "qsa_status_string", "qsa_last_hip_error"]
+           "qsa_train_forward", "qsa_train_backward_indexer", "qsa_status_string", "qsa_last_hip_error"]
 
 
 class QSAError(RuntimeError):
@@ -91,6 +92,10 @@ def lib() -> ctypes.CDLL:
     L.qsa_token_index_select.restype = ctypes.c_int
     L.qsa_token_index_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 5 + [sz]
     L.qsa_token_index_decode.restype = ctypes.c_int
+    L.qsa_train_forward.argtypes = [vp, vp, i32, i64] + [vp] * 10 + [sz]
+    L.qsa_train_forward.restype = ctypes.c_int
+    L.qsa_train_backward_indexer.argtypes = [vp, vp, i32, i64] + [vp] * 10 + [sz]
+    L.qsa_train_backward_indexer.restype = ctypes.c_int
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     L.qsa_last_hip_error.argtypes = []
@@ -281,6 +286,24 @@ def qsa_token_index_decode(h, B, cache_len, ctx_bound, q_idx, k_idx, ktok_cache,
                                         ctx_bound, _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
                                         _bf(ktok_cache, "ktok_cache"), _ptr(token_idx, torch.int32, "token_idx"),
                                         _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_token_index_decode")
+
+
+def qsa_train_forward(h, B, L, q, q_idx, k_cache, v_cache, kbar_cache, block_idx, out, stats, kl, ws, stream=None):
+    _check(lib().qsa_train_forward(h.ptr, _stream(stream), B, L, _bf(q, "q"), _bf(q_idx, "q_idx"),
+                                   _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
+                                   _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out"),
+                                   _ptr(stats, torch.float32, "stats"), _ptr(kl, torch.float32, "kl"),
+                                   _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_train_forward")
+
+
+def qsa_train_backward_indexer(h, B, L, q, q_idx, k_cache, kbar_cache, block_idx, stats, dkl, dq_idx, dk_idx, ws,
+                               stream=None):
+    _check(lib().qsa_train_backward_indexer(h.ptr, _stream(stream), B, L, _bf(q, "q"), _bf(q_idx, "q_idx"),
+                                            _bf(k_cache, "k_cache"), _bf(kbar_cache, "kbar_cache"),
+                                            _ptr(block_idx, torch.int32, "block_idx"),
+                                            _ptr(stats, torch.float32, "stats"), _ptr(dkl, torch.float32, "dkl"),
+                                            _ptr(dq_idx, torch.float32, "dq_idx"), _ptr(dk_idx, torch.float32, "dk_idx"),
+                                            _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_train_backward_indexer")
 
 
 def qsa_status_string(status: int) -> str:

@@ -22,81 +22,15 @@
 // Softmax is online in fp32 (base-2 exponentials, max over the 4 lane groups
 // by two xor-shuffles); P is rounded to bf16 for the PV product.
 #include "qsa_common.h"
+#include "attend_parts.h"
 
 namespace qsa {
-
-constexpr int kChunkBlocks = 8;                  // 32 tokens per step
-constexpr float kLog2e = 1.4426950408889634f;
 
 struct RowState {
     float m;        // running max of the raw logits of head l%16 (same in the 4 lane groups)
     float l;        // this lane's partial softmax denominator
     f32x4 o[16];    // O^T: dims 16n + 4*(l/16) + j of head l%16
 };
-
-// Q~^T fragments of one (query, KV group): lane (h = l%16, g = l/16) holds, for
-// k-step s, dims 32s + 8g .. +7 of head 12*grp + h, rotated at `pos` (heads
-// 12..15 of the 16-wide tile are zero).
-__device__ __forceinline__ void load_q_frags(const bf16_t *qrow /*[24][256] of this token*/, int grp, int64_t pos,
-                                             const Tables &tab, bf16x8 (&qf)[8])
-{
-    const int lane = threadIdx.x & 63;
-    const int h = lane & 15, g = lane >> 4;
-    if (h >= kGroup) {
-        for (int s = 0; s < 8; ++s) qf[s] = bf16x8{};
-        return;
-    }
-    const bf16_t *src = qrow + (grp * kGroup + h) * kHeadDim + 8 * g;
-    u32x4 x[8];
-    for (int s = 0; s < 8; ++s) x[s] = *reinterpret_cast<const u32x4 *>(src + 32 * s);
-    // rotary pairs (j, j + 32), j = 8g + e: k-step 0 holds x_j, k-step 1 holds x_{j+32}
-    const float *cs = tab.cos + pos * kPairs + 8 * g;
-    const float *sn = tab.sin + pos * kPairs + 8 * g;
-    uint32_t w0[4], w1[4];
-    for (int i = 0; i < 4; ++i) {
-        float r0[2], r1[2];
-        for (int e = 0; e < 2; ++e) {
-            float a = __uint_as_float(e ? (x[0][i] & 0xFFFF0000u) : (x[0][i] << 16));
-            float b = __uint_as_float(e ? (x[1][i] & 0xFFFF0000u) : (x[1][i] << 16));
-            rotate_pair(a, b, cs[2 * i + e], sn[2 * i + e]);
-            r0[e] = a;
-            r1[e] = b;
-        }
-        w0[i] = pack_bf16x2(r0[0], r0[1]);
-        w1[i] = pack_bf16x2(r1[0], r1[1]);
-    }
-    x[0] = u32x4{w0[0], w0[1], w0[2], w0[3]};
-    x[1] = u32x4{w1[0], w1[1], w1[2], w1[3]};
-    for (int s = 0; s < 8; ++s) qf[s] = __builtin_bit_cast(bf16x8, x[s]);
-}
-
-// Block id and valid-token mask (bit t = token t valid) of list entry li.
-// The list is the n_sel selected blocks (only ids in [0, o0) count), then the
-// tail blocks o0 .. o, whole except the query's own block o, whose tokens run
-// to own_last.  A selection made at the query itself has o0 = o (the tail is
-// the own block alone); one reused from an earlier position has o0 = its own
-// block there.
-__device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o0, int64_t o, int li,
-                                           int own_last, int64_t &blk, uint32_t &tmask)
-{
-    if (li < n_sel) {
-        const int64_t id = sel[li];
-        const bool ok = id >= 0 && id < o0;
-        blk = ok ? id : 0;
-        tmask = ok ? 0xFu : 0u;
-    } else if (li - n_sel <= o - o0) {
-        blk = o0 + (li - n_sel);
-        tmask = (blk == o) ? (1u << (own_last + 1)) - 1u : 0xFu;
-    } else {
-        blk = 0;
-        tmask = 0u;
-    }
-}
-
-// Chunks of a token list of n_sel selected blocks and tail blocks o0 .. o.
-__device__ __forceinline__ int list_chunks(int n_sel, int64_t o0, int64_t o) {
-    return static_cast<int>((n_sel + (o - o0) + 1 + kChunkBlocks - 1) / kChunkBlocks);
-}
 
 // Walk chunks [c_lo, c_hi) of one (query, group) token list.
 __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
@@ -224,6 +158,52 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     }
 }
 
+// Prefill attention of the training forward: the same walk as
+// attend_prefill_kernel (q_offset 0), and each head's natural-log log-sum-exp of
+// its scaled logits over T(p), sigma*m + ln(l), stored at stats[row*32 + head]
+// for the teacher of the indexer loss.
+__global__ __launch_bounds__(256) void attend_stats_kernel(
+    Tables tab, int64_t L, int64_t nblk_cap, int budget, float c2,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out, float *__restrict__ stats)
+{
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.y;
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * 2 + (wave >> 1);
+    const int grp = wave & 1;
+    if (i >= L) return;
+    const int64_t pos = i;
+    const int64_t o = pos / kBlock;
+    const int own_last = static_cast<int>(pos - o * kBlock);
+    const int n_sel = static_cast<int>(o < budget ? o : budget);
+    const int nchunks = list_chunks(n_sel, o, o);
+
+    bf16x8 qf[8];
+    load_q_frags(q + (b * L + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
+    const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const int32_t *sel = block_idx + (b * L + i) * budget;
+
+    RowState st;
+    init_state(st);
+    attend_chunks(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
+
+    float lt = st.l + __shfl_xor(st.l, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = 1.0f / lt;
+    const int h = lane & 15, g = lane >> 4;
+    if (h < kGroup) {
+        bf16_t *dst = out + ((b * L + i) * kQHeads + grp * kGroup + h) * kHeadDim + 4 * g;
+        for (int n = 0; n < 16; ++n) {
+            u32x2 w = u32x2{pack_bf16x2(st.o[n][0] * inv, st.o[n][1] * inv),
+                            pack_bf16x2(st.o[n][2] * inv, st.o[n][3] * inv)};
+            *reinterpret_cast<u32x2 *>(dst + 16 * n) = w;
+        }
+        if (g == 0) stats[(b * L + i) * kTrainStats + grp * kGroup + h] = (st.m * c2 + log2f(lt)) * kLn2;
+    }
+}
+
 // Decode, split over the token list: one wave per (split, group, sequence)
 // writes its unnormalised partial (m, l, O) for the 12 heads.  With sel_pos
 // (a reused selection) the list is block_idx as selected at position
@@ -325,6 +305,17 @@ hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, i
     dim3 grid(static_cast<unsigned>((L + 1) / 2), static_cast<unsigned>(B));
     hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, L, q_offset, nblk_cap, budget,
                        sigma * kLog2e, q, k_cache, v_cache, block_idx, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend_stats(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t nblk_cap, int budget,
+                               float sigma, const bf16_t *q, const bf16_t *k_cache, const bf16_t *v_cache,
+                               const int32_t *block_idx, bf16_t *out, float *stats)
+{
+    if (L <= 0) return hipSuccess;
+    dim3 grid(static_cast<unsigned>((L + 1) / 2), static_cast<unsigned>(B));
+    hipLaunchKernelGGL(attend_stats_kernel, grid, dim3(256), 0, st, tab, L, nblk_cap, budget, sigma * kLog2e, q,
+                       k_cache, v_cache, block_idx, out, stats);
     return hipGetLastError();
 }
 

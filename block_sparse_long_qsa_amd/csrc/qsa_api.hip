@@ -43,6 +43,12 @@ hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, in
 hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, const float *,
                                    const uint32_t *, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *, int32_t *,
                                    int);
+hipError_t launch_attend_stats(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int, float, const bf16_t *,
+                               const bf16_t *, const bf16_t *, const int32_t *, bf16_t *, float *);
+hipError_t launch_train_kl(const Tables &, hipStream_t, bool, int32_t, int64_t, int64_t, int, float, const bf16_t *,
+                           const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
+                           const float *, float *, float *);
+hipError_t launch_dk_idx(const Tables &, hipStream_t, int32_t, int64_t, int64_t, const float *, float *);
 hipError_t launch_token_keys(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, const bf16_t *, bf16_t *);
 hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t,
                                       const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, uint32_t *);
@@ -304,6 +310,11 @@ size_t qsa_workspace_size(const qsa_handle *h, int op, int32_t batch, int64_t le
         return index_select_layout(batch, len, h->cap).total;
     case QSA_OP_TOKEN_INDEX_DECODE:
         return decode_layout(h, batch, q_offset, 0).total;
+    case QSA_OP_TRAIN_FORWARD:
+        return align_up(static_cast<size_t>(batch) * len * kIdxHeads * kIdxDim * 2);
+    case QSA_OP_TRAIN_BACKWARD:
+        return align_up(static_cast<size_t>(batch) * len * kIdxHeads * kIdxDim * 2) +
+               align_up(static_cast<size_t>(batch) * nblk_cap(h) * kIdxDim * 4);
     default:
         return 0;
     }
@@ -566,6 +577,56 @@ qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, 
                                     reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
                                     reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
                                     reinterpret_cast<uint32_t *>(w + d.s2row), token_idx, h->p.budget_blocks);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+// Training path: sparse attention + per-head log-sum-exp, then the indexer's
+// KL loss against the max-pooled teacher (whole sequences: positions 0..L-1).
+qsa_status qsa_train_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
+                             const uint16_t *q_idx, const uint16_t *k_cache, const uint16_t *v_cache,
+                             const uint16_t *kbar_cache, const int32_t *block_idx, uint16_t *out, float *stats,
+                             float *kl, void *ws, size_t ws_bytes) {
+    qsa_status s = check_chunk(h, B, L, 0, true);
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q, q_idx, k_cache, v_cache, kbar_cache, block_idx, out, stats, kl, ws})) != QSA_OK) return s;
+    if (ws_bytes < qsa_workspace_size(h, QSA_OP_TRAIN_FORWARD, B, L, 0)) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bf16_t *qrot = static_cast<bf16_t *>(ws);
+    const int64_t nbc = nblk_cap(h);
+    const int budget = h->p.budget_blocks;
+    hipError_t e = launch_qidx_rotate(tables(h), st, B, L, 0, nullptr, q_idx, qrot);
+    if (e == hipSuccess)
+        e = launch_attend_stats(tables(h), st, B, L, nbc, budget, h->sigma, q, k_cache, v_cache, block_idx, out, stats);
+    if (e == hipSuccess)
+        e = launch_train_kl(tables(h), st, false, B, L, nbc, budget, h->sigma, q, k_cache, kbar_cache, qrot, block_idx,
+                            stats, kl, nullptr, nullptr, nullptr);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_train_backward_indexer(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
+                                      const uint16_t *q_idx, const uint16_t *k_cache, const uint16_t *kbar_cache,
+                                      const int32_t *block_idx, const float *stats, const float *dkl, float *dq_idx,
+                                      float *dk_idx, void *ws, size_t ws_bytes) {
+    qsa_status s = check_chunk(h, B, L, 0, true);
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q, q_idx, k_cache, kbar_cache, block_idx, stats, dkl, dq_idx, dk_idx, ws})) != QSA_OK)
+        return s;
+    if (ws_bytes < qsa_workspace_size(h, QSA_OP_TRAIN_BACKWARD, B, L, 0)) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w);
+    float *dkbar = reinterpret_cast<float *>(w + align_up(static_cast<size_t>(B) * L * kIdxHeads * kIdxDim * 2));
+    const int64_t nbc = nblk_cap(h);
+    hipError_t e = launch_qidx_rotate(tables(h), st, B, L, 0, nullptr, q_idx, qrot);
+    if (e == hipSuccess) e = launch_zero_words(st, reinterpret_cast<int32_t *>(dkbar), static_cast<int64_t>(B) * nbc * kIdxDim);
+    if (e == hipSuccess)
+        e = launch_train_kl(tables(h), st, true, B, L, nbc, h->p.budget_blocks, h->sigma, q, k_cache, kbar_cache, qrot,
+                            block_idx, const_cast<float *>(stats), nullptr, dkl, dq_idx, dkbar);
+    if (e == hipSuccess) e = launch_dk_idx(tables(h), st, B, L, nbc, dkbar, dk_idx);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

@@ -116,7 +116,8 @@ typedef struct qsa_handle qsa_handle;
 /* Operation codes for qsa_workspace_size. */
 enum { QSA_OP_APPEND = 0, QSA_OP_INDEX = 1, QSA_OP_SELECT = 2, QSA_OP_ATTEND = 3,
        QSA_OP_FORWARD = 4, QSA_OP_DECODE = 5, QSA_OP_INDEX_SELECT = 6, QSA_OP_INDEX_DECODE = 7,
-       QSA_OP_TOKEN_INDEX_SELECT = 8, QSA_OP_TOKEN_INDEX_DECODE = 9 };
+       QSA_OP_TOKEN_INDEX_SELECT = 8, QSA_OP_TOKEN_INDEX_DECODE = 9, QSA_OP_TRAIN_FORWARD = 10,
+       QSA_OP_TRAIN_BACKWARD = 11 };
 
 /* Fill *p with the layer's published shapes, budget 512, max_ctx 262144,
  * theta 1e7, no YaRN (factor 1), yarn_orig_ctx 262144.  Host only. */
@@ -282,6 +283,43 @@ qsa_status qsa_token_index_select(const qsa_handle *h, void *stream, int32_t B, 
 qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
                                   int64_t ctx_bound, const uint16_t *q_idx, const uint16_t *k_idx,
                                   uint16_t *ktok_cache, int32_t *token_idx, void *ws, size_t ws_bytes);
+
+/* Training path ([PKR] "QSA: ..." section: the indexer learns the attention
+ * distribution matched per micro-block with max pooling, and a fused kernel
+ * computes the sparse attention output and the indexer's KL-divergence loss
+ * without materialising intermediates).  Whole sequences: positions 0..L-1 of
+ * each of B sequences, whose caches qsa_append has filled (k_cache, v_cache,
+ * kbar_cache as in qsa_forward), with a selection block_idx [B][L][budget] (for
+ * instance from qsa_index_select; the top-k itself is not differentiated).
+ *
+ * qsa_train_forward: out [B][L][24][256] bf16 = qsa_attend's output; stats
+ * [B][L][32] fp32 per query: [0..23] each query head's natural-log log-sum-exp
+ * of its scaled logits over the token set T(p), [24] ln Z, [25] the log-sum-exp
+ * of the indexer scores over S(p), [26..31] 0; kl [B][L] fp32 = KL(pi || s),
+ * where for the valid selected blocks b of S(p) (the own block takes no part)
+ * A_b = max over the block's 4 tokens of the 24 heads' mean attention
+ * probability, Z = sum A, pi_b = A_b / Z, s_b = softmax over S(p) of the
+ * indexer scores I_b; kl = 0 when S(p) has fewer than 2 blocks.  With a budget
+ * covering every block the teacher is the dense one (the distillation stage).
+ * ws: qsa_workspace_size(QSA_OP_TRAIN_FORWARD, B, L, 0) bytes.
+ *
+ * qsa_train_backward_indexer: gradients of sum_p dkl[p] * kl[p] (dkl [B][L]
+ * fp32) with respect to the raw indexer queries, dq_idx [B][L][4][128] fp32,
+ * and raw indexer keys, dk_idx [B][L][128] fp32 (0 for the tokens of a
+ * trailing partial block), holding the teacher constant: dkl/dI_b = s_b - pi_b,
+ * ReLU' = [logit > 0], transposed rotations, 1/4 per pooled key.  stats: the
+ * forward's.  The gradient of the attention output with respect to q, k, v is
+ * not computed here.  ws: qsa_workspace_size(QSA_OP_TRAIN_BACKWARD, B, L, 0)
+ * bytes.  Both: q_idx [B][L][4][128], q [B][L][24][256] raw bf16; errors as for
+ * qsa_forward with q_offset = 0. */
+qsa_status qsa_train_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
+                             const uint16_t *q_idx, const uint16_t *k_cache, const uint16_t *v_cache,
+                             const uint16_t *kbar_cache, const int32_t *block_idx, uint16_t *out, float *stats,
+                             float *kl, void *ws, size_t ws_bytes);
+qsa_status qsa_train_backward_indexer(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
+                                      const uint16_t *q_idx, const uint16_t *k_cache, const uint16_t *kbar_cache,
+                                      const int32_t *block_idx, const float *stats, const float *dkl,
+                                      float *dq_idx, float *dk_idx, void *ws, size_t ws_bytes);
 
 /* Static string for a status code. */
 const char *qsa_status_string(qsa_status s);

@@ -1,0 +1,117 @@
+"""Parity of the training path (qsa_train_forward, qsa_train_backward_indexer)
+with the training oracle (oracle/train.py), through the C ABI, on seeded
+synthetic sequences.  The selection fed to both sides is the oracle's.
+
+Acceptance (derived from the arithmetic):
+  * out: as every attention output (2e-2 + 1e-2|ref| element-wise, 1e-2 normwise);
+  * per-head log-sum-exp: |d| <= 3e-3 -- the attention kernel sums its
+    probabilities after rounding each to bf16 (relative 2^-9), so ln(l) moves by
+    at most 2^-9 ~ 2e-3, plus fp32 logits;
+  * ln Z: |d| <= 1e-2 and kl: |d| <= 1e-2 + 1e-2 |kl| -- the teacher's
+    probabilities inherit the per-head log-sum-exp error (<= 2e-3 relative per
+    head) through a max over tokens and a sum over blocks;
+  * log-sum-exp of the indexer scores: |d| <= 1e-3 max(1, |ref|) (fp32 MFMA
+    scores, relative 1e-4);
+  * kl also moves with the scores: dKL/dI_b = s_b - pi_b, so |d| <= 2 max|dI|
+    (about 1e-4 |I| <= 5e-3 here); a per-head error of the log-sum-exp scales
+    all of that head's probabilities alike and cancels in pi = A / Z;
+  * gradients: normwise ||gpu - ref|| / ||ref|| <= 5e-3 and element-wise
+    |d| <= 5e-3 max|ref| per tensor -- the coefficients s - pi carry the scores'
+    relative error (1e-4 |I| <= 5e-3 in s); a ReLU mask flips only for a logit
+    within fp32 rounding of 0.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_qsa_amd as Q
+import oracle as O
+import synth
+from oracle import train as T
+from helpers import bits, check_out, f32, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    Q.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _oracle_selection(x, b, p, L):
+    kbar = O.indexer_keys(bits(x["k_idx"][b]), p)
+    qt = O.indexer_queries(bits(x["q_idx"][b]), np.arange(L), p)
+    return np.stack([O.select_blocks(O.block_scores(qt[i], kbar[:i // 4]), p.budget) for i in range(L)])
+
+
+def _run(B, L, budget, seed, needles=6):
+    w = synth.Workload("t", "prefill", B, L, budget, needles, "random", seed)
+    x = synth.prefill_inputs(w, "cpu")
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    p = O.Params(budget=budget)
+    h = Q.Handle(max_ctx=(L + 3) // 4 * 4, budget_blocks=budget)
+    c = Q.alloc_caches(h, B)
+    Q.qsa_append(h, B, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    sel = np.stack([_oracle_selection(x, b, p, L) for b in range(B)]).astype(np.int32)
+    bidx = torch.from_numpy(sel).to(DEV)
+    out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    stats = torch.empty((B, L, 32), dtype=torch.float32, device=DEV)
+    kl = torch.empty((B, L), dtype=torch.float32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_TRAIN_FORWARD, B, L, 0)
+    Q.qsa_train_forward(h, B, L, xd["q"], xd["q_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], bidx, out,
+                        stats, kl, ws)
+    g = np.random.default_rng(seed + 1000)
+    dkl_np = (g.random((B, L)) + 0.5).astype(np.float32)
+    dkl = torch.from_numpy(dkl_np).to(DEV)
+    dq = torch.empty((B, L, 4, 128), dtype=torch.float32, device=DEV)
+    dk = torch.empty((B, L, 128), dtype=torch.float32, device=DEV)
+    wsb = Q.workspace(h, Q.QSA_OP_TRAIN_BACKWARD, B, L, 0)
+    Q.qsa_train_backward_indexer(h, B, L, xd["q"], xd["q_idx"], c["k_cache"], c["kbar_cache"], bidx, stats, dkl,
+                                 dq, dk, wsb)
+    torch.cuda.synchronize()
+    return x, p, sel, dkl_np, f32(out), stats.cpu().numpy(), kl.cpu().numpy(), dq.cpu().numpy(), dk.cpu().numpy()
+
+
+def _check(B, L, budget, seed):
+    x, p, sel, dkl, out, stats, kl, dq, dk = _run(B, L, budget, seed)
+    worst = {"kl": 0.0, "lse": 0.0}
+    for b in range(B):
+        lay = oracle_layer(x, b, p)
+        rows = T.train_rows(lay, range(L), bits(x["q"][b]), bits(x["q_idx"][b]), sel[b])
+        for i, r in enumerate(rows):
+            check_out(out[b, i], r["out"], "seq %d row %d" % (b, i))
+            d_lse = np.abs(stats[b, i, :24] - r["lse"]).max()
+            assert d_lse <= 3e-3, (b, i, d_lse)
+            assert abs(kl[b, i] - r["kl"]) <= 1e-2 + 1e-2 * abs(r["kl"]), (b, i, kl[b, i], r["kl"])
+            if r["blocks"].shape[0] >= 1:
+                assert abs(stats[b, i, 24] - r["lnZ"]) <= 1e-2, (b, i)
+                assert abs(stats[b, i, 25] - r["lse_i"]) <= 1e-3 * max(1.0, abs(r["lse_i"])), (b, i)
+            assert np.all(stats[b, i, 26:] == 0)
+            worst["kl"] = max(worst["kl"], abs(kl[b, i] - r["kl"]))
+            worst["lse"] = max(worst["lse"], d_lse)
+        teach = [(r["A"], r["blocks"]) for r in rows]
+        gq, gk = T.indexer_grads(bits(x["q_idx"][b]), bits(x["k_idx"][b]), teach, dkl[b].astype(np.float64), p)
+        for name, got, ref in (("dq_idx", dq[b], gq), ("dk_idx", dk[b], gk)):
+            scale = max(np.abs(ref).max(), 1e-30)
+            worst[name] = max(worst.get(name, 0.0), np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30))
+            assert np.abs(got - ref).max() <= 5e-3 * scale, (name, b, np.abs(got - ref).max(), scale)
+            assert np.linalg.norm(got - ref) <= 5e-3 * np.linalg.norm(ref), (name, b)
+        # tokens of a trailing partial block get no gradient
+        assert np.all(dk[b, (L // 4) * 4:] == 0)
+    return worst
+
+
+def test_train_sparse_rows():
+    """Stage-2 reading: budget 16 over 300 tokens, so most rows select a subset."""
+    print("worst deviations", _check(2, 300, 16, 71))
+
+
+def test_train_dense_teacher():
+    """Stage-1 reading: the budget covers every block, so the teacher is the
+    dense max-pooled attention distribution over all complete blocks."""
+    print("worst deviations", _check(1, 203, 64, 72))
