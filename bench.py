@@ -458,6 +458,70 @@ def run_ratios(steps):
     print(json.dumps({"ratios": res}), flush=True)
 
 
+def train_bytes(L, budget):
+    """Algorithmic bytes of one indexer-loss pass (teacher + student) over L
+    query rows: per selected block 2 x 2,048 B of K~ (both KV groups) and 256 B
+    of k̄, per query its q (12,288 B), q_idx (1,024 B) and stats (128 B)."""
+    o = np.arange(L, dtype=np.int64) // 4
+    nsel = np.minimum(o, budget).sum()
+    return int(nsel) * (2 * 2048 + 256) + L * (12288 + 1024 + 128)
+
+
+def run_train(steps):
+    """One training step of the layer on the 32,768- and 262,144-token prefill
+    workloads: forward = qsa_append + qsa_index_select (the top-k, not
+    differentiated) + qsa_train_forward (sparse attention with log-sum-exp, then
+    the indexer KL loss); backward = qsa_train_backward_indexer (gradients to the
+    raw indexer queries and keys).  HIP events between the stages; one JSON line."""
+    res = {}
+    for key in ("prefill_32k", "prefill_256k"):
+        w = synth.WORKLOADS[key]
+        L, budget = w.seq_len, w.budget
+        x = synth.prefill_inputs(w, "cuda")
+        h = Q.Handle(max_ctx=L, budget_blocks=budget)
+        c = Q.alloc_caches(h, 1)
+        bidx = torch.empty((1, L, budget), dtype=torch.int32, device="cuda")
+        out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device="cuda")
+        stats = torch.empty((1, L, 32), dtype=torch.float32, device="cuda")
+        kl = torch.empty((1, L), dtype=torch.float32, device="cuda")
+        dkl = torch.full((1, L), 1.0 / L, dtype=torch.float32, device="cuda")
+        dq = torch.empty((1, L, 4, 128), dtype=torch.float32, device="cuda")
+        dk = torch.empty((1, L, 128), dtype=torch.float32, device="cuda")
+        ws_is = Q.workspace(h, Q.QSA_OP_INDEX_SELECT, 1, L, 0)
+        ws_f = Q.workspace(h, Q.QSA_OP_TRAIN_FORWARD, 1, L, 0)
+        ws_b = Q.workspace(h, Q.QSA_OP_TRAIN_BACKWARD, 1, L, 0)
+
+        def step(ev):
+            ev[0].record()
+            Q.qsa_append(h, 1, L, 0, x["k"], x["v"], x["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"],
+                         c["kpend"])
+            Q.qsa_index_select(h, 1, L, 0, x["q_idx"], c["kbar_cache"], bidx, ws_is)
+            ev[1].record()
+            Q.qsa_train_forward(h, 1, L, x["q"], x["q_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], bidx, out,
+                                stats, kl, ws_f)
+            ev[2].record()
+            Q.qsa_train_backward_indexer(h, 1, L, x["q"], x["q_idx"], c["k_cache"], c["kbar_cache"], bidx, stats, dkl,
+                                         dq, dk, ws_b)
+            ev[3].record()
+
+        step(_events(4))
+        torch.cuda.synchronize()
+        evs = [_events(4) for _ in range(steps)]
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        tot = sel_ms + fwd_ms + bwd_ms
+        res[w.name] = {"ms": tot, "tok_s": L / (tot * 1e-3),
+                       "stage_ms": {"append_index_select": sel_ms, "train_forward": fwd_ms, "backward_indexer": bwd_ms},
+                       "mean_kl": float(kl.mean()), "indexer_loss_bytes_per_pass": train_bytes(L, budget)}
+        del x, c, bidx, out, stats, kl, dkl, dq, dk, ws_is, ws_f, ws_b, h
+        torch.cuda.empty_cache()
+    print(json.dumps({"train": res, "steps": steps, "dtype": "bf16", "data": "synthetic"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -472,6 +536,8 @@ def main():
                     help="measure QSA against dense attention (the pages' module speed-ups) instead")
     ap.add_argument("--c5", action="store_true",
                     help="measure the 1M-token configuration instead (chunked prefill, B=8 decode)")
+    ap.add_argument("--train", action="store_true",
+                    help="measure a training step (indexer loss forward and backward) instead")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -485,6 +551,9 @@ def main():
         return
     if args.ratios:
         run_ratios(max(1, min(args.steps, 3)))
+        return
+    if args.train:
+        run_train(max(1, min(args.steps, 5)))
         return
     if args.calib_copy:
         src = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")
