@@ -39,9 +39,10 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # the factors are what the counters read for a plain 1 GiB copy).  The counter
 # summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
 # is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (443127850.9 * 2.000 + 3145752.4 * 1.000) * 1024
+ATTEND_TRAFFIC_BYTES = (441841124.1 * 2.000 + 3145752.5 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "bbd89e59bb959260ffe8bd8a46fb786327f2c9ca4bbf7407c7b52778b48aa44f",
+    "k_attend.hip": "7f864f01cedc5aeb1f43b4d32a2cfd7201dcd1e3a1cc28a566de73bf35aea9ba",
+    "attend_parts.h": "6380072ac4cf7c2148b475ebd7833dca2036f88a0fb2cecd7b1c0c67de52fc09",
     "qsa_common.h": "174608b1e7eeed848fb54879a70fe06889ff333acfb43e741c5fe5247ffc1673",
 }
 
