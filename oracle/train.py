@@ -28,9 +28,14 @@ Readings (the pages give no formula for the loss):
     to each of the block's raw keys, and the bf16 roundings of the rotated
     operands pass gradients unchanged.
 
-Parity status: pinned by tests/test_oracle_pins.py (closed forms of the KL,
-finite differences of the loss and of the whole gradient chain, max pooling
-of a planted token, the dense special case against the plain attention).
+The attention's own gradient (the backbone's, attention_grads) is torch
+autograd through the same token sets: softmax over T(p), dout contracted
+with the output, rotations passing their transposes.
+
+Parity status: pinned by tests/test_oracle_train_pins.py (closed forms of the
+KL, finite differences of the losses and of the whole gradient chains, max
+pooling of a planted token, the dense special case against the plain
+attention and against torch's SDPA backward).
 """
 from __future__ import annotations
 
@@ -39,6 +44,7 @@ import torch
 
 from . import (LayerOracle, Params, bf16_bits_to_f32, core_rotate, indexer_keys, indexer_queries, own_block,
                rope_table, token_set)
+from . import softmax_scale as softmax_scale_of
 
 
 def teacher_row(lay: LayerOracle, pos: int, q_bits: np.ndarray, sel: np.ndarray):
@@ -149,3 +155,48 @@ def indexer_grads(q_idx_bits: np.ndarray, k_idx_bits: np.ndarray, teach, dkl: np
     gq = qi.grad.numpy() if qi.grad is not None else np.zeros(qi.shape)
     gk = ki.grad.numpy() if ki.grad is not None else np.zeros(ki.shape)
     return gq, gk
+
+
+def attention_loss(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sel: np.ndarray, dout: torch.Tensor, p: Params,
+                   rounded=None):
+    """sum_p <dout_p, out_p> of the sparse attention (the token sets of `sel`,
+    queries at positions 0..L-1) as a differentiable function of the raw q
+    [L][24][256], k [L][2][256] and v [L][2][256] (fp64 torch tensors).
+    `rounded` = (q~ values, k~ values) replaces the forward values of the
+    rotated operands (their bf16 roundings) with the gradient passing
+    unchanged; None keeps exact fp64."""
+    L = q.shape[0]
+    c, s = rope_table(np.arange(L), p)
+    ct = torch.from_numpy(c.astype(np.float64))[:, None, :]
+    st = torch.from_numpy(s.astype(np.float64))[:, None, :]
+    qt = _rot_t(q, ct, st)
+    kt = _rot_t(k, ct, st)
+    if rounded is not None:
+        qt = qt + (torch.from_numpy(rounded[0]) - qt).detach()
+        kt = kt + (torch.from_numpy(rounded[1]) - kt).detach()
+    sigma = softmax_scale_of(p)
+    grp = p.n_q_heads // p.n_kv_heads
+    loss = torch.zeros((), dtype=torch.float64)
+    for pos in range(L):
+        toks = torch.from_numpy(token_set(sel[pos], pos, p))
+        for g in range(p.n_kv_heads):
+            z = sigma * (qt[pos, g * grp:(g + 1) * grp] @ kt[toks, g].T)
+            out = torch.softmax(z, dim=1) @ v[toks, g]
+            loss = loss + torch.sum(dout[pos, g * grp:(g + 1) * grp] * out)
+    return loss
+
+
+def attention_grads(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, sel: np.ndarray, dout: np.ndarray,
+                    p: Params):
+    """Gradients of sum_p <dout_p, out_p> with respect to the raw q, k, v (fp64),
+    at the bf16 values the forward uses.  Returns (dq, dk, dv)."""
+    q = torch.tensor(bf16_bits_to_f32(q_bits), dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(bf16_bits_to_f32(k_bits), dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(bf16_bits_to_f32(v_bits), dtype=torch.float64, requires_grad=True)
+    L = q_bits.shape[0]
+    pos = np.arange(L)
+    rq = core_rotate(q_bits, pos, p).astype(np.float64)
+    rk = core_rotate(k_bits, pos, p).astype(np.float64)
+    loss = attention_loss(q, k, v, sel, torch.tensor(dout, dtype=torch.float64), p, rounded=(rq, rk))
+    loss.backward()
+    return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()

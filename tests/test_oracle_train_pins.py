@@ -174,3 +174,61 @@ def test_indexer_loss_forward_matches_the_pinned_scores():
         I = O.block_scores(qt, kbar)[blocks] if blocks.size else np.zeros(0)
         ref += dkl[r] * T.kl_of(A, I)[0]
     assert abs(got - ref) < 1e-4 * max(1.0, abs(ref))
+
+
+def test_attention_gradients_finite_differences():
+    """Gradients of sum_p <dout_p, out_p> with respect to the raw q, k, v (through
+    the rotations and the token sets) equal central differences of the loss."""
+    rng = np.random.default_rng(12)
+    p = O.Params(budget=2)
+    L = 18
+    q = torch.tensor(rng.standard_normal((L, 24, 256)) * 0.5, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(rng.standard_normal((L, 2, 256)) * 0.5, dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(rng.standard_normal((L, 2, 256)), dtype=torch.float64, requires_grad=True)
+    sel = np.full((L, 2), -1, dtype=np.int32)
+    for r in range(L):
+        o = r // 4
+        c = np.sort(rng.choice(o, size=min(2, o), replace=False)) if o else np.zeros(0, np.int64)
+        sel[r, :c.shape[0]] = c
+    dout = torch.tensor(rng.standard_normal((L, 24, 256)), dtype=torch.float64)
+    loss = T.attention_loss(q, k, v, sel, dout, p)
+    loss.backward()
+    h = 1e-6
+    for (t, idx) in [(q, (17, 3, 5)), (q, (9, 20, 40)), (q, (12, 13, 200)), (k, (2, 0, 10)), (k, (14, 1, 50)),
+                     (k, (5, 1, 130)), (v, (0, 1, 7)), (v, (16, 0, 255))]:
+        with torch.no_grad():
+            e = torch.zeros_like(t)
+            e[idx] = h
+            args = [q, k, v]
+            ip = [a + e if a is t else a for a in args]
+            im = [a - e if a is t else a for a in args]
+            fd = (T.attention_loss(*ip, sel, dout, p) - T.attention_loss(*im, sel, dout, p)) / (2 * h)
+        assert abs(float(fd) - float(t.grad[idx])) < 1e-6 * max(1.0, abs(float(fd))), idx
+
+
+def test_attention_gradients_dense_case_match_sdpa_backward():
+    """With every block selected, the gradients equal torch's SDPA backward
+    (causal, GQA 12:1, fp64) on the rotated operands, with dq and dk rotated
+    back by the transposed rotation (rotation by minus the angle)."""
+    rng = np.random.default_rng(13)
+    p = O.Params(budget=64)
+    L = 37
+    bf = lambda a: O.f32_to_bf16_bits(a.astype(np.float32))
+    qb, kb, vb = bf(rng.standard_normal((L, 24, 256))), bf(rng.standard_normal((L, 2, 256))), bf(
+        rng.standard_normal((L, 2, 256)))
+    sel = np.stack([O.select_blocks(np.zeros(r // 4), p.budget) for r in range(L)])
+    dout = rng.standard_normal((L, 24, 256))
+    dq, dk, dv = T.attention_grads(qb, kb, vb, sel, dout, p)
+    pos = np.arange(L)
+    qt = torch.tensor(O.core_rotate(qb, pos, p), dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(O.core_rotate(kb, pos, p), dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(O.bf16_bits_to_f32(vb), dtype=torch.float64, requires_grad=True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(1, 0, 2)[None], kt.permute(1, 0, 2)[None], v.permute(1, 0, 2)[None], is_causal=True,
+        scale=O.softmax_scale(p), enable_gqa=True)
+    (o[0].permute(1, 0, 2) * torch.tensor(dout)).sum().backward()
+    c, s = O.rope_table(pos, p)
+    back = lambda g: O.rotate(g.astype(np.float32), c[:, None, :], -s[:, None, :])   # R^T
+    np.testing.assert_allclose(dv, v.grad.numpy(), rtol=0, atol=1e-9)
+    np.testing.assert_allclose(dq, back(qt.grad.numpy()), rtol=0, atol=2e-5 * np.abs(dq).max())
+    np.testing.assert_allclose(dk, back(kt.grad.numpy()), rtol=0, atol=2e-5 * np.abs(dk).max())
