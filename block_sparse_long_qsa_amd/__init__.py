@@ -28,7 +28,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPP
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
            "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
            "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
-           "qsa_train_forward", "qsa_train_backward_indexer", "qsa_status_string", "qsa_last_hip_error"]
+           "qsa_train_forward", "qsa_train_backward_indexer", "qsa_train_backward_attention",
+           "qsa_status_string", "qsa_last_hip_error"]
 
 
 class QSAError(RuntimeError):
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_train_forward.restype = ctypes.c_int
     L.qsa_train_backward_indexer.argtypes = [vp, vp, i32, i64] + [vp] * 10 + [sz]
     L.qsa_train_backward_indexer.restype = ctypes.c_int
+    L.qsa_train_backward_attention.argtypes = [vp, vp, i32, i64] + [vp] * 10
+    L.qsa_train_backward_attention.restype = ctypes.c_int
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     L.qsa_last_hip_error.argtypes = []
@@ -304,6 +307,15 @@ def qsa_train_backward_indexer(h, B, L, q, q_idx, k_cache, kbar_cache, block_idx
                                             _ptr(stats, torch.float32, "stats"), _ptr(dkl, torch.float32, "dkl"),
                                             _ptr(dq_idx, torch.float32, "dq_idx"), _ptr(dk_idx, torch.float32, "dk_idx"),
                                             _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_train_backward_indexer")
+
+
+def qsa_train_backward_attention(h, B, L, q, k_cache, v_cache, block_idx, out, dout, stats, dq, dk, dv,
+                                 stream=None):
+    _check(lib().qsa_train_backward_attention(h.ptr, _stream(stream), B, L, _bf(q, "q"), _bf(k_cache, "k_cache"),
+                                              _bf(v_cache, "v_cache"), _ptr(block_idx, torch.int32, "block_idx"),
+                                              _bf(out, "out"), _bf(dout, "dout"), _ptr(stats, torch.float32, "stats"),
+                                              _ptr(dq, torch.float32, "dq"), _ptr(dk, torch.float32, "dk"),
+                                              _ptr(dv, torch.float32, "dv")), "qsa_train_backward_attention")
 
 
 def qsa_status_string(status: int) -> str:

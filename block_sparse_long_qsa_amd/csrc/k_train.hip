@@ -247,6 +247,212 @@ __global__ __launch_bounds__(256) void dk_idx_kernel(Tables tab, int32_t B, int6
     dk_idx[gid] = v;
 }
 
+// ---------------------------------------------------------------------------
+// Backward of the sparse attention (the backbone's gradient): for query p and
+// KV group g over its token set T(p), with P = exp(sigma S - lse) and
+// D_h = <dO_h, O_h>:
+//   dS = P (dO V^T - D),  dQ~ = sigma dS K~,  dK~ += sigma dS^T Q~,  dV += P^T dO,
+// then dq = R(p)^T dQ~ and dk = R(t)^T dK~ (dims 0..63).  One wave per (group,
+// query) walks the query's chunks like the forward; the contractions over
+// tokens and heads read operands that LDS holds in the layout each MFMA wants:
+// Q~^T and dO^T [dim][head] (once per query), P^T and dS^T [token][head], dS
+// [head][token] and the chunk's K~ [token][dim].  V enters token-major for
+// dP^T = V dO^T: each lane loads the 64 bytes holding 8 dims x 4 tokens of its
+// block and keeps its token's 8 values.  dQ~ stays in registers; dK~ and dV
+// are added to the fp32 outputs with atomics (a token is attended by many
+// queries).  Masked tokens (invalid entries, the own block past p) take part
+// as exact zeros: their cache slots may hold any bits.
+__global__ __launch_bounds__(64) void attend_backward_kernel(
+    Tables tab, int64_t L, int64_t nblk_cap, int budget, float c2, float sigma,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_idx, const bf16_t *__restrict__ out, const bf16_t *__restrict__ dout,
+    const float *__restrict__ stats, float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dv)
+{
+    __shared__ __attribute__((aligned(16))) bf16_t qT[kHeadDim][16];
+    __shared__ __attribute__((aligned(16))) bf16_t oT[kHeadDim][16];
+    __shared__ __attribute__((aligned(16))) bf16_t pT[32][16];
+    __shared__ __attribute__((aligned(16))) bf16_t sT[32][16];
+    __shared__ __attribute__((aligned(16))) bf16_t sH[16][32];
+    __shared__ __attribute__((aligned(16))) bf16_t kt[32][kHeadDim];
+    const int lane = threadIdx.x;
+    const int grp = blockIdx.x;
+    const int64_t i = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int64_t row = b * L + i;
+    const int64_t pos = i;
+    const int64_t o = pos / kBlock;
+    const int own_last = static_cast<int>(pos - o * kBlock);
+    const int n_sel = static_cast<int>(o < budget ? o : budget);
+    const int nchunks = list_chunks(n_sel, o, o);
+    const int h = lane & 15, g = lane >> 4;
+
+    bf16x8 qf[8], dof[8];
+    load_q_frags(q + row * kQHeads * kHeadDim, grp, pos, tab, qf);
+    const bf16_t *dorow = dout + (row * kQHeads + grp * kGroup + h) * kHeadDim;
+    const bf16_t *orow = out + (row * kQHeads + grp * kGroup + h) * kHeadDim;
+    float dsum = 0.f;
+    for (int s = 0; s < 8; ++s) {
+        if (h < kGroup) {
+            const u32x4 dw = *reinterpret_cast<const u32x4 *>(dorow + 32 * s + 8 * g);
+            const u32x4 ow = *reinterpret_cast<const u32x4 *>(orow + 32 * s + 8 * g);
+            dof[s] = __builtin_bit_cast(bf16x8, dw);
+            for (int m = 0; m < 4; ++m)
+                dsum += __uint_as_float(dw[m] << 16) * __uint_as_float(ow[m] << 16) +
+                        __uint_as_float(dw[m] & 0xFFFF0000u) * __uint_as_float(ow[m] & 0xFFFF0000u);
+        } else {
+            dof[s] = bf16x8{};
+        }
+    }
+    dsum += __shfl_xor(dsum, 16);
+    dsum += __shfl_xor(dsum, 32);
+    const float Dh = dsum;
+    const float lse2 = (h < kGroup) ? stats[row * kTrainStats + grp * kGroup + h] * kLog2e : 0.f;
+    // Q~^T and dO^T in LDS: lane (h, g) holds dims 32s + 8g + e of head h
+    for (int s = 0; s < 8; ++s) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, qf[s]);
+        const u32x4 dw = __builtin_bit_cast(u32x4, dof[s]);
+        for (int m = 0; m < 4; ++m) {
+            const int d = 32 * s + 8 * g + 2 * m;
+            qT[d][h] = static_cast<bf16_t>(qw[m] & 0xFFFFu);
+            qT[d + 1][h] = static_cast<bf16_t>(qw[m] >> 16);
+            oT[d][h] = static_cast<bf16_t>(dw[m] & 0xFFFFu);
+            oT[d + 1][h] = static_cast<bf16_t>(dw[m] >> 16);
+        }
+    }
+    f32x4 dqa[16];
+    for (int n = 0; n < 16; ++n) dqa[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const int32_t *sel = block_idx + row * budget;
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int lb = kChunkBlocks * c;
+        int64_t kblk[2], oblk[2];
+        uint32_t kmask[2], omask[2];
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, o, lb + 4 * t + (h >> 2), own_last, kblk[t], kmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, o, lb + 4 * t + g, own_last, oblk[t], omask[t]);
+        const int tk = h & 3;
+        for (int t = 0; t < 2; ++t) {              // one 16-token tile at a time (register pressure)
+            const bool krow = (kmask[t] >> tk) & 1u;
+            const bf16_t *ksrc = kc + kblk[t] * kBlockElems + tk * 32 + 8 * g;
+            const bf16_t *vblk = vc + kblk[t] * kBlockElems;
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 kf = krow ? *reinterpret_cast<const bf16x8 *>(ksrc + s * 128) : bf16x8{};
+                // dims d0 .. d0+7 of token tk: 64 B = 8 dims x 4 tokens, [dim][token]
+                const bf16_t *vsrc = vblk + (32 * s + 8 * g) * kBlock;
+                uint32_t wv[4];
+                for (int m = 0; m < 4; ++m) {
+                    const u32x4 w = *reinterpret_cast<const u32x4 *>(vsrc + 8 * m);
+                    const int sh = 16 * (tk & 1);
+                    const uint32_t lo = (w[tk >> 1] >> sh) & 0xFFFFu;
+                    const uint32_t hi = (w[2 + (tk >> 1)] >> sh) & 0xFFFFu;
+                    wv[m] = krow ? (lo | (hi << 16)) : 0u;
+                }
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{wv[0], wv[1], wv[2], wv[3]});
+                *reinterpret_cast<bf16x8 *>(&kt[16 * t + h][32 * s + 8 * g]) = kf;
+                // S^T, dP^T: lane holds tokens 0..3 of entry lb + 4t + g (chunk tokens 16t + 4g + j) for head h
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], sc, 0, 0, 0);
+                dp = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, dof[s], dp, 0, 0, 0);
+            }
+            for (int j = 0; j < 4; ++j) {
+                const bool valid = ((omask[t] >> j) & 1u) && h < kGroup;
+                const float pj = valid ? exp2f(sc[j] * c2 - lse2) : 0.f;
+                const float ds = valid ? pj * (dp[j] - Dh) : 0.f;
+                const int tok = 16 * t + 4 * g + j;
+                pT[tok][h] = f32_to_bf16(pj);
+                sT[tok][h] = f32_to_bf16(ds);
+                sH[h][tok] = f32_to_bf16(ds);
+            }
+        }
+        __syncthreads();
+        // dV += P^T dO and dK~ += sigma dS^T Q~: 16x16x16 tiles, rows = chunk tokens, cols = dims
+        for (int t = 0; t < 2; ++t) {
+            const bf16x4 pa = *reinterpret_cast<const bf16x4 *>(&pT[16 * t + h][4 * g]);
+            const bf16x4 sa = *reinterpret_cast<const bf16x4 *>(&sT[16 * t + h][4 * g]);
+            const bool ev = omask[t] != 0u;
+            const int64_t tok0 = kBlock * oblk[t];
+            for (int n = 0; n < 16; ++n) {
+                const bf16x4 ob = *reinterpret_cast<const bf16x4 *>(&oT[16 * n + h][4 * g]);
+                const bf16x4 qb = *reinterpret_cast<const bf16x4 *>(&qT[16 * n + h][4 * g]);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 av = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ob, zero, 0, 0, 0);
+                const f32x4 ak = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(sa, qb, zero, 0, 0, 0);
+                if (!ev) continue;
+                for (int j = 0; j < 4; ++j) {
+                    if (!((omask[t] >> j) & 1u)) continue;
+                    const int64_t idx = ((b * L + tok0 + j) * kKVHeads + grp) * kHeadDim + 16 * n + h;
+                    atomicAdd(dv + idx, av[j]);
+                    atomicAdd(dk + idx, sigma * ak[j]);
+                }
+            }
+        }
+        // dQ~ += dS K~: 16x16x32 tiles, rows = heads, cols = dims, k = the chunk's 32 tokens
+        const bf16x8 sa8 = *reinterpret_cast<const bf16x8 *>(&sH[h][8 * g]);
+        for (int n = 0; n < 16; ++n) {
+            uint32_t kw[4];
+            for (int m = 0; m < 4; ++m)
+                kw[m] = static_cast<uint32_t>(kt[8 * g + 2 * m][16 * n + h]) |
+                        (static_cast<uint32_t>(kt[8 * g + 2 * m + 1][16 * n + h]) << 16);
+            dqa[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa8, __builtin_bit_cast(bf16x8, u32x4{kw[0], kw[1], kw[2], kw[3]}),
+                                                             dqa[n], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+    // dq = sigma R(p)^T dQ~: lane holds dims 16n + h of heads 4g + j; the rotary
+    // partner of dim d < 32 (tile n < 2) is dim d + 32 (tile n + 2), same lane
+    const float *cs = tab.cos + pos * kPairs;
+    const float *sn = tab.sin + pos * kPairs;
+    for (int n = 0; n < 2; ++n) {
+        const int d = 16 * n + h;
+        for (int j = 0; j < 4; ++j) {
+            const float a = dqa[n][j], bb = dqa[n + 2][j];
+            dqa[n][j] = a * cs[d] + bb * sn[d];
+            dqa[n + 2][j] = bb * cs[d] - a * sn[d];
+        }
+    }
+    for (int j = 0; j < 4; ++j) {
+        const int head = 4 * g + j;
+        if (head >= kGroup) continue;
+        float *dst = dq + (row * kQHeads + grp * kGroup + head) * kHeadDim;
+        for (int n = 0; n < 16; ++n) dst[16 * n + h] = sigma * dqa[n][j];
+    }
+}
+
+// dk[b][t][g] = R(t)^T dK~[b][t][g] in place (dims 0..63), one thread per
+// (token, group, rotary pair).
+__global__ __launch_bounds__(256) void dk_unrotate_kernel(Tables tab, int32_t B, int64_t L, float *__restrict__ dk)
+{
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= static_cast<int64_t>(B) * L * kKVHeads * kPairs) return;
+    const int d = static_cast<int>(gid % kPairs);
+    const int64_t rg = gid / kPairs;                   // (b, t, g)
+    const int64_t t = (rg / kKVHeads) % L;
+    float *x = dk + rg * kHeadDim;
+    const float c = tab.cos[t * kPairs + d], s = tab.sin[t * kPairs + d];
+    const float a = x[d], bb = x[d + kPairs];
+    x[d] = a * c + bb * s;
+    x[d + kPairs] = bb * c - a * s;
+}
+
+hipError_t launch_attend_backward(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t nblk_cap, int budget,
+                                  float sigma, const bf16_t *q, const bf16_t *k_cache, const bf16_t *v_cache,
+                                  const int32_t *block_idx, const bf16_t *out, const bf16_t *dout, const float *stats,
+                                  float *dq, float *dk, float *dv)
+{
+    if (L <= 0) return hipSuccess;
+    hipLaunchKernelGGL(attend_backward_kernel, dim3(kKVHeads, static_cast<unsigned>(L), static_cast<unsigned>(B)),
+                       dim3(64), 0, st, tab, L, nblk_cap, budget, sigma * kLog2e, sigma, q, k_cache, v_cache, block_idx,
+                       out, dout, stats, dq, dk, dv);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t total = static_cast<int64_t>(B) * L * kKVHeads * kPairs;
+    hipLaunchKernelGGL(dk_unrotate_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, st, tab, B, L,
+                       dk);
+    return hipGetLastError();
+}
+
 hipError_t launch_train_kl(const Tables &tab, hipStream_t st, bool backward, int32_t B, int64_t L, int64_t nblk_cap,
                            int budget, float sigma, const bf16_t *q, const bf16_t *k_cache, const bf16_t *kbar,
                            const bf16_t *qrot, const int32_t *block_idx, float *stats, float *kl, const float *dkl,

@@ -49,6 +49,9 @@ hipError_t launch_train_kl(const Tables &, hipStream_t, bool, int32_t, int64_t, 
                            const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
                            const float *, float *, float *);
 hipError_t launch_dk_idx(const Tables &, hipStream_t, int32_t, int64_t, int64_t, const float *, float *);
+hipError_t launch_attend_backward(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int, float, const bf16_t *,
+                                  const bf16_t *, const bf16_t *, const int32_t *, const bf16_t *, const bf16_t *,
+                                  const float *, float *, float *, float *);
 hipError_t launch_token_keys(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, const bf16_t *, bf16_t *);
 hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t,
                                       const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, uint32_t *);
@@ -627,6 +630,25 @@ qsa_status qsa_train_backward_indexer(const qsa_handle *h, void *stream, int32_t
         e = launch_train_kl(tables(h), st, true, B, L, nbc, h->p.budget_blocks, h->sigma, q, k_cache, kbar_cache, qrot,
                             block_idx, const_cast<float *>(stats), nullptr, dkl, dq_idx, dkbar);
     if (e == hipSuccess) e = launch_dk_idx(tables(h), st, B, L, nbc, dkbar, dk_idx);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
+                                        const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *block_idx,
+                                        const uint16_t *out, const uint16_t *dout, const float *stats, float *dq,
+                                        float *dk, float *dv) {
+    qsa_status s = check_chunk(h, B, L, 0, true);
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q, k_cache, v_cache, block_idx, out, dout, stats, dq, dk, dv})) != QSA_OK) return s;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t n = static_cast<int64_t>(B) * L * kKVHeads * kHeadDim;
+    hipError_t e = launch_zero_words(st, reinterpret_cast<int32_t *>(dk), n);
+    if (e == hipSuccess) e = launch_zero_words(st, reinterpret_cast<int32_t *>(dv), n);
+    if (e == hipSuccess)
+        e = launch_attend_backward(tables(h), st, B, L, nblk_cap(h), h->p.budget_blocks, h->sigma, q, k_cache, v_cache,
+                                   block_idx, out, dout, stats, dq, dk, dv);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

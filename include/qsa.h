@@ -308,9 +308,9 @@ qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, 
  * and raw indexer keys, dk_idx [B][L][128] fp32 (0 for the tokens of a
  * trailing partial block), holding the teacher constant: dkl/dI_b = s_b - pi_b,
  * ReLU' = [logit > 0], transposed rotations, 1/4 per pooled key.  stats: the
- * forward's.  The gradient of the attention output with respect to q, k, v is
- * not computed here.  ws: qsa_workspace_size(QSA_OP_TRAIN_BACKWARD, B, L, 0)
- * bytes.  Both: q_idx [B][L][4][128], q [B][L][24][256] raw bf16; errors as for
+ * forward's.  The gradient of the attention output with respect to q, k, v
+ * comes from qsa_train_backward_attention.
+ * ws: qsa_workspace_size(QSA_OP_TRAIN_BACKWARD, B, L, 0) bytes.  Both: q_idx [B][L][4][128], q [B][L][24][256] raw bf16; errors as for
  * qsa_forward with q_offset = 0. */
 qsa_status qsa_train_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
                              const uint16_t *q_idx, const uint16_t *k_cache, const uint16_t *v_cache,
@@ -320,6 +320,22 @@ qsa_status qsa_train_backward_indexer(const qsa_handle *h, void *stream, int32_t
                                       const uint16_t *q_idx, const uint16_t *k_cache, const uint16_t *kbar_cache,
                                       const int32_t *block_idx, const float *stats, const float *dkl,
                                       float *dq_idx, float *dk_idx, void *ws, size_t ws_bytes);
+
+/* Backward of the sparse attention (the backbone's gradient in the training
+ * path): with P = softmax over T(p) of the scaled logits (from the per-head
+ * log-sum-exp in stats, as qsa_train_forward wrote it) and D_h = <dout_h, out_h>,
+ * dS = P (dout V^T - D); dq [B][L][24][256] fp32 = gradient with respect to the
+ * raw q (sigma dS K~ rotated back at p); dk, dv [B][L][2][256] fp32 = gradients
+ * with respect to the raw k (rotated back at each token's position) and v,
+ * summed over every query that attends the token.  out [B][L][24][256] bf16 is
+ * qsa_train_forward's output, dout the same shape (the upstream gradient);
+ * block_idx and the caches as for qsa_train_forward.  dk and dv are cleared and
+ * accumulated with atomics (the summation order, and so the last bits, can vary
+ * between runs).  No workspace.  Errors as for qsa_train_forward. */
+qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32_t B, int64_t L, const uint16_t *q,
+                                        const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *block_idx,
+                                        const uint16_t *out, const uint16_t *dout, const float *stats, float *dq,
+                                        float *dk, float *dv);
 
 /* Static string for a status code. */
 const char *qsa_status_string(qsa_status s);

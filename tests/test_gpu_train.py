@@ -15,7 +15,11 @@ Acceptance (derived from the arithmetic):
   * kl also moves with the scores: dKL/dI_b = s_b - pi_b, so |d| <= 2 max|dI|
     (about 1e-4 |I| <= 5e-3 here); a per-head error of the log-sum-exp scales
     all of that head's probabilities alike and cancels in pi = A / Z;
-  * gradients: normwise ||gpu - ref|| / ||ref|| <= 5e-3 and element-wise
+  * attention gradients (dq, dk, dv): normwise and max-element errors <= 1e-2
+    relative to the oracle's norm / largest element -- P and dS enter the
+    MFMAs rounded to bf16 (2^-9 relative each) and D = <dout, out> uses the
+    bf16 output;
+  * indexer gradients: normwise ||gpu - ref|| / ||ref|| <= 5e-3 and element-wise
     |d| <= 5e-3 max|ref| per tensor -- the coefficients s - pi carry the scores'
     relative error (1e-4 |I| <= 5e-3 in s); a ReLU mask flips only for a logit
     within fp32 rounding of 0.
@@ -115,3 +119,43 @@ def test_train_dense_teacher():
     """Stage-1 reading: the budget covers every block, so the teacher is the
     dense max-pooled attention distribution over all complete blocks."""
     print("worst deviations", _check(1, 203, 64, 72))
+
+
+def test_train_attention_backward():
+    """qsa_train_backward_attention against the oracle's autograd gradients of
+    sum_p <dout_p, out_p> with respect to the raw q, k, v."""
+    B, L, budget = 2, 150, 16
+    w = synth.Workload("t", "prefill", B, L, budget, 6, "random", 73)
+    x = synth.prefill_inputs(w, "cpu")
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    p = O.Params(budget=budget)
+    h = Q.Handle(max_ctx=(L + 3) // 4 * 4, budget_blocks=budget)
+    c = Q.alloc_caches(h, B)
+    Q.qsa_append(h, B, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    sel = np.stack([_oracle_selection(x, b, p, L) for b in range(B)]).astype(np.int32)
+    bidx = torch.from_numpy(sel).to(DEV)
+    out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    stats = torch.empty((B, L, 32), dtype=torch.float32, device=DEV)
+    kl = torch.empty((B, L), dtype=torch.float32, device=DEV)
+    Q.qsa_train_forward(h, B, L, xd["q"], xd["q_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], bidx, out, stats,
+                        kl, Q.workspace(h, Q.QSA_OP_TRAIN_FORWARD, B, L, 0))
+    g = torch.Generator().manual_seed(74)
+    dout = torch.randn((B, L, 24, 256), generator=g).to(torch.bfloat16)
+    dq = torch.empty((B, L, 24, 256), dtype=torch.float32, device=DEV)
+    dk = torch.empty((B, L, 2, 256), dtype=torch.float32, device=DEV)
+    dv = torch.empty((B, L, 2, 256), dtype=torch.float32, device=DEV)
+    Q.qsa_train_backward_attention(h, B, L, xd["q"], c["k_cache"], c["v_cache"], bidx, out, dout.to(DEV), stats, dq,
+                                   dk, dv)
+    torch.cuda.synchronize()
+    worst = {}
+    for b in range(B):
+        rq, rk, rv = T.attention_grads(bits(x["q"][b]), bits(x["k"][b]), bits(x["v"][b]), sel[b],
+                                       dout[b].float().numpy().astype(np.float64), p)
+        for name, got, ref in (("dq", dq[b].cpu().numpy(), rq), ("dk", dk[b].cpu().numpy(), rk),
+                               ("dv", dv[b].cpu().numpy(), rv)):
+            nw = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+            mx = np.abs(got - ref).max() / np.abs(ref).max()
+            worst[name] = max(worst.get(name, 0.0), nw)
+            worst[name + "_max"] = max(worst.get(name + "_max", 0.0), mx)
+            assert nw <= 1e-2 and mx <= 1e-2, (name, b, nw, mx)
+    print("worst deviations", worst)
