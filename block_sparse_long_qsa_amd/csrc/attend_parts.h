@@ -57,10 +57,24 @@ __device__ __forceinline__ void load_q_frags(const bf16_t *qrow /*[24][256] of t
 // to own_last.  A selection made at the query itself has o0 = o (the tail is
 // the own block alone); one reused from an earlier position has o0 = its own
 // block there.
+template <bool kBranchFree = false>
 __device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o0, int64_t o, int li,
                                            int own_last, int64_t &blk, uint32_t &tmask)
 {
-    if (li < n_sel) {
+    if constexpr (kBranchFree) {
+        // The list read unconditionally (index clamped into the list), no
+        // branches: a chunk's entries are loaded together instead of one wait
+        // each.  The prefill walk gains about 1%; the decode split kernel
+        // measured slower with it.
+        const int64_t id = sel[li < n_sel ? li : 0];
+        const bool in_sel = li < n_sel;
+        const int64_t tb = o0 + (li - n_sel);
+        const bool in_tail = !in_sel && tb <= o;
+        const bool ok = in_sel && id >= 0 && id < o0;
+        const uint32_t tail_mask = (tb == o) ? (1u << (own_last + 1)) - 1u : 0xFu;
+        blk = ok ? id : (in_tail ? tb : 0);
+        tmask = ok ? 0xFu : (in_tail ? tail_mask : 0u);
+    } else if (li < n_sel) {
         const int64_t id = sel[li];
         const bool ok = id >= 0 && id < o0;
         blk = ok ? id : 0;

@@ -33,6 +33,7 @@ struct RowState {
 };
 
 // Walk chunks [c_lo, c_hi) of one (query, group) token list.
+template <bool kBranchFree>
 __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
                                               const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
                                               int n_sel, int64_t o0, int64_t o, int own_last, int c_lo, int c_hi,
@@ -46,7 +47,7 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         // ---- gather K~ (A operand of S^T): tile t, token row r -> list entry lb + 4t + r/4
         int64_t kblk[2];
         uint32_t kmask[2];
-        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry<kBranchFree>(sel, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
         bf16x8 kf[2][8];
         for (int t = 0; t < 2; ++t) {
             const bf16_t *src = kc + kblk[t] * kBlockElems + (r & 3) * 32 + 8 * g;
@@ -55,7 +56,7 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         // ---- gather V (A operand of O^T): list entries lb + g and lb + 4 + g, dim 16n + r
         int64_t vblk[2];
         uint32_t vmask[2];
-        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o0, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry<kBranchFree>(sel, n_sel, o0, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
         u32x2 vraw[16][2];
         for (int t = 0; t < 2; ++t) {
             const bf16_t *src = vc + vblk[t] * kBlockElems + r * kBlock;
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 
     RowState st;
     init_state(st);
-    attend_chunks(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
+    attend_chunks<true>(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
 
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(
 
     RowState st;
     init_state(st);
-    attend_chunks(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
+    attend_chunks<true>(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
 
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
         load_q_frags(q + b * kQHeads * kHeadDim, grp, pos, tab, qf);
         const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
         const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-        attend_chunks(qf, kc, vc, block_idx + b * budget, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
+        attend_chunks<false>(qf, kc, vc, block_idx + b * budget, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
     }
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
