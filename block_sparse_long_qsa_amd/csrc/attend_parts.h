@@ -57,6 +57,24 @@ __device__ __forceinline__ void load_q_frags(const bf16_t *qrow /*[24][256] of t
 // to own_last.  A selection made at the query itself has o0 = o (the tail is
 // the own block alone); one reused from an earlier position has o0 = its own
 // block there.
+// Entry li of the list from its (already loaded) selection value id, branch-free.
+__device__ __forceinline__ void entry_from_id(int64_t id, int n_sel, int64_t o0, int64_t o, int li, int own_last,
+                                              int64_t &blk, uint32_t &tmask)
+{
+    const bool in_sel = li < n_sel;
+    const int64_t tb = o0 + (li - n_sel);
+    const bool in_tail = !in_sel && tb <= o;
+    const bool ok = in_sel && id >= 0 && id < o0;
+    const uint32_t tail_mask = (tb == o) ? (1u << (own_last + 1)) - 1u : 0xFu;
+    blk = ok ? id : (in_tail ? tb : 0);
+    tmask = ok ? 0xFu : (in_tail ? tail_mask : 0u);
+}
+
+// The selection value entry li reads (clamped into the list; ignored past it).
+__device__ __forceinline__ int32_t entry_id(const int32_t *sel, int n_sel, int li) {
+    return sel[li < n_sel ? li : 0];
+}
+
 template <bool kBranchFree = false>
 __device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o0, int64_t o, int li,
                                            int own_last, int64_t &blk, uint32_t &tmask)
@@ -66,14 +84,7 @@ __device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_
         // branches: a chunk's entries are loaded together instead of one wait
         // each.  The prefill walk gains about 1%; the decode split kernel
         // measured slower with it.
-        const int64_t id = sel[li < n_sel ? li : 0];
-        const bool in_sel = li < n_sel;
-        const int64_t tb = o0 + (li - n_sel);
-        const bool in_tail = !in_sel && tb <= o;
-        const bool ok = in_sel && id >= 0 && id < o0;
-        const uint32_t tail_mask = (tb == o) ? (1u << (own_last + 1)) - 1u : 0xFu;
-        blk = ok ? id : (in_tail ? tb : 0);
-        tmask = ok ? 0xFu : (in_tail ? tail_mask : 0u);
+        entry_from_id(entry_id(sel, n_sel, li), n_sel, o0, o, li, own_last, blk, tmask);
     } else if (li < n_sel) {
         const int64_t id = sel[li];
         const bool ok = id >= 0 && id < o0;
