@@ -200,3 +200,70 @@ def attention_grads(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, 
     loss = attention_loss(q, k, v, sel, torch.tensor(dout, dtype=torch.float64), p, rounded=(rq, rk))
     loss.backward()
     return q.grad.numpy(), k.grad.numpy(), v.grad.numpy()
+
+
+def attention_grads_rows(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, sel: np.ndarray,
+                         dout: np.ndarray, rows, p: Params):
+    """attention_grads when only the query rows `rows` carry an upstream
+    gradient (dout [n][24][256] for those rows), for long sequences: the graph
+    holds those rows and the tokens they attend.  Returns (dq [n][24][256],
+    tokens [m] (positions), dk [m][2][256], dv [m][2][256]); every other
+    token's gradient is zero."""
+    rows = np.asarray(list(rows), dtype=np.int64)
+    tsets = [token_set(sel[r], int(r), p) for r in rows]
+    toks = np.unique(np.concatenate(tsets))
+    where = {int(t): i for i, t in enumerate(toks)}
+    q = torch.tensor(bf16_bits_to_f32(q_bits[rows]), dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(bf16_bits_to_f32(k_bits[toks]), dtype=torch.float64, requires_grad=True)
+    v = torch.tensor(bf16_bits_to_f32(v_bits[toks]), dtype=torch.float64, requires_grad=True)
+    cq, sq = rope_table(rows, p)
+    ck, sk = rope_table(toks, p)
+    qt = _rot_t(q, torch.from_numpy(cq.astype(np.float64))[:, None, :], torch.from_numpy(sq.astype(np.float64))[:, None, :])
+    kt = _rot_t(k, torch.from_numpy(ck.astype(np.float64))[:, None, :], torch.from_numpy(sk.astype(np.float64))[:, None, :])
+    qt = qt + (torch.from_numpy(core_rotate(q_bits[rows], rows, p).astype(np.float64)) - qt).detach()
+    kt = kt + (torch.from_numpy(core_rotate(k_bits[toks], toks, p).astype(np.float64)) - kt).detach()
+    sigma = softmax_scale_of(p)
+    grp = p.n_q_heads // p.n_kv_heads
+    d = torch.tensor(dout, dtype=torch.float64)
+    loss = torch.zeros((), dtype=torch.float64)
+    for i, ts in enumerate(tsets):
+        ix = torch.tensor([where[int(t)] for t in ts])
+        for g in range(p.n_kv_heads):
+            z = sigma * (qt[i, g * grp:(g + 1) * grp] @ kt[ix, g].T)
+            loss = loss + torch.sum(d[i, g * grp:(g + 1) * grp] * (torch.softmax(z, dim=1) @ v[ix, g]))
+    loss.backward()
+    return q.grad.numpy(), toks, k.grad.numpy(), v.grad.numpy()
+
+
+def indexer_grads_rows(q_idx_bits: np.ndarray, k_idx_bits: np.ndarray, teach, dkl: np.ndarray, rows, p: Params):
+    """indexer_grads when only the query rows `rows` carry an upstream gradient
+    (q_idx_bits [n][4][128] and teach / dkl for those rows; k_idx_bits [n_tok][128]
+    for the whole sequence).  Returns (dq_idx [n][4][128], dk_idx [n_tok][128])."""
+    rows = np.asarray(list(rows), dtype=np.int64)
+    used = np.unique(np.concatenate([bl for _, bl in teach] + [np.zeros(0, np.int64)])).astype(np.int64)
+    where = {int(b): i for i, b in enumerate(used)}
+    qi = torch.tensor(bf16_bits_to_f32(q_idx_bits), dtype=torch.float64, requires_grad=True)
+    tok = (used[:, None] * p.block + np.arange(p.block)[None, :]).reshape(-1)
+    ki = torch.tensor(bf16_bits_to_f32(k_idx_bits[tok]), dtype=torch.float64, requires_grad=True)
+    cq, sq = rope_table(rows, p)
+    qt = _rot_t(qi, torch.from_numpy(cq.astype(np.float64))[:, None, :], torch.from_numpy(sq.astype(np.float64))[:, None, :])
+    qt = qt + (torch.from_numpy(indexer_queries(q_idx_bits, rows, p).astype(np.float64)) - qt).detach()
+    pooled = ki.reshape(used.shape[0], p.block, -1).mean(dim=1)
+    cb, sb = rope_table(used * p.block, p)
+    kb = _rot_t(pooled, torch.from_numpy(cb.astype(np.float64)), torch.from_numpy(sb.astype(np.float64)))
+    kb = kb + (torch.from_numpy(indexer_keys(k_idx_bits, p)[used].astype(np.float64)) - kb).detach()
+    loss = torch.zeros((), dtype=torch.float64)
+    for i, (A, blocks) in enumerate(teach):
+        if blocks.shape[0] <= 1 or dkl[i] == 0.0:
+            continue
+        I = torch.relu(qt[i] @ kb[torch.tensor([where[int(b)] for b in blocks])].T).sum(dim=0)
+        pi = torch.from_numpy(A / A.sum())
+        logpi = torch.where(pi > 0, torch.log(torch.where(pi > 0, pi, torch.ones_like(pi))), torch.zeros_like(pi))
+        loss = loss + float(dkl[i]) * torch.sum(pi * (logpi - torch.log_softmax(I, dim=0)))
+    gk = np.zeros((k_idx_bits.shape[0], k_idx_bits.shape[1]))
+    gq = np.zeros(qi.shape)
+    if loss.requires_grad:
+        loss.backward()
+        gq = qi.grad.numpy()
+        gk[tok] = ki.grad.numpy()
+    return gq, gk

@@ -159,3 +159,76 @@ def test_train_attention_backward():
             worst[name + "_max"] = max(worst.get(name + "_max", 0.0), mx)
             assert nw <= 1e-2 and mx <= 1e-2, (name, b, nw, mx)
     print("worst deviations", worst)
+
+
+def test_train_fullsize_32k_sampled_rows():
+    """The 32,768-token workload at budget 512: every kernel of the training
+    step runs over all rows; sampled rows carry the upstream gradients (dkl and
+    dout zero elsewhere), so the oracle checks those rows' outputs, KL and
+    query gradients and every token's key and value gradients.  The sampled
+    rows use the oracle's selection; the other rows the most recent blocks."""
+    w = synth.WORKLOADS["prefill_32k"]
+    L, budget = w.seq_len, w.budget
+    x = synth.prefill_inputs(w, "cpu")
+    xd = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in x.items()}
+    p = O.Params(budget=budget)
+    rows = [3, 517, 2051, 8190, 16385, 24576, 32766, 32767]
+    sel = np.full((L, budget), -1, dtype=np.int32)
+    for i in range(L):
+        o = i // 4
+        n = min(o, budget)
+        sel[i, :n] = np.arange(o - n, o)
+    kbar = O.indexer_keys(bits(x["k_idx"][0]), p)
+    for i in rows:
+        qt = O.indexer_queries(bits(x["q_idx"][0, i:i + 1]), np.array([i]), p)[0]
+        sel[i] = O.select_blocks(O.block_scores(qt, kbar[:i // 4]), budget)
+    h = Q.Handle(max_ctx=L, budget_blocks=budget)
+    c = Q.alloc_caches(h, 1)
+    Q.qsa_append(h, 1, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    bidx = torch.from_numpy(sel[None]).to(DEV)
+    out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    stats = torch.empty((1, L, 32), dtype=torch.float32, device=DEV)
+    kl = torch.empty((1, L), dtype=torch.float32, device=DEV)
+    Q.qsa_train_forward(h, 1, L, xd["q"], xd["q_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], bidx, out, stats,
+                        kl, Q.workspace(h, Q.QSA_OP_TRAIN_FORWARD, 1, L, 0))
+    g = np.random.default_rng(75)
+    dkl = np.zeros((1, L), dtype=np.float32)
+    dkl[0, rows] = g.random(len(rows)) + 0.5
+    dout = torch.zeros((1, L, 24, 256), dtype=torch.bfloat16)
+    dout[0, rows] = torch.from_numpy(g.standard_normal((len(rows), 24, 256)).astype(np.float32)).to(torch.bfloat16)
+    dq_idx = torch.empty((1, L, 4, 128), dtype=torch.float32, device=DEV)
+    dk_idx = torch.empty((1, L, 128), dtype=torch.float32, device=DEV)
+    Q.qsa_train_backward_indexer(h, 1, L, xd["q"], xd["q_idx"], c["k_cache"], c["kbar_cache"], bidx, stats,
+                                 torch.from_numpy(dkl).to(DEV), dq_idx, dk_idx,
+                                 Q.workspace(h, Q.QSA_OP_TRAIN_BACKWARD, 1, L, 0))
+    dq = torch.empty((1, L, 24, 256), dtype=torch.float32, device=DEV)
+    dk = torch.empty((1, L, 2, 256), dtype=torch.float32, device=DEV)
+    dv = torch.empty((1, L, 2, 256), dtype=torch.float32, device=DEV)
+    Q.qsa_train_backward_attention(h, 1, L, xd["q"], c["k_cache"], c["v_cache"], bidx, out, dout.to(DEV), stats, dq,
+                                   dk, dv)
+    torch.cuda.synchronize()
+    lay = oracle_layer(x, 0, p)
+    res = T.train_rows(lay, rows, bits(x["q"][0]), bits(x["q_idx"][0]), sel)
+    o_np, st_np, kl_np = f32(out[0]), stats[0].cpu().numpy(), kl[0].cpu().numpy()
+    for i, r in zip(rows, res):
+        check_out(o_np[i], r["out"], "row %d" % i)
+        assert np.abs(st_np[i, :24] - r["lse"]).max() <= 3e-3, i
+        assert abs(kl_np[i] - r["kl"]) <= 1e-2 + 1e-2 * abs(r["kl"]), (i, kl_np[i], r["kl"])
+    teach = [(r["A"], r["blocks"]) for r in res]
+    gq, gk = T.indexer_grads_rows(bits(x["q_idx"][0, rows]), bits(x["k_idx"][0]), teach, dkl[0, rows].astype(np.float64),
+                                  rows, p)
+    dqi, dki = dq_idx[0].cpu().numpy(), dk_idx[0].cpu().numpy()
+    others = np.setdiff1d(np.arange(L), rows)
+    assert np.all(dqi[others] == 0)
+    for name, got, ref in (("dq_idx", dqi[rows], gq), ("dk_idx", dki, gk)):
+        assert np.linalg.norm(got - ref) <= 5e-3 * np.linalg.norm(ref), name
+        assert np.abs(got - ref).max() <= 5e-3 * np.abs(ref).max(), name
+    aq, toks, ak, av = T.attention_grads_rows(bits(x["q"][0]), bits(x["k"][0]), bits(x["v"][0]), sel,
+                                              dout[0, rows].float().numpy().astype(np.float64), rows, p)
+    dq_np, dk_np, dv_np = dq[0].cpu().numpy(), dk[0].cpu().numpy(), dv[0].cpu().numpy()
+    assert np.all(dq_np[others] == 0)
+    fk, fv = np.zeros_like(dk_np), np.zeros_like(dv_np)
+    fk[toks], fv[toks] = ak, av
+    for name, got, ref in (("dq", dq_np[rows], aq), ("dk", dk_np, fk), ("dv", dv_np, fv)):
+        assert np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref), name
+        assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max(), name

@@ -232,3 +232,41 @@ def test_attention_gradients_dense_case_match_sdpa_backward():
     np.testing.assert_allclose(dv, v.grad.numpy(), rtol=0, atol=1e-9)
     np.testing.assert_allclose(dq, back(qt.grad.numpy()), rtol=0, atol=2e-5 * np.abs(dq).max())
     np.testing.assert_allclose(dk, back(kt.grad.numpy()), rtol=0, atol=2e-5 * np.abs(dk).max())
+
+
+def test_row_subset_gradients_equal_the_full_ones():
+    """The row-subset forms (for long sequences) give the full forms' gradients
+    when only those rows carry an upstream gradient."""
+    rng = np.random.default_rng(14)
+    p = O.Params(budget=3)
+    L = 30
+    bf = lambda a: O.f32_to_bf16_bits(a.astype(np.float32))
+    qb, kb, vb = bf(rng.standard_normal((L, 24, 256))), bf(rng.standard_normal((L, 2, 256))), bf(
+        rng.standard_normal((L, 2, 256)))
+    qib, kib = bf(rng.standard_normal((L, 4, 128))), bf(rng.standard_normal((L, 128)))
+    sel = np.full((L, 3), -1, dtype=np.int32)
+    for r in range(L):
+        o = r // 4
+        c = np.sort(rng.choice(o, size=min(3, o), replace=False)) if o else np.zeros(0, np.int64)
+        sel[r, :c.shape[0]] = c
+    rows = [5, 17, 29]
+    dout = np.zeros((L, 24, 256))
+    dout[rows] = rng.standard_normal((3, 24, 256))
+    dq, dk, dv = T.attention_grads(qb, kb, vb, sel, dout, p)
+    sq, toks, sk, sv = T.attention_grads_rows(qb, kb, vb, sel, dout[rows], rows, p)
+    np.testing.assert_allclose(sq, dq[rows], rtol=0, atol=1e-12)
+    fk, fv = np.zeros_like(dk), np.zeros_like(dv)
+    fk[toks], fv[toks] = sk, sv
+    np.testing.assert_allclose(fk, dk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(fv, dv, rtol=0, atol=1e-12)
+    teach = []
+    for r in range(L):
+        o = r // 4
+        bl = sel[r][(sel[r] >= 0) & (sel[r] < o)].astype(np.int64)
+        teach.append((rng.random(bl.shape[0]) + 0.05, bl))
+    dkl = np.zeros(L)
+    dkl[rows] = [0.7, 1.3, 0.4]
+    gq, gk = T.indexer_grads(qib, kib, teach, dkl, p)
+    hq, hk = T.indexer_grads_rows(qib[rows], kib, [teach[r] for r in rows], dkl[rows], rows, p)
+    np.testing.assert_allclose(hq, gq[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hk, gk, rtol=0, atol=1e-12)
