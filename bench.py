@@ -39,11 +39,11 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # the factors are what the counters read for a plain 1 GiB copy).  The counter
 # summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
 # is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (441841124.1 * 2.000 + 3145752.5 * 1.000) * 1024
+ATTEND_TRAFFIC_BYTES = (430678081.2 * 2.000 + 3145785.7 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "7f864f01cedc5aeb1f43b4d32a2cfd7201dcd1e3a1cc28a566de73bf35aea9ba",
-    "attend_parts.h": "6380072ac4cf7c2148b475ebd7833dca2036f88a0fb2cecd7b1c0c67de52fc09",
-    "qsa_common.h": "174608b1e7eeed848fb54879a70fe06889ff333acfb43e741c5fe5247ffc1673",
+    "k_attend.hip": "ba8f510fe9fa6d6af1f5a83b4871a8ae784d40754716a5467cd2cf86011b2008",
+    "attend_parts.h": "43d7620572fc9e261b309bcd780d656d88ee040a82ea87fbd0eaeb196cd3961b",
+    "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }
 
 
