@@ -18,7 +18,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["qsa_api.hip", "k_prologue.hip", "k_indexer.hip", "k_select.hip", "k_attend.hip", "k_decode.hip",
+HIP_SOURCES = ["qsa_api.hip", "k_prologue.hip", "k_indexer.hip", "k_select.hip", "k_attend.hip", "k_decode.hip", "k_gdn.hip",
                "k_train.hip"]
 CPP_SOURCES = ["qsa_tables.cpp"]
 

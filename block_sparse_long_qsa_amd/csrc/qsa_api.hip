@@ -53,6 +53,10 @@ hipError_t launch_attend_backward(const Tables &, hipStream_t, int32_t, int64_t,
                                   const bf16_t *, const bf16_t *, const int32_t *, const bf16_t *, const bf16_t *,
                                   const float *, float *, float *, float *);
 hipError_t launch_token_keys(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, const bf16_t *, bf16_t *);
+hipError_t launch_gdn_prefill(hipStream_t, int, const int32_t *, int64_t, int, int, int, float, const bf16_t *,
+                              const bf16_t *, const bf16_t *, const float *, const float *, const float *, bf16_t *,
+                              float *, bf16_t *);
+size_t gdn_workspace_bytes(int, int64_t, int);
 hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t,
                                       const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, uint32_t *);
 }  // namespace qsa
@@ -649,6 +653,33 @@ qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32
     if (e == hipSuccess)
         e = launch_attend_backward(tables(h), st, B, L, nblk_cap(h), h->p.budget_blocks, h->sigma, q, k_cache, v_cache,
                                    block_idx, out, dout, stats, dq, dk, dv);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hv_heads) {
+    if (nseq < 1 || max_len < 0 || hv_heads < 1) return 0;
+    return align_up(gdn_workspace_bytes(nseq, max_len, hv_heads));
+}
+
+qsa_status qsa_gdn_chunk_prefill(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens,
+                                 int64_t max_len, int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q,
+                                 const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                                 const float *initial_state, uint16_t *o, float *final_state, void *ws,
+                                 size_t ws_bytes) {
+    if (!cu_seqlens || !q || !k || !v || !g || !beta || !o) return QSA_ERR_NULL;
+    if (nseq < 1 || nseq > 65535 || n_tokens < 0 || max_len < 0 || max_len > (int64_t(1) << 30) || hq_heads < 1 ||
+        hq_heads > 65535 || hv_heads < hq_heads || hv_heads % hq_heads != 0)
+        return QSA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k)) return QSA_ERR_ALIGN;
+    const size_t need = qsa_gdn_workspace_size(nseq, max_len, hv_heads);
+    if (need > 0) {
+        if (!ws) return QSA_ERR_NULL;
+        if (!aligned16(ws)) return QSA_ERR_ALIGN;
+        if (ws_bytes < need) return QSA_ERR_WORKSPACE;
+    }
+    hipError_t e = launch_gdn_prefill(static_cast<hipStream_t>(stream), nseq, cu_seqlens, n_tokens,
+                                      static_cast<int>(max_len), hq_heads, hv_heads, scale, q, k, v, g, beta,
+                                      initial_state, o, final_state, static_cast<bf16_t *>(ws));
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

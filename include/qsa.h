@@ -337,6 +337,39 @@ qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32
                                         const uint16_t *out, const uint16_t *dout, const float *stats, float *dq,
                                         float *dk, float *dv);
 
+/* Gated DeltaNet chunked prefill: the hybrid's other token mixer ([PKR]
+ * section "어텐션: GDN이 기억하고 QSA가 찾아낸다": per V head the state S
+ * [128][128] follows S_t = (alpha_t I - beta_t k_t k_t^T) S_{t-1} + beta_t
+ * k_t v_t^T; spec table: 48 V heads, 16 QK heads, head dim 128; section
+ * "FlashQLA": the chunked-prefill interface).  Independent of any qsa_handle;
+ * runs on the calling thread's current HIP device.
+ *
+ * nseq sequences packed back to back: cu_seqlens (device, int32 [nseq + 1],
+ * non-decreasing, cu_seqlens[0] = 0) gives sequence s the tokens
+ * cu_seqlens[s] .. cu_seqlens[s+1]-1 of the n_tokens packed ones, and no
+ * sequence may be longer than max_len (offsets outside [0, n_tokens] are
+ * clamped and longer sequences are cut at max_len, so a bad table cannot make
+ * the kernels touch memory outside the buffers).  q, k [n_tokens][hq_heads][128]
+ * bf16 (already normalised, as the layer's short convolution and L2 norm leave
+ * them), v [n_tokens][hv_heads][128] bf16, g [n_tokens][hv_heads] fp32 = ln
+ * alpha_t (<= 0), beta [n_tokens][hv_heads] fp32 in [0, 1]; V head h reads QK
+ * head h / (hv_heads / hq_heads).  initial_state [nseq][hv_heads][128][128]
+ * fp32 (S[k_dim][v_dim], NULL = zeros).  Outputs: o [n_tokens][hv_heads][128]
+ * bf16 with o_t = scale * S_t^T q_t (the state after token t); final_state
+ * (same layout as initial_state, may be NULL, may alias initial_state) the
+ * state after each sequence's last token.  ws: qsa_gdn_workspace_size(nseq,
+ * max_len, hv_heads) bytes.  Errors: QSA_ERR_NULL (q, k, v, g, beta, o,
+ * cu_seqlens or a needed ws missing), QSA_ERR_SHAPE (nseq outside 1..65535,
+ * n_tokens or max_len negative or max_len above 2^30, hq_heads outside 1..65535,
+ * hv_heads not a positive multiple of hq_heads), QSA_ERR_ALIGN (q, k or ws not
+ * 16-byte aligned), QSA_ERR_WORKSPACE, QSA_ERR_HIP. */
+size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hv_heads);
+qsa_status qsa_gdn_chunk_prefill(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens,
+                                 int64_t max_len, int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q,
+                                 const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
+                                 const float *initial_state, uint16_t *o, float *final_state, void *ws,
+                                 size_t ws_bytes);
+
 /* Static string for a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -295,3 +295,31 @@ def score_rows(seed: int, B: int, L: int, q_offset: int, tie_mode: str = "mixed"
                 v = np.where(rng.random(o) < 0.05, rng.random(o) * 5, 0.0).astype(np.float32)
             out[b, i, :o] = v
     return out
+
+
+def gdn_inputs(seed: int, lens, hq: int = 16, hv: int = 48, device="cpu", init_state: bool = False):
+    """Seeded inputs of a Gated DeltaNet chunked prefill over packed sequences.
+
+    Head counts default to the GDN row of the pages' spec table (16 QK heads,
+    48 V heads, dim 128).  q and k are uniform random unit vectors (normalised
+    Gaussians, as the layer's L2 norm leaves them) rounded to bf16; v is N(0,1)
+    in bf16; the log gate is g = -exp(N(-3, 1)) (alpha = exp(g) has median
+    0.95 and spans fast- and slow-decaying heads); beta = 1/(1+exp(-N(0,1))).
+    The optional initial state is N(0, 0.1^2) fp32.  Returns a dict with
+    cu_seqlens (int32, [nseq+1]) and q, k [N][hq][128], v [N][hv][128],
+    g, beta [N][hv], s0 [nseq][hv][128][128] or None, all on `device`.
+    """
+    lens = [int(x) for x in lens]
+    n = int(sum(lens))
+    gen = torch.Generator(device="cpu").manual_seed(_seed(seed, 11, len(lens), n))
+    q = torch.randn(n, hq, 128, generator=gen)
+    k = torch.randn(n, hq, 128, generator=gen)
+    q = (q / q.norm(dim=-1, keepdim=True).clamp_min(1e-6)).to(torch.bfloat16)
+    k = (k / k.norm(dim=-1, keepdim=True).clamp_min(1e-6)).to(torch.bfloat16)
+    v = torch.randn(n, hv, 128, generator=gen).to(torch.bfloat16)
+    g = -torch.exp(torch.randn(n, hv, generator=gen) - 3.0)
+    beta = torch.sigmoid(torch.randn(n, hv, generator=gen))
+    s0 = torch.randn(len(lens), hv, 128, 128, generator=gen) * 0.1 if init_state else None
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    out = {"cu_seqlens": cu, "lens": lens, "q": q, "k": k, "v": v, "g": g.float(), "beta": beta.float(), "s0": s0}
+    return {key: (val.to(device) if isinstance(val, torch.Tensor) else val) for key, val in out.items()}
