@@ -538,6 +538,98 @@ def run_train(steps):
     print(json.dumps({"train": res, "steps": steps, "dtype": "bf16", "data": "synthetic"}), flush=True)
 
 
+GDN_HQ, GDN_HV = 16, 48      # QK and V heads of the pages' GDN layers (head dim 128)
+
+
+def gdn_counts(lens, hq=GDN_HQ, hv=GDN_HV):
+    """Algorithmic work of the two GDN kernels over packed sequences `lens`
+    (chunks of 64; the last chunk of a sequence counts as a whole chunk, as the
+    kernels compute it).  Scan, per (chunk, V head): [K; Q] S, Tb X, P U and
+    K^T U = 8,388,608 flops; bytes: q, k once per QK head (32 KiB per chunk), v
+    and o (16 KiB each), g (256 B), Tb and P (16 KiB).  Prep, per (chunk, QK
+    head): the 10 causal 16 x 16 tiles of K K^T and Q K^T = 1,310,720 flops;
+    bytes: q, k (32 KiB), g and beta (512 B per V head), Tb and P written
+    (16 KiB per V head)."""
+    nck = sum((n + 63) // 64 for n in lens)
+    ntok = sum(lens)
+    scan_flops = nck * hv * 8388608
+    prep_flops = nck * hq * 1310720
+    qk_bytes = ntok * hq * 128 * 2 * 2
+    scan_bytes = qk_bytes + ntok * hv * (128 * 2 * 2 + 4) + nck * hv * 16384
+    prep_bytes = qk_bytes + ntok * hv * 8 + nck * hv * 16384
+    return {"scan_flops": scan_flops, "prep_flops": prep_flops, "scan_bytes": scan_bytes, "prep_bytes": prep_bytes}
+
+
+def gdn_cpu_baseline(x, n_tok=512):
+    """The oracle (token-by-token fp64 recurrence, all 48 V heads) on the first
+    n_tok tokens of the workload."""
+    from oracle import gdn as OG
+    f = lambda t: t[:n_tok].float().cpu().numpy().astype(np.float64)
+    q, k, v, g, b = f(x["q"]), f(x["k"]), f(x["v"]), f(x["g"]), f(x["beta"])
+    t0 = time.perf_counter()
+    OG.gdn_recurrent(q, k, v, g, b, 128 ** -0.5)
+    dt = time.perf_counter() - t0
+    return {"value": n_tok / dt, "unit": "tok/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": "first %d tokens of the 262,144-token sequence, all 48 V heads" % n_tok}
+
+
+def run_gdn(steps, cpu=True):
+    """Gated DeltaNet chunked prefill (the hybrid's other token mixer) on one
+    262,144-token sequence and on 8 packed sequences of 32,768 tokens; 16 QK
+    heads, 48 V heads, head dim 128.  HIP events around qsa_gdn_prep and
+    qsa_gdn_scan (the two kernels qsa_gdn_chunk_prefill launches) on the
+    current stream; one JSON line."""
+    res = {}
+    base = None
+    for name, lens in (("gdn_T262144_x1", [262144]), ("gdn_T32768_x8", [32768] * 8)):
+        x = synth.gdn_inputs(21, lens, GDN_HQ, GDN_HV, "cuda")
+        nseq, max_len = len(lens), max(lens)
+        o = torch.empty_like(x["v"])
+        fs = torch.empty(nseq, GDN_HV, 128, 128, device="cuda")
+        ws = torch.empty(Q.qsa_gdn_workspace_size(nseq, max_len, GDN_HQ, GDN_HV), dtype=torch.uint8, device="cuda")
+        scale = 128 ** -0.5
+
+        def step(ev):
+            ev[0].record()
+            Q.qsa_gdn_prep(nseq, x["cu_seqlens"], max_len, x["q"], x["k"], GDN_HV, x["g"], x["beta"], scale, ws)
+            ev[1].record()
+            Q.qsa_gdn_scan(nseq, x["cu_seqlens"], max_len, x["q"], x["k"], x["v"], x["g"], scale, None, o, fs, ws)
+            ev[2].record()
+
+        step(_events(3))
+        torch.cuda.synchronize()
+        evs = [_events(3) for _ in range(steps)]
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        prep_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        scan_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        c = gdn_counts(lens)
+        ntok = sum(lens)
+
+        def roof(flops, nbytes, ms):
+            tfs = flops / (ms * 1e-3) / 1e12
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            out = {"tflops": tfs, "mfma_frac": tfs / MFMA_BF16_PEAK_TFS, "gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                   "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "avg_ms": ms}
+            return out
+
+        res[name] = {"ms": prep_ms + scan_ms, "tok_s": ntok / ((prep_ms + scan_ms) * 1e-3),
+                     "gdn_prep_kernel": roof(c["prep_flops"], c["prep_bytes"], prep_ms),
+                     "gdn_scan_kernel": roof(c["scan_flops"], c["scan_bytes"], scan_ms)}
+        if base is None:
+            base = x if cpu else None
+        else:
+            del x
+        del o, fs, ws
+        torch.cuda.empty_cache()
+    line = {"gdn": res, "steps": steps, "dtype": "bf16", "data": "synthetic",
+            "config": {"hq_heads": GDN_HQ, "hv_heads": GDN_HV, "head_dim": 128, "chunk": 64}}
+    if base is not None:
+        line["cpu_baseline"] = gdn_cpu_baseline(base)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -554,6 +646,8 @@ def main():
                     help="measure the 1M-token configuration instead (chunked prefill, B=8 decode)")
     ap.add_argument("--train", action="store_true",
                     help="measure a training step (indexer loss forward and backward) instead")
+    ap.add_argument("--gdn", action="store_true",
+                    help="measure the Gated DeltaNet chunked prefill instead")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
@@ -570,6 +664,9 @@ def main():
         return
     if args.train:
         run_train(max(1, min(args.steps, 5)))
+        return
+    if args.gdn:
+        run_gdn(max(1, min(args.steps, 10)), cpu=not args.no_cpu_baseline)
         return
     if args.calib_copy:
         src = torch.full((1 << 30,), 7, dtype=torch.uint8, device="cuda")

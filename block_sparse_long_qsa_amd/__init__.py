@@ -29,7 +29,8 @@ EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", 
            "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
            "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
            "qsa_train_forward", "qsa_train_backward_indexer", "qsa_train_backward_attention",
-           "qsa_gdn_workspace_size", "qsa_gdn_chunk_prefill", "qsa_status_string", "qsa_last_hip_error"]
+           "qsa_gdn_workspace_size", "qsa_gdn_chunk_prefill", "qsa_gdn_prep", "qsa_gdn_scan",
+           "qsa_status_string", "qsa_last_hip_error"]
 
 
 class QSAError(RuntimeError):
@@ -99,10 +100,14 @@ def lib() -> ctypes.CDLL:
     L.qsa_train_backward_indexer.restype = ctypes.c_int
     L.qsa_train_backward_attention.argtypes = [vp, vp, i32, i64] + [vp] * 10
     L.qsa_train_backward_attention.restype = ctypes.c_int
-    L.qsa_gdn_workspace_size.argtypes = [i32, i64, i32]
+    L.qsa_gdn_workspace_size.argtypes = [i32, i64, i32, i32]
     L.qsa_gdn_workspace_size.restype = sz
     L.qsa_gdn_chunk_prefill.argtypes = [vp, i32, vp, i64, i64, i32, i32, ctypes.c_float] + [vp] * 9 + [sz]
     L.qsa_gdn_chunk_prefill.restype = ctypes.c_int
+    L.qsa_gdn_prep.argtypes = [vp, i32, vp, i64, i64, i32, i32, ctypes.c_float] + [vp] * 5 + [sz]
+    L.qsa_gdn_prep.restype = ctypes.c_int
+    L.qsa_gdn_scan.argtypes = [vp, i32, vp, i64, i64, i32, i32, ctypes.c_float] + [vp] * 8 + [sz]
+    L.qsa_gdn_scan.restype = ctypes.c_int
     L.qsa_status_string.argtypes = [ctypes.c_int]
     L.qsa_status_string.restype = ctypes.c_char_p
     L.qsa_last_hip_error.argtypes = []
@@ -322,8 +327,22 @@ def qsa_train_backward_attention(h, B, L, q, k_cache, v_cache, block_idx, out, d
                                               _ptr(dv, torch.float32, "dv")), "qsa_train_backward_attention")
 
 
-def qsa_gdn_workspace_size(nseq, max_len, hv_heads) -> int:
-    return int(lib().qsa_gdn_workspace_size(nseq, max_len, hv_heads))
+def qsa_gdn_workspace_size(nseq, max_len, hq_heads, hv_heads) -> int:
+    return int(lib().qsa_gdn_workspace_size(nseq, max_len, hq_heads, hv_heads))
+
+
+def _gdn_shapes(q, k, v, g, beta, o):
+    n_tok, hq = q.shape[0], q.shape[1]
+    hv = v.shape[1]
+    checks = [("k", k, q.shape), ("g", g, (n_tok, hv)), ("beta", beta, (n_tok, hv))]
+    if o is not None:
+        checks.append(("o", o, v.shape))
+    for name, t, shape in checks:
+        if t is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if v.shape[0] != n_tok or q.shape[2] != 128 or v.shape[2] != 128:
+        raise ValueError("q, k, v must be [n_tokens][heads][128] with one n_tokens")
+    return n_tok, hq, hv
 
 
 def qsa_gdn_chunk_prefill(nseq, cu_seqlens, max_len, q, k, v, g, beta, scale, initial_state, o, final_state, ws,
@@ -332,19 +351,29 @@ def qsa_gdn_chunk_prefill(nseq, cu_seqlens, max_len, q, k, v, g, beta, scale, in
     only).  q, k [n_tokens][Hq][128] bf16, v and o [n_tokens][Hv][128] bf16, g and
     beta [n_tokens][Hv] fp32, cu_seqlens int32 [nseq + 1] on the device, states
     [nseq][Hv][128][128] fp32 or None."""
-    n_tok, hq = q.shape[0], q.shape[1]
-    hv = v.shape[1]
-    for name, t, shape in (("k", k, q.shape), ("o", o, v.shape), ("g", g, (n_tok, hv)), ("beta", beta, (n_tok, hv))):
-        if tuple(t.shape) != tuple(shape):
-            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
-    if v.shape[0] != n_tok or q.shape[2] != 128 or v.shape[2] != 128:
-        raise ValueError("q, k, v must be [n_tokens][heads][128] with one n_tokens")
+    n_tok, hq, hv = _gdn_shapes(q, k, v, g, beta, o)
     _check(lib().qsa_gdn_chunk_prefill(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_tok,
                                        max_len, hq, hv, float(scale), _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
                                        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
                                        _ptr(initial_state, torch.float32, "initial_state"), _bf(o, "o"),
                                        _ptr(final_state, torch.float32, "final_state"), _ptr(ws, None, "ws"),
                                        _nbytes(ws)), "qsa_gdn_chunk_prefill")
+
+
+def qsa_gdn_prep(nseq, cu_seqlens, max_len, q, k, hv, g, beta, scale, ws, stream=None):
+    n_tok, hq = q.shape[0], q.shape[1]
+    _check(lib().qsa_gdn_prep(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_tok, max_len, hq,
+                              hv, float(scale), _bf(q, "q"), _bf(k, "k"), _ptr(g, torch.float32, "g"),
+                              _ptr(beta, torch.float32, "beta"), _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_gdn_prep")
+
+
+def qsa_gdn_scan(nseq, cu_seqlens, max_len, q, k, v, g, scale, initial_state, o, final_state, ws, stream=None):
+    n_tok, hq, hv = _gdn_shapes(q, k, v, g, None, o)
+    _check(lib().qsa_gdn_scan(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_tok, max_len, hq,
+                              hv, float(scale), _bf(q, "q"), _bf(k, "k"), _bf(v, "v"), _ptr(g, torch.float32, "g"),
+                              _ptr(initial_state, torch.float32, "initial_state"), _bf(o, "o"),
+                              _ptr(final_state, torch.float32, "final_state"), _ptr(ws, None, "ws"), _nbytes(ws)),
+           "qsa_gdn_scan")
 
 
 def qsa_status_string(status: int) -> str:

@@ -17,15 +17,23 @@
 //   O   = diag(scale gamma_t) Q S_0 + P U,  P[t][j] = scale exp(G_t - G_j) q_t.k_j  (j <= t),
 //   S_C = gamma_C S_0 + K^T diag(exp(G_C - G_t)) U.
 // Tb and P do not depend on the state: gdn_prep_kernel builds them for every
-// (chunk, V head) in parallel.  gdn_scan_kernel then walks the chunks of one
-// (sequence, V head, 16*NW value columns) in order with its columns of S in
-// registers (each column of S evolves on its own), so a head's state is
-// advanced by 128/(16*NW) work-groups at once.
+// (chunk, V head) in parallel, together with K^T of every (chunk, QK head).
+// gdn_scan_kernel then walks the chunks of one (sequence, V head, 16*NW value
+// columns) in order with its columns of S in registers (each column of S
+// evolves on its own), so a head's state is advanced by 128/(16*NW)
+// work-groups at once.  Each chunk's tiles (K, Q, K^T, Tb, P: 64 KiB) are
+// copied into LDS by the LDS-DMA path (global_load_lds, 16 bytes a lane) one
+// chunk ahead, into the other half of a double buffer.
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16; A lane l = row l%16, k = 8(l/16)..+7;
 // B lane l = column l%16, same k; C lane l = rows 4(l/16)..+3, column l%16.
 // Accumulator tiles that feed a later product as its B operand (S, X, U) are
 // rounded to bf16 and passed through a small per-wave LDS transpose.
+//
+// Tile layout (LDS and workspace alike): rows of 16-byte chunks, chunk c of
+// row r stored at position c ^ (r & 15) in 256-byte rows (128 bf16 wide) and
+// c ^ ((r >> 1) & 7) in 128-byte rows (64 wide), so that the 16 rows a
+// fragment read touches fall in distinct LDS banks.
 #include "qsa_common.h"
 
 namespace qsa {
@@ -66,175 +74,216 @@ __device__ __forceinline__ f32x4 mfma32(const bf16x8 &a, const bf16x8 &b, const 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Workspace of one (sequence, V head, chunk): Tb then P, [64][64] bf16 each.
+// Workspace: for every (sequence, V head, chunk) Tb then P, [64][64] bf16 each
+// (16 KiB); after all of them, for every (sequence, QK head, chunk) K^T
+// [128][64] bf16 (16 KiB).  Offsets in bf16 elements.
 __device__ __forceinline__ int64_t gdn_ws_off(int s, int hv, int Hv, int nchunk_cap, int c) {
     return ((static_cast<int64_t>(s) * Hv + hv) * nchunk_cap + c) * (2 * kGdnTile);
 }
+__device__ __forceinline__ int64_t gdn_kt_off(int nseq, int s, int hq, int Hq, int Hv, int nchunk_cap, int c) {
+    return static_cast<int64_t>(nseq) * Hv * nchunk_cap * (2 * kGdnTile) +
+           ((static_cast<int64_t>(s) * Hq + hq) * nchunk_cap + c) * (2 * kGdnTile);
+}
+
+// Byte offset of 16-byte chunk cc of row r in a swizzled tile.
+__device__ __forceinline__ int sw128(int r, int cc) { return r * 256 + ((cc ^ (r & 15)) << 4); }
+__device__ __forceinline__ int sw64(int r, int cc) { return r * 128 + ((cc ^ ((r >> 1) & 7)) << 4); }
+
+__device__ __forceinline__ float exp_e(float x) { return exp2f(x * 1.4426950408889634f); }
+
+// Two floats to a pair of bf16 (round to nearest even), low half first.
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// Barriers that order LDS only: global stores and loads stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+__device__ __forceinline__ void lds_wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Renumber work-group ids so that consecutive logical ids run on one XCD
+// (work-groups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int64_t xcd_local_id() {
+    const int64_t n = gridDim.x, b = blockIdx.x;
+    return n % 8 == 0 ? (b % 8) * (n / 8) + b / 8 : b;
+}
 
 // ---------------------------------------------------------------------------
-// Per (chunk, QK head, sequence): K K^T and Q K^T of the chunk on the matrix
-// cores (wave w owns rows 16w..16w+15, lower-triangular tiles only), then for
-// each V head that reads this QK head: Lt into LDS and P to the workspace, and
-// Tb by forward substitution, one column per lane (wave w solves head w of a
-// group of up to four).
-__global__ __launch_bounds__(256) void gdn_prep_kernel(const int32_t *__restrict__ cu, int64_t n_tok, int max_len,
-                                                       int nchunk_cap, int Hq, int Hv, float scale,
-                                                       const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
-                                                       const float *__restrict__ g, const float *__restrict__ beta,
-                                                       bf16_t *__restrict__ tp)
+// One wave per (sequence, chunk, V head): K K^T and Q K^T of the chunk (the 10
+// causal 16 x 16 tiles) on the matrix cores from fragments read straight from
+// q and k; Lt into LDS and P to the workspace; Tb by forward substitution, one
+// column per lane.  The first V head of each QK head also writes K^T.  Rows
+// past the end of the sequence repeat its last token: their beta is 0, so
+// their rows of Lt and Tb are zero (and so is every Tb column they own), and
+// causality zeroes their P columns for every real row.
+__global__ __launch_bounds__(64) void gdn_prep_kernel(const int32_t *__restrict__ cu, int64_t n_tok, int max_len,
+                                                      int nchunk_cap, int nseq, int Hq, int Hv, float scale,
+                                                      const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
+                                                      const float *__restrict__ g, const float *__restrict__ beta,
+                                                      bf16_t *__restrict__ ws)
 {
-    __shared__ __align__(16) float smem[4 * kGdnTile];   // K, Q tiles; then Lt of up to four heads
-    __shared__ float sG[4][kGdnChunk], sBeta[4][kGdnChunk];
-    bf16_t *sK = reinterpret_cast<bf16_t *>(smem);
-    bf16_t *sQ = sK + kGdnChunk * kGdnPad;
+    __shared__ __align__(16) float Lt[kGdnTile];    // 16 KiB; first the K^T staging tile
+    __shared__ float sG[kGdnChunk], sB[kGdnChunk];
 
-    const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+    const int64_t e = xcd_local_id();
+    const int hv = static_cast<int>(e % Hv);
+    const int c = static_cast<int>((e / Hv) % nchunk_cap);
+    const int s = static_cast<int>(e / (static_cast<int64_t>(Hv) * nchunk_cap));
     const GdnSpan sp = gdn_span(cu, s, n_tok, max_len);
     const int t0 = c * kGdnChunk;
     if (t0 >= sp.len) return;
-    const int nt = min(kGdnChunk, sp.len - t0);
-    const int rep = Hv / Hq;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int nt = min(kGdnChunk, sp.len - t0), last = nt - 1;
+    const int rep = Hv / Hq, hq = hv / rep;
+    const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+    const int64_t tok0 = sp.base + t0;
+    const int kstride = Hq * kGdnDim;
 
-    for (int p = tid; p < kGdnChunk * 16; p += 256) {
-        const int t = p >> 4, d8 = p & 15;
-        u32x4 kv = {0u, 0u, 0u, 0u}, qv = {0u, 0u, 0u, 0u};
-        if (t < nt) {
-            const int64_t off = ((sp.base + t0 + t) * Hq + hq) * kGdnDim + d8 * 8;
-            kv = *reinterpret_cast<const u32x4 *>(k + off);
-            qv = *reinterpret_cast<const u32x4 *>(q + off);
-        }
-        *reinterpret_cast<u32x4 *>(sK + t * kGdnPad + d8 * 8) = kv;
-        *reinterpret_cast<u32x4 *>(sQ + t * kGdnPad + d8 * 8) = qv;
-    }
-    __syncthreads();
-
-    f32x4 kk[4], qk[4];
+    bf16x8 kf[4][4], qf[4][4];   // rows 16i + l%16, dims 32s + 8(l/16) ..
+    {
+        const bf16_t *kb = k + (tok0 * Hq + hq) * kGdnDim + 8 * lg;
+        const bf16_t *qb = q + (tok0 * Hq + hq) * kGdnDim + 8 * lg;
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) kk[jt] = qk[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+            const int row = min(16 * i + lr, last);
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-        const bf16x8 ak = *reinterpret_cast<const bf16x8 *>(sK + (16 * w + lr) * kGdnPad + 32 * s4 + 8 * lg);
-        const bf16x8 aq = *reinterpret_cast<const bf16x8 *>(sQ + (16 * w + lr) * kGdnPad + 32 * s4 + 8 * lg);
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            if (jt > w) continue;
-            const bf16x8 bk = *reinterpret_cast<const bf16x8 *>(sK + (16 * jt + lr) * kGdnPad + 32 * s4 + 8 * lg);
-            kk[jt] = mfma32(ak, bk, kk[jt]);
-            qk[jt] = mfma32(aq, bk, qk[jt]);
-        }
-    }
-    __syncthreads();   // K and Q tiles are dead: the space holds Lt from here on
-
-    for (int r0 = 0; r0 < rep; r0 += 4) {
-        const int nr = min(4, rep - r0);
-        if (w < nr) {
-            float gv = 0.f, bv = 0.f;
-            if (lane < nt) {
-                const int64_t gi = (sp.base + t0 + lane) * Hv + hq * rep + r0 + w;
-                gv = g[gi];
-                bv = beta[gi];
+            for (int s4 = 0; s4 < 4; ++s4) {
+                kf[i][s4] = *reinterpret_cast<const bf16x8 *>(kb + row * kstride + 32 * s4);
+                qf[i][s4] = *reinterpret_cast<const bf16x8 *>(qb + row * kstride + 32 * s4);
             }
-            sG[w][lane] = wave_prefix_sum(gv);
-            sBeta[w][lane] = bv;
         }
-        __syncthreads();
-        for (int r = 0; r < nr; ++r) {
-            const int hv = hq * rep + r0 + r;
-            bf16_t *P = tp + gdn_ws_off(s, hv, Hv, nchunk_cap, c) + kGdnTile;
-            float *Lt = smem + r * kGdnTile;
+    }
+    {
+        const int64_t gi = (tok0 + min(lane, last)) * Hv + hv;
+        const float gv = g[gi], bv = beta[gi];
+        sG[lane] = wave_prefix_sum(lane < nt ? gv : 0.f);
+        sB[lane] = lane < nt ? bv : 0.f;
+    }
+    f32x4 kk[10], qk[10];   // tile (w, jt), jt <= w, at index w(w+1)/2 + jt
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
+    for (int w = 0; w < 4; ++w)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int t = 16 * w + 4 * lg + j, jj = 16 * jt + lr;
-                    float lv = 0.f, pv = 0.f;
-                    if (jt <= w) {
-                        const float Gj = sG[r][jj];
-                        const float Gprev = t > 0 ? sG[r][t - 1] : 0.f;
-                        if (jj < t) lv = sBeta[r][t] * expf(Gprev - Gj) * kk[jt][j];
-                        if (jj <= t) pv = scale * expf(sG[r][t] - Gj) * qk[jt][j];
-                        Lt[t * kGdnChunk + jj] = lv;   // tiles right of the diagonal are never read
-                    }
-                    P[t * kGdnChunk + jj] = f32_to_bf16(pv);
+        for (int jt = 0; jt <= w; ++jt) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                a = mfma32(kf[w][s4], kf[jt][s4], a);
+                b = mfma32(qf[w][s4], kf[jt][s4], b);
+            }
+            kk[w * (w + 1) / 2 + jt] = a;
+            qk[w * (w + 1) / 2 + jt] = b;
+        }
+
+    if (hv % rep == 0) {
+        // K^T of the chunk, through LDS: element (dim d, token t) at sw64(d, t/8) + 2(t%8).
+        unsigned char *tk = reinterpret_cast<unsigned char *>(Lt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                const u32x4 w4 = __builtin_bit_cast(u32x4, kf[i][s4]);
+                const int t = 16 * i + lr;
+#pragma unroll
+                for (int e8 = 0; e8 < 8; ++e8) {
+                    const int d = 32 * s4 + 8 * lg + e8;
+                    const uint32_t word = w4[e8 >> 1];
+                    *reinterpret_cast<bf16_t *>(tk + sw64(d, t >> 3) + 2 * (t & 7)) =
+                        static_cast<bf16_t>((e8 & 1) ? (word >> 16) : (word & 0xFFFFu));
                 }
             }
-        }
-        __syncthreads();
-        if (w < nr) {
-            // Column `lane` of T = (I + Lt)^{-1}: x_t = [t == lane] - sum_{j<t} Lt[t][j] x_j.
-            // x_j is still zero for j >= t and so is Lt[t][j]: whole float4 reads are exact.
-            const float *Lt = smem + w * kGdnTile;
-            float x[kGdnChunk];
+        wave_sync();
+        bf16_t *kt = ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c);
 #pragma unroll
-            for (int t = 0; t < kGdnChunk; ++t) x[t] = 0.f;
-#pragma unroll
-            for (int t = 0; t < kGdnChunk; ++t) {
-                float acc = lane == t ? 1.f : 0.f;
-#pragma unroll
-                for (int j4 = 0; j4 < (t + 3) / 4; ++j4) {
-                    const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Lt + t * kGdnChunk + 4 * j4);
-                    acc = fmaf(-l4[0], x[4 * j4 + 0], acc);
-                    acc = fmaf(-l4[1], x[4 * j4 + 1], acc);
-                    acc = fmaf(-l4[2], x[4 * j4 + 2], acc);
-                    acc = fmaf(-l4[3], x[4 * j4 + 3], acc);
-                }
-                x[t] = acc;
-            }
-            const float bc = sBeta[w][lane];
-            bf16_t *Tb = tp + gdn_ws_off(s, hq * rep + r0 + w, Hv, nchunk_cap, c);
-#pragma unroll
-            for (int t = 0; t < kGdnChunk; ++t) Tb[t * kGdnChunk + lane] = f32_to_bf16(x[t] * bc);
-        }
-        __syncthreads();
+        for (int m = 0; m < 16; ++m)
+            *reinterpret_cast<u32x4 *>(kt + 8 * (lane + 64 * m)) = *reinterpret_cast<const u32x4 *>(tk + 16 * (lane + 64 * m));
+        wave_sync();
     }
+    wave_sync();
+
+    bf16_t *Tb = ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c);
+    unsigned char *P = reinterpret_cast<unsigned char *>(Tb + kGdnTile);
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 16 * w + 4 * lg + j, jj = 16 * jt + lr;
+                float pv = 0.f;
+                if (jt <= w) {
+                    const float Gj = sG[jj];
+                    const float Gprev = t > 0 ? sG[t - 1] : 0.f;
+                    const float lv = jj < t ? sB[t] * exp_e(Gprev - Gj) * kk[w * (w + 1) / 2 + jt][j] : 0.f;
+                    if (jj <= t) pv = scale * exp_e(sG[t] - Gj) * qk[w * (w + 1) / 2 + jt][j];
+                    Lt[t * kGdnChunk + jj] = lv;   // tiles right of the diagonal are never read
+                }
+                *reinterpret_cast<bf16_t *>(P + sw64(t, jj >> 3) + 2 * (jj & 7)) = f32_to_bf16(pv);
+            }
+    wave_sync();
+
+    // Column `lane` of T = (I + Lt)^{-1}: x_t = [t == lane] - sum_{j<t} Lt[t][j] x_j.
+    // x_j is still zero for j >= t and so is Lt[t][j]: whole float4 reads are exact.
+    float x[kGdnChunk];
+#pragma unroll
+    for (int t = 0; t < kGdnChunk; ++t) x[t] = 0.f;
+    x[0] = lane == 0 ? 1.f : 0.f;
+#pragma unroll
+    for (int t = 1; t < kGdnChunk; ++t) {
+        f32x4 row[kGdnChunk / 4];
+#pragma unroll
+        for (int j4 = 0; j4 < (t + 3) / 4; ++j4) row[j4] = *reinterpret_cast<const f32x4 *>(Lt + t * kGdnChunk + 4 * j4);
+        float a0 = lane == t ? 1.f : 0.f, a1 = 0.f;
+#pragma unroll
+        for (int j4 = 0; j4 < (t + 3) / 4; ++j4) {
+            a0 = fmaf(-row[j4][0], x[4 * j4 + 0], a0);
+            a1 = fmaf(-row[j4][1], x[4 * j4 + 1], a1);
+            a0 = fmaf(-row[j4][2], x[4 * j4 + 2], a0);
+            a1 = fmaf(-row[j4][3], x[4 * j4 + 3], a1);
+        }
+        x[t] = a0 + a1;
+    }
+    const float bc = sB[lane];
+    unsigned char *tb = reinterpret_cast<unsigned char *>(Tb);
+#pragma unroll
+    for (int t = 0; t < kGdnChunk; ++t)
+        *reinterpret_cast<bf16_t *>(tb + sw64(t, lane >> 3) + 2 * (lane & 7)) = f32_to_bf16(x[t] * bc);
 }
 
 // ---------------------------------------------------------------------------
 // Chunk walk of one (sequence, V head, 16*NW value columns).  Wave w owns the
 // 16 columns c0 = 16*(NW*slice + w) .. +15 of S (rows 16i + 4(l/16) + j of
-// column c0 + l%16 in S[i][j]).  Per chunk, from LDS tiles shared by the waves:
-//   R_K = K S, R_Q = Q S                 (32 products)
+// column c0 + l%16 in S[i][j]).  Per chunk, from the LDS tiles:
+//   R_K = K S, R_Q = Q S                                  (32 products)
 //   X = V - diag(gamma_{t-1}) R_K;  U = Tb X              (8)
 //   O = diag(scale gamma_t) R_Q + P U                     (8)
 //   S = gamma_C S + K^T diag(exp(G_C - G_t)) U            (16)
-// The next chunk's tiles are loaded into registers while this one computes.
-template <int NW>
-struct GdnStage {
-    static constexpr int NT = 64 * NW;
-    static constexpr int kKd = 8 / NW;            // 16-byte K pieces per token of a thread
-    static constexpr int kQp = 16 / NW;           // Q pieces of a thread
-    static constexpr int kTp = 16 / NW;           // Tb + P pieces of a thread
-    u32x4 ka[kKd], kb[kKd];                       // tokens 2*(tid%32) and +1, dims 8*(kKd*(tid/32) + m) ..
-    u32x4 qv[kQp];
-    u32x4 tpv[kTp];
-    float gv;                                     // wave 0: g of token `lane`
-    bf16_t vv[16];                                // this wave's V: tokens 16i + 4(l/16) + j, column c0 + l%16
-};
-
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(const int32_t *__restrict__ cu, int64_t n_tok, int max_len,
-                                                          int nchunk_cap, int Hq, int Hv, float scale,
+// O is kept in registers and stored during the next chunk.  One more wave
+// (the producer) streams the tiles into LDS.
+template <int NW, int NP>
+__global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t *__restrict__ cu, int64_t n_tok, int max_len,
+                                                          int nchunk_cap, int nseq, int Hq, int Hv, float scale,
                                                           const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
                                                           const bf16_t *__restrict__ v, const float *__restrict__ g,
-                                                          const bf16_t *__restrict__ tp, const float *s0,
+                                                          const bf16_t *__restrict__ ws, const float *s0,
                                                           bf16_t *__restrict__ o, float *s_out)
 {
-    constexpr int NT = 64 * NW;
     constexpr int kSlices = kGdnDim / (16 * NW);
-    __shared__ __align__(16) bf16_t sK[kGdnChunk * kGdnPad];
-    __shared__ __align__(16) bf16_t sQ[kGdnChunk * kGdnPad];
-    __shared__ __align__(16) bf16_t sKt[kGdnDim * kGdnPad64];
-    __shared__ __align__(16) bf16_t sTb[kGdnChunk * kGdnPad64];
-    __shared__ __align__(16) bf16_t sP[kGdnChunk * kGdnPad64];
+    constexpr int kBuf = 65536;                       // K, Q (16 KiB each), K^T (16 KiB), Tb, P (8 KiB each)
+    constexpr int oQ = 16384, oKt = 32768, oTb = 49152, oP = 57344;
+    constexpr int kE = 4 * kGdnChunk;                 // exp(G_{t-1}), scale exp(G_t), exp(G_C - G_t), exp(G_C)
+    __shared__ __align__(16) unsigned char sbuf[2 * kBuf];
     __shared__ __align__(16) bf16_t sTr[NW][16 * kGdnPad];
-    __shared__ float sEp[kGdnChunk], sEc[kGdnChunk], sEt[kGdnChunk], sEC[1];
+    __shared__ __align__(16) float sE[2 * kE];
 
-    // Work-groups are dealt to the 8 XCDs round-robin; renumber them so that the
-    // column slices and V heads that share one QK head's tiles sit on one XCD.
-    const int64_t nwg = gridDim.x;
-    int64_t e = blockIdx.x;
-    if (nwg % 8 == 0) e = (e % 8) * (nwg / 8) + e / 8;
+    const int64_t e = xcd_local_id();
     const int slice = static_cast<int>(e % kSlices);
     const int hv = static_cast<int>((e / kSlices) % Hv);
     const int s = static_cast<int>(e / (static_cast<int64_t>(kSlices) * Hv));
@@ -245,106 +294,102 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(const int32_t *__rest
     const GdnSpan sp = gdn_span(cu, s, n_tok, max_len);
     const int nck = (sp.len + kGdnChunk - 1) / kGdnChunk;
     const int64_t sbase = (static_cast<int64_t>(s) * Hv + hv) * kGdnDim * kGdnDim;
+    const int kstride = Hq * kGdnDim, vstride = Hv * kGdnDim;
 
     f32x4 S[8];
+    if (s0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            S[i][j] = s0 ? s0[sbase + static_cast<int64_t>(16 * i + 4 * lg + j) * kGdnDim + col] : 0.f;
+            for (int j = 0; j < 4; ++j) S[i][j] = s0[sbase + (16 * i + 4 * lg + j) * kGdnDim + col];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    GdnStage<NW> st;
-    auto load = [&](int c) {
+    // The producer wave copies chunk c's tiles into `dst` (rows past the end
+    // repeat the last token; see gdn_prep_kernel for why that is harmless).
+    auto dma = [&](int c, unsigned char *dst, int pw) {
         const int t0 = c * kGdnChunk;
-        const int nt = min(kGdnChunk, sp.len - t0);
-        const int tp2 = tid & 31, dg = tid >> 5;
-#pragma unroll
-        for (int m = 0; m < GdnStage<NW>::kKd; ++m) {
-            const int d8 = dg * GdnStage<NW>::kKd + m;
-            const int ta = 2 * tp2, tb = ta + 1;
-            const bf16_t *src = k + ((sp.base + t0) * Hq + hq) * kGdnDim + d8 * 8;
-            st.ka[m] = ta < nt ? *reinterpret_cast<const u32x4 *>(src + static_cast<int64_t>(ta) * Hq * kGdnDim)
-                               : u32x4{0u, 0u, 0u, 0u};
-            st.kb[m] = tb < nt ? *reinterpret_cast<const u32x4 *>(src + static_cast<int64_t>(tb) * Hq * kGdnDim)
-                               : u32x4{0u, 0u, 0u, 0u};
+        const int last = min(kGdnChunk, sp.len - t0) - 1;
+        const int64_t tok0 = sp.base + t0;
+        const bf16_t *kt = ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c);
+        const bf16_t *tpw = ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c);
+#pragma unroll 8
+        for (int p = pw; p < 64; p += NP) {            // 1 KiB pieces of the buffer
+            const bf16_t *src;
+            if (p < 32) {
+                const int row = 4 * (p & 15) + (lane >> 4), cp = lane & 15;
+                src = (p < 16 ? k : q) + (tok0 * Hq + hq) * kGdnDim + min(row, last) * kstride + 8 * (cp ^ (row & 15));
+            } else if (p < 48) {
+                src = kt + 512 * (p - 32) + 8 * lane;
+            } else {
+                src = tpw + 512 * (p - 48) + 8 * lane;
+            }
+            __builtin_amdgcn_global_load_lds(src, dst + 1024 * p, 16, 0, 0);
         }
+    };
+    // Compute waves load chunk c's V columns and gates into registers.
+    bf16_t vnext[16];
+    float gnext = 0.f;
+    auto issue = [&](int c) {
+        const int t0 = c * kGdnChunk;
+        const int last = min(kGdnChunk, sp.len - t0) - 1;
+        const int64_t tok0 = sp.base + t0;
+        const bf16_t *vb = v + (tok0 * Hv + hv) * kGdnDim + col;
 #pragma unroll
-        for (int m = 0; m < GdnStage<NW>::kQp; ++m) {
-            const int p = tid + NT * m, t = p >> 4, d8 = p & 15;
-            st.qv[m] = t < nt ? *reinterpret_cast<const u32x4 *>(q + ((sp.base + t0 + t) * Hq + hq) * kGdnDim + d8 * 8)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
-        const bf16_t *ws = tp + gdn_ws_off(s, hv, Hv, nchunk_cap, c);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int m = 0; m < GdnStage<NW>::kTp; ++m)
-            st.tpv[m] = *reinterpret_cast<const u32x4 *>(ws + 8 * (tid + NT * m));
-        st.gv = (w == 0 && lane < nt) ? g[(sp.base + t0 + lane) * Hv + hv] : 0.f;
+            for (int j = 0; j < 4; ++j) vnext[4 * i + j] = vb[min(16 * i + 4 * lg + j, last) * vstride];
+        gnext = g[(tok0 + min(lane, last)) * Hv + hv];
+    };
+    auto gates = [&](int nt, float *__restrict__ ed) {            // wave 0
+        const float G = wave_prefix_sum(lane < nt ? gnext : 0.f);
+        const float Gprev = __shfl_up(G, 1);
+        const float GC = __shfl(G, 63);
+        ed[lane] = lane == 0 ? 1.f : exp_e(Gprev);
+        ed[kGdnChunk + lane] = scale * exp_e(G);
+        ed[2 * kGdnChunk + lane] = exp_e(GC - G);
+        ed[3 * kGdnChunk + lane] = exp_e(GC);
+    };
+
+    bf16_t vcur[16];
+    uint32_t opk[8];                // bf16 pairs of O
+    int o_t0 = 0, o_nt = 0;
+    auto store_o = [&]() {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 16 * i + 4 * lg + j;
-                st.vv[4 * i + j] = t < nt ? v[((sp.base + t0 + t) * Hv + hv) * kGdnDim + col] : bf16_t(0);
+                const uint32_t wd = opk[2 * i + (j >> 1)];
+                if (t < o_nt)
+                    o[((sp.base + o_t0 + t) * Hv + hv) * kGdnDim + col] = static_cast<bf16_t>((j & 1) ? (wd >> 16) : (wd & 0xFFFFu));
             }
-    };
-    bf16_t vcur[16];
-    auto store = [&]() {
-        const int tp2 = tid & 31, dg = tid >> 5;
-#pragma unroll
-        for (int m = 0; m < GdnStage<NW>::kKd; ++m) {
-            const int d8 = dg * GdnStage<NW>::kKd + m;
-            *reinterpret_cast<u32x4 *>(sK + (2 * tp2) * kGdnPad + d8 * 8) = st.ka[m];
-            *reinterpret_cast<u32x4 *>(sK + (2 * tp2 + 1) * kGdnPad + d8 * 8) = st.kb[m];
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-                const uint32_t a = st.ka[m][e2], b = st.kb[m][e2];
-                *reinterpret_cast<uint32_t *>(sKt + (d8 * 8 + 2 * e2) * kGdnPad64 + 2 * tp2) = (a & 0xFFFFu) | (b << 16);
-                *reinterpret_cast<uint32_t *>(sKt + (d8 * 8 + 2 * e2 + 1) * kGdnPad64 + 2 * tp2) =
-                    (a >> 16) | (b & 0xFFFF0000u);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < GdnStage<NW>::kQp; ++m) {
-            const int p = tid + NT * m, t = p >> 4, d8 = p & 15;
-            *reinterpret_cast<u32x4 *>(sQ + t * kGdnPad + d8 * 8) = st.qv[m];
-        }
-#pragma unroll
-        for (int m = 0; m < GdnStage<NW>::kTp; ++m) {
-            const int p = tid + NT * m;                  // 16-byte piece of [Tb; P]
-            const int row = (p >> 3) & 63, c8 = p & 7;
-            bf16_t *dst = (p < 512 ? sTb : sP) + row * kGdnPad64 + c8 * 8;
-            *reinterpret_cast<u32x4 *>(dst) = st.tpv[m];
-        }
-        if (w == 0) {
-            const float G = wave_prefix_sum(st.gv);
-            const float Gprev = __shfl_up(G, 1);
-            const float GC = __shfl(G, 63);
-            sEp[lane] = lane == 0 ? 1.f : expf(Gprev);
-            sEc[lane] = scale * expf(G);
-            sEt[lane] = expf(GC - G);
-            if (lane == 0) sEC[0] = expf(GC);
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vcur[i] = st.vv[i];
     };
 
-    if (nck > 0) {
-        load(0);
-        store();
-    }
-    __syncthreads();
-    bf16_t *tr = sTr[w];
-    for (int c = 0; c < nck; ++c) {
+    // One chunk on a compute wave: tiles from `cur`, gates from `ec`; the next
+    // chunk's gates go to `en`.
+    auto step = [&](int c, const unsigned char *cur, const float *ec, float *en, bf16_t *tr) {
         const int t0 = c * kGdnChunk;
         const int nt = min(kGdnChunk, sp.len - t0);
-        if (c + 1 < nck) load(c + 1);
+        if (c + 1 < nck) issue(c + 1);
+        const unsigned char *bK = cur, *bQ = cur + oQ, *bKt = cur + oKt, *bTb = cur + oTb, *bP = cur + oP;
 
         // S -> bf16 B operand (k = rows of S).
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + 16 * i + 4 * lg) =
-                u32x2{pack_bf16x2(S[i][0], S[i][1]), pack_bf16x2(S[i][2], S[i][3])};
-        wave_sync();
+                u32x2{pk_bf16(S[i][0], S[i][1]), pk_bf16(S[i][2], S[i][3])};
+        bf16x8 ak[4][4], aq[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4) {
+                ak[i][s4] = *reinterpret_cast<const bf16x8 *>(bK + sw128(16 * i + lr, 4 * s4 + lg));
+                aq[i][s4] = *reinterpret_cast<const bf16x8 *>(bQ + sw128(16 * i + lr, 4 * s4 + lg));
+            }
+        lds_wave_sync();
         bf16x8 bs[4];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) bs[s4] = *reinterpret_cast<const bf16x8 *>(tr + lr * kGdnPad + 32 * s4 + 8 * lg);
@@ -354,26 +399,36 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(const int32_t *__rest
             rk[i] = rq[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s4 = 0; s4 < 4; ++s4) {
-                rk[i] = mfma32(*reinterpret_cast<const bf16x8 *>(sK + (16 * i + lr) * kGdnPad + 32 * s4 + 8 * lg),
-                               bs[s4], rk[i]);
-                rq[i] = mfma32(*reinterpret_cast<const bf16x8 *>(sQ + (16 * i + lr) * kGdnPad + 32 * s4 + 8 * lg),
-                               bs[s4], rq[i]);
+                rk[i] = mfma32(ak[i][s4], bs[s4], rk[i]);
+                rq[i] = mfma32(aq[i][s4], bs[s4], rq[i]);
             }
         }
+        bf16x8 atb[4][2], ap[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                atb[i][s2] = *reinterpret_cast<const bf16x8 *>(bTb + sw64(16 * i + lr, 4 * s2 + lg));
+                ap[i][s2] = *reinterpret_cast<const bf16x8 *>(bP + sw64(16 * i + lr, 4 * s2 + lg));
+            }
+        f32x4 ep[4], eg[4], et[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            ep[i] = *reinterpret_cast<const f32x4 *>(ec + 16 * i + 4 * lg);
+            eg[i] = *reinterpret_cast<const f32x4 *>(ec + kGdnChunk + 16 * i + 4 * lg);
+            et[i] = *reinterpret_cast<const f32x4 *>(ec + 2 * kGdnChunk + 16 * i + 4 * lg);
+        }
+        const float gC = ec[3 * kGdnChunk];
         // X = V - diag(gamma_{t-1}) K S, rows = tokens.
-        wave_sync();
+        lds_wave_sync();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float xv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * i + 4 * lg + j;
-                xv[j] = bf16_to_f32(vcur[4 * i + j]) - sEp[t] * rk[i][j];
-            }
-            *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + 16 * i + 4 * lg) =
-                u32x2{pack_bf16x2(xv[0], xv[1]), pack_bf16x2(xv[2], xv[3])};
+            for (int j = 0; j < 4; ++j) xv[j] = bf16_to_f32(vcur[4 * i + j]) - ep[i][j] * rk[i][j];
+            *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + 16 * i + 4 * lg) = u32x2{pk_bf16(xv[0], xv[1]), pk_bf16(xv[2], xv[3])};
         }
-        wave_sync();
+        lds_wave_sync();
         bf16x8 bx[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) bx[s2] = *reinterpret_cast<const bf16x8 *>(tr + lr * kGdnPad + 32 * s2 + 8 * lg);
@@ -382,22 +437,23 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(const int32_t *__rest
         for (int i = 0; i < 4; ++i) {
             U[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                U[i] = mfma32(*reinterpret_cast<const bf16x8 *>(sTb + (16 * i + lr) * kGdnPad64 + 32 * s2 + 8 * lg),
-                              bx[s2], U[i]);
+            for (int s2 = 0; s2 < 2; ++s2) U[i] = mfma32(atb[i][s2], bx[s2], U[i]);
         }
+        bf16x8 akt[8][2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) akt[i][s2] = *reinterpret_cast<const bf16x8 *>(bKt + sw64(16 * i + lr, 4 * s2 + lg));
         // U (for P U) in rows 0..63 and diag(exp(G_C - G_t)) U (for K^T) in rows 64..127.
-        wave_sync();
+        lds_wave_sync();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int tb = 16 * i + 4 * lg;
-            *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + tb) =
-                u32x2{pack_bf16x2(U[i][0], U[i][1]), pack_bf16x2(U[i][2], U[i][3])};
+            *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + tb) = u32x2{pk_bf16(U[i][0], U[i][1]), pk_bf16(U[i][2], U[i][3])};
             *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + 64 + tb) =
-                u32x2{pack_bf16x2(sEt[tb] * U[i][0], sEt[tb + 1] * U[i][1]),
-                      pack_bf16x2(sEt[tb + 2] * U[i][2], sEt[tb + 3] * U[i][3])};
+                u32x2{pk_bf16(et[i][0] * U[i][0], et[i][1] * U[i][1]), pk_bf16(et[i][2] * U[i][2], et[i][3] * U[i][3])};
         }
-        wave_sync();
+        lds_wave_sync();
         bf16x8 bu[2], bw[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -409,64 +465,97 @@ __global__ __launch_bounds__(64 * NW) void gdn_scan_kernel(const int32_t *__rest
         for (int i = 0; i < 4; ++i) {
             f32x4 acc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = sEc[16 * i + 4 * lg + j] * rq[i][j];
+            for (int j = 0; j < 4; ++j) acc[j] = eg[i][j] * rq[i][j];
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                acc = mfma32(*reinterpret_cast<const bf16x8 *>(sP + (16 * i + lr) * kGdnPad64 + 32 * s2 + 8 * lg),
-                             bu[s2], acc);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * i + 4 * lg + j;
-                if (t < nt) o[((sp.base + t0 + t) * Hv + hv) * kGdnDim + col] = f32_to_bf16(acc[j]);
-            }
+            for (int s2 = 0; s2 < 2; ++s2) acc = mfma32(ap[i][s2], bu[s2], acc);
+            opk[2 * i] = pk_bf16(acc[0], acc[1]);
+            opk[2 * i + 1] = pk_bf16(acc[2], acc[3]);
         }
+
         // S = gamma_C S + K^T diag(exp(G_C - G_t)) U
-        const float gC = sEC[0];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) S[i][j] *= gC;
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-                S[i] = mfma32(*reinterpret_cast<const bf16x8 *>(sKt + (16 * i + lr) * kGdnPad64 + 32 * s2 + 8 * lg),
-                              bw[s2], S[i]);
+            for (int s2 = 0; s2 < 2; ++s2) S[i] = mfma32(akt[i][s2], bw[s2], S[i]);
         }
-        __syncthreads();   // every wave is done with this chunk's tiles
-        if (c + 1 < nck) store();
-        __syncthreads();
+        if (c + 1 < nck) {
+            if (w == 0) gates(min(kGdnChunk, sp.len - t0 - kGdnChunk), en);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vcur[i] = vnext[i];
+        }
+        o_t0 = t0;
+        o_nt = nt;
+        store_o();
+    };
+
+    // Waves NW .. NW+NP-1 are producers: they alone issue the LDS copies (so
+    // no compute wave ever waits for one before reading LDS) and wait for them
+    // before each barrier.  Barrier c+1 marks chunk c+1 landed in buffer (c+1)&1 and
+    // chunk c (buffer c&1) consumed, so the producer may refill c&1 next.
+    if (w >= NW) {
+        const int pw = w - NW;
+        if (nck > 0) dma(0, sbuf, pw);
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();
+        for (int c = 0; c < nck; ++c) {
+            if (c + 1 < nck) dma(c + 1, sbuf + ((c + 1) & 1) * kBuf, pw);
+            __builtin_amdgcn_s_waitcnt(0);
+            lds_barrier();
+        }
+        return;
+    }
+    if (nck > 0) {
+        issue(0);
+        if (w == 0) gates(min(kGdnChunk, sp.len), sE);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vcur[i] = vnext[i];
+    }
+    lds_barrier();
+    for (int c = 0; c < nck; ++c) {
+        const int b = c & 1;
+        step(c, sbuf + b * kBuf, sE + b * kE, sE + (b ^ 1) * kE, sTr[w]);
+        lds_barrier();
     }
     if (s_out) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) s_out[sbase + static_cast<int64_t>(16 * i + 4 * lg + j) * kGdnDim + col] = S[i][j];
+            for (int j = 0; j < 4; ++j) s_out[sbase + (16 * i + 4 * lg + j) * kGdnDim + col] = S[i][j];
     }
 }
 
-constexpr int kGdnScanWaves = 2;
+constexpr int kGdnScanWaves = 2;      // compute waves of a scan work-group (32 value columns)
+constexpr int kGdnScanProducers = 2;  // waves that stream its tiles
 
-hipError_t launch_gdn_prefill(hipStream_t stream, int nseq, const int32_t *cu, int64_t n_tok, int max_len, int Hq,
-                              int Hv, float scale, const bf16_t *q, const bf16_t *k, const bf16_t *v, const float *g,
-                              const float *beta, const float *s0, bf16_t *o, float *s_out, bf16_t *tp)
+hipError_t launch_gdn_prep(hipStream_t stream, int nseq, const int32_t *cu, int64_t n_tok, int max_len, int Hq, int Hv,
+                           float scale, const bf16_t *q, const bf16_t *k, const float *g, const float *beta, bf16_t *ws)
 {
     const int nchunk_cap = (max_len + kGdnChunk - 1) / kGdnChunk;
-    if (nchunk_cap > 0) {
-        hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(nchunk_cap), static_cast<unsigned>(Hq),
-                                                 static_cast<unsigned>(nseq)),
-                           dim3(256), 0, stream, cu, n_tok, max_len, nchunk_cap, Hq, Hv, scale, q, k, g, beta, tp);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    constexpr int kSlices = kGdnDim / (16 * kGdnScanWaves);
-    const int64_t nwg = static_cast<int64_t>(nseq) * Hv * kSlices;
-    hipLaunchKernelGGL(gdn_scan_kernel<kGdnScanWaves>, dim3(static_cast<unsigned>(nwg)), dim3(64 * kGdnScanWaves), 0,
-                       stream, cu, n_tok, max_len, nchunk_cap, Hq, Hv, scale, q, k, v, g, tp, s0, o, s_out);
+    if (nchunk_cap == 0) return hipSuccess;
+    const int64_t nwg = static_cast<int64_t>(nseq) * nchunk_cap * Hv;
+    hipLaunchKernelGGL(gdn_prep_kernel, dim3(static_cast<unsigned>(nwg)), dim3(64), 0, stream, cu, n_tok, max_len,
+                       nchunk_cap, nseq, Hq, Hv, scale, q, k, g, beta, ws);
     return hipGetLastError();
 }
 
-size_t gdn_workspace_bytes(int nseq, int64_t max_len, int Hv) {
+hipError_t launch_gdn_scan(hipStream_t stream, int nseq, const int32_t *cu, int64_t n_tok, int max_len, int Hq, int Hv,
+                           float scale, const bf16_t *q, const bf16_t *k, const bf16_t *v, const float *g,
+                           const float *s0, bf16_t *o, float *s_out, const bf16_t *ws)
+{
+    const int nchunk_cap = (max_len + kGdnChunk - 1) / kGdnChunk;
+    constexpr int kSlices = kGdnDim / (16 * kGdnScanWaves);
+    const int64_t nwg = static_cast<int64_t>(nseq) * Hv * kSlices;
+    hipLaunchKernelGGL((gdn_scan_kernel<kGdnScanWaves, kGdnScanProducers>), dim3(static_cast<unsigned>(nwg)),
+                       dim3(64 * (kGdnScanWaves + kGdnScanProducers)), 0,
+                       stream, cu, n_tok, max_len, nchunk_cap, nseq, Hq, Hv, scale, q, k, v, g, ws, s0, o, s_out);
+    return hipGetLastError();
+}
+
+size_t gdn_workspace_bytes(int nseq, int64_t max_len, int Hq, int Hv) {
     const int64_t nchunk_cap = (max_len + kGdnChunk - 1) / kGdnChunk;
-    return static_cast<size_t>(nseq) * Hv * nchunk_cap * 2 * kGdnTile * sizeof(bf16_t);
+    return static_cast<size_t>(nseq) * (Hv + Hq) * nchunk_cap * 2 * kGdnTile * sizeof(bf16_t);
 }
 
 }  // namespace qsa

@@ -53,10 +53,12 @@ hipError_t launch_attend_backward(const Tables &, hipStream_t, int32_t, int64_t,
                                   const bf16_t *, const bf16_t *, const int32_t *, const bf16_t *, const bf16_t *,
                                   const float *, float *, float *, float *);
 hipError_t launch_token_keys(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, const bf16_t *, bf16_t *);
-hipError_t launch_gdn_prefill(hipStream_t, int, const int32_t *, int64_t, int, int, int, float, const bf16_t *,
-                              const bf16_t *, const bf16_t *, const float *, const float *, const float *, bf16_t *,
-                              float *, bf16_t *);
-size_t gdn_workspace_bytes(int, int64_t, int);
+hipError_t launch_gdn_prep(hipStream_t, int, const int32_t *, int64_t, int, int, int, float, const bf16_t *,
+                           const bf16_t *, const float *, const float *, bf16_t *);
+hipError_t launch_gdn_scan(hipStream_t, int, const int32_t *, int64_t, int, int, int, float, const bf16_t *,
+                           const bf16_t *, const bf16_t *, const float *, const float *, bf16_t *, float *,
+                           const bf16_t *);
+size_t gdn_workspace_bytes(int, int64_t, int, int);
 hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t,
                                       const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, uint32_t *);
 }  // namespace qsa
@@ -656,30 +658,73 @@ qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 
-size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hv_heads) {
-    if (nseq < 1 || max_len < 0 || hv_heads < 1) return 0;
-    return align_up(gdn_workspace_bytes(nseq, max_len, hv_heads));
+size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hq_heads, int32_t hv_heads) {
+    if (nseq < 1 || max_len < 0 || hq_heads < 1 || hv_heads < 1) return 0;
+    return align_up(gdn_workspace_bytes(nseq, max_len, hq_heads, hv_heads));
 }
+
+namespace {
+// Checks shared by the GDN entry points (everything before the first launch).
+qsa_status gdn_check(int32_t nseq, const int32_t *cu, int64_t n_tokens, int64_t max_len, int32_t hq, int32_t hv,
+                     std::initializer_list<const void *> needed, const void *q, const void *k, const void *ws,
+                     size_t ws_bytes) {
+    if (!cu) return QSA_ERR_NULL;
+    for (const void *p : needed)
+        if (!p) return QSA_ERR_NULL;
+    if (nseq < 1 || nseq > 65535 || n_tokens < 0 || max_len < 0 || max_len > (int64_t(1) << 30) || hq < 1 ||
+        hq > 65535 || hv < hq || hv % hq != 0)
+        return QSA_ERR_SHAPE;
+    if (!aligned16(q) || !aligned16(k)) return QSA_ERR_ALIGN;
+    const size_t need = qsa_gdn_workspace_size(nseq, max_len, hq, hv);
+    if (need > 0) {
+        if (!ws) return QSA_ERR_NULL;
+        if (!aligned16(ws)) return QSA_ERR_ALIGN;
+        if (ws_bytes < need) return QSA_ERR_WORKSPACE;
+    }
+    return QSA_OK;
+}
+}  // namespace
 
 qsa_status qsa_gdn_chunk_prefill(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens,
                                  int64_t max_len, int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q,
                                  const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
                                  const float *initial_state, uint16_t *o, float *final_state, void *ws,
                                  size_t ws_bytes) {
-    if (!cu_seqlens || !q || !k || !v || !g || !beta || !o) return QSA_ERR_NULL;
-    if (nseq < 1 || nseq > 65535 || n_tokens < 0 || max_len < 0 || max_len > (int64_t(1) << 30) || hq_heads < 1 ||
-        hq_heads > 65535 || hv_heads < hq_heads || hv_heads % hq_heads != 0)
-        return QSA_ERR_SHAPE;
-    if (!aligned16(q) || !aligned16(k)) return QSA_ERR_ALIGN;
-    const size_t need = qsa_gdn_workspace_size(nseq, max_len, hv_heads);
-    if (need > 0) {
-        if (!ws) return QSA_ERR_NULL;
-        if (!aligned16(ws)) return QSA_ERR_ALIGN;
-        if (ws_bytes < need) return QSA_ERR_WORKSPACE;
-    }
-    hipError_t e = launch_gdn_prefill(static_cast<hipStream_t>(stream), nseq, cu_seqlens, n_tokens,
-                                      static_cast<int>(max_len), hq_heads, hv_heads, scale, q, k, v, g, beta,
-                                      initial_state, o, final_state, static_cast<bf16_t *>(ws));
+    qsa_status s = gdn_check(nseq, cu_seqlens, n_tokens, max_len, hq_heads, hv_heads, {q, k, v, g, beta, o}, q, k, ws,
+                             ws_bytes);
+    if (s != QSA_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    bf16_t *tp = static_cast<bf16_t *>(ws);
+    hipError_t e = launch_gdn_prep(st, nseq, cu_seqlens, n_tokens, static_cast<int>(max_len), hq_heads, hv_heads,
+                                   scale, q, k, g, beta, tp);
+    if (e == hipSuccess)
+        e = launch_gdn_scan(st, nseq, cu_seqlens, n_tokens, static_cast<int>(max_len), hq_heads, hv_heads, scale, q,
+                            k, v, g, initial_state, o, final_state, tp);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_gdn_prep(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens, int64_t max_len,
+                        int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q, const uint16_t *k,
+                        const float *g, const float *beta, void *ws, size_t ws_bytes) {
+    qsa_status s = gdn_check(nseq, cu_seqlens, n_tokens, max_len, hq_heads, hv_heads, {q, k, g, beta}, q, k, ws,
+                             ws_bytes);
+    if (s != QSA_OK) return s;
+    hipError_t e = launch_gdn_prep(static_cast<hipStream_t>(stream), nseq, cu_seqlens, n_tokens,
+                                   static_cast<int>(max_len), hq_heads, hv_heads, scale, q, k, g, beta,
+                                   static_cast<bf16_t *>(ws));
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_gdn_scan(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens, int64_t max_len,
+                        int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, const float *g, const float *initial_state, uint16_t *o,
+                        float *final_state, const void *ws, size_t ws_bytes) {
+    qsa_status s = gdn_check(nseq, cu_seqlens, n_tokens, max_len, hq_heads, hv_heads, {q, k, v, g, o}, q, k, ws,
+                             ws_bytes);
+    if (s != QSA_OK) return s;
+    hipError_t e = launch_gdn_scan(static_cast<hipStream_t>(stream), nseq, cu_seqlens, n_tokens,
+                                   static_cast<int>(max_len), hq_heads, hv_heads, scale, q, k, v, g, initial_state, o,
+                                   final_state, static_cast<const bf16_t *>(ws));
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

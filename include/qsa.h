@@ -358,17 +358,33 @@ qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32
  * bf16 with o_t = scale * S_t^T q_t (the state after token t); final_state
  * (same layout as initial_state, may be NULL, may alias initial_state) the
  * state after each sequence's last token.  ws: qsa_gdn_workspace_size(nseq,
- * max_len, hv_heads) bytes.  Errors: QSA_ERR_NULL (q, k, v, g, beta, o,
+ * max_len, hq_heads, hv_heads) bytes.  Errors: QSA_ERR_NULL (q, k, v, g, beta, o,
  * cu_seqlens or a needed ws missing), QSA_ERR_SHAPE (nseq outside 1..65535,
  * n_tokens or max_len negative or max_len above 2^30, hq_heads outside 1..65535,
  * hv_heads not a positive multiple of hq_heads), QSA_ERR_ALIGN (q, k or ws not
  * 16-byte aligned), QSA_ERR_WORKSPACE, QSA_ERR_HIP. */
-size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hv_heads);
+size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hq_heads, int32_t hv_heads);
 qsa_status qsa_gdn_chunk_prefill(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens,
                                  int64_t max_len, int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q,
                                  const uint16_t *k, const uint16_t *v, const float *g, const float *beta,
                                  const float *initial_state, uint16_t *o, float *final_state, void *ws,
                                  size_t ws_bytes);
+
+/* The two stages of qsa_gdn_chunk_prefill, for callers that time or schedule
+ * them apart (same arguments and errors; run qsa_gdn_prep, then qsa_gdn_scan
+ * on the same ws and stream).  qsa_gdn_prep writes, for every chunk of 64
+ * tokens and V head, the two 64 x 64 bf16 matrices that do not depend on the
+ * state (the inverse of the chunk's unit lower-triangular delta-rule system
+ * times diag(beta), and the decayed, scaled causal q.k products) into ws;
+ * qsa_gdn_scan walks the chunks in order, carrying the state, and writes o and
+ * final_state. */
+qsa_status qsa_gdn_prep(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens, int64_t max_len,
+                        int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q, const uint16_t *k,
+                        const float *g, const float *beta, void *ws, size_t ws_bytes);
+qsa_status qsa_gdn_scan(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens, int64_t max_len,
+                        int32_t hq_heads, int32_t hv_heads, float scale, const uint16_t *q, const uint16_t *k,
+                        const uint16_t *v, const float *g, const float *initial_state, uint16_t *o,
+                        float *final_state, const void *ws, size_t ws_bytes);
 
 /* Static string for a status code. */
 const char *qsa_status_string(qsa_status s);

@@ -36,7 +36,7 @@ def run_gdn(x, scale, with_final=True, max_len=None):
     max_len = max(lens) if max_len is None else max_len
     o = torch.empty_like(x["v"])
     fs = torch.empty(nseq, hv, 128, 128, device="cuda") if with_final else None
-    ws = torch.empty(max(Q.qsa_gdn_workspace_size(nseq, max_len, hv), 16), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(max(Q.qsa_gdn_workspace_size(nseq, max_len, x["q"].shape[1], hv), 16), dtype=torch.uint8, device="cuda")
     Q.qsa_gdn_chunk_prefill(nseq, cu, max_len, x["q"], x["k"], x["v"], x["g"], x["beta"], scale, x["s0"], o, fs, ws)
     torch.cuda.synchronize()
     return o, fs
