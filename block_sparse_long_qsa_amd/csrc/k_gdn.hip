@@ -21,9 +21,8 @@
 // gdn_scan_kernel then walks the chunks of one (sequence, V head, 16*NW value
 // columns) in order with its columns of S in registers (each column of S
 // evolves on its own), so a head's state is advanced by 128/(16*NW)
-// work-groups at once.  Each chunk's tiles (K, Q, K^T, Tb, P: 64 KiB) are
-// copied into LDS by the LDS-DMA path (global_load_lds, 16 bytes a lane) one
-// chunk ahead, into the other half of a double buffer.
+// work-groups at once; its memory traffic runs on separate producer and store
+// waves (see gdn_scan_kernel).
 //
 // Matrix cores: v_mfma_f32_16x16x32_bf16; A lane l = row l%16, k = 8(l/16)..+7;
 // B lane l = column l%16, same k; C lane l = rows 4(l/16)..+3, column l%16.
@@ -103,6 +102,14 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+// A barrier with no memory fence (the caller has waited for what it needs);
+// the empty asm statements keep the compiler from moving memory accesses
+// across it.
+__device__ __forceinline__ void raw_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 __device__ __forceinline__ void lds_wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
@@ -258,30 +265,39 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const int32_t *__restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Chunk walk of one (sequence, V head, 16*NW value columns).  Wave w owns the
-// 16 columns c0 = 16*(NW*slice + w) .. +15 of S (rows 16i + 4(l/16) + j of
-// column c0 + l%16 in S[i][j]).  Per chunk, from the LDS tiles:
+// Chunk walk of one (sequence, V head, 16*NW value columns).  Compute wave w
+// owns the 16 columns c0 = 16*(NW*slice + w) .. +15 of S (rows 16i + 4(l/16)
+// + j of column c0 + l%16 in S[i][j]).  Per chunk, from LDS only:
 //   R_K = K S, R_Q = Q S                                  (32 products)
 //   X = V - diag(gamma_{t-1}) R_K;  U = Tb X              (8)
 //   O = diag(scale gamma_t) R_Q + P U                     (8)
 //   S = gamma_C S + K^T diag(exp(G_C - G_t)) U            (16)
-// O is kept in registers and stored during the next chunk.  One more wave
-// (the producer) streams the tiles into LDS.
+// All global traffic of the walk runs on two more kinds of wave, so that a
+// compute wave never waits on memory: NP producer waves copy each chunk's
+// tiles (K, Q, K^T, Tb, P, the V columns, and the gates one chunk earlier)
+// into a two-slot LDS ring with the LDS-DMA path (global_load_lds) one chunk
+// ahead, and one store wave writes each chunk's O from LDS to memory while the
+// next chunk computes.
 template <int NW, int NP>
-__global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t *__restrict__ cu, int64_t n_tok, int max_len,
-                                                          int nchunk_cap, int nseq, int Hq, int Hv, float scale,
-                                                          const bf16_t *__restrict__ q, const bf16_t *__restrict__ k,
-                                                          const bf16_t *__restrict__ v, const float *__restrict__ g,
-                                                          const bf16_t *__restrict__ ws, const float *s0,
-                                                          bf16_t *__restrict__ o, float *s_out)
+__global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
+    const int32_t *__restrict__ cu, int64_t n_tok, int max_len, int nchunk_cap, int nseq, int Hq, int Hv, float scale,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
+    const float *__restrict__ g, const bf16_t *__restrict__ ws, const float *s0, bf16_t *__restrict__ o, float *s_out)
 {
-    constexpr int kSlices = kGdnDim / (16 * NW);
-    constexpr int kBuf = 65536;                       // K, Q (16 KiB each), K^T (16 KiB), Tb, P (8 KiB each)
-    constexpr int oQ = 16384, oKt = 32768, oTb = 49152, oP = 57344;
+    constexpr int kCols = 16 * NW;                    // value columns of the work-group
+    constexpr int kSlices = kGdnDim / kCols;
+    // One ring slot: K, Q (sw128), K^T, Tb, P (sw64), V [64][kCols] bf16.
+    constexpr int oQ = 16384, oKt = 32768, oTb = 49152, oP = 57344, oV = 65536;
+    constexpr int kSlot = oV + kGdnChunk * kCols * 2;
+    constexpr int kMainPieces = kSlot / 1024;         // 1 KiB copies per chunk (16-byte lanes)
     constexpr int kE = 4 * kGdnChunk;                 // exp(G_{t-1}), scale exp(G_t), exp(G_C - G_t), exp(G_C)
-    __shared__ __align__(16) unsigned char sbuf[2 * kBuf];
+    static_assert(kSlot % 1024 == 0, "ring slot must be whole 1 KiB pieces");
+    __shared__ __align__(16) unsigned char sbuf[2 * kSlot];
+    __shared__ __align__(16) float sg[3][kGdnChunk];            // gates g, three chunks
+    __shared__ __align__(16) bf16_t sO[2][kGdnChunk * kCols];   // O staging, [token][kCols]
     __shared__ __align__(16) bf16_t sTr[NW][16 * kGdnPad];
     __shared__ __align__(16) float sE[2 * kE];
+    __shared__ __align__(16) unsigned char sdummy[256];        // target of the L2 touches
 
     const int64_t e = xcd_local_id();
     const int slice = static_cast<int>(e % kSlices);
@@ -289,13 +305,144 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
     const int s = static_cast<int>(e / (static_cast<int64_t>(kSlices) * Hv));
     const int hq = hv / (Hv / Hq);
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int col = 16 * (NW * slice + w) + lr;
+    // The wave index is read into a scalar register: the roles below branch on it
+    // and the LDS-DMA destination (M0) is computed from it.
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const GdnSpan sp = gdn_span(cu, s, n_tok, max_len);
     const int nck = (sp.len + kGdnChunk - 1) / kGdnChunk;
-    const int64_t sbase = (static_cast<int64_t>(s) * Hv + hv) * kGdnDim * kGdnDim;
     const int kstride = Hq * kGdnDim, vstride = Hv * kGdnDim;
+    const int col0 = kCols * slice;                   // first value column of the work-group
 
+    auto chunk_nt = [&](int c) { return min(kGdnChunk, sp.len - c * kGdnChunk); };
+
+    // ---- producer waves: pieces p = pw, pw + NP, ... of the kMainPieces of a
+    // chunk (rows past the end repeat the last token; see gdn_prep_kernel for
+    // why that is harmless), and the gates of the chunk after it.
+    if (w >= NW + 1) {
+        const int pw = w - NW - 1;
+        // Producer 0 copies K, K^T and V; producer 1 copies Q, Tb and P.
+        // Every loop is unrolled so that a copy costs a few address operations.
+        static_assert(NP == 2, "the copy split below is written for two producers");
+        const int lrow = lane >> 4, lcp = lane & 15;
+        const int rowbytes = kstride * 2;
+        auto copy_main = [&](int c, unsigned char *dst) {
+            const int last = chunk_nt(c) - 1;
+            const int64_t tok0 = sp.base + c * kGdnChunk;
+            const unsigned char *rows = reinterpret_cast<const unsigned char *>((pw == 0 ? k : q) + (tok0 * Hq + hq) * kGdnDim);
+            unsigned char *drows = dst + (pw == 0 ? 0 : oQ);
+#pragma unroll
+            for (int n = 0; n < 16; ++n) {         // K or Q: rows 4n .. 4n+3, swizzled 16-byte chunks
+                const int row = 4 * n + lrow;
+                const int src = min(row, last) * rowbytes + 16 * (lcp ^ ((4 * (n & 3)) + lrow));
+                __builtin_amdgcn_global_load_lds(rows + src, drows + 1024 * n, 16, 0, 0);
+            }
+            const unsigned char *flat = reinterpret_cast<const unsigned char *>(
+                pw == 0 ? ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c) : ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c));
+            unsigned char *dflat = dst + (pw == 0 ? oKt : oTb);
+#pragma unroll
+            for (int n = 0; n < 16; ++n)           // K^T, or Tb then P: contiguous 16 KiB
+                __builtin_amdgcn_global_load_lds(flat + 1024 * n + 16 * lane, dflat + 1024 * n, 16, 0, 0);
+            if (pw == 0) {
+                constexpr int kChunksPerRow = kCols / 8;
+                constexpr int kRowsPerPiece = 64 / kChunksPerRow;
+                const unsigned char *vr = reinterpret_cast<const unsigned char *>(v + (tok0 * Hv + hv) * kGdnDim + col0);
+#pragma unroll
+                for (int n = 0; n < (kSlot - oV) / 1024; ++n) {   // V: kRowsPerPiece tokens per 1 KiB
+                    const int row = n * kRowsPerPiece + lane / kChunksPerRow;
+                    const int64_t src = static_cast<int64_t>(min(row, last)) * vstride * 2 + 16 * (lane % kChunksPerRow);
+                    __builtin_amdgcn_global_load_lds(vr + src, dst + oV + 1024 * n, 16, 0, 0);
+                }
+            }
+        };
+        // Pull chunk c's lines into L2 one chunk before its copy: 4-byte
+        // LDS-DMA loads, one 128-byte line per lane, into a scratch area
+        // nothing reads (the only load form that needs no destination register).
+        auto touch = [&](int c) {
+            const int last = chunk_nt(c) - 1;
+            const int64_t tok0 = sp.base + c * kGdnChunk;
+            const unsigned char *kt = reinterpret_cast<const unsigned char *>(ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c));
+            const unsigned char *tpw = reinterpret_cast<const unsigned char *>(ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c));
+            const unsigned char *kr = reinterpret_cast<const unsigned char *>(k + (tok0 * Hq + hq) * kGdnDim);
+            const unsigned char *qr = reinterpret_cast<const unsigned char *>(q + (tok0 * Hq + hq) * kGdnDim);
+            const int row = min(lane >> 1, last), half = 128 * (lane & 1);
+            const int64_t kq = static_cast<int64_t>(row) * kstride * 2 + half;                 // rows 0..31
+            const int64_t kq2 = static_cast<int64_t>(min(32 + (lane >> 1), last)) * kstride * 2 + half;
+            __builtin_amdgcn_global_load_lds(kr + kq, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(kr + kq2, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(qr + kq, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(qr + kq2, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(kt + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(kt + 8192 + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(tpw + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(tpw + 8192 + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds(v + ((tok0 + min(lane, last)) * Hv + hv) * kGdnDim + col0, static_cast<void *>(sdummy), 4, 0, 0);
+        };
+        // Gates go through a register: loaded at the top of the iteration
+        // (always, from a valid chunk) and written to the ring after the wait.
+        auto load_gates = [&](int c) {
+            c = min(c, nck - 1);
+            const int last = chunk_nt(c) - 1;
+            return g[(sp.base + c * kGdnChunk + min(lane, last)) * Hv + hv];
+        };
+        constexpr int kWaitLds = 0xF | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
+        if (nck > 0) {
+            const float g0 = load_gates(0), g1 = load_gates(1);
+            copy_main(0, sbuf);
+            __builtin_amdgcn_s_waitcnt(0);
+            if (pw == 0) {
+                sg[0][lane] = g0;
+                sg[1][lane] = g1;
+                if (nck > 1) touch(1);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLds);
+        raw_barrier();
+        raw_barrier();
+        for (int c = 0; c < nck; ++c) {
+            // Chunk c+1 is copied now and must land before barrier c+1; its
+            // lines were touched one iteration ago.  Chunk c+2 is touched now.
+            const float gn = load_gates(c + 2);
+            if (c + 1 < nck) copy_main(c + 1, sbuf + ((c + 1) & 1) * kSlot);
+            __builtin_amdgcn_s_waitcnt(0);
+            if (pw == 0 && c + 2 < nck) {
+                sg[(c + 2) % 3][lane] = gn;
+                touch(c + 2);
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitLds);
+            raw_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
+    }
+
+    // ---- store wave: O of chunk c-1 from sO[(c-1)&1] while chunk c computes.
+    if (w == NW) {
+        constexpr int kChunksPerRow = kCols / 8;
+        auto store = [&](int c) {
+            const int nt = chunk_nt(c);
+            const bf16_t *src = sO[c & 1];
+#pragma unroll
+            for (int n = 0; n < kGdnChunk * kChunksPerRow / 64; ++n) {
+                const int idx = lane + 64 * n, t = idx / kChunksPerRow, cc = idx % kChunksPerRow;
+                const u32x4 val = *reinterpret_cast<const u32x4 *>(src + t * kCols + 8 * cc);
+                if (t < nt)
+                    *reinterpret_cast<u32x4 *>(o + ((sp.base + c * kGdnChunk + t) * Hv + hv) * kGdnDim + col0 + 8 * cc) = val;
+            }
+        };
+        lds_barrier();
+        lds_barrier();
+        for (int c = 0; c < nck; ++c) {
+            if (c > 0) store(c - 1);
+            lds_barrier();
+        }
+        if (nck > 0) store(nck - 1);
+        return;
+    }
+
+    // ---- compute waves
+    const int lcol = 16 * w + lr;                     // column within the work-group
+    const int col = col0 + lcol;
+    const int64_t sbase = (static_cast<int64_t>(s) * Hv + hv) * kGdnDim * kGdnDim;
     f32x4 S[8];
     if (s0) {
 #pragma unroll
@@ -306,45 +453,8 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
 #pragma unroll
         for (int i = 0; i < 8; ++i) S[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-
-    // The producer wave copies chunk c's tiles into `dst` (rows past the end
-    // repeat the last token; see gdn_prep_kernel for why that is harmless).
-    auto dma = [&](int c, unsigned char *dst, int pw) {
-        const int t0 = c * kGdnChunk;
-        const int last = min(kGdnChunk, sp.len - t0) - 1;
-        const int64_t tok0 = sp.base + t0;
-        const bf16_t *kt = ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c);
-        const bf16_t *tpw = ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c);
-#pragma unroll 8
-        for (int p = pw; p < 64; p += NP) {            // 1 KiB pieces of the buffer
-            const bf16_t *src;
-            if (p < 32) {
-                const int row = 4 * (p & 15) + (lane >> 4), cp = lane & 15;
-                src = (p < 16 ? k : q) + (tok0 * Hq + hq) * kGdnDim + min(row, last) * kstride + 8 * (cp ^ (row & 15));
-            } else if (p < 48) {
-                src = kt + 512 * (p - 32) + 8 * lane;
-            } else {
-                src = tpw + 512 * (p - 48) + 8 * lane;
-            }
-            __builtin_amdgcn_global_load_lds(src, dst + 1024 * p, 16, 0, 0);
-        }
-    };
-    // Compute waves load chunk c's V columns and gates into registers.
-    bf16_t vnext[16];
-    float gnext = 0.f;
-    auto issue = [&](int c) {
-        const int t0 = c * kGdnChunk;
-        const int last = min(kGdnChunk, sp.len - t0) - 1;
-        const int64_t tok0 = sp.base + t0;
-        const bf16_t *vb = v + (tok0 * Hv + hv) * kGdnDim + col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) vnext[4 * i + j] = vb[min(16 * i + 4 * lg + j, last) * vstride];
-        gnext = g[(tok0 + min(lane, last)) * Hv + hv];
-    };
-    auto gates = [&](int nt, float *__restrict__ ed) {            // wave 0
-        const float G = wave_prefix_sum(lane < nt ? gnext : 0.f);
+    auto gates = [&](int c, float *ed) {              // wave 0
+        const float G = wave_prefix_sum(lane < chunk_nt(c) ? sg[c % 3][lane] : 0.f);
         const float Gprev = __shfl_up(G, 1);
         const float GC = __shfl(G, 63);
         ed[lane] = lane == 0 ? 1.f : exp_e(Gprev);
@@ -352,29 +462,16 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
         ed[2 * kGdnChunk + lane] = exp_e(GC - G);
         ed[3 * kGdnChunk + lane] = exp_e(GC);
     };
+    bf16_t *tr = sTr[w];
 
-    bf16_t vcur[16];
-    uint32_t opk[8];                // bf16 pairs of O
-    int o_t0 = 0, o_nt = 0;
-    auto store_o = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 16 * i + 4 * lg + j;
-                const uint32_t wd = opk[2 * i + (j >> 1)];
-                if (t < o_nt)
-                    o[((sp.base + o_t0 + t) * Hv + hv) * kGdnDim + col] = static_cast<bf16_t>((j & 1) ? (wd >> 16) : (wd & 0xFFFFu));
-            }
-    };
-
-    // One chunk on a compute wave: tiles from `cur`, gates from `ec`; the next
-    // chunk's gates go to `en`.
-    auto step = [&](int c, const unsigned char *cur, const float *ec, float *en, bf16_t *tr) {
-        const int t0 = c * kGdnChunk;
-        const int nt = min(kGdnChunk, sp.len - t0);
-        if (c + 1 < nck) issue(c + 1);
+    lds_barrier();                                    // chunk 0 and the gates of chunks 0, 1 have landed
+    if (w == 0 && nck > 0) gates(0, sE);
+    lds_barrier();
+    for (int c = 0; c < nck; ++c) {
+        const unsigned char *cur = sbuf + (c & 1) * kSlot;
         const unsigned char *bK = cur, *bQ = cur + oQ, *bKt = cur + oKt, *bTb = cur + oTb, *bP = cur + oP;
+        const bf16_t *bV = reinterpret_cast<const bf16_t *>(cur + oV);
+        const float *ec = sE + (c & 1) * kE;
 
         // S -> bf16 B operand (k = rows of S).
 #pragma unroll
@@ -412,11 +509,14 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
                 ap[i][s2] = *reinterpret_cast<const bf16x8 *>(bP + sw64(16 * i + lr, 4 * s2 + lg));
             }
         f32x4 ep[4], eg[4], et[4];
+        float vv[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             ep[i] = *reinterpret_cast<const f32x4 *>(ec + 16 * i + 4 * lg);
             eg[i] = *reinterpret_cast<const f32x4 *>(ec + kGdnChunk + 16 * i + 4 * lg);
             et[i] = *reinterpret_cast<const f32x4 *>(ec + 2 * kGdnChunk + 16 * i + 4 * lg);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[4 * i + j] = bf16_to_f32(bV[(16 * i + 4 * lg + j) * kCols + lcol]);
         }
         const float gC = ec[3 * kGdnChunk];
         // X = V - diag(gamma_{t-1}) K S, rows = tokens.
@@ -425,7 +525,7 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
         for (int i = 0; i < 4; ++i) {
             float xv[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) xv[j] = bf16_to_f32(vcur[4 * i + j]) - ep[i][j] * rk[i][j];
+            for (int j = 0; j < 4; ++j) xv[j] = vv[4 * i + j] - ep[i][j] * rk[i][j];
             *reinterpret_cast<u32x2 *>(tr + lr * kGdnPad + 16 * i + 4 * lg) = u32x2{pk_bf16(xv[0], xv[1]), pk_bf16(xv[2], xv[3])};
         }
         lds_wave_sync();
@@ -460,7 +560,8 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
             bu[s2] = *reinterpret_cast<const bf16x8 *>(tr + lr * kGdnPad + 32 * s2 + 8 * lg);
             bw[s2] = *reinterpret_cast<const bf16x8 *>(tr + lr * kGdnPad + 64 + 32 * s2 + 8 * lg);
         }
-        // O = diag(scale gamma_t) Q S + P U
+        // O = diag(scale gamma_t) Q S + P U, staged as bf16 for the store wave.
+        bf16_t *so = sO[c & 1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f32x4 acc;
@@ -468,10 +569,13 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
             for (int j = 0; j < 4; ++j) acc[j] = eg[i][j] * rq[i][j];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) acc = mfma32(ap[i][s2], bu[s2], acc);
-            opk[2 * i] = pk_bf16(acc[0], acc[1]);
-            opk[2 * i + 1] = pk_bf16(acc[2], acc[3]);
+            const uint32_t p01 = pk_bf16(acc[0], acc[1]), p23 = pk_bf16(acc[2], acc[3]);
+            const int tb = 16 * i + 4 * lg;
+            so[(tb + 0) * kCols + lcol] = static_cast<bf16_t>(p01 & 0xFFFFu);
+            so[(tb + 1) * kCols + lcol] = static_cast<bf16_t>(p01 >> 16);
+            so[(tb + 2) * kCols + lcol] = static_cast<bf16_t>(p23 & 0xFFFFu);
+            so[(tb + 3) * kCols + lcol] = static_cast<bf16_t>(p23 >> 16);
         }
-
         // S = gamma_C S + K^T diag(exp(G_C - G_t)) U
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -480,42 +584,7 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) S[i] = mfma32(akt[i][s2], bw[s2], S[i]);
         }
-        if (c + 1 < nck) {
-            if (w == 0) gates(min(kGdnChunk, sp.len - t0 - kGdnChunk), en);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) vcur[i] = vnext[i];
-        }
-        o_t0 = t0;
-        o_nt = nt;
-        store_o();
-    };
-
-    // Waves NW .. NW+NP-1 are producers: they alone issue the LDS copies (so
-    // no compute wave ever waits for one before reading LDS) and wait for them
-    // before each barrier.  Barrier c+1 marks chunk c+1 landed in buffer (c+1)&1 and
-    // chunk c (buffer c&1) consumed, so the producer may refill c&1 next.
-    if (w >= NW) {
-        const int pw = w - NW;
-        if (nck > 0) dma(0, sbuf, pw);
-        __builtin_amdgcn_s_waitcnt(0);
-        lds_barrier();
-        for (int c = 0; c < nck; ++c) {
-            if (c + 1 < nck) dma(c + 1, sbuf + ((c + 1) & 1) * kBuf, pw);
-            __builtin_amdgcn_s_waitcnt(0);
-            lds_barrier();
-        }
-        return;
-    }
-    if (nck > 0) {
-        issue(0);
-        if (w == 0) gates(min(kGdnChunk, sp.len), sE);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vcur[i] = vnext[i];
-    }
-    lds_barrier();
-    for (int c = 0; c < nck; ++c) {
-        const int b = c & 1;
-        step(c, sbuf + b * kBuf, sE + b * kE, sE + (b ^ 1) * kE, sTr[w]);
+        if (w == 0 && c + 1 < nck) gates(c + 1, sE + ((c + 1) & 1) * kE);
         lds_barrier();
     }
     if (s_out) {
@@ -527,7 +596,7 @@ __global__ __launch_bounds__(64 * (NW + NP)) void gdn_scan_kernel(const int32_t 
 }
 
 constexpr int kGdnScanWaves = 2;      // compute waves of a scan work-group (32 value columns)
-constexpr int kGdnScanProducers = 2;  // waves that stream its tiles
+constexpr int kGdnScanProducers = 2;  // waves that stream its tiles (plus one store wave)
 
 hipError_t launch_gdn_prep(hipStream_t stream, int nseq, const int32_t *cu, int64_t n_tok, int max_len, int Hq, int Hv,
                            float scale, const bf16_t *q, const bf16_t *k, const float *g, const float *beta, bf16_t *ws)
@@ -548,7 +617,7 @@ hipError_t launch_gdn_scan(hipStream_t stream, int nseq, const int32_t *cu, int6
     constexpr int kSlices = kGdnDim / (16 * kGdnScanWaves);
     const int64_t nwg = static_cast<int64_t>(nseq) * Hv * kSlices;
     hipLaunchKernelGGL((gdn_scan_kernel<kGdnScanWaves, kGdnScanProducers>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(64 * (kGdnScanWaves + kGdnScanProducers)), 0,
+                       dim3(64 * (kGdnScanWaves + kGdnScanProducers + 1)), 0,
                        stream, cu, n_tok, max_len, nchunk_cap, nseq, Hq, Hv, scale, q, k, v, g, ws, s0, o, s_out);
     return hipGetLastError();
 }
