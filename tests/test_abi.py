@@ -84,3 +84,30 @@ def test_null_handle_and_status_strings():
 def test_no_cpu_fallback_in_binding():
     src = open(os.path.join(ROOT, "block_sparse_long_qsa_amd", "__init__.py")).read()
     assert "oracle" not in src and "import synth" not in src
+
+
+def test_gdn_workspace_size():
+    # Tb and P per (sequence, V head, chunk of 64) and K^T per (sequence, QK head, chunk): 16 KiB each.
+    assert Q.qsa_gdn_workspace_size(1, 64, 16, 48) == (48 + 16) * 16384
+    assert Q.qsa_gdn_workspace_size(2, 65, 16, 48) == 2 * 2 * (48 + 16) * 16384
+    assert Q.qsa_gdn_workspace_size(1, 0, 16, 48) == 0
+    assert Q.qsa_gdn_workspace_size(0, 64, 16, 48) == 0
+
+
+def _gdn_call(nseq=1, cu=16, n_tok=64, max_len=64, hq=2, hv=6, q=16, k=16, v=16, g=16, beta=16, o=16, ws=16,
+              ws_bytes=None):
+    lib = Q.lib()
+    if ws_bytes is None:
+        ws_bytes = lib.qsa_gdn_workspace_size(nseq, max_len, hq, hv)
+    # Pointer values are never dereferenced: every case fails a host check first.
+    return lib.qsa_gdn_chunk_prefill(None, nseq, cu, n_tok, max_len, hq, hv, 0.1, q, k, v, g, beta, None, o, None,
+                                     ws, ws_bytes)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), 1), (dict(q=None), 1), (dict(v=None), 1), (dict(o=None), 1), (dict(ws=None), 1),
+    (dict(nseq=0), 2), (dict(nseq=70000), 2), (dict(n_tok=-1), 2), (dict(max_len=-1), 2), (dict(hq=0), 2),
+    (dict(hv=5), 2), (dict(hv=1), 2), (dict(q=24), 4), (dict(k=8), 4), (dict(ws=8), 4), (dict(ws_bytes=100), 6),
+])
+def test_gdn_rejects_bad_arguments_on_the_host(kw, status):
+    assert _gdn_call(**kw) == status

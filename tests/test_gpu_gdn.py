@@ -112,3 +112,52 @@ def test_gdn_no_initial_state_and_no_final_state():
     ro, _ = oracle_seq(x, 0, 0.2)
     for h in range(2):
         check(_np(o[:, h]), ro[:, h], "head %d out" % h)
+
+
+def _bench_config_run(lens):
+    """The bench's launch configuration: qsa_gdn_prep then qsa_gdn_scan, 16 QK
+    heads, 48 V heads, no initial state."""
+    x = synth.gdn_inputs(21, lens, 16, 48, "cuda")
+    nseq, max_len = len(lens), max(lens)
+    o = torch.empty_like(x["v"])
+    fs = torch.empty(nseq, 48, 128, 128, device="cuda")
+    ws = torch.empty(Q.qsa_gdn_workspace_size(nseq, max_len, 16, 48), dtype=torch.uint8, device="cuda")
+    scale = 128 ** -0.5
+    Q.qsa_gdn_prep(nseq, x["cu_seqlens"], max_len, x["q"], x["k"], 48, x["g"], x["beta"], scale, ws)
+    Q.qsa_gdn_scan(nseq, x["cu_seqlens"], max_len, x["q"], x["k"], x["v"], x["g"], scale, None, o, fs, ws)
+    torch.cuda.synchronize()
+    del ws
+    return x, o, fs, scale
+
+
+def _oracle_one_head(x, s, hv, scale, upto=None):
+    a, b = int(x["cu_seqlens"][s]), int(x["cu_seqlens"][s + 1])
+    b = b if upto is None else a + upto
+    hq = hv // 3
+    sl = lambda t, h: _np(t[a:b, h:h + 1])
+    return OG.gdn_recurrent(sl(x["q"], hq), sl(x["k"], hq), sl(x["v"], hv), sl(x["g"], hv), sl(x["beta"], hv), scale)
+
+
+def test_gdn_full_size_262144_bench_config():
+    """One 262,144-token sequence: V head 47 (QK head 15) checked over every
+    token and its final state; V head 0 over the first 4,096 tokens."""
+    print("gdn full size: T=262144, hq=16, hv=48", flush=True)
+    x, o, fs, scale = _bench_config_run([262144])
+    ro, rs = _oracle_one_head(x, 0, 47, scale)
+    check(_np(o[:, 47]), ro[:, 0], "head 47 out")
+    check(_np(fs[0, 47]), rs[0], "head 47 state")
+    ro, _ = _oracle_one_head(x, 0, 0, scale, upto=4096)
+    check(_np(o[:4096, 0]), ro[:, 0], "head 0 out, first 4096 tokens")
+
+
+def test_gdn_full_size_8x32768_bench_config():
+    """Eight packed 32,768-token sequences: sequence 7, V head 23 over every
+    token and its final state; sequence 0, V head 5 over its first 4,096."""
+    print("gdn full size: 8 x 32768, hq=16, hv=48", flush=True)
+    x, o, fs, scale = _bench_config_run([32768] * 8)
+    ro, rs = _oracle_one_head(x, 7, 23, scale)
+    a = 7 * 32768
+    check(_np(o[a:a + 32768, 23]), ro[:, 0], "seq 7 head 23 out")
+    check(_np(fs[7, 23]), rs[0], "seq 7 head 23 state")
+    ro, _ = _oracle_one_head(x, 0, 5, scale, upto=4096)
+    check(_np(o[:4096, 5]), ro[:, 0], "seq 0 head 5 out, first 4096 tokens")
