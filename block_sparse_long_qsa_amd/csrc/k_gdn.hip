@@ -117,6 +117,10 @@ __device__ __forceinline__ void lds_wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (and nothing else).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 // Renumber work-group ids so that consecutive logical ids run on one XCD
 // (work-groups are dealt to the 8 XCDs round-robin).
 __device__ __forceinline__ int64_t xcd_local_id() {
@@ -272,14 +276,17 @@ __global__ __launch_bounds__(64) void gdn_prep_kernel(const int32_t *__restrict_
 //   X = V - diag(gamma_{t-1}) R_K;  U = Tb X              (8)
 //   O = diag(scale gamma_t) R_Q + P U                     (8)
 //   S = gamma_C S + K^T diag(exp(G_C - G_t)) U            (16)
-// All global traffic of the walk runs on two more kinds of wave, so that a
-// compute wave never waits on memory: NP producer waves copy each chunk's
-// tiles (K, Q, K^T, Tb, P, the V columns, and the gates one chunk earlier)
-// into a two-slot LDS ring with the LDS-DMA path (global_load_lds) one chunk
-// ahead, and one store wave writes each chunk's O from LDS to memory while the
-// next chunk computes.
-template <int NW, int NP>
-__global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
+// All global traffic of the walk runs on other waves, so a compute wave never
+// waits on memory: two producer waves copy each chunk's tiles into a two-slot
+// LDS ring with the LDS-DMA path (global_load_lds), and a store wave writes
+// each chunk's O from LDS while the next chunk computes.  Each chunk step has
+// two barriers: A after the products with K and Q, B at the end.  A slot's K, Q
+// part is refilled (two chunks ahead) as soon as barrier A releases it and its
+// other part (K^T, Tb, P, V) after barrier B, so every copy has more than one
+// step to land: K, Q of chunk c+1 must be in by barrier B of chunk c, the rest
+// by barrier A of chunk c+1.
+template <int NW>
+__global__ __launch_bounds__(64 * (NW + 3)) void gdn_scan_kernel(
     const int32_t *__restrict__ cu, int64_t n_tok, int max_len, int nchunk_cap, int nseq, int Hq, int Hv, float scale,
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
     const float *__restrict__ g, const bf16_t *__restrict__ ws, const float *s0, bf16_t *__restrict__ o, float *s_out)
@@ -289,7 +296,7 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
     // One ring slot: K, Q (sw128), K^T, Tb, P (sw64), V [64][kCols] bf16.
     constexpr int oQ = 16384, oKt = 32768, oTb = 49152, oP = 57344, oV = 65536;
     constexpr int kSlot = oV + kGdnChunk * kCols * 2;
-    constexpr int kMainPieces = kSlot / 1024;         // 1 KiB copies per chunk (16-byte lanes)
+    constexpr int kVPieces = (kSlot - oV) / 1024;
     constexpr int kE = 4 * kGdnChunk;                 // exp(G_{t-1}), scale exp(G_t), exp(G_C - G_t), exp(G_C)
     static_assert(kSlot % 1024 == 0, "ring slot must be whole 1 KiB pieces");
     __shared__ __align__(16) unsigned char sbuf[2 * kSlot];
@@ -297,7 +304,6 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
     __shared__ __align__(16) bf16_t sO[2][kGdnChunk * kCols];   // O staging, [token][kCols]
     __shared__ __align__(16) bf16_t sTr[NW][16 * kGdnPad];
     __shared__ __align__(16) float sE[2 * kE];
-    __shared__ __align__(16) unsigned char sdummy[256];        // target of the L2 touches
 
     const int64_t e = xcd_local_id();
     const int slice = static_cast<int>(e % kSlices);
@@ -315,101 +321,83 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
 
     auto chunk_nt = [&](int c) { return min(kGdnChunk, sp.len - c * kGdnChunk); };
 
-    // ---- producer waves: pieces p = pw, pw + NP, ... of the kMainPieces of a
-    // chunk (rows past the end repeat the last token; see gdn_prep_kernel for
-    // why that is harmless), and the gates of the chunk after it.
-    if (w >= NW + 1) {
+    // ---- producer waves.  Group KQ of chunk c: producer 0 copies K, producer 1
+    // copies Q and the gates (into sg[c % 3]); group TPKV: producer 0 copies Tb,
+    // P and the V columns, producer 1 copies K^T.  Rows past the end of the
+    // sequence repeat its last token (see gdn_prep_kernel for why that is
+    // harmless).  Issue order per producer: ..., KQ(c+1) [after A(c-1)],
+    // TPKV(c+1) [after B(c-1)], KQ(c+2) [after A(c)], ...; so before A(c)
+    // (TPKV(c) landed) and before B(c) (KQ(c+1) landed) the wave may leave the
+    // two younger groups in flight.
+    if (w > NW) {
         const int pw = w - NW - 1;
-        // Producer 0 copies K, K^T and V; producer 1 copies Q, Tb and P.
-        // Every loop is unrolled so that a copy costs a few address operations.
-        static_assert(NP == 2, "the copy split below is written for two producers");
-        const int lrow = lane >> 4, lcp = lane & 15;
-        const int rowbytes = kstride * 2;
-        auto copy_main = [&](int c, unsigned char *dst) {
+        const int lrow = lane >> 4, lcp = lane & 15, rowbytes = kstride * 2;
+        auto slot = [&](int c) { return sbuf + (c & 1) * kSlot; };
+        auto copy_kq = [&](int c) {
+            unsigned char *dst = slot(c);
             const int last = chunk_nt(c) - 1;
             const int64_t tok0 = sp.base + c * kGdnChunk;
             const unsigned char *rows = reinterpret_cast<const unsigned char *>((pw == 0 ? k : q) + (tok0 * Hq + hq) * kGdnDim);
             unsigned char *drows = dst + (pw == 0 ? 0 : oQ);
 #pragma unroll
-            for (int n = 0; n < 16; ++n) {         // K or Q: rows 4n .. 4n+3, swizzled 16-byte chunks
+            for (int n = 0; n < 16; ++n) {         // rows 4n .. 4n+3, swizzled 16-byte chunks
                 const int row = 4 * n + lrow;
                 const int src = min(row, last) * rowbytes + 16 * (lcp ^ ((4 * (n & 3)) + lrow));
                 __builtin_amdgcn_global_load_lds(rows + src, drows + 1024 * n, 16, 0, 0);
             }
+            if (pw == 1)
+                __builtin_amdgcn_global_load_lds(g + (tok0 + min(lane, last)) * Hv + hv, static_cast<void *>(sg[c % 3]), 4, 0, 0);
+        };
+        auto copy_tpkv = [&](int c) {
+            unsigned char *dst = slot(c);
+            const int last = chunk_nt(c) - 1;
+            const int64_t tok0 = sp.base + c * kGdnChunk;
             const unsigned char *flat = reinterpret_cast<const unsigned char *>(
-                pw == 0 ? ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c) : ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c));
-            unsigned char *dflat = dst + (pw == 0 ? oKt : oTb);
+                pw == 0 ? ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c) : ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c));
+            unsigned char *dflat = dst + (pw == 0 ? oTb : oKt);
 #pragma unroll
-            for (int n = 0; n < 16; ++n)           // K^T, or Tb then P: contiguous 16 KiB
+            for (int n = 0; n < 16; ++n)           // Tb then P, or K^T: contiguous 16 KiB
                 __builtin_amdgcn_global_load_lds(flat + 1024 * n + 16 * lane, dflat + 1024 * n, 16, 0, 0);
             if (pw == 0) {
                 constexpr int kChunksPerRow = kCols / 8;
                 constexpr int kRowsPerPiece = 64 / kChunksPerRow;
                 const unsigned char *vr = reinterpret_cast<const unsigned char *>(v + (tok0 * Hv + hv) * kGdnDim + col0);
 #pragma unroll
-                for (int n = 0; n < (kSlot - oV) / 1024; ++n) {   // V: kRowsPerPiece tokens per 1 KiB
+                for (int n = 0; n < kVPieces; ++n) {
                     const int row = n * kRowsPerPiece + lane / kChunksPerRow;
                     const int64_t src = static_cast<int64_t>(min(row, last)) * vstride * 2 + 16 * (lane % kChunksPerRow);
                     __builtin_amdgcn_global_load_lds(vr + src, dst + oV + 1024 * n, 16, 0, 0);
                 }
             }
         };
-        // Pull chunk c's lines into L2 one chunk before its copy: 4-byte
-        // LDS-DMA loads, one 128-byte line per lane, into a scratch area
-        // nothing reads (the only load form that needs no destination register).
-        auto touch = [&](int c) {
-            const int last = chunk_nt(c) - 1;
-            const int64_t tok0 = sp.base + c * kGdnChunk;
-            const unsigned char *kt = reinterpret_cast<const unsigned char *>(ws + gdn_kt_off(nseq, s, hq, Hq, Hv, nchunk_cap, c));
-            const unsigned char *tpw = reinterpret_cast<const unsigned char *>(ws + gdn_ws_off(s, hv, Hv, nchunk_cap, c));
-            const unsigned char *kr = reinterpret_cast<const unsigned char *>(k + (tok0 * Hq + hq) * kGdnDim);
-            const unsigned char *qr = reinterpret_cast<const unsigned char *>(q + (tok0 * Hq + hq) * kGdnDim);
-            const int row = min(lane >> 1, last), half = 128 * (lane & 1);
-            const int64_t kq = static_cast<int64_t>(row) * kstride * 2 + half;                 // rows 0..31
-            const int64_t kq2 = static_cast<int64_t>(min(32 + (lane >> 1), last)) * kstride * 2 + half;
-            __builtin_amdgcn_global_load_lds(kr + kq, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(kr + kq2, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(qr + kq, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(qr + kq2, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(kt + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(kt + 8192 + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(tpw + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(tpw + 8192 + 128 * lane, static_cast<void *>(sdummy), 4, 0, 0);
-            __builtin_amdgcn_global_load_lds(v + ((tok0 + min(lane, last)) * Hv + hv) * kGdnDim + col0, static_cast<void *>(sdummy), 4, 0, 0);
-        };
-        // Gates go through a register: loaded at the top of the iteration
-        // (always, from a valid chunk) and written to the ring after the wait.
-        auto load_gates = [&](int c) {
-            c = min(c, nck - 1);
-            const int last = chunk_nt(c) - 1;
-            return g[(sp.base + c * kGdnChunk + min(lane, last)) * Hv + hv];
-        };
-        constexpr int kWaitLds = 0xF | (3 << 14) | (7 << 4);   // lgkmcnt(0) only
-        if (nck > 0) {
-            const float g0 = load_gates(0), g1 = load_gates(1);
-            copy_main(0, sbuf);
-            __builtin_amdgcn_s_waitcnt(0);
+        // vmcnt immediates: n_KQ + n_TPKV, n_KQ, n_TPKV (per producer), and 0.
+        auto wait_groups = [&](bool kq, bool tpkv) {
             if (pw == 0) {
-                sg[0][lane] = g0;
-                sg[1][lane] = g1;
-                if (nck > 1) touch(1);
+                if (kq && tpkv) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16 + 16 + kVPieces));
+                else if (kq) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+                else if (tpkv) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16 + kVPieces));
+                else __builtin_amdgcn_s_waitcnt(0);
+            } else {
+                if (kq && tpkv) __builtin_amdgcn_s_waitcnt(vmcnt_imm(17 + 16));
+                else if (kq) __builtin_amdgcn_s_waitcnt(vmcnt_imm(17));
+                else if (tpkv) __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+                else __builtin_amdgcn_s_waitcnt(0);
             }
+        };
+        if (nck > 0) {
+            copy_kq(0);
+            copy_tpkv(0);
         }
-        __builtin_amdgcn_s_waitcnt(kWaitLds);
-        raw_barrier();
-        raw_barrier();
+        if (nck > 1) copy_kq(1);
+        wait_groups(nck > 1, false);                  // chunk 0 whole
+        raw_barrier();                                // B(-1)
         for (int c = 0; c < nck; ++c) {
-            // Chunk c+1 is copied now and must land before barrier c+1; its
-            // lines were touched one iteration ago.  Chunk c+2 is touched now.
-            const float gn = load_gates(c + 2);
-            if (c + 1 < nck) copy_main(c + 1, sbuf + ((c + 1) & 1) * kSlot);
-            __builtin_amdgcn_s_waitcnt(0);
-            if (pw == 0 && c + 2 < nck) {
-                sg[(c + 2) % 3][lane] = gn;
-                touch(c + 2);
-            }
-            __builtin_amdgcn_s_waitcnt(kWaitLds);
-            raw_barrier();
+            if (c + 1 < nck) copy_tpkv(c + 1);
+            wait_groups(c + 1 < nck, c + 1 < nck);    // TPKV(c)
+            raw_barrier();                            // A(c)
+            if (c + 2 < nck) copy_kq(c + 2);
+            wait_groups(c + 2 < nck, c + 1 < nck);    // KQ(c+1)
+            raw_barrier();                            // B(c)
         }
         __builtin_amdgcn_s_waitcnt(0);
         return;
@@ -429,11 +417,11 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
                     *reinterpret_cast<u32x4 *>(o + ((sp.base + c * kGdnChunk + t) * Hv + hv) * kGdnDim + col0 + 8 * cc) = val;
             }
         };
-        lds_barrier();
-        lds_barrier();
+        lds_barrier();                                // B(-1)
         for (int c = 0; c < nck; ++c) {
             if (c > 0) store(c - 1);
-            lds_barrier();
+            lds_barrier();                            // A(c)
+            lds_barrier();                            // B(c)
         }
         if (nck > 0) store(nck - 1);
         return;
@@ -464,14 +452,13 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
     };
     bf16_t *tr = sTr[w];
 
-    lds_barrier();                                    // chunk 0 and the gates of chunks 0, 1 have landed
-    if (w == 0 && nck > 0) gates(0, sE);
-    lds_barrier();
+    lds_barrier();                                    // B(-1): chunk 0 and the gates of chunk 0 have landed
     for (int c = 0; c < nck; ++c) {
         const unsigned char *cur = sbuf + (c & 1) * kSlot;
         const unsigned char *bK = cur, *bQ = cur + oQ, *bKt = cur + oKt, *bTb = cur + oTb, *bP = cur + oP;
         const bf16_t *bV = reinterpret_cast<const bf16_t *>(cur + oV);
-        const float *ec = sE + (c & 1) * kE;
+        float *ec = sE + (c & 1) * kE;
+        if (w == 0) gates(c, ec);                     // read by every compute wave after barrier A
 
         // S -> bf16 B operand (k = rows of S).
 #pragma unroll
@@ -500,6 +487,7 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
                 rq[i] = mfma32(aq[i][s4], bs[s4], rq[i]);
             }
         }
+        lds_barrier();                                // A(c): K and Q of this slot are free
         bf16x8 atb[4][2], ap[4][2];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -520,7 +508,6 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
         }
         const float gC = ec[3 * kGdnChunk];
         // X = V - diag(gamma_{t-1}) K S, rows = tokens.
-        lds_wave_sync();
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float xv[4];
@@ -584,8 +571,7 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) S[i] = mfma32(akt[i][s2], bw[s2], S[i]);
         }
-        if (w == 0 && c + 1 < nck) gates(c + 1, sE + ((c + 1) & 1) * kE);
-        lds_barrier();
+        lds_barrier();                                // B(c)
     }
     if (s_out) {
 #pragma unroll
@@ -596,7 +582,6 @@ __global__ __launch_bounds__(64 * (NW + NP + 1)) void gdn_scan_kernel(
 }
 
 constexpr int kGdnScanWaves = 2;      // compute waves of a scan work-group (32 value columns)
-constexpr int kGdnScanProducers = 2;  // waves that stream its tiles (plus one store wave)
 
 hipError_t launch_gdn_prep(hipStream_t stream, int nseq, const int32_t *cu, int64_t n_tok, int max_len, int Hq, int Hv,
                            float scale, const bf16_t *q, const bf16_t *k, const float *g, const float *beta, bf16_t *ws)
@@ -616,8 +601,8 @@ hipError_t launch_gdn_scan(hipStream_t stream, int nseq, const int32_t *cu, int6
     const int nchunk_cap = (max_len + kGdnChunk - 1) / kGdnChunk;
     constexpr int kSlices = kGdnDim / (16 * kGdnScanWaves);
     const int64_t nwg = static_cast<int64_t>(nseq) * Hv * kSlices;
-    hipLaunchKernelGGL((gdn_scan_kernel<kGdnScanWaves, kGdnScanProducers>), dim3(static_cast<unsigned>(nwg)),
-                       dim3(64 * (kGdnScanWaves + kGdnScanProducers + 1)), 0,
+    hipLaunchKernelGGL((gdn_scan_kernel<kGdnScanWaves>), dim3(static_cast<unsigned>(nwg)),
+                       dim3(64 * (kGdnScanWaves + 3)), 0,
                        stream, cu, n_tok, max_len, nchunk_cap, nseq, Hq, Hv, scale, q, k, v, g, ws, s0, o, s_out);
     return hipGetLastError();
 }
