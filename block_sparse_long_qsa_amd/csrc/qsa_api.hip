@@ -674,6 +674,8 @@ qsa_status gdn_check(int32_t nseq, const int32_t *cu, int64_t n_tokens, int64_t 
     if (nseq < 1 || nseq > 65535 || n_tokens < 0 || max_len < 0 || max_len > (int64_t(1) << 30) || hq < 1 ||
         hq > 65535 || hv < hq || hv % hq != 0)
         return QSA_ERR_SHAPE;
+    // Launch grids: nseq * chunks * hv one-wave work-groups (prep), nseq * hv * 4 (scan).
+    if (static_cast<int64_t>(nseq) * ((max_len + 63) / 64) * hv > int64_t(0xFFFFFFFF)) return QSA_ERR_SHAPE;
     if (!aligned16(q) || !aligned16(k)) return QSA_ERR_ALIGN;
     const size_t need = qsa_gdn_workspace_size(nseq, max_len, hq, hv);
     if (need > 0) {

@@ -361,7 +361,8 @@ qsa_status qsa_train_backward_attention(const qsa_handle *h, void *stream, int32
  * max_len, hq_heads, hv_heads) bytes.  Errors: QSA_ERR_NULL (q, k, v, g, beta, o,
  * cu_seqlens or a needed ws missing), QSA_ERR_SHAPE (nseq outside 1..65535,
  * n_tokens or max_len negative or max_len above 2^30, hq_heads outside 1..65535,
- * hv_heads not a positive multiple of hq_heads), QSA_ERR_ALIGN (q, k or ws not
+ * hv_heads not a positive multiple of hq_heads, or nseq * ceil(max_len / 64) *
+ * hv_heads above 2^32 - 1), QSA_ERR_ALIGN (q, k or ws not
  * 16-byte aligned), QSA_ERR_WORKSPACE, QSA_ERR_HIP. */
 size_t qsa_gdn_workspace_size(int32_t nseq, int64_t max_len, int32_t hq_heads, int32_t hv_heads);
 qsa_status qsa_gdn_chunk_prefill(void *stream, int32_t nseq, const int32_t *cu_seqlens, int64_t n_tokens,
