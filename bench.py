@@ -39,9 +39,9 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # the factors are what the counters read for a plain 1 GiB copy).  The counter
 # summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
 # is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (430678081.2 * 2.000 + 3145785.7 * 1.000) * 1024
+ATTEND_TRAFFIC_BYTES = (401085059.4 * 2.000 + 3145801.6 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "ba8f510fe9fa6d6af1f5a83b4871a8ae784d40754716a5467cd2cf86011b2008",
+    "k_attend.hip": "8d374596186407406bee377f4fa124ada4c8010f4fc53a242e2b4d0785848f98",
     "attend_parts.h": "43d7620572fc9e261b309bcd780d656d88ee040a82ea87fbd0eaeb196cd3961b",
     "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }
@@ -55,6 +55,10 @@ def attend_traffic_bytes():
             if hashlib.sha256(f.read()).hexdigest() != digest:
                 return None
     return ATTEND_TRAFFIC_BYTES
+
+
+def _progress(msg):
+    print(msg, file=sys.stderr, flush=True)
 
 
 def _events(n):
@@ -252,6 +256,7 @@ def run_c5(steps):
     wp, wd = synth.WORKLOADS["prefill_1m"], synth.WORKLOADS["decode_1m"]
     L = wp.seq_len
     t_pre = qsa_prefill_1m_ms(steps)
+    _progress("c5 prefill done")
     ev = _events(2)
     sd = setup_decode(wd)
     for _ in range(3):
@@ -414,10 +419,12 @@ def run_ratios(steps):
     del sp
     torch.cuda.empty_cache()
     t_dense = dense_prefill_ms(wp.seq_len, reps=2)
+    _progress("ratios: prefill 262144 done")
     res["prefill_262144"] = {"qsa_ms": t_qsa, "dense_sdpa_ms": t_dense, "speedup": t_dense / t_qsa}
     wp_1m = synth.WORKLOADS["prefill_1m"]
     t_qsa_1m = qsa_prefill_1m_ms(1)
     t_dense_1m = dense_prefill_ms(1 << 20, reps=1)
+    _progress("ratios: prefill 1048576 done")
     res["prefill_1048576"] = {"qsa_ms": t_qsa_1m, "dense_sdpa_ms": t_dense_1m, "speedup": t_dense_1m / t_qsa_1m,
                               "dense_sdpa_tflops": 4 * 24 * 256 * (1 << 20) ** 2 / 2 / (t_dense_1m * 1e-3) / 1e12}
     wd = synth.WORKLOADS["decode_1m"]
@@ -451,6 +458,7 @@ def run_ratios(steps):
     idx = {}
     for key, w in (("prefill_262144", synth.WORKLOADS["prefill_256k"]), ("prefill_1048576", wp_1m)):
         t = indexer_ratio_prefill(w, steps)
+        _progress("ratios: indexer " + key + " done")
         idx[key] = {"r4_ms": t["r4"], "r1_ms": t["r1"], "speedup": t["r1"] / t["r4"]}
     t = indexer_ratio_decode(wd, steps)
     idx["decode_B8_ctx1048576"] = {"r4_ms": t["r4"], "r1_ms": t["r1"], "speedup": t["r1"] / t["r4"]}

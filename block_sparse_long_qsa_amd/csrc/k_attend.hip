@@ -117,7 +117,19 @@ __device__ __forceinline__ void init_state(RowState &st) {
     for (int n = 0; n < 16; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Prefill: 4 waves per workgroup = 2 queries x 2 KV groups.
+// Prefill work-group order: all queries of KV group 0, then all of group 1,
+// four consecutive queries per work-group.  The work-groups resident at any
+// time then gather from one group's cache (half of the K~/V bytes), which
+// the device's last-level cache holds far better than both groups' caches.
+__device__ __forceinline__ void prefill_slot(int64_t L, int wave, int64_t &i, int &grp)
+{
+    const int64_t nt = (L + 3) / 4;
+    const int64_t x = blockIdx.x;
+    grp = x >= nt ? 1 : 0;
+    i = (x - grp * nt) * 4 + wave;
+}
+
+// Prefill: 4 waves per workgroup = 4 queries of one KV group.
 __global__ __launch_bounds__(256) void attend_prefill_kernel(
     Tables tab, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
@@ -126,8 +138,9 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 2 + (wave >> 1);
-    const int grp = wave & 1;
+    int64_t i;
+    int grp;
+    prefill_slot(L, wave, i, grp);
     if (i >= L) return;
     const int64_t pos = q_offset + i;
     const int64_t o = pos / kBlock;
@@ -171,8 +184,9 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
-    const int64_t i = static_cast<int64_t>(blockIdx.x) * 2 + (wave >> 1);
-    const int grp = wave & 1;
+    int64_t i;
+    int grp;
+    prefill_slot(L, wave, i, grp);
     if (i >= L) return;
     const int64_t pos = i;
     const int64_t o = pos / kBlock;
@@ -303,7 +317,7 @@ hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, i
                                  const bf16_t *v_cache, const int32_t *block_idx, bf16_t *out)
 {
     if (L <= 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>((L + 1) / 2), static_cast<unsigned>(B));
+    dim3 grid(static_cast<unsigned>(2 * ((L + 3) / 4)), static_cast<unsigned>(B));
     hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, L, q_offset, nblk_cap, budget,
                        sigma * kLog2e, q, k_cache, v_cache, block_idx, out);
     return hipGetLastError();
@@ -314,7 +328,7 @@ hipError_t launch_attend_stats(const Tables &tab, hipStream_t st, int32_t B, int
                                const int32_t *block_idx, bf16_t *out, float *stats)
 {
     if (L <= 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>((L + 1) / 2), static_cast<unsigned>(B));
+    dim3 grid(static_cast<unsigned>(2 * ((L + 3) / 4)), static_cast<unsigned>(B));
     hipLaunchKernelGGL(attend_stats_kernel, grid, dim3(256), 0, st, tab, L, nblk_cap, budget, sigma * kLog2e, q,
                        k_cache, v_cache, block_idx, out, stats);
     return hipGetLastError();

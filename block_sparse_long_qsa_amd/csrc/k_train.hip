@@ -275,8 +275,8 @@ __global__ __launch_bounds__(64) void attend_backward_kernel(
     __shared__ __attribute__((aligned(16))) bf16_t sH[16][32];
     __shared__ __attribute__((aligned(16))) bf16_t kt[32][kHeadDim];
     const int lane = threadIdx.x;
-    const int grp = blockIdx.x;
-    const int64_t i = blockIdx.y;
+    const int64_t i = blockIdx.x;
+    const int grp = blockIdx.y;      // group-major: each group's queries run together
     const int64_t b = blockIdx.z;
     const int64_t row = b * L + i;
     const int64_t pos = i;
@@ -442,7 +442,7 @@ hipError_t launch_attend_backward(const Tables &tab, hipStream_t st, int32_t B, 
                                   float *dq, float *dk, float *dv)
 {
     if (L <= 0) return hipSuccess;
-    hipLaunchKernelGGL(attend_backward_kernel, dim3(kKVHeads, static_cast<unsigned>(L), static_cast<unsigned>(B)),
+    hipLaunchKernelGGL(attend_backward_kernel, dim3(static_cast<unsigned>(L), kKVHeads, static_cast<unsigned>(B)),
                        dim3(64), 0, st, tab, L, nblk_cap, budget, sigma * kLog2e, sigma, q, k_cache, v_cache, block_idx,
                        out, dout, stats, dq, dk, dv);
     hipError_t e = hipGetLastError();
