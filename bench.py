@@ -482,8 +482,7 @@ def run_train(steps):
     differentiated) + qsa_train_forward (sparse attention with log-sum-exp, then
     the indexer KL loss); backward = qsa_train_backward_indexer (gradients to the
     raw indexer queries and keys) + qsa_train_backward_attention (gradients to
-    q, k, v; 32,768 tokens only: its fp32 atomics grow with the attended
-    tokens).  HIP events between the stages; one JSON line."""
+    q, k, v).  HIP events between the stages; one JSON line."""
     res = {}
     for key in ("prefill_32k", "prefill_256k"):
         w = synth.WORKLOADS[key]
@@ -498,13 +497,12 @@ def run_train(steps):
         dkl = torch.full((1, L), 1.0 / L, dtype=torch.float32, device="cuda")
         dq = torch.empty((1, L, 4, 128), dtype=torch.float32, device="cuda")
         dk = torch.empty((1, L, 128), dtype=torch.float32, device="cuda")
-        attn_bwd = L <= 32768          # its fp32 atomics make it slow on longer sequences
         g = torch.Generator(device="cuda")
         g.manual_seed(11)
-        dout = torch.randn((1, L, 24, 256), device="cuda", generator=g).to(torch.bfloat16) if attn_bwd else None
-        dqa = torch.empty((1, L, 24, 256), dtype=torch.float32, device="cuda") if attn_bwd else None
-        dka = torch.empty((1, L, 2, 256), dtype=torch.float32, device="cuda") if attn_bwd else None
-        dva = torch.empty((1, L, 2, 256), dtype=torch.float32, device="cuda") if attn_bwd else None
+        dout = torch.randn((1, L, 24, 256), device="cuda", generator=g).to(torch.bfloat16)
+        dqa = torch.empty((1, L, 24, 256), dtype=torch.float32, device="cuda")
+        dka = torch.empty((1, L, 2, 256), dtype=torch.float32, device="cuda")
+        dva = torch.empty((1, L, 2, 256), dtype=torch.float32, device="cuda")
         ws_is = Q.workspace(h, Q.QSA_OP_INDEX_SELECT, 1, L, 0)
         ws_f = Q.workspace(h, Q.QSA_OP_TRAIN_FORWARD, 1, L, 0)
         ws_b = Q.workspace(h, Q.QSA_OP_TRAIN_BACKWARD, 1, L, 0)
@@ -521,9 +519,8 @@ def run_train(steps):
             Q.qsa_train_backward_indexer(h, 1, L, x["q"], x["q_idx"], c["k_cache"], c["kbar_cache"], bidx, stats, dkl,
                                          dq, dk, ws_b)
             ev[3].record()
-            if attn_bwd:
-                Q.qsa_train_backward_attention(h, 1, L, x["q"], c["k_cache"], c["v_cache"], bidx, out, dout, stats,
-                                               dqa, dka, dva)
+            Q.qsa_train_backward_attention(h, 1, L, x["q"], c["k_cache"], c["v_cache"], bidx, out, dout, stats,
+                                           dqa, dka, dva)
             ev[4].record()
 
         step(_events(5))
@@ -535,9 +532,10 @@ def run_train(steps):
         sel_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         fwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
         bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-        att_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs])) if attn_bwd else None
-        tot = sel_ms + fwd_ms + bwd_ms + (att_ms or 0.0)
-        res[w.name] = {"ms": tot, "tok_s": L / (tot * 1e-3), "attention_backward": attn_bwd,
+        att_ms = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+        tot = sel_ms + fwd_ms + bwd_ms + att_ms
+        _progress("train: " + w.name + " done")
+        res[w.name] = {"ms": tot, "tok_s": L / (tot * 1e-3),
                        "stage_ms": {"append_index_select": sel_ms, "train_forward": fwd_ms, "backward_indexer": bwd_ms,
                                     "backward_attention": att_ms},
                        "mean_kl": float(kl.mean()), "indexer_loss_bytes_per_pass": train_bytes(L, budget)}

@@ -232,3 +232,86 @@ def test_train_fullsize_32k_sampled_rows():
     for name, got, ref in (("dq", dq_np[rows], aq), ("dk", dk_np, fk), ("dv", dv_np, fv)):
         assert np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref), name
         assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max(), name
+
+
+def test_train_attention_backward_262k_bench_config():
+    """The attention backward on the 262,144-token workload at budget 512 (the
+    size bench.py --train times).  Call 1: only sampled rows carry an upstream
+    gradient, so the oracle gives those rows' dq and every token's dk, dv.
+    Call 2: every row carries a random dout; checked on every token through
+    two identities of the softmax backward that hold at any size: the
+    probabilities of a (row, head) sum to one, so summed over tokens dv of a
+    KV group equals the sum of dout over rows and the group's heads; and the
+    dS of a (row, head) sum to zero (sum_t P_t (dP_t - D) with
+    D = <dout, out>), so dk summed over tokens vanishes on the dims RoPE
+    leaves alone (64..255), up to the bf16 rounding of out (about 2e-3 of the
+    norm of dk there)."""
+    w = synth.WORKLOADS["prefill_256k"]
+    L, budget = w.seq_len, w.budget
+    x = synth.prefill_inputs(w, DEV)
+    p = O.Params(budget=budget)
+    rows = [5, 4099, 65537, 131070, 196611, 262143]
+    sel = np.full((L, budget), -1, dtype=np.int32)
+    o = np.arange(L) // 4
+    n = np.minimum(o, budget)
+    col = np.arange(budget)[None, :]
+    np.copyto(sel, (o - n)[:, None] + col, where=col < n[:, None])
+    kbar = O.indexer_keys(bits(x["k_idx"][0]), p)
+    for i in rows:
+        qt = O.indexer_queries(bits(x["q_idx"][0, i:i + 1]), np.array([i]), p)[0]
+        sel[i] = O.select_blocks(O.block_scores(qt, kbar[:i // 4]), budget)
+    del kbar
+    h = Q.Handle(max_ctx=L, budget_blocks=budget)
+    c = Q.alloc_caches(h, 1)
+    Q.qsa_append(h, 1, L, 0, x["k"], x["v"], x["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    bidx = torch.from_numpy(sel[None]).to(DEV)
+    out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    stats = torch.empty((1, L, 32), dtype=torch.float32, device=DEV)
+    kl = torch.empty((1, L), dtype=torch.float32, device=DEV)
+    Q.qsa_train_forward(h, 1, L, x["q"], x["q_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], bidx, out, stats,
+                        kl, Q.workspace(h, Q.QSA_OP_TRAIN_FORWARD, 1, L, 0))
+    dq = torch.empty((1, L, 24, 256), dtype=torch.float32, device=DEV)
+    dk = torch.empty((1, L, 2, 256), dtype=torch.float32, device=DEV)
+    dv = torch.empty((1, L, 2, 256), dtype=torch.float32, device=DEV)
+
+    # call 1: sampled rows
+    g = np.random.default_rng(76)
+    d_rows = torch.from_numpy(g.standard_normal((len(rows), 24, 256)).astype(np.float32)).to(torch.bfloat16)
+    dout = torch.zeros((1, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    dout[0, rows] = d_rows.to(DEV)
+    Q.qsa_train_backward_attention(h, 1, L, x["q"], c["k_cache"], c["v_cache"], bidx, out, dout, stats, dq, dk, dv)
+    torch.cuda.synchronize()
+    print("262k backward, sampled rows: launched", flush=True)
+    q_rows = bits(x["q"][0, rows])
+    k_all, v_all = bits(x["k"][0]), bits(x["v"][0])
+    full_q = np.zeros((L, 24, 256), dtype=np.uint16)
+    full_q[rows] = q_rows
+    aq, toks, ak, av = T.attention_grads_rows(full_q, k_all, v_all, sel, d_rows.float().numpy().astype(np.float64),
+                                              rows, p)
+    del full_q
+    dq_rows = dq[0, rows].cpu().numpy()
+    dk_np, dv_np = dk[0].cpu().numpy(), dv[0].cpu().numpy()
+    assert int(torch.count_nonzero(dq[0])) == int(torch.count_nonzero(dq[0, rows]))   # other rows: exact zeros
+    fk, fv = np.zeros_like(dk_np), np.zeros_like(dv_np)
+    fk[toks], fv[toks] = ak, av
+    for name, got, ref in (("dq", dq_rows, aq), ("dk", dk_np, fk), ("dv", dv_np, fv)):
+        assert np.linalg.norm(got - ref) <= 1e-2 * np.linalg.norm(ref), name
+        assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max(), name
+    del dk_np, dv_np, fk, fv
+
+    # call 2: every row, identities on every token
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(77)
+    dout = torch.randn((1, L, 24, 256), device=DEV, generator=gen).to(torch.bfloat16)
+    Q.qsa_train_backward_attention(h, 1, L, x["q"], c["k_cache"], c["v_cache"], bidx, out, dout, stats, dq, dk, dv)
+    torch.cuda.synchronize()
+    print("262k backward, every row: launched", flush=True)
+    for grp in range(2):
+        ref = dout[0, :, 12 * grp:12 * (grp + 1)].double().sum(dim=(0, 1)).cpu().numpy()
+        got = dv[0, :, grp].double().sum(dim=0).cpu().numpy()
+        assert np.linalg.norm(got - ref) <= 1e-3 * np.linalg.norm(ref), ("dv sum", grp)
+        ksum = dk[0, :, grp, 64:].double().sum(dim=0).cpu().numpy()
+        knorm = float(dk[0, :, grp, 64:].double().norm())
+        assert knorm > 0 and np.linalg.norm(ksum) <= 2e-2 * knorm, ("dk sum", grp, np.linalg.norm(ksum), knorm)
+        print("group %d: |sum dv - sum dout| / |sum dout| = %.3g, |sum dk[64:]| / |dk[64:]| = %.3g"
+              % (grp, np.linalg.norm(got - ref) / np.linalg.norm(ref), np.linalg.norm(ksum) / knorm), flush=True)
