@@ -39,10 +39,10 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # the factors are what the counters read for a plain 1 GiB copy).  The counter
 # summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
 # is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (401085059.4 * 2.000 + 3145801.6 * 1.000) * 1024
+ATTEND_TRAFFIC_BYTES = (399616845.9 * 2.000 + 3145803.7 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "8d374596186407406bee377f4fa124ada4c8010f4fc53a242e2b4d0785848f98",
-    "attend_parts.h": "43d7620572fc9e261b309bcd780d656d88ee040a82ea87fbd0eaeb196cd3961b",
+    "k_attend.hip": "7bd2bbde49f8700e33526e128a99a5c826151ee872f751a2fde2b415ee74f486",
+    "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }
 

@@ -71,12 +71,13 @@ __device__ __forceinline__ void entry_from_id(int64_t id, int n_sel, int64_t o0,
 }
 
 // The selection value entry li reads (clamped into the list; ignored past it).
-__device__ __forceinline__ int32_t entry_id(const int32_t *sel, int n_sel, int li) {
-    return sel[li < n_sel ? li : 0];
+// sel holds the entries from sel_off on (sel_off <= li for every li read).
+__device__ __forceinline__ int32_t entry_id(const int32_t *sel, int n_sel, int li, int sel_off) {
+    return sel[(li < n_sel ? li : sel_off) - sel_off];
 }
 
 template <bool kBranchFree = false>
-__device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_t o0, int64_t o, int li,
+__device__ __forceinline__ void list_entry(const int32_t *sel, int sel_off, int n_sel, int64_t o0, int64_t o, int li,
                                            int own_last, int64_t &blk, uint32_t &tmask)
 {
     if constexpr (kBranchFree) {
@@ -84,9 +85,9 @@ __device__ __forceinline__ void list_entry(const int32_t *sel, int n_sel, int64_
         // branches: a chunk's entries are loaded together instead of one wait
         // each.  The prefill walk gains about 1%; the decode split kernel
         // measured slower with it.
-        entry_from_id(entry_id(sel, n_sel, li), n_sel, o0, o, li, own_last, blk, tmask);
+        entry_from_id(entry_id(sel, n_sel, li, sel_off), n_sel, o0, o, li, own_last, blk, tmask);
     } else if (li < n_sel) {
-        const int64_t id = sel[li];
+        const int64_t id = sel[li - sel_off];
         const bool ok = id >= 0 && id < o0;
         blk = ok ? id : 0;
         tmask = ok ? 0xFu : 0u;

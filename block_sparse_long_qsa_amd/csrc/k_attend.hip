@@ -32,12 +32,13 @@ struct RowState {
     f32x4 o[16];    // O^T: dims 16n + 4*(l/16) + j of head l%16
 };
 
-// Walk chunks [c_lo, c_hi) of one (query, group) token list.
+// Walk chunks [c_lo, c_hi) of one (query, group) token list; sel holds the
+// selection from entry sel_off on.
 template <bool kBranchFree>
 __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
                                               const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
-                                              int n_sel, int64_t o0, int64_t o, int own_last, int c_lo, int c_hi,
-                                              float c2, RowState &st)
+                                              int sel_off, int n_sel, int64_t o0, int64_t o, int own_last, int c_lo,
+                                              int c_hi, float c2, RowState &st)
 {
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;           // K-load token row / V-load dim
@@ -47,7 +48,7 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         // ---- gather K~ (A operand of S^T): tile t, token row r -> list entry lb + 4t + r/4
         int64_t kblk[2];
         uint32_t kmask[2];
-        for (int t = 0; t < 2; ++t) list_entry<kBranchFree>(sel, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry<kBranchFree>(sel, sel_off, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, kblk[t], kmask[t]);
         bf16x8 kf[2][8];
         for (int t = 0; t < 2; ++t) {
             const bf16_t *src = kc + kblk[t] * kBlockElems + (r & 3) * 32 + 8 * g;
@@ -56,7 +57,7 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         // ---- gather V (A operand of O^T): list entries lb + g and lb + 4 + g, dim 16n + r
         int64_t vblk[2];
         uint32_t vmask[2];
-        for (int t = 0; t < 2; ++t) list_entry<kBranchFree>(sel, n_sel, o0, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry<kBranchFree>(sel, sel_off, n_sel, o0, o, lb + 4 * t + g, own_last, vblk[t], vmask[t]);
         u32x2 vraw[16][2];
         for (int t = 0; t < 2; ++t) {
             const bf16_t *src = vc + vblk[t] * kBlockElems + r * kBlock;
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
 
     RowState st;
     init_state(st);
-    attend_chunks<true>(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
+    attend_chunks<true>(qf, kc, vc, sel, 0, n_sel, o, o, own_last, 0, nchunks, c2, st);
 
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(
 
     RowState st;
     init_state(st);
-    attend_chunks<true>(qf, kc, vc, sel, n_sel, o, o, own_last, 0, nchunks, c2, st);
+    attend_chunks<true>(qf, kc, vc, sel, 0, n_sel, o, o, own_last, 0, nchunks, c2, st);
 
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
@@ -244,6 +245,14 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
     const int c_lo = split * per;
     const int c_hi = (c_lo + per < nchunks) ? c_lo + per : nchunks;
 
+    // The split's part of the selection, staged in LDS once: the walk then
+    // reads its entries without a global round trip before each chunk's gathers.
+    __shared__ int32_t lsel[kMaxBudget];
+    const int e_lo = kChunkBlocks * c_lo;
+    const int e_hi = (kChunkBlocks * c_hi < n_sel) ? kChunkBlocks * c_hi : n_sel;
+    for (int e = e_lo + lane; e < e_hi; e += 64) lsel[e - e_lo] = block_idx[b * budget + e];
+    __syncthreads();
+
     RowState st;
     init_state(st);
     if (c_lo < c_hi) {
@@ -251,7 +260,7 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
         load_q_frags(q + b * kQHeads * kHeadDim, grp, pos, tab, qf);
         const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
         const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-        attend_chunks<false>(qf, kc, vc, block_idx + b * budget, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
+        attend_chunks<false>(qf, kc, vc, lsel, e_lo, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
     }
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);

@@ -330,8 +330,8 @@ __global__ __launch_bounds__(64) void attend_backward_kernel(
         const int lb = kChunkBlocks * c;
         int64_t kblk[2], oblk[2];
         uint32_t kmask[2], omask[2];
-        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, o, lb + 4 * t + (h >> 2), own_last, kblk[t], kmask[t]);
-        for (int t = 0; t < 2; ++t) list_entry(sel, n_sel, o, o, lb + 4 * t + g, own_last, oblk[t], omask[t]);
+        for (int t = 0; t < 2; ++t) list_entry(sel, 0, n_sel, o, o, lb + 4 * t + (h >> 2), own_last, kblk[t], kmask[t]);
+        for (int t = 0; t < 2; ++t) list_entry(sel, 0, n_sel, o, o, lb + 4 * t + g, own_last, oblk[t], omask[t]);
         const int tk = h & 3;
         for (int t = 0; t < 2; ++t) {              // one 16-token tile at a time (register pressure)
             const bool krow = (kmask[t] >> tk) & 1u;
