@@ -121,18 +121,40 @@ def _check(status: int, where: str):
         raise QSAError(status, where, lib().qsa_last_hip_error())
 
 
-def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor", numel: Optional[int] = None):
+    """Device address of t after checking what the kernels assume of it: a
+    contiguous device tensor of the given dtype holding at least `numel`
+    elements (the library sees only the pointer, so a host tensor or a short
+    buffer would otherwise reach a kernel)."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor, got one on %s" % (name, t.device))
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s holds %d elements, the call needs %d" % (name, t.numel(), numel))
     return t.data_ptr()
 
 
-def _bf(t, name):
-    return _ptr(t, torch.bfloat16, name)
+def _bf(t, name, numel: Optional[int] = None):
+    return _ptr(t, torch.bfloat16, name, numel)
+
+
+# Elements per token / per sequence of the layouts in include/qsa.h.
+_Q, _KV, _QI, _KI, _ST = 24 * 256, 2 * 256, 4 * 128, 128, 32
+
+
+def _caches(h, B, k_cache=None, v_cache=None, kbar_cache=None, kpend=None):
+    """Pointers of the caches a call passes, each checked against B sequences of
+    the handle's capacity (absent ones are None)."""
+    n = h.max_ctx
+    return (_bf(k_cache, "k_cache", B * 2 * n * 256) if k_cache is not None else None,
+            _bf(v_cache, "v_cache", B * 2 * n * 256) if v_cache is not None else None,
+            _bf(kbar_cache, "kbar_cache", B * (n // 4) * 128) if kbar_cache is not None else None,
+            _bf(kpend, "kpend", B * 4 * 128) if kpend is not None else None)
 
 
 def _nbytes(t):
@@ -219,65 +241,76 @@ def alloc_caches(h: Handle, batch: int, device="cuda"):
 
 
 def qsa_append(h, B, L, q_offset, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend, stream=None):
-    _check(lib().qsa_append(h.ptr, _stream(stream), B, L, q_offset, _bf(k, "k"), _bf(v, "v"), _bf(k_idx, "k_idx"),
-                            _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
-                            _bf(kpend, "kpend")), "qsa_append")
+    n = B * L
+    kc, vc, kb, kp = _caches(h, B, k_cache, v_cache, kbar_cache, kpend)
+    _check(lib().qsa_append(h.ptr, _stream(stream), B, L, q_offset, _bf(k, "k", n * _KV), _bf(v, "v", n * _KV),
+                            _bf(k_idx, "k_idx", n * _KI), kc, vc, kb, kp), "qsa_append")
 
 
 def qsa_index(h, B, L, q_offset, q_idx, kbar_cache, scores, ws, stream=None):
-    _check(lib().qsa_index(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"), _bf(kbar_cache, "kbar_cache"),
-                           _ptr(scores, torch.float32, "scores"), _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_index")
+    ncol = (q_offset + L + 3) // 4
+    _, _, kb, _ = _caches(h, B, kbar_cache=kbar_cache)
+    _check(lib().qsa_index(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx", B * L * _QI), kb,
+                           _ptr(scores, torch.float32, "scores", B * L * ncol), _ptr(ws, None, "ws"), _nbytes(ws)),
+           "qsa_index")
 
 
 def qsa_select(h, B, L, q_offset, scores, block_idx, stream=None):
-    _check(lib().qsa_select(h.ptr, _stream(stream), B, L, q_offset, _ptr(scores, torch.float32, "scores"),
-                            _ptr(block_idx, torch.int32, "block_idx")), "qsa_select")
+    ncol = (q_offset + L + 3) // 4
+    _check(lib().qsa_select(h.ptr, _stream(stream), B, L, q_offset, _ptr(scores, torch.float32, "scores", B * L * ncol),
+                            _ptr(block_idx, torch.int32, "block_idx", B * L * h.budget)), "qsa_select")
 
 
 def qsa_index_select(h, B, L, q_offset, q_idx, kbar_cache, block_idx, ws, stream=None):
-    _check(lib().qsa_index_select(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"),
-                                  _bf(kbar_cache, "kbar_cache"), _ptr(block_idx, torch.int32, "block_idx"),
+    _, _, kb, _ = _caches(h, B, kbar_cache=kbar_cache)
+    _check(lib().qsa_index_select(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx", B * L * _QI), kb,
+                                  _ptr(block_idx, torch.int32, "block_idx", B * L * h.budget),
                                   _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_index_select")
 
 
 def qsa_attend(h, B, L, q_offset, q, k_cache, v_cache, block_idx, out, stream=None):
-    _check(lib().qsa_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q"), _bf(k_cache, "k_cache"),
-                            _bf(v_cache, "v_cache"), _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out")),
+    kc, vc, _, _ = _caches(h, B, k_cache, v_cache)
+    _check(lib().qsa_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q", B * L * _Q), kc, vc,
+                            _ptr(block_idx, torch.int32, "block_idx", B * L * h.budget), _bf(out, "out", B * L * _Q)),
            "qsa_attend")
 
 
 def qsa_forward(h, B, L, q_offset, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, block_idx, ws,
                 stream=None):
-    _check(lib().qsa_forward(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
-                             _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"), _bf(k_cache, "k_cache"),
-                             _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"),
-                             _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
+    n = B * L
+    kc, vc, kb, kp = _caches(h, B, k_cache, v_cache, kbar_cache, kpend)
+    _check(lib().qsa_forward(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q", n * _Q), _bf(k, "k", n * _KV),
+                             _bf(v, "v", n * _KV), _bf(q_idx, "q_idx", n * _QI), _bf(k_idx, "k_idx", n * _KI),
+                             kc, vc, kb, kp, _bf(out, "out", n * _Q),
+                             _ptr(block_idx, torch.int32, "block_idx", n * h.budget), _ptr(ws, None, "ws"),
                              _nbytes(ws)), "qsa_forward")
 
 
 def qsa_decode(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out,
                block_idx, ws, stream=None):
-    _check(lib().qsa_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"), ctx_bound,
-                            _bf(q, "q"), _bf(k, "k"), _bf(v, "v"), _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
-                            _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
-                            _bf(kpend, "kpend"), _bf(out, "out"), _ptr(block_idx, torch.int32, "block_idx"),
+    kc, vc, kb, kp = _caches(h, B, k_cache, v_cache, kbar_cache, kpend)
+    _check(lib().qsa_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len", B), ctx_bound,
+                            _bf(q, "q", B * _Q), _bf(k, "k", B * _KV), _bf(v, "v", B * _KV),
+                            _bf(q_idx, "q_idx", B * _QI), _bf(k_idx, "k_idx", B * _KI), kc, vc, kb, kp,
+                            _bf(out, "out", B * _Q), _ptr(block_idx, torch.int32, "block_idx", B * h.budget),
                             _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_decode")
 
 
 def qsa_decode_reuse(h, B, cache_len, sel_pos, ctx_bound, q, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend,
                      block_idx, out, ws, stream=None):
-    _check(lib().qsa_decode_reuse(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"),
-                                  _ptr(sel_pos, torch.int32, "sel_pos"), ctx_bound, _bf(q, "q"), _bf(k, "k"),
-                                  _bf(v, "v"), _bf(k_idx, "k_idx"), _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"),
-                                  _bf(kbar_cache, "kbar_cache"), _bf(kpend, "kpend"),
-                                  _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out"), _ptr(ws, None, "ws"),
-                                  _nbytes(ws)), "qsa_decode_reuse")
+    kc, vc, kb, kp = _caches(h, B, k_cache, v_cache, kbar_cache, kpend)
+    _check(lib().qsa_decode_reuse(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len", B),
+                                  _ptr(sel_pos, torch.int32, "sel_pos", B), ctx_bound, _bf(q, "q", B * _Q),
+                                  _bf(k, "k", B * _KV), _bf(v, "v", B * _KV), _bf(k_idx, "k_idx", B * _KI),
+                                  kc, vc, kb, kp, _ptr(block_idx, torch.int32, "block_idx", B * h.budget),
+                                  _bf(out, "out", B * _Q), _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_decode_reuse")
 
 
 def qsa_index_decode(h, B, cache_len, ctx_bound, q_idx, k_idx, kbar_cache, kpend, block_idx, ws, stream=None):
-    _check(lib().qsa_index_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"), ctx_bound,
-                                  _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"), _bf(kbar_cache, "kbar_cache"),
-                                  _bf(kpend, "kpend"), _ptr(block_idx, torch.int32, "block_idx"), _ptr(ws, None, "ws"),
+    _, _, kb, kp = _caches(h, B, kbar_cache=kbar_cache, kpend=kpend)
+    _check(lib().qsa_index_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len", B), ctx_bound,
+                                  _bf(q_idx, "q_idx", B * _QI), _bf(k_idx, "k_idx", B * _KI), kb, kp,
+                                  _ptr(block_idx, torch.int32, "block_idx", B * h.budget), _ptr(ws, None, "ws"),
                                   _nbytes(ws)), "qsa_index_decode")
 
 
@@ -287,44 +320,55 @@ def alloc_token_keys(h: Handle, batch: int, device="cuda") -> torch.Tensor:
 
 
 def qsa_token_index_select(h, B, L, q_offset, q_idx, k_idx, ktok_cache, token_idx, ws, stream=None):
-    _check(lib().qsa_token_index_select(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx"),
-                                        _bf(k_idx, "k_idx"), _bf(ktok_cache, "ktok_cache"),
-                                        _ptr(token_idx, torch.int32, "token_idx"), _ptr(ws, None, "ws"),
-                                        _nbytes(ws)), "qsa_token_index_select")
+    _check(lib().qsa_token_index_select(h.ptr, _stream(stream), B, L, q_offset, _bf(q_idx, "q_idx", B * L * _QI),
+                                        _bf(k_idx, "k_idx", B * L * _KI),
+                                        _bf(ktok_cache, "ktok_cache", B * h.max_ctx * 128),
+                                        _ptr(token_idx, torch.int32, "token_idx", B * L * h.budget),
+                                        _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_token_index_select")
 
 
 def qsa_token_index_decode(h, B, cache_len, ctx_bound, q_idx, k_idx, ktok_cache, token_idx, ws, stream=None):
-    _check(lib().qsa_token_index_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len"),
-                                        ctx_bound, _bf(q_idx, "q_idx"), _bf(k_idx, "k_idx"),
-                                        _bf(ktok_cache, "ktok_cache"), _ptr(token_idx, torch.int32, "token_idx"),
+    _check(lib().qsa_token_index_decode(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len", B),
+                                        ctx_bound, _bf(q_idx, "q_idx", B * _QI), _bf(k_idx, "k_idx", B * _KI),
+                                        _bf(ktok_cache, "ktok_cache", B * h.max_ctx * 128),
+                                        _ptr(token_idx, torch.int32, "token_idx", B * h.budget),
                                         _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_token_index_decode")
 
 
 def qsa_train_forward(h, B, L, q, q_idx, k_cache, v_cache, kbar_cache, block_idx, out, stats, kl, ws, stream=None):
-    _check(lib().qsa_train_forward(h.ptr, _stream(stream), B, L, _bf(q, "q"), _bf(q_idx, "q_idx"),
-                                   _bf(k_cache, "k_cache"), _bf(v_cache, "v_cache"), _bf(kbar_cache, "kbar_cache"),
-                                   _ptr(block_idx, torch.int32, "block_idx"), _bf(out, "out"),
-                                   _ptr(stats, torch.float32, "stats"), _ptr(kl, torch.float32, "kl"),
-                                   _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_train_forward")
+    n = B * L
+    kc, vc, kb, _ = _caches(h, B, k_cache, v_cache, kbar_cache)
+    _check(lib().qsa_train_forward(h.ptr, _stream(stream), B, L, _bf(q, "q", n * _Q), _bf(q_idx, "q_idx", n * _QI),
+                                   kc, vc, kb, _ptr(block_idx, torch.int32, "block_idx", n * h.budget),
+                                   _bf(out, "out", n * _Q), _ptr(stats, torch.float32, "stats", n * _ST),
+                                   _ptr(kl, torch.float32, "kl", n), _ptr(ws, None, "ws"), _nbytes(ws)),
+           "qsa_train_forward")
 
 
 def qsa_train_backward_indexer(h, B, L, q, q_idx, k_cache, kbar_cache, block_idx, stats, dkl, dq_idx, dk_idx, ws,
                                stream=None):
-    _check(lib().qsa_train_backward_indexer(h.ptr, _stream(stream), B, L, _bf(q, "q"), _bf(q_idx, "q_idx"),
-                                            _bf(k_cache, "k_cache"), _bf(kbar_cache, "kbar_cache"),
-                                            _ptr(block_idx, torch.int32, "block_idx"),
-                                            _ptr(stats, torch.float32, "stats"), _ptr(dkl, torch.float32, "dkl"),
-                                            _ptr(dq_idx, torch.float32, "dq_idx"), _ptr(dk_idx, torch.float32, "dk_idx"),
+    n = B * L
+    kc, _, kb, _ = _caches(h, B, k_cache, kbar_cache=kbar_cache)
+    _check(lib().qsa_train_backward_indexer(h.ptr, _stream(stream), B, L, _bf(q, "q", n * _Q),
+                                            _bf(q_idx, "q_idx", n * _QI), kc, kb,
+                                            _ptr(block_idx, torch.int32, "block_idx", n * h.budget),
+                                            _ptr(stats, torch.float32, "stats", n * _ST),
+                                            _ptr(dkl, torch.float32, "dkl", n),
+                                            _ptr(dq_idx, torch.float32, "dq_idx", n * _QI),
+                                            _ptr(dk_idx, torch.float32, "dk_idx", n * _KI),
                                             _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_train_backward_indexer")
 
 
 def qsa_train_backward_attention(h, B, L, q, k_cache, v_cache, block_idx, out, dout, stats, dq, dk, dv,
                                  stream=None):
-    _check(lib().qsa_train_backward_attention(h.ptr, _stream(stream), B, L, _bf(q, "q"), _bf(k_cache, "k_cache"),
-                                              _bf(v_cache, "v_cache"), _ptr(block_idx, torch.int32, "block_idx"),
-                                              _bf(out, "out"), _bf(dout, "dout"), _ptr(stats, torch.float32, "stats"),
-                                              _ptr(dq, torch.float32, "dq"), _ptr(dk, torch.float32, "dk"),
-                                              _ptr(dv, torch.float32, "dv")), "qsa_train_backward_attention")
+    n = B * L
+    kc, vc, _, _ = _caches(h, B, k_cache, v_cache)
+    _check(lib().qsa_train_backward_attention(h.ptr, _stream(stream), B, L, _bf(q, "q", n * _Q), kc, vc,
+                                              _ptr(block_idx, torch.int32, "block_idx", n * h.budget),
+                                              _bf(out, "out", n * _Q), _bf(dout, "dout", n * _Q),
+                                              _ptr(stats, torch.float32, "stats", n * _ST),
+                                              _ptr(dq, torch.float32, "dq", n * _Q), _ptr(dk, torch.float32, "dk", n * _KV),
+                                              _ptr(dv, torch.float32, "dv", n * _KV)), "qsa_train_backward_attention")
 
 
 def qsa_gdn_workspace_size(nseq, max_len, hq_heads, hv_heads) -> int:

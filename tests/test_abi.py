@@ -111,3 +111,14 @@ def _gdn_call(nseq=1, cu=16, n_tok=64, max_len=64, hq=2, hv=6, q=16, k=16, v=16,
 ])
 def test_gdn_rejects_bad_arguments_on_the_host(kw, status):
     assert _gdn_call(**kw) == status
+
+
+def test_binding_rejects_host_tensors():
+    """The binding hands only addresses to the library, so it refuses a host
+    tensor (its address is not a device address) before any call."""
+    import torch
+    with pytest.raises(ValueError, match="device tensor"):
+        Q._ptr(torch.zeros(16, dtype=torch.float32), torch.float32, "x")
+    with pytest.raises(ValueError, match="device tensor"):
+        Q._bf(torch.zeros(16, dtype=torch.bfloat16), "q")
+    assert Q._ptr(None) is None

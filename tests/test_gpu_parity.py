@@ -574,3 +574,22 @@ def test_index_decode_equals_decode_selection():
         nb = (n + 1) // 4
         assert torch.equal(c2["kbar_cache"][b, :nb], c["kbar_cache"][b, :nb])
         assert torch.equal(c2["kpend"][b, :(n % 4) + 1], c["kpend"][b, :(n % 4) + 1])
+
+
+def test_binding_checks_buffers_before_launch():
+    """A short or host buffer is refused by the binding before anything is
+    enqueued (the library sees only its address)."""
+    B, L = 1, 64
+    h = Q.Handle(max_ctx=L, budget_blocks=16)
+    c = Q.alloc_caches(h, B)
+    q = torch.zeros((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bidx = torch.full((B, L, 16), -1, dtype=torch.int32, device=DEV)
+    short = torch.empty((B, L - 1, 24, 256), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError, match="needs"):
+        Q.qsa_attend(h, B, L, 0, q, c["k_cache"], c["v_cache"], bidx, short)
+    with pytest.raises(ValueError, match="device tensor"):
+        Q.qsa_attend(h, B, L, 0, q.cpu(), c["k_cache"], c["v_cache"], bidx, torch.empty_like(q))
+    small = Q.alloc_caches(Q.Handle(max_ctx=L // 2, budget_blocks=16), B)
+    with pytest.raises(ValueError, match="k_cache"):
+        Q.qsa_attend(h, B, L, 0, q, small["k_cache"], c["v_cache"], bidx, torch.empty_like(q))
+    torch.cuda.synchronize()
