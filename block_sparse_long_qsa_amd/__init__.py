@@ -396,28 +396,34 @@ def qsa_gdn_chunk_prefill(nseq, cu_seqlens, max_len, q, k, v, g, beta, scale, in
     beta [n_tokens][Hv] fp32, cu_seqlens int32 [nseq + 1] on the device, states
     [nseq][Hv][128][128] fp32 or None."""
     n_tok, hq, hv = _gdn_shapes(q, k, v, g, beta, o)
-    _check(lib().qsa_gdn_chunk_prefill(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_tok,
+    ns = max(nseq, 0) * hv * 128 * 128
+    _check(lib().qsa_gdn_chunk_prefill(_stream(stream), nseq,
+                                       _ptr(cu_seqlens, torch.int32, "cu_seqlens", max(nseq, 0) + 1), n_tok,
                                        max_len, hq, hv, float(scale), _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
                                        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
-                                       _ptr(initial_state, torch.float32, "initial_state"), _bf(o, "o"),
-                                       _ptr(final_state, torch.float32, "final_state"), _ptr(ws, None, "ws"),
+                                       _ptr(initial_state, torch.float32, "initial_state", ns), _bf(o, "o"),
+                                       _ptr(final_state, torch.float32, "final_state", ns), _ptr(ws, None, "ws"),
                                        _nbytes(ws)), "qsa_gdn_chunk_prefill")
 
 
 def qsa_gdn_prep(nseq, cu_seqlens, max_len, q, k, hv, g, beta, scale, ws, stream=None):
     n_tok, hq = q.shape[0], q.shape[1]
-    _check(lib().qsa_gdn_prep(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_tok, max_len, hq,
-                              hv, float(scale), _bf(q, "q"), _bf(k, "k"), _ptr(g, torch.float32, "g"),
-                              _ptr(beta, torch.float32, "beta"), _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_gdn_prep")
+    if tuple(k.shape) != tuple(q.shape) or q.dim() != 3 or q.shape[2] != 128:
+        raise ValueError("q, k must be [n_tokens][heads][128] of one shape")
+    _check(lib().qsa_gdn_prep(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens", max(nseq, 0) + 1),
+                              n_tok, max_len, hq, hv, float(scale), _bf(q, "q"), _bf(k, "k"),
+                              _ptr(g, torch.float32, "g", n_tok * hv), _ptr(beta, torch.float32, "beta", n_tok * hv),
+                              _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_gdn_prep")
 
 
 def qsa_gdn_scan(nseq, cu_seqlens, max_len, q, k, v, g, scale, initial_state, o, final_state, ws, stream=None):
     n_tok, hq, hv = _gdn_shapes(q, k, v, g, None, o)
-    _check(lib().qsa_gdn_scan(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens"), n_tok, max_len, hq,
-                              hv, float(scale), _bf(q, "q"), _bf(k, "k"), _bf(v, "v"), _ptr(g, torch.float32, "g"),
-                              _ptr(initial_state, torch.float32, "initial_state"), _bf(o, "o"),
-                              _ptr(final_state, torch.float32, "final_state"), _ptr(ws, None, "ws"), _nbytes(ws)),
-           "qsa_gdn_scan")
+    ns = max(nseq, 0) * hv * 128 * 128
+    _check(lib().qsa_gdn_scan(_stream(stream), nseq, _ptr(cu_seqlens, torch.int32, "cu_seqlens", max(nseq, 0) + 1),
+                              n_tok, max_len, hq, hv, float(scale), _bf(q, "q"), _bf(k, "k"), _bf(v, "v"),
+                              _ptr(g, torch.float32, "g"), _ptr(initial_state, torch.float32, "initial_state", ns),
+                              _bf(o, "o"), _ptr(final_state, torch.float32, "final_state", ns), _ptr(ws, None, "ws"),
+                              _nbytes(ws)), "qsa_gdn_scan")
 
 
 def qsa_status_string(status: int) -> str:
