@@ -199,9 +199,12 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
     return e;
 }
 
+// The batch is a grid dimension (y or z) of every QSA kernel: at most 65,535.
+constexpr int32_t kMaxBatch = 65535;
+
 qsa_status check_chunk(const qsa_handle *h, int32_t B, int64_t L, int64_t q_offset, bool aligned_offset) {
     if (!h) return QSA_ERR_NULL;
-    if (B < 1 || L < 0 || q_offset < 0) return QSA_ERR_SHAPE;
+    if (B < 1 || B > kMaxBatch || L < 0 || q_offset < 0) return QSA_ERR_SHAPE;
     if (aligned_offset && (q_offset % kBlock) != 0) return QSA_ERR_ALIGN;
     if (q_offset + L > h->p.max_ctx) return QSA_ERR_CAPACITY;
     return QSA_OK;
@@ -438,7 +441,7 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
                       const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache,
                       uint16_t *kpend, uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes) {
     if (!h) return QSA_ERR_NULL;
-    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (B < 1 || B > kMaxBatch || ctx_bound < 0) return QSA_ERR_SHAPE;
     if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
     qsa_status s = check_ptrs({cache_len, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, ws});
     if (s != QSA_OK) return s;
@@ -480,7 +483,7 @@ qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const 
                             uint16_t *kbar_cache, uint16_t *kpend, const int32_t *block_idx, uint16_t *out, void *ws,
                             size_t ws_bytes) {
     if (!h) return QSA_ERR_NULL;
-    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (B < 1 || B > kMaxBatch || ctx_bound < 0) return QSA_ERR_SHAPE;
     if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
     qsa_status s = check_ptrs({cache_len, sel_pos, q, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend, block_idx, out,
                                ws});
@@ -511,7 +514,7 @@ qsa_status qsa_index_decode(const qsa_handle *h, void *stream, int32_t B, const 
                             const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *kbar_cache, uint16_t *kpend,
                             int32_t *block_idx, void *ws, size_t ws_bytes) {
     if (!h) return QSA_ERR_NULL;
-    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (B < 1 || B > kMaxBatch || ctx_bound < 0) return QSA_ERR_SHAPE;
     if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
     qsa_status s = check_ptrs({cache_len, q_idx, k_idx, kbar_cache, kpend, block_idx, ws});
     if (s != QSA_OK) return s;
@@ -562,7 +565,7 @@ qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, 
                                   int64_t ctx_bound, const uint16_t *q_idx, const uint16_t *k_idx,
                                   uint16_t *ktok_cache, int32_t *token_idx, void *ws, size_t ws_bytes) {
     if (!h) return QSA_ERR_NULL;
-    if (B < 1 || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (B < 1 || B > kMaxBatch || ctx_bound < 0) return QSA_ERR_SHAPE;
     if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
     qsa_status s = check_ptrs({cache_len, q_idx, k_idx, ktok_cache, token_idx, ws});
     if (s != QSA_OK) return s;

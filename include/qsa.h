@@ -34,6 +34,7 @@
  *     surface at the caller's next synchronisation.
  *   - A call with L = 0 is a no-op that returns QSA_OK after the shape checks
  *     (its pointers may then be NULL).
+ *   - The batch B is 1 .. 65535 (QSA_ERR_SHAPE otherwise).
  *   - Inputs must be finite; non-finite values are not detected.
  *   - Calls that share a cache must be ordered (same stream or explicit
  *     events); the handle itself is immutable and may be shared by threads.

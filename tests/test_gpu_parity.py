@@ -593,3 +593,14 @@ def test_binding_checks_buffers_before_launch():
     with pytest.raises(ValueError, match="k_cache"):
         Q.qsa_attend(h, B, L, 0, q, small["k_cache"], c["v_cache"], bidx, torch.empty_like(q))
     torch.cuda.synchronize()
+
+
+def test_batch_beyond_grid_limit_is_a_shape_error():
+    """B is a grid dimension of the kernels: B > 65535 is refused on the host
+    (QSA_ERR_SHAPE) before any pointer is looked at."""
+    h = Q.Handle(max_ctx=64, budget_blocks=16)
+    lib = Q.lib()
+    assert lib.qsa_attend(h.ptr, None, 65536, 4, 0, None, None, None, None, None) == 2
+    assert lib.qsa_append(h.ptr, None, 65536, 4, 0, None, None, None, None, None, None, None) == 2
+    assert lib.qsa_decode(h.ptr, None, 65536, None, 64, *([None] * 12), 0) == 2
+    assert lib.qsa_attend(h.ptr, None, 0, 4, 0, None, None, None, None, None) == 2
