@@ -604,3 +604,53 @@ def test_batch_beyond_grid_limit_is_a_shape_error():
     assert lib.qsa_append(h.ptr, None, 65536, 4, 0, None, None, None, None, None, None, None) == 2
     assert lib.qsa_decode(h.ptr, None, 65536, None, 64, *([None] * 12), 0) == 2
     assert lib.qsa_attend(h.ptr, None, 0, 4, 0, None, None, None, None, None) == 2
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 8, 13])
+def test_forward_tiny_prefills(L):
+    """Whole calls of a few tokens (B = 2, budget 2): rows before the first
+    complete block have no candidate and attend their own tokens only; rows
+    with fewer complete blocks than the budget take them all.  Every row vs
+    the oracle."""
+    B, budget = 2, 2
+    w = synth.Workload("t", "prefill", B, L, budget, 0, "random", 40 + L)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=16, budget_blocks=budget)
+    out, bidx, _ = _forward(h, xd, B, L)
+    _check_forward(x, f32(out), bidx.cpu().numpy(), O.Params(budget=budget), range(L), seqs=(0, 1))
+
+
+def test_forward_chunks_of_one_block_equal_one_shot():
+    """Chunks of 4 tokens (one micro-block each; every chunk but the first
+    attends only cached blocks plus its own) are bit-identical to one shot."""
+    B, L, budget = 2, 96, 8
+    w = synth.Workload("t", "prefill", B, L, budget, 2, "random", 47)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=96, budget_blocks=budget)
+    o1, b1, _ = _forward(h, xd, B, L)
+    o2, b2, _ = _forward(h, xd, B, L, chunks=[(s, s + 4) for s in range(0, L, 4)])
+    assert torch.equal(b1, b2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    _check_forward(x, f32(o2), b2.cpu().numpy(), O.Params(budget=budget), [0, 3, 4, 35, 36, 95], seqs=(0, 1))
+
+
+def test_empty_calls_touch_nothing():
+    """L = 0 is a no-op that succeeds: caches and outputs keep their bytes."""
+    B = 2
+    h = Q.Handle(max_ctx=64, budget_blocks=4)
+    c = Q.alloc_caches(h, B)
+    for t in c.values():
+        t.view(torch.int16).fill_(0x1234)
+    before = {k: v.clone() for k, v in c.items()}
+    e = lambda *s, dt=torch.bfloat16: torch.empty(s, dtype=dt, device=DEV)
+    q, kv, qi, ki = e(B, 0, 24, 256), e(B, 0, 2, 256), e(B, 0, 4, 128), e(B, 0, 128)
+    out, bidx = e(B, 0, 24, 256), e(B, 0, 4, dt=torch.int32)
+    ws = Q.workspace(h, Q.QSA_OP_FORWARD, B, 0, 16)
+    Q.qsa_forward(h, B, 0, 16, q, kv, kv, qi, ki, c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], out, bidx,
+                  ws)
+    Q.qsa_append(h, B, 0, 16, kv, kv, ki, c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    Q.qsa_attend(h, B, 0, 16, q, c["k_cache"], c["v_cache"], bidx, out)
+    Q.qsa_index_select(h, B, 0, 16, qi, c["kbar_cache"], bidx, Q.workspace(h, Q.QSA_OP_INDEX_SELECT, B, 0, 16))
+    torch.cuda.synchronize()
+    for k in c:
+        assert torch.equal(c[k], before[k]), k
