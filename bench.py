@@ -70,13 +70,26 @@ def setup_prefill(w):
     L = w.seq_len
     h = Q.Handle(max_ctx=L, budget_blocks=w.budget, yarn_factor=w.yarn_factor)
     c = Q.alloc_caches(h, 1)
-    ws = Q.workspace(h, Q.QSA_OP_INDEX_SELECT, 1, L, 0)
+    ws = Q.workspace(h, Q.QSA_OP_FORWARD, 1, L, 0)      # also large enough for qsa_index_select
     bidx = torch.empty((1, L, w.budget), dtype=torch.int32, device="cuda")
     out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device="cuda")
     return dict(x=x, h=h, c=c, ws=ws, bidx=bidx, out=out, L=L)
 
 
+def prefill_forward(s, ev):
+    """One prefill as the library runs it: qsa_forward (append, then index +
+    select on the handle's second stream slice by slice while the slices
+    attend on this one)."""
+    x, h, c, L = s["x"], s["h"], s["c"], s["L"]
+    ev[0].record()
+    Q.qsa_forward(h, 1, L, 0, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], c["k_cache"], c["v_cache"],
+                  c["kbar_cache"], c["kpend"], s["out"], s["bidx"], s["ws"])
+    ev[1].record()
+
+
 def prefill_stages(s, ev):
+    """The same work as three calls on one stream, with events between them:
+    the per-stage times and the attention kernel's own duration."""
     x, h, c, L = s["x"], s["h"], s["c"], s["L"]
     ev[0].record()
     Q.qsa_append(h, 1, L, 0, x["k"], x["v"], x["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
@@ -410,12 +423,12 @@ def run_ratios(steps):
     wp = synth.WORKLOADS["prefill_256k"]
     sp = setup_prefill(wp)
     for _ in range(2):
-        prefill_stages(sp, _events(4))
-    ev = [_events(4) for _ in range(steps)]
+        prefill_forward(sp, _events(2))
+    ev = [_events(2) for _ in range(steps)]
     for e in ev:
-        prefill_stages(sp, e)
+        prefill_forward(sp, e)
     torch.cuda.synchronize()
-    t_qsa = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    t_qsa = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     del sp
     torch.cuda.empty_cache()
     t_dense = dense_prefill_ms(wp.seq_len, reps=2)
@@ -690,25 +703,33 @@ def main():
 
     for _ in range(args.warmup):
         if sp:
-            prefill_stages(sp, _events(4))
+            prefill_forward(sp, _events(2))
         if sd:
             decode_step(sd)
     torch.cuda.synchronize()
     print("warmup done", file=sys.stderr, flush=True)
 
-    ev_p = [_events(4) for _ in range(args.steps)]
+    ev_f = [_events(2) for _ in range(args.steps)]
     ev_d = [_events(2) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if sp:
-            prefill_stages(sp, ev_p[i])
+            prefill_forward(sp, ev_f[i])
         if sd:
             ev_d[i][0].record()
             decode_step(sd)
             ev_d[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev_p = []
+    if sp:                  # per-stage times: the staged calls, after the timed region
+        n_st = max(1, min(args.steps, 5))
+        prefill_stages(sp, _events(4))
+        ev_p = [_events(4) for _ in range(n_st)]
+        for e in ev_p:
+            prefill_stages(sp, e)
+        torch.cuda.synchronize()
 
     if sp is None:
         t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_d]))
@@ -718,7 +739,8 @@ def main():
         return
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in ev_p])   # ms
     t_append, t_isel, t_attn = st.mean(axis=0)
-    t_prefill = float(st.sum(axis=1).mean())
+    t_prefill = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_f]))
+    t_staged = float(st.sum(axis=1).mean())
     t_dec = float(np.mean([e[0].elapsed_time(e[1]) for e in ev_d])) if sd else None
 
     L = wp.seq_len
@@ -746,7 +768,8 @@ def main():
             "decode": {"batch": wd.batch, "ctx": wd.seq_len, "budget_blocks": wd.budget},
         },
         "prefill": {
-            "ms": t_prefill, "tok_s": L / (t_prefill * 1e-3),
+            "ms": t_prefill, "tok_s": L / (t_prefill * 1e-3), "call": "qsa_forward",
+            "staged_ms": t_staged,
             "stage_ms": {"append": float(t_append), "index_select": float(t_isel), "attend": float(t_attn)},
             "index_select_tflops_equiv": idx_tfs,
             "index_select_mfma_frac": idx_tfs / MFMA_BF16_PEAK_TFS,

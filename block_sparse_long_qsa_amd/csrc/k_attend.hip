@@ -130,19 +130,21 @@ __device__ __forceinline__ void prefill_slot(int64_t L, int wave, int64_t &i, in
     i = (x - grp * nt) * 4 + wave;
 }
 
-// Prefill: 4 waves per workgroup = 4 queries of one KV group.
+// Prefill: 4 waves per workgroup = 4 queries of one KV group.  The launch
+// covers rows row0 .. row0+L-1 of buffers holding ld rows per sequence.
 __global__ __launch_bounds__(256) void attend_prefill_kernel(
-    Tables tab, int64_t L, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
+    Tables tab, int64_t L, int64_t row0, int64_t ld, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
     const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out)
 {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int64_t b = blockIdx.y;
-    int64_t i;
+    int64_t il;
     int grp;
-    prefill_slot(L, wave, i, grp);
-    if (i >= L) return;
+    prefill_slot(L, wave, il, grp);
+    if (il >= L) return;
+    const int64_t i = row0 + il;
     const int64_t pos = q_offset + i;
     const int64_t o = pos / kBlock;
     const int own_last = static_cast<int>(pos - o * kBlock);
@@ -150,10 +152,10 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     const int nchunks = list_chunks(n_sel, o, o);
 
     bf16x8 qf[8];
-    load_q_frags(q + (b * L + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
+    load_q_frags(q + (b * ld + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
     const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
     const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-    const int32_t *sel = block_idx + (b * L + i) * budget;
+    const int32_t *sel = block_idx + (b * ld + i) * budget;
 
     RowState st;
     init_state(st);
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
     const float inv = 1.0f / lt;
     const int h = lane & 15, g = lane >> 4;
     if (h < kGroup) {
-        bf16_t *dst = out + ((b * L + i) * kQHeads + grp * kGroup + h) * kHeadDim + 4 * g;
+        bf16_t *dst = out + ((b * ld + i) * kQHeads + grp * kGroup + h) * kHeadDim + 4 * g;
         for (int n = 0; n < 16; ++n) {
             u32x2 w = u32x2{pack_bf16x2(st.o[n][0] * inv, st.o[n][1] * inv),
                             pack_bf16x2(st.o[n][2] * inv, st.o[n][3] * inv)};
@@ -321,13 +323,13 @@ __global__ __launch_bounds__(256) void attend_decode_merge_kernel(int nsplit, fl
 }
 
 // ---------------------------------------------------------------- launchers
-hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
-                                 int64_t nblk_cap, int budget, float sigma, const bf16_t *q, const bf16_t *k_cache,
-                                 const bf16_t *v_cache, const int32_t *block_idx, bf16_t *out)
+hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t row0, int64_t ld,
+                                 int64_t q_offset, int64_t nblk_cap, int budget, float sigma, const bf16_t *q,
+                                 const bf16_t *k_cache, const bf16_t *v_cache, const int32_t *block_idx, bf16_t *out)
 {
     if (L <= 0) return hipSuccess;
     dim3 grid(static_cast<unsigned>(2 * ((L + 3) / 4)), static_cast<unsigned>(B));
-    hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, L, q_offset, nblk_cap, budget,
+    hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, L, row0, ld, q_offset, nblk_cap, budget,
                        sigma * kLog2e, q, k_cache, v_cache, block_idx, out);
     return hipGetLastError();
 }

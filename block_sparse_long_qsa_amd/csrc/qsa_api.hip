@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+#include <new>
 #include <vector>
 
 #include "qsa.h"
@@ -29,8 +31,9 @@ hipError_t launch_indexer_topk(hipStream_t, int32_t, int64_t, int64_t, int, int6
 hipError_t launch_zero_words(hipStream_t, int32_t *, int64_t);
 hipError_t launch_select_fixup(hipStream_t, int32_t, int64_t, int64_t, int, int, const int32_t *, int32_t *, int64_t,
                                const bf16_t *, int64_t, const bf16_t *, int64_t);
-hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int, float,
-                                 const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, bf16_t *);
+hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int64_t, int64_t,
+                                 int, float, const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *,
+                                 bf16_t *);
 hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, const int32_t *, int64_t, int64_t,
                                 int, int, float,
                                 const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
@@ -65,6 +68,12 @@ hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, cons
 
 using namespace qsa;
 
+// qsa_forward splits a long prefill into row slices: the fused index + select
+// of slice k+1 runs on the handle's second stream while slice k attends on the
+// caller's stream (the first is bound by the vector ALUs and matrix cores, the
+// second by memory).  At most this many slices per call.
+constexpr int kForwardSlicesMax = 64;
+
 struct qsa_handle {
     qsa_params p;
     int cap;            // candidate list length per query of the fused index + select stage
@@ -72,6 +81,9 @@ struct qsa_handle {
     float *d_cos;
     float *d_sin;
     float sigma;        // softmax scale of the core logits
+    hipStream_t side;   // the sliced prefill's index + select stream (default priority)
+    hipEvent_t ev[kForwardSlicesMax + 2];   // fork, one per slice, join
+    std::mutex mu;      // one sliced prefill enqueues its events at a time
 };
 
 namespace {
@@ -174,18 +186,19 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int r
 }
 
 // keys: pooled k̄ (rsh = 2, key_cap = max_ctx / 4) or token keys (rsh = 0, key_cap = max_ctx).
-hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
-                            const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *bidx, char *w,
-                            const IdxSelLayout &f, int rsh = 2, int64_t key_cap = -1) {
-    if (key_cap < 0) key_cap = nblk_cap(h);
-    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
+// The fused index + select launches for rows r_lo .. r_hi-1 of an L-row call
+// whose indexer queries are already rotated into the workspace.
+hipError_t index_select_rows(const qsa_handle *h, hipStream_t st, int32_t B, int64_t L, int64_t q_offset, int64_t r_lo,
+                             int64_t r_hi, const uint16_t *kbar_cache, int32_t *bidx, char *w, const IdxSelLayout &f,
+                             int rsh, int64_t key_cap) {
+    const bf16_t *qrot = reinterpret_cast<const bf16_t *>(w + f.qrot);
     uint2 *cand = reinterpret_cast<uint2 *>(w + f.cand);
     int32_t *ovf = reinterpret_cast<int32_t *>(w + f.ovf);
     const int budget = h->p.budget_blocks;
     const int64_t qstride = L * kIdxHeads * kIdxDim;
-    hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
-    for (int64_t r0 = 0; r0 < L && e == hipSuccess; r0 += f.rows) {
-        const int64_t nr = (r0 + f.rows < L) ? f.rows : L - r0;
+    hipError_t e = hipSuccess;
+    for (int64_t r0 = r_lo; r0 < r_hi && e == hipSuccess; r0 += f.rows) {
+        const int64_t nr = (r0 + f.rows < r_hi) ? f.rows : r_hi - r0;
         const int64_t pos0 = q_offset + r0;
         const bf16_t *qr = qrot + r0 * kIdxHeads * kIdxDim;
         e = launch_zero_words(st, ovf, 1);
@@ -197,6 +210,27 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
                                     kbar_cache, key_cap);
     }
     return e;
+}
+
+hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int64_t L, int64_t q_offset,
+                            const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *bidx, char *w,
+                            const IdxSelLayout &f, int rsh = 2, int64_t key_cap = -1) {
+    if (key_cap < 0) key_cap = nblk_cap(h);
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + f.qrot);
+    hipError_t e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx, qrot);
+    if (e == hipSuccess) e = index_select_rows(h, st, B, L, q_offset, 0, L, kbar_cache, bidx, w, f, rsh, key_cap);
+    return e;
+}
+
+// Rows per slice of a sliced prefill, or 0 for one pass on the caller's stream.
+// 8,192-row slices measured best on the 262,144-token prefill (4,096: the
+// launches are too small to fill the device; 16,384 and 32,768: less overlap).
+int64_t forward_slice_rows(int64_t L) {
+    constexpr int64_t kSlice = 8192;
+    if (L < 2 * kSlice) return 0;
+    int64_t r = kSlice;
+    if ((L + r - 1) / r > kForwardSlicesMax) r = ((L + kForwardSlicesMax - 1) / kForwardSlicesMax + 63) / 64 * 64;
+    return r;
 }
 
 // The batch is a grid dimension (y or z) of every QSA kernel: at most 65,535.
@@ -262,7 +296,7 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
 
     DeviceGuard guard(device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
-    qsa_handle *h = static_cast<qsa_handle *>(calloc(1, sizeof(qsa_handle)));
+    qsa_handle *h = new (std::nothrow) qsa_handle();
     if (!h) return QSA_ERR_SHAPE;
     h->p = p;
     h->cap = p.topk_cap ? p.topk_cap : kDefaultCap;
@@ -277,10 +311,11 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->d_sin), n * sizeof(float));
     if (e == hipSuccess) e = hipMemcpy(h->d_cos, hc.data(), n * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(h->d_sin, hs.data(), n * sizeof(float), hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
+    for (int i = 0; i < kForwardSlicesMax + 2 && e == hipSuccess; ++i)
+        e = hipEventCreateWithFlags(&h->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
-        if (h->d_cos) (void)hipFree(h->d_cos);
-        if (h->d_sin) (void)hipFree(h->d_sin);
-        free(h);
+        qsa_destroy(h);
         return hip_fail(e);
     }
     *out = h;
@@ -290,9 +325,13 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
 void qsa_destroy(qsa_handle *h) {
     if (!h) return;
     DeviceGuard guard(h->device);
+    if (h->side) (void)hipStreamSynchronize(h->side);
+    for (int i = 0; i < kForwardSlicesMax + 2; ++i)
+        if (h->ev[i]) (void)hipEventDestroy(h->ev[i]);
+    if (h->side) (void)hipStreamDestroy(h->side);
     if (h->d_cos) (void)hipFree(h->d_cos);
     if (h->d_sin) (void)hipFree(h->d_sin);
-    free(h);
+    delete h;
 }
 
 qsa_status qsa_get_params(const qsa_handle *h, qsa_params *out) {
@@ -387,7 +426,7 @@ qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = launch_attend_prefill(tables(h), st, B, L, q_offset, nblk_cap(h), h->p.budget_blocks, h->sigma, q,
+    hipError_t e = launch_attend_prefill(tables(h), st, B, L, 0, L, q_offset, nblk_cap(h), h->p.budget_blocks, h->sigma, q,
                                   k_cache, v_cache, block_idx, out);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
@@ -429,11 +468,48 @@ qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, 
     hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nbc, k, v, k_idx, k_cache, v_cache, kbar_cache,
                                   kpend, true, true);
     if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
-    if (e == hipSuccess) e = run_index_select(h, st, B, L, q_offset, q_idx, kbar_cache, bidx, w, f);
-    if (e == hipSuccess)
-        e = launch_attend_prefill(tables(h), st, B, L, q_offset, nbc, h->p.budget_blocks, h->sigma, q, k_cache,
-                                  v_cache, bidx, out);
-    return e == hipSuccess ? QSA_OK : hip_fail(e);
+    const int64_t R = forward_slice_rows(L);
+    const int budget = h->p.budget_blocks;
+    if (R == 0) {
+        if (e == hipSuccess) e = run_index_select(h, st, B, L, q_offset, q_idx, kbar_cache, bidx, w, f);
+        if (e == hipSuccess)
+            e = launch_attend_prefill(tables(h), st, B, L, 0, L, q_offset, nbc, budget, h->sigma, q, k_cache, v_cache,
+                                      bidx, out);
+        return e == hipSuccess ? QSA_OK : hip_fail(e);
+    }
+    // Sliced: rotate every indexer query here, then fork to the side stream,
+    // which runs slice after slice of index + select and records an event
+    // after each; slice k attends here once its event has fired.  The last
+    // wait (or, after an error, the join event) makes every side-stream launch
+    // precede whatever the caller enqueues next.
+    if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx,
+                                                 reinterpret_cast<bf16_t *>(w + f.qrot));
+    if (e != hipSuccess) return hip_fail(e);
+    qsa_handle *hm = const_cast<qsa_handle *>(h);     // the stream, events and lock only
+    std::lock_guard<std::mutex> lock(hm->mu);
+    const int ns = static_cast<int>((L + R - 1) / R);
+    e = hipEventRecord(hm->ev[0], st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(hm->side, hm->ev[0], 0);
+    int recorded = 0;
+    for (int k = 0; k < ns && e == hipSuccess; ++k) {
+        const int64_t r0 = k * R, r1 = (r0 + R < L) ? r0 + R : L;
+        e = index_select_rows(h, hm->side, B, L, q_offset, r0, r1, kbar_cache, bidx, w, f, 2, nbc);
+        if (e == hipSuccess) e = hipEventRecord(hm->ev[k + 1], hm->side);
+        if (e == hipSuccess) recorded = k + 1;
+    }
+    for (int k = 0; k < recorded && e == hipSuccess; ++k) {
+        const int64_t r0 = k * R, r1 = (r0 + R < L) ? r0 + R : L;
+        e = hipStreamWaitEvent(st, hm->ev[k + 1], 0);
+        if (e == hipSuccess)
+            e = launch_attend_prefill(tables(h), st, B, r1 - r0, r0, L, q_offset, nbc, budget, h->sigma, q, k_cache,
+                                      v_cache, bidx, out);
+    }
+    if (e != hipSuccess) {      // keep the side stream's launches ahead of the caller's next work
+        if (hipEventRecord(hm->ev[kForwardSlicesMax + 1], hm->side) == hipSuccess)
+            (void)hipStreamWaitEvent(st, hm->ev[kForwardSlicesMax + 1], 0);
+        return hip_fail(e);
+    }
+    return QSA_OK;
 }
 
 qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
