@@ -222,15 +222,19 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
     return e;
 }
 
-// Rows per slice of a sliced prefill, or 0 for one pass on the caller's stream.
-// 8,192-row slices measured best on the 262,144-token prefill (4,096: the
-// launches are too small to fill the device; 16,384 and 32,768: less overlap).
-int64_t forward_slice_rows(int64_t L) {
-    constexpr int64_t kSlice = 8192;
-    if (L < 2 * kSlice) return 0;
-    int64_t r = kSlice;
-    if ((L + r - 1) / r > kForwardSlicesMax) r = ((L + kForwardSlicesMax - 1) / kForwardSlicesMax + 63) / 64 * 64;
-    return r;
+// Slices of a sliced prefill: index + select in slices of ri rows (at least
+// 32,768 = 512 work-groups of the fused kernel, enough to fill the device even
+// deep in a 1M context), attention in slices of ra rows (8,192: the finer the
+// attention slices, the sooner each selection slice is consumed).  ri = 0: one
+// pass on the caller's stream.
+struct ForwardSlices { int64_t ri, ra; };
+ForwardSlices forward_slices(int64_t L) {
+    constexpr int64_t kAttendRows = 8192, kSelectRows = 32768;
+    if (L < 2 * kSelectRows) return {0, 0};     // fewer than two selection slices: nothing to overlap
+    int64_t ri = kSelectRows;
+    if ((L + ri - 1) / ri > kForwardSlicesMax)
+        ri = ((L + kForwardSlicesMax - 1) / kForwardSlicesMax + kAttendRows - 1) / kAttendRows * kAttendRows;
+    return {ri, kAttendRows};
 }
 
 // The batch is a grid dimension (y or z) of every QSA kernel: at most 65,535.
@@ -468,9 +472,9 @@ qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, 
     hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nbc, k, v, k_idx, k_cache, v_cache, kbar_cache,
                                   kpend, true, true);
     if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
-    const int64_t R = forward_slice_rows(L);
+    const ForwardSlices fs = forward_slices(L);
     const int budget = h->p.budget_blocks;
-    if (R == 0) {
+    if (fs.ri == 0) {
         if (e == hipSuccess) e = run_index_select(h, st, B, L, q_offset, q_idx, kbar_cache, bidx, w, f);
         if (e == hipSuccess)
             e = launch_attend_prefill(tables(h), st, B, L, 0, L, q_offset, nbc, budget, h->sigma, q, k_cache, v_cache,
@@ -479,30 +483,33 @@ qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, 
     }
     // Sliced: rotate every indexer query here, then fork to the side stream,
     // which runs slice after slice of index + select and records an event
-    // after each; slice k attends here once its event has fired.  The last
-    // wait (or, after an error, the join event) makes every side-stream launch
-    // precede whatever the caller enqueues next.
+    // after each; each attention slice runs here once the event of the
+    // selection slice holding its rows has fired.  The last wait (or, after an
+    // error, the join event) makes every side-stream launch precede whatever
+    // the caller enqueues next.
     if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx,
                                                  reinterpret_cast<bf16_t *>(w + f.qrot));
     if (e != hipSuccess) return hip_fail(e);
     qsa_handle *hm = const_cast<qsa_handle *>(h);     // the stream, events and lock only
     std::lock_guard<std::mutex> lock(hm->mu);
-    const int ns = static_cast<int>((L + R - 1) / R);
+    const int ns = static_cast<int>((L + fs.ri - 1) / fs.ri);
     e = hipEventRecord(hm->ev[0], st);
     if (e == hipSuccess) e = hipStreamWaitEvent(hm->side, hm->ev[0], 0);
     int recorded = 0;
     for (int k = 0; k < ns && e == hipSuccess; ++k) {
-        const int64_t r0 = k * R, r1 = (r0 + R < L) ? r0 + R : L;
+        const int64_t r0 = k * fs.ri, r1 = (r0 + fs.ri < L) ? r0 + fs.ri : L;
         e = index_select_rows(h, hm->side, B, L, q_offset, r0, r1, kbar_cache, bidx, w, f, 2, nbc);
         if (e == hipSuccess) e = hipEventRecord(hm->ev[k + 1], hm->side);
         if (e == hipSuccess) recorded = k + 1;
     }
     for (int k = 0; k < recorded && e == hipSuccess; ++k) {
-        const int64_t r0 = k * R, r1 = (r0 + R < L) ? r0 + R : L;
+        const int64_t s0 = k * fs.ri, s1 = (s0 + fs.ri < L) ? s0 + fs.ri : L;
         e = hipStreamWaitEvent(st, hm->ev[k + 1], 0);
-        if (e == hipSuccess)
+        for (int64_t r0 = s0; r0 < s1 && e == hipSuccess; r0 += fs.ra) {
+            const int64_t r1 = (r0 + fs.ra < s1) ? r0 + fs.ra : s1;
             e = launch_attend_prefill(tables(h), st, B, r1 - r0, r0, L, q_offset, nbc, budget, h->sigma, q, k_cache,
                                       v_cache, bidx, out);
+        }
     }
     if (e != hipSuccess) {      // keep the side stream's launches ahead of the caller's next work
         if (hipEventRecord(hm->ev[kForwardSlicesMax + 1], hm->side) == hipSuccess)

@@ -212,10 +212,11 @@ qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
  * it receives the selection ([B][L][budget]).  Earlier chunks must already be
  * in the caches.  q_offset % 4 == 0.
  * ws: qsa_workspace_size(QSA_OP_FORWARD) bytes.
- * With L >= 16,384 the rows are split into slices (8,192 rows, at most 64
- * slices): index + select of each slice runs on the handle's own stream, and
- * each slice attends on `stream` as soon as its selection is done, so the
- * selection of later slices overlaps the attention of earlier ones.  The call
+ * With L >= 65,536 the rows are split into slices: index + select of each
+ * 32,768-row slice (at most 64 slices) runs on the handle's own stream, and
+ * its rows attend on `stream` in 8,192-row launches as soon as its selection
+ * is done, so the selection of later slices overlaps the attention of earlier
+ * ones.  The call
  * forks from `stream` and joins back into it (events): work enqueued on
  * `stream` afterwards starts after all of it, and the results are bitwise those
  * of the three calls on one stream.  Calls on one handle enqueue their slices

@@ -657,25 +657,29 @@ def test_empty_calls_touch_nothing():
 
 
 def test_forward_sliced_on_two_streams_equals_staged_calls():
-    """qsa_forward on 16,384 rows or more runs index + select slice by slice
-    on the handle's second stream while finished slices attend on the
-    caller's.  With B = 2, two chunks (16,400 rows: two slices; 24,600 rows
-    at q_offset 16,400: a ragged last slice) it is bit-identical to
-    qsa_append + qsa_index_select + qsa_attend on one stream over all rows,
-    and sampled rows match the oracle."""
-    B, L, budget = 2, 41000, 64
+    """qsa_forward on 65,536 rows or more runs index + select in 32,768-row
+    slices on the handle's second stream while finished slices attend in
+    8,192-row launches on the caller's.  With B = 2 and 70,000 rows (three
+    selection slices, the last ragged, and a ragged attention launch), in one
+    call and as two chunks (65,536 rows sliced, then 4,464 at q_offset 65,536
+    in one pass), it is bit-identical to qsa_append + qsa_index_select +
+    qsa_attend on one stream over all rows, and sampled rows match the oracle."""
+    B, L, budget = 2, 70000, 64
     w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 48)
     x, xd = _prefill(w)
     h = Q.Handle(max_ctx=L, budget_blocks=budget)
-    o1, b1, _ = _forward(h, xd, B, L, chunks=[(0, 16400), (16400, L)])
     c = Q.alloc_caches(h, B)
-    o2 = torch.empty_like(o1)
-    b2 = torch.empty_like(b1)
+    o2 = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    b2 = torch.empty((B, L, budget), dtype=torch.int32, device=DEV)
     Q.qsa_append(h, B, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
     Q.qsa_index_select(h, B, L, 0, xd["q_idx"], c["kbar_cache"], b2, Q.workspace(h, Q.QSA_OP_INDEX_SELECT, B, L, 0))
     Q.qsa_attend(h, B, L, 0, xd["q"], c["k_cache"], c["v_cache"], b2, o2)
     torch.cuda.synchronize()
-    assert torch.equal(b1, b2)
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
-    rows = [0, 8191, 8192, 16399, 16400, 24591, 24592, 40975, 40976, 40999]
-    _check_forward(x, f32(o1), b1.cpu().numpy(), O.Params(budget=budget), rows, seqs=(0, 1))
+    del c
+    for chunks in (None, [(0, 65536), (65536, L)]):
+        o1, b1, _ = _forward(h, xd, B, L, chunks=chunks)
+        assert torch.equal(b1, b2), chunks
+        assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), chunks
+        del o1, b1
+    rows = [0, 8191, 8192, 32767, 32768, 65535, 65536, 69631, 69632, 69999]
+    _check_forward(x, f32(o2), b2.cpu().numpy(), O.Params(budget=budget), rows, seqs=(0, 1))
