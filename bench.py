@@ -39,9 +39,9 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # the factors are what the counters read for a plain 1 GiB copy).  The counter
 # summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
 # is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (399616845.9 * 2.000 + 3145803.7 * 1.000) * 1024
+ATTEND_TRAFFIC_BYTES = (385188351.2 * 2.000 + 3145797.6 * 1.000) * 1024
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "7e1bf619614ccd03cf208530321c93490364c8e3e38f14b34632987342f6cff4",
+    "k_attend.hip": "d83b0d5ef1d82e8850dcf340c511e7c1fc497fda95611a191d20551b14b5465d",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }
@@ -775,7 +775,7 @@ def main():
             "index_select_mfma_frac": idx_tfs / MFMA_BF16_PEAK_TFS,
         },
         "roofline": {
-            "kernel": "attend_prefill_kernel (qsa_attend)",
+            "kernel": "attend_prefill_kernel (qsa_attend: one launch over all rows)",
             "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "traffic": None if tr_bytes is None else tr_bytes / (t_attn * 1e-3) / 1e9,
