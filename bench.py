@@ -77,9 +77,8 @@ def setup_prefill(w):
 
 
 def prefill_forward(s, ev):
-    """One prefill as the library runs it: qsa_forward (append, then index +
-    select on the handle's second stream slice by slice while the slices
-    attend on this one)."""
+    """One prefill as the library runs it: qsa_forward (append, fused index +
+    select, then the attention in launches of 4,096 rows)."""
     x, h, c, L = s["x"], s["h"], s["c"], s["L"]
     ev[0].record()
     Q.qsa_forward(h, 1, L, 0, x["q"], x["k"], x["v"], x["q_idx"], x["k_idx"], c["k_cache"], c["v_cache"],

@@ -6,7 +6,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-#include <mutex>
 #include <new>
 #include <vector>
 
@@ -68,12 +67,6 @@ hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, cons
 
 using namespace qsa;
 
-// qsa_forward splits a long prefill into row slices: the fused index + select
-// of slice k+1 runs on the handle's second stream while slice k attends on the
-// caller's stream (the first is bound by the vector ALUs and matrix cores, the
-// second by memory).  At most this many slices per call.
-constexpr int kForwardSlicesMax = 64;
-
 struct qsa_handle {
     qsa_params p;
     int cap;            // candidate list length per query of the fused index + select stage
@@ -81,9 +74,6 @@ struct qsa_handle {
     float *d_cos;
     float *d_sin;
     float sigma;        // softmax scale of the core logits
-    hipStream_t side;   // the sliced prefill's index + select stream (default priority)
-    hipEvent_t ev[kForwardSlicesMax + 2];   // fork, one per slice, join
-    std::mutex mu;      // one sliced prefill enqueues its events at a time
 };
 
 namespace {
@@ -222,21 +212,6 @@ hipError_t run_index_select(const qsa_handle *h, hipStream_t st, int32_t B, int6
     return e;
 }
 
-// Slices of a sliced prefill: index + select in slices of ri rows (at least
-// 32,768 = 512 work-groups of the fused kernel, enough to fill the device even
-// deep in a 1M context), attention in slices of ra rows (8,192: the finer the
-// attention slices, the sooner each selection slice is consumed).  ri = 0: one
-// pass on the caller's stream.
-struct ForwardSlices { int64_t ri, ra; };
-ForwardSlices forward_slices(int64_t L) {
-    constexpr int64_t kAttendRows = 8192, kSelectRows = 32768;
-    if (L < 2 * kSelectRows) return {0, 0};     // fewer than two selection slices: nothing to overlap
-    int64_t ri = kSelectRows;
-    if ((L + ri - 1) / ri > kForwardSlicesMax)
-        ri = ((L + kForwardSlicesMax - 1) / kForwardSlicesMax + kAttendRows - 1) / kAttendRows * kAttendRows;
-    return {ri, kAttendRows};
-}
-
 // The batch is a grid dimension (y or z) of every QSA kernel: at most 65,535.
 constexpr int32_t kMaxBatch = 65535;
 
@@ -315,9 +290,6 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->d_sin), n * sizeof(float));
     if (e == hipSuccess) e = hipMemcpy(h->d_cos, hc.data(), n * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(h->d_sin, hs.data(), n * sizeof(float), hipMemcpyHostToDevice);
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking);
-    for (int i = 0; i < kForwardSlicesMax + 2 && e == hipSuccess; ++i)
-        e = hipEventCreateWithFlags(&h->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) {
         qsa_destroy(h);
         return hip_fail(e);
@@ -329,10 +301,6 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
 void qsa_destroy(qsa_handle *h) {
     if (!h) return;
     DeviceGuard guard(h->device);
-    if (h->side) (void)hipStreamSynchronize(h->side);
-    for (int i = 0; i < kForwardSlicesMax + 2; ++i)
-        if (h->ev[i]) (void)hipEventDestroy(h->ev[i]);
-    if (h->side) (void)hipStreamDestroy(h->side);
     if (h->d_cos) (void)hipFree(h->d_cos);
     if (h->d_sin) (void)hipFree(h->d_sin);
     delete h;
@@ -472,51 +440,11 @@ qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, 
     hipError_t e = launch_kv_pool(tables(h), st, B, L, q_offset, nbc, k, v, k_idx, k_cache, v_cache, kbar_cache,
                                   kpend, true, true);
     if (e == hipSuccess) e = launch_kpend_store(st, B, L, q_offset, k_idx, kpend);
-    const ForwardSlices fs = forward_slices(L);
-    const int budget = h->p.budget_blocks;
-    if (fs.ri == 0) {
-        if (e == hipSuccess) e = run_index_select(h, st, B, L, q_offset, q_idx, kbar_cache, bidx, w, f);
-        if (e == hipSuccess)
-            e = launch_attend_prefill(tables(h), st, B, L, 0, L, q_offset, nbc, budget, h->sigma, q, k_cache, v_cache,
-                                      bidx, out);
-        return e == hipSuccess ? QSA_OK : hip_fail(e);
-    }
-    // Sliced: rotate every indexer query here, then fork to the side stream,
-    // which runs slice after slice of index + select and records an event
-    // after each; each attention slice runs here once the event of the
-    // selection slice holding its rows has fired.  The last wait (or, after an
-    // error, the join event) makes every side-stream launch precede whatever
-    // the caller enqueues next.
-    if (e == hipSuccess) e = launch_qidx_rotate(tables(h), st, B, L, q_offset, nullptr, q_idx,
-                                                 reinterpret_cast<bf16_t *>(w + f.qrot));
-    if (e != hipSuccess) return hip_fail(e);
-    qsa_handle *hm = const_cast<qsa_handle *>(h);     // the stream, events and lock only
-    std::lock_guard<std::mutex> lock(hm->mu);
-    const int ns = static_cast<int>((L + fs.ri - 1) / fs.ri);
-    e = hipEventRecord(hm->ev[0], st);
-    if (e == hipSuccess) e = hipStreamWaitEvent(hm->side, hm->ev[0], 0);
-    int recorded = 0;
-    for (int k = 0; k < ns && e == hipSuccess; ++k) {
-        const int64_t r0 = k * fs.ri, r1 = (r0 + fs.ri < L) ? r0 + fs.ri : L;
-        e = index_select_rows(h, hm->side, B, L, q_offset, r0, r1, kbar_cache, bidx, w, f, 2, nbc);
-        if (e == hipSuccess) e = hipEventRecord(hm->ev[k + 1], hm->side);
-        if (e == hipSuccess) recorded = k + 1;
-    }
-    for (int k = 0; k < recorded && e == hipSuccess; ++k) {
-        const int64_t s0 = k * fs.ri, s1 = (s0 + fs.ri < L) ? s0 + fs.ri : L;
-        e = hipStreamWaitEvent(st, hm->ev[k + 1], 0);
-        for (int64_t r0 = s0; r0 < s1 && e == hipSuccess; r0 += fs.ra) {
-            const int64_t r1 = (r0 + fs.ra < s1) ? r0 + fs.ra : s1;
-            e = launch_attend_prefill(tables(h), st, B, r1 - r0, r0, L, q_offset, nbc, budget, h->sigma, q, k_cache,
-                                      v_cache, bidx, out);
-        }
-    }
-    if (e != hipSuccess) {      // keep the side stream's launches ahead of the caller's next work
-        if (hipEventRecord(hm->ev[kForwardSlicesMax + 1], hm->side) == hipSuccess)
-            (void)hipStreamWaitEvent(st, hm->ev[kForwardSlicesMax + 1], 0);
-        return hip_fail(e);
-    }
-    return QSA_OK;
+    if (e == hipSuccess) e = run_index_select(h, st, B, L, q_offset, q_idx, kbar_cache, bidx, w, f);
+    if (e == hipSuccess)
+        e = launch_attend_prefill(tables(h), st, B, L, 0, L, q_offset, nbc, h->p.budget_blocks, h->sigma, q, k_cache,
+                                  v_cache, bidx, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 
 qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len, int64_t ctx_bound,

@@ -37,9 +37,7 @@
  *   - The batch B is 1 .. 65535 (QSA_ERR_SHAPE otherwise).
  *   - Inputs must be finite; non-finite values are not detected.
  *   - Calls that share a cache must be ordered (same stream or explicit
- *     events); the handle's parameters and tables are immutable and it may be
- *     shared by threads (qsa_forward serialises its use of the handle's
- *     stream and events with a lock).
+ *     events); the handle itself is immutable and may be shared by threads.
  *
  * Token-major input layouts (per call, positions q_offset .. q_offset+L-1):
  *   q      bf16 [B][L][24][256]     query heads
@@ -129,14 +127,12 @@ void qsa_default_params(qsa_params *p);
 /* Validate *params, build the fp32 cos/sin tables of positions 0..max_ctx-1 on
  * the host (fp64 libm cos/sin of position * frequency, rounded once to fp32)
  * and upload them to `device`.  The handle owns that device memory (2 x
- * max_ctx x 32 x 4 bytes), one HIP stream (default priority, non-blocking)
- * and 66 events for qsa_forward's sliced prefill, until qsa_destroy.  Returns QSA_ERR_NULL,
+ * max_ctx x 32 x 4 bytes) until qsa_destroy.  Returns QSA_ERR_NULL,
  * QSA_ERR_UNSUPPORTED, QSA_ERR_SHAPE or QSA_ERR_HIP on failure (*out = NULL). */
 qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out);
 
-/* Release the handle, its tables, stream and events (after the handle's own
- * stream has drained).  NULL is a no-op.  Not stream-ordered: the caller must
- * make sure no enqueued call still uses the handle. */
+/* Release the handle and its tables.  NULL is a no-op.  Not stream-ordered:
+ * the caller must make sure no enqueued call still uses the handle. */
 void qsa_destroy(qsa_handle *h);
 
 /* Copy the handle's parameters to *out.  Host only. */
@@ -211,16 +207,7 @@ qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
  * for positions q_offset .. q_offset+L-1.  block_idx may be NULL; when given
  * it receives the selection ([B][L][budget]).  Earlier chunks must already be
  * in the caches.  q_offset % 4 == 0.
- * ws: qsa_workspace_size(QSA_OP_FORWARD) bytes.
- * With L >= 65,536 the rows are split into slices: index + select of each
- * 32,768-row slice (at most 64 slices) runs on the handle's own stream, and
- * its rows attend on `stream` in 8,192-row launches as soon as its selection
- * is done, so the selection of later slices overlaps the attention of earlier
- * ones.  The call
- * forks from `stream` and joins back into it (events): work enqueued on
- * `stream` afterwards starts after all of it, and the results are bitwise those
- * of the three calls on one stream.  Calls on one handle enqueue their slices
- * one after another (a lock inside the handle). */
+ * ws: qsa_workspace_size(QSA_OP_FORWARD) bytes. */
 qsa_status qsa_forward(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
                        const uint16_t *q, const uint16_t *k, const uint16_t *v,
                        const uint16_t *q_idx, const uint16_t *k_idx,

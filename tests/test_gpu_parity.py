@@ -656,14 +656,12 @@ def test_empty_calls_touch_nothing():
         assert torch.equal(c[k], before[k]), k
 
 
-def test_forward_sliced_on_two_streams_equals_staged_calls():
-    """qsa_forward on 65,536 rows or more runs index + select in 32,768-row
-    slices on the handle's second stream while finished slices attend in
-    8,192-row launches on the caller's.  With B = 2 and 70,000 rows (three
-    selection slices, the last ragged, and a ragged attention launch), in one
-    call and as two chunks (65,536 rows sliced, then 4,464 at q_offset 65,536
-    in one pass), it is bit-identical to qsa_append + qsa_index_select +
-    qsa_attend on one stream over all rows, and sampled rows match the oracle."""
+def test_forward_long_equals_staged_calls():
+    """A 70,000-row prefill with B = 2 (the attention in 4,096-row launches,
+    the last one ragged; index + select in 65,536-row launches), in one
+    qsa_forward call and as two chunks (65,536 rows, then 4,464 at q_offset
+    65,536), is bit-identical to qsa_append + qsa_index_select + qsa_attend
+    over all rows, and sampled rows match the oracle."""
     B, L, budget = 2, 70000, 64
     w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 48)
     x, xd = _prefill(w)
