@@ -34,21 +34,24 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 
-# HBM-side bytes of one attend_prefill_kernel launch on the 262,144-token
-# workload, read by rocprofv3 --pmc (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB;
-# the factors are what the counters read for a plain 1 GiB copy).  The counter
-# summary is profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure
-# is reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (385188351.2 * 2.000 + 3145797.6 * 1.000) * 1024
+# HBM-side bytes of the attention over the 262,144-token workload (64 launches
+# of attend_prefill_kernel, 4,096 rows each), read by rocprofv3 --pmc
+# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB per launch, mean of the 192
+# launches of three passes; the factors are what the counters read for a plain
+# 1 GiB copy).  The counter summary is
+# profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure is
+# reported only while the kernel's sources hash to the digests it was taken with.
+ATTEND_TRAFFIC_BYTES = (3939544.6 * 2.000 + 49152.0 * 1.000) * 1024 * 64
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "d83b0d5ef1d82e8850dcf340c511e7c1fc497fda95611a191d20551b14b5465d",
+    "k_attend.hip": "0a2f3b528cb1437049ebd20b262c0011ebbf35eec9cdece7cf0def5da3ba1526",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }
 
 
 def attend_traffic_bytes():
-    """Counter-measured bytes per launch, or None if the kernel changed since."""
+    """Counter-measured HBM-side bytes of the attention over the workload (all
+    its launches), or None if the kernel changed since."""
     import hashlib
     for name, digest in ATTEND_TRAFFIC_SOURCES.items():
         with open(os.path.join(ROOT, "block_sparse_long_qsa_amd", "csrc", name), "rb") as f:
@@ -774,11 +777,11 @@ def main():
             "index_select_mfma_frac": idx_tfs / MFMA_BF16_PEAK_TFS,
         },
         "roofline": {
-            "kernel": "attend_prefill_kernel (qsa_attend: one launch over all rows)",
+            "kernel": "attend_prefill_kernel (qsa_attend: %d launches of up to 4,096 rows)" % ((L + 4095) // 4096),
             "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": attn_gbs / HBM_PEAK_GBS,
             "traffic": None if tr_bytes is None else tr_bytes / (t_attn * 1e-3) / 1e9,
-            "traffic_bytes_per_launch": tr_bytes,
+            "traffic_bytes_per_pass": tr_bytes,
             "algorithmic_bytes": attn_bytes, "gathered_tokens": sum_T, "avg_ms": float(t_attn),
         },
     }
