@@ -199,6 +199,56 @@ def test_pooled_score_equals_mean_of_token_logits():
         kraw[4:8].astype(np.float64), 4, w).T).mean(axis=1).sum()) > 1e-3
 
 
+def _bf16_ulp(x):
+    """Spacing of bf16 values at |x| (8 significand bits), floored at 2^-16."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -8)))
+    return 2.0 ** (e - 7)
+
+
+def _kbar_reference(kraw_bits, key_pos, w):
+    """Independent fp64 pooled key: the fp32 token-order mean of each complete
+    block's four raw bf16 keys (written out here, not the oracle's pooling),
+    rotated through complex multiplication at key_pos(b)."""
+    raw = (kraw_bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    nb = raw.shape[0] // 4
+    acc = raw[0:4 * nb:4].copy()
+    for t in (1, 2, 3):
+        acc = np.float32(acc + raw[t:4 * nb:4])
+    mean = np.float32(acc * np.float32(0.25)).astype(np.float64)
+    pos = key_pos(np.arange(nb))[:, None].astype(np.float64)
+    return _rot_complex(mean, pos, w[None, :])
+
+
+def _within_one_ulp(got, ref):
+    return bool(np.all(np.abs(got.astype(np.float64) - ref) <= _bf16_ulp(ref)))
+
+
+@pytest.mark.parametrize("yarn", [1.0, 4.0])
+def test_indexer_keys_pooled_then_rotated_at_block_start(yarn):
+    """oracle.indexer_keys itself: every k̄[b] is within one bf16 ulp of the
+    fp64 rotation, at the block-start position 4b, of the fp32 token-order mean
+    of the block's four raw keys ([PKR] "QSA: ...": compression before the
+    positional encoding, one block-start position per pooled key).  A ragged
+    tail of 3 tokens yields no key.  The same check fails for the plausible
+    slips: rotating at b, at the block's last token 4b+3, or not at all."""
+    rng = np.random.default_rng(21)
+    p = O.Params(yarn_factor=yarn)
+    if yarn == 1.0:   # closed form, independent of the oracle's frequency code
+        w = np.array([p.rope_theta ** (-2.0 * j / 64.0) for j in range(32)])
+    else:             # the YaRN frequencies are pinned by their hand-derived bands
+        w = O.inv_freq(p)
+    n_blocks = 700
+    kb = O.f32_to_bf16_bits(rng.standard_normal((4 * n_blocks + 3, 128)).astype(np.float32))
+    got = O.indexer_keys(kb, p)
+    assert got.shape == (n_blocks, 128)
+    assert np.array_equal(O.bf16_round(got), got)          # bf16 values
+    assert _within_one_ulp(got, _kbar_reference(kb, lambda b: 4 * b, w))
+    # non-rotary dims are the plain mean, rounded once
+    assert _within_one_ulp(got[:, 64:], _kbar_reference(kb, lambda b: 4 * b, w)[:, 64:])
+    for wrong in (lambda b: b, lambda b: 4 * b + 3, lambda b: 0 * b):
+        assert not _within_one_ulp(got, _kbar_reference(kb, wrong, w))
+
+
 def test_token_level_indexer_brute_force():
     """r = 1: every key rotated at its own position (fp64 complex arithmetic on
     the bf16 inputs), logits against the query rotated at p, ReLU, sum over
