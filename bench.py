@@ -9,10 +9,14 @@ One step = one pass of the whole hot path:
 Inputs are seeded synthetic tensors already resident in HBM when timing starts.
 
 Printed: ONE JSON line.  `value` is prefill tokens/s at 262,144 tokens; decode
-tokens/s sits beside it.  `roofline` covers the dominant kernel (the sparse
-attention gather) with its duration from HIP events recorded on the stream the
-kernel runs on; `cpu_baseline` times the CPU oracle on a bounded sample of the
-same prefill rows (rank 0, N = 1 only).
+tokens/s sits beside it.  `roofline` covers the dominant kernel, the sparse
+attention (attend_prefill_kernel), with its duration from HIP events recorded
+on the stream the kernel runs on: its algorithmic FLOP/s against the bf16 MFMA
+peak, and beside it the rate of its gathers against gather ceilings measured in
+the same run (libqsa_probe.so) and its compulsory HBM bytes against the HBM
+peak.  `cpu_baseline` times the CPU oracle on a bounded sample of the same
+prefill rows (all threads and one thread), and `decode.cpu_baseline` on the
+decode query of two of the 64 sequences (rank 0, N = 1 only).
 """
 from __future__ import annotations
 
@@ -191,10 +195,72 @@ def measured_ceilings():
             "how": "4 GiB device copy (read + write bytes) and 8192^3 bf16 torch.matmul"}
 
 
+def gather_ceilings(sp, reps=3):
+    """Rates at which this GPU gathers 2 KiB micro-blocks, measured in this run
+    with the benchmark's probe (libqsa_probe.so: the attention walk's loads with
+    no arithmetic, both KV groups, 8 list entries per step):
+      * l2_resident: every id in the first 128 blocks (1 MiB of K~/V), at the
+        probe's full occupancy -- the ceiling of any gather;
+      * no_reuse: ids uniform over the workload's whole cache, at the
+        attention's occupancy (one wave per SIMD) -- random gathers that the
+        L2 cannot serve;
+      * attention_stream: the attention's own selection lists in its own
+        launch shape (4,096 rows, group-major) -- its access stream alone.
+    Returns {name: {"ms", "GBs"}} with GB/s of gathered bytes."""
+    from block_sparse_long_qsa_amd import probe
+    kc, vc = sp["c"]["k_cache"], sp["c"]["v_cache"]
+    nblk = kc.shape[2]
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda")
+
+    def timed(idx, **kw):
+        probe.gather(kc, vc, idx, sink, **kw)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e = _events(2)
+            e[0].record()
+            probe.gather(kc, vc, idx, sink, **kw)
+            e[1].record()
+            torch.cuda.synchronize()
+            ts.append(e[0].elapsed_time(e[1]))
+        ms = float(np.median(ts))
+        nbytes = idx.shape[0] * 2 * (idx.shape[1] // 8 * 8) * 4096
+        return {"ms": ms, "GBs": nbytes / (ms * 1e-3) / 1e9}
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    res = {}
+    idx = torch.randint(0, 128, (65536, 512), generator=g, dtype=torch.int32, device="cuda")
+    res["l2_resident"] = timed(idx, pad_kib=0)
+    idx = torch.randint(0, nblk, (65536, 512), generator=g, dtype=torch.int32, device="cuda")
+    res["no_reuse"] = timed(idx, pad_kib=96)
+    del idx
+    res["attention_stream"] = timed(sp["bidx"][0], pad_kib=96, launch_rows=4096)
+    torch.cuda.empty_cache()
+    res["how"] = ("probe gathers (libqsa_probe.so), 16-byte loads, 8 list entries per step, K~ and V of both "
+                  "groups; GB/s of gathered bytes")
+    return res
+
+
+def _cpu_info():
+    """The host CPU's model name and the threads this process may use."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
-    """Time the oracle on an evenly spaced sample of the prefill's rows."""
+    """Time the oracle on an evenly spaced sample of the prefill's rows (all the
+    threads BLAS uses), then on a fixed 8-row sample with one thread."""
     import oracle as O
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     x = s_pref["x"]
     L = w.seq_len
     t0 = time.time()
@@ -207,6 +273,7 @@ def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
     rows = np.arange(stride - 1, L, stride)
     t0 = time.time()
     lay = O.LayerOracle(host["k"], host["v"], host["k_idx"], p)
+    t_pool = time.time() - t0
     done = []
     outs, sels = [], []
     for r in rows:
@@ -218,6 +285,13 @@ def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
             break
     dt = time.time() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    # the same oracle rows with one thread: every 32,768-th row (8 rows)
+    fixed = np.arange(L // 8 - 1, L, L // 8)
+    with threadpool_limits(limits=1):
+        t1 = time.time()
+        for r in fixed:
+            lay.row(int(r), synth.bf16_bits(x["q"][0, r]), synth.bf16_bits(x["q_idx"][0, r]))
+        dt1 = time.time() - t1
     # parity of the GPU rows against the oracle rows just computed
     gpu_out = s_pref["out"][0, done].float().cpu().numpy()
     gpu_sel = s_pref["bidx"][0, done].cpu().numpy()
@@ -226,10 +300,48 @@ def cpu_baseline(s_pref, w, n_rows=None, budget_s=20.0):
     return {
         "value": len(done) / dt, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
         "sample": "%d prefill rows of the L=%d sequence, every %d-th row (rows %d..%d), incl. pooling all %d "
-                  "blocks; host copy of inputs %.1f s not counted" % (len(done), L, stride, done[0], done[-1],
-                                                                     L // 4, t_copy),
+                  "blocks (%.1f s); host copy of inputs %.1f s not counted" % (
+                      len(done), L, stride, done[0], done[-1], L // 4, t_pool, t_copy),
+        "one_core": {"value": len(fixed) / dt1, "unit": "tok/s", "threads": 1,
+                     "sample": "prefill rows %s (every %d-th row), pooling not counted" % (
+                         ",".join(str(int(r)) for r in fixed), L // 8)},
+        **_cpu_info(),
         "parity_on_sample": {"rows": len(done), "max_abs_err": max_err, "selection_sym_diff": sel_diff},
     }
+
+
+def cpu_baseline_decode(sd, wd, n_seq=2):
+    """The oracle's decode rows for the first n_seq sequences of the decode
+    workload (inputs regenerated from the same seeds), timed per query with all
+    BLAS threads (pooling the cached keys is a per-sequence set-up, timed
+    apart), and their parity with the GPU's decode step."""
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    x = synth.decode_inputs(wd, "cuda", batch=n_seq)
+    p = O.Params(budget=wd.budget, yarn_factor=wd.yarn_factor)
+    ctx = wd.seq_len
+    t_pool = t_row = 0.0
+    max_err, sel_diff = 0.0, 0
+    for b in range(n_seq):
+        host = {n: synth.bf16_bits(x[n][b]) for n in ("k", "v", "k_idx")}
+        t0 = time.time()
+        lay = O.LayerOracle(host["k"], host["v"], host["k_idx"], p)
+        t1 = time.time()
+        o, sel, _ = lay.row(ctx, synth.bf16_bits(x["q"][b, 0]), synth.bf16_bits(x["q_idx"][b, 0]))
+        t2 = time.time()
+        t_pool += t1 - t0
+        t_row += t2 - t1
+        g = sd["out"][b, 0].float().cpu().numpy()
+        gs = sd["bidx"][b, 0].cpu().numpy()
+        max_err = max(max_err, float(np.max(np.abs(g - o))))
+        sel_diff += len(set(gs[gs >= 0].tolist()) ^ set(sel[sel >= 0].tolist()))
+    del x
+    torch.cuda.empty_cache()
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n_seq / t_row, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": "the decode query of sequences 0..%d of %d (context %d each); pooling their cached keys "
+                      "%.1f s not counted" % (n_seq - 1, wd.batch, ctx, t_pool),
+            "parity_on_sample": {"seqs": n_seq, "max_abs_err": max_err, "selection_sym_diff": sel_diff}}
 
 
 def qsa_prefill_1m_ms(steps):
@@ -747,7 +859,13 @@ def main():
 
     L = wp.seq_len
     attn_bytes, sum_T = attention_bytes(L, wp.budget)
-    attn_gbs = attn_bytes / (t_attn * 1e-3) / 1e9
+    attn_flops = 24576 * sum_T                 # 2 FLOP x 2 products x 24 heads x 256 dims per gathered token
+    attn_tfs = attn_flops / (t_attn * 1e-3) / 1e12
+    gath_bytes = 2048 * sum_T                  # K~ and V of both KV groups per gathered token
+    gath_gbs = gath_bytes / (t_attn * 1e-3) / 1e9
+    # compulsory HBM bytes of the attention pass: the K~/V caches once, q read,
+    # output written and the selection read once
+    comp_bytes = L * (2048 + 2 * 24 * 256 * 2 + 4 * wp.budget)
     tr_bytes = attend_traffic_bytes()
     idx_tfs = indexer_flops(L) / (t_isel * 1e-3) / 1e12
     res = {
@@ -778,11 +896,15 @@ def main():
         },
         "roofline": {
             "kernel": "attend_prefill_kernel (qsa_attend: %d launches of up to 4,096 rows)" % ((L + 4095) // 4096),
-            "bound": "hbm", "achieved": attn_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": attn_gbs / HBM_PEAK_GBS,
+            "bound": "mfma", "achieved": attn_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+            "frac": attn_tfs / MFMA_BF16_PEAK_TFS,
             "traffic": None if tr_bytes is None else tr_bytes / (t_attn * 1e-3) / 1e9,
+            "traffic_unit": "GB/s, HBM side (rocprofv3 FETCH_SIZE/WRITE_SIZE scaled by a copy kernel's reading)",
             "traffic_bytes_per_pass": tr_bytes,
-            "algorithmic_bytes": attn_bytes, "gathered_tokens": sum_T, "avg_ms": float(t_attn),
+            "algorithmic_flops": attn_flops, "gathered_tokens": sum_T, "avg_ms": float(t_attn),
+            "gather": {"achieved_GBs": gath_gbs, "gathered_bytes": gath_bytes},
+            "compulsory_hbm": {"bytes": comp_bytes, "GBs": comp_bytes / (t_attn * 1e-3) / 1e9,
+                               "frac_of_hbm_peak": comp_bytes / (t_attn * 1e-3) / 1e9 / HBM_PEAK_GBS},
         },
     }
     if sd:
@@ -794,13 +916,22 @@ def main():
     if not args.no_ceilings:
         ceil = measured_ceilings()
         res["measured_ceilings"] = ceil
-        res["roofline"]["frac_of_measured_copy"] = attn_gbs / ceil["copy_GBs"]
+        gc = gather_ceilings(sp)
+        ceil["gather"] = gc
+        gr = res["roofline"]["gather"]
+        gr["l2_resident_ceiling_GBs"] = gc["l2_resident"]["GBs"]
+        gr["frac_of_l2_resident_ceiling"] = gath_gbs / gc["l2_resident"]["GBs"]
+        gr["no_reuse_GBs"] = gc["no_reuse"]["GBs"]
+        gr["own_stream_without_arithmetic_ms"] = gc["attention_stream"]["ms"]
+        gr["kernel_ms_over_own_stream_ms"] = float(t_attn) / gc["attention_stream"]["ms"]
         res["prefill"]["index_select_frac_of_measured_gemm"] = idx_tfs / ceil["gemm_bf16_TFs"]
         if sd:
             res["decode"]["roofline"]["frac_of_measured_copy"] = res["decode"]["roofline"]["achieved"] / ceil["copy_GBs"]
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         res["cpu_baseline"] = cpu_baseline(sp, wp, n_rows=args.cpu_rows)
+        if sd:
+            res["decode"]["cpu_baseline"] = cpu_baseline_decode(sd, wd)
     print(json.dumps(res), flush=True)
 
 

@@ -16,18 +16,20 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqsa.so")
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")     # benchmark-only gather probe, not the QSA boundary
 ARCH = "gfx950"
 
 HIP_SOURCES = ["qsa_api.hip", "k_prologue.hip", "k_indexer.hip", "k_select.hip", "k_attend.hip", "k_decode.hip", "k_gdn.hip",
                "k_train.hip"]
 CPP_SOURCES = ["qsa_tables.cpp"]
+PROBE_SOURCES = ["probe_gather.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+             "-Wall", "-Werror", "-Wno-unused-function", "-Wno-unused-variable",
              "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-CPP_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fno-builtin", "-ffp-contract=off"]
+CPP_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-fno-builtin", "-ffp-contract=off", "-Wall", "-Werror"]
 
 
 def _run(cmd):
@@ -48,8 +50,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     for src in CPP_SOURCES:
         obj = os.path.join(OBJ, src + ".o")
         jobs_list.append((["g++"] + CPP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
+    probe_jobs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(OBJ, src + ".o")
+        probe_jobs.append(([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        outs = list(ex.map(lambda j: _run(j[0]), jobs_list))
+        outs = list(ex.map(lambda j: _run(j[0]), jobs_list + probe_jobs))
     if verbose:
         for o in outs:
             if o.strip():
@@ -57,6 +63,9 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + [o for _, o in jobs_list])
     os.replace(tmp, LIB)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + [o for _, o in probe_jobs])
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -81,14 +81,17 @@ __device__ __forceinline__ void attend_chunks(const bf16x8 (&qf)[8], const bf16_
         cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
         cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
         const float m_new = fmaxf(st.m, cmax);
-        const float alpha = exp2f((st.m - m_new) * c2);
+        // While every token so far was masked m_new is -inf; 0 then serves as
+        // the reference so that alpha and p come out 0 instead of NaN.
+        const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = exp2f((st.m - m_ref) * c2);
         st.m = m_new;
         uint32_t pw[4];
         float psum = 0.f;
         for (int t = 0; t < 2; ++t) {
             float p[4];
             for (int j = 0; j < 4; ++j) {
-                p[j] = exp2f((sc[t][j] - m_new) * c2);
+                p[j] = exp2f((sc[t][j] - m_ref) * c2);
             }
             pw[2 * t] = pack_bf16x2(p[0], p[1]);
             pw[2 * t + 1] = pack_bf16x2(p[2], p[3]);

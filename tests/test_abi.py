@@ -122,3 +122,23 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="device tensor"):
         Q._bf(torch.zeros(16, dtype=torch.bfloat16), "q")
     assert Q._ptr(None) is None
+
+
+def test_probe_library_exports_its_header_and_checks_arguments():
+    """The benchmark's gather probe (include/qsa_probe.h, libqsa_probe.so):
+    every declared symbol is exported, the binding passes the declared number
+    of arguments, and bad arguments are refused before any HIP call."""
+    from block_sparse_long_qsa_amd import probe
+    src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "qsa_probe.h")).read(), flags=re.S)
+    decls = re.findall(r"\b(qsa_[a-z_]+)\s*\(([^;{]*?)\)\s*;", src)
+    assert [d[0] for d in decls] == ["qsa_probe_gather"]
+    lib = probe.lib()
+    assert len(lib.qsa_probe_gather.argtypes) == decls[0][1].count(",") + 1
+    ok = dict(stream=None, k=16, v=16, gs=2048, nb=1, idx=16, rows=1, ll=8, lr=4096, step=8, pad=0, sink=16)
+    def call(**kw):
+        a = {**ok, **kw}
+        return lib.qsa_probe_gather(a["stream"], a["k"], a["v"], a["gs"], a["nb"], a["idx"], a["rows"], a["ll"],
+                                    a["lr"], a["step"], a["pad"], a["sink"])
+    for kw in (dict(k=None), dict(v=None), dict(idx=None), dict(sink=None), dict(rows=-1), dict(ll=-1),
+               dict(lr=0), dict(nb=0), dict(step=3), dict(step=16), dict(pad=32)):
+        assert call(**kw) == 1, kw

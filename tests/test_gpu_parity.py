@@ -236,6 +236,44 @@ def test_attend_with_oracle_selection():
     check_out(f32(out[0]), ref, "attend")
 
 
+def test_attend_skips_leading_invalid_entries():
+    """qsa_attend skips block_idx entries outside [0, floor(p/4)), also when
+    they fill the whole first chunks of a row's walk (12 leading entries of -1
+    or ids >= floor(p/4)); the rest of the list and the own block are attended
+    as the oracle attends them.  Rows whose every entry is invalid attend their
+    own block alone."""
+    B, L, budget = 1, 600, 32
+    w = synth.Workload("t", "prefill", B, L, budget, 4, "random", 41)
+    x, xd = _prefill(w)
+    rng = np.random.default_rng(41)
+    sel = np.full((L, budget), -1, dtype=np.int32)
+    for i in range(L):
+        o = i // 4
+        bad = np.where(rng.random(12) < 0.5, -1, o + rng.integers(0, 50, 12)).astype(np.int32)
+        if i % 7 == 0:                                   # nothing valid at all
+            sel[i] = np.where(rng.random(budget) < 0.5, -1, o + rng.integers(0, 9, budget))
+            continue
+        n_ok = min(o, budget - 12)
+        ok = np.sort(rng.choice(o, n_ok, replace=False)).astype(np.int32) if n_ok > 0 else np.zeros(0, np.int32)
+        row = np.concatenate([bad, ok])
+        sel[i, :row.size] = row[:budget]
+    h = Q.Handle(max_ctx=1024, budget_blocks=budget)
+    c = Q.alloc_caches(h, B)
+    Q.qsa_append(h, B, L, 0, xd["k"], xd["v"], xd["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"])
+    out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+    Q.qsa_attend(h, B, L, 0, xd["q"], c["k_cache"], c["v_cache"], torch.from_numpy(sel[None]).to(DEV), out)
+    torch.cuda.synchronize()
+    o = f32(out[0])
+    assert np.isfinite(o).all()
+    p = O.Params(budget=budget)
+    lay = oracle_layer(x, 0, p)
+    for i in range(0, L, 3):
+        # the entries the walk reads are the first min(floor(p/4), budget); only ids in [0, floor(p/4)) count
+        n_read = min(i // 4, budget)
+        ref = lay.row_reused(i, bits(x["q"][0, i]), sel[i, :n_read], i)
+        check_out(o[i], ref, "row %d" % i)
+
+
 # ---------------------------------------------------------------- forward
 def _check_forward(x, out, bidx, p, rows, seqs=(0,), q_offset=0):
     n_swapped = 0
@@ -470,6 +508,36 @@ def test_decode_reuse_selection_position_bounds():
         Q.qsa_decode_reuse(h, B, cache_len, cache_len, 1024, xd["q"], new["k"], new["v"], new["k_idx"],
                            c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], sel, outs["neg"], ws)
     assert e.value.status == 5
+
+
+def test_decode_reuse_selection_position_below_every_id():
+    """A reused selection whose ids all lie at or past the block of sel_pos: the
+    first chunks of every split's walk are wholly masked, and the step attends
+    only the tail from sel_pos's own block to p, as the oracle's reused row."""
+    budget, n, B = 32, 1200, 1
+    w = synth.Workload("t", "decode", B, n, budget, 4, "random", 43)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    x, out0, bidx0, c = _decode_setup(w, [n], h)
+    xd = _to(x)
+    new = {k: xd[k][:, n:n + 1].contiguous() for k in ("k", "v", "k_idx")}
+    cache_len = torch.tensor([n], dtype=torch.int32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_DECODE, B, 1, n)
+    rng = np.random.default_rng(43)
+    sel_np = np.sort(rng.choice(np.arange(200, 300), budget, replace=False)).astype(np.int32)[None]
+    sel = torch.from_numpy(sel_np).to(DEV)
+    p = O.Params(budget=budget)
+    lay = oracle_layer(x, 0, p, n_keys=n + 1)
+    for sp in (4 * 200, 4 * 100 + 3, 4 * 40 + 2):
+        assert sp // 4 <= sel_np.min()
+        o = torch.empty_like(out0)
+        Q.qsa_decode_reuse(h, B, cache_len, torch.tensor([sp], dtype=torch.int32, device=DEV), n, xd["q"],
+                           new["k"], new["v"], new["k_idx"], c["k_cache"], c["v_cache"], c["kbar_cache"],
+                           c["kpend"], sel, o, ws)
+        torch.cuda.synchronize()
+        got = f32(o[0, 0])
+        assert np.isfinite(got).all(), "sel_pos %d" % sp
+        ref = lay.row_reused(n, bits(x["q"][0, 0]), sel_np[0], sp)
+        check_out(got, ref, "sel_pos %d" % sp)
 
 
 # ---------------------------------------------------------------- token-level indexer (r = 1)
