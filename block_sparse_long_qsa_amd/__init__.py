@@ -15,7 +15,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libqsa.so")
+# QSA_LIB_PATH names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree libqsa.so.
+LIB_PATH = os.environ.get("QSA_LIB_PATH") or os.path.join(_PKG, "libqsa.so")
 
 (QSA_OP_APPEND, QSA_OP_INDEX, QSA_OP_SELECT, QSA_OP_ATTEND, QSA_OP_FORWARD, QSA_OP_DECODE, QSA_OP_INDEX_SELECT,
  QSA_OP_INDEX_DECODE, QSA_OP_TOKEN_INDEX_SELECT, QSA_OP_TOKEN_INDEX_DECODE, QSA_OP_TRAIN_FORWARD,

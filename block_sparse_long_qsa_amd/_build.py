@@ -69,5 +69,33 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB
 
 
+ASAN_DIR = os.path.join(OBJ, "asan")
+ASAN_RUNTIME = "/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so"
+
+
+def build_asan(jobs: int = 8) -> str:
+    """libqsa.so with its host code built under AddressSanitizer (device code
+    as usual), into _build/asan/.  Host-only checking: the library's argument
+    checks, workspace sizing and table construction run instrumented; load it
+    with the ASan runtime preloaded (ASAN_RUNTIME) and no GPU."""
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    jobs_list = []
+    for src in HIP_SOURCES:
+        obj = os.path.join(ASAN_DIR, src + ".o")
+        jobs_list.append(([HIPCC] + HIP_FLAGS + san + ["-c", os.path.join(CSRC, src), "-o", obj], obj))
+    clangxx = os.path.join(os.path.dirname(HIPCC), "..", "llvm", "bin", "clang++")
+    for src in CPP_SOURCES:
+        obj = os.path.join(ASAN_DIR, src + ".o")
+        jobs_list.append(([clangxx] + CPP_FLAGS + ["-fsanitize=address", "-fno-omit-frame-pointer", "-c",
+                                                   os.path.join(CSRC, src), "-o", obj], obj))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda j: _run(j[0]), jobs_list))
+    lib = os.path.join(ASAN_DIR, "libqsa.so")
+    _run([HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+          "-shared-libsan", "-o", lib] + [o for _, o in jobs_list])
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

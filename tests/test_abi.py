@@ -142,3 +142,16 @@ def test_probe_library_exports_its_header_and_checks_arguments():
     for kw in (dict(k=None), dict(v=None), dict(idx=None), dict(sink=None), dict(rows=-1), dict(ll=-1),
                dict(lr=0), dict(nb=0), dict(step=3), dict(step=16), dict(pad=32)):
         assert call(**kw) == 1, kw
+
+
+def test_create_without_a_gpu_builds_tables_then_reports_hip():
+    """Valid parameters on a machine with no usable GPU: the host rotary tables
+    are built (1,048,576 positions, YaRN 4), then the device step fails with
+    QSA_ERR_HIP and a recorded HIP code, and no handle is returned."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    p = Q.default_params(max_ctx=1 << 20, yarn_factor=4.0)
+    h = ctypes.c_void_p(123)
+    assert Q.lib().qsa_create(ctypes.byref(p), 0, ctypes.byref(h)) == 7
+    assert h.value is None and Q.qsa_last_hip_error() != 0

@@ -1,6 +1,10 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
-times, on sampled rows the oracle computes one by one, plus properties checked
-on every row (needles, selection invariants).
+times: sampled rows the oracle computes one by one (every 1,024th row and the
+last 24 at 262,144 tokens; every 16,384th row and the chunk boundaries at
+1,048,576; 8 of the 64 decode sequences at 131,072 and 3 of 8 at 1,048,576),
+the selection invariants on every row and every sequence, checked on the
+device (count min(budget, floor(p/4)), strictly ascending, every id in
+[0, floor(p/4)), -1 padding after the ids), and every needle probe's needle.
 
 Large inputs are drawn on the GPU by the seeded generator (a GPU and a CPU
 generator give different streams); the oracle reads host copies of those
@@ -83,6 +87,30 @@ def _check_rows(x, out, bidx, p, rows):
     return worst
 
 
+def _check_invariants(bidx, budget, q_offset=0, pos=None):
+    """Selection invariants of every row, on the device, in row slices: row i
+    (query position q_offset + i, or pos[i]) holds min(budget, floor(p/4))
+    strictly ascending ids in [0, floor(p/4)) followed by -1."""
+    sel_all = bidx.reshape(-1, budget)
+    n_rows = sel_all.shape[0]
+    col = torch.arange(budget, device=DEV)
+    for r0 in range(0, n_rows, 65536):
+        sel = sel_all[r0:r0 + 65536]
+        if pos is None:
+            p = torch.arange(r0, r0 + sel.shape[0], device=DEV, dtype=torch.int64) + q_offset
+        else:
+            p = pos[r0:r0 + sel.shape[0]].to(torch.int64)
+        o = p // 4
+        n = torch.clamp(o, max=budget)
+        valid = col[None, :] < n[:, None]
+        s64 = sel.to(torch.int64)
+        assert torch.equal(sel >= 0, valid), "rows %d..: ids / padding layout" % r0
+        assert bool(((s64 < o[:, None]) | ~valid).all()), "rows %d..: id past floor(p/4)" % r0
+        asc = (s64[:, 1:] > s64[:, :-1]) | ~valid[:, 1:]
+        assert bool(asc.all()), "rows %d..: not strictly ascending" % r0
+    return n_rows
+
+
 def _sample_rows(L, stride, tail, extra=()):
     rows = set(range(stride - 1, L, stride)) | set(range(L - tail, L)) | set(int(e) for e in extra if 0 <= e < L)
     return np.array(sorted(rows), dtype=np.int64)
@@ -92,6 +120,7 @@ def test_prefill_32k_sampled():
     w = synth.WORKLOADS["prefill_32k"]
     x = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in synth.prefill_inputs(w, "cpu").items()}
     out, bidx = _prefill_run(w, x)
+    _check_invariants(bidx, w.budget)
     n = _check_needles_prefill(x["needles"][0], bidx)
     plan = x["needles"][0]
     rows = _sample_rows(w.seq_len, 512, 16, [p[0] for p in plan.probes[::8]] + [2044, 2047, 2048, 2051, 2052])
@@ -103,10 +132,11 @@ def test_prefill_256k_sampled_bench_config():
     w = synth.WORKLOADS["prefill_256k"]
     x = synth.prefill_inputs(w, DEV)
     out, bidx = _prefill_run(w, x)
+    _check_invariants(bidx, w.budget)
     n = _check_needles_prefill(x["needles"][0], bidx)
     plan = x["needles"][0]
-    # every 4096th row, the recency-scaled tail, and one probe of every 16th needle
-    rows = _sample_rows(w.seq_len, 4096, 24, [p[0] for p in plan.probes[::16]] + [262144 - 257, 262144 - 256])
+    # every 1024th row, the recency-scaled tail, and one probe of every 16th needle
+    rows = _sample_rows(w.seq_len, 1024, 24, [p[0] for p in plan.probes[::16]] + [262144 - 257, 262144 - 256])
     worst = _check_rows(x, out, bidx, O.Params(budget=w.budget), rows)
     _say("prefill 256k: %d rows vs oracle (max abs err %.4g), %d needle probes" % (len(rows), worst, n))
 
@@ -133,6 +163,7 @@ def _decode_run(w):
 
 def _check_decode(w, x, out, bidx, seqs):
     p = O.Params(budget=w.budget, yarn_factor=w.yarn_factor)
+    _check_invariants(bidx, w.budget, pos=torch.full((w.batch,), w.seq_len, device=DEV))
     bi = bidx.cpu().numpy()
     for b in range(w.batch):                      # needles of every sequence
         for blk in x["needles"][b].blocks:
@@ -151,23 +182,26 @@ def _check_decode(w, x, out, bidx, seqs):
 def test_decode_128k_sampled_bench_config():
     w = synth.WORKLOADS["decode_128k"]
     x, out, bidx = _decode_run(w)
-    worst = _check_decode(w, x, out, bidx, seqs=(0, 17, 63))
-    _say("decode 128k: 3 sequences vs oracle (max abs err %.4g), needles of 64 sequences" % worst)
+    seqs = tuple(range(0, 64, 9))
+    worst = _check_decode(w, x, out, bidx, seqs=seqs)
+    _say("decode 128k: %d sequences vs oracle (max abs err %.4g), invariants and needles of 64 sequences" % (
+        len(seqs), worst))
 
 
 def test_decode_1m_yarn_sampled():
     w = synth.WORKLOADS["decode_1m"]
     x, out, bidx = _decode_run(w)
-    worst = _check_decode(w, x, out, bidx, seqs=(0, 7))
-    _say("decode 1M yarn: 2 sequences vs oracle (max abs err %.4g), needles of 8 sequences" % worst)
+    worst = _check_decode(w, x, out, bidx, seqs=(0, 3, 7))
+    _say("decode 1M yarn: 3 sequences vs oracle (max abs err %.4g), invariants and needles of 8 sequences" % worst)
 
 
 def test_prefill_1m_yarn_chunked_sampled():
     w = synth.WORKLOADS["prefill_1m"]
     x = synth.prefill_inputs(w, DEV)
     out, bidx = _prefill_run(w, x, chunk=w.chunk)
+    _check_invariants(bidx, w.budget)
     n = _check_needles_prefill(x["needles"][0], bidx)
     bounds = [c + d for c in range(w.chunk, w.seq_len, w.chunk) for d in (-1, 0, 1)]
-    rows = _sample_rows(w.seq_len, 65536, 4, bounds[::2])
+    rows = _sample_rows(w.seq_len, 16384, 4, bounds[::2])
     worst = _check_rows(x, out, bidx, O.Params(budget=w.budget, yarn_factor=w.yarn_factor), rows)
     _say("prefill 1M chunked yarn: %d rows vs oracle (max abs err %.4g), %d needle probes" % (len(rows), worst, n))

@@ -724,6 +724,77 @@ def test_empty_calls_touch_nothing():
         assert torch.equal(c[k], before[k]), k
 
 
+def _poison(caches, ws, on):
+    """Fill the caches and the workspace: zeros, or bit patterns no valid slot
+    holds (NaN in K~, -NaN in V, +Inf in k̄ and the pending keys, 0xFF bytes in
+    the workspace)."""
+    pats = {"k_cache": 0x7FC0, "v_cache": -64, "kbar_cache": 0x7F80, "kpend": 0x7F80}   # -64 = 0xFFC0
+    for name, t in caches.items():
+        t.view(torch.int16).fill_(pats[name] if on else 0)
+    ws.fill_(0xFF if on else 0)
+
+
+def test_poisoned_caches_and_workspace_leave_results_unchanged():
+    """Cache slots the call does not write (past each sequence's length, the
+    partial own block, k̄ of incomplete blocks) and every workspace byte are
+    filled with NaN / Inf / 0xFF patterns before qsa_forward (two chunks) and
+    qsa_decode (ragged lengths): outputs and selections are bitwise those of
+    zero-filled buffers, and finite."""
+    budget = 32
+    B, L = 2, 1001
+    w = synth.Workload("t", "prefill", B, L, budget, 4, "random", 47)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=2048, budget_blocks=budget)
+    res = {}
+    for on in (False, True):
+        c = Q.alloc_caches(h, B)
+        out = torch.empty((B, L, 24, 256), dtype=torch.bfloat16, device=DEV)
+        bidx = torch.empty((B, L, budget), dtype=torch.int32, device=DEV)
+        ws = Q.workspace(h, Q.QSA_OP_FORWARD, B, 512, 0)
+        _poison(c, ws, on)
+        for s0, s1 in ((0, 512), (512, L)):
+            ws.fill_(0xFF if on else 0)
+            sl = lambda t: t[:, s0:s1].contiguous()
+            o = torch.empty((B, s1 - s0, 24, 256), dtype=torch.bfloat16, device=DEV)
+            bi = torch.empty((B, s1 - s0, budget), dtype=torch.int32, device=DEV)
+            Q.qsa_forward(h, B, s1 - s0, s0, sl(xd["q"]), sl(xd["k"]), sl(xd["v"]), sl(xd["q_idx"]),
+                          sl(xd["k_idx"]), c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], o, bi, ws)
+            out[:, s0:s1] = o
+            bidx[:, s0:s1] = bi
+        torch.cuda.synchronize()
+        res[on] = (out, bidx)
+    assert torch.equal(res[False][1], res[True][1])
+    assert torch.equal(res[False][0].view(torch.int16), res[True][0].view(torch.int16))
+    assert torch.isfinite(res[True][0].float()).all()
+
+    lens = [1500, 3, 0, 701, 1202, 255]
+    wd = synth.Workload("t", "decode", len(lens), max(lens), budget, 4, "random", 48)
+    xdc = _to(synth.decode_inputs(wd, "cpu", ctx=max(lens), batch=len(lens)))
+    dres = {}
+    for on in (False, True):
+        c = Q.alloc_caches(h, len(lens))
+        ws = Q.workspace(h, Q.QSA_OP_DECODE, len(lens), 1, max(lens))
+        _poison(c, ws, on)
+        for b, n in enumerate(lens):
+            if n:
+                sl = lambda t: t[b:b + 1, :n].contiguous()
+                cs = {k: v[b:b + 1] for k, v in c.items()}
+                Q.qsa_append(h, 1, n, 0, sl(xdc["k"]), sl(xdc["v"]), sl(xdc["k_idx"]), cs["k_cache"],
+                             cs["v_cache"], cs["kbar_cache"], cs["kpend"])
+        new = {n: torch.stack([xdc[n][b, lens[b]] for b in range(len(lens))])[:, None].contiguous()
+               for n in ("k", "v", "k_idx")}
+        cache_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        out = torch.empty((len(lens), 1, 24, 256), dtype=torch.bfloat16, device=DEV)
+        bidx = torch.empty((len(lens), 1, budget), dtype=torch.int32, device=DEV)
+        Q.qsa_decode(h, len(lens), cache_len, max(lens), xdc["q"], new["k"], new["v"], xdc["q_idx"], new["k_idx"],
+                     c["k_cache"], c["v_cache"], c["kbar_cache"], c["kpend"], out, bidx, ws)
+        torch.cuda.synchronize()
+        dres[on] = (out, bidx)
+    assert torch.equal(dres[False][1], dres[True][1])
+    assert torch.equal(dres[False][0].view(torch.int16), dres[True][0].view(torch.int16))
+    assert torch.isfinite(dres[True][0].float()).all()
+
+
 def test_forward_long_equals_staged_calls():
     """A 70,000-row prefill with B = 2 (the attention in 4,096-row launches,
     the last one ragged; index + select in 65,536-row launches), in one
