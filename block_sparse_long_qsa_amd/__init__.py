@@ -29,7 +29,7 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPP
 # The C entry points (kept in step with include/qsa.h).
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
            "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
-           "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
+           "qsa_decode_noalloc", "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
            "qsa_train_forward", "qsa_train_backward_indexer", "qsa_train_backward_attention",
            "qsa_gdn_workspace_size", "qsa_gdn_chunk_prefill", "qsa_gdn_prep", "qsa_gdn_scan",
            "qsa_status_string", "qsa_last_hip_error"]
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_forward.restype = ctypes.c_int
     L.qsa_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 12 + [sz]
     L.qsa_decode.restype = ctypes.c_int
+    L.qsa_decode_noalloc.argtypes = [vp, vp, i32, vp, i64] + [vp] * 11
+    L.qsa_decode_noalloc.restype = ctypes.c_int
     L.qsa_decode_reuse.argtypes = [vp, vp, i32, vp, vp, i64] + [vp] * 11 + [sz]
     L.qsa_decode_reuse.restype = ctypes.c_int
     L.qsa_index_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 6 + [sz]
@@ -296,6 +298,20 @@ def qsa_decode(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cac
                             _bf(q_idx, "q_idx", B * _QI), _bf(k_idx, "k_idx", B * _KI), kc, vc, kb, kp,
                             _bf(out, "out", B * _Q), _ptr(block_idx, torch.int32, "block_idx", B * h.budget),
                             _ptr(ws, None, "ws"), _nbytes(ws)), "qsa_decode")
+
+
+# Bytes of the library's per-GPU scratch array behind qsa_decode_noalloc.
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def qsa_decode_noalloc(h, B, cache_len, ctx_bound, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out,
+                       block_idx=None, stream=None):
+    kc, vc, kb, kp = _caches(h, B, k_cache, v_cache, kbar_cache, kpend)
+    _check(lib().qsa_decode_noalloc(h.ptr, _stream(stream), B, _ptr(cache_len, torch.int32, "cache_len", B),
+                                    ctx_bound, _bf(q, "q", B * _Q), _bf(k, "k", B * _KV), _bf(v, "v", B * _KV),
+                                    _bf(q_idx, "q_idx", B * _QI), _bf(k_idx, "k_idx", B * _KI), kc, vc, kb, kp,
+                                    _bf(out, "out", B * _Q),
+                                    _ptr(block_idx, torch.int32, "block_idx", B * h.budget)), "qsa_decode_noalloc")
 
 
 def qsa_decode_reuse(h, B, cache_len, sel_pos, ctx_bound, q, k, v, k_idx, k_cache, v_cache, kbar_cache, kpend,

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -74,11 +75,36 @@ struct qsa_handle {
     float *d_cos;
     float *d_sin;
     float sigma;        // softmax scale of the core logits
+    char *scratch;      // device address of this device's no-allocation scratch array
 };
 
 namespace {
 
 thread_local int g_last_hip = 0;
+
+// Scratch of qsa_decode_noalloc: one array per GPU, held until the process
+// ends.  In host code `scratch` is a stand-in for the symbol, not a device
+// address: kernels and copies get the address hipGetSymbolAddress returns for
+// the current device (kept in g_scratch per device, set by qsa_create).
+static __device__ __align__(256) char scratch[QSA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char *g_scratch[kMaxDevices] = {};
+
+// The device address of the current device's scratch array (dev is current).
+hipError_t scratch_address(int dev, char **out) {
+    *out = nullptr;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<char *>(p);
+    }
+    *out = g_scratch[dev];
+    return hipSuccess;
+}
 
 // Candidate lists of one fused index + select launch: at most this many bytes.
 constexpr size_t kCandBytes = size_t(4) << 30;
@@ -231,6 +257,47 @@ qsa_status check_ptrs(std::initializer_list<const void *> ptrs) {
     return QSA_OK;
 }
 
+// Host checks shared by the decode entry points (before anything is enqueued).
+qsa_status check_decode(const qsa_handle *h, int32_t B, int64_t ctx_bound, std::initializer_list<const void *> ptrs,
+                        const int32_t *block_idx) {
+    if (!h) return QSA_ERR_NULL;
+    if (B < 1 || B > kMaxBatch || ctx_bound < 0) return QSA_ERR_SHAPE;
+    if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
+    const qsa_status s = check_ptrs(ptrs);
+    if (s != QSA_OK) return s;
+    if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
+    return QSA_OK;
+}
+
+// One decode step with its scratch at w (layout d): append -> scan -> two-stage
+// select -> split-K attention -> merge.
+hipError_t run_decode(const qsa_handle *h, hipStream_t st, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
+                      const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *q_idx,
+                      const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache,
+                      uint16_t *kpend, uint16_t *out, int32_t *block_idx, char *w, const DecLayout &d) {
+    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
+    float *scores = reinterpret_cast<float *>(w + d.scores);
+    int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + d.bidx);
+    float *part_o = reinterpret_cast<float *>(w + d.part_o);
+    float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
+    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
+    const int budget = h->p.budget_blocks;
+    const int64_t nbc = nblk_cap(h);
+    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, q_idx, k_cache,
+                                        v_cache, kbar_cache, kpend, qrot, dhist);
+    if (e == hipSuccess)
+        e = launch_decode_scan(st, B, cache_len, ctx_bound, 2, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
+    if (e == hipSuccess)
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 2, d.ncol, scores, dhist,
+                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
+                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
+                                    reinterpret_cast<uint32_t *>(w + d.s2row), bidx, budget);
+    if (e == hipSuccess)
+        e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, budget, d.nsplit, h->sigma, q,
+                                 k_cache, v_cache, bidx, part_o, part_ml, out);
+    return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -288,6 +355,7 @@ qsa_status qsa_create(const qsa_params *params, int device, qsa_handle **out) {
     h->sigma = static_cast<float>(sigma);
     hipError_t e = hipMalloc(reinterpret_cast<void **>(&h->d_cos), n * sizeof(float));
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&h->d_sin), n * sizeof(float));
+    if (e == hipSuccess) e = scratch_address(device, &h->scratch);
     if (e == hipSuccess) e = hipMemcpy(h->d_cos, hc.data(), n * sizeof(float), hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipMemcpy(h->d_sin, hs.data(), n * sizeof(float), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
@@ -451,40 +519,34 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
                       const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *q_idx,
                       const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache,
                       uint16_t *kpend, uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes) {
-    if (!h) return QSA_ERR_NULL;
-    if (B < 1 || B > kMaxBatch || ctx_bound < 0) return QSA_ERR_SHAPE;
-    if (ctx_bound >= h->p.max_ctx) return QSA_ERR_CAPACITY;
-    qsa_status s = check_ptrs({cache_len, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, ws});
+    qsa_status s = check_decode(h, B, ctx_bound, {cache_len, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache,
+                                                  kpend, out, ws}, block_idx);
     if (s != QSA_OK) return s;
-    if (block_idx && !aligned16(block_idx)) return QSA_ERR_ALIGN;
     const DecLayout d = decode_layout(h, B, ctx_bound);
     if (d.nchunk > kDecodeChunkMax) return QSA_ERR_CAPACITY;
     if (ws_bytes < d.total) return QSA_ERR_WORKSPACE;
     DeviceGuard guard(h->device);
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *w = static_cast<char *>(ws);
-    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
-    float *scores = reinterpret_cast<float *>(w + d.scores);
-    int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + d.bidx);
-    float *part_o = reinterpret_cast<float *>(w + d.part_o);
-    float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
-    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
-    const int budget = h->p.budget_blocks;
-    const int64_t nbc = nblk_cap(h);
+    const hipError_t e = run_decode(h, static_cast<hipStream_t>(stream), B, cache_len, ctx_bound, q, k, v, q_idx,
+                                    k_idx, k_cache, v_cache, kbar_cache, kpend, out, block_idx,
+                                    static_cast<char *>(ws), d);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
 
-    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, q_idx, k_cache, v_cache,
-                                        kbar_cache, kpend, qrot, dhist);
-    if (e == hipSuccess)
-        e = launch_decode_scan(st, B, cache_len, ctx_bound, 2, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
-    if (e == hipSuccess)
-        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 2, d.ncol, scores, dhist,
-                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
-                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
-                                    reinterpret_cast<uint32_t *>(w + d.s2row), bidx, budget);
-    if (e == hipSuccess)
-        e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, budget, d.nsplit, h->sigma, q,
-                                 k_cache, v_cache, bidx, part_o, part_ml, out);
+qsa_status qsa_decode_noalloc(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                              int64_t ctx_bound, const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const uint16_t *q_idx, const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache,
+                              uint16_t *kbar_cache, uint16_t *kpend, uint16_t *out, int32_t *block_idx) {
+    qsa_status s = check_decode(h, B, ctx_bound, {cache_len, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache,
+                                                  kpend, out}, block_idx);
+    if (s != QSA_OK) return s;
+    const DecLayout d = decode_layout(h, B, ctx_bound);
+    if (d.nchunk > kDecodeChunkMax) return QSA_ERR_CAPACITY;
+    if (d.total > QSA_NOALLOC_SCRATCH_BYTES || !h->scratch) return QSA_ERR_WORKSPACE;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    const hipError_t e = run_decode(h, static_cast<hipStream_t>(stream), B, cache_len, ctx_bound, q, k, v, q_idx,
+                                    k_idx, k_cache, v_cache, kbar_cache, kpend, out, block_idx, h->scratch, d);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

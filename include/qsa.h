@@ -229,6 +229,29 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
                       uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
                       uint16_t *out, int32_t *block_idx, void *ws, size_t ws_bytes);
 
+/* qsa_decode for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the same
+ * kernels and results as qsa_decode, with no workspace argument.  The step's
+ * scratch (rotated query, score rows, histograms, selection lists, split
+ * partials) lives in a fixed device array of QSA_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; its address is
+ * resolved once per device by qsa_create.  The caller still passes every input,
+ * cache and output.  Returns QSA_ERR_WORKSPACE, before anything is enqueued,
+ * when qsa_workspace_size(QSA_OP_DECODE, B, 1, ctx_bound) exceeds
+ * QSA_NOALLOC_SCRATCH_BYTES (it covers, for instance, B = 64 at ctx_bound =
+ * 131,072 and B = 8 at 1,048,576).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (other streams, other threads, other
+ * handles) race and must be serialised by the caller.  The array keeps the last
+ * call's contents; each call clears what it accumulates into.  Calls no
+ * hipMalloc, hipFree or other allocating routine. */
+#define QSA_NOALLOC_SCRATCH_BYTES (32u << 20)
+qsa_status qsa_decode_noalloc(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
+                              int64_t ctx_bound,
+                              const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const uint16_t *q_idx, const uint16_t *k_idx,
+                              uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache, uint16_t *kpend,
+                              uint16_t *out, int32_t *block_idx);
+
 /* Decode one new token per sequence reusing a block selection made at an
  * earlier position instead of scoring and selecting again ([PKR] section on the
  * MTP module for speculative decoding: the top-k block indices are reused
