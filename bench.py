@@ -344,9 +344,8 @@ def cpu_baseline_decode(sd, wd, n_seq=2):
             "parity_on_sample": {"seqs": n_seq, "max_abs_err": max_err, "selection_sym_diff": sel_diff}}
 
 
-def qsa_prefill_1m_ms(steps):
-    """QSA chunked prefill of 1,048,576 tokens (YaRN 4) in 65,536-token
-    qsa_forward calls: one warm-up pass, then the mean of `steps` passes (ms)."""
+def prefill_1m_state():
+    """Inputs, handle, caches and buffers of the 1,048,576-token chunked prefill (YaRN 4)."""
     wp = synth.WORKLOADS["prefill_1m"]
     L, C = wp.seq_len, wp.chunk
     x = synth.prefill_inputs(wp, "cuda")
@@ -355,6 +354,16 @@ def qsa_prefill_1m_ms(steps):
     ws = Q.workspace(h, Q.QSA_OP_FORWARD, 1, C, L - C)
     out = torch.empty((1, L, 24, 256), dtype=torch.bfloat16, device="cuda")
     bidx = torch.empty((1, L, wp.budget), dtype=torch.int32, device="cuda")
+    return dict(w=wp, x=x, h=h, c=c, ws=ws, out=out, bidx=bidx, L=L, C=C)
+
+
+def qsa_prefill_1m_ms(steps, st=None):
+    """QSA chunked prefill of 1,048,576 tokens (YaRN 4) in 65,536-token
+    qsa_forward calls: one warm-up pass, then the mean of `steps` passes (ms)."""
+    own = st is None
+    if own:
+        st = prefill_1m_state()
+    x, h, c, ws, out, bidx, L, C = (st[k] for k in ("x", "h", "c", "ws", "out", "bidx", "L", "C"))
 
     def prefill():
         for s0 in range(0, L, C):
@@ -371,9 +380,31 @@ def qsa_prefill_1m_ms(steps):
     ev[1].record()
     torch.cuda.synchronize()
     t = ev[0].elapsed_time(ev[1]) / steps
-    del x, c, ws, out, bidx, h
-    torch.cuda.empty_cache()
+    if own:
+        del st, x, c, ws, out, bidx, h
+        torch.cuda.empty_cache()
     return t
+
+
+def dense_attend_ms(h, c, x, out, L, reps=1):
+    """This library's dense causal GQA kernel (qsa_dense_attend) over every
+    query of an L-token prefill whose K~/V caches are already filled: one
+    warm-up call on the last 16 rows, then the mean of `reps` full calls (ms)."""
+    Q.qsa_dense_attend(h, 1, 16, L - 16, x["q"][:, L - 16:], c["k_cache"], c["v_cache"], out[:, L - 16:])
+    torch.cuda.synchronize()
+    ev = _events(2)
+    ev[0].record()
+    for _ in range(reps):
+        Q.qsa_dense_attend(h, 1, L, 0, x["q"], c["k_cache"], c["v_cache"], out)
+    ev[1].record()
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[1]) / reps
+
+
+def dense_flops(L):
+    """Algorithmic FLOPs of dense causal attention over L queries: 2 products x
+    2 FLOP x 24 heads x 256 dims per (query, key <= query) pair."""
+    return 4 * 24 * 256 * L * (L + 1) // 2
 
 
 def run_c5(steps):
@@ -526,8 +557,10 @@ def indexer_ratio_decode(wd, steps):
 def run_ratios(steps):
     """QSA against dense attention on this GPU, as in the pages' module
     speed-ups (prefill and decode at 1M tokens): QSA prefill (append + fused
-    index/select + sparse attention) against dense causal SDPA at 262,144 and
-    1,048,576 tokens, and QSA decode of 8 x 1,048,576 against the same split-K
+    index/select + sparse attention) against this library's dense causal GQA
+    kernel over the same caches (qsa_dense_attend; PyTorch's SDPA beside it for
+    reference) at 262,144 and 1,048,576 tokens, and QSA decode of 8 x 1,048,576
+    against the same split-K
     decode kernel over every cached token (qsa_decode_reuse with a selection
     made at position 0: no selected block, the tail is the whole context).
     Then the indexer alone at compression ratio 4 against ratio 1 (the pages'
@@ -545,15 +578,28 @@ def run_ratios(steps):
     t_qsa = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
     del sp
     torch.cuda.empty_cache()
-    t_dense = dense_prefill_ms(wp.seq_len, reps=2)
+    t_dense = dense_attend_ms(sp["h"], sp["c"], sp["x"], sp["out"], wp.seq_len, reps=2)
+    del sp
+    torch.cuda.empty_cache()
+    t_sdpa = dense_prefill_ms(wp.seq_len, reps=2)
     _progress("ratios: prefill 262144 done")
-    res["prefill_262144"] = {"qsa_ms": t_qsa, "dense_sdpa_ms": t_dense, "speedup": t_dense / t_qsa}
+    res["prefill_262144"] = {"qsa_ms": t_qsa, "dense_ms": t_dense, "speedup": t_dense / t_qsa,
+                             "dense_tflops": dense_flops(wp.seq_len) / (t_dense * 1e-3) / 1e12,
+                             "dense_kernel": "qsa_dense_attend (this library)",
+                             "torch_sdpa_ms": t_sdpa}
     wp_1m = synth.WORKLOADS["prefill_1m"]
-    t_qsa_1m = qsa_prefill_1m_ms(1)
-    t_dense_1m = dense_prefill_ms(1 << 20, reps=1)
+    st = prefill_1m_state()
+    t_qsa_1m = qsa_prefill_1m_ms(1, st)
+    t_dense_1m = dense_attend_ms(st["h"], st["c"], st["x"], st["out"], st["L"], reps=1)
+    del st
+    torch.cuda.empty_cache()
+    t_sdpa_1m = dense_prefill_ms(1 << 20, reps=1)
     _progress("ratios: prefill 1048576 done")
-    res["prefill_1048576"] = {"qsa_ms": t_qsa_1m, "dense_sdpa_ms": t_dense_1m, "speedup": t_dense_1m / t_qsa_1m,
-                              "dense_sdpa_tflops": 4 * 24 * 256 * (1 << 20) ** 2 / 2 / (t_dense_1m * 1e-3) / 1e12}
+    res["prefill_1048576"] = {"qsa_ms": t_qsa_1m, "dense_ms": t_dense_1m, "speedup": t_dense_1m / t_qsa_1m,
+                              "dense_tflops": dense_flops(1 << 20) / (t_dense_1m * 1e-3) / 1e12,
+                              "dense_kernel": "qsa_dense_attend (this library)",
+                              "torch_sdpa_ms": t_sdpa_1m,
+                              "torch_sdpa_tflops": dense_flops(1 << 20) / (t_sdpa_1m * 1e-3) / 1e12}
     wd = synth.WORKLOADS["decode_1m"]
     sd = setup_decode(wd)
     x, c = sd["x"], sd["c"]

@@ -28,7 +28,8 @@ STATUS = {0: "QSA_OK", 1: "QSA_ERR_NULL", 2: "QSA_ERR_SHAPE", 3: "QSA_ERR_UNSUPP
 
 # The C entry points (kept in step with include/qsa.h).
 EXPORTS = ["qsa_default_params", "qsa_create", "qsa_destroy", "qsa_get_params", "qsa_workspace_size",
-           "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_forward", "qsa_decode",
+           "qsa_append", "qsa_index", "qsa_select", "qsa_index_select", "qsa_attend", "qsa_dense_attend", "qsa_forward",
+           "qsa_decode",
            "qsa_decode_noalloc", "qsa_decode_reuse", "qsa_index_decode", "qsa_token_index_select", "qsa_token_index_decode",
            "qsa_train_forward", "qsa_train_backward_indexer", "qsa_train_backward_attention",
            "qsa_gdn_workspace_size", "qsa_gdn_chunk_prefill", "qsa_gdn_prep", "qsa_gdn_scan",
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
     L.qsa_index_select.restype = ctypes.c_int
     L.qsa_attend.argtypes = [vp, vp, i32, i64, i64] + [vp] * 5
     L.qsa_attend.restype = ctypes.c_int
+    L.qsa_dense_attend.argtypes = [vp, vp, i32, i64, i64] + [vp] * 4
+    L.qsa_dense_attend.restype = ctypes.c_int
     L.qsa_forward.argtypes = [vp, vp, i32, i64, i64] + [vp] * 12 + [sz]
     L.qsa_forward.restype = ctypes.c_int
     L.qsa_decode.argtypes = [vp, vp, i32, vp, i64] + [vp] * 12 + [sz]
@@ -277,6 +280,12 @@ def qsa_attend(h, B, L, q_offset, q, k_cache, v_cache, block_idx, out, stream=No
     _check(lib().qsa_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q", B * L * _Q), kc, vc,
                             _ptr(block_idx, torch.int32, "block_idx", B * L * h.budget), _bf(out, "out", B * L * _Q)),
            "qsa_attend")
+
+
+def qsa_dense_attend(h, B, L, q_offset, q, k_cache, v_cache, out, stream=None):
+    kc, vc, _, _ = _caches(h, B, k_cache, v_cache)
+    _check(lib().qsa_dense_attend(h.ptr, _stream(stream), B, L, q_offset, _bf(q, "q", B * L * _Q), kc, vc,
+                                  _bf(out, "out", B * L * _Q)), "qsa_dense_attend")
 
 
 def qsa_forward(h, B, L, q_offset, q, k, v, q_idx, k_idx, k_cache, v_cache, kbar_cache, kpend, out, block_idx, ws,

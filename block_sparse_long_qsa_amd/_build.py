@@ -20,7 +20,7 @@ PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")     # benchmark-only gather pro
 ARCH = "gfx950"
 
 HIP_SOURCES = ["qsa_api.hip", "k_prologue.hip", "k_indexer.hip", "k_select.hip", "k_attend.hip", "k_decode.hip", "k_gdn.hip",
-               "k_train.hip"]
+               "k_train.hip", "k_dense.hip"]
 CPP_SOURCES = ["qsa_tables.cpp"]
 PROBE_SOURCES = ["probe_gather.hip"]
 

@@ -34,6 +34,8 @@ hipError_t launch_select_fixup(hipStream_t, int32_t, int64_t, int64_t, int, int,
 hipError_t launch_attend_prefill(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int64_t, int64_t,
                                  int, float, const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *,
                                  bf16_t *);
+hipError_t launch_dense_attend(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int64_t, int64_t, int64_t, float,
+                               const bf16_t *, const bf16_t *, const bf16_t *, bf16_t *);
 hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int32_t *, const int32_t *, int64_t, int64_t,
                                 int, int, float,
                                 const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
@@ -468,6 +470,18 @@ qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
     hipStream_t st = static_cast<hipStream_t>(stream);
     hipError_t e = launch_attend_prefill(tables(h), st, B, L, 0, L, q_offset, nblk_cap(h), h->p.budget_blocks, h->sigma, q,
                                   k_cache, v_cache, block_idx, out);
+    return e == hipSuccess ? QSA_OK : hip_fail(e);
+}
+
+qsa_status qsa_dense_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                            const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache, uint16_t *out) {
+    qsa_status s = check_chunk(h, B, L, q_offset, true);
+    if (s != QSA_OK || L == 0) return s;
+    if ((s = check_ptrs({q, k_cache, v_cache, out})) != QSA_OK) return s;
+    DeviceGuard guard(h->device);
+    if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
+    const hipError_t e = launch_dense_attend(tables(h), static_cast<hipStream_t>(stream), B, L, 0, L, q_offset,
+                                             nblk_cap(h), h->sigma, q, k_cache, v_cache, out);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

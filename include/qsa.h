@@ -203,6 +203,18 @@ qsa_status qsa_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
                       const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
                       const int32_t *block_idx, uint16_t *out);
 
+/* Dense causal GQA attention over the same caches: the dense baseline of the
+ * pages' module speed-ups ([PKR] "QSA: ...", kernel-latency figure: indexer +
+ * sparse core attention against a dense paged GQA kernel).  For each query
+ * p = q_offset + i and head h (KV head h / 12): softmax(sigma * q~_h . K~^T) V
+ * over every token 0..p, with the rotation, scale and precision of
+ * qsa_attend (bf16 operands, fp32 logits and softmax, P rounded to bf16 for the
+ * PV product, bf16 output); this equals qsa_attend with every block before the
+ * query's own selected.  The caches must hold positions 0..p.
+ * q_offset % 4 == 0.  Needs no workspace. */
+qsa_status qsa_dense_attend(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
+                            const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache, uint16_t *out);
+
 /* Prefill (or one prefill chunk): qsa_append, qsa_index_select and qsa_attend
  * for positions q_offset .. q_offset+L-1.  block_idx may be NULL; when given
  * it receives the selection ([B][L][budget]).  Earlier chunks must already be
