@@ -45,9 +45,9 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # 1 GiB copy).  The counter summary is
 # profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure is
 # reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (3939544.6 * 2.000 + 49152.0 * 1.000) * 1024 * 64
+ATTEND_TRAFFIC_BYTES = (3923227.5 * 2.000 + 49152.0 * 1.000) * 1024 * 64
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "0a2f3b528cb1437049ebd20b262c0011ebbf35eec9cdece7cf0def5da3ba1526",
+    "k_attend.hip": "41735dbeac645a9e310e71d3f2a25212d0cb74806763b5878672dfbbf490cf56",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
 }
