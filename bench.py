@@ -576,8 +576,6 @@ def run_ratios(steps):
         prefill_forward(sp, e)
     torch.cuda.synchronize()
     t_qsa = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    del sp
-    torch.cuda.empty_cache()
     t_dense = dense_attend_ms(sp["h"], sp["c"], sp["x"], sp["out"], wp.seq_len, reps=2)
     del sp
     torch.cuda.empty_cache()
