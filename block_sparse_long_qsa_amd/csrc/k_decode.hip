@@ -7,26 +7,20 @@
 
 namespace qsa {
 
-constexpr int kDecodeBins = 2048;      // histogram of score bits 30..20 per sequence
+constexpr int kDecodeBins = 2048;      // histogram of score bits 30..20
 
-// One wave per sequence.  p = cache_len[b]:
-//   lanes: head g = lane/32, chunk c = lane%32 -> rotate k at p into K~ slot p%4
-//          and copy v into V slot p%4 (when k is given);
+// Append the new token of sequence b at position p, one wave (lane = 0..63):
+//   lanes: head g = lane/32, chunk c = lane%32 -> rotate k at p into K~ slot
+//          p%4 and copy v into V slot p%4 (when k is given);
 //   lanes 0..15: raw k_idx into kpend[p%4]; when p%4 == 3 pool the completed
-//          block (kpend slots 0..2 + this token) into kbar;
-//   lanes: head lane/16, chunk lane%16 -> rotated q_idx at p into qrot (when
-//          q_idx is given).
-__global__ __launch_bounds__(64) void decode_append_kernel(
-    Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t nblk_cap,
-    const bf16_t *__restrict__ k, const bf16_t *__restrict__ v, const bf16_t *__restrict__ k_idx,
-    const bf16_t *__restrict__ q_idx,
-    bf16_t *__restrict__ k_cache, bf16_t *__restrict__ v_cache, bf16_t *__restrict__ kbar,
-    bf16_t *__restrict__ kpend, bf16_t *__restrict__ qrot, uint32_t *__restrict__ dhist)
+//          block (kpend slots 0..2 + this token) into kbar[p/4] -- a block
+//          that is no candidate of the query at p (candidates are < p/4).
+__device__ __forceinline__ void append_one(const Tables &tab, int lane, int64_t b, int64_t p, int64_t nblk_cap,
+                                           const bf16_t *__restrict__ k, const bf16_t *__restrict__ v,
+                                           const bf16_t *__restrict__ k_idx, bf16_t *__restrict__ k_cache,
+                                           bf16_t *__restrict__ v_cache, bf16_t *__restrict__ kbar,
+                                           bf16_t *__restrict__ kpend)
 {
-    const int lane = threadIdx.x;
-    const int64_t b = blockIdx.x;
-    for (int x = lane; x < kDecodeBins; x += 64) dhist[b * kDecodeBins + x] = 0;   // filled by the scan
-    const int64_t p = decode_pos(cache_len, b, ctx_bound);
     const int64_t blk = p / kBlock;
     const int t = static_cast<int>(p - blk * kBlock);
     const float *cs = tab.cos + p * kPairs;
@@ -108,30 +102,19 @@ __global__ __launch_bounds__(64) void decode_append_kernel(
                       pack_bf16x2(r[6], r[7])};
         }
     }
-    if (q_idx) {   // rotated indexer query (not needed when a selection is reused)
-        const int h = lane >> 4, c = lane & 15;
-        const bf16_t *src = q_idx + (b * kIdxHeads + h) * kIdxDim;
-        u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);
-        if (c < 8) {
-            const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (c ^ 4));
-            const bool first_half = c < 4;
-            const int j0 = 8 * (c & 3);
-            uint32_t w[4];
-            for (int i = 0; i < 4; ++i) {
-                float r[2];
-                for (int e = 0; e < 2; ++e) {
-                    float me = __uint_as_float(e ? (x[i] & 0xFFFF0000u) : (x[i] << 16));
-                    float pa = __uint_as_float(e ? (xp[i] & 0xFFFF0000u) : (xp[i] << 16));
-                    float a = first_half ? me : pa, bb = first_half ? pa : me;
-                    rotate_pair(a, bb, cs[j0 + 2 * i + e], sn[j0 + 2 * i + e]);
-                    r[e] = first_half ? a : bb;
-                }
-                w[i] = pack_bf16x2(r[0], r[1]);
-            }
-            x = u32x4{w[0], w[1], w[2], w[3]};
-        }
-        *reinterpret_cast<u32x4 *>(qrot + (b * kIdxHeads + h) * kIdxDim + 8 * c) = x;
-    }
+}
+
+// One wave per sequence: append_one at p = cache_len[b] (the step of a reused
+// selection, which scores nothing).
+__global__ __launch_bounds__(64) void decode_append_kernel(
+    Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t nblk_cap,
+    const bf16_t *__restrict__ k, const bf16_t *__restrict__ v, const bf16_t *__restrict__ k_idx,
+    bf16_t *__restrict__ k_cache, bf16_t *__restrict__ v_cache, bf16_t *__restrict__ kbar,
+    bf16_t *__restrict__ kpend)
+{
+    const int64_t b = blockIdx.x;
+    append_one(tab, threadIdx.x, b, decode_pos(cache_len, b, ctx_bound), nblk_cap, k, v, k_idx, k_cache, v_cache,
+               kbar, kpend);
 }
 
 // 8 dims (chunk c of 16) of a 128-dim row rotated at one position: chunks
@@ -155,73 +138,86 @@ __device__ __forceinline__ u32x4 rotate_chunk8(u32x4 x, u32x4 xp, int c, const f
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// Token-level indexer step (r = 1), one wave per sequence, p = cache_len[b]:
-// the new token's indexer key rotated at p goes to ktok[b][p], the indexer
-// query rotated at p to qrot, and the sequence's score histogram is cleared.
-__global__ __launch_bounds__(64) void token_decode_append_kernel(
-    Tables tab, const int32_t *__restrict__ cache_len, int64_t ctx_bound, int64_t tok_cap,
-    const bf16_t *__restrict__ k_idx, const bf16_t *__restrict__ q_idx, bf16_t *__restrict__ ktok,
-    bf16_t *__restrict__ qrot, uint32_t *__restrict__ dhist)
-{
-    const int lane = threadIdx.x;
-    const int64_t b = blockIdx.x;
-    for (int x = lane; x < kDecodeBins; x += 64) dhist[b * kDecodeBins + x] = 0;
-    const int64_t p = decode_pos(cache_len, b, ctx_bound);
-    const float *cs = tab.cos + p * kPairs;
-    const float *sn = tab.sin + p * kPairs;
-    const int c = lane & 15, h = lane >> 4;
-    {   // lanes 0..15: the key; the query's 4 heads over all 64 lanes
-        const bf16_t *src = q_idx + (b * kIdxHeads + h) * kIdxDim;
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);
-        const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (c ^ 4));
-        *reinterpret_cast<u32x4 *>(qrot + (b * kIdxHeads + h) * kIdxDim + 8 * c) = rotate_chunk8(x, xp, c, cs, sn);
-    }
-    if (lane < 16) {
-        const bf16_t *src = k_idx + b * kIdxDim;
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * c);
-        const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (c ^ 4));
-        *reinterpret_cast<u32x4 *>(ktok + (b * tok_cap + p) * kIdxDim + 8 * c) = rotate_chunk8(x, xp, c, cs, sn);
-    }
-}
-
 // Score scan: scores[b][blk] = sum_h ReLU(<q~_h, k̄_blk>) for blk < floor(p/r),
 // r = 1 << rsh (4: pooled micro-blocks; 1: one rotated key per token).
-// v_mfma_f32_16x16x32_bf16 with A = q~ (4 real rows of 16), B = 16 pooled keys;
+// v_mfma_f32_16x16x32_bf16 with A = q~ (4 real rows of 16), B = 16 keys;
 // lanes 0..15 end with the 4 heads of one block.  Each wave streams 512 blocks
 // and collects their scores in LDS, then writes them with one 16-byte store per
 // lane and 256 scores: 4-byte stores interleaved with the k̄ loads cost about 6%
 // of the scan.
-constexpr int kScanBlocksPerWave = 512;
-constexpr int kScanBlocksPerWG = 4 * kScanBlocksPerWave;
 
-// Each workgroup also histograms the top 11 value bits of its scores and adds
-// the histogram to the sequence's (zeroed by decode_append_kernel).
-__global__ __launch_bounds__(256) void decode_scan_kernel(const int32_t *__restrict__ cache_len, int64_t ctx_bound,
-                                                          int rsh, int64_t nblk_cap,
-                                                          int64_t ncol, const bf16_t *__restrict__ qrot,
-                                                          const bf16_t *__restrict__ kbar,
-                                                          float *__restrict__ scores, uint32_t *__restrict__ dhist)
+// What the first work-group of a sequence appends while the others scan: the
+// new token's K~/V (k non-null), its raw indexer key (pooled at r = 4 into the
+// key cache when its block completes) or, at r = 1, its indexer key rotated at
+// p into the token-key cache.  Nothing appended is read by the scan of the
+// same step (candidates are < floor(p/r)).
+struct DecodeAppend {
+    const bf16_t *k, *v, *k_idx;
+    bf16_t *k_cache, *v_cache, *kpend;
+    int64_t kv_blk_cap;                  // blocks per sequence and KV group of the K~/V caches
+};
+
+// Per-work-group summary of the score histogram.  Work-group w of a row
+// writes the bins of its own 2048-bin histogram of score bits 30..20 whose
+// count of scores in higher bins (within w) is below the budget K -- the bins
+// from the top down to d_w, the highest bin whose suffix count within w
+// reaches K, or every bin if w holds fewer than K scores -- as words
+// (bin << 21 | count), preceded by their number.  A bin enters only if it is
+// non-empty and the higher bins hold fewer than K scores, so at most K words.
+// The row's boundary bin d* (the highest bin whose suffix count over the row
+// reaches K) is >= every d_w, hence the summaries give the exact row count of
+// every bin >= d*: no histogram has to be cleared between steps.
+
+__global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int32_t *__restrict__ cache_len,
+                                                          int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol,
+                                                          int budget, int nwg, const bf16_t *__restrict__ q_idx,
+                                                          bf16_t *__restrict__ keys, float *__restrict__ scores,
+                                                          uint32_t *__restrict__ summ, DecodeAppend ap)
 {
     __shared__ uint32_t lh[kDecodeBins];
     __shared__ __attribute__((aligned(16))) uint32_t sl[4][kScanBlocksPerWave];   // each wave's score bits
+    __shared__ uint32_t wsum[4];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
-    const int64_t o = decode_pos(cache_len, b, ctx_bound) >> rsh;
+    const int64_t p = decode_pos(cache_len, b, ctx_bound);
+    const int64_t o = p >> rsh;
+    const float *cs = tab.cos + p * kPairs;
+    const float *sn = tab.sin + p * kPairs;
+    if (blockIdx.x == 0 && wave == 0) {
+        if (rsh == 2) {
+            append_one(tab, lane, b, p, ap.kv_blk_cap, ap.k, ap.v, ap.k_idx, ap.k_cache, ap.v_cache, keys, ap.kpend);
+        } else if (lane < 16) {       // token keys: the new key rotated at p into keys[b][p]
+            const bf16_t *src = ap.k_idx + b * kIdxDim;
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(src + 8 * lane);
+            const u32x4 xp = *reinterpret_cast<const u32x4 *>(src + 8 * (lane ^ 4));
+            *reinterpret_cast<u32x4 *>(keys + (b * key_cap + p) * kIdxDim + 8 * lane) =
+                rotate_chunk8(x, xp, lane, cs, sn);
+        }
+    }
     if (static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG >= o) return;     // whole workgroup idle
     for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
     __syncthreads();
     const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG + wave * kScanBlocksPerWave;
     if (w0 < o) {
     const int r = lane & 15, g = lane >> 4;
+    // A = q~: lane (head r < 4, k-group g) holds dims 32s + 8g .. +7 of head r,
+    // rotated here at p (pairs j, j + 32 sit in k-steps 0 and 1 of one lane)
     bf16x8 af[4];
-    for (int s = 0; s < 4; ++s) {
-        if (r < kIdxHeads)
-            af[s] = *reinterpret_cast<const bf16x8 *>(qrot + (b * kIdxHeads + r) * kIdxDim + 32 * s + 8 * g);
-        else
-            af[s] = bf16x8{};
+    if (r < kIdxHeads) {
+        const bf16_t *src = q_idx + (b * kIdxHeads + r) * kIdxDim + 8 * g;
+        u32x4 x[4];
+        for (int s = 0; s < 4; ++s) x[s] = *reinterpret_cast<const u32x4 *>(src + 32 * s);
+        const u32x4 x0 = rotate_chunk8(x[0], x[1], g, cs, sn);          // chunk g pairs with chunk g + 4
+        const u32x4 x1 = rotate_chunk8(x[1], x[0], g + 4, cs, sn);
+        af[0] = __builtin_bit_cast(bf16x8, x0);
+        af[1] = __builtin_bit_cast(bf16x8, x1);
+        af[2] = __builtin_bit_cast(bf16x8, x[2]);
+        af[3] = __builtin_bit_cast(bf16x8, x[3]);
+    } else {
+        for (int s = 0; s < 4; ++s) af[s] = bf16x8{};
     }
-    const bf16_t *kb = kbar + b * nblk_cap * kIdxDim;
+    const bf16_t *kb = keys + b * key_cap * kIdxDim;
     const int64_t wend = (w0 + kScanBlocksPerWave < o) ? w0 + kScanBlocksPerWave : o;
     for (int64_t c0 = w0; c0 < wend; c0 += 64) {
         bf16x8 bf[4][4];
@@ -256,39 +252,58 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(const int32_t *__restr
                 for (int e = 0; e < 4 && i + e < n; ++e) dst[i + e] = __uint_as_float(sl[wave][i + e]);
         }
     }
-    for (int x = threadIdx.x; x < kDecodeBins; x += 256)
-        if (lh[x]) atomicAdd(&dhist[b * kDecodeBins + x], lh[x]);
+    // ---- the work-group's histogram summary: thread t owns bins 8t .. 8t+7
+    constexpr int kPer = kDecodeBins / 256;
+    uint32_t h[kPer];
+    uint32_t part = 0;
+    for (int i = 0; i < kPer; ++i) {
+        h[i] = lh[threadIdx.x * kPer + i];
+        part += h[i];
+    }
+    uint32_t total;
+    const uint32_t below = block_scan_nt<256>(part, wsum, total);       // scores in lower threads' bins
+    uint32_t above = total - below - part;                               // scores in higher threads' bins
+    uint32_t emit = 0;
+    bool take[kPer];
+    for (int i = kPer - 1; i >= 0; --i) {
+        take[i] = h[i] != 0u && above < static_cast<uint32_t>(budget);
+        emit += take[i] ? 1u : 0u;
+        above += h[i];
+    }
+    uint32_t n_emit;
+    uint32_t pos = block_scan_nt<256>(emit, wsum, n_emit);
+    uint32_t *slot = summ + (b * nwg + blockIdx.x) * kSumSlot;
+    if (threadIdx.x == 0) slot[0] = n_emit;
+    for (int i = 0; i < kPer; ++i)
+        if (take[i]) slot[1 + pos++] = (static_cast<uint32_t>(threadIdx.x * kPer + i) << 21) | h[i];
 }
 
 hipError_t launch_decode_append(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
                                 int64_t ctx_bound, int64_t nblk_cap, const bf16_t *k, const bf16_t *v, const bf16_t *k_idx,
-                                const bf16_t *q_idx, bf16_t *k_cache, bf16_t *v_cache, bf16_t *kbar,
-                                bf16_t *kpend, bf16_t *qrot, uint32_t *dhist)
+                                bf16_t *k_cache, bf16_t *v_cache, bf16_t *kbar, bf16_t *kpend)
 {
     hipLaunchKernelGGL(decode_append_kernel, dim3(B), dim3(64), 0, st, tab, cache_len, ctx_bound, nblk_cap, k, v,
-                       k_idx, q_idx,
-                       k_cache, v_cache, kbar, kpend, qrot, dhist);
+                       k_idx, k_cache, v_cache, kbar, kpend);
     return hipGetLastError();
 }
 
-hipError_t launch_token_decode_append(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
-                                      int64_t ctx_bound, int64_t tok_cap, const bf16_t *k_idx, const bf16_t *q_idx,
-                                      bf16_t *ktok, bf16_t *qrot, uint32_t *dhist)
-{
-    hipLaunchKernelGGL(token_decode_append_kernel, dim3(B), dim3(64), 0, st, tab, cache_len, ctx_bound, tok_cap, k_idx,
-                       q_idx, ktok, qrot, dhist);
-    return hipGetLastError();
-}
+// Work-groups of the scan per row (the summary slots a row holds).
+int64_t decode_scan_wgs(int64_t ncol) { return (ncol + kScanBlocksPerWG - 1) / kScanBlocksPerWG; }
 
-hipError_t launch_decode_scan(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t ctx_bound, int rsh,
-                              int64_t nblk_cap, int64_t ncol, const bf16_t *qrot, const bf16_t *kbar, float *scores,
-                              uint32_t *dhist)
+// The scan over rows of at most ncol = ctx_bound >> rsh keys, with the append
+// of the new token done by each row's first work-group (a grid of at least one
+// work-group per row even when no row has a candidate).
+hipError_t launch_decode_scan(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
+                              int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol, int budget,
+                              const bf16_t *q_idx, bf16_t *keys, float *scores, uint32_t *summ,
+                              const bf16_t *k, const bf16_t *v, const bf16_t *k_idx, bf16_t *k_cache,
+                              bf16_t *v_cache, bf16_t *kpend, int64_t kv_blk_cap)
 {
-    const int64_t o_max = ctx_bound >> rsh;
-    if (o_max <= 0) return hipSuccess;
-    dim3 grid(static_cast<unsigned>((o_max + kScanBlocksPerWG - 1) / kScanBlocksPerWG), static_cast<unsigned>(B));
-    hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, cache_len, ctx_bound, rsh, nblk_cap, ncol, qrot, kbar,
-                       scores, dhist);
+    const int64_t nwg = decode_scan_wgs(ncol);
+    const DecodeAppend ap{k, v, k_idx, k_cache, v_cache, kpend, kv_blk_cap};
+    dim3 grid(static_cast<unsigned>(nwg), static_cast<unsigned>(B));
+    hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, tab, cache_len, ctx_bound, rsh, key_cap, ncol,
+                       budget, static_cast<int>(nwg), q_idx, keys, scores, summ, ap);
     return hipGetLastError();
 }
 

@@ -282,31 +282,11 @@ __global__ __launch_bounds__(kSelThreads) void select_fixup_kernel(
 }
 
 // Block-wide exclusive prefix sum for NT threads.
-template <int NT>
-__device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t *wsum /* LDS [NT/64] */, uint32_t &total)
-{
-    constexpr int NW = NT / 64;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t incl = v;
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t before = 0;
-    total = 0;
-    for (int w = 0; w < NW; ++w) {
-        if (w < wave) before += wsum[w];
-        total += wsum[w];
-    }
-    __syncthreads();
-    return before + incl - v;
-}
 
 // Decode selection from a score row whose histogram of bits 30..20 (2048
-// digits) the scan kernel already built: the boundary digit d* and the count
-// above it come from the histogram.  Inside digit d* the high 12 score bits
+// digits) above the boundary the scan kernel's work-groups already
+// summarised: the boundary digit d* and the count above it come from the sum
+// of their summaries.  Inside digit d* the high 12 score bits
 // are equal, so (low 20 bits, ordinal) is one 32-bit key ordering (score
 // desc, block desc).  Rows whose boundary digit holds more than kEqMax scores
 // use the plain radix select.
@@ -410,9 +390,10 @@ __device__ void boundary_digit(const uint32_t *__restrict__ dh, uint32_t K, uint
 
 __global__ __launch_bounds__(256) void select_chunk_kernel(
     const int32_t *__restrict__ cache_len, int64_t pos_bound, int rsh, int64_t ncol, const float *__restrict__ scores,
-    const uint32_t *__restrict__ dhist, int budget, int nchunk, int32_t *__restrict__ cnt,
+    const uint32_t *__restrict__ summ, int nwg, int budget, int nchunk, int32_t *__restrict__ cnt,
     int32_t *__restrict__ gtb, uint32_t *__restrict__ eqs, int32_t *__restrict__ eqi, uint32_t *__restrict__ rowinfo)
 {
+    __shared__ uint32_t lh[kSelMaxBins];
     __shared__ uint32_t wsum[4];
     __shared__ uint32_t s_dig[2];
     __shared__ uint32_t wcnt[2][4];
@@ -432,10 +413,23 @@ __global__ __launch_bounds__(256) void select_chunk_kernel(
         const int64_t j = wb + 64 * u + lane;
         v[u] = (j < c1) ? srow[j] : 0xFFFFFFFFu;          // sentinel: -1 as int32, below every threshold
     }
-    const uint32_t *dh = dhist + b * kSelMaxBins;
-    boundary_digit<256>(dh, static_cast<uint32_t>(budget), wsum, s_dig);
+    // the row's histogram above the boundary, from the scan work-groups' summaries
+    for (int x = tid; x < kSelMaxBins; x += 256) lh[x] = 0;
+    __syncthreads();
+    // 16 threads per summary slot, 16 slots at a time: the slots' reads overlap
+    const int64_t nw_b = (o + kScanBlocksPerWG - 1) / kScanBlocksPerWG;       // work-groups that scanned this row
+    for (int64_t w = tid >> 4; w < nw_b; w += 16) {
+        const uint32_t *slot = summ + (b * nwg + w) * kSumSlot;
+        const uint32_t n = min(slot[0], static_cast<uint32_t>(kSumWords));
+        for (uint32_t i = tid & 15; i < n; i += 16) {
+            const uint32_t word = slot[1 + i];
+            atomicAdd(&lh[word >> 21], word & 0x1FFFFFu);
+        }
+    }
+    __syncthreads();
+    boundary_digit<256>(lh, static_cast<uint32_t>(budget), wsum, s_dig);
     const uint32_t dstar = s_dig[0];
-    const uint32_t n_eq = dh[dstar];
+    const uint32_t n_eq = lh[dstar];
     const bool store_eq = n_eq <= static_cast<uint32_t>(kEqMax);
     if (ch == 0 && tid == 0) {                              // the row's boundary for stage two
         rowinfo[b * 3] = dstar;
@@ -560,7 +554,7 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
 }
 
 hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int rsh,
-                                   int64_t ncol, const float *scores, const uint32_t *dhist, int32_t *cnt,
+                                   int64_t ncol, const float *scores, const uint32_t *summ, int nwg, int32_t *cnt,
                                    int32_t *gtb, uint32_t *eqs, int32_t *eqi, uint32_t *rowinfo, int32_t *block_idx,
                                    int budget)
 {
@@ -568,8 +562,8 @@ hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cac
     const int64_t nchunk = (ncol + kSelChunk - 1) / kSelChunk;
     if (nchunk > kSelChunkMax) return hipErrorInvalidValue;
     hipLaunchKernelGGL(select_chunk_kernel, dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(B)), dim3(256),
-                       0, st, cache_len, pos_bound, rsh, ncol, scores, dhist, budget, static_cast<int>(nchunk), cnt, gtb,
-                       eqs, eqi, rowinfo);
+                       0, st, cache_len, pos_bound, rsh, ncol, scores, summ, nwg, budget, static_cast<int>(nchunk), cnt,
+                       gtb, eqs, eqi, rowinfo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(select_gather_kernel, dim3(static_cast<unsigned>(B)), dim3(kHistNT), 0, st, cache_len, pos_bound,

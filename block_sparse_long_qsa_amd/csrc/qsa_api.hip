@@ -41,13 +41,14 @@ hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int3
                                 const bf16_t *, const bf16_t *, const bf16_t *, const int32_t *, float *, float *,
                                 bf16_t *);
 hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const bf16_t *,
-                                const bf16_t *, const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *,
-                                bf16_t *, bf16_t *, uint32_t *);
-hipError_t launch_decode_scan(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, int64_t, const bf16_t *,
-                              const bf16_t *, float *, uint32_t *);
+                                const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *, bf16_t *);
+int64_t decode_scan_wgs(int64_t);
+hipError_t launch_decode_scan(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, int64_t, int,
+                              const bf16_t *, bf16_t *, float *, uint32_t *, const bf16_t *, const bf16_t *,
+                              const bf16_t *, bf16_t *, bf16_t *, bf16_t *, int64_t);
 hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, const float *,
-                                   const uint32_t *, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *, int32_t *,
-                                   int);
+                                   const uint32_t *, int, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *,
+                                   int32_t *, int);
 hipError_t launch_attend_stats(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int, float, const bf16_t *,
                                const bf16_t *, const bf16_t *, const int32_t *, bf16_t *, float *);
 hipError_t launch_train_kl(const Tables &, hipStream_t, bool, int32_t, int64_t, int64_t, int, float, const bf16_t *,
@@ -64,8 +65,7 @@ hipError_t launch_gdn_scan(hipStream_t, int, const int32_t *, int64_t, int, int,
                            const bf16_t *, const bf16_t *, const float *, const float *, bf16_t *, float *,
                            const bf16_t *);
 size_t gdn_workspace_bytes(int, int64_t, int, int);
-hipError_t launch_token_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t,
-                                      const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, uint32_t *);
+
 }  // namespace qsa
 
 using namespace qsa;
@@ -173,8 +173,8 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
 constexpr int64_t kDecodeChunkMax = 1024;
 
 struct DecLayout {
-    size_t qrot, scores, bidx, part_o, part_ml, hist, s2cnt, s2gt, s2eqs, s2eqi, s2row, total;
-    int64_t ncol, nchunk;
+    size_t scores, bidx, part_o, part_ml, summ, s2cnt, s2gt, s2eqs, s2eqi, s2row, total;
+    int64_t ncol, nchunk, nwg;
     int nsplit;
 };
 // rsh: log2 of the indexer's compression ratio (2: pooled micro-blocks; 0: tokens).
@@ -183,18 +183,19 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int r
     d.ncol = ctx_bound >> rsh;
     if (d.ncol < 1) d.ncol = 1;
     d.nsplit = decode_splits(B);
-    d.qrot = 0;
-    d.scores = align_up(static_cast<size_t>(B) * kIdxHeads * kIdxDim * 2);
+    d.nwg = decode_scan_wgs(d.ncol);
+    d.scores = 0;
     d.bidx = d.scores + align_up(static_cast<size_t>(B) * d.ncol * 4);
     d.part_o = d.bidx + align_up(static_cast<size_t>(B) * h->p.budget_blocks * 4);
     const size_t slots = static_cast<size_t>(B) * kKVHeads * d.nsplit * kGroup;
     d.part_ml = d.part_o + align_up(slots * kHeadDim * 4);
-    d.hist = d.part_ml + align_up(slots * 2 * 4);
+    // the scan work-groups' histogram summaries, one slot per (row, work-group)
+    d.summ = d.part_ml + align_up(slots * 2 * 4);
     // two-stage selection: per 4,096-score chunk a count pair and the chunk's
     // lists (at most budget blocks above the boundary digit, 1,024 at it)
     d.nchunk = (d.ncol + 4095) / 4096;
     const size_t nck = static_cast<size_t>(B) * d.nchunk;
-    d.s2cnt = d.hist + align_up(static_cast<size_t>(B) * 2048 * 4);
+    d.s2cnt = d.summ + align_up(static_cast<size_t>(B) * d.nwg * kSumSlot * 4);
     d.s2gt = d.s2cnt + align_up(nck * 2 * 4);
     d.s2eqs = d.s2gt + align_up(nck * kMaxBudget * 4);
     d.s2eqi = d.s2eqs + align_up(nck * 1024 * 4);
@@ -271,32 +272,42 @@ qsa_status check_decode(const qsa_handle *h, int32_t B, int64_t ctx_bound, std::
     return QSA_OK;
 }
 
-// One decode step with its scratch at w (layout d): append -> scan -> two-stage
-// select -> split-K attention -> merge.
+// The selection half of a decode step with its scratch at w (layout d): the
+// scan (whose first work-group per row appends the new token: K~/V when k is
+// given, the indexer key pooled at r = 4 or rotated into the token keys at
+// r = 1) -> the two-stage select from the scan's histogram summaries.
+hipError_t run_decode_select(const qsa_handle *h, hipStream_t st, int32_t B, const int32_t *cache_len,
+                             int64_t ctx_bound, int rsh, int64_t key_cap, const uint16_t *q_idx, uint16_t *keys,
+                             const uint16_t *k, const uint16_t *v, const uint16_t *k_idx, uint16_t *k_cache,
+                             uint16_t *v_cache, uint16_t *kpend, int32_t *bidx, char *w, const DecLayout &d) {
+    float *scores = reinterpret_cast<float *>(w + d.scores);
+    uint32_t *summ = reinterpret_cast<uint32_t *>(w + d.summ);
+    hipError_t e = launch_decode_scan(tables(h), st, B, cache_len, ctx_bound, rsh, key_cap, d.ncol,
+                                      h->p.budget_blocks, q_idx, keys, scores, summ, k, v, k_idx, k_cache, v_cache,
+                                      kpend, nblk_cap(h));
+    if (e == hipSuccess)
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, rsh, d.ncol, scores, summ, static_cast<int>(d.nwg),
+                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
+                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
+                                    reinterpret_cast<uint32_t *>(w + d.s2row), bidx, h->p.budget_blocks);
+    return e;
+}
+
+// One decode step with its scratch at w (layout d): scan (+ append) ->
+// two-stage select -> split-K attention -> merge.
 hipError_t run_decode(const qsa_handle *h, hipStream_t st, int32_t B, const int32_t *cache_len, int64_t ctx_bound,
                       const uint16_t *q, const uint16_t *k, const uint16_t *v, const uint16_t *q_idx,
                       const uint16_t *k_idx, uint16_t *k_cache, uint16_t *v_cache, uint16_t *kbar_cache,
                       uint16_t *kpend, uint16_t *out, int32_t *block_idx, char *w, const DecLayout &d) {
-    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
-    float *scores = reinterpret_cast<float *>(w + d.scores);
     int32_t *bidx = block_idx ? block_idx : reinterpret_cast<int32_t *>(w + d.bidx);
     float *part_o = reinterpret_cast<float *>(w + d.part_o);
     float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
-    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
-    const int budget = h->p.budget_blocks;
     const int64_t nbc = nblk_cap(h);
-    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, q_idx, k_cache,
-                                        v_cache, kbar_cache, kpend, qrot, dhist);
+    hipError_t e = run_decode_select(h, st, B, cache_len, ctx_bound, 2, nbc, q_idx, kbar_cache, k, v, k_idx, k_cache,
+                                     v_cache, kpend, bidx, w, d);
     if (e == hipSuccess)
-        e = launch_decode_scan(st, B, cache_len, ctx_bound, 2, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
-    if (e == hipSuccess)
-        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 2, d.ncol, scores, dhist,
-                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
-                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
-                                    reinterpret_cast<uint32_t *>(w + d.s2row), bidx, budget);
-    if (e == hipSuccess)
-        e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, budget, d.nsplit, h->sigma, q,
-                                 k_cache, v_cache, bidx, part_o, part_ml, out);
+        e = launch_attend_decode(tables(h), st, B, cache_len, nullptr, ctx_bound, nbc, h->p.budget_blocks, d.nsplit,
+                                 h->sigma, q, k_cache, v_cache, bidx, part_o, part_ml, out);
     return e;
 }
 
@@ -584,10 +595,9 @@ qsa_status qsa_decode_reuse(const qsa_handle *h, void *stream, int32_t B, const 
     char *w = static_cast<char *>(ws);
     float *part_o = reinterpret_cast<float *>(w + d.part_o);
     float *part_ml = reinterpret_cast<float *>(w + d.part_ml);
-    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
     const int64_t nbc = nblk_cap(h);
-    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, nullptr, k_cache,
-                                        v_cache, kbar_cache, kpend, nullptr, dhist);
+    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, k, v, k_idx, k_cache, v_cache,
+                                        kbar_cache, kpend);
     if (e == hipSuccess)
         e = launch_attend_decode(tables(h), st, B, cache_len, sel_pos, ctx_bound, nbc, h->p.budget_blocks, d.nsplit,
                                  h->sigma, q, k_cache, v_cache, block_idx, part_o, part_ml, out);
@@ -612,19 +622,8 @@ qsa_status qsa_index_decode(const qsa_handle *h, void *stream, int32_t B, const 
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(ws);
-    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
-    float *scores = reinterpret_cast<float *>(w + d.scores);
-    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
-    const int64_t nbc = nblk_cap(h);
-    hipError_t e = launch_decode_append(tables(h), st, B, cache_len, ctx_bound, nbc, nullptr, nullptr, k_idx, q_idx,
-                                        nullptr, nullptr, kbar_cache, kpend, qrot, dhist);
-    if (e == hipSuccess)
-        e = launch_decode_scan(st, B, cache_len, ctx_bound, 2, nbc, d.ncol, qrot, kbar_cache, scores, dhist);
-    if (e == hipSuccess)
-        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 2, d.ncol, scores, dhist,
-                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
-                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
-                                    reinterpret_cast<uint32_t *>(w + d.s2row), block_idx, h->p.budget_blocks);
+    const hipError_t e = run_decode_select(h, st, B, cache_len, ctx_bound, 2, nblk_cap(h), q_idx, kbar_cache, nullptr,
+                                           nullptr, k_idx, nullptr, nullptr, kpend, block_idx, w, d);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 
@@ -663,19 +662,8 @@ qsa_status qsa_token_index_decode(const qsa_handle *h, void *stream, int32_t B, 
     if (!guard.ok) return hip_fail(hipErrorInvalidDevice);
     hipStream_t st = static_cast<hipStream_t>(stream);
     char *w = static_cast<char *>(ws);
-    bf16_t *qrot = reinterpret_cast<bf16_t *>(w + d.qrot);
-    float *scores = reinterpret_cast<float *>(w + d.scores);
-    uint32_t *dhist = reinterpret_cast<uint32_t *>(w + d.hist);
-    const int64_t cap = h->p.max_ctx;
-    hipError_t e = launch_token_decode_append(tables(h), st, B, cache_len, ctx_bound, cap, k_idx, q_idx, ktok_cache,
-                                              qrot, dhist);
-    if (e == hipSuccess)
-        e = launch_decode_scan(st, B, cache_len, ctx_bound, 0, cap, d.ncol, qrot, ktok_cache, scores, dhist);
-    if (e == hipSuccess)
-        e = launch_select_two_stage(st, B, cache_len, ctx_bound, 0, d.ncol, scores, dhist,
-                                    reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
-                                    reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
-                                    reinterpret_cast<uint32_t *>(w + d.s2row), token_idx, h->p.budget_blocks);
+    const hipError_t e = run_decode_select(h, st, B, cache_len, ctx_bound, 0, h->p.max_ctx, q_idx, ktok_cache,
+                                           nullptr, nullptr, k_idx, nullptr, nullptr, nullptr, token_idx, w, d);
     return e == hipSuccess ? QSA_OK : hip_fail(e);
 }
 

@@ -31,6 +31,14 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// Decode score scan geometry: each wave streams 512 keys, a work-group of 4
+// waves 2,048; each work-group leaves a summary of its score histogram in a
+// slot of 1 + kSumWords words (see decode_scan_kernel).
+constexpr int kScanBlocksPerWave = 512;
+constexpr int kScanBlocksPerWG = 4 * kScanBlocksPerWave;
+constexpr int kSumWords = kMaxBudget;
+constexpr int kSumSlot = 1 + kSumWords;
+
 // Handle contents visible to the launchers.
 struct Tables {
     const float *cos;   // [max_ctx][32]
@@ -160,6 +168,30 @@ __device__ __forceinline__ void bitonic_stages(uint32_t (&k)[R], int lane) {
 template <int R>
 __device__ __forceinline__ void wave_sort_desc(uint32_t (&k)[R], int lane) {
     bitonic_stages<R, 2>(k, lane);
+}
+
+// Exclusive prefix sum of v over the NT threads of a workgroup (every thread
+// calls it); total receives the sum over all threads.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_nt(uint32_t v, uint32_t *wsum /* LDS [NT/64] */, uint32_t &total)
+{
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t incl = v;
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = 0;
+    total = 0;
+    for (int w = 0; w < NW; ++w) {
+        if (w < wave) before += wsum[w];
+        total += wsum[w];
+    }
+    __syncthreads();
+    return before + incl - v;
 }
 
 // Write the n (<= 64*R) selected block ids of sel[] to out[] ascending.
