@@ -226,6 +226,119 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(
     }
 }
 
+// The decode walk: the arithmetic of attend_chunks with the gathers of the
+// next chunk issued while the current one computes -- its K~ once the current
+// logits are formed, its V after the current PV product -- so that a wave
+// keeps a chunk's worth of loads in flight through its walk with no more
+// registers than one chunk needs.
+__device__ __forceinline__ void fetch_chunk_k(const bf16_t *__restrict__ kc, const int32_t *__restrict__ sel,
+                                              int sel_off, int n_sel, int64_t o0, int64_t o, int own_last, int c,
+                                              bf16x8 (&kf)[2][8])
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int lb = kChunkBlocks * c;
+    for (int t = 0; t < 2; ++t) {
+        int64_t blk;
+        uint32_t m;
+        list_entry<false>(sel, sel_off, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, blk, m);
+        const bf16_t *src = kc + blk * kBlockElems + (r & 3) * 32 + 8 * g;
+        for (int s = 0; s < 8; ++s) kf[t][s] = *reinterpret_cast<const bf16x8 *>(src + s * 128);
+    }
+}
+
+__device__ __forceinline__ void fetch_chunk_v(const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
+                                              int sel_off, int n_sel, int64_t o0, int64_t o, int own_last, int c,
+                                              u32x2 (&vraw)[16][2], uint32_t (&vmask)[2])
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int lb = kChunkBlocks * c;
+    for (int t = 0; t < 2; ++t) {
+        int64_t blk;
+        list_entry<false>(sel, sel_off, n_sel, o0, o, lb + 4 * t + g, own_last, blk, vmask[t]);
+        const bf16_t *src = vc + blk * kBlockElems + r * kBlock;
+        for (int n = 0; n < 16; ++n) vraw[n][t] = *reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock);
+    }
+}
+
+// One chunk of the decode walk; with kNext the next chunk's K~ is fetched
+// after the logits and its V after the PV product.  The last chunk of a walk
+// is a separate instance without fetches, so that every instance is straight
+// code and the wait before a product counts only the loads it needs.
+template <bool kNext>
+__device__ __forceinline__ void decode_chunk(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
+                                             const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
+                                             int sel_off, int n_sel, int64_t o0, int64_t o, int own_last, int c,
+                                             float c2, bf16x8 (&kf)[2][8], u32x2 (&vraw)[16][2],
+                                             uint32_t (&vmask)[2], RowState &st)
+{
+    // ---- S^T = K~ . Q~^T, then the next chunk's K~ into the freed registers
+    f32x4 sc[2];
+    for (int t = 0; t < 2; ++t) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], qf[s], acc, 0, 0, 0);
+        sc[t] = acc;
+    }
+    if constexpr (kNext) fetch_chunk_k(kc, sel, sel_off, n_sel, o0, o, own_last, c + 1, kf);
+    // lane holds tokens j = 0..3 of list entry 8c + 4t + g for head l%16
+    float cmax = -INFINITY;
+    for (int t = 0; t < 2; ++t) {
+        for (int j = 0; j < 4; ++j) {
+            if (!((vmask[t] >> j) & 1u)) sc[t][j] = -INFINITY;
+            cmax = fmaxf(cmax, sc[t][j]);
+        }
+    }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    const float m_new = fmaxf(st.m, cmax);
+    const float m_ref = (m_new == -INFINITY) ? 0.f : m_new;     // as in attend_chunks
+    const float alpha = exp2f((st.m - m_ref) * c2);
+    st.m = m_new;
+    uint32_t pw[4];
+    float psum = 0.f;
+    for (int t = 0; t < 2; ++t) {
+        float p[4];
+        for (int j = 0; j < 4; ++j) p[j] = exp2f((sc[t][j] - m_ref) * c2);
+        pw[2 * t] = pack_bf16x2(p[0], p[1]);
+        pw[2 * t + 1] = pack_bf16x2(p[2], p[3]);
+        for (int j = 0; j < 4; ++j) psum += bf16_to_f32(f32_to_bf16(p[j]));
+    }
+    st.l = st.l * alpha + psum;
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, u32x4{pw[0], pw[1], pw[2], pw[3]});
+    // ---- O^T += V^T . P^T (masked tokens' V zeroed), then the next chunk's V
+    for (int n = 0; n < 16; ++n) {
+        u32x2 lo = vraw[n][0], hi = vraw[n][1];
+        const uint32_t m0 = vmask[0], m1 = vmask[1];
+        lo[0] &= ((m0 & 1u) ? 0xFFFFu : 0u) | ((m0 & 2u) ? 0xFFFF0000u : 0u);
+        lo[1] &= ((m0 & 4u) ? 0xFFFFu : 0u) | ((m0 & 8u) ? 0xFFFF0000u : 0u);
+        hi[0] &= ((m1 & 1u) ? 0xFFFFu : 0u) | ((m1 & 2u) ? 0xFFFF0000u : 0u);
+        hi[1] &= ((m1 & 4u) ? 0xFFFFu : 0u) | ((m1 & 8u) ? 0xFFFF0000u : 0u);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        f32x4 acc = st.o[n];
+        for (int j = 0; j < 4; ++j) acc[j] *= alpha;
+        st.o[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, acc, 0, 0, 0);
+    }
+    if constexpr (kNext) fetch_chunk_v(vc, sel, sel_off, n_sel, o0, o, own_last, c + 1, vraw, vmask);
+}
+
+__device__ __forceinline__ void decode_walk(const bf16x8 (&qf)[8], const bf16_t *__restrict__ kc,
+                                            const bf16_t *__restrict__ vc, const int32_t *__restrict__ sel,
+                                            int sel_off, int n_sel, int64_t o0, int64_t o, int own_last, int c_lo,
+                                            int c_hi, float c2, RowState &st)
+{
+    if (c_lo >= c_hi) return;
+    bf16x8 kf[2][8];
+    u32x2 vraw[16][2];
+    uint32_t vmask[2];
+    fetch_chunk_k(kc, sel, sel_off, n_sel, o0, o, own_last, c_lo, kf);
+    fetch_chunk_v(vc, sel, sel_off, n_sel, o0, o, own_last, c_lo, vraw, vmask);
+    int c = c_lo;
+    for (; c + 1 < c_hi; ++c)
+        decode_chunk<true>(qf, kc, vc, sel, sel_off, n_sel, o0, o, own_last, c, c2, kf, vraw, vmask, st);
+    decode_chunk<false>(qf, kc, vc, sel, sel_off, n_sel, o0, o, own_last, c, c2, kf, vraw, vmask, st);
+}
+
 // Decode, split over the token list: one wave per (split, group, sequence)
 // writes its unnormalised partial (m, l, O) for the 12 heads.  With sel_pos
 // (a reused selection) the list is block_idx as selected at position
@@ -266,7 +379,7 @@ __global__ __launch_bounds__(64) void attend_decode_split_kernel(
         load_q_frags(q + b * kQHeads * kHeadDim, grp, pos, tab, qf);
         const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
         const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-        attend_chunks<false>(qf, kc, vc, lsel, e_lo, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
+        decode_walk(qf, kc, vc, lsel, e_lo, n_sel, o0, o, own_last, c_lo, c_hi, c2, st);
     }
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);

@@ -3,6 +3,8 @@
 // 인덱서 자체의 비용을 줄이는 희소 어텐션": the indexer compares the query with the
 // mean-pooled, block-start-rotated keys of fully observed blocks, so one
 // decode step reads n/4 pooled keys instead of n token keys).
+#include <type_traits>
+
 #include "qsa_common.h"
 
 namespace qsa {
@@ -138,6 +140,26 @@ __device__ __forceinline__ u32x4 rotate_chunk8(u32x4 x, u32x4 xp, int c, const f
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// rotate_chunk8 for a chunk of the rotary dims with its 8 angles' cosines and
+// sines already loaded (tc[k], ts[k]: pair j0 + k); first_half: the chunk holds
+// dims j of the pairs (j, j + 32), else dims j + 32.
+__device__ __forceinline__ u32x4 rotate_chunk8_t(u32x4 x, u32x4 xp, bool first_half, const float (&tc)[8],
+                                                 const float (&ts)[8]) {
+    uint32_t w[4];
+    for (int i = 0; i < 4; ++i) {
+        float r[2];
+        for (int e = 0; e < 2; ++e) {
+            float me = __uint_as_float(e ? (x[i] & 0xFFFF0000u) : (x[i] << 16));
+            float pa = __uint_as_float(e ? (xp[i] & 0xFFFF0000u) : (xp[i] << 16));
+            float a = first_half ? me : pa, bb = first_half ? pa : me;
+            rotate_pair(a, bb, tc[2 * i + e], ts[2 * i + e]);
+            r[e] = first_half ? a : bb;
+        }
+        w[i] = pack_bf16x2(r[0], r[1]);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
 // Score scan: scores[b][blk] = sum_h ReLU(<q~_h, k̄_blk>) for blk < floor(p/r),
 // r = 1 << rsh (4: pooled micro-blocks; 1: one rotated key per token).
 // v_mfma_f32_16x16x32_bf16 with A = q~ (4 real rows of 16), B = 16 keys;
@@ -170,12 +192,13 @@ struct DecodeAppend {
 
 __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int32_t *__restrict__ cache_len,
                                                           int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol,
-                                                          int budget, int nwg, const bf16_t *__restrict__ q_idx,
+                                                          int budget, int bpw, int nwg,
+                                                          const bf16_t *__restrict__ q_idx,
                                                           bf16_t *__restrict__ keys, float *__restrict__ scores,
                                                           uint32_t *__restrict__ summ, DecodeAppend ap)
 {
     __shared__ uint32_t lh[kDecodeBins];
-    __shared__ __attribute__((aligned(16))) uint32_t sl[4][kScanBlocksPerWave];   // each wave's score bits
+    __shared__ __attribute__((aligned(16))) uint32_t sl[4][kScanBlocksPerWaveMax];   // each wave's score bits
     __shared__ uint32_t wsum[4];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -195,21 +218,44 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
                 rotate_chunk8(x, xp, lane, cs, sn);
         }
     }
-    if (static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG >= o) return;     // whole workgroup idle
+    if (static_cast<int64_t>(blockIdx.x) * 4 * bpw >= o) return;     // whole workgroup idle
     for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
     __syncthreads();
-    const int64_t w0 = static_cast<int64_t>(blockIdx.x) * kScanBlocksPerWG + wave * kScanBlocksPerWave;
+    const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * bpw;
     if (w0 < o) {
     const int r = lane & 15, g = lane >> 4;
+    const bf16_t *kb = keys + b * key_cap * kIdxDim;
+    const int64_t wend = (w0 + bpw < o) ? w0 + bpw : o;
+    // B = 16 blocks of keys per MFMA, 4 MFMAs of 64 blocks per step; blocks
+    // past the row (o) read block w0 instead (in bounds, results discarded)
+    auto load_step = [&](int64_t c0, bf16x8 (&bf)[4][4]) {
+        for (int u = 0; u < 4; ++u) {
+            int64_t blk = c0 + 16 * u + r;
+            if (blk >= o) blk = w0;
+            for (int s = 0; s < 4; ++s)
+                bf[u][s] = *reinterpret_cast<const bf16x8 *>(kb + blk * kIdxDim + 32 * s + 8 * g);
+        }
+    };
     // A = q~: lane (head r < 4, k-group g) holds dims 32s + 8g .. +7 of head r,
-    // rotated here at p (pairs j, j + 32 sit in k-steps 0 and 1 of one lane)
-    bf16x8 af[4];
+    // rotated here at p (pairs j, j + 32 sit in k-steps 0 and 1 of one lane).
+    // Its loads go first and the first step's keys right after, so that the
+    // rotation waits for the query alone.
+    u32x4 x[4];
+    float tc[8], ts[8];
     if (r < kIdxHeads) {
         const bf16_t *src = q_idx + (b * kIdxHeads + r) * kIdxDim + 8 * g;
-        u32x4 x[4];
         for (int s = 0; s < 4; ++s) x[s] = *reinterpret_cast<const u32x4 *>(src + 32 * s);
-        const u32x4 x0 = rotate_chunk8(x[0], x[1], g, cs, sn);          // chunk g pairs with chunk g + 4
-        const u32x4 x1 = rotate_chunk8(x[1], x[0], g + 4, cs, sn);
+        for (int e = 0; e < 8; ++e) {
+            tc[e] = cs[8 * g + e];
+            ts[e] = sn[8 * g + e];
+        }
+    }
+    bf16x8 bf[4][4];
+    load_step(w0, bf);
+    bf16x8 af[4];
+    if (r < kIdxHeads) {
+        const u32x4 x0 = rotate_chunk8_t(x[0], x[1], true, tc, ts);      // chunk g pairs with chunk g + 4
+        const u32x4 x1 = rotate_chunk8_t(x[1], x[0], false, tc, ts);
         af[0] = __builtin_bit_cast(bf16x8, x0);
         af[1] = __builtin_bit_cast(bf16x8, x1);
         af[2] = __builtin_bit_cast(bf16x8, x[2]);
@@ -217,32 +263,33 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     } else {
         for (int s = 0; s < 4; ++s) af[s] = bf16x8{};
     }
-    const bf16_t *kb = keys + b * key_cap * kIdxDim;
-    const int64_t wend = (w0 + kScanBlocksPerWave < o) ? w0 + kScanBlocksPerWave : o;
-    for (int64_t c0 = w0; c0 < wend; c0 += 64) {
-        bf16x8 bf[4][4];
+    // One step: the 16 MFMAs, then (kNext) the next step's keys into the
+    // registers they freed, then the scores of this step into LDS and the
+    // histogram -- the loads stay in flight while the scores are stored.
+    auto step = [&](int64_t c0, auto next) {
+        f32x4 acc[4];
         for (int u = 0; u < 4; ++u) {
-            int64_t blk = c0 + 16 * u + r;
-            if (blk >= o) blk = w0;                      // in bounds; result discarded
-            for (int s = 0; s < 4; ++s)
-                bf[u][s] = *reinterpret_cast<const bf16x8 *>(kb + blk * kIdxDim + 32 * s + 8 * g);
+            acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; ++s) acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[u][s], acc[u], 0, 0, 0);
         }
+        if constexpr (decltype(next)::value) load_step(c0 + 64, bf);
         for (int u = 0; u < 4; ++u) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s], bf[u][s], acc, 0, 0, 0);
             const int64_t blk = c0 + 16 * u + r;
             if (g == 0 && blk < o) {
-                float sc = fmaxf(acc[0], 0.f) + fmaxf(acc[1], 0.f) + fmaxf(acc[2], 0.f) + fmaxf(acc[3], 0.f);
+                float sc = fmaxf(acc[u][0], 0.f) + fmaxf(acc[u][1], 0.f) + fmaxf(acc[u][2], 0.f) + fmaxf(acc[u][3], 0.f);
                 const uint32_t bits = __float_as_uint(sc) & 0x7FFFFFFFu;
                 sl[wave][blk - w0] = bits;
                 atomicAdd(&lh[bits >> 20], 1u);
             }
         }
-    }
+    };
+    int64_t c0 = w0;
+    for (; c0 + 64 < wend; c0 += 64) step(c0, std::true_type{});
+    step(c0, std::false_type{});
     }
     __syncthreads();
     if (w0 < o) {   // the wave's scores, blocks w0 .. wend-1
-        const int64_t n = ((w0 + kScanBlocksPerWave < o) ? w0 + kScanBlocksPerWave : o) - w0;
+        const int64_t n = ((w0 + bpw < o) ? w0 + bpw : o) - w0;
         float *dst = scores + b * ncol + w0;
         const bool vec = ((b * ncol + w0) & 3) == 0;
         for (int i = 4 * lane; i < n; i += 256) {
@@ -288,22 +335,23 @@ hipError_t launch_decode_append(const Tables &tab, hipStream_t st, int32_t B, co
 }
 
 // Work-groups of the scan per row (the summary slots a row holds).
-int64_t decode_scan_wgs(int64_t ncol) { return (ncol + kScanBlocksPerWG - 1) / kScanBlocksPerWG; }
+int64_t decode_scan_wgs(int64_t ncol, int bpw) { return (ncol + 4 * bpw - 1) / (4 * bpw); }
 
 // The scan over rows of at most ncol = ctx_bound >> rsh keys, with the append
 // of the new token done by each row's first work-group (a grid of at least one
 // work-group per row even when no row has a candidate).
 hipError_t launch_decode_scan(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
-                              int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol, int budget,
+                              int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol, int budget, int bpw,
                               const bf16_t *q_idx, bf16_t *keys, float *scores, uint32_t *summ,
                               const bf16_t *k, const bf16_t *v, const bf16_t *k_idx, bf16_t *k_cache,
                               bf16_t *v_cache, bf16_t *kpend, int64_t kv_blk_cap)
 {
-    const int64_t nwg = decode_scan_wgs(ncol);
+    if (bpw < 64 || bpw > kScanBlocksPerWaveMax || bpw % 64 != 0) return hipErrorInvalidValue;
+    const int64_t nwg = decode_scan_wgs(ncol, bpw);
     const DecodeAppend ap{k, v, k_idx, k_cache, v_cache, kpend, kv_blk_cap};
     dim3 grid(static_cast<unsigned>(nwg), static_cast<unsigned>(B));
     hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, tab, cache_len, ctx_bound, rsh, key_cap, ncol,
-                       budget, static_cast<int>(nwg), q_idx, keys, scores, summ, ap);
+                       budget, bpw, static_cast<int>(nwg), q_idx, keys, scores, summ, ap);
     return hipGetLastError();
 }
 

@@ -390,7 +390,7 @@ __device__ void boundary_digit(const uint32_t *__restrict__ dh, uint32_t K, uint
 
 __global__ __launch_bounds__(256) void select_chunk_kernel(
     const int32_t *__restrict__ cache_len, int64_t pos_bound, int rsh, int64_t ncol, const float *__restrict__ scores,
-    const uint32_t *__restrict__ summ, int nwg, int budget, int nchunk, int32_t *__restrict__ cnt,
+    const uint32_t *__restrict__ summ, int nwg, int bpw, int budget, int nchunk, int32_t *__restrict__ cnt,
     int32_t *__restrict__ gtb, uint32_t *__restrict__ eqs, int32_t *__restrict__ eqi, uint32_t *__restrict__ rowinfo)
 {
     __shared__ uint32_t lh[kSelMaxBins];
@@ -417,7 +417,7 @@ __global__ __launch_bounds__(256) void select_chunk_kernel(
     for (int x = tid; x < kSelMaxBins; x += 256) lh[x] = 0;
     __syncthreads();
     // 16 threads per summary slot, 16 slots at a time: the slots' reads overlap
-    const int64_t nw_b = (o + kScanBlocksPerWG - 1) / kScanBlocksPerWG;       // work-groups that scanned this row
+    const int64_t nw_b = (o + 4 * bpw - 1) / (4 * bpw);       // work-groups that scanned this row
     for (int64_t w = tid >> 4; w < nw_b; w += 16) {
         const uint32_t *slot = summ + (b * nwg + w) * kSumSlot;
         const uint32_t n = min(slot[0], static_cast<uint32_t>(kSumWords));
@@ -554,7 +554,7 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
 }
 
 hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int rsh,
-                                   int64_t ncol, const float *scores, const uint32_t *summ, int nwg, int32_t *cnt,
+                                   int64_t ncol, const float *scores, const uint32_t *summ, int nwg, int bpw, int32_t *cnt,
                                    int32_t *gtb, uint32_t *eqs, int32_t *eqi, uint32_t *rowinfo, int32_t *block_idx,
                                    int budget)
 {
@@ -562,7 +562,7 @@ hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cac
     const int64_t nchunk = (ncol + kSelChunk - 1) / kSelChunk;
     if (nchunk > kSelChunkMax) return hipErrorInvalidValue;
     hipLaunchKernelGGL(select_chunk_kernel, dim3(static_cast<unsigned>(nchunk), static_cast<unsigned>(B)), dim3(256),
-                       0, st, cache_len, pos_bound, rsh, ncol, scores, summ, nwg, budget, static_cast<int>(nchunk), cnt,
+                       0, st, cache_len, pos_bound, rsh, ncol, scores, summ, nwg, bpw, budget, static_cast<int>(nchunk), cnt,
                        gtb, eqs, eqi, rowinfo);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -42,12 +42,12 @@ hipError_t launch_attend_decode(const Tables &, hipStream_t, int32_t, const int3
                                 bf16_t *);
 hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int64_t, const bf16_t *,
                                 const bf16_t *, const bf16_t *, bf16_t *, bf16_t *, bf16_t *, bf16_t *);
-int64_t decode_scan_wgs(int64_t);
+int64_t decode_scan_wgs(int64_t, int);
 hipError_t launch_decode_scan(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, int64_t, int,
-                              const bf16_t *, bf16_t *, float *, uint32_t *, const bf16_t *, const bf16_t *,
+                              int, const bf16_t *, bf16_t *, float *, uint32_t *, const bf16_t *, const bf16_t *,
                               const bf16_t *, bf16_t *, bf16_t *, bf16_t *, int64_t);
 hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, const float *,
-                                   const uint32_t *, int, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *,
+                                   const uint32_t *, int, int, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *,
                                    int32_t *, int);
 hipError_t launch_attend_stats(const Tables &, hipStream_t, int32_t, int64_t, int64_t, int, float, const bf16_t *,
                                const bf16_t *, const bf16_t *, const int32_t *, bf16_t *, float *);
@@ -175,15 +175,27 @@ constexpr int64_t kDecodeChunkMax = 1024;
 struct DecLayout {
     size_t scores, bidx, part_o, part_ml, summ, s2cnt, s2gt, s2eqs, s2eqi, s2row, total;
     int64_t ncol, nchunk, nwg;
-    int nsplit;
+    int nsplit, bpw;
 };
+
+// Keys per wave of the decode scan: about one wave per SIMD over all rows
+// (long streams per wave read faster than many short ones), a multiple of 64
+// between 256 and kScanBlocksPerWaveMax.
+int decode_scan_bpw(int32_t B, int64_t ncol) {
+    const int64_t per = (static_cast<int64_t>(B) * ncol + 1023) / 1024;
+    int64_t bpw = (per + 63) / 64 * 64;
+    if (bpw < 256) bpw = 256;
+    if (bpw > kScanBlocksPerWaveMax) bpw = kScanBlocksPerWaveMax;
+    return static_cast<int>(bpw);
+}
 // rsh: log2 of the indexer's compression ratio (2: pooled micro-blocks; 0: tokens).
 DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int rsh = 2) {
     DecLayout d{};
     d.ncol = ctx_bound >> rsh;
     if (d.ncol < 1) d.ncol = 1;
     d.nsplit = decode_splits(B);
-    d.nwg = decode_scan_wgs(d.ncol);
+    d.bpw = decode_scan_bpw(B, d.ncol);
+    d.nwg = decode_scan_wgs(d.ncol, d.bpw);
     d.scores = 0;
     d.bidx = d.scores + align_up(static_cast<size_t>(B) * d.ncol * 4);
     d.part_o = d.bidx + align_up(static_cast<size_t>(B) * h->p.budget_blocks * 4);
@@ -283,10 +295,10 @@ hipError_t run_decode_select(const qsa_handle *h, hipStream_t st, int32_t B, con
     float *scores = reinterpret_cast<float *>(w + d.scores);
     uint32_t *summ = reinterpret_cast<uint32_t *>(w + d.summ);
     hipError_t e = launch_decode_scan(tables(h), st, B, cache_len, ctx_bound, rsh, key_cap, d.ncol,
-                                      h->p.budget_blocks, q_idx, keys, scores, summ, k, v, k_idx, k_cache, v_cache,
+                                      h->p.budget_blocks, d.bpw, q_idx, keys, scores, summ, k, v, k_idx, k_cache, v_cache,
                                       kpend, nblk_cap(h));
     if (e == hipSuccess)
-        e = launch_select_two_stage(st, B, cache_len, ctx_bound, rsh, d.ncol, scores, summ, static_cast<int>(d.nwg),
+        e = launch_select_two_stage(st, B, cache_len, ctx_bound, rsh, d.ncol, scores, summ, static_cast<int>(d.nwg), d.bpw,
                                     reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),
                                     reinterpret_cast<uint32_t *>(w + d.s2eqs), reinterpret_cast<int32_t *>(w + d.s2eqi),
                                     reinterpret_cast<uint32_t *>(w + d.s2row), bidx, h->p.budget_blocks);

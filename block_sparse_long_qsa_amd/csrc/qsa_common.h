@@ -31,11 +31,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Decode score scan geometry: each wave streams 512 keys, a work-group of 4
-// waves 2,048; each work-group leaves a summary of its score histogram in a
-// slot of 1 + kSumWords words (see decode_scan_kernel).
-constexpr int kScanBlocksPerWave = 512;
-constexpr int kScanBlocksPerWG = 4 * kScanBlocksPerWave;
+// Decode score scan geometry: each wave streams bpw consecutive keys (a
+// multiple of 64, at most kScanBlocksPerWaveMax, chosen per call), a
+// work-group of 4 waves 4*bpw; each work-group leaves a summary of its score
+// histogram in a slot of 1 + kSumWords words (see decode_scan_kernel).
+constexpr int kScanBlocksPerWaveMax = 2048;
 constexpr int kSumWords = kMaxBudget;
 constexpr int kSumSlot = 1 + kSumWords;
 
