@@ -45,11 +45,11 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # 1 GiB copy).  The counter summary is
 # profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure is
 # reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (3923227.5 * 2.000 + 49152.0 * 1.000) * 1024 * 64
+ATTEND_TRAFFIC_BYTES = (3924597.8 * 2.000 + 49152.0 * 1.000) * 1024 * 64
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "41735dbeac645a9e310e71d3f2a25212d0cb74806763b5878672dfbbf490cf56",
+    "k_attend.hip": "20e54ce4393fe6e92c910fb5c614a4440d08841b7c526526c4b1c9b2c2683e2b",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
-    "qsa_common.h": "ec8fd2afde43dcdcf0ee0cdc56f897f86d1e183e715d4c044c16e8b2b014806d",
+    "qsa_common.h": "e68f00491eca878a52d16e3650d7ec7653f15dcb5c7fc4ff03e9c640f02d6a24",
 }
 
 

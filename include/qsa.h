@@ -244,9 +244,9 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
 /* qsa_decode for callers that cannot allocate device memory -- code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc: the same
  * kernels and results as qsa_decode, with no workspace argument.  The step's
- * scratch (rotated query, score rows, histograms, selection lists, split
- * partials) lives in a fixed device array of QSA_NOALLOC_SCRATCH_BYTES that the
- * library holds on every GPU it runs on until the process ends; its address is
+ * scratch (score rows, histogram summaries, selection lists, split partials)
+ * lives in a fixed device array of QSA_NOALLOC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on until the process ends; its address is
  * resolved once per device by qsa_create.  The caller still passes every input,
  * cache and output.  Returns QSA_ERR_WORKSPACE, before anything is enqueued,
  * when qsa_workspace_size(QSA_OP_DECODE, B, 1, ctx_bound) exceeds
