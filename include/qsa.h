@@ -254,8 +254,9 @@ qsa_status qsa_decode(const qsa_handle *h, void *stream, int32_t B, const int32_
  * 131,072 and B = 8 at 1,048,576).  Every call on one GPU shares that GPU's
  * array: calls that overlap on one GPU (other streams, other threads, other
  * handles) race and must be serialised by the caller.  The array keeps the last
- * call's contents; each call clears what it accumulates into.  Calls no
- * hipMalloc, hipFree or other allocating routine. */
+ * call's contents; a call reads no word of it that the same call has not
+ * written first, so nothing needs clearing between calls.  Calls no hipMalloc,
+ * hipFree or other allocating routine. */
 #define QSA_NOALLOC_SCRATCH_BYTES (32u << 20)
 qsa_status qsa_decode_noalloc(const qsa_handle *h, void *stream, int32_t B, const int32_t *cache_len,
                               int64_t ctx_bound,
