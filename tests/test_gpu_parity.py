@@ -395,6 +395,26 @@ def test_decode_small_ragged_lengths():
             assert np.array_equal(bits(c["kbar_cache"][b, n // 4]), ref_kbar[n // 4])
 
 
+def test_decode_long_ragged_rows_many_scan_workgroups():
+    """Rows of 16,383 / 10,000 / 2,047 / 75 candidate blocks in one call: the
+    scan splits each row over up to 16 work-groups (256 keys per wave at this
+    batch), rows leave different numbers of histogram summaries, one row keeps
+    all its candidates; selections and outputs against the oracle's rows."""
+    budget = 512
+    lens = [65535, 40003, 8190, 300]
+    w = synth.Workload("t", "decode", len(lens), max(lens), budget, 8, "random", 31)
+    h = Q.Handle(max_ctx=65540, budget_blocks=budget)
+    x, out, bidx, _ = _decode_setup(w, lens, h)
+    p = O.Params(budget=budget)
+    o = f32(out)
+    bi = bidx.cpu().numpy()
+    for b, n in enumerate(lens):
+        lay = oracle_layer(x, b, p, n_keys=n + 1)
+        ref, sel, sc = lay.row(n, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
+        check_selection(bi[b, 0], sel, sc, budget, n // 4, "seq %d" % b)
+        check_out(o[b, 0], ref, "seq %d" % b)
+
+
 def test_decode_matches_prefill_row():
     """Decode at p and prefill row p (same n+1 tokens, same query) both meet the
     oracle's row p, and agree with each other."""
