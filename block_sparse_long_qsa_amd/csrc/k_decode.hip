@@ -163,10 +163,10 @@ __device__ __forceinline__ u32x4 rotate_chunk8_t(u32x4 x, u32x4 xp, bool first_h
 // Score scan: scores[b][blk] = sum_h ReLU(<q~_h, k̄_blk>) for blk < floor(p/r),
 // r = 1 << rsh (4: pooled micro-blocks; 1: one rotated key per token).
 // v_mfma_f32_16x16x32_bf16 with A = q~ (4 real rows of 16), B = 16 keys;
-// lanes 0..15 end with the 4 heads of one block.  Each wave streams 512 blocks
-// and collects their scores in LDS, then writes them with one 16-byte store per
-// lane and 256 scores: 4-byte stores interleaved with the k̄ loads cost about 6%
-// of the scan.
+// lanes 0..15 end with the 4 heads of one block.  Each wave streams bpw
+// consecutive blocks (chosen per call, up to kScanBlocksPerWaveMax) and collects
+// their scores in LDS, then writes them with one 16-byte store per lane and 256
+// scores: 4-byte stores interleaved with the k̄ loads cost about 6% of the scan.
 
 // What the first work-group of a sequence appends while the others scan: the
 // new token's K~/V (k non-null), its raw indexer key (pooled at r = 4 into the
