@@ -10,10 +10,6 @@
 namespace qsa {
 
 constexpr int kDecodeBins = 2048;      // histogram of score bits 30..20
-// Raw buffer resources (gfx9 family): word 3 of the descriptor for untyped
-// 32-bit accesses, and the non-temporal cache-policy bit of buffer loads.
-constexpr int kBufferRsrcWord3 = 0x00020000;
-constexpr int kCachePolicyNT = 2;
 
 // Append the new token of sequence b at position p, one wave (lane = 0..63):
 //   lanes: head g = lane/32, chunk c = lane%32 -> rotate k at p into K~ slot
@@ -230,21 +226,14 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     const int r = lane & 15, g = lane >> 4;
     const bf16_t *kb = keys + b * key_cap * kIdxDim;
     const int64_t wend = (w0 + bpw < o) ? w0 + bpw : o;
-    // B = 16 blocks of keys per MFMA, 4 MFMAs of 64 blocks per step.  The
-    // keys are read through a buffer resource over the wave's own run w0 ..
-    // wend-1, so blocks past it read as zeros (results discarded), and with
-    // the non-temporal policy: the k-bar stream is read once per step, and
-    // marking it so keeps it from evicting the K~/V blocks that the split
-    // attention gathers next (and again at the following steps) from the
-    // memory-side cache.
-    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<bf16_t *>(kb + w0 * kIdxDim), 0, static_cast<int>((wend - w0) * kIdxDim * 2), kBufferRsrcWord3);
+    // B = 16 blocks of keys per MFMA, 4 MFMAs of 64 blocks per step; blocks
+    // past the row (o) read block w0 instead (in bounds, results discarded)
     auto load_step = [&](int64_t c0, bf16x8 (&bf)[4][4]) {
         for (int u = 0; u < 4; ++u) {
-            const int off = static_cast<int>(c0 - w0 + 16 * u + r) * (kIdxDim * 2) + 16 * g;
+            int64_t blk = c0 + 16 * u + r;
+            if (blk >= o) blk = w0;
             for (int s = 0; s < 4; ++s)
-                bf[u][s] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, off + 64 * s, 0,
-                                                                                             kCachePolicyNT));
+                bf[u][s] = *reinterpret_cast<const bf16x8 *>(kb + blk * kIdxDim + 32 * s + 8 * g);
         }
     };
     // A = q~: lane (head r < 4, k-group g) holds dims 32s + 8g .. +7 of head r,
