@@ -243,7 +243,8 @@ __device__ __forceinline__ void fetch_chunk_k(const bf16_t *__restrict__ kc, con
         uint32_t m;
         list_entry<false>(sel, sel_off, n_sel, o0, o, lb + 4 * t + (r >> 2), own_last, blk, m);
         const bf16_t *src = kc + blk * kBlockElems + (r & 3) * 32 + 8 * g;
-        for (int s = 0; s < 8; ++s) kf[t][s] = *reinterpret_cast<const bf16x8 *>(src + s * 128);
+        for (int s = 0; s < 8; ++s)
+            kf[t][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(src + s * 128));
     }
 }
 
@@ -258,7 +259,8 @@ __device__ __forceinline__ void fetch_chunk_v(const bf16_t *__restrict__ vc, con
         int64_t blk;
         list_entry<false>(sel, sel_off, n_sel, o0, o, lb + 4 * t + g, own_last, blk, vmask[t]);
         const bf16_t *src = vc + blk * kBlockElems + r * kBlock;
-        for (int n = 0; n < 16; ++n) vraw[n][t] = *reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock);
+        for (int n = 0; n < 16; ++n)
+            vraw[n][t] = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(src + 16 * n * kBlock));
     }
 }
 
