@@ -415,6 +415,29 @@ def test_decode_long_ragged_rows_many_scan_workgroups():
         check_out(o[b, 0], ref, "seq %d" % b)
 
 
+@pytest.mark.parametrize("B", [130, 256])
+def test_decode_large_batch_few_splits(B):
+    """Batches whose split attention has two splits per (sequence, KV group)
+    (B = 130) or one (B = 256, the merge of a single partial), ragged lengths
+    from 0 to 700 tokens: every sequence's selection and output against the
+    oracle's row."""
+    budget = 32
+    rng = np.random.default_rng(40 + B)
+    lens = [int(v) for v in rng.integers(0, 701, size=B)]
+    lens[:6] = [0, 1, 3, 4, 127, 700]
+    w = synth.Workload("t", "decode", B, max(lens), budget, 4, "random", 41 + B)
+    h = Q.Handle(max_ctx=1024, budget_blocks=budget)
+    x, out, bidx, _ = _decode_setup(w, lens, h)
+    p = O.Params(budget=budget)
+    o = f32(out)
+    bi = bidx.cpu().numpy()
+    for b, n in enumerate(lens):
+        lay = oracle_layer(x, b, p, n_keys=n + 1)
+        ref, sel, sc = lay.row(n, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
+        check_selection(bi[b, 0], sel, sc, budget, n // 4, "seq %d" % b)
+        check_out(o[b, 0], ref, "seq %d" % b)
+
+
 def test_decode_matches_prefill_row():
     """Decode at p and prefill row p (same n+1 tokens, same query) both meet the
     oracle's row p, and agree with each other."""
