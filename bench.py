@@ -47,7 +47,7 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # reported only while the kernel's sources hash to the digests it was taken with.
 ATTEND_TRAFFIC_BYTES = (3923186.3 * 2.000 + 49152.0 * 1.000) * 1024 * 64
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "e01de6b97378d139a9003b598df5d596364e6b374e66b3d5e92b50d367931106",
+    "k_attend.hip": "f9d3b2c65f147f04b87d581cdbbe871b2fc61a4b642ad94bfbca5a224944cece",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "e68f00491eca878a52d16e3650d7ec7653f15dcb5c7fc4ff03e9c640f02d6a24",
 }

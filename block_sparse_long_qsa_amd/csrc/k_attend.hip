@@ -230,7 +230,10 @@ __global__ __launch_bounds__(256) void attend_stats_kernel(
 // next chunk issued while the current one computes -- its K~ once the current
 // logits are formed, its V after the current PV product -- so that a wave
 // keeps a chunk's worth of loads in flight through its walk with no more
-// registers than one chunk needs.
+// registers than one chunk needs.  The gathers are non-temporal loads: a
+// decode step reads each selected block once per (sequence, KV group).  (The
+// prefill walk keeps plain loads: there the walks that run together reuse each
+// other's blocks through the L2.)
 __device__ __forceinline__ void fetch_chunk_k(const bf16_t *__restrict__ kc, const int32_t *__restrict__ sel,
                                               int sel_off, int n_sel, int64_t o0, int64_t o, int own_last, int c,
                                               bf16x8 (&kf)[2][8])
