@@ -207,7 +207,10 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     const int64_t o = p >> rsh;
     const float *cs = tab.cos + p * kPairs;
     const float *sn = tab.sin + p * kPairs;
-    if (blockIdx.x == 0 && wave == 0) {
+    // The row's first wave appends the new token.  With candidates to scan it
+    // does so once its first keys are in flight (below), so that the append's
+    // round trips overlap that wait; nothing it writes is read by the scan.
+    auto append = [&]() {
         if (rsh == 2) {
             append_one(tab, lane, b, p, ap.kv_blk_cap, ap.k, ap.v, ap.k_idx, ap.k_cache, ap.v_cache, keys, ap.kpend);
         } else if (lane < 16) {       // token keys: the new key rotated at p into keys[b][p]
@@ -217,7 +220,9 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
             *reinterpret_cast<u32x4 *>(keys + (b * key_cap + p) * kIdxDim + 8 * lane) =
                 rotate_chunk8(x, xp, lane, cs, sn);
         }
-    }
+    };
+    const bool appender = blockIdx.x == 0 && wave == 0;
+    if (appender && o == 0) append();
     if (static_cast<int64_t>(blockIdx.x) * 4 * bpw >= o) return;     // whole workgroup idle
     for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
     __syncthreads();
@@ -252,6 +257,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     }
     bf16x8 bf[4][4];
     load_step(w0, bf);
+    if (appender) append();           // w0 = 0 < o here
     bf16x8 af[4];
     if (r < kIdxHeads) {
         const u32x4 x0 = rotate_chunk8_t(x[0], x[1], true, tc, ts);      // chunk g pairs with chunk g + 4
