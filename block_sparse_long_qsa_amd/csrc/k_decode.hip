@@ -190,16 +190,25 @@ struct DecodeAppend {
 // reaches K) is >= every d_w, hence the summaries give the exact row count of
 // every bin >= d*: no histogram has to be cleared between steps.
 
+// kList: instead of its scores, each work-group stores the list of its
+// scores whose digit (bits 30..20) is at or above the lowest digit of its
+// summary -- (score bits, block) pairs in block order, at most 4*bpw of them,
+// in cand[(b * nwg + blockIdx.x) * 4 * bpw ..] with their count in candn[..].
+// The row's boundary digit is at or above every work-group's lowest summary
+// digit, so these lists hold every score a selection can take.
+template <bool kList>
 __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int32_t *__restrict__ cache_len,
                                                           int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol,
                                                           int budget, int bpw, int nwg,
                                                           const bf16_t *__restrict__ q_idx,
                                                           bf16_t *__restrict__ keys, float *__restrict__ scores,
-                                                          uint32_t *__restrict__ summ, DecodeAppend ap)
+                                                          uint32_t *__restrict__ summ, uint2 *__restrict__ cand,
+                                                          uint32_t *__restrict__ candn, DecodeAppend ap)
 {
     __shared__ uint32_t lh[kDecodeBins];
     __shared__ __attribute__((aligned(16))) uint32_t sl[4][kScanBlocksPerWaveMax];   // each wave's score bits
     __shared__ uint32_t wsum[4];
+    __shared__ uint32_t s_low, s_lcnt[4];
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
@@ -223,8 +232,12 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     };
     const bool appender = blockIdx.x == 0 && wave == 0;
     if (appender && o == 0) append();
-    if (static_cast<int64_t>(blockIdx.x) * 4 * bpw >= o) return;     // whole workgroup idle
+    if (static_cast<int64_t>(blockIdx.x) * 4 * bpw >= o) {           // whole workgroup idle
+        if (kList && threadIdx.x == 0) candn[b * nwg + blockIdx.x] = 0u;
+        return;
+    }
     for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
+    if (threadIdx.x == 0) s_low = 0xFFFFFFFFu;
     __syncthreads();
     const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * bpw;
     if (w0 < o) {
@@ -294,7 +307,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     step(c0, std::false_type{});
     }
     __syncthreads();
-    if (w0 < o) {   // the wave's scores, blocks w0 .. wend-1
+    if (!kList && w0 < o) {   // the wave's scores, blocks w0 .. wend-1
         const int64_t n = ((w0 + bpw < o) ? w0 + bpw : o) - w0;
         float *dst = scores + b * ncol + w0;
         const bool vec = ((b * ncol + w0) & 3) == 0;
@@ -327,8 +340,61 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     uint32_t pos = block_scan_nt<256>(emit, wsum, n_emit);
     uint32_t *slot = summ + (b * nwg + blockIdx.x) * kSumSlot;
     if (threadIdx.x == 0) slot[0] = n_emit;
+    uint32_t low = 0xFFFFFFFFu;
     for (int i = 0; i < kPer; ++i)
-        if (take[i]) slot[1 + pos++] = (static_cast<uint32_t>(threadIdx.x * kPer + i) << 21) | h[i];
+        if (take[i]) {
+            slot[1 + pos++] = (static_cast<uint32_t>(threadIdx.x * kPer + i) << 21) | h[i];
+            low = min(low, static_cast<uint32_t>(threadIdx.x * kPer + i));
+        }
+    if constexpr (kList) {
+        // ---- the candidate list: this wave's scores of digit >= the lowest
+        // summary digit, in rounds of 256 blocks (lane l: blocks 4l .. 4l+3 of
+        // the round, one 16-byte LDS read), counted, then written in block order
+        if (low != 0xFFFFFFFFu) atomicMin(&s_low, low);
+        __syncthreads();
+        const uint32_t T = (s_low == 0xFFFFFFFFu) ? 0xFFFFFFFFu : (s_low << 20);
+        const int64_t n = (w0 < o) ? (((w0 + bpw < o) ? w0 + bpw : o) - w0) : 0;
+        auto flags = [&](int64_t i0, bool (&f)[4], uint32_t (&v)[4]) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(&sl[wave][i0]);
+            for (int j = 0; j < 4; ++j) {
+                v[j] = x[j];
+                f[j] = i0 + j < n && x[j] >= T;
+            }
+        };
+        uint32_t cnt = 0;
+        for (int64_t r0 = 0; r0 < n; r0 += 256) {
+            bool f[4];
+            uint32_t v[4];
+            flags(r0 + 4 * lane, f, v);
+            for (int j = 0; j < 4; ++j) cnt += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(f[j])));
+        }
+        if (lane == 0) s_lcnt[wave] = cnt;
+        __syncthreads();
+        uint32_t base = 0, tot = 0;
+        for (int k = 0; k < 4; ++k) {
+            if (k < wave) base += s_lcnt[k];
+            tot += s_lcnt[k];
+        }
+        uint2 *dst = cand + (b * nwg + blockIdx.x) * (4 * static_cast<int64_t>(bpw));
+        for (int64_t r0 = 0; r0 < n; r0 += 256) {
+            bool f[4];
+            uint32_t v[4];
+            flags(r0 + 4 * lane, f, v);
+            uint64_t m[4];
+            uint32_t before = 0;                 // set flags of lower lanes, all four positions
+            for (int j = 0; j < 4; ++j) {
+                m[j] = __builtin_amdgcn_ballot_w64(f[j]);
+                before += lanes_below(m[j]);
+            }
+            uint32_t own = 0;
+            for (int j = 0; j < 4; ++j) {
+                if (f[j]) dst[base + before + own] = make_uint2(v[j], static_cast<uint32_t>(w0 + r0 + 4 * lane + j));
+                own += f[j] ? 1u : 0u;
+            }
+            for (int j = 0; j < 4; ++j) base += static_cast<uint32_t>(__popcll(m[j]));
+        }
+        if (threadIdx.x == 0) candn[b * nwg + blockIdx.x] = tot;
+    }
 }
 
 hipError_t launch_decode_append(const Tables &tab, hipStream_t st, int32_t B, const int32_t *cache_len,
@@ -350,14 +416,18 @@ hipError_t launch_decode_scan(const Tables &tab, hipStream_t st, int32_t B, cons
                               int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol, int budget, int bpw,
                               const bf16_t *q_idx, bf16_t *keys, float *scores, uint32_t *summ,
                               const bf16_t *k, const bf16_t *v, const bf16_t *k_idx, bf16_t *k_cache,
-                              bf16_t *v_cache, bf16_t *kpend, int64_t kv_blk_cap)
+                              bf16_t *v_cache, bf16_t *kpend, int64_t kv_blk_cap, uint2 *cand, uint32_t *candn)
 {
     if (bpw < 64 || bpw > kScanBlocksPerWaveMax || bpw % 64 != 0) return hipErrorInvalidValue;
     const int64_t nwg = decode_scan_wgs(ncol, bpw);
     const DecodeAppend ap{k, v, k_idx, k_cache, v_cache, kpend, kv_blk_cap};
     dim3 grid(static_cast<unsigned>(nwg), static_cast<unsigned>(B));
-    hipLaunchKernelGGL(decode_scan_kernel, grid, dim3(256), 0, st, tab, cache_len, ctx_bound, rsh, key_cap, ncol,
-                       budget, bpw, static_cast<int>(nwg), q_idx, keys, scores, summ, ap);
+    if (cand)
+        hipLaunchKernelGGL(decode_scan_kernel<true>, grid, dim3(256), 0, st, tab, cache_len, ctx_bound, rsh, key_cap,
+                           ncol, budget, bpw, static_cast<int>(nwg), q_idx, keys, scores, summ, cand, candn, ap);
+    else
+        hipLaunchKernelGGL(decode_scan_kernel<false>, grid, dim3(256), 0, st, tab, cache_len, ctx_bound, rsh, key_cap,
+                           ncol, budget, bpw, static_cast<int>(nwg), q_idx, keys, scores, summ, cand, candn, ap);
     return hipGetLastError();
 }
 

@@ -553,6 +553,161 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
     finish_digit_select(eqk, eqb, sel, selq, wsum, n_eq, k_rem, above, budget, out);
 }
 
+// Decode selection from the scan's candidate lists (rows scanned by at most
+// kListMaxWG work-groups): one 1,024-thread work-group per row.  The row's
+// boundary digit d* and the count above it come from the scan's summaries;
+// the lists, concatenated in work-group order, hold the row's scores of digit
+// >= each work-group's lowest summary digit in block order, hence every score
+// of digit >= d*.  Blocks above d* are taken, the digit-d* entries ranked by
+// (low score bits, ordinal) and the two ascending lists merged, as in the
+// two-stage path; a crowded boundary digit (or more candidates than the
+// fast path holds) uses the exact radix select over the candidates.
+constexpr int kListMaxWG = 8;
+constexpr int kListPerLane = 16;          // fast path: up to 16 candidates per thread
+
+__global__ __launch_bounds__(kHistNT) void select_list_kernel(
+    const int32_t *__restrict__ cache_len, int64_t pos_bound, int rsh, const uint32_t *__restrict__ summ, int nwg,
+    int bpw, const uint2 *__restrict__ cand, const uint32_t *__restrict__ candn, int32_t *__restrict__ block_idx,
+    int budget)
+{
+    constexpr int NW = kHistNT / 64;
+    __shared__ uint32_t hist[kSelMaxBins];
+    __shared__ __attribute__((aligned(16))) uint32_t eqk[kEqMax];
+    __shared__ int32_t eqb[kEqMax];
+    __shared__ int32_t sel[kMaxBudget];
+    __shared__ int32_t selq[kMaxBudget];
+    __shared__ uint32_t wsum[NW];
+    __shared__ uint32_t wcnt[2][NW];
+    __shared__ uint32_t s_dig[2];
+    __shared__ uint32_t pre[kListMaxWG + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t b = blockIdx.x;
+    const int64_t o = decode_pos(cache_len, b, pos_bound) >> rsh;
+    int32_t *out = block_idx + b * budget;
+    if (take_all(o, budget, out)) return;
+    const int64_t cap = 4 * static_cast<int64_t>(bpw);
+    const int nw_b = static_cast<int>((o + cap - 1) / cap);     // <= nwg <= kListMaxWG (the launcher checks nwg)
+    // list lengths (lanes 0 .. nw_b-1 of wave 0) and their prefix
+    if (wave == 0) {
+        const uint32_t c = lane < nw_b ? candn[b * nwg + lane] : 0u;
+        uint32_t incl = c;
+        for (int off = 1; off <= kListMaxWG; off <<= 1) {            // lanes 0 .. kListMaxWG
+            const uint32_t x = __shfl_up(incl, off);
+            if (lane >= off) incl += x;
+        }
+        if (lane <= nw_b) pre[lane] = incl - c;                // pre[nw_b] = the total
+    }
+    for (int x = tid; x < kSelMaxBins; x += kHistNT) hist[x] = 0;
+    __syncthreads();
+    const uint32_t n_c = pre[nw_b];
+    const uint2 *crow = cand + b * nwg * cap;
+    auto cand_at = [&](int64_t j) -> uint2 {
+        const int w = chunk_of(pre, nw_b, static_cast<uint32_t>(j));
+        return crow[w * cap + (j - pre[w])];
+    };
+    // the candidates this thread classifies (wave w: w*S .. w*S + S-1, S a
+    // multiple of 64), loaded before the summaries so both round trips overlap
+    const uint32_t S = ((n_c + NW * 64 - 1) / (NW * 64)) * 64;
+    const bool fast = n_c <= static_cast<uint32_t>(kHistNT * kListPerLane);
+    uint2 v[kListPerLane];
+#pragma unroll
+    for (int u = 0; u < kListPerLane; ++u) {
+        const uint32_t j = wave * S + 64 * u + lane;
+        v[u] = (fast && 64u * u < S && j < n_c) ? cand_at(j) : make_uint2(0xFFFFFFFFu, 0u);
+    }
+    // the row's histogram at and above the boundary, from the summaries: 16
+    // threads per slot, each slot's first 8 words per thread loaded with its count
+    for (int w = tid >> 4; w < nw_b; w += kHistNT / 16) {
+        const uint32_t *slot = summ + (b * nwg + w) * kSumSlot;
+        const uint32_t i0 = tid & 15;
+        uint32_t word[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) word[k] = slot[1 + i0 + 16 * k];
+        const uint32_t n = min(slot[0], static_cast<uint32_t>(kSumWords));
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (i0 + 16 * k < n) atomicAdd(&hist[word[k] >> 21], word[k] & 0x1FFFFFu);
+        for (uint32_t i = i0 + 128; i < n; i += 16) {
+            const uint32_t wd = slot[1 + i];
+            atomicAdd(&hist[wd >> 21], wd & 0x1FFFFFu);
+        }
+    }
+    __syncthreads();
+    boundary_digit<kHistNT>(hist, static_cast<uint32_t>(budget), wsum, s_dig);
+    const uint32_t dstar = s_dig[0];
+    const uint32_t above = s_dig[1];
+    const uint32_t n_eq = hist[dstar];
+    const uint32_t k_rem = static_cast<uint32_t>(budget) - above;
+    if (n_eq > static_cast<uint32_t>(kEqMax) || !fast || n_c <= static_cast<uint32_t>(budget)) {
+        __syncthreads();                               // every thread has read hist[dstar]
+        if (n_c <= static_cast<uint32_t>(budget)) {    // (cannot happen: the lists hold >= budget scores)
+            for (uint32_t t = tid; t < static_cast<uint32_t>(budget); t += kHistNT)
+                out[t] = (t < n_c) ? static_cast<int32_t>(cand_at(t).y) : -1;
+            return;
+        }
+        radix_topk<kHistNT>(n_c, budget, [&](int64_t j) { return cand_at(j).x; },
+                            [&](int64_t j) { return static_cast<int64_t>(cand_at(j).y); }, out, hist);
+        return;
+    }
+    const int32_t T0 = static_cast<int32_t>(dstar << 20);
+    const int32_t T1 = dstar >= 2047u ? INT32_MAX : static_cast<int32_t>((dstar + 1) << 20);
+    uint32_t ng = 0, nge = 0;
+#pragma unroll
+    for (int u = 0; u < kListPerLane; ++u) {
+        ng += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u].x) >= T1)));
+        nge += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(static_cast<int32_t>(v[u].x) >= T0)));
+    }
+    if (lane == 0) {
+        wcnt[0][wave] = ng;
+        wcnt[1][wave] = nge - ng;
+    }
+    __syncthreads();
+    uint32_t gpos = 0, epos = 0, gtot = 0, etot = 0;
+    for (int w = 0; w < NW; ++w) {
+        if (w < wave) {
+            gpos += wcnt[0][w];
+            epos += wcnt[1][w];
+        }
+        gtot += wcnt[0][w];
+        etot += wcnt[1][w];
+    }
+    if (gtot != above || etot != n_eq) {               // the lists disagree with the summaries: exact path
+        radix_topk<kHistNT>(n_c, budget, [&](int64_t j) { return cand_at(j).x; },
+                            [&](int64_t j) { return static_cast<int64_t>(cand_at(j).y); }, out, hist);
+        return;
+    }
+#pragma unroll
+    for (int u = 0; u < kListPerLane; ++u) {
+        const bool ge = static_cast<int32_t>(v[u].x) >= T0;
+        const uint64_t gem = __builtin_amdgcn_ballot_w64(ge);
+        if (gem == 0) continue;                                  // wave-uniform
+        const bool g = static_cast<int32_t>(v[u].x) >= T1;
+        const uint64_t gm = __builtin_amdgcn_ballot_w64(g);
+        const uint64_t em = gem & ~gm;
+        if (g) sel[gpos + lanes_below(gm)] = static_cast<int32_t>(v[u].y);
+        if (ge && !g) {
+            const uint32_t t = epos + lanes_below(em);
+            eqk[t] = ((v[u].x & 0xFFFFFu) << 10) | t;
+            eqb[t] = static_cast<int32_t>(v[u].y);
+        }
+        gpos += static_cast<uint32_t>(__popcll(gm));
+        epos += static_cast<uint32_t>(__popcll(em));
+    }
+    __syncthreads();
+    finish_digit_select(eqk, eqb, sel, selq, wsum, n_eq, k_rem, above, budget, out);
+}
+
+hipError_t launch_select_list(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int rsh,
+                              const uint32_t *summ, int nwg, int bpw, const uint2 *cand, const uint32_t *candn,
+                              int32_t *block_idx, int budget)
+{
+    if (B <= 0) return hipSuccess;
+    if (nwg > kListMaxWG) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(select_list_kernel, dim3(static_cast<unsigned>(B)), dim3(kHistNT), 0, st, cache_len, pos_bound,
+                       rsh, summ, nwg, bpw, cand, candn, block_idx, budget);
+    return hipGetLastError();
+}
+
 hipError_t launch_select_two_stage(hipStream_t st, int32_t B, const int32_t *cache_len, int64_t pos_bound, int rsh,
                                    int64_t ncol, const float *scores, const uint32_t *summ, int nwg, int bpw, int32_t *cnt,
                                    int32_t *gtb, uint32_t *eqs, int32_t *eqi, uint32_t *rowinfo, int32_t *block_idx,

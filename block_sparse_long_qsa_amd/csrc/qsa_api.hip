@@ -45,7 +45,9 @@ hipError_t launch_decode_append(const Tables &, hipStream_t, int32_t, const int3
 int64_t decode_scan_wgs(int64_t, int);
 hipError_t launch_decode_scan(const Tables &, hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, int64_t, int,
                               int, const bf16_t *, bf16_t *, float *, uint32_t *, const bf16_t *, const bf16_t *,
-                              const bf16_t *, bf16_t *, bf16_t *, bf16_t *, int64_t);
+                              const bf16_t *, bf16_t *, bf16_t *, bf16_t *, int64_t, uint2 *, uint32_t *);
+hipError_t launch_select_list(hipStream_t, int32_t, const int32_t *, int64_t, int, const uint32_t *, int, int,
+                              const uint2 *, const uint32_t *, int32_t *, int);
 hipError_t launch_select_two_stage(hipStream_t, int32_t, const int32_t *, int64_t, int, int64_t, const float *,
                                    const uint32_t *, int, int, int32_t *, int32_t *, uint32_t *, int32_t *, uint32_t *,
                                    int32_t *, int);
@@ -174,10 +176,16 @@ IdxSelLayout index_select_layout(int32_t B, int64_t L, int cap) {
 // The decode selection handles rows of up to 1,024 chunks of 4,096 scores.
 constexpr int64_t kDecodeChunkMax = 1024;
 
+// Rows scanned by at most this many work-groups take their selection from the
+// scan's candidate lists in one launch; longer rows use the two-stage path
+// over the score rows.
+constexpr int64_t kListMaxWG = 8;
+
 struct DecLayout {
-    size_t scores, bidx, part_o, part_ml, summ, s2cnt, s2gt, s2eqs, s2eqi, s2row, total;
+    size_t scores, bidx, part_o, part_ml, summ, s2cnt, s2gt, s2eqs, s2eqi, s2row, candn, total;
     int64_t ncol, nchunk, nwg;
     int nsplit, bpw;
+    bool list;        // candidate lists (at scores, 4*bpw (score, block) pairs per scan work-group) instead of score rows
 };
 
 // Keys per wave of the decode scan: about one wave per SIMD over all rows
@@ -198,8 +206,10 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int r
     d.nsplit = decode_splits(B);
     d.bpw = decode_scan_bpw(B, d.ncol);
     d.nwg = decode_scan_wgs(d.ncol, d.bpw);
+    d.list = d.nwg <= kListMaxWG;
     d.scores = 0;
-    d.bidx = d.scores + align_up(static_cast<size_t>(B) * d.ncol * 4);
+    d.bidx = d.scores + align_up(d.list ? static_cast<size_t>(B) * d.nwg * 4 * d.bpw * 8
+                                        : static_cast<size_t>(B) * d.ncol * 4);
     d.part_o = d.bidx + align_up(static_cast<size_t>(B) * h->p.budget_blocks * 4);
     const size_t slots = static_cast<size_t>(B) * kKVHeads * d.nsplit * kGroup;
     d.part_ml = d.part_o + align_up(slots * kHeadDim * 4);
@@ -208,13 +218,14 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int r
     // two-stage selection: per 4,096-score chunk a count pair and the chunk's
     // lists (at most budget blocks above the boundary digit, 1,024 at it)
     d.nchunk = (d.ncol + 4095) / 4096;
-    const size_t nck = static_cast<size_t>(B) * d.nchunk;
+    const size_t nck = d.list ? 0 : static_cast<size_t>(B) * d.nchunk;     // (the list path has no chunks)
     d.s2cnt = d.summ + align_up(static_cast<size_t>(B) * d.nwg * kSumSlot * 4);
     d.s2gt = d.s2cnt + align_up(nck * 2 * 4);
     d.s2eqs = d.s2gt + align_up(nck * kMaxBudget * 4);
     d.s2eqi = d.s2eqs + align_up(nck * 1024 * 4);
     d.s2row = d.s2eqi + align_up(nck * 1024 * 4);
-    d.total = d.s2row + align_up(static_cast<size_t>(B) * 3 * 4);
+    d.candn = d.s2row + align_up(static_cast<size_t>(B) * 3 * 4);
+    d.total = d.candn + align_up(static_cast<size_t>(B) * d.nwg * 4);
     return d;
 }
 
@@ -296,9 +307,17 @@ hipError_t run_decode_select(const qsa_handle *h, hipStream_t st, int32_t B, con
                              uint16_t *v_cache, uint16_t *kpend, int32_t *bidx, char *w, const DecLayout &d) {
     float *scores = reinterpret_cast<float *>(w + d.scores);
     uint32_t *summ = reinterpret_cast<uint32_t *>(w + d.summ);
+    uint2 *cand = d.list ? reinterpret_cast<uint2 *>(w + d.scores) : nullptr;
+    uint32_t *candn = reinterpret_cast<uint32_t *>(w + d.candn);
     hipError_t e = launch_decode_scan(tables(h), st, B, cache_len, ctx_bound, rsh, key_cap, d.ncol,
                                       h->p.budget_blocks, d.bpw, q_idx, keys, scores, summ, k, v, k_idx, k_cache, v_cache,
-                                      kpend, nblk_cap(h));
+                                      kpend, nblk_cap(h), cand, candn);
+    if (d.list) {
+        if (e == hipSuccess)
+            e = launch_select_list(st, B, cache_len, ctx_bound, rsh, summ, static_cast<int>(d.nwg), d.bpw, cand, candn,
+                                   bidx, h->p.budget_blocks);
+        return e;
+    }
     if (e == hipSuccess)
         e = launch_select_two_stage(st, B, cache_len, ctx_bound, rsh, d.ncol, scores, summ, static_cast<int>(d.nwg), d.bpw,
                                     reinterpret_cast<int32_t *>(w + d.s2cnt), reinterpret_cast<int32_t *>(w + d.s2gt),

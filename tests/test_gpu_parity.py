@@ -348,10 +348,13 @@ def test_forward_yarn_small():
 
 
 # ---------------------------------------------------------------- decode
-def _decode_setup(w, ctx_per_seq, h):
-    """Caches filled by qsa_append to each sequence's own length, then one decode step."""
+def _decode_setup(w, ctx_per_seq, h, edit=None):
+    """Caches filled by qsa_append to each sequence's own length, then one
+    decode step; edit(x) may change the host inputs first."""
     B = len(ctx_per_seq)
     x = synth.decode_inputs(w, "cpu", ctx=max(ctx_per_seq), batch=B)
+    if edit is not None:
+        edit(x)
     xd = _to(x)
     c = Q.alloc_caches(h, B)
     for b, n in enumerate(ctx_per_seq):
@@ -436,6 +439,35 @@ def test_decode_large_batch_few_splits(B):
         ref, sel, sc = lay.row(n, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
         check_selection(bi[b, 0], sel, sc, budget, n // 4, "seq %d" % b)
         check_out(o[b, 0], ref, "seq %d" % b)
+
+
+def test_decode_crowded_boundary_digits():
+    """Ties at the selection boundary: sequence 0 has a zero indexer query (every
+    score is 0, so the boundary digit holds all 1,250 candidates, more than the
+    digit's fast path ranks), sequence 1 zero keys for 400 of its 750 blocks
+    (fewer than 512 positive scores, then a boundary digit of about 420 tied
+    zeros), sequence 2 no ties.  Ties go to the later block; selections and
+    outputs against the oracle's rows."""
+    budget = 512
+    lens = [5000, 3000, 4500]
+
+    def edit(x):
+        x["q_idx"][0] = 0
+        x["k_idx"][1, 4 * 100:4 * 500] = 0
+
+    w = synth.Workload("t", "decode", len(lens), max(lens), budget, 4, "random", 36)
+    h = Q.Handle(max_ctx=8192, budget_blocks=budget)
+    x, out, bidx, _ = _decode_setup(w, lens, h, edit)
+    p = O.Params(budget=budget)
+    o = f32(out)
+    bi = bidx.cpu().numpy()
+    for b, n in enumerate(lens):
+        lay = oracle_layer(x, b, p, n_keys=n + 1)
+        ref, sel, sc = lay.row(n, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
+        check_selection(bi[b, 0], sel, sc, budget, n // 4, "seq %d" % b)
+        check_out(o[b, 0], ref, "seq %d" % b)
+    # all scores tie in sequence 0: the selection is the last 512 blocks
+    assert np.array_equal(bi[0, 0], np.arange(lens[0] // 4 - budget, lens[0] // 4))
 
 
 def test_decode_matches_prefill_row():
