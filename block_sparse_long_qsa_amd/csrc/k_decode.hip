@@ -190,12 +190,13 @@ struct DecodeAppend {
 // reaches K) is >= every d_w, hence the summaries give the exact row count of
 // every bin >= d*: no histogram has to be cleared between steps.
 
-// kList: instead of its scores, each work-group stores the list of its
-// scores whose digit (bits 30..20) is at or above the lowest digit of its
-// summary -- (score bits, block) pairs in block order, at most 4*bpw of them,
-// in cand[(b * nwg + blockIdx.x) * 4 * bpw ..] with their count in candn[..].
-// The row's boundary digit is at or above every work-group's lowest summary
-// digit, so these lists hold every score a selection can take.
+// kList: instead of its scores, each wave stores the list of its scores whose
+// digit (bits 30..20) is at or above the lowest digit of its work-group's
+// summary -- (score bits, block) pairs in block order, at most bpw of them, in
+// cand[((b * nwg + blockIdx.x) * 4 + wave) * bpw ..] with their count in
+// candn[(b * nwg + blockIdx.x) * 4 + wave].  The row's boundary digit is at or
+// above every work-group's lowest summary digit, so these lists, taken in
+// order, hold every score a selection can take.
 template <bool kList>
 __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int32_t *__restrict__ cache_len,
                                                           int64_t ctx_bound, int rsh, int64_t key_cap, int64_t ncol,
@@ -208,7 +209,7 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     __shared__ uint32_t lh[kDecodeBins];
     __shared__ __attribute__((aligned(16))) uint32_t sl[4][kScanBlocksPerWaveMax];   // each wave's score bits
     __shared__ uint32_t wsum[4];
-    __shared__ uint32_t s_low, s_lcnt[4];
+    __shared__ uint32_t s_low;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
@@ -233,11 +234,11 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     const bool appender = blockIdx.x == 0 && wave == 0;
     if (appender && o == 0) append();
     if (static_cast<int64_t>(blockIdx.x) * 4 * bpw >= o) {           // whole workgroup idle
-        if (kList && threadIdx.x == 0) candn[b * nwg + blockIdx.x] = 0u;
+        if (kList && threadIdx.x < 4) candn[(b * nwg + blockIdx.x) * 4 + threadIdx.x] = 0u;
         return;
     }
     for (int x = threadIdx.x; x < kDecodeBins; x += 256) lh[x] = 0;
-    if (threadIdx.x == 0) s_low = 0xFFFFFFFFu;
+    if (threadIdx.x == 0) s_low = 0u;       // (all scores are candidates below the budget)
     __syncthreads();
     const int64_t w0 = (static_cast<int64_t>(blockIdx.x) * 4 + wave) * bpw;
     if (w0 < o) {
@@ -334,66 +335,46 @@ __global__ __launch_bounds__(256) void decode_scan_kernel(Tables tab, const int3
     for (int i = kPer - 1; i >= 0; --i) {
         take[i] = h[i] != 0u && above < static_cast<uint32_t>(budget);
         emit += take[i] ? 1u : 0u;
+        // the summary's lowest digit: the one whose count reaches the budget
+        if (kList && take[i] && above + h[i] >= static_cast<uint32_t>(budget))
+            s_low = static_cast<uint32_t>(threadIdx.x * kPer + i);
         above += h[i];
     }
     uint32_t n_emit;
     uint32_t pos = block_scan_nt<256>(emit, wsum, n_emit);
     uint32_t *slot = summ + (b * nwg + blockIdx.x) * kSumSlot;
     if (threadIdx.x == 0) slot[0] = n_emit;
-    uint32_t low = 0xFFFFFFFFu;
     for (int i = 0; i < kPer; ++i)
-        if (take[i]) {
-            slot[1 + pos++] = (static_cast<uint32_t>(threadIdx.x * kPer + i) << 21) | h[i];
-            low = min(low, static_cast<uint32_t>(threadIdx.x * kPer + i));
-        }
+        if (take[i]) slot[1 + pos++] = (static_cast<uint32_t>(threadIdx.x * kPer + i) << 21) | h[i];
     if constexpr (kList) {
         // ---- the candidate list: this wave's scores of digit >= the lowest
-        // summary digit, in rounds of 256 blocks (lane l: blocks 4l .. 4l+3 of
-        // the round, one 16-byte LDS read), counted, then written in block order
-        if (low != 0xFFFFFFFFu) atomicMin(&s_low, low);
-        __syncthreads();
-        const uint32_t T = (s_low == 0xFFFFFFFFu) ? 0xFFFFFFFFu : (s_low << 20);
+        // summary digit (s_low, published by the block scan's barriers), in
+        // rounds of 256 blocks (lane l: blocks 4l .. 4l+3 of the round, one
+        // 16-byte LDS read), written in block order
+        const uint32_t T = s_low << 20;
         const int64_t n = (w0 < o) ? (((w0 + bpw < o) ? w0 + bpw : o) - w0) : 0;
-        auto flags = [&](int64_t i0, bool (&f)[4], uint32_t (&v)[4]) {
+        const int64_t li = (b * nwg + blockIdx.x) * 4 + wave;
+        uint2 *dst = cand + li * bpw;
+        uint32_t base = 0;
+        for (int64_t r0 = 0; r0 < n; r0 += 256) {
+            const int64_t i0 = r0 + 4 * lane;
             const u32x4 x = *reinterpret_cast<const u32x4 *>(&sl[wave][i0]);
-            for (int j = 0; j < 4; ++j) {
-                v[j] = x[j];
-                f[j] = i0 + j < n && x[j] >= T;
-            }
-        };
-        uint32_t cnt = 0;
-        for (int64_t r0 = 0; r0 < n; r0 += 256) {
             bool f[4];
-            uint32_t v[4];
-            flags(r0 + 4 * lane, f, v);
-            for (int j = 0; j < 4; ++j) cnt += static_cast<uint32_t>(__popcll(__builtin_amdgcn_ballot_w64(f[j])));
-        }
-        if (lane == 0) s_lcnt[wave] = cnt;
-        __syncthreads();
-        uint32_t base = 0, tot = 0;
-        for (int k = 0; k < 4; ++k) {
-            if (k < wave) base += s_lcnt[k];
-            tot += s_lcnt[k];
-        }
-        uint2 *dst = cand + (b * nwg + blockIdx.x) * (4 * static_cast<int64_t>(bpw));
-        for (int64_t r0 = 0; r0 < n; r0 += 256) {
-            bool f[4];
-            uint32_t v[4];
-            flags(r0 + 4 * lane, f, v);
             uint64_t m[4];
             uint32_t before = 0;                 // set flags of lower lanes, all four positions
             for (int j = 0; j < 4; ++j) {
+                f[j] = i0 + j < n && x[j] >= T;
                 m[j] = __builtin_amdgcn_ballot_w64(f[j]);
                 before += lanes_below(m[j]);
             }
             uint32_t own = 0;
             for (int j = 0; j < 4; ++j) {
-                if (f[j]) dst[base + before + own] = make_uint2(v[j], static_cast<uint32_t>(w0 + r0 + 4 * lane + j));
+                if (f[j]) dst[base + before + own] = make_uint2(x[j], static_cast<uint32_t>(w0 + i0 + j));
                 own += f[j] ? 1u : 0u;
             }
             for (int j = 0; j < 4; ++j) base += static_cast<uint32_t>(__popcll(m[j]));
         }
-        if (threadIdx.x == 0) candn[b * nwg + blockIdx.x] = tot;
+        if (lane == 0) candn[li] = base;
     }
 }
 

@@ -556,9 +556,9 @@ __global__ __launch_bounds__(kHistNT) void select_gather_kernel(
 // Decode selection from the scan's candidate lists (rows scanned by at most
 // kListMaxWG work-groups): one 1,024-thread work-group per row.  The row's
 // boundary digit d* and the count above it come from the scan's summaries;
-// the lists, concatenated in work-group order, hold the row's scores of digit
-// >= each work-group's lowest summary digit in block order, hence every score
-// of digit >= d*.  Blocks above d* are taken, the digit-d* entries ranked by
+// the lists (one per scan wave), concatenated in order, hold the row's scores
+// of digit >= each work-group's lowest summary digit in block order, hence
+// every score of digit >= d*.  Blocks above d* are taken, the digit-d* entries ranked by
 // (low score bits, ordinal) and the two ascending lists merged, as in the
 // two-stage path; a crowded boundary digit (or more candidates than the
 // fast path holds) uses the exact radix select over the candidates.
@@ -579,30 +579,31 @@ __global__ __launch_bounds__(kHistNT) void select_list_kernel(
     __shared__ uint32_t wsum[NW];
     __shared__ uint32_t wcnt[2][NW];
     __shared__ uint32_t s_dig[2];
-    __shared__ uint32_t pre[kListMaxWG + 1];
+    __shared__ uint32_t pre[4 * kListMaxWG + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int64_t b = blockIdx.x;
     const int64_t o = decode_pos(cache_len, b, pos_bound) >> rsh;
     int32_t *out = block_idx + b * budget;
     if (take_all(o, budget, out)) return;
-    const int64_t cap = 4 * static_cast<int64_t>(bpw);
-    const int nw_b = static_cast<int>((o + cap - 1) / cap);     // <= nwg <= kListMaxWG (the launcher checks nwg)
-    // list lengths (lanes 0 .. nw_b-1 of wave 0) and their prefix
+    const int64_t cap = bpw;                                   // entries per wave's list
+    const int nw_b = static_cast<int>((o + 4 * cap - 1) / (4 * cap));   // <= nwg <= kListMaxWG (checked by the launcher)
+    const int nl = 4 * nw_b;                                   // the row's lists, one per scan wave, in block order
+    // list lengths (lanes 0 .. nl-1 of wave 0) and their prefix
     if (wave == 0) {
-        const uint32_t c = lane < nw_b ? candn[b * nwg + lane] : 0u;
+        const uint32_t c = lane < nl ? candn[b * nwg * 4 + lane] : 0u;
         uint32_t incl = c;
-        for (int off = 1; off <= kListMaxWG; off <<= 1) {            // lanes 0 .. kListMaxWG
+        for (int off = 1; off <= 4 * kListMaxWG; off <<= 1) {        // lanes 0 .. 4*kListMaxWG
             const uint32_t x = __shfl_up(incl, off);
             if (lane >= off) incl += x;
         }
-        if (lane <= nw_b) pre[lane] = incl - c;                // pre[nw_b] = the total
+        if (lane <= nl) pre[lane] = incl - c;                  // pre[nl] = the total
     }
     for (int x = tid; x < kSelMaxBins; x += kHistNT) hist[x] = 0;
     __syncthreads();
-    const uint32_t n_c = pre[nw_b];
-    const uint2 *crow = cand + b * nwg * cap;
+    const uint32_t n_c = pre[nl];
+    const uint2 *crow = cand + b * nwg * 4 * cap;
     auto cand_at = [&](int64_t j) -> uint2 {
-        const int w = chunk_of(pre, nw_b, static_cast<uint32_t>(j));
+        const int w = chunk_of(pre, nl, static_cast<uint32_t>(j));
         return crow[w * cap + (j - pre[w])];
     };
     // the candidates this thread classifies (wave w: w*S .. w*S + S-1, S a

@@ -185,7 +185,7 @@ struct DecLayout {
     size_t scores, bidx, part_o, part_ml, summ, s2cnt, s2gt, s2eqs, s2eqi, s2row, candn, total;
     int64_t ncol, nchunk, nwg;
     int nsplit, bpw;
-    bool list;        // candidate lists (at scores, 4*bpw (score, block) pairs per scan work-group) instead of score rows
+    bool list;        // candidate lists (at scores, bpw (score, block) pairs per scan wave) instead of score rows
 };
 
 // Keys per wave of the decode scan: about one wave per SIMD over all rows
@@ -225,7 +225,7 @@ DecLayout decode_layout(const qsa_handle *h, int32_t B, int64_t ctx_bound, int r
     d.s2eqi = d.s2eqs + align_up(nck * 1024 * 4);
     d.s2row = d.s2eqi + align_up(nck * 1024 * 4);
     d.candn = d.s2row + align_up(static_cast<size_t>(B) * 3 * 4);
-    d.total = d.candn + align_up(static_cast<size_t>(B) * d.nwg * 4);
+    d.total = d.candn + align_up(static_cast<size_t>(B) * d.nwg * 4 * 4);      // one count per scan wave
     return d;
 }
 
