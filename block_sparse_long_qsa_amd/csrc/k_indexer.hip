@@ -173,8 +173,9 @@ hipError_t launch_indexer_scores(hipStream_t st, int32_t B, int64_t L, int64_t q
 // thresholds need no workgroup barrier.  After the last tile each wave takes
 // its queries' exact top-`budget` from their lists: every kept score in a bin
 // above the boundary bin (the highest bin whose suffix count reaches `budget`)
-// is selected, and the rest come from the boundary bin, ranked in LDS; the
-// selection is written in ascending block order.  A list that outgrew `cap`
+// is selected, and the rest come from the boundary bin, ranked in LDS.  Both
+// parts keep the list's (ascending) block order, so one bitonic merge writes
+// the selection in ascending block order.  A list that outgrew `cap`
 // (it keeps counting without storing) or a boundary bin too crowded to rank
 // here sends its row to select_fixup_kernel, which recomputes it exactly.
 // Workgroups are issued latest-queries-first (longest rows first).
@@ -200,24 +201,47 @@ constexpr int kTopkBMax = 1536;        // boundary-bin entries a wave ranks in L
 constexpr int kTopkRankMax = 512;      // clamped end bins: ranked by counting up to this many
 constexpr int kU = 32;                 // list entries per lane in flight in the final pass
 
-// The k_rem largest of nb packed boundary keys (nb <= 64*R): their block ids go
-// to dst[0 .. k_rem), in rank order.  Padding keys are 0: a real key is 0 only
-// for ordinal 0 with equal low score bits, the smallest real key, which ties
-// the padding at the end of the order where no rank below k_rem < nb reaches.
+// Which of nb packed boundary keys (nb <= 64*R; the low 11 bits of a key are
+// its ordinal) are among the k_rem largest, 0 < k_rem < nb: afterwards
+// bkey[t] is 1 for those ordinals and 0 for the others.  Padding keys are 0: a
+// real key is 0 only for ordinal 0 with equal low score bits, the smallest
+// real key, so every rank below k_rem < nb holds a real key.
 template <int R>
-__device__ __forceinline__ void boundary_take(const uint32_t *bkey, const int32_t *bid, uint32_t nb, uint32_t k_rem, int32_t *dst,
-                              int lane) {
+__device__ __forceinline__ void boundary_mark(uint32_t *bkey, uint32_t nb, uint32_t k_rem, int lane) {
     uint32_t k[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = r * 64 + lane;
         k[r] = (i < nb) ? bkey[i] : 0u;
+        if (i < nb) bkey[i] = 0u;                 // the same lane's read came first
     }
     wave_sort_desc<R>(k, lane);
+    wave_sync();
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const uint32_t i = lane * R + r;
-        if (i < k_rem) dst[i] = bid[k[r] & 0x7FFu];
+        if (i < k_rem) bkey[k[r] & 0x7FFu] = 1u;
+    }
+}
+
+// Write n (<= 64*R) block ids to out[] ascending, given as two ascending runs
+// sel[0 .. above) and sel[above .. n) of distinct ids: the first run followed
+// by the second reversed (then 0 padding) is bitonic, so the last merge phase
+// of the wave's bitonic network (log2(64 R) steps) orders it.
+template <int R>
+__device__ __forceinline__ void emit_merged(const int32_t *sel, int above, int n, int32_t *__restrict__ out, int lane) {
+    uint32_t k[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = lane * R + r;
+        const int src = e < above ? e : n - 1 - e + above;
+        k[r] = (e < n) ? static_cast<uint32_t>(sel[src]) + 1u : 0u;    // ids + 1 sort ahead of the padding
+    }
+    bitonic_steps<R, 64 * R, 32 * R>(k, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int i = lane * R + r;
+        if (i < n) out[n - 1 - i] = static_cast<int32_t>(k[r] - 1u);
     }
 }
 
@@ -504,10 +528,13 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             continue;
         }
         wave_sync();
-        // the k_rem best boundary entries join sel[above ..)
+        // the k_rem best boundary entries join sel[above ..), in list order
+        // except on the clamped path (rank order)
+        bool in_order = true;
         if (nb == k_rem) {
             for (uint32_t t = lane; t < nb; t += 64) sel[above + t] = bid[t];
         } else if (clamped) {
+            in_order = false;
             // rank = entries ahead in (score desc, ordinal desc); ranks are unique
             for (uint32_t t = lane; t < nb; t += 64) {
                 const uint32_t kx = bkey[t];
@@ -520,19 +547,36 @@ __global__ __launch_bounds__(256, 2) void indexer_topk_kernel(
             }
         } else {
             const uint32_t n64 = (nb + 63) >> 6;
-            if (n64 <= 1)       boundary_take<1>(bkey, bid, nb, k_rem, sel + above, lane);
-            else if (n64 <= 2)  boundary_take<2>(bkey, bid, nb, k_rem, sel + above, lane);
-            else if (n64 <= 4)  boundary_take<4>(bkey, bid, nb, k_rem, sel + above, lane);
-            else if (n64 <= 8)  boundary_take<8>(bkey, bid, nb, k_rem, sel + above, lane);
-            else if (n64 <= 16) boundary_take<16>(bkey, bid, nb, k_rem, sel + above, lane);
-            else                boundary_take<32>(bkey, bid, nb, k_rem, sel + above, lane);
+            if (n64 <= 1)       boundary_mark<1>(bkey, nb, k_rem, lane);
+            else if (n64 <= 2)  boundary_mark<2>(bkey, nb, k_rem, lane);
+            else if (n64 <= 4)  boundary_mark<4>(bkey, nb, k_rem, lane);
+            else if (n64 <= 8)  boundary_mark<8>(bkey, nb, k_rem, lane);
+            else if (n64 <= 16) boundary_mark<16>(bkey, nb, k_rem, lane);
+            else                boundary_mark<32>(bkey, nb, k_rem, lane);
+            wave_sync();
+            // the marked entries, compacted in list order
+            uint32_t pos = static_cast<uint32_t>(above);
+            for (uint32_t t0 = 0; t0 < nb; t0 += 64) {
+                const uint32_t t = t0 + lane;
+                const bool f = t < nb && bkey[t] != 0u;
+                const uint64_t fm = __builtin_amdgcn_ballot_w64(f);
+                if (f) sel[pos + lanes_below(fm)] = bid[t];
+                pos += static_cast<uint32_t>(__popcll(fm));
+            }
         }
         wave_sync();
         // ascending block order
-        if (budget <= 64)       emit_sorted<1>(sel, budget, out, lane);
-        else if (budget <= 128) emit_sorted<2>(sel, budget, out, lane);
-        else if (budget <= 256) emit_sorted<4>(sel, budget, out, lane);
-        else                    emit_sorted<8>(sel, budget, out, lane);
+        if (in_order) {
+            if (budget <= 64)       emit_merged<1>(sel, static_cast<int>(above), budget, out, lane);
+            else if (budget <= 128) emit_merged<2>(sel, static_cast<int>(above), budget, out, lane);
+            else if (budget <= 256) emit_merged<4>(sel, static_cast<int>(above), budget, out, lane);
+            else                    emit_merged<8>(sel, static_cast<int>(above), budget, out, lane);
+        } else {
+            if (budget <= 64)       emit_sorted<1>(sel, budget, out, lane);
+            else if (budget <= 128) emit_sorted<2>(sel, budget, out, lane);
+            else if (budget <= 256) emit_sorted<4>(sel, budget, out, lane);
+            else                    emit_sorted<8>(sel, budget, out, lane);
+        }
         wave_sync();
     }
 }
