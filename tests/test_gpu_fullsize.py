@@ -1,7 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
 times: sampled rows the oracle computes one by one (every 1,024th row and the
 last 24 at 262,144 tokens; every 16,384th row and the chunk boundaries at
-1,048,576; 8 of the 64 decode sequences at 131,072 and 3 of 8 at 1,048,576),
+1,048,576; 8 of the 64 decode sequences at 131,072 and 3 of 8 at 1,048,576;
+4 rows of a 32-row ragged decode whose longest row holds 80,000 tokens),
 the selection invariants on every row and every sequence, checked on the
 device (count min(budget, floor(p/4)), strictly ascending, every id in
 [0, floor(p/4)), -1 padding after the ids), and every needle probe's needle.
@@ -186,6 +187,51 @@ def test_decode_128k_sampled_bench_config():
     worst = _check_decode(w, x, out, bidx, seqs=seqs)
     _say("decode 128k: %d sequences vs oracle (max abs err %.4g), invariants and needles of 64 sequences" % (
         len(seqs), worst))
+
+
+def test_decode_long_rows_candidate_lists():
+    """One call of 32 ragged rows whose longest row (80,000 cached tokens,
+    20,000 candidate blocks) the scan covers with 8 work-groups, so the
+    selection reads the scan's candidate lists.  Row 0 has a zero indexer
+    query: every score is 0, every score is a candidate -- more than the list
+    selection holds in registers -- and the exact radix path takes it (ties go
+    to the later block: its last 512 blocks).  Row 1 (60,000 tokens) takes the
+    list path over 6 work-groups; rows 2.. are short.  Invariants on every
+    row, rows 0, 1, 2 and 31 against the oracle."""
+    budget, B = 512, 32
+    lens = [80000, 60000] + [300 + 97 * b for b in range(2, B)]
+    w = synth.Workload("t", "decode", B, max(lens), budget, 4, "random", 47)
+    x = synth.decode_inputs(w, DEV, ctx=max(lens), batch=B)
+    x["q_idx"][0] = 0
+    h = Q.Handle(max_ctx=max(lens) + 4, budget_blocks=budget)
+    c = Q.alloc_caches(h, B)
+    for b, n in enumerate(lens):
+        cs = {k: v[b:b + 1] for k, v in c.items()}
+        Q.qsa_append(h, 1, n, 0, x["k"][b:b + 1, :n].contiguous(), x["v"][b:b + 1, :n].contiguous(),
+                     x["k_idx"][b:b + 1, :n].contiguous(), cs["k_cache"], cs["v_cache"], cs["kbar_cache"],
+                     cs["kpend"])
+    new = {n: torch.stack([x[n][b, lens[b]] for b in range(B)])[:, None].contiguous() for n in ("k", "v", "k_idx")}
+    cache_len = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    ws = Q.workspace(h, Q.QSA_OP_DECODE, B, 1, max(lens))
+    out = torch.empty((B, 1, 24, 256), dtype=torch.bfloat16, device=DEV)
+    bidx = torch.empty((B, 1, budget), dtype=torch.int32, device=DEV)
+    Q.qsa_decode(h, B, cache_len, max(lens), x["q"], new["k"], new["v"], x["q_idx"], new["k_idx"], c["k_cache"],
+                 c["v_cache"], c["kbar_cache"], c["kpend"], out, bidx, ws)
+    torch.cuda.synchronize()
+    _check_invariants(bidx, budget, pos=cache_len)
+    bi = bidx.cpu().numpy()
+    assert np.array_equal(bi[0, 0], np.arange(lens[0] // 4 - budget, lens[0] // 4)), "row 0: not its last blocks"
+    p = O.Params(budget=budget)
+    worst = 0.0
+    for b in (0, 1, 2, B - 1):
+        n = lens[b]
+        lay = O.LayerOracle(bits(x["k"][b, :n + 1]), bits(x["v"][b, :n + 1]), bits(x["k_idx"][b, :n + 1]), p)
+        ref, sel, sc = lay.row(n, bits(x["q"][b, 0]), bits(x["q_idx"][b, 0]))
+        check_selection(bi[b, 0], sel, sc, budget, n // 4, "row %d" % b)
+        err, _ = check_out(out[b, 0].float().cpu().numpy(), ref, "row %d" % b)
+        worst = max(worst, err)
+        del lay
+    _say("decode long rows: invariants of %d rows, 4 vs oracle (max abs err %.4g)" % (B, worst))
 
 
 def test_decode_1m_yarn_sampled():
