@@ -939,7 +939,8 @@ def main():
             "index_select_mfma_frac": idx_tfs / MFMA_BF16_PEAK_TFS,
         },
         "roofline": {
-            "kernel": "attend_prefill_kernel (qsa_attend: %d launches of up to 4,096 rows)" % ((L + 4095) // 4096),
+            "kernel": "attend_prefill_kernel (qsa_attend: %d launches of up to 2,048 rows, two queries per wave)"
+                      % ((L + 2047) // 2048),
             "bound": "mfma", "achieved": attn_tfs, "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
             "frac": attn_tfs / MFMA_BF16_PEAK_TFS,
             "traffic": None if tr_bytes is None else tr_bytes / (t_attn * 1e-3) / 1e9,

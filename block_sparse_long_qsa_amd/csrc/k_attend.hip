@@ -4,8 +4,9 @@
 // incomplete block are always included; spec table: 24 query heads, 2 KV
 // heads, head dim 256, RoPE on 64 dims).
 //
-// One wave computes one (query, KV head) pair: the 12 query heads of the group
-// share every gathered K~/V micro-block.  The token list of query p is the
+// A wave walks (query, KV head) pairs -- two in turn in the prefill kernel, one
+// in the training and decode kernels: the 12 query heads of the group share
+// every gathered K~/V micro-block.  The token list of query p is the
 // selected blocks (ascending) followed by its own block 4*floor(p/4) .. p; it is
 // walked in chunks of 8 blocks (32 tokens).
 //
@@ -133,49 +134,82 @@ __device__ __forceinline__ void prefill_slot(int64_t L, int wave, int64_t &i, in
     i = (x - grp * nt) * 4 + wave;
 }
 
-// Prefill: 4 waves per workgroup = 4 queries of one KV group.  The launch
-// covers rows row0 .. row0+L-1 of buffers holding ld rows per sequence.
-__global__ __launch_bounds__(256) void attend_prefill_kernel(
-    Tables tab, int64_t L, int64_t row0, int64_t ld, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
-    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out)
+// Prefill work-group order with two queries per wave: wave w of work-group x
+// takes rows 2s and 2s+1, s = 4x' + w, of one KV group (group 0's work-groups
+// first, as in prefill_slot).
+__device__ __forceinline__ void prefill_pair_slot(int64_t L, int wave, int64_t &i0, int &grp)
 {
-    const int wave = threadIdx.x >> 6;
+    const int64_t nt = (L + 7) / 8;
+    const int64_t x = blockIdx.x;
+    grp = x >= nt ? 1 : 0;
+    i0 = ((x - grp * nt) * 4 + wave) * 2;
+}
+
+// Normalise a finished walk and store the 12 heads of (row, group).
+__device__ __forceinline__ void store_row(const RowState &st, bf16_t *__restrict__ out_row /*[24][256]*/, int grp)
+{
     const int lane = threadIdx.x & 63;
-    const int64_t b = blockIdx.y;
-    int64_t il;
-    int grp;
-    prefill_slot(L, wave, il, grp);
-    if (il >= L) return;
-    const int64_t i = row0 + il;
-    const int64_t pos = q_offset + i;
-    const int64_t o = pos / kBlock;
-    const int own_last = static_cast<int>(pos - o * kBlock);
-    const int n_sel = static_cast<int>(o < budget ? o : budget);
-    const int nchunks = list_chunks(n_sel, o, o);
-
-    bf16x8 qf[8];
-    load_q_frags(q + (b * ld + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
-    const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
-    const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-    const int32_t *sel = block_idx + (b * ld + i) * budget;
-
-    RowState st;
-    init_state(st);
-    attend_chunks<true>(qf, kc, vc, sel, 0, n_sel, o, o, own_last, 0, nchunks, c2, st);
-
     float lt = st.l + __shfl_xor(st.l, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = 1.0f / lt;
     const int h = lane & 15, g = lane >> 4;
     if (h < kGroup) {
-        bf16_t *dst = out + ((b * ld + i) * kQHeads + grp * kGroup + h) * kHeadDim + 4 * g;
+        bf16_t *dst = out_row + (grp * kGroup + h) * kHeadDim + 4 * g;
         for (int n = 0; n < 16; ++n) {
             u32x2 w = u32x2{pack_bf16x2(st.o[n][0] * inv, st.o[n][1] * inv),
                             pack_bf16x2(st.o[n][2] * inv, st.o[n][3] * inv)};
             *reinterpret_cast<u32x2 *>(dst + 16 * n) = w;
         }
     }
+}
+
+// Prefill: 4 waves per work-group, each walking the token lists of two
+// neighbouring queries of one KV group, one chunk of each in turn, each into
+// its own softmax state (a query's chunks in ascending order, as a walk of
+// its own would take them, so the output does not depend on the pairing).
+// Two walks per wave put twice as many walks in progress on a CU for the same
+// bytes in flight, each advancing at half the pace.
+__global__ __launch_bounds__(256) void attend_prefill_kernel(
+    Tables tab, int64_t L, int64_t row0, int64_t ld, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out)
+{
+    const int wave = threadIdx.x >> 6;
+    const int64_t b = blockIdx.y;
+    int64_t il;
+    int grp;
+    prefill_pair_slot(L, wave, il, grp);
+    if (il >= L) return;
+    const bool two = il + 1 < L;          // a ragged launch may end on a lone row
+    const int64_t i0 = row0 + il, i1 = two ? i0 + 1 : i0;
+    const int64_t pos0 = q_offset + i0, pos1 = q_offset + i1;
+    const int64_t o0 = pos0 / kBlock, o1 = pos1 / kBlock;
+    const int own0 = static_cast<int>(pos0 - o0 * kBlock), own1 = static_cast<int>(pos1 - o1 * kBlock);
+    const int nsel0 = static_cast<int>(o0 < budget ? o0 : budget), nsel1 = static_cast<int>(o1 < budget ? o1 : budget);
+    const int nch0 = list_chunks(nsel0, o0, o0), nch1 = two ? list_chunks(nsel1, o1, o1) : 0;
+
+    bf16x8 qf0[8], qf1[8];
+    load_q_frags(q + (b * ld + i0) * kQHeads * kHeadDim, grp, pos0, tab, qf0);
+    load_q_frags(q + (b * ld + i1) * kQHeads * kHeadDim, grp, pos1, tab, qf1);
+    const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
+    const int32_t *sel0 = block_idx + (b * ld + i0) * budget;
+    const int32_t *sel1 = block_idx + (b * ld + i1) * budget;
+
+    RowState st0, st1;
+    init_state(st0);
+    init_state(st1);
+    const int nmax = nch0 > nch1 ? nch0 : nch1;
+    for (int c = 0; c < nmax; ++c) {
+        // the two chunks are not interleaved by the scheduler: one chunk's
+        // gathers and logits at a time fit the register file with both states
+        if (c < nch0) attend_chunks<true>(qf0, kc, vc, sel0, 0, nsel0, o0, o0, own0, c, c + 1, c2, st0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (c < nch1) attend_chunks<true>(qf1, kc, vc, sel1, 0, nsel1, o1, o1, own1, c, c + 1, c2, st1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    store_row(st0, out + (b * ld + i0) * kQHeads * kHeadDim, grp);
+    if (two) store_row(st1, out + (b * ld + i1) * kQHeads * kHeadDim, grp);
 }
 
 // Prefill attention of the training forward: the same walk as
@@ -451,18 +485,24 @@ __global__ __launch_bounds__(256) void attend_decode_merge_kernel(int nsplit, fl
 // what the L2 holds.  Over a long launch the later work-groups start at
 // scattered times and that sharing is lost: at 262,144 tokens one launch over
 // all rows took 114 ms, launches of 32,768 / 8,192 / 4,096 / 2,048 rows 105 /
-// 89 / 85 / 84 ms, with bitwise the same output.
+// 89 / 85 / 84 ms, with bitwise the same output (one query per wave; the
+// training forward's walk keeps that form and 4,096-row launches).
 constexpr int64_t kAttendLaunchRows = 4096;
+// The prefill walk with two queries per wave, in launches of 2,048 rows (one
+// resident set of work-groups per KV group): 84.3-84.4 ms at 262,144 tokens
+// against 85.1-85.4 ms for one query per wave in 4,096-row launches, with
+// bitwise the same output.
+constexpr int64_t kAttendPairLaunchRows = 2048;
 
 hipError_t launch_attend_prefill(const Tables &tab, hipStream_t st, int32_t B, int64_t L, int64_t row0, int64_t ld,
                                  int64_t q_offset, int64_t nblk_cap, int budget, float sigma, const bf16_t *q,
                                  const bf16_t *k_cache, const bf16_t *v_cache, const int32_t *block_idx, bf16_t *out)
 {
-    for (int64_t r = 0; r < L; r += kAttendLaunchRows) {
-        const int64_t n = (r + kAttendLaunchRows < L) ? kAttendLaunchRows : L - r;
-        dim3 grid(static_cast<unsigned>(2 * ((n + 3) / 4)), static_cast<unsigned>(B));
-        hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, n, row0 + r, ld, q_offset, nblk_cap,
-                           budget, sigma * kLog2e, q, k_cache, v_cache, block_idx, out);
+    for (int64_t r = 0; r < L; r += kAttendPairLaunchRows) {
+        const int64_t n = (r + kAttendPairLaunchRows < L) ? kAttendPairLaunchRows : L - r;
+        dim3 grid(static_cast<unsigned>(2 * ((n + 7) / 8)), static_cast<unsigned>(B));
+        hipLaunchKernelGGL(attend_prefill_kernel, grid, dim3(256), 0, st, tab, n, row0 + r, ld, q_offset,
+                           nblk_cap, budget, sigma * kLog2e, q, k_cache, v_cache, block_idx, out);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
