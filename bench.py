@@ -38,16 +38,16 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 
-# HBM-side bytes of the attention over the 262,144-token workload (64 launches
-# of attend_prefill_kernel, 4,096 rows each), read by rocprofv3 --pmc
-# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB per launch, mean of the 192
+# HBM-side bytes of the attention over the 262,144-token workload (128 launches
+# of attend_prefill_kernel, 2,048 rows each), read by rocprofv3 --pmc
+# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000 KiB per launch, mean of the 384
 # launches of three passes; the factors are what the counters read for a plain
 # 1 GiB copy).  The counter summary is
 # profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure is
 # reported only while the kernel's sources hash to the digests it was taken with.
-ATTEND_TRAFFIC_BYTES = (3923186.3 * 2.000 + 49152.0 * 1.000) * 1024 * 64
+ATTEND_TRAFFIC_BYTES = (1809360.5 * 2.000 + 26109.4 * 1.000) * 1024 * 128
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "f9d3b2c65f147f04b87d581cdbbe871b2fc61a4b642ad94bfbca5a224944cece",
+    "k_attend.hip": "0f32f414afc5516dce9fe37cf06f8750129db07a8696fc43c1e2dc63d8c893a9",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "e68f00491eca878a52d16e3650d7ec7653f15dcb5c7fc4ff03e9c640f02d6a24",
 }
