@@ -122,21 +122,11 @@ __device__ __forceinline__ void init_state(RowState &st) {
     for (int n = 0; n < 16; ++n) st.o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Prefill work-group order: all queries of KV group 0, then all of group 1,
-// four consecutive queries per work-group.  The work-groups resident at any
-// time then gather from one group's cache (half of the K~/V bytes), so more
-// of the blocks they ask for are still in the L2: fewer bytes cross to HBM.
-__device__ __forceinline__ void prefill_slot(int64_t L, int wave, int64_t &i, int &grp)
-{
-    const int64_t nt = (L + 3) / 4;
-    const int64_t x = blockIdx.x;
-    grp = x >= nt ? 1 : 0;
-    i = (x - grp * nt) * 4 + wave;
-}
-
-// Prefill work-group order with two queries per wave: wave w of work-group x
-// takes rows 2s and 2s+1, s = 4x' + w, of one KV group (group 0's work-groups
-// first, as in prefill_slot).
+// Prefill work-group order: all queries of KV group 0, then all of group 1;
+// wave w of work-group x takes rows 2s and 2s+1, s = 4x' + w.  The work-groups
+// resident at any time then gather from one group's cache (half of the K~/V
+// bytes), so more of the blocks they ask for are still in the L2: fewer bytes
+// cross to HBM.
 __device__ __forceinline__ void prefill_pair_slot(int64_t L, int wave, int64_t &i0, int &grp)
 {
     const int64_t nt = (L + 7) / 8;
@@ -145,8 +135,11 @@ __device__ __forceinline__ void prefill_pair_slot(int64_t L, int wave, int64_t &
     i0 = ((x - grp * nt) * 4 + wave) * 2;
 }
 
-// Normalise a finished walk and store the 12 heads of (row, group).
-__device__ __forceinline__ void store_row(const RowState &st, bf16_t *__restrict__ out_row /*[24][256]*/, int grp)
+// Normalise a finished walk and store the 12 heads of (row, group); with
+// stats_row, also each head's natural-log log-sum-exp of its scaled logits,
+// sigma*m + ln(l), at stats_row[head].
+__device__ __forceinline__ void store_row(const RowState &st, bf16_t *__restrict__ out_row /*[24][256]*/, int grp,
+                                          float c2, float *__restrict__ stats_row)
 {
     const int lane = threadIdx.x & 63;
     float lt = st.l + __shfl_xor(st.l, 16);
@@ -160,6 +153,7 @@ __device__ __forceinline__ void store_row(const RowState &st, bf16_t *__restrict
                             pack_bf16x2(st.o[n][2] * inv, st.o[n][3] * inv)};
             *reinterpret_cast<u32x2 *>(dst + 16 * n) = w;
         }
+        if (stats_row && g == 0) stats_row[grp * kGroup + h] = (st.m * c2 + log2f(lt)) * kLn2;
     }
 }
 
@@ -169,10 +163,12 @@ __device__ __forceinline__ void store_row(const RowState &st, bf16_t *__restrict
 // its own would take them, so the output does not depend on the pairing).
 // Two walks per wave put twice as many walks in progress on a CU for the same
 // bytes in flight, each advancing at half the pace.
-__global__ __launch_bounds__(256) void attend_prefill_kernel(
-    Tables tab, int64_t L, int64_t row0, int64_t ld, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
+// Rows row0 + il, row0 + il + 1 of a launch of L rows over buffers of ld rows
+// per sequence; stats (or null) receives the log-sum-exps, 32 floats a row.
+__device__ __forceinline__ void attend_pair(
+    const Tables &tab, int64_t L, int64_t row0, int64_t ld, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
-    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out)
+    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out, float *__restrict__ stats)
 {
     const int wave = threadIdx.x >> 6;
     const int64_t b = blockIdx.y;
@@ -208,56 +204,30 @@ __global__ __launch_bounds__(256) void attend_prefill_kernel(
         if (c < nch1) attend_chunks<true>(qf1, kc, vc, sel1, 0, nsel1, o1, o1, own1, c, c + 1, c2, st1);
         __builtin_amdgcn_sched_barrier(0);
     }
-    store_row(st0, out + (b * ld + i0) * kQHeads * kHeadDim, grp);
-    if (two) store_row(st1, out + (b * ld + i1) * kQHeads * kHeadDim, grp);
+    store_row(st0, out + (b * ld + i0) * kQHeads * kHeadDim, grp, c2, stats ? stats + (b * ld + i0) * kTrainStats : nullptr);
+    if (two)
+        store_row(st1, out + (b * ld + i1) * kQHeads * kHeadDim, grp, c2,
+                  stats ? stats + (b * ld + i1) * kTrainStats : nullptr);
 }
 
-// Prefill attention of the training forward: the same walk as
-// attend_prefill_kernel (q_offset 0), and each head's natural-log log-sum-exp of
-// its scaled logits over T(p), sigma*m + ln(l), stored at stats[row*32 + head]
-// for the teacher of the indexer loss.
+__global__ __launch_bounds__(256) void attend_prefill_kernel(
+    Tables tab, int64_t L, int64_t row0, int64_t ld, int64_t q_offset, int64_t nblk_cap, int budget, float c2,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
+    const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out)
+{
+    attend_pair(tab, L, row0, ld, q_offset, nblk_cap, budget, c2, q, k_cache, v_cache, block_idx, out, nullptr);
+}
+
+// Prefill attention of the training forward: the walk of attend_prefill_kernel
+// (q_offset 0) over rows row0 .. row0+n-1 of L, and each head's natural-log
+// log-sum-exp of its scaled logits over T(p), sigma*m + ln(l), stored at
+// stats[row*32 + head] for the teacher of the indexer loss.
 __global__ __launch_bounds__(256) void attend_stats_kernel(
     Tables tab, int64_t L, int64_t n, int64_t row0, int64_t nblk_cap, int budget, float c2,
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k_cache, const bf16_t *__restrict__ v_cache,
     const int32_t *__restrict__ block_idx, bf16_t *__restrict__ out, float *__restrict__ stats)
 {
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int64_t b = blockIdx.y;
-    int64_t il;
-    int grp;
-    prefill_slot(n, wave, il, grp);
-    if (il >= n) return;
-    const int64_t i = row0 + il;          // rows row0 .. row0+n-1 of L
-    const int64_t pos = i;
-    const int64_t o = pos / kBlock;
-    const int own_last = static_cast<int>(pos - o * kBlock);
-    const int n_sel = static_cast<int>(o < budget ? o : budget);
-    const int nchunks = list_chunks(n_sel, o, o);
-
-    bf16x8 qf[8];
-    load_q_frags(q + (b * L + i) * kQHeads * kHeadDim, grp, pos, tab, qf);
-    const bf16_t *kc = k_cache + kcache_block_base(b, grp, 0, nblk_cap);
-    const bf16_t *vc = v_cache + kcache_block_base(b, grp, 0, nblk_cap);
-    const int32_t *sel = block_idx + (b * L + i) * budget;
-
-    RowState st;
-    init_state(st);
-    attend_chunks<true>(qf, kc, vc, sel, 0, n_sel, o, o, own_last, 0, nchunks, c2, st);
-
-    float lt = st.l + __shfl_xor(st.l, 16);
-    lt += __shfl_xor(lt, 32);
-    const float inv = 1.0f / lt;
-    const int h = lane & 15, g = lane >> 4;
-    if (h < kGroup) {
-        bf16_t *dst = out + ((b * L + i) * kQHeads + grp * kGroup + h) * kHeadDim + 4 * g;
-        for (int n = 0; n < 16; ++n) {
-            u32x2 w = u32x2{pack_bf16x2(st.o[n][0] * inv, st.o[n][1] * inv),
-                            pack_bf16x2(st.o[n][2] * inv, st.o[n][3] * inv)};
-            *reinterpret_cast<u32x2 *>(dst + 16 * n) = w;
-        }
-        if (g == 0) stats[(b * L + i) * kTrainStats + grp * kGroup + h] = (st.m * c2 + log2f(lt)) * kLn2;
-    }
+    attend_pair(tab, n, row0, L, 0, nblk_cap, budget, c2, q, k_cache, v_cache, block_idx, out, stats);
 }
 
 // The decode walk: the arithmetic of attend_chunks with the gathers of the
@@ -485,10 +455,8 @@ __global__ __launch_bounds__(256) void attend_decode_merge_kernel(int nsplit, fl
 // what the L2 holds.  Over a long launch the later work-groups start at
 // scattered times and that sharing is lost: at 262,144 tokens one launch over
 // all rows took 114 ms, launches of 32,768 / 8,192 / 4,096 / 2,048 rows 105 /
-// 89 / 85 / 84 ms, with bitwise the same output (one query per wave; the
-// training forward's walk keeps that form and 4,096-row launches).
-constexpr int64_t kAttendLaunchRows = 4096;
-// The prefill walk with two queries per wave, in launches of 2,048 rows (one
+// 89 / 85 / 84 ms, with bitwise the same output (one query per wave).  The
+// walk with two queries per wave, in launches of 2,048 rows (one
 // resident set of work-groups per KV group): 84.3-84.4 ms at 262,144 tokens
 // against 85.1-85.4 ms for one query per wave in 4,096-row launches, with
 // bitwise the same output.
@@ -513,9 +481,9 @@ hipError_t launch_attend_stats(const Tables &tab, hipStream_t st, int32_t B, int
                                float sigma, const bf16_t *q, const bf16_t *k_cache, const bf16_t *v_cache,
                                const int32_t *block_idx, bf16_t *out, float *stats)
 {
-    for (int64_t r = 0; r < L; r += kAttendLaunchRows) {     // short launches: see launch_attend_prefill
-        const int64_t n = (r + kAttendLaunchRows < L) ? kAttendLaunchRows : L - r;
-        dim3 grid(static_cast<unsigned>(2 * ((n + 3) / 4)), static_cast<unsigned>(B));
+    for (int64_t r = 0; r < L; r += kAttendPairLaunchRows) {     // as launch_attend_prefill
+        const int64_t n = (r + kAttendPairLaunchRows < L) ? kAttendPairLaunchRows : L - r;
+        dim3 grid(static_cast<unsigned>(2 * ((n + 7) / 8)), static_cast<unsigned>(B));
         hipLaunchKernelGGL(attend_stats_kernel, grid, dim3(256), 0, st, tab, L, n, r, nblk_cap, budget,
                            sigma * kLog2e, q, k_cache, v_cache, block_idx, out, stats);
         const hipError_t e = hipGetLastError();

@@ -871,7 +871,7 @@ def test_poisoned_caches_and_workspace_leave_results_unchanged():
 
 
 def test_forward_long_equals_staged_calls():
-    """A 70,000-row prefill with B = 2 (the attention in 4,096-row launches,
+    """A 70,000-row prefill with B = 2 (the attention in 2,048-row launches,
     the last one ragged; index + select in 65,536-row launches), in one
     qsa_forward call and as two chunks (65,536 rows, then 4,464 at q_offset
     65,536), is bit-identical to qsa_append + qsa_index_select + qsa_attend
@@ -895,3 +895,22 @@ def test_forward_long_equals_staged_calls():
         del o1, b1
     rows = [0, 8191, 8192, 32767, 32768, 65535, 65536, 69631, 69632, 69999]
     _check_forward(x, f32(o2), b2.cpu().numpy(), O.Params(budget=budget), rows, seqs=(0, 1))
+
+
+def test_forward_attention_launch_boundaries_and_lone_rows():
+    """The prefill attention takes two neighbouring rows per wave in launches
+    of 2,048 rows: rows on both sides of each launch boundary, a last launch of
+    three rows (the pair 4,096-4,097, then row 4,098 alone), and, as chunks of
+    2,052 and 2,047 rows (the second an odd count at q_offset 2,052, whose last
+    row is alone in its wave), bitwise the one-shot result; rows against the
+    oracle."""
+    B, L, budget = 2, 4099, 64
+    w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 52)
+    x, xd = _prefill(w)
+    h = Q.Handle(max_ctx=4100, budget_blocks=budget)       # a whole number of blocks
+    o1, b1, _ = _forward(h, xd, B, L)
+    o2, b2, _ = _forward(h, xd, B, L, chunks=[(0, 2052), (2052, L)])
+    assert torch.equal(b1, b2)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    rows = [0, 1, 2, 2045, 2046, 2047, 2048, 2049, 2050, 2051, 2052, 2053, 4094, 4095, 4096, 4097, 4098]
+    _check_forward(x, f32(o1), b1.cpu().numpy(), O.Params(budget=budget), rows, seqs=(0, 1))
