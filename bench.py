@@ -44,10 +44,12 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # launches of three passes; the factors are what the counters read for a plain
 # 1 GiB copy).  The counter summary is
 # profiles/attend_prefill_kernel_L262144__hbm_counters.md.  The figure is
-# reported only while the kernel's sources hash to the digests it was taken with.
+# reported only while the kernel's sources hash to these digests (sources whose
+# attend_prefill_kernel compiles to the same instructions as the build the
+# counters were taken with).
 ATTEND_TRAFFIC_BYTES = (1809360.5 * 2.000 + 26109.4 * 1.000) * 1024 * 128
 ATTEND_TRAFFIC_SOURCES = {
-    "k_attend.hip": "0f32f414afc5516dce9fe37cf06f8750129db07a8696fc43c1e2dc63d8c893a9",
+    "k_attend.hip": "bc30d8cfe032675f6ab2ee4a2c5b4ba106d1456b11c4725e88382c6761329cc4",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",
     "qsa_common.h": "e68f00491eca878a52d16e3650d7ec7653f15dcb5c7fc4ff03e9c640f02d6a24",
 }
