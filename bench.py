@@ -47,7 +47,7 @@ MFMA_BF16_PEAK_TFS = 2500.0    # MI355X dense bf16, TFLOP/s
 # reported only while the kernel's sources hash to these digests (sources whose
 # attend_prefill_kernel compiles to the same instructions as the build the
 # counters were taken with).
-ATTEND_TRAFFIC_BYTES = (1809360.5 * 2.000 + 26109.4 * 1.000) * 1024 * 128
+ATTEND_TRAFFIC_BYTES = (1809886.1 * 2.000 + 26109.4 * 1.000) * 1024 * 128
 ATTEND_TRAFFIC_SOURCES = {
     "k_attend.hip": "bc30d8cfe032675f6ab2ee4a2c5b4ba106d1456b11c4725e88382c6761329cc4",
     "attend_parts.h": "25edb0e75d70d3aa067623febdd54d9bef69310f4a4340d74e159cf22e4f59a5",

@@ -110,8 +110,12 @@ hipError_t scratch_address(int dev, char **out) {
     return hipSuccess;
 }
 
-// Candidate lists of one fused index + select launch: at most this many bytes.
-constexpr size_t kCandBytes = size_t(4) << 30;
+// Candidate lists of one fused index + select launch: at most this many bytes
+// (the lists of 64 queries reserve 4 MiB at the default cap: 262,144 rows of
+// one sequence in one launch, whose last work-groups are its shortest rows;
+// in four 65,536-row launches each launch's tail left CUs idle, 15.24 against
+// 14.86 ms at 262,144 tokens).
+constexpr size_t kCandBytes = size_t(16) << 30;
 constexpr int kDefaultCap = 8192;
 constexpr size_t kAlign = 256;
 

@@ -184,8 +184,8 @@ qsa_status qsa_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, i
  * lies at or below the query's budget-th largest score; the exact selection is
  * then taken from that short list.  A list longer than topk_cap is recomputed
  * exactly for its row.  Same results as qsa_index + qsa_select.  The
- * workspace holds the rotated queries and the lists of at most 4 GiB of query
- * rows at a time.  ws: qsa_workspace_size(QSA_OP_INDEX_SELECT) bytes. */
+ * workspace holds the rotated queries and the lists of at most 16 GiB of
+ * query rows at a time (8 topk_cap bytes per row and sequence).  ws: qsa_workspace_size(QSA_OP_INDEX_SELECT) bytes. */
 qsa_status qsa_index_select(const qsa_handle *h, void *stream, int32_t B, int64_t L, int64_t q_offset,
                             const uint16_t *q_idx, const uint16_t *kbar_cache, int32_t *block_idx,
                             void *ws, size_t ws_bytes);

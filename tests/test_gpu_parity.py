@@ -871,12 +871,13 @@ def test_poisoned_caches_and_workspace_leave_results_unchanged():
 
 
 def test_forward_long_equals_staged_calls():
-    """A 70,000-row prefill with B = 2 (the attention in 2,048-row launches,
-    the last one ragged; index + select in 65,536-row launches), in one
-    qsa_forward call and as two chunks (65,536 rows, then 4,464 at q_offset
-    65,536), is bit-identical to qsa_append + qsa_index_select + qsa_attend
-    over all rows, and sampled rows match the oracle."""
-    B, L, budget = 2, 70000, 64
+    """A 140,000-row prefill with B = 2 (the attention in 2,048-row launches,
+    the last one ragged; index + select in launches of 131,072 rows, the
+    16 GiB of candidate lists they may hold, then 8,928), in one qsa_forward
+    call and as two chunks (65,536 rows, then 74,464 at q_offset 65,536), is
+    bit-identical to qsa_append + qsa_index_select + qsa_attend over all rows,
+    and sampled rows match the oracle."""
+    B, L, budget = 2, 140000, 64
     w = synth.Workload("t", "prefill", B, L, budget, 8, "random", 48)
     x, xd = _prefill(w)
     h = Q.Handle(max_ctx=L, budget_blocks=budget)
@@ -893,7 +894,7 @@ def test_forward_long_equals_staged_calls():
         assert torch.equal(b1, b2), chunks
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), chunks
         del o1, b1
-    rows = [0, 8191, 8192, 32767, 32768, 65535, 65536, 69631, 69632, 69999]
+    rows = [0, 8191, 8192, 32767, 32768, 65535, 65536, 131071, 131072, 131073, 137215, 137216, 139999]
     _check_forward(x, f32(o2), b2.cpu().numpy(), O.Params(budget=budget), rows, seqs=(0, 1))
 
 
